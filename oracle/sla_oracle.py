@@ -1,0 +1,321 @@
+"""Plain float64 CPU oracle for the sparse + linear attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports this module;
+only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may use it.  It shares no code, constant or helper with the HIP
+library: it computes every step from its definition, slowly and directly, so
+that a reader can check it against the sources by eye.
+
+Sources (cited by short key):
+
+* [SA2 §n]  - the web write-up of SpargeAttention2 (arXiv:2602.13515) titled
+  "清華發明AI「注意力瘦身術」：視頻生成速度提升16倍的神奇技術", section n
+  (§一 the hybrid Top-k / Top-p mask, §四 the pool -> select -> block pipeline,
+  §六 why the two selection rules fail in opposite regimes).
+* [SLA2 §n] - the web write-up of SLA2 (arXiv:2602.12675), section n
+  (§一 sparse branch for important regions, linear branch for the rest;
+  §二 the learnable mixing ratio and the two-matrix learnable router).
+* [DEF] - the textbook dense attention softmax(Q K^T / sqrt(d)) V, which is the
+  only formula the pages print.
+* [FM]  - the feature map phi(x) = elu(x) + 1 of Katharopoulos et al. 2020,
+  "Transformers are RNNs", used for the linear branch.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* pooled scores use the attention scale 1/sqrt(d); P is a row softmax;
+* k = ceil(k_frac * Nk - 1e-9) from float32 k_frac widened to float64;
+* Top-p keeps the item whose cumulative mass first reaches p (inclusive);
+  p <= 0 keeps nothing; if p is never reached every block is kept;
+* ties are broken toward the lower block index, in one order shared by both
+  rules, so the union is the longer prefix of that order;
+* the last block of a sequence may be partial: pooling divides by the true
+  count and keys past N do not exist for either branch;
+* the router is a row vector times a [d, d] matrix, shared by all heads;
+* the linear branch is normalised over the unselected keys only, with no
+  1/sqrt(d); it is 0 when every block is selected, and the sparse branch is 0
+  when none is;
+* O = alpha_h * O_sparse + (1 - alpha_h) * O_linear per head.
+
+Every function works on float64 numpy arrays; inputs given in bf16/fp32 are
+widened exactly, so input rounding is never mistaken for kernel error.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+def as_f64(x) -> np.ndarray:
+    """Widen a torch tensor (any float dtype) or array to float64 exactly."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu").to(torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- partition
+def n_blocks(N: int, b: int) -> int:
+    """Number of blocks of size b covering N tokens; the last may be partial
+    [SA2 §四: the computation is cut into small blocks]."""
+    return -(-N // b)
+
+
+def block_range(i: int, b: int, N: int) -> Tuple[int, int]:
+    """Token range [start, end) of block i."""
+    return i * b, min((i + 1) * b, N)
+
+
+# ---------------------------------------------------------------- pooling
+def pool(X: np.ndarray, b: int) -> np.ndarray:
+    """Block mean pooling of one head's [N, d] rows -> [ceil(N/b), d]
+    [SA2 §四: neighbouring tokens are merged into a quick overview].
+    The mean divides the block's sum by its true token count."""
+    N, d = X.shape
+    nb = n_blocks(N, b)
+    out = np.empty((nb, d), dtype=np.float64)
+    for i in range(nb):
+        s, e = block_range(i, b, N)
+        out[i] = X[s:e].sum(axis=0) / float(e - s)
+    return out
+
+
+def route(xbar: np.ndarray, W: Optional[np.ndarray]) -> np.ndarray:
+    """Learned router projection of pooled vectors, row vector times matrix
+    [SLA2 §二: two learnable projection matrices map query and key features
+    into a space suited to routing].  Identity when W is None."""
+    if W is None:
+        return xbar
+    return xbar @ W
+
+
+def block_scores(qhat: np.ndarray, khat: np.ndarray) -> np.ndarray:
+    """Pooled block logits S_ij = qhat_i . khat_j / sqrt(d) [DEF]."""
+    d = qhat.shape[1]
+    return (qhat @ khat.T) / math.sqrt(d)
+
+
+def row_softmax(S: np.ndarray) -> np.ndarray:
+    """P_ij = exp(S_ij - max_j S_ij) / sum_j exp(S_ij - max_j S_ij)."""
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    return E / E.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------- selection
+def k_from_frac(k_frac: float, Nk: int) -> int:
+    """Top-k count: at least the fraction k_frac of the key blocks.
+    k_frac is taken as the float32 the C interface receives."""
+    kf = float(np.float32(k_frac))
+    k = math.ceil(kf * Nk - 1e-9)
+    return max(0, min(Nk, k))
+
+
+def block_order(P_row: np.ndarray) -> np.ndarray:
+    """Block indices by probability, largest first, ties to the lower index."""
+    Nk = len(P_row)
+    return np.lexsort((np.arange(Nk), -P_row))
+
+
+def topk_count(k: int, Nk: int) -> int:
+    """Top-k keeps a fixed number of blocks whatever the distribution
+    [SA2 §一: a fixed number, e.g. always 3]."""
+    return max(0, min(Nk, k))
+
+
+def topp_count(P_sorted: np.ndarray, p: float) -> int:
+    """Top-p keeps blocks in order until their cumulative importance reaches
+    the threshold p [SA2 §一: keep adding until the sum reaches e.g. 60%].
+    Returns the smallest n with sum of the first n >= p (inclusive reading);
+    0 when p <= 0; every block when p is never reached."""
+    p64 = float(np.float32(p))
+    if p64 <= 0.0:
+        return 0
+    c = np.cumsum(P_sorted)
+    hit = np.nonzero(c >= p64)[0]
+    return int(hit[0]) + 1 if len(hit) else len(P_sorted)
+
+
+def select_row(P_row: np.ndarray, k: int, p: float) -> Tuple[np.ndarray, Dict]:
+    """Hybrid selection for one query block: the union of the Top-k set and
+    the Top-p set [SA2 §一: run both rules, then merge their results].
+    Both sets are prefixes of the same order, so the union is the prefix of
+    length max(k, kp).  Returns ascending block indices and diagnostics."""
+    order = block_order(P_row)
+    Ps = P_row[order]
+    kk = topk_count(k, len(P_row))
+    kp = topp_count(Ps, p)
+    n = max(kk, kp)
+    info = dict(order=order, cum=np.cumsum(Ps), k=kk, kp=kp, n=n)
+    return np.sort(order[:n]), info
+
+
+# ---------------------------------------------------------------- mask
+def mask(Q, K, bq: int, bk: int, k_frac: float, p: float, Wq=None, Wk=None,
+         keep_info: bool = True):
+    """Block mask of every (b, h, query block) as CSR.
+
+    Q, K: [B, H, N, d].  Rows are ordered (b, h, i); column indices ascending.
+    Returns (row_ptr int64 [R+1], col_idx int64 [nnz], info) where info holds,
+    per row, the logits S, the probabilities P, the order, the cumulative sums
+    and the counts (used to judge blocks that sit on the selection cut).
+    [SA2 §四: pool -> hybrid select on the pooled map -> block-level mask
+    marking each block important or negligible.]
+    """
+    Q = as_f64(Q)
+    K = as_f64(K)
+    Wq = None if Wq is None else as_f64(Wq)
+    Wk = None if Wk is None else as_f64(Wk)
+    B, H, N, d = Q.shape
+    Nq, Nk = n_blocks(N, bq), n_blocks(N, bk)
+    k = k_from_frac(k_frac, Nk)
+    counts: List[int] = []
+    cols: List[np.ndarray] = []
+    S_all = np.empty((B, H, Nq, Nk))
+    P_all = np.empty((B, H, Nq, Nk))
+    rows_info = []
+    for b in range(B):
+        for h in range(H):
+            qhat = route(pool(Q[b, h], bq), Wq)
+            khat = route(pool(K[b, h], bk), Wk)
+            S = block_scores(qhat, khat)
+            P = row_softmax(S)
+            S_all[b, h] = S
+            P_all[b, h] = P
+            for i in range(Nq):
+                sel, info = select_row(P[i], k, p)
+                counts.append(len(sel))
+                cols.append(sel)
+                if keep_info:
+                    rows_info.append(info)
+    row_ptr = np.zeros(len(counts) + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col_idx = np.concatenate(cols).astype(np.int64) if cols else np.zeros(0, np.int64)
+    meta = dict(S=S_all, P=P_all, rows=rows_info, k=k, Nq=Nq, Nk=Nk)
+    return row_ptr, col_idx, meta
+
+
+# ---------------------------------------------------------------- branches
+def _keys_of(blocks: Iterable[int], bk: int, N: int) -> np.ndarray:
+    """Token indices of the given key blocks (partial last block clipped)."""
+    idx = [np.arange(*block_range(int(j), bk, N)) for j in blocks]
+    return np.concatenate(idx) if idx else np.zeros(0, dtype=np.int64)
+
+
+def phi(x: np.ndarray) -> np.ndarray:
+    """Linear-attention feature map elu(x) + 1 [FM]: x + 1 for x > 0, exp(x)
+    otherwise (always positive)."""
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def _rows(B: int, H: int, Nq: int, rows):
+    if rows is None:
+        return [(b, h, i) for b in range(B) for h in range(H) for i in range(Nq)]
+    return list(rows)
+
+
+def sparse_branch(Q, K, V, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+    """Exact softmax attention of each query token over the keys of its
+    block's selected key blocks only, renormalised over them
+    [SLA2 §一: important regions get precise sparse attention; SLA2 §二: the
+    sparse branch renormalises over what it keeps].  Two-pass softmax
+    (max, then exp / sum).  Zero when no block is selected.
+    Returns {(b, h, i): [rows_in_block, d]} for the requested rows."""
+    Q, K, V = as_f64(Q), as_f64(K), as_f64(V)
+    B, H, N, d = Q.shape
+    Nq = n_blocks(N, bq)
+    out = {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        s, e = block_range(i, bq, N)
+        keys = _keys_of(sel, bk, N)
+        if len(keys) == 0:
+            out[(b, h, i)] = np.zeros((e - s, d))
+            continue
+        Sx = Q[b, h, s:e] @ K[b, h, keys].T / math.sqrt(d)
+        m = Sx.max(axis=1, keepdims=True)
+        E = np.exp(Sx - m)
+        out[(b, h, i)] = (E @ V[b, h, keys]) / E.sum(axis=1, keepdims=True)
+    return out
+
+
+def linear_branch(Q, K, V, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+    """Linear attention of each query token over the keys of the key blocks
+    its block did NOT select [SLA2 §一: the less important regions go to the
+    cheaper linear attention], by direct summation:
+        O_l(t) = sum_u (phi(q_t).phi(k_u)) v_u / sum_u phi(q_t).phi(k_u)
+    over the unselected keys u.  Zero when every block is selected."""
+    Q, K, V = as_f64(Q), as_f64(K), as_f64(V)
+    B, H, N, d = Q.shape
+    Nq, Nk = n_blocks(N, bq), n_blocks(N, bk)
+    out = {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = set(int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]])
+        unsel = [j for j in range(Nk) if j not in sel]
+        s, e = block_range(i, bq, N)
+        keys = _keys_of(unsel, bk, N)
+        if len(keys) == 0:
+            out[(b, h, i)] = np.zeros((e - s, d))
+            continue
+        A = phi(Q[b, h, s:e]) @ phi(K[b, h, keys]).T
+        out[(b, h, i)] = (A @ V[b, h, keys]) / A.sum(axis=1, keepdims=True)
+    return out
+
+
+def combine(Os: np.ndarray, Ol: np.ndarray, alpha_h: float) -> np.ndarray:
+    """O = alpha * O_sparse + (1 - alpha) * O_linear [SLA2 §二: the final
+    result is the ratio times the sparse result plus one minus the ratio times
+    the linear result]."""
+    a = float(alpha_h)
+    return a * Os + (1.0 - a) * Ol
+
+
+def attn(Q, K, V, alpha, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+    """Full forward output for the requested rows given a mask (CSR).
+    Branches whose weight is exactly zero are not evaluated."""
+    alpha = as_f64(alpha)
+    Qa = as_f64(Q)
+    B, H, N, d = Qa.shape
+    Nq = n_blocks(N, bq)
+    rows = _rows(B, H, Nq, rows)
+    need_s = [r for r in rows if alpha[r[1]] != 0.0]
+    need_l = [r for r in rows if alpha[r[1]] != 1.0]
+    Os = sparse_branch(Qa, K, V, bq, bk, row_ptr, col_idx, need_s) if need_s else {}
+    Ol = linear_branch(Qa, K, V, bq, bk, row_ptr, col_idx, need_l) if need_l else {}
+    out = {}
+    for (b, h, i) in rows:
+        s, e = block_range(i, bq, N)
+        zero = np.zeros((e - s, d))
+        out[(b, h, i)] = combine(Os.get((b, h, i), zero), Ol.get((b, h, i), zero), alpha[h])
+    return out
+
+
+def dense(Q, K, V, rows: Optional[Sequence[Tuple[int, int, int]]] = None, bq: int = 128) -> Dict:
+    """Dense attention softmax(Q K^T / sqrt(d)) V [DEF], per query block of
+    size bq (the blocking only selects which outputs to compute)."""
+    Q, K, V = as_f64(Q), as_f64(K), as_f64(V)
+    B, H, N, d = Q.shape
+    Nq = n_blocks(N, bq)
+    out = {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        s, e = block_range(i, bq, N)
+        Sx = Q[b, h, s:e] @ K[b, h].T / math.sqrt(d)
+        m = Sx.max(axis=1, keepdims=True)
+        E = np.exp(Sx - m)
+        out[(b, h, i)] = (E @ V[b, h]) / E.sum(axis=1, keepdims=True)
+    return out
+
+
+def assemble(blocks: Dict, B: int, H: int, N: int, d: int, bq: int) -> np.ndarray:
+    """Place per-row outputs into a [B, H, N, d] array (NaN where not computed)."""
+    out = np.full((B, H, N, d), np.nan)
+    for (b, h, i), v in blocks.items():
+        s, e = block_range(i, bq, N)
+        out[b, h, s:e] = v
+    return out
