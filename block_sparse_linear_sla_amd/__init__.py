@@ -1,0 +1,202 @@
+"""Python binding of libsla.so, the gfx950 sparse + linear attention forward.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library.  Tensors are torch CUDA tensors (device memory); work goes on
+torch's current stream.  The functions carry the C interface's names
+(include/sla.h); each allocates its outputs and workspace with torch unless
+buffers are passed in.
+
+There is no fallback: if libsla.so is missing or cannot be loaded, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("SLA_LIB", os.path.join(_HERE, "libsla.so"))
+
+SLA_F32, SLA_BF16 = 0, 1
+STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
+          -3: "SLA_ERR_WORKSPACE", -4: "SLA_ERR_CAPACITY", -5: "SLA_ERR_HIP"}
+EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_sparse_fwd",
+           "sla_linear_fwd", "sla_attn_fwd", "sla_dense_fwd", "sla_status_string")
+
+
+class SlaError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("bq", ctypes.c_int32), ("bk", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Select(ctypes.Structure):
+    _fields_ = [("k_frac", ctypes.c_float), ("p", ctypes.c_float),
+                ("Wq", ctypes.c_void_p), ("Wk", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsla.so once (raises if it is missing: there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} not found; build it with "
+                               "`python -m block_sparse_linear_sla_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, S, vp = ctypes.POINTER(Problem), ctypes.POINTER(Select), ctypes.c_void_p
+        L.sla_workspace_bytes.argtypes = [P, S]
+        L.sla_workspace_bytes.restype = ctypes.c_size_t
+        L.sla_mask_capacity.argtypes = [P]
+        L.sla_mask_capacity.restype = ctypes.c_int64
+        L.sla_mask.argtypes = [P, S, vp, vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
+        L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.sla_linear_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_attn_fwd.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
+                                   ctypes.c_size_t, vp]
+        L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp]
+        L.sla_status_string.argtypes = [ctypes.c_int]
+        L.sla_status_string.restype = ctypes.c_char_p
+        for fn in ("sla_mask", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd", "sla_dense_fwd"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise SlaError(fn, status, lib().sla_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SLA_BF16
+    if t.dtype == torch.float32:
+        return SLA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def problem(q: torch.Tensor, bq: int, bk: int) -> Problem:
+    if q.dim() != 4:
+        raise ValueError("expected [B, H, N, d]")
+    B, H, N, d = q.shape
+    return Problem(B, H, N, d, bq, bk, _dtype_code(q))
+
+
+def select(k_frac: float, p: float, wq: Optional[torch.Tensor] = None,
+           wk: Optional[torch.Tensor] = None) -> Select:
+    return Select(float(k_frac), float(p), _ptr(wq), _ptr(wk))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(*ts: torch.Tensor, like: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous CUDA tensors")
+        if t.shape != like.shape or t.dtype != like.dtype:
+            raise ValueError("Q, K, V (and outputs) must share shape and dtype")
+
+
+def sla_workspace_bytes(prob: Problem, sel: Optional[Select] = None) -> int:
+    return int(lib().sla_workspace_bytes(ctypes.byref(prob), ctypes.byref(sel) if sel else None))
+
+
+def sla_mask_capacity(prob: Problem) -> int:
+    return int(lib().sla_mask_capacity(ctypes.byref(prob)))
+
+
+def workspace(prob: Problem, sel: Optional[Select] = None, device=None) -> torch.Tensor:
+    n = sla_workspace_bytes(prob, sel)
+    if n == 0:
+        raise ValueError("invalid problem")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sla_mask(q, k, bq: int, bk: int, k_frac: float, p: float, wq=None, wk=None,
+             return_logits: bool = False, ws: Optional[torch.Tensor] = None,
+             row_ptr: Optional[torch.Tensor] = None, col_idx: Optional[torch.Tensor] = None):
+    """Block mask as CSR: (row_ptr int32 [R+1], col_idx int32 [capacity]) and,
+    if asked, the pooled logits (float64 [B, H, Nq, Nk]).  Only the first
+    row_ptr[-1] entries of col_idx are meaningful."""
+    _need(q, k, like=q)
+    prob, sel = problem(q, bq, bk), select(k_frac, p, wq, wk)
+    cap = sla_mask_capacity(prob)
+    B, H = q.shape[:2]
+    Nq, Nk = -(-q.shape[2] // bq), -(-q.shape[2] // bk)
+    dev = q.device
+    rp = row_ptr if row_ptr is not None else torch.empty(B * H * Nq + 1, dtype=torch.int32, device=dev)
+    ci = col_idx if col_idx is not None else torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    logits = torch.empty((B, H, Nq, Nk), dtype=torch.float64, device=dev) if return_logits else None
+    w = ws if ws is not None else workspace(prob, sel, dev)
+    _check("sla_mask", lib().sla_mask(ctypes.byref(prob), ctypes.byref(sel), _ptr(q), _ptr(k),
+                                      _ptr(rp), _ptr(ci), ci.numel(), _ptr(logits), _ptr(w),
+                                      w.numel(), _stream()))
+    return (rp, ci, logits) if return_logits else (rp, ci)
+
+
+def sla_sparse_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None):
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    o = out if out is not None else torch.empty_like(q)
+    _check("sla_sparse_fwd", lib().sla_sparse_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                                  _ptr(row_ptr), _ptr(col_idx), _ptr(o), _stream()))
+    return o
+
+
+def sla_linear_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None, ws=None):
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    o = out if out is not None else torch.empty_like(q)
+    w = ws if ws is not None else workspace(prob, None, q.device)
+    _check("sla_linear_fwd", lib().sla_linear_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                                  _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(w),
+                                                  w.numel(), _stream()))
+    return o
+
+
+def sla_attn_fwd(q, k, v, alpha, bq: int, bk: int, k_frac: float, p: float, wq=None, wk=None,
+                 out=None, ws=None, row_ptr=None, col_idx=None) -> Tuple[torch.Tensor, ...]:
+    """Whole forward.  Returns (O, row_ptr, col_idx)."""
+    _need(q, k, v, like=q)
+    if not alpha.is_cuda or alpha.dtype != torch.float32 or alpha.numel() != q.shape[1]:
+        raise ValueError("alpha must be a CUDA float32 tensor of H entries")
+    prob, sel = problem(q, bq, bk), select(k_frac, p, wq, wk)
+    cap = sla_mask_capacity(prob)
+    B, H = q.shape[:2]
+    Nq = -(-q.shape[2] // bq)
+    dev = q.device
+    o = out if out is not None else torch.empty_like(q)
+    rp = row_ptr if row_ptr is not None else torch.empty(B * H * Nq + 1, dtype=torch.int32, device=dev)
+    ci = col_idx if col_idx is not None else torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    w = ws if ws is not None else workspace(prob, sel, dev)
+    _check("sla_attn_fwd", lib().sla_attn_fwd(ctypes.byref(prob), ctypes.byref(sel), _ptr(q), _ptr(k),
+                                              _ptr(v), _ptr(alpha), _ptr(o), _ptr(rp), _ptr(ci),
+                                              ci.numel(), _ptr(w), w.numel(), _stream()))
+    return o, rp, ci
+
+
+def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None):
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    o = out if out is not None else torch.empty_like(q)
+    _check("sla_dense_fwd", lib().sla_dense_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                                _stream()))
+    return o

@@ -1,0 +1,202 @@
+// Host side of the C interface: argument validation, workspace carving and
+// the launch sequence of each entry point.  Nothing here synchronises, copies
+// device memory to the host or allocates.
+#include <math.h>
+
+#include "sla.h"
+#include "sla_internal.h"
+
+namespace sla {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const Shape& s, bool router) {
+  WsLayout L{};
+  const size_t BH = (size_t)s.B * s.H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  L.qbar = take(BH * s.Nq * s.d * sizeof(double));
+  L.kbar = take(BH * s.Nk * s.d * sizeof(double));
+  L.qhat = router ? take(BH * s.Nq * s.d * sizeof(double)) : 0;
+  L.khat = router ? take(BH * s.Nk * s.d * sizeof(double)) : 0;
+  L.S = take(BH * s.Nq * s.Nk * sizeof(double));
+  L.counts = take((size_t)s.R() * sizeof(int32_t));
+  L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
+  // Linear summary partials: chunks of key blocks sized so that the summary
+  // pass has on the order of a thousand workgroups.
+  int cb = (int)((BH * s.Nk + 1023) / 1024);
+  if (cb < 4) cb = 4;
+  if (cb > s.Nk) cb = s.Nk;
+  L.chunk_blocks = cb;
+  L.nchunk = (s.Nk + cb - 1) / cb;
+  const size_t per = (size_t)s.d * s.d + s.d;
+  L.hpart = take(BH * L.nchunk * per * sizeof(float));
+  L.htot = take(BH * per * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace sla
+
+using sla::Mode;
+using sla::Shape;
+using sla::WsLayout;
+
+namespace {
+
+// Validates the shape; fills s on success.
+int check_problem(const sla_problem* p, Shape* s) {
+  if (p == nullptr) return SLA_ERR_INVALID_ARG;
+  if (p->B < 1 || p->H < 1 || p->N < 1 || p->d < 1 || p->bq < 1 || p->bk < 1) return SLA_ERR_INVALID_ARG;
+  if (p->dtype != SLA_F32 && p->dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (p->d != 64 && p->d != 128) return SLA_ERR_UNSUPPORTED;
+  if ((p->bq != 64 && p->bq != 128) || (p->bk != 64 && p->bk != 128)) return SLA_ERR_UNSUPPORTED;
+  const long long elems = (long long)p->B * p->H * p->N * p->d;
+  if (elems >= (1LL << 31)) return SLA_ERR_UNSUPPORTED;
+  s->B = p->B; s->H = p->H; s->N = p->N; s->d = p->d; s->bq = p->bq; s->bk = p->bk;
+  s->dtype = p->dtype;
+  s->Nq = (p->N + p->bq - 1) / p->bq;
+  s->Nk = (p->N + p->bk - 1) / p->bk;
+  if (s->Nk > 4096) return SLA_ERR_UNSUPPORTED;
+  if ((long long)s->B * s->H * s->Nq * s->Nk >= (1LL << 31)) return SLA_ERR_UNSUPPORTED;
+  return SLA_OK;
+}
+
+int check_select(const sla_select* sel, int* k, const Shape& s) {
+  if (sel == nullptr) return SLA_ERR_INVALID_ARG;
+  const float kf = sel->k_frac, p = sel->p;
+  if (!(kf >= 0.f && kf <= 1.f) || !(p >= 0.f && p <= 1.f)) return SLA_ERR_INVALID_ARG;
+  if ((sel->Wq == nullptr) != (sel->Wk == nullptr)) return SLA_ERR_INVALID_ARG;
+  long long kk = (long long)ceil((double)kf * (double)s.Nk - 1e-9);
+  if (kk < 0) kk = 0;
+  if (kk > s.Nk) kk = s.Nk;
+  *k = (int)kk;
+  return SLA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_HIP; }
+
+hipError_t run_summary(const Shape& s, const void* K, const void* V, const float* alpha, char* ws,
+                       const WsLayout& L, hipStream_t st) {
+  return s.dtype == SLA_BF16 ? sla::launch_summary_bf16(s, K, V, alpha, ws, L, st)
+                             : sla::launch_summary_f32(s, K, V, alpha, ws, L, st);
+}
+
+hipError_t run_attn(const Shape& s, Mode m, const void* Q, const void* K, const void* V,
+                    const int32_t* rp, const int32_t* ci, const float* alpha, const float* htot,
+                    void* O, hipStream_t st) {
+  return s.dtype == SLA_BF16 ? sla::launch_attn_bf16(s, m, Q, K, V, rp, ci, alpha, htot, O, st)
+                             : sla::launch_attn_f32(s, m, Q, K, V, rp, ci, alpha, htot, O, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sla_workspace_bytes(const sla_problem* prob, const sla_select* sel) {
+  Shape s;
+  if (check_problem(prob, &s) != SLA_OK) return 0;
+  const bool router = sel != nullptr && sel->Wq != nullptr;
+  return sla::ws_layout(s, router).total;
+}
+
+int64_t sla_mask_capacity(const sla_problem* prob) {
+  Shape s;
+  if (check_problem(prob, &s) != SLA_OK) return -1;
+  return (int64_t)s.B * s.H * s.Nq * s.Nk;
+}
+
+int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+             int32_t* row_ptr, int32_t* col_idx, int64_t capacity, double* block_logits, void* ws,
+             size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  int k;
+  if ((rc = check_select(sel, &k, s)) != SLA_OK) return rc;
+  if (Q == nullptr || K == nullptr || row_ptr == nullptr || col_idx == nullptr) return SLA_ERR_INVALID_ARG;
+  if (capacity < (int64_t)s.B * s.H * s.Nq * s.Nk) return SLA_ERR_CAPACITY;
+  const WsLayout L = sla::ws_layout(s, sel->Wq != nullptr);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx,
+                                     block_logits, static_cast<char*>(ws), L,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (!Q || !K || !V || !row_ptr || !col_idx || !O_s) return SLA_ERR_INVALID_ARG;
+  return hip_status(run_attn(s, sla::MODE_SPARSE, Q, K, V, row_ptr, col_idx, nullptr, nullptr, O_s,
+                             static_cast<hipStream_t>(stream)));
+}
+
+int sla_linear_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_l, void* ws,
+                   size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (!Q || !K || !V || !row_ptr || !col_idx || !O_l) return SLA_ERR_INVALID_ARG;
+  const WsLayout L = sla::ws_layout(s, false);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = run_summary(s, K, V, nullptr, w, L, st);
+  if (e != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(run_attn(s, sla::MODE_LINEAR, Q, K, V, row_ptr, col_idx, nullptr,
+                             reinterpret_cast<const float*>(w + L.htot), O_l, st));
+}
+
+int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+                 const void* V, const float* alpha, void* O, int32_t* row_ptr, int32_t* col_idx,
+                 int64_t capacity, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  int k;
+  if ((rc = check_select(sel, &k, s)) != SLA_OK) return rc;
+  if (!Q || !K || !V || !alpha || !O || !row_ptr || !col_idx) return SLA_ERR_INVALID_ARG;
+  if (capacity < (int64_t)s.B * s.H * s.Nq * s.Nk) return SLA_ERR_CAPACITY;
+  const WsLayout L = sla::ws_layout(s, sel->Wq != nullptr);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  hipError_t e = sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx,
+                                  nullptr, w, L, st);
+  if (e != hipSuccess) return SLA_ERR_HIP;
+  e = run_summary(s, K, V, alpha, w, L, st);
+  if (e != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(run_attn(s, sla::MODE_FUSED, Q, K, V, row_ptr, col_idx, alpha,
+                             reinterpret_cast<const float*>(w + L.htot), O, st));
+}
+
+int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
+                  void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (!Q || !K || !V || !O) return SLA_ERR_INVALID_ARG;
+  return hip_status(run_attn(s, sla::MODE_DENSE, Q, K, V, nullptr, nullptr, nullptr, nullptr, O,
+                             static_cast<hipStream_t>(stream)));
+}
+
+const char* sla_status_string(int status) {
+  switch (status) {
+    case SLA_OK: return "ok";
+    case SLA_ERR_INVALID_ARG: return "invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "unsupported shape, block size or dtype";
+    case SLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SLA_ERR_CAPACITY: return "col_idx capacity below B*H*Nq*Nk";
+    case SLA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Internal declarations shared by the host side of the C interface and the
+// kernel translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sla {
+
+// Problem shape with derived block counts.
+struct Shape {
+  int B, H, N, d, bq, bk, dtype;
+  int Nq, Nk;  // ceil(N / bq), ceil(N / bk)
+  long long R() const { return (long long)B * H * Nq; }
+  int words() const { return (Nk + 31) / 32; }  // bitmask words per mask row
+};
+
+// Byte offsets of the workspace regions (all 256-byte aligned).
+struct WsLayout {
+  size_t qbar, kbar;   // pooled means, double [B*H*Nq*d], [B*H*Nk*d]
+  size_t qhat, khat;   // routed pooled vectors (router only), same sizes
+  size_t S;            // pooled logits, double [B*H*Nq*Nk]
+  size_t counts;       // int32 [R]
+  size_t bits;         // uint32 [R * words]
+  size_t hpart;        // linear summary partials, float [B*H*nchunk*(d*d + d)]
+  size_t htot;         // linear summaries, float [B*H*(d*d + d)]
+  size_t total;
+  int nchunk;          // key-block chunks per head in the summary pass
+  int chunk_blocks;    // key blocks per chunk
+};
+
+WsLayout ws_layout(const Shape& s, bool router);
+
+// Mode of the attention kernels.
+enum Mode : int {
+  MODE_SPARSE = 0,  // O = O_s over the CSR row
+  MODE_LINEAR = 1,  // O = O_l over the complement of the CSR row
+  MODE_FUSED = 2,   // O = alpha_h O_s + (1 - alpha_h) O_l
+  MODE_DENSE = 3,   // O = softmax attention over every key block
+};
+
+// mask.hip: pooling, optional router, pooled logits, selection, CSR.
+hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const float* Wk,
+                       const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
+                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st);
+
+// attn_bf16.hip / attn_f32.hip: linear summaries (H = sum_u phi(k_u)^T v_u,
+// z = sum_u phi(k_u) per head) into the workspace; heads whose alpha is
+// exactly 1 are skipped when alpha is given.
+hipError_t launch_summary_bf16(const Shape& s, const void* K, const void* V, const float* alpha,
+                               char* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,
+                              char* ws, const WsLayout& L, hipStream_t st);
+
+// Attention over the mask.  htot (float [B*H*(d*d + d)]) is needed for the
+// linear and fused modes; alpha for the fused mode.
+hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
+                            const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,
+                            const float* htot, void* O, hipStream_t st);
+hipError_t launch_attn_f32(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
+                           const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,
+                           const float* htot, void* O, hipStream_t st);
+
+}  // namespace sla

@@ -1,0 +1,141 @@
+/*
+ * sla.h - C interface of the MI355X (gfx950) sparse + linear attention forward.
+ *
+ * The library computes, for attention inputs Q, K, V of shape [B, H, N, d]:
+ *
+ *   1. a block mask: Q and K are cut into blocks of bq and bk tokens and
+ *      mean-pooled per block; the pooled vectors (optionally passed through
+ *      two router matrices) give block logits S_ij = q_i . k_j / sqrt(d) and a
+ *      row softmax P; each query block keeps the union of its Top-k blocks
+ *      (k = ceil(k_frac * Nk)) and its Top-p blocks (the shortest
+ *      largest-first prefix whose probability mass reaches p).  Sources: the
+ *      SpargeAttention2 write-up "清華發明AI「注意力瘦身術」：視頻生成速度提升16倍
+ *      的神奇技術" (arXiv:2602.13515), §一 (hybrid Top-k / Top-p) and §四
+ *      (pool, select, block-level mask);
+ *   2. the sparse branch: exact softmax attention of each query over the keys
+ *      of its selected blocks only (SLA2 write-up, arXiv:2602.12675, §一);
+ *   3. the linear branch: linear attention with phi(x) = elu(x) + 1 over the
+ *      keys of the blocks NOT selected (SLA2 write-up §一), and the mix
+ *      O = alpha_h * O_sparse + (1 - alpha_h) * O_linear with one alpha per
+ *      head (SLA2 write-up §二).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  Q, K, V and
+ *     outputs are contiguous [B, H, N, d] (d fastest) in the problem dtype
+ *     (fp32 or bf16).  Blocks are consecutive tokens; the last block of a
+ *     sequence may be partial.
+ *   - The mask is CSR over rows r = (b * H + h) * Nq + i: row_ptr int32
+ *     [R + 1], col_idx int32 (key-block indices ascending within a row),
+ *     with Nq = ceil(N / bq), Nk = ceil(N / bk), R = B * H * Nq.
+ *   - The library never allocates device memory and never synchronises.
+ *     Scratch space comes from the caller's workspace (size from
+ *     sla_workspace_bytes).  All work is enqueued on the caller's HIP stream
+ *     (a hipStream_t passed as void*; NULL = the default stream).
+ *   - Every function returns a status: SLA_OK (0) or a negative code.
+ *     Argument errors are detected on the host before anything is launched
+ *     and nothing is then written.  SLA_ERR_HIP reports a launch failure.
+ *   - No global state: calls on different streams may run concurrently as
+ *     long as their workspaces and outputs do not overlap.
+ *   - Supported: dtype fp32 or bf16; d in {64, 128}; bq, bk in {64, 128};
+ *     Nk <= 4096; B * H * N * d < 2^31.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sla_dtype { SLA_F32 = 0, SLA_BF16 = 1 };
+
+enum sla_status {
+  SLA_OK = 0,
+  SLA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, k_frac/p outside [0,1] or NaN */
+  SLA_ERR_UNSUPPORTED = -2, /* d, bq, bk, dtype or size outside the supported set */
+  SLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than sla_workspace_bytes */
+  SLA_ERR_CAPACITY = -4,    /* col_idx capacity below B*H*Nq*Nk */
+  SLA_ERR_HIP = -5          /* a kernel launch failed */
+};
+
+/* Problem shape.  dtype is an sla_dtype value. */
+typedef struct sla_problem {
+  int32_t B, H, N, d;
+  int32_t bq, bk;
+  int32_t dtype;
+} sla_problem;
+
+/* Selection parameters.
+ *   k_frac  Top-k fraction in [0, 1]; k = ceil(k_frac * Nk - 1e-9) computed
+ *           in double from this float.
+ *   p       Top-p mass threshold in [0, 1]; the block whose cumulative mass
+ *           first reaches p is kept; p = 0 keeps none by Top-p.
+ *   Wq, Wk  optional router matrices (both or neither), DEVICE fp32 [d, d]
+ *           row-major, shared by all heads: q_hat = q_bar . Wq (row vector
+ *           times matrix), k_hat = k_bar . Wk.  SLA2 write-up §二: a learnable
+ *           router of two projection matrices. */
+typedef struct sla_select {
+  float k_frac;
+  float p;
+  const float* Wq;
+  const float* Wk;
+} sla_select;
+
+/* Bytes of device workspace every entry point below needs for this problem
+ * (host-only arithmetic; 0 on invalid arguments).  sel may be NULL (no router). */
+size_t sla_workspace_bytes(const sla_problem* prob, const sla_select* sel);
+
+/* Worst-case number of mask entries, B * H * Nq * Nk (the col_idx capacity the
+ * mask calls require), or -1 on invalid arguments. */
+int64_t sla_mask_capacity(const sla_problem* prob);
+
+/* Build the block mask (SpargeAttention2 write-up §一, §四).
+ *   Q, K          inputs [B, H, N, d]
+ *   row_ptr       out, int32 [B*H*Nq + 1]; row_ptr[R] is the number of entries
+ *   col_idx       out, int32 [capacity]; entries past row_ptr[R] are untouched
+ *   capacity      must be >= sla_mask_capacity(prob)
+ *   block_logits  optional out, double [B, H, Nq, Nk]: the pooled logits S that
+ *                 the selection used (for inspection); NULL to skip
+ *   ws, ws_bytes  workspace (>= sla_workspace_bytes) */
+int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+             int32_t* row_ptr, int32_t* col_idx, int64_t capacity, double* block_logits,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse branch alone (SLA2 write-up §一): O_s[t] = softmax over the keys of the
+ * blocks listed in row (b, h, t / bq) of the mask, of q_t . k / sqrt(d), times V.
+ * Rows with no selected block are written as 0.  Output O_s [B, H, N, d]. */
+int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
+
+/* Linear branch alone (SLA2 write-up §一): O_l[t] = sum_u (phi(q_t).phi(k_u)) v_u /
+ * sum_u phi(q_t).phi(k_u) over the keys u of the blocks NOT listed in the row;
+ * phi(x) = elu(x) + 1.  Rows whose blocks are all listed are written as 0.
+ * Output O_l [B, H, N, d].  Needs the workspace. */
+int sla_linear_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_l,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* The whole forward: mask, then O = alpha_h * O_s + (1 - alpha_h) * O_l
+ * (SLA2 write-up §二), written once in the input dtype.
+ *   alpha    DEVICE fp32 [H], each in [0, 1]; a branch whose weight is exactly
+ *            0 for a head is not evaluated for that head
+ *   row_ptr, col_idx, capacity   the mask, returned as by sla_mask */
+int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+                 const void* V, const float* alpha, void* O, int32_t* row_ptr,
+                 int32_t* col_idx, int64_t capacity, void* ws, size_t ws_bytes, void* stream);
+
+/* Dense softmax(Q K^T / sqrt(d)) V over every key, the comparator the sparse
+ * path is measured against.  Output O [B, H, N, d]. */
+int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
+                  void* stream);
+
+/* Static text for a status code. */
+const char* sla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

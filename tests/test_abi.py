@@ -1,0 +1,136 @@
+"""The C interface loads without a GPU, exports every declared symbol, and
+rejects invalid arguments on the host before launching anything (CPU only:
+no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_linear_sla_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(S.LIB_PATH),
+                                reason="libsla.so not built (run __graft_entry__.build())")
+
+INVALID, UNSUPPORTED, WORKSPACE, CAPACITY = -1, -2, -3, -4
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(sla_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert set(names) == set(S.EXPORTS), names
+    L = S.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = S.lib()
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert len(L.sla_status_string(code)) > 0
+
+
+def prob(**kw):
+    base = dict(B=1, H=2, N=1024, d=64, bq=64, bk=64, dtype=S.SLA_F32)
+    base.update(kw)
+    return S.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), INVALID), (dict(H=-1), INVALID), (dict(N=0), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(d=256), UNSUPPORTED), (dict(bq=32), UNSUPPORTED),
+    (dict(bk=256), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(N=4096 * 64 + 1, bk=64, H=1), UNSUPPORTED),          # Nk > 4096
+    (dict(B=64, H=64, N=8192, d=128), UNSUPPORTED),           # > 2^31 elements
+])
+def test_bad_problem(kw, code):
+    L = S.lib()
+    p = prob(**kw)
+    sel = S.Select(0.1, 0.6, None, None)
+    assert L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(sel)) == 0
+    assert L.sla_mask_capacity(ctypes.byref(p)) == -1
+    st = None
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, 1 << 30, None,
+                      FAKE, 1 << 40, st) == code
+    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, st) == code
+    assert L.sla_linear_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, st) == code
+    assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          1 << 30, FAKE, 1 << 40, st) == code
+    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, st) == code
+
+
+def test_null_problem_and_select():
+    L = S.lib()
+    p = prob()
+    assert L.sla_workspace_bytes(None, None) == 0
+    assert L.sla_mask(None, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, FAKE, 1 << 40, None) == INVALID
+    assert L.sla_mask(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, FAKE, 1 << 40,
+                      None) == INVALID
+
+
+@pytest.mark.parametrize("kf,pp", [(-0.1, 0.5), (1.5, 0.5), (0.1, -1e-3), (0.1, 1.01),
+                                   (float("nan"), 0.5), (0.1, float("nan"))])
+def test_bad_selection_parameters(kf, pp):
+    L = S.lib()
+    p = prob()
+    sel = S.Select(kf, pp, None, None)
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, 1 << 30, None, FAKE,
+                      1 << 40, None) == INVALID
+    assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          1 << 30, FAKE, 1 << 40, None) == INVALID
+
+
+def test_router_needs_both_matrices():
+    L = S.lib()
+    p = prob()
+    sel = S.Select(0.1, 0.6, FAKE, None)
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, 1 << 30, None, FAKE,
+                      1 << 40, None) == INVALID
+
+
+def test_null_tensors():
+    L = S.lib()
+    p = prob()
+    sel = S.Select(0.1, 0.6, None, None)
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), None, FAKE, FAKE, FAKE, 1 << 30, None, FAKE,
+                      1 << 40, None) == INVALID
+    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.sla_linear_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
+    assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                          1 << 30, FAKE, 1 << 40, None) == INVALID    # alpha
+    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None) == INVALID
+
+
+def test_capacity_and_workspace_checks():
+    L = S.lib()
+    p = prob()
+    sel = S.Select(0.1, 0.6, None, None)
+    cap = L.sla_mask_capacity(ctypes.byref(p))
+    assert cap == 1 * 2 * 16 * 16
+    need = L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(sel))
+    assert need > 0
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, cap - 1, None, FAKE,
+                      need, None) == CAPACITY
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, cap, None, FAKE,
+                      need - 1, None) == WORKSPACE
+    assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, cap, None, None,
+                      need, None) == WORKSPACE
+    assert L.sla_linear_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == WORKSPACE
+    assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          cap - 1, FAKE, need, None) == CAPACITY
+
+
+def test_workspace_grows_with_router():
+    L = S.lib()
+    p = prob(B=2, H=16, N=32760, d=128, bq=128, bk=64, dtype=S.SLA_BF16)
+    a = L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(S.Select(0.03, 0.6, None, None)))
+    b = L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(S.Select(0.03, 0.6, FAKE, FAKE)))
+    assert b > a > 0

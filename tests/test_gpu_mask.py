@@ -1,0 +1,113 @@
+"""GPU parity of sla_mask against the oracle: the CSR must match exactly except
+at blocks that sit on the selection cut (pooled logit within 1e-5 of the
+threshold logit, or cumulative mass within 1e-5 of p); the float64 pooled
+logits must agree to float64 rounding."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_linear_sla_amd as S
+import gen
+from oracle import sla_oracle as O
+from tests import _util as U
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    # name, dtype, N, d, bq, bk, k_frac, p, router
+    ("fp32-ragged-1000", "fp32", 1000, 64, 64, 64, 0.1, 0.6, False),
+    ("fp32-ragged-1001-d128", "fp32", 1001, 128, 128, 64, 0.1, 0.6, False),
+    ("bf16-ragged-1000", "bf16", 1000, 128, 128, 64, 0.05, 0.9, False),
+    ("bf16-ragged-1001-d64", "bf16", 1001, 64, 64, 128, 0.2, 0.5, False),
+    ("bf16-bq128-bk128", "bf16", 4000, 128, 128, 128, 0.1, 0.7, False),
+    ("bf16-router", "bf16", 2000, 128, 128, 64, 0.03, 0.6, True),
+    ("bf16-empty", "bf16", 1500, 128, 128, 64, 0.0, 0.0, False),
+    ("bf16-topk-only", "bf16", 1500, 128, 128, 64, 0.25, 0.0, False),
+    ("bf16-full", "bf16", 700, 128, 128, 64, 1.0, 0.5, False),
+    ("bf16-p1", "bf16", 1500, 128, 128, 64, 0.0, 1.0, False),
+]
+
+
+def _small_inputs(dtype, N, d, bq, bk, k_frac, p, router, seed=7):
+    wl = gen.Workload("adhoc", B=2, H=3, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=k_frac, p=p,
+                      dtype=dtype, router=router, seed=seed)
+    return gen.make(wl)
+
+
+def run_and_check(x, k_frac, p, check_logits=True):
+    wl = x.wl
+    q, k = U.dev(x.Q, x.K)
+    wq, wk = U.dev(x.Wq, x.Wk)
+    rp, ci, logits = S.sla_mask(q, k, wl.bq, wl.bk, k_frac, p, wq, wk, return_logits=True)
+    torch.cuda.synchronize()
+    rp_g, ci_g = U.csr(rp, ci)
+    rp_o, ci_o, meta = U.oracle_mask_per_head(x, k_frac, p)
+    B, H, N, _ = x.Q.shape
+    Nq, Nk = O.n_blocks(N, wl.bq), O.n_blocks(N, wl.bk)
+    U.check_csr_structure(rp_g, ci_g, B * H * Nq, Nk)
+    if check_logits:
+        Sg = logits.cpu().numpy().reshape(meta["S"].shape)
+        err = np.max(np.abs(Sg - meta["S"]) / np.maximum(1.0, np.abs(meta["S"])))
+        assert err < 1e-10, f"pooled logits differ by {err}"
+    bad, excused, rows = U.mask_mismatches(rp_g, ci_g, rp_o, ci_o, meta, p)
+    assert not bad, f"{len(bad)} unexcused mask differences, e.g. {bad[:5]}"
+    return rp_g, ci_g, excused, rows
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_mask_small(case):
+    name, dtype, N, d, bq, bk, k_frac, p, router = case
+    print(f"[mask] {name}", flush=True)
+    x = _small_inputs(dtype, N, d, bq, bk, k_frac, p, router)
+    rp, ci, excused, rows = run_and_check(x, k_frac, p)
+    Nk = O.n_blocks(N, bk)
+    R = len(rp) - 1
+    if k_frac == 0 and p == 0:
+        assert rp[-1] == 0
+    if k_frac == 1:
+        assert rp[-1] == R * Nk
+
+
+def test_mask_tiny_workload():
+    wl = gen.WORKLOADS["tiny-fp32-N1024"]
+    print(f"[mask] {wl.name}", flush=True)
+    x = gen.make(wl)
+    rp, ci, excused, rows = run_and_check(x, wl.k_frac, wl.p)
+    assert rows == 0  # nothing near the cut at this size
+
+
+@pytest.mark.parametrize("name", ["video480p-sparse-N32760", "video480p-sla2-N32760"])
+def test_mask_480p(name):
+    wl = gen.WORKLOADS[name]
+    print(f"[mask] {name}", flush=True)
+    x = gen.make(wl)
+    rp, ci, excused, rows = run_and_check(x, wl.k_frac, wl.p)
+    sparsity = 1 - rp[-1] / float(wl.B * wl.H * wl.Nq * wl.Nk)
+    print(f"  sparsity {sparsity:.4f}, differing rows {rows}, excused blocks {excused}")
+
+
+@pytest.mark.parametrize("tau,p", [(0.25, 0.9), (1.0, 0.6), (4.0, 0.3)])
+def test_mask_router_sweep(tau, p):
+    wl = gen.WORKLOADS["video480p-router-N32760"].with_(tau=tau, p=p)
+    print(f"[mask] router tau={tau} p={p}", flush=True)
+    x = gen.make(wl)
+    rp, ci, excused, rows = run_and_check(x, wl.k_frac, p)
+    print(f"  sparsity {1 - rp[-1] / float(wl.B * wl.H * wl.Nq * wl.Nk):.4f}, excused {excused}")
+
+
+def test_mask_720p():
+    wl = gen.WORKLOADS["video720p-sla2-N75600"]
+    print(f"[mask] {wl.name}", flush=True)
+    x = gen.make(wl)
+    rp, ci, excused, rows = run_and_check(x, wl.k_frac, wl.p, check_logits=True)
+    print(f"  sparsity {1 - rp[-1] / float(wl.B * wl.H * wl.Nq * wl.Nk):.4f}, excused {excused}")
+
+
+def test_mask_deterministic():
+    wl = gen.WORKLOADS["video480p-sla2-N32760"]
+    x = gen.make(wl, heads=2)
+    q, k = U.dev(x.Q, x.K)
+    a = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    b = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    n = int(a[0][-1])
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1][:n], b[1][:n])
