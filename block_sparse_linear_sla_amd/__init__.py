@@ -24,7 +24,8 @@ SLA_F32, SLA_BF16 = 0, 1
 STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
           -3: "SLA_ERR_WORKSPACE", -4: "SLA_ERR_CAPACITY", -5: "SLA_ERR_HIP"}
 EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_sparse_fwd",
-           "sla_linear_fwd", "sla_attn_fwd", "sla_dense_fwd", "sla_status_string")
+           "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
+           "sla_dense_fwd", "sla_status_string")
 
 
 class SlaError(RuntimeError):
@@ -61,14 +62,17 @@ def lib() -> ctypes.CDLL:
         L.sla_mask_capacity.argtypes = [P]
         L.sla_mask_capacity.restype = ctypes.c_int64
         L.sla_mask.argtypes = [P, S, vp, vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
-        L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_linear_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_attn_fwd.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
                                    ctypes.c_size_t, vp]
-        L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp]
+        L.sla_kv_prepare.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_fused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
-        for fn in ("sla_mask", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd", "sla_dense_fwd"):
+        for fn in ("sla_mask", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
+                   "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -152,12 +156,14 @@ def sla_mask(q, k, bq: int, bk: int, k_frac: float, p: float, wq=None, wk=None,
     return (rp, ci, logits) if return_logits else (rp, ci)
 
 
-def sla_sparse_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None):
+def sla_sparse_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None, ws=None):
     _need(q, k, v, like=q)
     prob = problem(q, bq, bk)
     o = out if out is not None else torch.empty_like(q)
+    w = ws if ws is not None else workspace(prob, None, q.device)
     _check("sla_sparse_fwd", lib().sla_sparse_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
-                                                  _ptr(row_ptr), _ptr(col_idx), _ptr(o), _stream()))
+                                                  _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(w),
+                                                  w.numel(), _stream()))
     return o
 
 
@@ -193,10 +199,31 @@ def sla_attn_fwd(q, k, v, alpha, bq: int, bk: int, k_frac: float, p: float, wq=N
     return o, rp, ci
 
 
-def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None):
+def sla_kv_prepare(k, v, bq: int, bk: int, ws: torch.Tensor, alpha=None):
+    """One pass over K and V leaving in ws what sla_fused_fwd reads."""
+    _need(k, v, like=k)
+    prob = problem(k, bq, bk)
+    _check("sla_kv_prepare", lib().sla_kv_prepare(ctypes.byref(prob), _ptr(k), _ptr(v), _ptr(alpha),
+                                                  _ptr(ws), ws.numel(), _stream()))
+
+
+def sla_fused_fwd(q, k, v, alpha, bq: int, bk: int, row_ptr, col_idx, ws: torch.Tensor, out=None):
+    """alpha-mixed sparse + linear output over a given mask, reading the totals
+    that sla_kv_prepare left in ws."""
     _need(q, k, v, like=q)
     prob = problem(q, bq, bk)
     o = out if out is not None else torch.empty_like(q)
+    _check("sla_fused_fwd", lib().sla_fused_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(alpha), _ptr(row_ptr), _ptr(col_idx), _ptr(o),
+                                                _ptr(ws), ws.numel(), _stream()))
+    return o
+
+
+def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None, ws=None):
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    o = out if out is not None else torch.empty_like(q)
+    w = ws if ws is not None else workspace(prob, None, q.device)
     _check("sla_dense_fwd", lib().sla_dense_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                                _stream()))
+                                                _ptr(w), w.numel(), _stream()))
     return o

@@ -32,7 +32,7 @@ def flags() -> list:
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
             # packed fp32 vector ops stay off: the compiler must not emit them
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-Wno-unused-result", "-I", INCLUDE, "-I", CSRC]
+            "-Wno-unused-result", "-Wno-pass-failed", "-I", INCLUDE, "-I", CSRC]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -6,6 +6,7 @@
 #include "sla.h"
 #include "sla_internal.h"
 
+
 namespace sla {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -19,23 +20,31 @@ WsLayout ws_layout(const Shape& s, bool router) {
     off = align256(off + bytes);
     return o;
   };
+  // Linear summaries first, so their offsets do not depend on the router.
+  // The preparation pass runs one workgroup per chunk of key blocks of a head;
+  // chunks are sized so the grid is a single round at two workgroups per CU
+  // (about 512), which keeps the per-chunk partials few.
+  int nch = (int)(512 / BH);
+  if (nch < 1) nch = 1;
+  if (nch > s.Nk) nch = s.Nk;
+  const int cb = (s.Nk + nch - 1) / nch;
+  L.chunk_blocks = cb;
+  L.nchunk = (s.Nk + cb - 1) / cb;
+  const size_t per = (size_t)s.d * s.d + s.d;
+  L.htot = take(BH * per * sizeof(float));
+  L.hpart = take(BH * L.nchunk * per * sizeof(float));
   L.qbar = take(BH * s.Nq * s.d * sizeof(double));
   L.kbar = take(BH * s.Nk * s.d * sizeof(double));
   L.qhat = router ? take(BH * s.Nq * s.d * sizeof(double)) : 0;
   L.khat = router ? take(BH * s.Nk * s.d * sizeof(double)) : 0;
   L.S = take(BH * s.Nq * s.Nk * sizeof(double));
+  const bool bf = s.dtype == SLA_BF16;
+  const size_t npad = (size_t)s.Nk * s.bk;
+  L.vt = bf ? take(BH * s.d * npad * 2) : 0;
+  L.pk = bf ? take(BH * s.d * npad * 2) : 0;
+  L.zblk = bf ? take(BH * s.Nk * s.d * sizeof(float)) : 0;
   L.counts = take((size_t)s.R() * sizeof(int32_t));
   L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
-  // Linear summary partials: chunks of key blocks sized so that the summary
-  // pass has on the order of a thousand workgroups.
-  int cb = (int)((BH * s.Nk + 1023) / 1024);
-  if (cb < 4) cb = 4;
-  if (cb > s.Nk) cb = s.Nk;
-  L.chunk_blocks = cb;
-  L.nchunk = (s.Nk + cb - 1) / cb;
-  const size_t per = (size_t)s.d * s.d + s.d;
-  L.hpart = take(BH * L.nchunk * per * sizeof(float));
-  L.htot = take(BH * per * sizeof(float));
   L.total = off;
   return L;
 }
@@ -80,17 +89,18 @@ int check_select(const sla_select* sel, int* k, const Shape& s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_HIP; }
 
-hipError_t run_summary(const Shape& s, const void* K, const void* V, const float* alpha, char* ws,
-                       const WsLayout& L, hipStream_t st) {
-  return s.dtype == SLA_BF16 ? sla::launch_summary_bf16(s, K, V, alpha, ws, L, st)
-                             : sla::launch_summary_f32(s, K, V, alpha, ws, L, st);
+hipError_t run_prep(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
+                    char* ws, const WsLayout& L, hipStream_t st) {
+  if (s.dtype == SLA_BF16) return sla::launch_prep_bf16(s, lin, K, V, alpha, ws, L, st);
+  return lin ? sla::launch_summary_f32(s, K, V, alpha, ws, L, st) : hipSuccess;
 }
 
 hipError_t run_attn(const Shape& s, Mode m, const void* Q, const void* K, const void* V,
-                    const int32_t* rp, const int32_t* ci, const float* alpha, const float* htot,
-                    void* O, hipStream_t st) {
-  return s.dtype == SLA_BF16 ? sla::launch_attn_bf16(s, m, Q, K, V, rp, ci, alpha, htot, O, st)
-                             : sla::launch_attn_f32(s, m, Q, K, V, rp, ci, alpha, htot, O, st);
+                    const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
+                    const WsLayout& L, void* O, hipStream_t st) {
+  if (s.dtype == SLA_BF16) return sla::launch_attn_bf16(s, m, Q, K, rp, ci, alpha, ws, L, O, st);
+  return sla::launch_attn_f32(s, m, Q, K, V, rp, ci, alpha,
+                              reinterpret_cast<const float*>(ws + L.htot), O, st);
 }
 
 }  // namespace
@@ -128,13 +138,18 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
 }
 
 int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
-                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream) {
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* ws,
+                   size_t ws_bytes, void* stream) {
   Shape s;
   int rc = check_problem(prob, &s);
   if (rc != SLA_OK) return rc;
   if (!Q || !K || !V || !row_ptr || !col_idx || !O_s) return SLA_ERR_INVALID_ARG;
-  return hip_status(run_attn(s, sla::MODE_SPARSE, Q, K, V, row_ptr, col_idx, nullptr, nullptr, O_s,
-                             static_cast<hipStream_t>(stream)));
+  const WsLayout L = sla::ws_layout(s, false);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (run_prep(s, false, K, V, nullptr, w, L, st) != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(run_attn(s, sla::MODE_SPARSE, Q, K, V, row_ptr, col_idx, nullptr, w, L, O_s, st));
 }
 
 int sla_linear_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
@@ -148,10 +163,8 @@ int sla_linear_fwd(const sla_problem* prob, const void* Q, const void* K, const 
   if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = run_summary(s, K, V, nullptr, w, L, st);
-  if (e != hipSuccess) return SLA_ERR_HIP;
-  return hip_status(run_attn(s, sla::MODE_LINEAR, Q, K, V, row_ptr, col_idx, nullptr,
-                             reinterpret_cast<const float*>(w + L.htot), O_l, st));
+  if (run_prep(s, true, K, V, nullptr, w, L, st) != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(run_attn(s, sla::MODE_LINEAR, Q, K, V, row_ptr, col_idx, nullptr, w, L, O_l, st));
 }
 
 int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
@@ -168,23 +181,50 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
   if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  hipError_t e = sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx,
-                                  nullptr, w, L, st);
-  if (e != hipSuccess) return SLA_ERR_HIP;
-  e = run_summary(s, K, V, alpha, w, L, st);
-  if (e != hipSuccess) return SLA_ERR_HIP;
+  if (sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx, nullptr, w, L,
+                       st) != hipSuccess)
+    return SLA_ERR_HIP;
+  if (run_prep(s, true, K, V, alpha, w, L, st) != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(run_attn(s, sla::MODE_FUSED, Q, K, V, row_ptr, col_idx, alpha, w, L, O, st));
+}
+
+int sla_kv_prepare(const sla_problem* prob, const void* K, const void* V, const float* alpha,
+                   void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (!K || !V) return SLA_ERR_INVALID_ARG;
+  const WsLayout L = sla::ws_layout(s, false);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(run_prep(s, true, K, V, alpha, static_cast<char*>(ws), L,
+                             static_cast<hipStream_t>(stream)));
+}
+
+int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                  const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                  const void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (!Q || !K || !V || !alpha || !row_ptr || !col_idx || !O) return SLA_ERR_INVALID_ARG;
+  const WsLayout L = sla::ws_layout(s, false);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
   return hip_status(run_attn(s, sla::MODE_FUSED, Q, K, V, row_ptr, col_idx, alpha,
-                             reinterpret_cast<const float*>(w + L.htot), O, st));
+                             static_cast<const char*>(ws), L, O, static_cast<hipStream_t>(stream)));
 }
 
 int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
-                  void* stream) {
+                  void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   int rc = check_problem(prob, &s);
   if (rc != SLA_OK) return rc;
   if (!Q || !K || !V || !O) return SLA_ERR_INVALID_ARG;
-  return hip_status(run_attn(s, sla::MODE_DENSE, Q, K, V, nullptr, nullptr, nullptr, nullptr, O,
-                             static_cast<hipStream_t>(stream)));
+  const WsLayout L = sla::ws_layout(s, false);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (run_prep(s, false, K, V, nullptr, w, L, st) != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(run_attn(s, sla::MODE_DENSE, Q, K, V, nullptr, nullptr, nullptr, w, L, O, st));
 }
 
 const char* sla_status_string(int status) {

@@ -25,6 +25,8 @@ struct WsLayout {
   size_t bits;         // uint32 [R * words]
   size_t hpart;        // linear summary partials, float [B*H*nchunk*(d*d + d)]
   size_t htot;         // linear summaries, float [B*H*(d*d + d)]
+  size_t vt, pk;       // bf16 path: V^T and phi(K)^T, bf16 [B*H*d*(Nk*bk)]
+  size_t zblk;         // bf16 path: per-key-block sums of phi(K), float [B*H*Nk*d]
   size_t total;
   int nchunk;          // key-block chunks per head in the summary pass
   int chunk_blocks;    // key blocks per chunk
@@ -45,19 +47,20 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
                        const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
                        double* logits_out, char* ws, const WsLayout& L, hipStream_t st);
 
-// attn_bf16.hip / attn_f32.hip: linear summaries (H = sum_u phi(k_u)^T v_u,
-// z = sum_u phi(k_u) per head) into the workspace; heads whose alpha is
-// exactly 1 are skipped when alpha is given.
-hipError_t launch_summary_bf16(const Shape& s, const void* K, const void* V, const float* alpha,
-                               char* ws, const WsLayout& L, hipStream_t st);
+// attn_bf16.hip: the K/V preparation pass (V^T always; with lin also phi(K)^T,
+// per-block phi(K) sums and the per-head linear totals; heads whose alpha is
+// exactly 1 skip the linear part when alpha is given) and the attention kernel.
+hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
+                            char* ws, const WsLayout& L, hipStream_t st);
+hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K,
+                            const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,
+                            const char* ws, const WsLayout& L, void* O, hipStream_t st);
+hipError_t launch_summary_reduce(const float* hpart, const float* alpha, int H, long long BH,
+                                 int nchunk, int per, float* htot, hipStream_t st);
+
+// attn_f32.hip: linear totals and attention for float32 inputs.
 hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,
                               char* ws, const WsLayout& L, hipStream_t st);
-
-// Attention over the mask.  htot (float [B*H*(d*d + d)]) is needed for the
-// linear and fused modes; alpha for the fused mode.
-hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
-                            const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,
-                            const float* htot, void* O, hipStream_t st);
 hipError_t launch_attn_f32(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
                            const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,
                            const float* htot, void* O, hipStream_t st);

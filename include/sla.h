@@ -105,9 +105,11 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
 
 /* Sparse branch alone (SLA2 write-up §一): O_s[t] = softmax over the keys of the
  * blocks listed in row (b, h, t / bq) of the mask, of q_t . k / sqrt(d), times V.
- * Rows with no selected block are written as 0.  Output O_s [B, H, N, d]. */
+ * Rows with no selected block are written as 0.  Output O_s [B, H, N, d].
+ * Needs the workspace (the bf16 path stages a transposed copy of V there). */
 int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
-                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s,
+                   void* ws, size_t ws_bytes, void* stream);
 
 /* Linear branch alone (SLA2 write-up §一): O_l[t] = sum_u (phi(q_t).phi(k_u)) v_u /
  * sum_u phi(q_t).phi(k_u) over the keys u of the blocks NOT listed in the row;
@@ -126,10 +128,31 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
                  const void* V, const float* alpha, void* O, int32_t* row_ptr,
                  int32_t* col_idx, int64_t capacity, void* ws, size_t ws_bytes, void* stream);
 
+/* The two stages that follow the mask in sla_attn_fwd, for callers that time
+ * or schedule them separately (sla_attn_fwd == sla_mask, then these two).
+ *
+ * sla_kv_prepare: one pass over K and V that leaves in the workspace what the
+ * fused stage reads: the per-head linear-attention totals H = sum_u phi(k_u)^T
+ * v_u ([d, d]) and z = sum_u phi(k_u) ([d]) over every key (float32) and, for
+ * bf16, transposed copies of V and phi(K) plus per-key-block sums of phi(K).
+ * alpha (DEVICE fp32 [H]) may be NULL; heads whose alpha is exactly 1 skip
+ * the linear part when it is given.
+ *
+ * sla_fused_fwd: O = alpha_h * O_s + (1 - alpha_h) * O_l over the given mask,
+ * with O_l = phi(q) (H - G) / phi(q) (z - g), where G, g are the same sums
+ * over the listed blocks only (SLA2 write-up §一, §二).  It reads what
+ * sla_kv_prepare left in the SAME workspace for the same K, V and alpha;
+ * calling it without that is undefined. */
+int sla_kv_prepare(const sla_problem* prob, const void* K, const void* V, const float* alpha,
+                   void* ws, size_t ws_bytes, void* stream);
+int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                  const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                  const void* ws, size_t ws_bytes, void* stream);
+
 /* Dense softmax(Q K^T / sqrt(d)) V over every key, the comparator the sparse
- * path is measured against.  Output O [B, H, N, d]. */
+ * path is measured against.  Output O [B, H, N, d].  Needs the workspace. */
 int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
-                  void* stream);
+                  void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* sla_status_string(int status);
