@@ -68,6 +68,17 @@ __device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8), each
+// XCD with its own L2.  Map them so that every XCD walks a contiguous range of
+// mask rows: adjacent query blocks of a head select largely the same key
+// blocks, so their K / V^T tiles are then shared in one L2.
+__device__ __forceinline__ long long xcd_row(long long b, long long R) {
+  constexpr long long NX = 8;
+  const long long q = R / NX, r = R % NX;
+  const long long x = b % NX, local = b / NX;
+  return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
 // Position of key offset o inside its 16-key group in the transposed tiles.
 __device__ __forceinline__ int kperm(int o) { return (o & ~12) | ((o & 4) << 1) | ((o & 8) >> 1); }
 
@@ -243,55 +254,163 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------ attention
-template <int D, int BQ, int BK, int MODE>
-struct Cfg {
-  static constexpr int NW = BQ / 32;                 // wavefronts
-  static constexpr int NT = NW * 64;                 // threads
-  static constexpr bool LINM = MODE == MODE_FUSED || MODE == MODE_LINEAR;
-  static constexpr int NSTAGE = LINM ? 1 : 2;        // LDS buffers of the loop tiles
-  static constexpr int CHK = D / 8;                  // 16-byte chunks per K-tile row
-  static constexpr int CHV = BK / 8;                 // 16-byte chunks per transposed-tile row
-  static constexpr int KT_BYTES = BK * D * 2;
-  static constexpr int VT_BYTES = D * BK * 2;
-  static constexpr int STAGE_BYTES = KT_BYTES + VT_BYTES + (LINM ? VT_BYTES : 0);
-  static constexpr int LOOP_BYTES = STAGE_BYTES;       // stage 0; stage 1 has its own array
-  static constexpr int HU_BYTES = LINM ? 2 * D * D * 2 : 0;
-  static constexpr int MAIN_BYTES = LOOP_BYTES > HU_BYTES ? LOOP_BYTES : HU_BYTES;
-  static constexpr int ZU_OFF = MAIN_BYTES;
-  static constexpr int SMEM = ZU_OFF + (LINM ? D * 4 : 0);
-  static constexpr int TT = (D / 32) * (D / 32);     // 32x32 tiles of G
-  static constexpr int TPW = (TT + NW - 1) / NW;     // G tiles per wavefront
-  // direct-load instructions per wavefront per tile (64 chunks of 16 B each)
-  static constexpr int KLOADS = (BK * CHK) / (64 * NW);
-  static constexpr int VLOADS = (D * CHV) / (64 * NW);
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
 };
 
+// LDS tiles are stored as "planes": every 16-element k-slice that an MFMA
+// operand read takes is a plane of 32 bytes per row (two 16-byte halves), and
+// row r keeps its halves swapped when bit 3 of r is set.  The 16 rows that a
+// 16-lane group reads then sit in 16 distinct 16-byte bank groups, and every
+// operand read is one per-lane base address plus a compile-time offset.
+template <int D, int BK>
+struct Tiles {
+  static constexpr int KPB = BK * 32;        // bytes of one K plane (16 d of BK keys)
+  static constexpr int VPB = D * 32;         // bytes of one V^T / phi(K)^T plane (16 keys)
+  static constexpr int KT_BYTES = BK * D * 2;
+  static constexpr int VT_BYTES = D * BK * 2;
+  static constexpr int HPB = D * 32;         // bytes of one H_u^T plane (16 d_k)
+};
+
+__device__ __forceinline__ int lane_base(int lane) {
+  const int l32 = lane & 31, hi = lane >> 5;
+  return l32 * 32 + 16 * (hi ^ ((l32 >> 3) & 1));
+}
+
+__device__ __forceinline__ uint4 rd16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Direct loads of key block j into the LDS stage at sb by wavefront w of NWL.
+// Load slot u fills the 1 KB at sb + 1024 u: 32 rows x 32 bytes of one plane;
+// lane l brings row l/2, stored half l%2.  K rows past N are clamped (their
+// scores are masked); V^T / phi(K)^T are zero past N.
+template <int D, int BK, int NWL>
+__device__ __forceinline__ void load_tiles(const uint16_t* Kb, const uint16_t* Vtb, const uint16_t* Pkb,
+                                           int j, int N, size_t npad, bool doK, bool doP, char* sb,
+                                           int w, int lane) {
+  using T = Tiles<D, BK>;
+  const int lrow = lane >> 1, lpos = lane & 1;
+  if (doK) {
+#pragma unroll
+    for (int ii = 0; ii < T::KT_BYTES / 1024 / NWL; ++ii) {
+      const int u = w + NWL * ii;
+      const int t = u / (T::KPB / 1024), r = (u % (T::KPB / 1024)) * 32 + lrow;
+      const int hh = lpos ^ ((r >> 3) & 1);
+      const int key = min(j * BK + r, N - 1);
+      g2lds16(Kb + (size_t)key * D + 16 * t + 8 * hh, sb + 1024 * u);
+    }
+  }
+#pragma unroll
+  for (int ii = 0; ii < T::VT_BYTES / 1024 / NWL; ++ii) {
+    const int u = w + NWL * ii;
+    const int pl = u / (T::VPB / 1024), r = (u % (T::VPB / 1024)) * 32 + lrow;
+    const int hh = lpos ^ ((r >> 3) & 1);
+    const size_t go = (size_t)r * npad + (size_t)j * BK + 16 * pl + 8 * hh;
+    g2lds16(Vtb + go, sb + T::KT_BYTES + 1024 * u);
+    if (doP) g2lds16(Pkb + go, sb + T::KT_BYTES + T::VT_BYTES + 1024 * u);
+  }
+}
+
+// max of v over lanes l and l^32 (v_permlane32_swap exchanges the two halves;
+// taking the max with the own value makes the result independent of which
+// output holds which half)
+__device__ __forceinline__ float pair_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
+// Online-softmax attention of one wavefront's 32 queries over one key block,
+// 32 keys at a time: S^T = K Q^T, running max / sum, O^T += V^T P^T.
+template <int D, int BK, bool MASK>
+__device__ __forceinline__ void attend_block(const char* Ks, const char* Vt, const bf16x8 (&qf)[D / 16],
+                                             f32x16 (&acc_o)[D / 32], float& m_run, float& l_run,
+                                             int lb, int hi, int key0, int N, float scale_log2) {
+  using T = Tiles<D, BK>;
+#pragma unroll
+  for (int kt = 0; kt < BK / 32; ++kt) {
+    f32x16 sa = f32x16{};
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) sa = mfma(as_bf16x8(rd16(Ks + t * T::KPB + kt * 1024 + lb)), qf[t], sa);
+    if (MASK) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * hi + (i & 3);
+        if (key >= N) sa[i] = -INFINITY;
+      }
+    }
+    float mx = sa[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sa[i]);
+    mx = pair_max(mx);
+    // Conditional rescale: the running max moves only when some lane's max
+    // exceeds it by more than 2^8 in exp2 units, so P <= 2^8 and the O / l
+    // rescale is skipped for most tiles.
+    if (__ballot((mx - m_run) * scale_log2 > 8.f)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
+      l_run *= corr;
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
+      m_run = m_new;
+    }
+    const float mneg = -m_run * scale_log2;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sa[i] = __builtin_amdgcn_exp2f(fmaf(sa[i], scale_log2, mneg));
+      psum += sa[i];
+    }
+    l_run += psum;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 pb;
+      pb.x = pk_bf16(sa[8 * s + 0], sa[8 * s + 1]);
+      pb.y = pk_bf16(sa[8 * s + 2], sa[8 * s + 3]);
+      pb.z = pk_bf16(sa[8 * s + 4], sa[8 * s + 5]);
+      pb.w = pk_bf16(sa[8 * s + 6], sa[8 * s + 7]);
+      const bf16x8 bp = as_bf16x8(pb);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc_o[dt] = mfma(as_bf16x8(rd16(Vt + (2 * kt + s) * T::VPB + dt * 1024 + lb)), bp, acc_o[dt]);
+    }
+  }
+}
+
+// Q fragments of 32 query rows (B operand of S^T = K Q^T), zero past N.
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, int N, int hi,
+                                       bf16x8 (&qf)[D / 16]) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (q < N) v = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + q) * D + 16 * t + 8 * hi);
+    qf[t] = as_bf16x8(v);
+  }
+}
+
+// Sparse (CSR row) or dense (every key block) softmax attention; BQ/32
+// wavefronts of 32 queries, tiles double-buffered.
 template <int D, int BQ, int BK, int MODE>
 __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
-    const uint16_t* __restrict__ pk_g, const float* __restrict__ zblk, const int* __restrict__ row_ptr,
-    const int* __restrict__ col_idx, const float* __restrict__ alpha, const float* __restrict__ htot,
-    uint16_t* __restrict__ O, int H, int N, int Nq, int Nk, float scale_log2) {
-  using C = Cfg<D, BQ, BK, MODE>;
-  static_assert(C::KLOADS >= 1 && C::VLOADS >= 1, "tile too small for the workgroup");
-  static_assert(C::KLOADS * 64 * C::NW == BK * C::CHK && C::VLOADS * 64 * C::NW == D * C::CHV,
-                "tiles must split evenly over the wavefronts");
-  // Stage 0 (and the epilogue buffers) and stage 1 are distinct LDS arrays so
-  // that the compiler can tell the prefetch into one from reads of the other.
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
-  __shared__ __attribute__((aligned(16))) char smem1[C::NSTAGE == 2 ? C::STAGE_BYTES : 16];
-  uint16_t* HuHi = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* HuLo = reinterpret_cast<uint16_t*>(smem + D * D * 2);
-  float* zu = reinterpret_cast<float*>(smem + C::ZU_OFF);
+    const int* __restrict__ row_ptr, const int* __restrict__ col_idx, uint16_t* __restrict__ O, int N,
+    int Nq, int Nk, float scale_log2) {
+  using T = Tiles<D, BK>;
+  constexpr int NW = BQ / 32;
+  constexpr int STAGE = T::KT_BYTES + T::VT_BYTES;
+  static_assert(T::KT_BYTES % (1024 * NW) == 0 && T::VT_BYTES % (1024 * NW) == 0, "tile split");
+  // Two distinct LDS arrays: the compiler can then tell the prefetch into one
+  // stage from the operand reads of the other.
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
-  const long long row = blockIdx.x;
+  const int lb = lane_base(lane);
+  const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
   const long long bh = row / Nq;
   const int qi = (int)(row % Nq);
-  const int h = (int)(bh % H);
   const size_t npad = (size_t)Nk * BK;
-
   int nsel, base = 0;
   if (MODE == MODE_DENSE) {
     nsel = Nk;
@@ -299,245 +418,224 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
     base = row_ptr[row];
     nsel = row_ptr[row + 1] - base;
   }
-  float ws_ = 0.f, wl_ = 0.f;
+  const uint16_t* Kb = K + (size_t)bh * N * D;
+  const uint16_t* Vtb = vt_g + (size_t)bh * D * npad;
+  const int q = qi * BQ + 32 * w + l32;
+  bf16x8 qf[D / 16];
+  load_q<D>(Q, bh, q, N, hi, qf);
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto blk = [&](int b) { return (MODE == MODE_DENSE) ? b : col_idx[base + b]; };
+  auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
+    const int j = blk(b);
+    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of block b have landed
+    __syncthreads();                // ... and every wavefront's; block b-1 consumed
+    if (b + 1 < nsel) load_tiles<D, BK, NW>(Kb, Vtb, nullptr, blk(b + 1), N, npad, true, false, nxt, w, lane);
+    if ((j + 1) * BK > N)
+      attend_block<D, BK, true>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N, scale_log2);
+    else
+      attend_block<D, BK, false>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N, scale_log2);
+  };
+  if (nsel > 0) load_tiles<D, BK, NW>(Kb, Vtb, nullptr, blk(0), N, npad, true, false, st0, w, lane);
+  for (int b = 0; b < nsel; b += 2) {
+    step(b, st0, st1);
+    if (b + 1 < nsel) step(b + 1, st1, st0);
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
+  if (q < N) {
+    const size_t orow = ((size_t)bh * N + q) * D;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        uint2 wv;
+        wv.x = pk_bf16(acc_o[mt][4 * i4 + 0] * inv_l, acc_o[mt][4 * i4 + 1] * inv_l);
+        wv.y = pk_bf16(acc_o[mt][4 * i4 + 2] * inv_l, acc_o[mt][4 * i4 + 3] * inv_l);
+        *reinterpret_cast<uint2*>(O + orow + 32 * mt + 8 * i4 + 4 * hi) = wv;
+      }
+  }
+}
+
+// Fused sparse + linear (+ alpha mix) over the CSR row.  2*BQ/32 wavefronts:
+// wavefronts [0, NA) run the softmax attention of 32 queries each, wavefronts
+// [NA, 2 NA) accumulate G = sum phi(K_j)^T V_j over the row's blocks - one of
+// each per SIMD, so G's matrix ops overlap the softmax's vector work.  After
+// the loop the G wavefronts store H_u = H - G (hi + lo bf16) in LDS and the
+// attention wavefronts apply it to phi(Q) and mix the branches.
+template <int D, int BQ, int BK, int MODE>
+__global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
+    const uint16_t* __restrict__ pk_g, const float* __restrict__ zblk, const int* __restrict__ row_ptr,
+    const int* __restrict__ col_idx, const float* __restrict__ alpha, const float* __restrict__ htot,
+    uint16_t* __restrict__ O, int H, int N, int Nq, int Nk, float scale_log2) {
+  using T = Tiles<D, BK>;
+  constexpr int NA = BQ / 32;                    // attention wavefronts
+  constexpr int NWT = 2 * NA;                    // all wavefronts
+  constexpr int STAGE = T::KT_BYTES + 2 * T::VT_BYTES;
+  constexpr int HU = 2 * D * D * 2;
+  constexpr int S0 = STAGE > HU ? STAGE : HU;
+  constexpr bool TWO = S0 + STAGE + D * 4 <= 160 * 1024;   // double-buffer when LDS allows
+  constexpr int TT = (D / 32) * (D / 32);
+  constexpr int TPW = (TT + NA - 1) / NA;       // G tiles per G wavefront
+  static_assert(T::KT_BYTES % (1024 * NWT) == 0 && T::VT_BYTES % (1024 * NWT) == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char st0[S0];
+  __shared__ __attribute__((aligned(16))) char st1[TWO ? STAGE : 16];
+  __shared__ float zu[D];
+  char* HuHi = st0;
+  char* HuLo = st0 + D * D * 2;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const bool attn_wave = w < NA;
+  const int wr = attn_wave ? w : w - NA;        // index within the role
+  const int lb = lane_base(lane);
+  const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
+  const long long bh = row / Nq;
+  const int qi = (int)(row % Nq);
+  const int h = (int)(bh % H);
+  const size_t npad = (size_t)Nk * BK;
+  const int base = row_ptr[row];
+  const int nsel = row_ptr[row + 1] - base;
+  float ws_, wl_;
   if (MODE == MODE_FUSED) {
-    const float a = alpha[h];
-    ws_ = a;
-    wl_ = 1.f - a;
-  } else if (MODE == MODE_LINEAR) {
-    wl_ = 1.f;
+    ws_ = alpha[h];
+    wl_ = 1.f - ws_;
   } else {
-    ws_ = 1.f;
+    ws_ = 0.f;
+    wl_ = 1.f;
   }
   const bool do_s = ws_ != 0.f;
-  const bool lin = C::LINM && (wl_ != 0.f) && (nsel < Nk);
+  const bool lin = (wl_ != 0.f) && (nsel < Nk);
   const int nblk = (do_s || lin) ? nsel : 0;
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vtb = vt_g + (size_t)bh * D * npad;
-  const uint16_t* Pkb = C::LINM ? pk_g + (size_t)bh * D * npad : nullptr;
+  const uint16_t* Pkb = pk_g + (size_t)bh * D * npad;
+  const float* Hh = htot + (size_t)bh * (D * D + D);
 
-  // Issue the direct loads of key block j into the LDS stage at sb.
-  auto load_block = [&](int j, char* sb) {
-    if (do_s) {
-#pragma unroll
-      for (int ii = 0; ii < C::KLOADS; ++ii) {
-        const int u = w + C::NW * ii;               // 1 KB slot of the tile
-        const int g = 64 * u + lane;                // 16-byte chunk slot
-        const int r = g / C::CHK, pc = g % C::CHK;
-        const int lc = pc ^ (r % C::CHK);
-        const int key = min(j * BK + r, N - 1);     // rows past N are masked later
-        g2lds16(Kb + (size_t)key * D + 8 * lc, sb + 1024 * u);
+  // The block loop; both roles run it with the same loads and barriers, each
+  // with its own per-block work, so neither role keeps the other's state live.
+  auto run_loop = [&](auto&& work) __attribute__((always_inline)) {
+    auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (TWO && b + 1 < nblk)
+        load_tiles<D, BK, NWT>(Kb, Vtb, Pkb, col_idx[base + b + 1], N, npad, do_s, lin, nxt, w, lane);
+      work(col_idx[base + b], cur);
+      if (!TWO) {
+        __syncthreads();  // the single stage is consumed before it is refilled
+        if (b + 1 < nblk)
+          load_tiles<D, BK, NWT>(Kb, Vtb, Pkb, col_idx[base + b + 1], N, npad, do_s, lin, cur, w, lane);
       }
+    };
+    if (nblk > 0) load_tiles<D, BK, NWT>(Kb, Vtb, Pkb, col_idx[base], N, npad, do_s, lin, st0, w, lane);
+    if (TWO) {
+      for (int b = 0; b < nblk; b += 2) {
+        step(b, st0, st1);
+        if (b + 1 < nblk) step(b + 1, st1, st0);
+      }
+    } else {
+      for (int b = 0; b < nblk; ++b) step(b, st0, st0);
     }
-#pragma unroll
-    for (int ii = 0; ii < C::VLOADS; ++ii) {
-      const int u = w + C::NW * ii;
-      const int g = 64 * u + lane;
-      const int r = g / C::CHV, pc = g % C::CHV;
-      const int lc = pc ^ (r % C::CHV);
-      const size_t go = (size_t)r * npad + (size_t)j * BK + 8 * lc;
-      g2lds16(Vtb + go, sb + C::KT_BYTES + 1024 * u);
-      if (C::LINM && lin) g2lds16(Pkb + go, sb + C::KT_BYTES + C::VT_BYTES + 1024 * u);
-    }
+    __syncthreads();  // every wavefront is done with the loop tiles
   };
 
-  // Q fragments of this wavefront's 32 query rows
-  const int q = qi * BQ + 32 * w + l32;
-  bf16x8 qf[D / 16];
+  if (!attn_wave) {
+    // ---- G wavefronts: G = sum over listed blocks of phi(K_j)^T V_j
+    f32x16 acc_g[TPW];
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (q < N) v = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + q) * D + 16 * t + 8 * hi);
-    qf[t] = as_bf16x8(v);
-  }
-
-  f32x16 acc_o[D / 32];
-  f32x16 acc_g[C::LINM ? C::TPW : 1];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
-#pragma unroll
-  for (int t = 0; t < (C::LINM ? C::TPW : 1); ++t) acc_g[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-
-  // One key block: wait for its tiles in `cur`, prefetch the next block into
-  // `nxt` (double-buffered modes), compute.
-  auto block_step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
-    const int j = (MODE == MODE_DENSE) ? b : col_idx[base + b];
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of block b have landed
-    __syncthreads();                // ... and every other wavefront's; block b-1 consumed
-    if (C::NSTAGE == 2 && b + 1 < nblk) load_block((MODE == MODE_DENSE) ? b + 1 : col_idx[base + b + 1], nxt);
-    const uint16_t* Ks = reinterpret_cast<const uint16_t*>(cur);
-    const uint16_t* Vt = reinterpret_cast<const uint16_t*>(cur + C::KT_BYTES);
-    const uint16_t* Pk = reinterpret_cast<const uint16_t*>(cur + C::KT_BYTES + C::VT_BYTES);
-    const int key0 = j * BK;
-    if (do_s) {
-      // S^T = K Q^T for BK/32 key tiles
-      f32x16 sacc[BK / 32];
-#pragma unroll
-      for (int kt = 0; kt < BK / 32; ++kt) {
-        f32x16 a = f32x16{};
-        const int r = 32 * kt + l32;
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const int pc = (2 * t + hi) ^ (r % C::CHK);
-          const uint4 kv = *reinterpret_cast<const uint4*>(Ks + r * D + 8 * pc);
-          a = mfma(as_bf16x8(kv), qf[t], a);
-        }
-        sacc[kt] = a;
-      }
-      if (key0 + BK > N) {
-#pragma unroll
-        for (int kt = 0; kt < BK / 32; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key >= N) sacc[kt][i] = -INFINITY;
-          }
-      }
-      // G += phi(K)^T V over this block; independent of the softmax below, so
-      // the scheduler can overlap these matrix ops with its vector work
-      if (C::LINM && lin) {
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s) {
-          const int lc = 2 * s + hi;
-#pragma unroll
-          for (int u = 0; u < C::TPW; ++u) {
-            const int tix = w * C::TPW + u;
-            if (tix >= C::TT) continue;
-            const int mt = tix / (D / 32), nt = tix % (D / 32);
-            const int ra = 32 * mt + l32, rb = 32 * nt + l32;
-            const uint4 av = *reinterpret_cast<const uint4*>(Pk + ra * BK + 8 * (lc ^ (ra % C::CHV)));
-            const uint4 bv = *reinterpret_cast<const uint4*>(Vt + rb * BK + 8 * (lc ^ (rb % C::CHV)));
-            acc_g[u] = mfma(as_bf16x8(av), as_bf16x8(bv), acc_g[u]);
-          }
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < BK / 32; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      const float mneg = -m_new * scale_log2;
-      float psum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < BK / 32; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sacc[kt][i], scale_log2, mneg));
-          sacc[kt][i] = pv;
-          psum += pv;
-        }
-      l_run = l_run * corr + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int kt = 0; kt < BK / 32; ++kt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          uint4 pb;
-          pb.x = pk_bf16(sacc[kt][8 * s + 0], sacc[kt][8 * s + 1]);
-          pb.y = pk_bf16(sacc[kt][8 * s + 2], sacc[kt][8 * s + 3]);
-          pb.z = pk_bf16(sacc[kt][8 * s + 4], sacc[kt][8 * s + 5]);
-          pb.w = pk_bf16(sacc[kt][8 * s + 6], sacc[kt][8 * s + 7]);
-          const bf16x8 bp = as_bf16x8(pb);
-          const int lc = 4 * kt + 2 * s + hi;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const int r = 32 * dt + l32;
-            const uint4 vv = *reinterpret_cast<const uint4*>(Vt + r * BK + 8 * (lc ^ (r % C::CHV)));
-            acc_o[dt] = mfma(as_bf16x8(vv), bp, acc_o[dt]);
-          }
-        }
-    }
-    if (C::LINM && lin && !do_s) {
+    for (int t = 0; t < TPW; ++t) acc_g[t] = f32x16{};
+    run_loop([&](int, const char* cur) __attribute__((always_inline)) {
+      if (!lin) return;
+      const char* Vt = cur + T::KT_BYTES;
+      const char* Pk = cur + T::KT_BYTES + T::VT_BYTES;
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
-        const int lc = 2 * s + hi;
 #pragma unroll
-        for (int u = 0; u < C::TPW; ++u) {
-          const int tix = w * C::TPW + u;
-          if (tix >= C::TT) continue;
+        for (int u = 0; u < TPW; ++u) {
+          const int tix = wr * TPW + u;
+          if (tix >= TT) continue;
           const int mt = tix / (D / 32), nt = tix % (D / 32);
-          const int ra = 32 * mt + l32, rb = 32 * nt + l32;
-          const uint4 av = *reinterpret_cast<const uint4*>(Pk + ra * BK + 8 * (lc ^ (ra % C::CHV)));
-          const uint4 bv = *reinterpret_cast<const uint4*>(Vt + rb * BK + 8 * (lc ^ (rb % C::CHV)));
-          acc_g[u] = mfma(as_bf16x8(av), as_bf16x8(bv), acc_g[u]);
+          acc_g[u] = mfma(as_bf16x8(rd16(Pk + s * T::VPB + mt * 1024 + lb)),
+                          as_bf16x8(rd16(Vt + s * T::VPB + nt * 1024 + lb)), acc_g[u]);
         }
       }
-    }
-    if (C::NSTAGE == 1) {
-      __syncthreads();  // the single stage is consumed before it is refilled
-      if (b + 1 < nblk) load_block(col_idx[base + b + 1], cur);
-    }
-  };
-
-  if (nblk > 0) load_block((MODE == MODE_DENSE) ? 0 : col_idx[base], smem);
-  if (C::NSTAGE == 2) {
-    for (int b = 0; b < nblk; b += 2) {
-      block_step(b, smem, smem1);
-      if (b + 1 < nblk) block_step(b + 1, smem1, smem);
-    }
-  } else {
-    for (int b = 0; b < nblk; ++b) block_step(b, smem, smem);
-  }
-
-  // ---------------- epilogue
-  float inv_l = 0.f;
-  if (do_s) {
-    const float lt = l_run + __shfl_xor(l_run, 32);
-    inv_l = lt > 0.f ? 1.f / lt : 0.f;
-  }
-  float den = 1.f;
-  if (C::LINM && lin) {
-    const float* Hh = htot + (size_t)bh * (D * D + D);
-    if (C::NSTAGE == 2) __syncthreads();
-    // H_u^T = (H - G)^T as hi + lo bf16, rows d_v, 16-byte chunks of d_k swizzled
+    });
+    if (lin) {
+      // H_u^T = (H - G)^T as hi + lo bf16 planes (rows d_v, 16-wide d_k slices)
 #pragma unroll
-    for (int u = 0; u < C::TPW; ++u) {
-      const int tix = w * C::TPW + u;
-      if (tix >= C::TT) continue;
-      const int mt = tix / (D / 32), nt = tix % (D / 32);
-      const int dv = 32 * nt + l32;
+      for (int u = 0; u < TPW; ++u) {
+        const int tix = wr * TPW + u;
+        if (tix >= TT) continue;
+        const int mt = tix / (D / 32), nt = tix % (D / 32);
+        const int dv = 32 * nt + l32;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int dk = 32 * mt + 8 * i4 + 4 * hi;
-        float hv[4], lv[4];
-        uint32_t hb[4];
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int dk = 32 * mt + 8 * i4 + 4 * hi;
+          float hv[4], lv[4];
+          uint32_t hb[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          hv[r] = Hh[(dk + r) * D + dv] - acc_g[u][4 * i4 + r];
-          hb[r] = pk_bf16(hv[r], 0.f) & 0xffffu;
-          lv[r] = hv[r] - bf2f(hb[r]);
+          for (int r = 0; r < 4; ++r) {
+            hv[r] = Hh[(dk + r) * D + dv] - acc_g[u][4 * i4 + r];
+            hb[r] = pk_bf16(hv[r], 0.f) & 0xffffu;
+            lv[r] = hv[r] - bf2f(hb[r]);
+          }
+          const int off = (dk >> 4) * T::HPB + dv * 32 + 16 * (((dk >> 3) & 1) ^ ((dv >> 3) & 1)) + 8 * hi;
+          uint2 wv;
+          wv.x = hb[0] | (hb[1] << 16);
+          wv.y = hb[2] | (hb[3] << 16);
+          *reinterpret_cast<uint2*>(HuHi + off) = wv;
+          wv.x = pk_bf16(lv[0], lv[1]);
+          wv.y = pk_bf16(lv[2], lv[3]);
+          *reinterpret_cast<uint2*>(HuLo + off) = wv;
         }
-        const int pc = (4 * mt + i4) ^ (dv % (D / 8));
-        uint2 wv;
-        wv.x = hb[0] | (hb[1] << 16);
-        wv.y = hb[2] | (hb[3] << 16);
-        *reinterpret_cast<uint2*>(HuHi + dv * D + 8 * pc + 4 * hi) = wv;
-        wv.x = pk_bf16(lv[0], lv[1]);
-        wv.y = pk_bf16(lv[2], lv[3]);
-        *reinterpret_cast<uint2*>(HuLo + dv * D + 8 * pc + 4 * hi) = wv;
       }
+      __syncthreads();  // H_u^T and z_u complete
     }
+    return;
+  }
+
+  // ---- attention wavefronts
+  const int q = qi * BQ + 32 * wr + l32;
+  bf16x8 qf[D / 16];
+  load_q<D>(Q, bh, q, N, hi, qf);
+  f32x16 acc_o[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  run_loop([&](int j, const char* cur) __attribute__((always_inline)) {
+    if (!do_s) return;
+    if ((j + 1) * BK > N)
+      attend_block<D, BK, true>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N,
+                                scale_log2);
+    else
+      attend_block<D, BK, false>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N,
+                                 scale_log2);
+  });
+  if (lin) {
     if (tid < D) {
       float g = 0.f;
       for (int b = 0; b < nsel; ++b) g += zblk[((size_t)bh * Nk + col_idx[base + b]) * D + tid];
       zu[tid] = Hh[D * D + tid] - g;
     }
-    __syncthreads();
+    __syncthreads();  // H_u^T and z_u complete
   }
 
-  const size_t orow = ((size_t)bh * N + q) * D;
+  float inv_l = 0.f;
+  if (do_s) {
+    const float lt = l_run + __shfl_xor(l_run, 32);
+    inv_l = lt > 0.f ? 1.f / lt : 0.f;
+  }
   f32x16 acc_n[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) acc_n[mt] = f32x16{};
-  if (C::LINM && lin) {
+  float den = 1.f;
+  if (lin) {
     // num^T = H_u^T phi(Q)^T with phi(Q) split into hi + lo once per k-step
     float dpart = 0.f;
 #pragma unroll
@@ -558,10 +656,8 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
                                               pk_bf16(fl[4], fl[5]), pk_bf16(fl[6], fl[7])));
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
-        const int r = 32 * mt + l32;
-        const int pc = (2 * t + hi) ^ (r % (D / 8));
-        const uint4 ah = *reinterpret_cast<const uint4*>(HuHi + r * D + 8 * pc);
-        const uint4 al = *reinterpret_cast<const uint4*>(HuLo + r * D + 8 * pc);
+        const uint4 ah = rd16(HuHi + t * T::HPB + mt * 1024 + lb);
+        const uint4 al = rd16(HuLo + t * T::HPB + mt * 1024 + lb);
         acc_n[mt] = mfma(as_bf16x8(ah), bh4, acc_n[mt]);
         acc_n[mt] = mfma(as_bf16x8(ah), bl4, acc_n[mt]);
         acc_n[mt] = mfma(as_bf16x8(al), bh4, acc_n[mt]);
@@ -569,19 +665,17 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
     }
     den = dpart + __shfl_xor(dpart, 32);
   }
-  const float wl_den = (C::LINM && lin) ? wl_ / den : 0.f;
+  const float wl_den = lin ? wl_ / den : 0.f;
   const float ws_l = ws_ * inv_l;
   if (q < N) {
+    const size_t orow = ((size_t)bh * N + q) * D;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 4 * i4 + r;
-          o[r] = ws_l * acc_o[mt][i] + wl_den * acc_n[mt][i];
-        }
+        for (int r = 0; r < 4; ++r) o[r] = ws_l * acc_o[mt][4 * i4 + r] + wl_den * acc_n[mt][4 * i4 + r];
         uint2 wv;
         wv.x = pk_bf16(o[0], o[1]);
         wv.y = pk_bf16(o[2], o[3]);
@@ -642,7 +736,6 @@ template <int D, int BQ, int BK>
 hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K, const int32_t* rp,
                          const int32_t* ci, const float* alpha, const char* ws, const WsLayout& L,
                          void* O, hipStream_t st) {
-  const dim3 grid((unsigned)s.R()), block(BQ / 32 * 64);
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
@@ -651,16 +744,25 @@ hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K
   const float* zb = reinterpret_cast<const float*>(ws + L.zblk);
   const float* ht = reinterpret_cast<const float*>(ws + L.htot);
   uint16_t* o = static_cast<uint16_t*>(O);
-#define SLA_GO(M)                                                                                  \
-  hipLaunchKernelGGL((attn_kernel<D, BQ, BK, M>), grid, block, 0, st, q, k, vt, pk, zb, rp, ci,    \
-                     alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2)
+  const dim3 grid((unsigned)s.R());
   switch (mode) {
-    case MODE_SPARSE: SLA_GO(MODE_SPARSE); break;
-    case MODE_LINEAR: SLA_GO(MODE_LINEAR); break;
-    case MODE_FUSED: SLA_GO(MODE_FUSED); break;
-    default: SLA_GO(MODE_DENSE); break;
+    case MODE_SPARSE:
+      hipLaunchKernelGGL((attn_kernel<D, BQ, BK, MODE_SPARSE>), grid, dim3(BQ / 32 * 64), 0, st, q, k, vt,
+                         rp, ci, o, s.N, s.Nq, s.Nk, sl2);
+      break;
+    case MODE_DENSE:
+      hipLaunchKernelGGL((attn_kernel<D, BQ, BK, MODE_DENSE>), grid, dim3(BQ / 32 * 64), 0, st, q, k, vt,
+                         rp, ci, o, s.N, s.Nq, s.Nk, sl2);
+      break;
+    case MODE_LINEAR:
+      hipLaunchKernelGGL((fused_kernel<D, BQ, BK, MODE_LINEAR>), grid, dim3(BQ / 32 * 128), 0, st, q, k,
+                         vt, pk, zb, rp, ci, alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2);
+      break;
+    default:
+      hipLaunchKernelGGL((fused_kernel<D, BQ, BK, MODE_FUSED>), grid, dim3(BQ / 32 * 128), 0, st, q, k,
+                         vt, pk, zb, rp, ci, alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2);
+      break;
   }
-#undef SLA_GO
   return hipGetLastError();
 }
 
