@@ -17,9 +17,9 @@
 // Pipeline (six launches, no host synchronisation):
 //   pool      one workgroup per (b, h, block) of Q and of K   - HBM bound
 //   router    pooled rows times W                               (optional)
-//   score     per (b, h) 64x64-tiled float64 product q_hat k_hat^T / sqrt(d)
-//   select    one workgroup per mask row: softmax, bitonic sort, prefix mass,
-//             n = max(k, kp), bitmask of the kept blocks
+//   score     per (b, h) 64x64-tiled float64 MFMA product q_hat k_hat^T / sqrt(d)
+//   select    one wavefront per mask row: softmax, radix descent to the Top-k
+//             and Top-p cut points, n = max(k, kp), bitmask of the kept blocks
 //   scan      one workgroup: exclusive scan of the per-row counts -> row_ptr
 //   emit      one wavefront per row: bitmask -> ascending col_idx
 #include "sla_internal.h"
@@ -143,59 +143,68 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const double* __restri
   }
 }
 
-// S[bh, i, j] = qh[bh, i, :] . kh[bh, j, :] / sqrt(D); 64x64 tile per
-// workgroup, 4x4 outputs per thread, float64 FMA.
+// S[bh, i, j] = qh[bh, i, :] . kh[bh, j, :] / sqrt(D) on the float64 matrix
+// cores (v_mfma_f64_16x16x4f64: lane l supplies A row l%16 / B column l%16 at
+// k = l/16; accumulator element i of lane l is row 4*i + l/16, column l%16).
+// 64x64 tile per workgroup, a 32x32 quarter (2x2 MFMA blocks) per wavefront,
+// operands staged in LDS 32 k at a time.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qh,
                                                          const double* __restrict__ kh,
                                                          double* __restrict__ S, int Nq, int Nk) {
-  constexpr int T = 64, KC = 16;
-  __shared__ double As[KC][T + 1];
-  __shared__ double Bs[KC][T + 1];
+  constexpr int T = 64, KC = 32, LD = KC + 1;
+  __shared__ double As[T * LD];
+  __shared__ double Bs[T * LD];
   const long long bh = blockIdx.z;
   const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
   const double* qb = qh + (size_t)bh * Nq * D;
   const double* kb = kh + (size_t)bh * Nk * D;
-  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  double acc[4][4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wr = w >> 1, wc = w & 1;
+  const int l16 = lane & 15, kq = lane >> 4;
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = 0.0;
+    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
   for (int kc = 0; kc < D; kc += KC) {
+    __syncthreads();
 #pragma unroll
     for (int u = 0; u < (T * KC) / kThreads; ++u) {
       const int e = tid + kThreads * u;
       const int r = e / KC, kk = e % KC;
-      As[kk][r] = (i0 + r < Nq) ? qb[(size_t)(i0 + r) * D + kc + kk] : 0.0;
-      Bs[kk][r] = (j0 + r < Nk) ? kb[(size_t)(j0 + r) * D + kc + kk] : 0.0;
+      As[r * LD + kk] = (i0 + r < Nq) ? qb[(size_t)(i0 + r) * D + kc + kk] : 0.0;
+      Bs[r * LD + kk] = (j0 + r < Nk) ? kb[(size_t)(j0 + r) * D + kc + kk] : 0.0;
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) {
-      double av[4], bv[4];
+    for (int s = 0; s < KC / 4; ++s) {
+      const int kk = 4 * s + kq;
+      double av[2], bv[2];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) av[a] = As[kk][ty + 16 * a];
+      for (int a = 0; a < 2; ++a) av[a] = As[(32 * wr + 16 * a + l16) * LD + kk];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bv[b] = Bs[kk][tx + 16 * b];
+      for (int b = 0; b < 2; ++b) bv[b] = Bs[(32 * wc + 16 * b + l16) * LD + kk];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fma(av[a], bv[b], acc[a][b]);
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
-    __syncthreads();
   }
   const double sd = sqrt((double)D);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int i = i0 + ty + 16 * a;
-    if (i >= Nq) continue;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int j = j0 + tx + 16 * b;
-      if (j < Nk) S[((size_t)bh * Nq + i) * Nk + j] = acc[a][b] / sd;
+    for (int b = 0; b < 2; ++b) {
+      const int j = j0 + 32 * wc + 16 * b + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i0 + 32 * wr + 16 * a + 4 * i + kq;
+        if (r < Nq && j < Nk) S[((size_t)bh * Nq + r) * Nk + j] = acc[a][b][i] / sd;
+      }
     }
-  }
 }
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -214,118 +223,212 @@ __device__ __forceinline__ int wave_min_int(int v) {
   return v;
 }
 
-// One workgroup per mask row.  NP = padded power of two >= Nk.
-template <int NP>
-__global__ __launch_bounds__(kThreads) void select_kernel(const double* __restrict__ S, int Nk, int k,
-                                                          double p, int* __restrict__ counts,
-                                                          uint32_t* __restrict__ bits, int W) {
-  constexpr int NW = kThreads / 64;
-  __shared__ double pv[NP];
-  __shared__ int iv[NP];
-  __shared__ double red_d[NW];
-  __shared__ int red_i[NW];
-  __shared__ double tot[kThreads];
-  __shared__ uint32_t words[NP / 32];
-  const long long row = blockIdx.x;
-  const double* srow = S + (size_t)row * Nk;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// ---------------------------------------------------------------- selection
+// One wavefront per mask row (four rows per workgroup, no barriers).  Lane l
+// holds the row's blocks j = l + 64 e, e < E.  P_j = exp(S_j - max) / sum in
+// float64; its bit pattern is an order-preserving 64-bit key (P >= 0).
+//
+// The order is P descending with ties to the lower block index; Top-k keeps
+// the first k, Top-p the first kp where kp is the smallest count whose
+// cumulative mass reaches p, the union keeps the first max(k, kp) [SA2 §一].
+// Both cut points are found without sorting, by an 8-pass radix descent over
+// the key bytes with per-wavefront LDS histograms: by count for Top-k, by mass
+// for Top-p.  Mass is accumulated in 2^-62 fixed point, so the sums are exact
+// and independent of the order the lanes add them in (the result is
+// bit-for-bit repeatable); it differs from a sequential float64 cumulative
+// sum by at most Nk * 2^-62.  Equal keys at the cut are taken in ascending
+// block order, ranked with ballots.
 
-  // 1. logits, row max
-  double lmax = -INFINITY;
-  for (int j = tid; j < NP; j += kThreads) {
-    const double s = (j < Nk) ? srow[j] : -INFINITY;
-    pv[j] = s;
-    iv[j] = j;
-    lmax = fmax(lmax, s);
+constexpr double kMassScale = 4611686018427387904.0;  // 2^62
+
+__device__ __forceinline__ unsigned long long mass_of(unsigned long long key) {
+  const double pr = __longlong_as_double((long long)key);
+  return (unsigned long long)(pr * kMassScale + 0.5);
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T u = __shfl_up(v, o);
+    if (lane >= o) v += u;
   }
-  for (int w = tid; w < NP / 32; w += kThreads) words[w] = 0u;
-  lmax = wave_max(lmax);
-  if (lane == 0) red_d[wv] = lmax;
-  __syncthreads();
-  double m = red_d[0];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) m = fmax(m, red_d[w]);
-  __syncthreads();
-  // 2. softmax normaliser
-  double lsum = 0.0;
-  for (int j = tid; j < Nk; j += kThreads) lsum += exp(pv[j] - m);
-  lsum = wave_sum(lsum);
-  if (lane == 0) red_d[wv] = lsum;
-  __syncthreads();
-  double Z = 0.0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) Z += red_d[w];
-  for (int j = tid; j < NP; j += kThreads) pv[j] = (j < Nk) ? exp(pv[j] - m) / Z : -1.0;
-  __syncthreads();
+  return v;
+}
 
-  // 3. bitonic sort: probability descending, ties to the lower block index
-  for (int size = 2; size <= NP; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < NP / 2; t += kThreads) {
-        const int i = 2 * stride * (t / stride) + (t % stride);
-        const int j = i + stride;
-        const double pi = pv[i], pj = pv[j];
-        const int ii = iv[i], ij = iv[j];
-        const bool j_first = (pj > pi) || (pj == pi && ij < ii);
-        const bool i_first = (pi > pj) || (pi == pj && ii < ij);
-        const bool swap = ((i & size) == 0) ? j_first : i_first;
-        if (swap) {
-          pv[i] = pj; pv[j] = pi;
-          iv[i] = ij; iv[j] = ii;
-        }
-      }
-      __syncthreads();
+// Radix descent for the element at which the running total of `weight` over
+// the descending key order first reaches `target` (which the caller guarantees
+// the total reaches).  Returns its key, the count and total weight of the
+// valid elements with a strictly larger key, and the number of elements with
+// exactly that key.  BYMASS: weight = fixed-point mass, else weight = 1.
+template <int E, bool BYMASS>
+__device__ void radix_cut(const unsigned long long (&key)[E], unsigned valid_bits,
+                          unsigned long long target, unsigned* hcnt, unsigned long long* hmass,
+                          int lane, unsigned long long& cut_key, unsigned& above_cnt,
+                          unsigned long long& above_w, unsigned& tie_cnt) {
+  unsigned long long prefix = 0;
+  above_cnt = 0;
+  above_w = 0;
+  tie_cnt = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    for (int b = lane; b < 256; b += 64) {
+      hcnt[b] = 0u;
+      if (BYMASS) hmass[b] = 0ull;
     }
-  }
-
-  // 4. cumulative mass in sorted order; kp = first n with mass(n) >= p
-  constexpr int E = (NP + kThreads - 1) / kThreads;
-  const int e0 = tid * E;
-  double local = 0.0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int n = e0 + e;
-    if (n < Nk) local += pv[n];
-  }
-  tot[tid] = local;
-  __syncthreads();
-  // exclusive prefix over thread totals (Hillis-Steele in LDS)
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const double add = (tid >= off) ? tot[tid - off] : 0.0;
-    __syncthreads();
-    tot[tid] += add;
-    __syncthreads();
-  }
-  double run = (tid > 0) ? tot[tid - 1] : 0.0;
-  int first = 0x7fffffff;
-  if (p > 0.0) {
+    // LDS operations of one wavefront are performed in issue order, so the
+    // clears above land before these atomics and the reads below.
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int n = e0 + e;
-      if (n < Nk) {
-        run += pv[n];
-        if (run >= p && first == 0x7fffffff) first = n + 1;
+      const bool in = ((valid_bits >> e) & 1u) && (pass == 0 || (key[e] >> (shift + 8)) == prefix);
+      if (in) {
+        const int bin = (int)((key[e] >> shift) & 255ull);
+        atomicAdd(&hcnt[bin], 1u);
+        if (BYMASS) atomicAdd(&hmass[bin], mass_of(key[e]));
       }
     }
-  }
-  first = wave_min_int(first);
-  if (lane == 0) red_i[wv] = first;
-  __syncthreads();
-  int kp = red_i[0];
+    // lane l owns bins 255-4l-i (i = 0..3): lane 0 holds the largest keys
+    unsigned c[4];
+    unsigned long long wgt[4];
+    unsigned long long wl = 0, cl = 0;
 #pragma unroll
-  for (int w = 1; w < NW; ++w) kp = min(kp, red_i[w]);
-  if (p <= 0.0) kp = 0;
-  else if (kp == 0x7fffffff) kp = Nk;
-  const int nsel = max(min(k, Nk), kp);
-
-  // 5. bitmask of the kept blocks
-  for (int n = tid; n < nsel; n += kThreads) {
-    const int j = iv[n];
-    atomicOr(&words[j >> 5], 1u << (j & 31));
+    for (int i = 0; i < 4; ++i) {
+      const int bin = 255 - 4 * lane - i;
+      c[i] = hcnt[bin];
+      wgt[i] = BYMASS ? hmass[bin] : (unsigned long long)c[i];
+      wl += wgt[i];
+      cl += c[i];
+    }
+    const unsigned long long w_incl = wave_incl_scan(wl, lane), w_excl = w_incl - wl;
+    const unsigned long long c_incl = wave_incl_scan(cl, lane), c_excl = c_incl - cl;
+    // the single lane whose bins hold the crossing
+    const bool here = above_w + w_excl < target && above_w + w_incl >= target;
+    const int src = __ffsll((long long)__ballot(here)) - 1;
+    // within it, the first bin (largest keys first) where the total reaches target
+    int pick = 3;
+    unsigned long long wb = above_w + w_excl;
+    unsigned cb = (unsigned)c_excl;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (found) continue;
+      if (wb + wgt[i] >= target) {
+        pick = i;
+        found = true;
+      } else {
+        wb += wgt[i];
+        cb += c[i];
+      }
+    }
+    unsigned tc = c[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) tc = (i == pick) ? c[i] : tc;
+    prefix = (prefix << 8) | (unsigned long long)__shfl(255 - 4 * lane - pick, src);
+    above_w = __shfl(wb, src);
+    above_cnt += __shfl(cb, src);
+    tie_cnt = __shfl(tc, src);
+    if (tie_cnt == 1u && pass < 7) {
+      // a single element left under this prefix: it is the cut; fetch its key
+      unsigned long long mine = 0;
+      bool has = false;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool m = ((valid_bits >> e) & 1u) && (key[e] >> shift) == prefix;
+        mine = m ? key[e] : mine;
+        has = has || m;
+      }
+      const int owner = __ffsll((long long)__ballot(has)) - 1;
+      cut_key = __shfl(mine, owner);
+      return;
+    }
   }
-  __syncthreads();
-  for (int w = tid; w < W; w += kThreads) bits[(size_t)row * W + w] = words[w];
-  if (tid == 0) counts[row] = nsel;
+  cut_key = prefix;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ S, long long R, int Nk,
+                                                     int k, double p, int* __restrict__ counts,
+                                                     uint32_t* __restrict__ bits, int W) {
+  __shared__ unsigned hcnt_all[4][256];
+  __shared__ unsigned long long hmass_all[4][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + wv;
+  if (row >= R) return;  // whole wavefront; the kernel has no barrier
+  unsigned* hcnt = hcnt_all[wv];
+  unsigned long long* hmass = hmass_all[wv];
+  const double* srow = S + (size_t)row * Nk;
+
+  double sv[E];
+  unsigned valid_bits = 0;
+  double mx = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    const bool ok = j < Nk;
+    sv[e] = ok ? srow[j] : -INFINITY;
+    valid_bits |= (ok ? 1u : 0u) << e;
+    mx = fmax(mx, sv[e]);
+  }
+  mx = wave_max(mx);
+  double z = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((valid_bits >> e) & 1u) z += exp(sv[e] - mx);
+  z = wave_sum(z);
+  unsigned long long key[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    key[e] = ((valid_bits >> e) & 1u) ? (unsigned long long)__double_as_longlong(exp(sv[e] - mx) / z) : 0ull;
+
+  const int kk = min(k, Nk);
+  unsigned long long kkey = 0, kw = 0, pkey = 0, pw = 0;
+  unsigned kabove = 0, ktie = 0, pabove = 0, ptie = 0;
+  // Top-k cut (the kk-th element in the order)
+  if (kk > 0 && kk < Nk)
+    radix_cut<E, false>(key, valid_bits, (unsigned long long)kk, hcnt, hmass, lane, kkey, kabove, kw, ktie);
+  // Top-p cut (the element whose cumulative mass first reaches p)
+  int kp = 0;
+  if (p > 0.0) {
+    const unsigned long long target = (unsigned long long)ceil(p * kMassScale);
+    unsigned long long tot = 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((valid_bits >> e) & 1u) tot += mass_of(key[e]);
+    tot = __shfl(wave_incl_scan(tot, lane), 63);
+    if (tot < target) {
+      kp = Nk;  // p is never reached: every block
+    } else {
+      radix_cut<E, true>(key, valid_bits, target, hcnt, hmass, lane, pkey, pabove, pw, ptie);
+      const unsigned long long f = mass_of(pkey);  // > 0: this element makes the total reach p
+      const unsigned long long nt = (target - pw + f - 1) / f;
+      kp = (int)pabove + (int)min(nt, (unsigned long long)ptie);
+    }
+  }
+  const int nsel = max(kk, kp);
+  const bool all = nsel >= Nk;
+  const unsigned long long ckey = (nsel == kk) ? kkey : pkey;
+  const int ties_needed = nsel - (int)((nsel == kk) ? kabove : pabove);
+
+  // kept: every valid block when all, else key > cut, or key == cut and among
+  // the first ties_needed such blocks in block order
+  int ties_before = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool valid = (valid_bits >> e) & 1u;
+    const bool gt = valid && nsel > 0 && key[e] > ckey;
+    const bool eq = valid && nsel > 0 && key[e] == ckey;
+    const unsigned long long eqm = __ballot(eq);
+    const int rank = ties_before + __popcll(eqm & ((1ull << lane) - 1ull));
+    const bool sel = all ? valid : (gt || (eq && rank < ties_needed));
+    ties_before += __popcll(eqm);
+    const unsigned long long sm = __ballot(sel);
+    if (lane == 0) {
+      if (2 * e < W) bits[(size_t)row * W + 2 * e] = (uint32_t)(sm & 0xffffffffull);
+      if (2 * e + 1 < W) bits[(size_t)row * W + 2 * e + 1] = (uint32_t)(sm >> 32);
+    }
+  }
+  if (lane == 0) counts[row] = nsel;
 }
 
 // Exclusive scan of counts[R] into row_ptr[R + 1] with one workgroup.
@@ -386,11 +489,11 @@ __global__ __launch_bounds__(kThreads) void emit_kernel(const uint32_t* __restri
   }
 }
 
-template <int NP>
+template <int E>
 hipError_t launch_select(const double* S, long long R, int Nk, int k, double p, int* counts,
                          uint32_t* bits, int W, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<NP>), dim3((unsigned)R), dim3(kThreads), 0, st, S, Nk, k, p,
-                     counts, bits, W);
+  hipLaunchKernelGGL((select_kernel<E>), dim3((unsigned)((R + 3) / 4)), dim3(kThreads), 0, st, S, R, Nk,
+                     k, p, counts, bits, W);
   return hipGetLastError();
 }
 
@@ -451,16 +554,16 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
     hipLaunchKernelGGL((score_kernel<64>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  int np = 64;
-  while (np < s.Nk) np <<= 1;
-  switch (np) {
-    case 64: e = launch_select<64>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 128: e = launch_select<128>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 256: e = launch_select<256>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 512: e = launch_select<512>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 1024: e = launch_select<1024>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 2048: e = launch_select<2048>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    default: e = launch_select<4096>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+  int E = 1;
+  while (64 * E < s.Nk) E <<= 1;
+  switch (E) {
+    case 1: e = launch_select<1>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 2: e = launch_select<2>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 4: e = launch_select<4>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 8: e = launch_select<8>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 16: e = launch_select<16>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 32: e = launch_select<32>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    default: e = launch_select<64>(S, R, s.Nk, k, p, counts, bits, W, st); break;
   }
   if (e != hipSuccess) return e;
 
