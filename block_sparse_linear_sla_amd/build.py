@@ -18,6 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsla.so")
 SOURCES = ["sla_api.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip"]
+# per-source extra flags: the attention kernels keep their matrix accumulators
+# in ordinary VGPRs (their softmax reads them every step), so the compiler is
+# told to use the VGPR form of the MFMA instructions there
+EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
 
 
@@ -37,7 +41,7 @@ def flags() -> list:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

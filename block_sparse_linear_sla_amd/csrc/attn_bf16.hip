@@ -50,7 +50,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void gbl_void;
+
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -85,12 +89,6 @@ __device__ __forceinline__ int kperm(int o) { return (o & ~12) | ((o & 4) << 1) 
 __device__ __forceinline__ uint32_t elem(const uint4& v, int e) {
   const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// 16-byte direct load global -> LDS; lane l of the wavefront writes
-// lds_wave_base + 16 * l.
-__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void*)gsrc, (lds_void*)lds_wave_base, 16, 0, 0);
 }
 
 // ------------------------------------------------------------------ prep
@@ -254,23 +252,27 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------ attention
-template <bool B>
-struct BoolTag {
-  static constexpr bool value = B;
-};
+constexpr int LDS_BYTES = 160 * 1024;  // LDS of one gfx950 compute unit
+constexpr int KU = 64;                 // keys per attention unit; a listed block of BK keys is BK/64 units
 
-// LDS tiles are stored as "planes": every 16-element k-slice that an MFMA
-// operand read takes is a plane of 32 bytes per row (two 16-byte halves), and
-// row r keeps its halves swapped when bit 3 of r is set.  The 16 rows that a
-// 16-lane group reads then sit in 16 distinct 16-byte bank groups, and every
-// operand read is one per-lane base address plus a compile-time offset.
-template <int D, int BK>
+// LDS tile layouts of one 64-key unit.  Every direct load instruction brings
+// 64 x 16 bytes that land in LDS in lane order, so a tile is stored as rows of
+// whole 128-byte global lines and each load covers 8 complete lines.  Inside
+// a row the 16-byte chunks are XOR-swizzled by the row index, so the 16 rows
+// that a 16-lane group reads for one MFMA operand hit 16 distinct 16-byte bank
+// groups:
+//   K tile     [D/64][64 keys][128 B]  chunk c of key r stored at c ^ ((r >> 1) & 7)
+//   V^T tile   [D][128 B]              chunk c of row d stored at c ^ ((d >> 1) & 7)
+//   phi(K)^T tile: as V^T
+// H_u^T (written with ordinary LDS stores after the loop) keeps a "plane"
+// layout: every 16-element k-slice is a plane of 32 bytes per row, the two
+// 16-byte halves swapped when bit 3 of the row is set.
+template <int D>
 struct Tiles {
-  static constexpr int KPB = BK * 32;        // bytes of one K plane (16 d of BK keys)
-  static constexpr int VPB = D * 32;         // bytes of one V^T / phi(K)^T plane (16 keys)
-  static constexpr int KT_BYTES = BK * D * 2;
-  static constexpr int VT_BYTES = D * BK * 2;
-  static constexpr int HPB = D * 32;         // bytes of one H_u^T plane (16 d_k)
+  static constexpr int KHALF = KU * 128;       // bytes of one 64-d half of the K tile
+  static constexpr int KT_BYTES = KU * D * 2;  // K tile
+  static constexpr int VT_BYTES = D * KU * 2;  // V^T (or phi(K)^T) tile
+  static constexpr int HPB = D * 32;           // bytes of one H_u^T plane (16 d_k)
 };
 
 __device__ __forceinline__ int lane_base(int lane) {
@@ -278,101 +280,215 @@ __device__ __forceinline__ int lane_base(int lane) {
   return l32 * 32 + 16 * (hi ^ ((l32 >> 3) & 1));
 }
 
+// Per-lane byte offsets of the MFMA operand reads (lane l: row l%32 of a
+// 32-row tile, k-slice half l/32): the 16-wide k-step t of 32 rows of 128 bytes
+// is at off[t].  K: d-step t of key subtile kt at (t/4) KHALF + 4096 kt +
+// off[t%4]; V^T / phi(K)^T: key plane pl of row tile dt at 4096 dt + off[pl].
+template <int D>
+struct ReadPlan {
+  int off[4];
+  __device__ __forceinline__ explicit ReadPlan(int lane) {
+    const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) off[t] = l32 * 128 + 16 * ((2 * t + hi) ^ ((l32 >> 1) & 7));
+  }
+  __device__ __forceinline__ const char* kp(const char* Ks, int kt, int t) const {
+    return Ks + (t / 4) * Tiles<D>::KHALF + kt * 4096 + off[t % 4];
+  }
+  __device__ __forceinline__ const char* vp(const char* Vt, int dt, int pl) const {
+    return Vt + dt * 4096 + off[pl];
+  }
+};
+
 __device__ __forceinline__ uint4 rd16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// Direct loads of key block j into the LDS stage at sb by wavefront w of NWL.
-// Load slot u fills the 1 KB at sb + 1024 u: 32 rows x 32 bytes of one plane;
-// lane l brings row l/2, stored half l%2.  K rows past N are clamped (their
-// scores are masked); V^T / phi(K)^T are zero past N.
-template <int D, int BK, int NWL>
-__device__ __forceinline__ void load_tiles(const uint16_t* Kb, const uint16_t* Vtb, const uint16_t* Pkb,
-                                           int j, int N, size_t npad, bool doK, bool doP, char* sb,
-                                           int w, int lane) {
-  using T = Tiles<D, BK>;
-  const int lrow = lane >> 1, lpos = lane & 1;
-  if (doK) {
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their no-wait maxima).  Direct
+// loads to LDS count on vmcnt, in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Buffer resource over [base, base + bytes) for raw (unstructured) buffer
+// loads; reads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct buffer load of 16 (or 4) bytes per lane into LDS: lane l writes
+// lds_wave_base + 16 l (4 l); the byte address is voff + soff in the buffer.
+__device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                        void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, (int)soff, 0, 0);
+}
+__device__ __forceinline__ void b2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                       void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, (int)voff, (int)soff, 0, 0);
+}
+
+// Direct loads of one unit's tiles into LDS, split over NWL wavefronts.  Load
+// slot u of a tile fills the 1 KB at tile + 1024 u (8 rows of 128 bytes, in
+// the swizzled layouts above): lane l brings the 16-byte chunk that belongs at
+// position l.  Each load is a per-head buffer resource, the unit's byte
+// offset (scalar) and a per-lane byte offset fixed for the kernel.  K rows
+// past N read as zeros (their scores are masked); V^T / phi(K)^T are zero past N.
+template <int D, int NWL>
+struct LoadPlan {
+  using T = Tiles<D>;
+  static constexpr int NK = T::KT_BYTES / 1024 / NWL;   // K slots per wavefront
+  static constexpr int NV = T::VT_BYTES / 1024 / NWL;   // V^T (or phi(K)^T) slots per wavefront
+  static_assert(NK * NWL * 1024 == T::KT_BYTES && NV * NWL * 1024 == T::VT_BYTES, "tile split");
+  uint32_t koff[NK], voff[NV];
+  int w;
+
+  __device__ __forceinline__ LoadPlan(int w_, int lane, size_t npad) : w(w_) {
 #pragma unroll
-    for (int ii = 0; ii < T::KT_BYTES / 1024 / NWL; ++ii) {
+    for (int ii = 0; ii < NK; ++ii) {
       const int u = w + NWL * ii;
-      const int t = u / (T::KPB / 1024), r = (u % (T::KPB / 1024)) * 32 + lrow;
-      const int hh = lpos ^ ((r >> 3) & 1);
-      const int key = min(j * BK + r, N - 1);
-      g2lds16(Kb + (size_t)key * D + 16 * t + 8 * hh, sb + 1024 * u);
+      const int hd = u / 8, key = 8 * (u % 8) + (lane >> 3);
+      const int c = (lane & 7) ^ ((key >> 1) & 7);
+      koff[ii] = (uint32_t)(key * D * 2 + hd * 128 + 16 * c);
+    }
+#pragma unroll
+    for (int ii = 0; ii < NV; ++ii) {
+      const int u = w + NWL * ii;
+      const int d = 8 * u + (lane >> 3);
+      const int c = (lane & 7) ^ ((d >> 1) & 7);
+      voff[ii] = (uint32_t)((size_t)d * npad * 2 + 16 * c);
     }
   }
+  // K tile of the unit starting at key key0 (K of one head as a buffer)
+  __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int key0, char* dst) const {
+    const uint32_t soff = (uint32_t)key0 * (D * 2);
 #pragma unroll
-  for (int ii = 0; ii < T::VT_BYTES / 1024 / NWL; ++ii) {
-    const int u = w + NWL * ii;
-    const int pl = u / (T::VPB / 1024), r = (u % (T::VPB / 1024)) * 32 + lrow;
-    const int hh = lpos ^ ((r >> 3) & 1);
-    const size_t go = (size_t)r * npad + (size_t)j * BK + 16 * pl + 8 * hh;
-    g2lds16(Vtb + go, sb + T::KT_BYTES + 1024 * u);
-    if (doP) g2lds16(Pkb + go, sb + T::KT_BYTES + T::VT_BYTES + 1024 * u);
+    for (int ii = 0; ii < NK; ++ii) b2lds16(rk, koff[ii], soff, dst + 1024 * (w + NWL * ii));
   }
-}
+  // transposed [d, npad] tile (V^T or phi(K)^T of one head) of the unit at key0
+  __device__ __forceinline__ void load_t(__amdgpu_buffer_rsrc_t rt, int key0, char* dst) const {
+    const uint32_t soff = (uint32_t)key0 * 2;
+#pragma unroll
+    for (int ii = 0; ii < NV; ++ii) b2lds16(rt, voff[ii], soff, dst + 1024 * (w + NWL * ii));
+  }
+};
 
 // max of v over lanes l and l^32 (v_permlane32_swap exchanges the two halves;
 // taking the max with the own value makes the result independent of which
 // output holds which half)
 __device__ __forceinline__ float pair_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+  return __builtin_elementwise_maximum(
+      v, __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
-// Online-softmax attention of one wavefront's 32 queries over one key block,
-// 32 keys at a time: S^T = K Q^T, running max / sum, O^T += V^T P^T.
-template <int D, int BK, bool MASK>
-__device__ __forceinline__ void attend_block(const char* Ks, const char* Vt, const bf16x8 (&qf)[D / 16],
-                                             f32x16 (&acc_o)[D / 32], float& m_run, float& l_run,
-                                             int lb, int hi, int key0, int N, float scale_log2) {
-  using T = Tiles<D, BK>;
+// Running online-softmax state of one query; lanes l and l^32 hold the two
+// key halves of the same query and keep identical m.
+struct Softmax {
+  float m;     // running max of the raw scores
+  float thr;   // m + 8 / scale_log2: a unit max above it moves m
+  float mneg;  // -m * scale_log2
+  float l;     // this lane's running sum of the (bf16-rounded) P values
+  __device__ __forceinline__ Softmax() : m(-INFINITY), thr(-INFINITY), mneg(0.f), l(0.f) {}
+};
+
+// S^T of a whole unit (two 32-key subtiles) with the K fragments read four
+// MFMAs ahead of their use, so the LDS latency stays hidden behind the
+// matrix ops already issued.
+template <int D>
+__device__ __forceinline__ void score_unit(const char* Ks, const bf16x8 (&qf)[D / 16], const ReadPlan<D>& rp,
+                                           f32x16 (&s)[2]) {
+  constexpr int NT = D / 16;        // k-steps per subtile
+  constexpr int NI = 2 * NT;        // MFMAs of the unit
+  constexpr int PF = 4;             // fragments in flight
+  uint4 fr[PF];
 #pragma unroll
-  for (int kt = 0; kt < BK / 32; ++kt) {
-    f32x16 sa = f32x16{};
+  for (int i = 0; i < PF; ++i) fr[i] = rd16(rp.kp(Ks, i / NT, i % NT));
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) sa = mfma(as_bf16x8(rd16(Ks + t * T::KPB + kt * 1024 + lb)), qf[t], sa);
-    if (MASK) {
+  for (int i = 0; i < NI; ++i) {
+    const uint4 a = fr[i % PF];
+    if (i + PF < NI) fr[i % PF] = rd16(rp.kp(Ks, (i + PF) / NT, (i + PF) % NT));
+    s[i / NT] = mfma(as_bf16x8(a), qf[i % NT], s[i / NT]);
+  }
+  // keep that order: the scheduler would otherwise pull each read down to
+  // just before its MFMA
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // PF LDS reads
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (key >= N) sa[i] = -INFINITY;
-      }
+  for (int i = 0; i + PF < NI; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+}
+
+// S^T subtile kt (32 keys x 32 queries) of the unit whose K tile is Ks.
+template <int D>
+__device__ __forceinline__ f32x16 score_subtile(const char* Ks, int kt, const bf16x8 (&qf)[D / 16],
+                                                const ReadPlan<D>& rp) {
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) s = mfma(as_bf16x8(rd16(rp.kp(Ks, kt, t))), qf[t], s);
+  return s;
+}
+
+// One software-pipelined step of an attention wavefront (32 queries): the
+// scores of the next unit, sn = K_next Q^T, are computed while the current
+// unit's scores sc go through the online softmax and O^T += V_cur^T P^T, so
+// the matrix cores work on one unit while the vector ALU works on the other.
+// Softmax: one max exchange and rescale test per 64 keys; P = exp2(S c - m c)
+// with c = log2(e)/sqrt(d), rounded to bf16; l += sum of the rounded P (v_dot2
+// with ones).  The running max moves only when a unit max exceeds it by more
+// than 2^8 in exp2 units, so P <= 2^8 and the O / l rescale is skipped for
+// most units.  lim < 64 marks a unit running past N: keys at offset >= lim get
+// score -inf.
+template <int D>
+__device__ __forceinline__ void attend_step(const char* Kn, const char* Vc, const bf16x8 (&qf)[D / 16],
+                                            f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&acc_o)[D / 32],
+                                            Softmax& sm, const ReadPlan<D>& rp, int hi, int lim,
+                                            float scale_log2, float thr8) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  if (lim < KU) {
+    const int limh = lim - 4 * hi;  // key offset of element i of subtile h2: 32 h2 + 8 (i/4) + 4 hi + i%4
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * h2 + 8 * (i >> 2) + (i & 3) >= limh) sc[h2][i] = -INFINITY;
+  }
+  sn[0] = score_subtile<D>(Kn, 0, qf, rp);
+  float mx = __builtin_elementwise_maximum(sc[0][0], sc[1][0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i)
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[0][i]), sc[1][i]);
+  mx = pair_max(mx);
+  if (__ballot(mx > sm.thr)) {
+    const float m_new = fmaxf(sm.m, mx);
+    const float corr = __builtin_amdgcn_exp2f((sm.m - m_new) * scale_log2);
+    sm.l *= corr;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
+    sm.m = m_new;
+    sm.mneg = -m_new * scale_log2;
+    sm.thr = m_new + thr8;
+  }
+  sn[1] = score_subtile<D>(Kn, 1, qf, rp);
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const int h2 = s4 >> 1, s = s4 & 1;
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[h2][8 * s + 2 * e], scale_log2, sm.mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[h2][8 * s + 2 * e + 1], scale_log2, sm.mneg));
+      pw[e] = pk_bf16(p0, p1);
+      sm.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, sm.l, false);
     }
-    float mx = sa[0];
+    const bf16x8 bp = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sa[i]);
-    mx = pair_max(mx);
-    // Conditional rescale: the running max moves only when some lane's max
-    // exceeds it by more than 2^8 in exp2 units, so P <= 2^8 and the O / l
-    // rescale is skipped for most tiles.
-    if (__ballot((mx - m_run) * scale_log2 > 8.f)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float corr = __builtin_amdgcn_exp2f((m_run - m_new) * scale_log2);
-      l_run *= corr;
-#pragma unroll
-      for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
-      m_run = m_new;
-    }
-    const float mneg = -m_run * scale_log2;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sa[i] = __builtin_amdgcn_exp2f(fmaf(sa[i], scale_log2, mneg));
-      psum += sa[i];
-    }
-    l_run += psum;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 pb;
-      pb.x = pk_bf16(sa[8 * s + 0], sa[8 * s + 1]);
-      pb.y = pk_bf16(sa[8 * s + 2], sa[8 * s + 3]);
-      pb.z = pk_bf16(sa[8 * s + 4], sa[8 * s + 5]);
-      pb.w = pk_bf16(sa[8 * s + 6], sa[8 * s + 7]);
-      const bf16x8 bp = as_bf16x8(pb);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-        acc_o[dt] = mfma(as_bf16x8(rd16(Vt + (2 * kt + s) * T::VPB + dt * 1024 + lb)), bp, acc_o[dt]);
-    }
+    for (int dt = 0; dt < D / 32; ++dt)
+      acc_o[dt] = mfma(as_bf16x8(rd16(rp.vp(Vc, dt, s4))), bp, acc_o[dt]);
   }
 }
 
@@ -388,29 +504,91 @@ __device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, i
   }
 }
 
-// Sparse (CSR row) or dense (every key block) softmax attention; BQ/32
-// wavefronts of 32 queries, tiles double-buffered.
-template <int D, int BQ, int BK, int MODE>
+// Second half of a unit for one attention wavefront: the online softmax of
+// its scores sc and O^T += V^T P^T (see attend_step for the arithmetic).
+template <int D>
+__device__ __forceinline__ void softmax_pv(const char* Vc, f32x16 (&sc)[2], f32x16 (&acc_o)[D / 32],
+                                           Softmax& sm, const ReadPlan<D>& rp, int hi, int lim,
+                                           float scale_log2, float thr8) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  // V^T fragments of the first key plane, read now so they land during the max
+  uint4 vf[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) vf[dt] = rd16(rp.vp(Vc, dt, 0));
+  if (lim < KU) {
+    const int limh = lim - 4 * hi;  // key offset of element i of subtile h2: 32 h2 + 8 (i/4) + 4 hi + i%4
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * h2 + 8 * (i >> 2) + (i & 3) >= limh) sc[h2][i] = -INFINITY;
+  }
+  float mx = __builtin_elementwise_maximum(sc[0][0], sc[1][0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i)
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[0][i]), sc[1][i]);
+  mx = pair_max(mx);
+  if (__ballot(mx > sm.thr)) {
+    const float m_new = fmaxf(sm.m, mx);
+    const float corr = __builtin_amdgcn_exp2f((sm.m - m_new) * scale_log2);
+    sm.l *= corr;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
+    sm.m = m_new;
+    sm.mneg = -m_new * scale_log2;
+    sm.thr = m_new + thr8;
+  }
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const int h2 = s4 >> 1, s = s4 & 1;
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[h2][8 * s + 2 * e], scale_log2, sm.mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[h2][8 * s + 2 * e + 1], scale_log2, sm.mneg));
+      pw[e] = pk_bf16(p0, p1);
+      sm.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, sm.l, false);
+    }
+    const bf16x8 bp = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const uint4 a = vf[dt];
+      if (s4 + 1 < 4) vf[dt] = rd16(rp.vp(Vc, dt, s4 + 1));  // next key plane, one k-step ahead
+      acc_o[dt] = mfma(as_bf16x8(a), bp, acc_o[dt]);
+    }
+  }
+}
+
+// Sparse (CSR row) or dense (every key block) softmax attention.  BQ/32
+// wavefronts of 32 queries; two workgroups share a compute unit, so each SIMD
+// holds one wavefront of each and the two interleave on their own.  The
+// row's 64-key units stream through two LDS stages (K | V^T, distinct arrays,
+// loop unrolled by two): unit b+1 loads while unit b is computed.  The load
+// after the row's last unit repeats that unit, which keeps every step's count
+// of loads fixed.
+template <int D, int BQ, int SUB, int MODE>
 __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
     const int* __restrict__ row_ptr, const int* __restrict__ col_idx, uint16_t* __restrict__ O, int N,
     int Nq, int Nk, float scale_log2) {
-  using T = Tiles<D, BK>;
+  using T = Tiles<D>;
   constexpr int NW = BQ / 32;
+  using LP = LoadPlan<D, NW>;
   constexpr int STAGE = T::KT_BYTES + T::VT_BYTES;
-  static_assert(T::KT_BYTES % (1024 * NW) == 0 && T::VT_BYTES % (1024 * NW) == 0, "tile split");
-  // Two distinct LDS arrays: the compiler can then tell the prefetch into one
+  static_assert(2 * STAGE <= LDS_BYTES / 2, "two workgroups per compute unit");
+  // Two distinct LDS arrays: the compiler can then tell the loads into one
   // stage from the operand reads of the other.
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
-  const int lb = lane_base(lane);
+  const ReadPlan<D> rdp(lane);
   const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
   const long long bh = row / Nq;
   const int qi = (int)(row % Nq);
-  const size_t npad = (size_t)Nk * BK;
+  const size_t npad = (size_t)Nk * SUB * KU;
   int nsel, base = 0;
   if (MODE == MODE_DENSE) {
     nsel = Nk;
@@ -418,6 +596,7 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
     base = row_ptr[row];
     nsel = row_ptr[row + 1] - base;
   }
+  const int nunits = nsel * SUB;
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vtb = vt_g + (size_t)bh * D * npad;
   const int q = qi * BQ + 32 * w + l32;
@@ -426,26 +605,46 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
   f32x16 acc_o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  Softmax sm;
+  const float thr8 = 8.f / scale_log2;
+  const LP lp(w, lane, npad);
+  const auto rk = buf_rsrc(Kb, (uint32_t)((size_t)N * D * 2));
+  const auto rv = buf_rsrc(Vtb, (uint32_t)((size_t)D * npad * 2));
 
-  auto blk = [&](int b) { return (MODE == MODE_DENSE) ? b : col_idx[base + b]; };
-  auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
-    const int j = blk(b);
-    __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads of block b have landed
-    __syncthreads();                // ... and every wavefront's; block b-1 consumed
-    if (b + 1 < nsel) load_tiles<D, BK, NW>(Kb, Vtb, nullptr, blk(b + 1), N, npad, true, false, nxt, w, lane);
-    if ((j + 1) * BK > N)
-      attend_block<D, BK, true>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N, scale_log2);
-    else
-      attend_block<D, BK, false>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N, scale_log2);
+  // first key of unit x (clamped to the row's last unit)
+  auto key0 = [&](int x) {
+    const int xc = min(x, nunits - 1);
+    const int blk = (MODE == MODE_DENSE) ? xc / SUB : col_idx[base + xc / SUB];
+    return (blk * SUB + xc % SUB) * KU;
   };
-  if (nsel > 0) load_tiles<D, BK, NW>(Kb, Vtb, nullptr, blk(0), N, npad, true, false, st0, w, lane);
-  for (int b = 0; b < nsel; b += 2) {
+  auto issue = [&](int k0x, char* sb) __attribute__((always_inline)) {
+    lp.load_k(rk, k0x, sb);
+    lp.load_t(rv, k0x, sb + T::KT_BYTES);
+  };
+  // kcur: first key of the unit being computed.  The next unit's column index
+  // is read before the barrier, whose wait absorbs the scalar load, so the
+  // LDS-read waits inside the step count LDS reads only.
+  int kcur = nunits > 0 ? key0(0) : 0;
+  auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
+    const int knext = key0(b + 1);
+    wait_vm<0>();     // this wavefront's loads of unit b have landed
+    __syncthreads();  // ... and every wavefront's; unit b-1 consumed
+    issue(knext, nxt);
+    f32x16 sc[2];
+    score_unit<D>(cur, qf, rdp, sc);
+    softmax_pv<D>(cur + T::KT_BYTES, sc, acc_o, sm, rdp, hi, min(KU, N - kcur), scale_log2, thr8);
+    kcur = knext;
+  };
+  if (nunits > 0) issue(kcur, st0);
+  int b = 0;
+  for (; b + 2 <= nunits; b += 2) {
     step(b, st0, st1);
-    if (b + 1 < nsel) step(b + 1, st1, st0);
+    step(b + 1, st1, st0);
   }
+  if (b < nunits) step(b, st0, st1);
+  wait_vm<0>();  // no direct load outlives the workgroup
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = sm.l + __shfl_xor(sm.l, 32);
   const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
   if (q < N) {
     const size_t orow = ((size_t)bh * N + q) * D;
@@ -462,43 +661,63 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
 }
 
 // Fused sparse + linear (+ alpha mix) over the CSR row.  2*BQ/32 wavefronts:
-// wavefronts [0, NA) run the softmax attention of 32 queries each, wavefronts
-// [NA, 2 NA) accumulate G = sum phi(K_j)^T V_j over the row's blocks - one of
-// each per SIMD, so G's matrix ops overlap the softmax's vector work.  After
-// the loop the G wavefronts store H_u = H - G (hi + lo bf16) in LDS and the
-// attention wavefronts apply it to phi(Q) and mix the branches.
-template <int D, int BQ, int BK, int MODE>
+// wavefronts [0, NA) run the softmax attention of 32 queries each (the
+// pipelined step above), wavefronts [NA, 2 NA) accumulate G = sum phi(K_j)^T
+// V_j and g = sum of the per-block phi sums over the row's blocks - one of
+// each per SIMD, so G's matrix ops fill the gaps of the softmax.  Two rings of
+// NS LDS tiles: K, and V^T | phi(K)^T | the block's phi sums; step b reads K
+// of unit b+1 and the second ring's tiles of unit b, and issues K of unit b+NS
+// and the second ring's tiles of unit b+NS-1.  After the loop the G
+// wavefronts store H_u = H - G (hi + lo bf16) and z_u = z - g in LDS and the
+// attention wavefronts apply them to phi(Q) and mix the branches.
+template <int D, int BQ, int SUB, int MODE>
 __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
     const uint16_t* __restrict__ pk_g, const float* __restrict__ zblk, const int* __restrict__ row_ptr,
     const int* __restrict__ col_idx, const float* __restrict__ alpha, const float* __restrict__ htot,
     uint16_t* __restrict__ O, int H, int N, int Nq, int Nk, float scale_log2) {
-  using T = Tiles<D, BK>;
+  using T = Tiles<D>;
   constexpr int NA = BQ / 32;                    // attention wavefronts
   constexpr int NWT = 2 * NA;                    // all wavefronts
-  constexpr int STAGE = T::KT_BYTES + 2 * T::VT_BYTES;
-  constexpr int HU = 2 * D * D * 2;
-  constexpr int S0 = STAGE > HU ? STAGE : HU;
-  constexpr bool TWO = S0 + STAGE + D * 4 <= 160 * 1024;   // double-buffer when LDS allows
   constexpr int TT = (D / 32) * (D / 32);
   constexpr int TPW = (TT + NA - 1) / NA;       // G tiles per G wavefront
-  static_assert(T::KT_BYTES % (1024 * NWT) == 0 && T::VT_BYTES % (1024 * NWT) == 0, "tile split");
-  __shared__ __attribute__((aligned(16))) char st0[S0];
-  __shared__ __attribute__((aligned(16))) char st1[TWO ? STAGE : 16];
+  using LP = LoadPlan<D, NWT>;
+  constexpr bool LOADK = MODE != MODE_LINEAR;   // the softmax branch needs K
+  constexpr int KB = LOADK ? T::KT_BYTES : 16;
+  constexpr int OFF_P = T::VT_BYTES;            // phi(K)^T tile
+  constexpr int OFF_Z = 2 * T::VT_BYTES;        // sum of phi(k) over the block's keys
+  constexpr int HU_HALF = D * D * 2;            // H_u^T hi (or lo) part, bf16
+  constexpr int VB = OFF_Z + D * 4 > HU_HALF ? OFF_Z + D * 4 : HU_HALF;
+  constexpr int NS = 3;
+  static_assert(NS * (KB + VB) + D * 4 <= LDS_BYTES, "LDS");
+  // direct loads per unit of each wavefront; the last wavefront also brings
+  // the block's phi sums (D floats, D/64 four-byte loads)
+  constexpr int NL = (LOADK ? LP::NK : 0) + 2 * LP::NV;
+  constexpr int NLZ = NL + D / 64;
+  static_assert((NS - 1) * NLZ < 64, "vmcnt");
+  __shared__ __attribute__((aligned(16))) char k0[KB];
+  __shared__ __attribute__((aligned(16))) char k1[KB];
+  __shared__ __attribute__((aligned(16))) char k2[KB];
+  __shared__ __attribute__((aligned(16))) char v0[VB];
+  __shared__ __attribute__((aligned(16))) char v1[VB];
+  __shared__ __attribute__((aligned(16))) char v2[VB];
   __shared__ float zu[D];
-  char* HuHi = st0;
-  char* HuLo = st0 + D * D * 2;
+  char* HuHi = v0;
+  char* HuLo = v1;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hi = lane >> 5;
   const bool attn_wave = w < NA;
+  const bool zwave = w == NWT - 1;
   const int wr = attn_wave ? w : w - NA;        // index within the role
   const int lb = lane_base(lane);
+  const ReadPlan<D> rdp(lane);
   const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
   const long long bh = row / Nq;
   const int qi = (int)(row % Nq);
   const int h = (int)(bh % H);
-  const size_t npad = (size_t)Nk * BK;
+  const size_t npad = (size_t)Nk * SUB * KU;
   const int base = row_ptr[row];
   const int nsel = row_ptr[row + 1] - base;
   float ws_, wl_;
@@ -511,62 +730,114 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   }
   const bool do_s = ws_ != 0.f;
   const bool lin = (wl_ != 0.f) && (nsel < Nk);
-  const int nblk = (do_s || lin) ? nsel : 0;
+  const int nunits = (do_s || lin) ? nsel * SUB : 0;
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
   const uint16_t* Vtb = vt_g + (size_t)bh * D * npad;
   const uint16_t* Pkb = pk_g + (size_t)bh * D * npad;
+  const float* Zb = zblk + (size_t)bh * Nk * D;
   const float* Hh = htot + (size_t)bh * (D * D + D);
+  const LP lp(w, lane, npad);
+  const auto rk = buf_rsrc(Kb, (uint32_t)((size_t)N * D * 2));
+  const auto rv = buf_rsrc(Vtb, (uint32_t)((size_t)D * npad * 2));
+  const auto rp = buf_rsrc(Pkb, (uint32_t)((size_t)D * npad * 2));
+  const auto rz = buf_rsrc(Zb, (uint32_t)((size_t)Nk * D * 4));
 
-  // The block loop; both roles run it with the same loads and barriers, each
-  // with its own per-block work, so neither role keeps the other's state live.
-  auto run_loop = [&](auto&& work) __attribute__((always_inline)) {
-    auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (TWO && b + 1 < nblk)
-        load_tiles<D, BK, NWT>(Kb, Vtb, Pkb, col_idx[base + b + 1], N, npad, do_s, lin, nxt, w, lane);
-      work(col_idx[base + b], cur);
-      if (!TWO) {
-        __syncthreads();  // the single stage is consumed before it is refilled
-        if (b + 1 < nblk)
-          load_tiles<D, BK, NWT>(Kb, Vtb, Pkb, col_idx[base + b + 1], N, npad, do_s, lin, cur, w, lane);
-      }
-    };
-    if (nblk > 0) load_tiles<D, BK, NWT>(Kb, Vtb, Pkb, col_idx[base], N, npad, do_s, lin, st0, w, lane);
-    if (TWO) {
-      for (int b = 0; b < nblk; b += 2) {
-        step(b, st0, st1);
-        if (b + 1 < nblk) step(b + 1, st1, st0);
-      }
-    } else {
-      for (int b = 0; b < nblk; ++b) step(b, st0, st0);
+  auto ks = [&](int i) -> char* {
+    i %= NS;
+    return i == 0 ? k0 : i == 1 ? k1 : k2;
+  };
+  auto vs = [&](int i) -> char* {
+    i %= NS;
+    return i == 0 ? v0 : i == 1 ? v1 : v2;
+  };
+  // listed block of unit x and its first key (x clamped to the row's last unit)
+  auto blk_of = [&](int x) { return col_idx[base + min(x, nunits - 1) / SUB]; };
+  auto key0 = [&](int x) {
+    const int xc = min(x, nunits - 1);
+    return (col_idx[base + xc / SUB] * SUB + xc % SUB) * KU;
+  };
+  auto issue_k = [&](int x, char* dst) __attribute__((always_inline)) {
+    if (LOADK) lp.load_k(rk, key0(x), dst);
+  };
+  auto issue_v = [&](int x, char* dst) __attribute__((always_inline)) {
+    const int k0x = key0(x);
+    lp.load_t(rv, k0x, dst);
+    lp.load_t(rp, k0x, dst + OFF_P);
+    if (zwave) {
+      const uint32_t zoff = (uint32_t)blk_of(x) * (D * 4);
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c) b2lds4(rz, (uint32_t)(64 * c + lane) * 4, zoff, dst + OFF_Z + 256 * c);
     }
-    __syncthreads();  // every wavefront is done with the loop tiles
   };
 
+  // The unit loop; every wavefront runs it with the same loads and barriers,
+  // each role with its own per-unit work, so neither keeps the other's state.
+  auto run_loop = [&](auto&& prologue_work, auto&& work) __attribute__((always_inline)) {
+    if (nunits > 0) {
+      issue_k(0, k0);
+#pragma unroll
+      for (int i = 1; i < NS; ++i) {
+        issue_k(i, ks(i));
+        issue_v(i - 1, vs(i - 1));
+      }
+      if (zwave) wait_vm<(NS - 1) * NLZ>(); else wait_vm<(NS - 1) * NL>();
+      __syncthreads();
+      prologue_work();
+    }
+    auto step = [&](auto rt, int b) __attribute__((always_inline)) {
+      constexpr int r = decltype(rt)::value;
+      if (zwave) wait_vm<(NS - 2) * NLZ>(); else wait_vm<(NS - 2) * NL>();
+      __syncthreads();
+      const int kc0 = key0(b);
+      issue_k(b + NS, ks(r));
+      issue_v(b + NS - 1, vs(r + NS - 1));
+      work(rt, kc0, ks(r + 1), vs(r));
+    };
+    for (int b = 0; b < nunits; b += 6) {  // unrolled by lcm(NS, 2)
+      step(IntTag<0>{}, b);
+      if (b + 1 < nunits) step(IntTag<1>{}, b + 1);
+      if (b + 2 < nunits) step(IntTag<2>{}, b + 2);
+      if (b + 3 < nunits) step(IntTag<3>{}, b + 3);
+      if (b + 4 < nunits) step(IntTag<4>{}, b + 4);
+      if (b + 5 < nunits) step(IntTag<5>{}, b + 5);
+    }
+    wait_vm<0>();
+    __syncthreads();  // every wavefront is done with the loop tiles
+  };
+  auto no_prologue = [&]() {};
+  auto no_work = [&](auto, int, const char*, const char*) {};
+
   if (!attn_wave) {
-    // ---- G wavefronts: G = sum over listed blocks of phi(K_j)^T V_j
+    // ---- G wavefronts: G = sum over listed blocks of phi(K_j)^T V_j, g = sum of phi sums
     f32x16 acc_g[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) acc_g[t] = f32x16{};
-    run_loop([&](int, const char* cur) __attribute__((always_inline)) {
-      if (!lin) return;
-      const char* Vt = cur + T::KT_BYTES;
-      const char* Pk = cur + T::KT_BYTES + T::VT_BYTES;
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-#pragma unroll
-        for (int u = 0; u < TPW; ++u) {
-          const int tix = wr * TPW + u;
-          if (tix >= TT) continue;
-          const int mt = tix / (D / 32), nt = tix % (D / 32);
-          acc_g[u] = mfma(as_bf16x8(rd16(Pk + s * T::VPB + mt * 1024 + lb)),
-                          as_bf16x8(rd16(Vt + s * T::VPB + nt * 1024 + lb)), acc_g[u]);
-        }
-      }
-    });
+    const int zd = wr * 64 + lane;  // the d of g this lane keeps
+    float gsum = 0.f;
     if (lin) {
+      run_loop(no_prologue, [&](auto rt, int, const char*, const char* cur) __attribute__((always_inline)) {
+        constexpr int r = decltype(rt)::value;
+        const char* Vt = cur;
+        const char* Pk = cur + OFF_P;
+#pragma unroll
+        for (int s = 0; s < KU / 16; ++s) {
+#pragma unroll
+          for (int u = 0; u < TPW; ++u) {
+            const int tix = wr * TPW + u;
+            if (tix >= TT) continue;
+            const int mt = tix / (D / 32), nt = tix % (D / 32);
+            acc_g[u] = mfma(as_bf16x8(rd16(rdp.vp(Pk, mt, s))), as_bf16x8(rd16(rdp.vp(Vt, nt, s))), acc_g[u]);
+          }
+        }
+        // the block's phi sums count once, with its first unit (6 is a multiple of SUB)
+        if (r % SUB == 0 && zd < D) gsum += reinterpret_cast<const float*>(cur + OFF_Z)[zd];
+      });
+    } else {
+      run_loop(no_prologue, no_work);
+    }
+    if (lin) {
+      if (zd < D) zu[zd] = Hh[D * D + zd] - gsum;
       // H_u^T = (H - G)^T as hi + lo bf16 planes (rows d_v, 16-wide d_k slices)
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
@@ -607,28 +878,31 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   f32x16 acc_o[D / 32];
 #pragma unroll
   for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  run_loop([&](int j, const char* cur) __attribute__((always_inline)) {
-    if (!do_s) return;
-    if ((j + 1) * BK > N)
-      attend_block<D, BK, true>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N,
-                                scale_log2);
-    else
-      attend_block<D, BK, false>(cur, cur + T::KT_BYTES, qf, acc_o, m_run, l_run, lb, hi, j * BK, N,
-                                 scale_log2);
-  });
-  if (lin) {
-    if (tid < D) {
-      float g = 0.f;
-      for (int b = 0; b < nsel; ++b) g += zblk[((size_t)bh * Nk + col_idx[base + b]) * D + tid];
-      zu[tid] = Hh[D * D + tid] - g;
-    }
-    __syncthreads();  // H_u^T and z_u complete
+  Softmax sm;
+  const float thr8 = 8.f / scale_log2;
+  if (do_s) {
+    f32x16 s0[2], s1[2];
+    run_loop(
+        [&]() __attribute__((always_inline)) {
+          s0[0] = score_subtile<D>(k0, 0, qf, rdp);
+          s0[1] = score_subtile<D>(k0, 1, qf, rdp);
+        },
+        [&](auto rt, int kc0, const char* kn, const char* cur) __attribute__((always_inline)) {
+          constexpr int r = decltype(rt)::value;
+          const int lim = min(KU, N - kc0);
+          if (r % 2 == 0)
+            attend_step<D>(kn, cur, qf, s0, s1, acc_o, sm, rdp, hi, lim, scale_log2, thr8);
+          else
+            attend_step<D>(kn, cur, qf, s1, s0, acc_o, sm, rdp, hi, lim, scale_log2, thr8);
+        });
+  } else {
+    run_loop(no_prologue, no_work);
   }
+  if (lin) __syncthreads();  // H_u^T and z_u complete
 
   float inv_l = 0.f;
   if (do_s) {
-    const float lt = l_run + __shfl_xor(l_run, 32);
+    const float lt = sm.l + __shfl_xor(sm.l, 32);
     inv_l = lt > 0.f ? 1.f / lt : 0.f;
   }
   f32x16 acc_n[D / 32];
@@ -732,7 +1006,7 @@ hipError_t prep_dispatch(const Shape& s, bool lin, const void* K, const void* V,
                                reinterpret_cast<float*>(ws + L.htot), st);
 }
 
-template <int D, int BQ, int BK>
+template <int D, int BQ, int SUB>
 hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K, const int32_t* rp,
                          const int32_t* ci, const float* alpha, const char* ws, const WsLayout& L,
                          void* O, hipStream_t st) {
@@ -747,19 +1021,19 @@ hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K
   const dim3 grid((unsigned)s.R());
   switch (mode) {
     case MODE_SPARSE:
-      hipLaunchKernelGGL((attn_kernel<D, BQ, BK, MODE_SPARSE>), grid, dim3(BQ / 32 * 64), 0, st, q, k, vt,
+      hipLaunchKernelGGL((attn_kernel<D, BQ, SUB, MODE_SPARSE>), grid, dim3(BQ / 32 * 64), 0, st, q, k, vt,
                          rp, ci, o, s.N, s.Nq, s.Nk, sl2);
       break;
     case MODE_DENSE:
-      hipLaunchKernelGGL((attn_kernel<D, BQ, BK, MODE_DENSE>), grid, dim3(BQ / 32 * 64), 0, st, q, k, vt,
+      hipLaunchKernelGGL((attn_kernel<D, BQ, SUB, MODE_DENSE>), grid, dim3(BQ / 32 * 64), 0, st, q, k, vt,
                          rp, ci, o, s.N, s.Nq, s.Nk, sl2);
       break;
     case MODE_LINEAR:
-      hipLaunchKernelGGL((fused_kernel<D, BQ, BK, MODE_LINEAR>), grid, dim3(BQ / 32 * 128), 0, st, q, k,
+      hipLaunchKernelGGL((fused_kernel<D, BQ, SUB, MODE_LINEAR>), grid, dim3(BQ / 32 * 128), 0, st, q, k,
                          vt, pk, zb, rp, ci, alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2);
       break;
     default:
-      hipLaunchKernelGGL((fused_kernel<D, BQ, BK, MODE_FUSED>), grid, dim3(BQ / 32 * 128), 0, st, q, k,
+      hipLaunchKernelGGL((fused_kernel<D, BQ, SUB, MODE_FUSED>), grid, dim3(BQ / 32 * 128), 0, st, q, k,
                          vt, pk, zb, rp, ci, alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2);
       break;
   }
@@ -782,7 +1056,7 @@ hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void
                             const WsLayout& L, void* O, hipStream_t st) {
 #define SLA_ATTN(DD, QQ, KK)                                                  \
   if (s.d == DD && s.bq == QQ && s.bk == KK)                                  \
-    return attn_dispatch<DD, QQ, KK>(s, mode, Q, K, rp, ci, alpha, ws, L, O, st);
+    return attn_dispatch<DD, QQ, KK / 64>(s, mode, Q, K, rp, ci, alpha, ws, L, O, st);
   SLA_ATTN(128, 128, 64)
   SLA_ATTN(128, 128, 128)
   SLA_ATTN(128, 64, 64)
