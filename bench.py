@@ -195,7 +195,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": fused_flops / (st_fused * 1e-3) / 1e12,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": fused_flops / (st_fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic(), "kernel": "attn_kernel<128,128,64,FUSED>",
+                     "traffic": stored_traffic(), "kernel": f"fused_kernel<d={wl.d},bq={wl.bq},bk={wl.bk}>",
                      "flops_per_launch": fused_flops, "ms_per_launch": st_fused},
         "mask_roofline": {"bound": "hbm", "achieved": mask_bytes / (st_mask * 1e-3) / 1e9,
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
