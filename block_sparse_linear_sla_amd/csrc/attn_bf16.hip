@@ -423,75 +423,6 @@ __device__ __forceinline__ void score_unit(const char* Ks, const bf16x8 (&qf)[D 
   __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
 }
 
-// S^T subtile kt (32 keys x 32 queries) of the unit whose K tile is Ks.
-template <int D>
-__device__ __forceinline__ f32x16 score_subtile(const char* Ks, int kt, const bf16x8 (&qf)[D / 16],
-                                                const ReadPlan<D>& rp) {
-  f32x16 s = f32x16{};
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) s = mfma(as_bf16x8(rd16(rp.kp(Ks, kt, t))), qf[t], s);
-  return s;
-}
-
-// One software-pipelined step of an attention wavefront (32 queries): the
-// scores of the next unit, sn = K_next Q^T, are computed while the current
-// unit's scores sc go through the online softmax and O^T += V_cur^T P^T, so
-// the matrix cores work on one unit while the vector ALU works on the other.
-// Softmax: one max exchange and rescale test per 64 keys; P = exp2(S c - m c)
-// with c = log2(e)/sqrt(d), rounded to bf16; l += sum of the rounded P (v_dot2
-// with ones).  The running max moves only when a unit max exceeds it by more
-// than 2^8 in exp2 units, so P <= 2^8 and the O / l rescale is skipped for
-// most units.  lim < 64 marks a unit running past N: keys at offset >= lim get
-// score -inf.
-template <int D>
-__device__ __forceinline__ void attend_step(const char* Kn, const char* Vc, const bf16x8 (&qf)[D / 16],
-                                            f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&acc_o)[D / 32],
-                                            Softmax& sm, const ReadPlan<D>& rp, int hi, int lim,
-                                            float scale_log2, float thr8) {
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  if (lim < KU) {
-    const int limh = lim - 4 * hi;  // key offset of element i of subtile h2: 32 h2 + 8 (i/4) + 4 hi + i%4
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * h2 + 8 * (i >> 2) + (i & 3) >= limh) sc[h2][i] = -INFINITY;
-  }
-  sn[0] = score_subtile<D>(Kn, 0, qf, rp);
-  float mx = __builtin_elementwise_maximum(sc[0][0], sc[1][0]);
-#pragma unroll
-  for (int i = 1; i < 16; ++i)
-    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[0][i]), sc[1][i]);
-  mx = pair_max(mx);
-  if (__ballot(mx > sm.thr)) {
-    const float m_new = fmaxf(sm.m, mx);
-    const float corr = __builtin_amdgcn_exp2f((sm.m - m_new) * scale_log2);
-    sm.l *= corr;
-#pragma unroll
-    for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
-    sm.m = m_new;
-    sm.mneg = -m_new * scale_log2;
-    sm.thr = m_new + thr8;
-  }
-  sn[1] = score_subtile<D>(Kn, 1, qf, rp);
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-    const int h2 = s4 >> 1, s = s4 & 1;
-    uint32_t pw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[h2][8 * s + 2 * e], scale_log2, sm.mneg));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[h2][8 * s + 2 * e + 1], scale_log2, sm.mneg));
-      pw[e] = pk_bf16(p0, p1);
-      sm.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, sm.l, false);
-    }
-    const bf16x8 bp = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-      acc_o[dt] = mfma(as_bf16x8(rd16(rp.vp(Vc, dt, s4))), bp, acc_o[dt]);
-  }
-}
-
 // Q fragments of 32 query rows (B operand of S^T = K Q^T), zero past N.
 template <int D>
 __device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, int N, int hi,
@@ -505,7 +436,12 @@ __device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, i
 }
 
 // Second half of a unit for one attention wavefront: the online softmax of
-// its scores sc and O^T += V^T P^T (see attend_step for the arithmetic).
+// its scores sc (two 32-key subtiles) and O^T += V^T P^T.  One max exchange
+// and rescale test per 64 keys; P = exp2(S c - m c) with c = log2(e)/sqrt(d),
+// rounded to bf16; l += sum of the rounded P (v_dot2 with ones).  The running
+// max moves only when a unit max exceeds it by more than 2^8 in exp2 units,
+// so P <= 2^8 and the O / l rescale is skipped for most units.  lim < 64
+// marks a unit running past N: keys at offset >= lim get score -inf.
 template <int D>
 __device__ __forceinline__ void softmax_pv(const char* Vc, f32x16 (&sc)[2], f32x16 (&acc_o)[D / 32],
                                            Softmax& sm, const ReadPlan<D>& rp, int hi, int lim,
@@ -660,16 +596,131 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
   }
 }
 
-// Fused sparse + linear (+ alpha mix) over the CSR row.  2*BQ/32 wavefronts:
-// wavefronts [0, NA) run the softmax attention of 32 queries each (the
-// pipelined step above), wavefronts [NA, 2 NA) accumulate G = sum phi(K_j)^T
-// V_j and g = sum of the per-block phi sums over the row's blocks - one of
-// each per SIMD, so G's matrix ops fill the gaps of the softmax.  Two rings of
-// NS LDS tiles: K, and V^T | phi(K)^T | the block's phi sums; step b reads K
-// of unit b+1 and the second ring's tiles of unit b, and issues K of unit b+NS
-// and the second ring's tiles of unit b+NS-1.  After the loop the G
-// wavefronts store H_u = H - G (hi + lo bf16) and z_u = z - g in LDS and the
-// attention wavefronts apply them to phi(Q) and mix the branches.
+// S^T of the 32-key half KT of a unit (K tile Ks), K fragments read four
+// MFMAs ahead (order pinned as in score_unit).
+template <int D, int KT>
+__device__ __forceinline__ f32x16 score_half(const char* Ks, const bf16x8 (&qf)[D / 16], const ReadPlan<D>& rp) {
+  constexpr int NT = D / 16;
+  constexpr int PF = 4;
+  uint4 fr[PF];
+#pragma unroll
+  for (int i = 0; i < PF; ++i) fr[i] = rd16(rp.kp(Ks, KT, i));
+  f32x16 s = f32x16{};
+#pragma unroll
+  for (int i = 0; i < NT; ++i) {
+    const uint4 a = fr[i % PF];
+    if (i + PF < NT) fr[i % PF] = rd16(rp.kp(Ks, KT, i + PF));
+    s = mfma(as_bf16x8(a), qf[i], s);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+  for (int i = 0; i + PF < NT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  return s;
+}
+
+// G tiles of one wavefront in the fused kernel: TPW 32 x 32 tiles of the D x D
+// product phi(K)^T V; tile u is (row tile mt, column tile nt).  When a
+// wavefront has at least a full row of tiles the column tile is a constant.
+template <int D, int TPW>
+struct GTiles {
+  static constexpr int NCT = D / 32;                    // column tiles per row
+  __device__ static int mt(int wq, int u) { return (wq * TPW + u) / NCT; }
+  __device__ static int nt(int wq, int u) { return TPW >= NCT ? u % NCT : (wq * TPW + u) % NCT; }
+};
+
+// B operand of a G tile: the V^T fragment of column tile nt (a register array
+// index, so a constant nt folds and a wave-uniform one selects).
+template <int D>
+__device__ __forceinline__ uint4 pick_frag(const uint4 (&vf)[D / 32], int nt) {
+  uint4 b = vf[0];
+#pragma unroll
+  for (int c = 1; c < D / 32; ++c)
+    if (nt == c) b = vf[c];
+  return b;
+}
+
+// One fused-kernel wavefront's share of a unit: keys [32 KT, 32 KT + 32),
+// i.e. key planes 2 KT and 2 KT + 1 of the V^T / phi(K)^T tiles.
+//   DO_S: online softmax of its scores sc (lim = keys of the unit below N)
+//         and O^T += V^T P^T, as in softmax_pv but over 32 keys;
+//   DO_G: G += phi(K)^T V for its G tiles; the V^T fragments read for the
+//         P V product serve as the B operand, and these matrix ops do not
+//         wait for the softmax.
+template <int D, int TPW, int KT, bool DO_S, bool DO_G>
+__device__ __forceinline__ void fused_half(const char* Vt, const char* Pk, f32x16& sc, f32x16 (&acc_o)[D / 32],
+                                           Softmax& sm, f32x16 (&acc_g)[TPW], const ReadPlan<D>& rp, int wq,
+                                           int hi, int lim, float scale_log2, float thr8) {
+  using GT = GTiles<D, TPW>;
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  uint4 vf[2][D / 32];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) vf[j][dt] = rd16(rp.vp(Vt, dt, 2 * KT + j));
+  if (DO_G) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const uint4 a = rd16(rp.vp(Pk, GT::mt(wq, u), 2 * KT + j));
+        acc_g[u] = mfma(as_bf16x8(a), as_bf16x8(pick_frag<D>(vf[j], GT::nt(wq, u))), acc_g[u]);
+      }
+  }
+  if (!DO_S) return;
+  if (lim < 32 * KT + 32) {
+    const int limh = lim - 32 * KT - 4 * hi;  // key offset of element i: 32 KT + 8 (i/4) + 4 hi + i%4
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) >= limh) sc[i] = -INFINITY;
+  }
+  float mx = __builtin_elementwise_maximum(sc[0], sc[1]);
+#pragma unroll
+  for (int i = 2; i < 16; i += 2)
+    mx = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mx, sc[i]), sc[i + 1]);
+  mx = pair_max(mx);
+  if (__ballot(mx > sm.thr)) {
+    const float m_new = fmaxf(sm.m, mx);
+    const float corr = __builtin_amdgcn_exp2f((sm.m - m_new) * scale_log2);
+    sm.l *= corr;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc_o[t] *= corr;
+    sm.m = m_new;
+    sm.mneg = -m_new * scale_log2;
+    sm.thr = m_new + thr8;
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[8 * j + 2 * e], scale_log2, sm.mneg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[8 * j + 2 * e + 1], scale_log2, sm.mneg));
+      pw[e] = pk_bf16(p0, p1);
+      sm.l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pw[e]), ones, sm.l, false);
+    }
+    const bf16x8 bp = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] = mfma(as_bf16x8(vf[j][dt]), bp, acc_o[dt]);
+  }
+}
+
+// Fused sparse + linear (+ alpha mix) over the CSR row.  2*BQ/32 wavefronts in
+// two groups; wavefront i of either group owns queries [32 i, 32 i + 32) of
+// the query block, and group g takes keys [32 g, 32 g + 32) of every 64-key
+// unit of the row: its half of S = K Q^T, the online softmax over those keys
+// with O^T += V^T P^T, and its share of G = sum phi(K)^T V over them (the
+// V^T fragments of P V reused as the B operand, one phi(K)^T read per key
+// plane).  Units stream through a ring of NS LDS stages (K | V^T | phi(K)^T |
+// the block's phi sums; distinct arrays, loop unrolled by NS), NS-1 units
+// ahead.  Afterwards the two wavefronts of a query slice swap halves of their
+// partials through LDS: each merges the two softmax partials over half of the
+// d range and sums the two G partials over half of its G tiles; the G halves
+// become H_u = H - G (hi + lo bf16) in LDS, and each wavefront applies H_u to
+// phi(Q) for its half of d and mixes the branches into the output.
 template <int D, int BQ, int SUB, int MODE>
 __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
@@ -677,40 +728,45 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
     const int* __restrict__ col_idx, const float* __restrict__ alpha, const float* __restrict__ htot,
     uint16_t* __restrict__ O, int H, int N, int Nq, int Nk, float scale_log2) {
   using T = Tiles<D>;
-  constexpr int NA = BQ / 32;                    // attention wavefronts
+  constexpr int NA = BQ / 32;                    // wavefronts per group
   constexpr int NWT = 2 * NA;                    // all wavefronts
-  constexpr int TT = (D / 32) * (D / 32);
-  constexpr int TPW = (TT + NA - 1) / NA;       // G tiles per G wavefront
+  constexpr int TT = (D / 32) * (D / 32);        // G tiles
+  constexpr int TPW = TT / NA;                   // G tiles per wavefront (each group covers all)
+  static_assert(TPW * NA == TT, "G tiles split");
+  using GT = GTiles<D, TPW>;
   using LP = LoadPlan<D, NWT>;
-  constexpr bool LOADK = MODE != MODE_LINEAR;   // the softmax branch needs K
-  constexpr int KB = LOADK ? T::KT_BYTES : 16;
-  constexpr int OFF_P = T::VT_BYTES;            // phi(K)^T tile
-  constexpr int OFF_Z = 2 * T::VT_BYTES;        // sum of phi(k) over the block's keys
-  constexpr int HU_HALF = D * D * 2;            // H_u^T hi (or lo) part, bf16
-  constexpr int VB = OFF_Z + D * 4 > HU_HALF ? OFF_Z + D * 4 : HU_HALF;
+  constexpr bool LOADK = MODE != MODE_LINEAR;    // the softmax branch needs K
+  constexpr int OFF_V = LOADK ? T::KT_BYTES : 0; // V^T tile
+  constexpr int OFF_P = OFF_V + T::VT_BYTES;     // phi(K)^T tile
+  constexpr int OFF_Z = OFF_P + T::VT_BYTES;     // sum of phi(k) over the block's keys
+  constexpr int STAGE = OFF_Z + D * 4;
+  constexpr int HU_HALF = D * D * 2;             // H_u^T hi (or lo) part, bf16
   constexpr int NS = 3;
-  static_assert(NS * (KB + VB) + D * 4 <= LDS_BYTES, "LDS");
+  // epilogue exchange areas: softmax halves in stages 0 / 1, G halves in stage 2
+  constexpr int SXB = ((D / 64) * 16 + 2) * 64 * 4;           // one softmax half (O tiles + m, l)
+  constexpr int PPS = STAGE / (2 * SXB);                      // query slices per stage
+  constexpr int GXT = TPW >= 2 ? TPW / 2 : 1;                  // G tiles sent per wavefront
+  constexpr int GXB = GXT * 16 * 64 * 2;                      // their bf16 bytes
+  static_assert(NS * STAGE + D * 4 <= LDS_BYTES, "LDS");
+  static_assert(HU_HALF <= STAGE && NA * 2 * GXB <= STAGE && (!LOADK || (PPS >= 1 && 2 * PPS >= NA)),
+                "epilogue areas");
   // direct loads per unit of each wavefront; the last wavefront also brings
   // the block's phi sums (D floats, D/64 four-byte loads)
   constexpr int NL = (LOADK ? LP::NK : 0) + 2 * LP::NV;
   constexpr int NLZ = NL + D / 64;
   static_assert((NS - 1) * NLZ < 64, "vmcnt");
-  __shared__ __attribute__((aligned(16))) char k0[KB];
-  __shared__ __attribute__((aligned(16))) char k1[KB];
-  __shared__ __attribute__((aligned(16))) char k2[KB];
-  __shared__ __attribute__((aligned(16))) char v0[VB];
-  __shared__ __attribute__((aligned(16))) char v1[VB];
-  __shared__ __attribute__((aligned(16))) char v2[VB];
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[STAGE];
   __shared__ float zu[D];
-  char* HuHi = v0;
-  char* HuLo = v1;
+  char* HuHi = st0;
+  char* HuLo = st1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = w / NA, wq = w % NA;
   const int l32 = lane & 31, hi = lane >> 5;
-  const bool attn_wave = w < NA;
   const bool zwave = w == NWT - 1;
-  const int wr = attn_wave ? w : w - NA;        // index within the role
   const int lb = lane_base(lane);
   const ReadPlan<D> rdp(lane);
   const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
@@ -743,13 +799,9 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   const auto rp = buf_rsrc(Pkb, (uint32_t)((size_t)D * npad * 2));
   const auto rz = buf_rsrc(Zb, (uint32_t)((size_t)Nk * D * 4));
 
-  auto ks = [&](int i) -> char* {
+  auto stage = [&](int i) -> char* {
     i %= NS;
-    return i == 0 ? k0 : i == 1 ? k1 : k2;
-  };
-  auto vs = [&](int i) -> char* {
-    i %= NS;
-    return i == 0 ? v0 : i == 1 ? v1 : v2;
+    return i == 0 ? st0 : i == 1 ? st1 : st2;
   };
   // listed block of unit x and its first key (x clamped to the row's last unit)
   auto blk_of = [&](int x) { return col_idx[base + min(x, nunits - 1) / SUB]; };
@@ -757,160 +809,189 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
     const int xc = min(x, nunits - 1);
     return (col_idx[base + xc / SUB] * SUB + xc % SUB) * KU;
   };
-  auto issue_k = [&](int x, char* dst) __attribute__((always_inline)) {
-    if (LOADK) lp.load_k(rk, key0(x), dst);
-  };
-  auto issue_v = [&](int x, char* dst) __attribute__((always_inline)) {
+  auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
     const int k0x = key0(x);
-    lp.load_t(rv, k0x, dst);
-    lp.load_t(rp, k0x, dst + OFF_P);
+    if (LOADK) lp.load_k(rk, k0x, sb);
+    lp.load_t(rv, k0x, sb + OFF_V);
+    lp.load_t(rp, k0x, sb + OFF_P);
     if (zwave) {
       const uint32_t zoff = (uint32_t)blk_of(x) * (D * 4);
 #pragma unroll
-      for (int c = 0; c < D / 64; ++c) b2lds4(rz, (uint32_t)(64 * c + lane) * 4, zoff, dst + OFF_Z + 256 * c);
+      for (int c = 0; c < D / 64; ++c) b2lds4(rz, (uint32_t)(64 * c + lane) * 4, zoff, sb + OFF_Z + 256 * c);
     }
   };
 
-  // The unit loop; every wavefront runs it with the same loads and barriers,
-  // each role with its own per-unit work, so neither keeps the other's state.
-  auto run_loop = [&](auto&& prologue_work, auto&& work) __attribute__((always_inline)) {
-    if (nunits > 0) {
-      issue_k(0, k0);
+  // per-wavefront state
+  const int q = qi * BQ + 32 * wq + l32;
+  bf16x8 qf[D / 16];
+  load_q<D>(Q, bh, q, N, hi, qf);
+  f32x16 acc_o[D / 32], acc_g[TPW];
 #pragma unroll
-      for (int i = 1; i < NS; ++i) {
-        issue_k(i, ks(i));
-        issue_v(i - 1, vs(i - 1));
-      }
-      if (zwave) wait_vm<(NS - 1) * NLZ>(); else wait_vm<(NS - 1) * NL>();
-      __syncthreads();
-      prologue_work();
+  for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) acc_g[t] = f32x16{};
+  Softmax sm;
+  const float thr8 = 8.f / scale_log2;
+  const int zd = wq * 64 + lane;  // group 0: the d of g this lane keeps
+  float gsum = 0.f;
+
+  // The unit loop: every wavefront issues its share of the loads and passes
+  // the same barriers; work(I, b, cur) is the per-unit computation.
+  auto run_loop = [&](auto&& work) __attribute__((always_inline)) {
+    if (nunits > 0) {
+#pragma unroll
+      for (int i = 0; i < NS - 1; ++i) issue(i, stage(i));
     }
     auto step = [&](auto rt, int b) __attribute__((always_inline)) {
       constexpr int r = decltype(rt)::value;
-      if (zwave) wait_vm<(NS - 2) * NLZ>(); else wait_vm<(NS - 2) * NL>();
+      if (b + 1 < nunits) {
+        if (zwave) wait_vm<(NS - 2) * NLZ>(); else wait_vm<(NS - 2) * NL>();
+      } else {
+        wait_vm<0>();
+      }
       __syncthreads();
-      const int kc0 = key0(b);
-      issue_k(b + NS, ks(r));
-      issue_v(b + NS - 1, vs(r + NS - 1));
-      work(rt, kc0, ks(r + 1), vs(r));
+      if (b + NS - 1 < nunits) issue(b + NS - 1, stage(r + NS - 1));
+      work(rt, b, stage(r));
     };
-    for (int b = 0; b < nunits; b += 6) {  // unrolled by lcm(NS, 2)
+    for (int b = 0; b < nunits; b += NS) {
       step(IntTag<0>{}, b);
       if (b + 1 < nunits) step(IntTag<1>{}, b + 1);
       if (b + 2 < nunits) step(IntTag<2>{}, b + 2);
-      if (b + 3 < nunits) step(IntTag<3>{}, b + 3);
-      if (b + 4 < nunits) step(IntTag<4>{}, b + 4);
-      if (b + 5 < nunits) step(IntTag<5>{}, b + 5);
     }
-    wait_vm<0>();
     __syncthreads();  // every wavefront is done with the loop tiles
   };
-  auto no_prologue = [&]() {};
-  auto no_work = [&](auto, int, const char*, const char*) {};
+  // per-unit work of group KT with the branch flags known
+  auto make_work = [&](auto kt_tag, auto s_tag, auto g_tag) {
+    constexpr int KT_ = decltype(kt_tag)::value;
+    constexpr bool S_ = decltype(s_tag)::value != 0, G_ = decltype(g_tag)::value != 0;
+    return [&](auto rt, int b, const char* cur) __attribute__((always_inline)) {
+      constexpr int r = decltype(rt)::value;
+      f32x16 sc;
+      if (S_) sc = score_half<D, KT_>(cur, qf, rdp);
+      const int lim = S_ ? min(KU, N - key0(b)) : KU;
+      fused_half<D, TPW, KT_, S_, G_>(cur + OFF_V, cur + OFF_P, sc, acc_o, sm, acc_g, rdp, wq, hi, lim,
+                                       scale_log2, thr8);
+      // the block's phi sums count once: group 0, first unit of the block (3 is a multiple of SUB
+      // or SUB is 1... the unit index b decides)
+      if (G_ && KT_ == 0 && zd < D && (b % SUB) == 0) gsum += reinterpret_cast<const float*>(cur + OFF_Z)[zd];
+      (void)r;
+    };
+  };
+  // the whole per-wavefront program, with the group index G as a constant
+  auto body = [&](auto g_tag) __attribute__((always_inline)) {
+  constexpr int G = decltype(g_tag)::value;
+  if (do_s && lin) run_loop(make_work(g_tag, IntTag<1>{}, IntTag<1>{}));
+  else if (do_s) run_loop(make_work(g_tag, IntTag<1>{}, IntTag<0>{}));
+  else if (lin) run_loop(make_work(g_tag, IntTag<0>{}, IntTag<1>{}));
+  else run_loop(make_work(g_tag, IntTag<0>{}, IntTag<0>{}));
 
-  if (!attn_wave) {
-    // ---- G wavefronts: G = sum over listed blocks of phi(K_j)^T V_j, g = sum of phi sums
-    f32x16 acc_g[TPW];
+  // ---- epilogue: swap halves of the partials within each query slice
+  constexpr int HT = D / 64;  // O tiles per half of d
+  constexpr int own0 = G * HT;  // first O tile this wavefront finishes
+  {
+    char* sx = (wq / PPS == 0 ? st0 : st1) + (wq % PPS) * 2 * SXB;
+    float* mine = reinterpret_cast<float*>(sx + G * SXB);        // written by this wavefront
+    uint16_t* gx = reinterpret_cast<uint16_t*>(st2 + wq * 2 * GXB + G * GXB);
+    if (LOADK) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) acc_g[t] = f32x16{};
-    const int zd = wr * 64 + lane;  // the d of g this lane keeps
-    float gsum = 0.f;
-    if (lin) {
-      run_loop(no_prologue, [&](auto rt, int, const char*, const char* cur) __attribute__((always_inline)) {
-        constexpr int r = decltype(rt)::value;
-        const char* Vt = cur;
-        const char* Pk = cur + OFF_P;
+      for (int t = 0; t < HT; ++t)
 #pragma unroll
-        for (int s = 0; s < KU / 16; ++s) {
-#pragma unroll
-          for (int u = 0; u < TPW; ++u) {
-            const int tix = wr * TPW + u;
-            if (tix >= TT) continue;
-            const int mt = tix / (D / 32), nt = tix % (D / 32);
-            acc_g[u] = mfma(as_bf16x8(rd16(rdp.vp(Pk, mt, s))), as_bf16x8(rd16(rdp.vp(Vt, nt, s))), acc_g[u]);
-          }
-        }
-        // the block's phi sums count once, with its first unit (6 is a multiple of SUB)
-        if (r % SUB == 0 && zd < D) gsum += reinterpret_cast<const float*>(cur + OFF_Z)[zd];
-      });
-    } else {
-      run_loop(no_prologue, no_work);
+        for (int e = 0; e < 16; ++e) mine[(16 * t + e) * 64 + lane] = acc_o[(1 - G) * HT + t][e];
+      mine[16 * HT * 64 + lane] = sm.m;
+      mine[16 * HT * 64 + 64 + lane] = sm.l;
     }
-    if (lin) {
-      if (zd < D) zu[zd] = Hh[D * D + zd] - gsum;
-      // H_u^T = (H - G)^T as hi + lo bf16 planes (rows d_v, 16-wide d_k slices)
+    if (lin && (TPW >= 2 || G == 1)) {
+      const int u0 = TPW >= 2 ? (1 - G) * GXT : 0;  // first G tile the partner finishes
 #pragma unroll
-      for (int u = 0; u < TPW; ++u) {
-        const int tix = wr * TPW + u;
-        if (tix >= TT) continue;
-        const int mt = tix / (D / 32), nt = tix % (D / 32);
-        const int dv = 32 * nt + l32;
+      for (int t = 0; t < GXT; ++t)
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int dk = 32 * mt + 8 * i4 + 4 * hi;
-          float hv[4], lv[4];
-          uint32_t hb[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            hv[r] = Hh[(dk + r) * D + dv] - acc_g[u][4 * i4 + r];
-            hb[r] = pk_bf16(hv[r], 0.f) & 0xffffu;
-            lv[r] = hv[r] - bf2f(hb[r]);
-          }
-          const int off = (dk >> 4) * T::HPB + dv * 32 + 16 * (((dk >> 3) & 1) ^ ((dv >> 3) & 1)) + 8 * hi;
-          uint2 wv;
-          wv.x = hb[0] | (hb[1] << 16);
-          wv.y = hb[2] | (hb[3] << 16);
-          *reinterpret_cast<uint2*>(HuHi + off) = wv;
-          wv.x = pk_bf16(lv[0], lv[1]);
-          wv.y = pk_bf16(lv[2], lv[3]);
-          *reinterpret_cast<uint2*>(HuLo + off) = wv;
-        }
+        for (int e = 0; e < 16; e += 2)
+          *reinterpret_cast<uint32_t*>(gx + ((16 * t + e) * 64 + 2 * lane)) =
+              pk_bf16(acc_g[u0 + t][e], acc_g[u0 + t][e + 1]);
+    }
+  }
+  __syncthreads();
+  float m_all, l_all;
+  {
+    const char* sx = (wq / PPS == 0 ? st0 : st1) + (wq % PPS) * 2 * SXB;
+    const float* theirs = reinterpret_cast<const float*>(sx + (1 - G) * SXB);
+    const uint16_t* gx = reinterpret_cast<const uint16_t*>(st2 + wq * 2 * GXB + (1 - G) * GXB);
+    l_all = 0.f;
+    m_all = -INFINITY;
+    if (LOADK) {
+      const float m1 = theirs[16 * HT * 64 + lane], l1 = theirs[16 * HT * 64 + 64 + lane];
+      const float m = fmaxf(sm.m, m1);
+      float c0 = 0.f, c1 = 0.f;
+      if (m != -INFINITY) {
+        c0 = __builtin_amdgcn_exp2f((sm.m - m) * scale_log2);
+        c1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
       }
-      __syncthreads();  // H_u^T and z_u complete
-    }
-    return;
-  }
-
-  // ---- attention wavefronts
-  const int q = qi * BQ + 32 * wr + l32;
-  bf16x8 qf[D / 16];
-  load_q<D>(Q, bh, q, N, hi, qf);
-  f32x16 acc_o[D / 32];
+      l_all = sm.l * c0 + l1 * c1;
+      m_all = m;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
-  Softmax sm;
-  const float thr8 = 8.f / scale_log2;
-  if (do_s) {
-    f32x16 s0[2], s1[2];
-    run_loop(
-        [&]() __attribute__((always_inline)) {
-          s0[0] = score_subtile<D>(k0, 0, qf, rdp);
-          s0[1] = score_subtile<D>(k0, 1, qf, rdp);
-        },
-        [&](auto rt, int kc0, const char* kn, const char* cur) __attribute__((always_inline)) {
-          constexpr int r = decltype(rt)::value;
-          const int lim = min(KU, N - kc0);
-          if (r % 2 == 0)
-            attend_step<D>(kn, cur, qf, s0, s1, acc_o, sm, rdp, hi, lim, scale_log2, thr8);
-          else
-            attend_step<D>(kn, cur, qf, s1, s0, acc_o, sm, rdp, hi, lim, scale_log2, thr8);
-        });
-  } else {
-    run_loop(no_prologue, no_work);
+      for (int t = 0; t < HT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          acc_o[own0 + t][e] = acc_o[own0 + t][e] * c0 + theirs[(16 * t + e) * 64 + lane] * c1;
+    }
+    if (lin && (TPW >= 2 || G == 0)) {
+      const int u0 = TPW >= 2 ? G * GXT : 0;
+#pragma unroll
+      for (int t = 0; t < GXT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const uint32_t pr = *reinterpret_cast<const uint32_t*>(gx + ((16 * t + e) * 64 + 2 * lane));
+          acc_g[u0 + t][e] += bf2f(pr & 0xffffu);
+          acc_g[u0 + t][e + 1] += bf2f(pr >> 16);
+        }
+    }
   }
-  if (lin) __syncthreads();  // H_u^T and z_u complete
+  (void)m_all;
+  __syncthreads();  // exchange areas read; stages 0 / 1 take H_u
+  if (lin) {
+    if (G == 0 && zd < D) zu[zd] = Hh[D * D + zd] - gsum;
+    // H_u^T = (H - G)^T as hi + lo bf16 planes (rows d_v, 16-wide d_k slices)
+#pragma unroll
+    for (int t = 0; t < GXT; ++t) {
+      if (TPW < 2 && G != 0) break;
+      const int u = TPW >= 2 ? G * GXT + t : 0;
+      const int mt = GT::mt(wq, u), nt = GT::nt(wq, u);
+      const int dv = 32 * nt + l32;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int dk = 32 * mt + 8 * i4 + 4 * hi;
+        float hv[4], lv[4];
+        uint32_t hb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          hv[r] = Hh[(dk + r) * D + dv] - acc_g[u][4 * i4 + r];
+          hb[r] = pk_bf16(hv[r], 0.f) & 0xffffu;
+          lv[r] = hv[r] - bf2f(hb[r]);
+        }
+        const int off = (dk >> 4) * T::HPB + dv * 32 + 16 * (((dk >> 3) & 1) ^ ((dv >> 3) & 1)) + 8 * hi;
+        uint2 wv;
+        wv.x = hb[0] | (hb[1] << 16);
+        wv.y = hb[2] | (hb[3] << 16);
+        *reinterpret_cast<uint2*>(HuHi + off) = wv;
+        wv.x = pk_bf16(lv[0], lv[1]);
+        wv.y = pk_bf16(lv[2], lv[3]);
+        *reinterpret_cast<uint2*>(HuLo + off) = wv;
+      }
+    }
+    __syncthreads();  // H_u^T and z_u complete
+  }
 
   float inv_l = 0.f;
   if (do_s) {
-    const float lt = sm.l + __shfl_xor(sm.l, 32);
+    const float lt = l_all + __shfl_xor(l_all, 32);
     inv_l = lt > 0.f ? 1.f / lt : 0.f;
   }
-  f32x16 acc_n[D / 32];
+  f32x16 acc_n[HT];
 #pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) acc_n[mt] = f32x16{};
+  for (int t = 0; t < HT; ++t) acc_n[t] = f32x16{};
   float den = 1.f;
   if (lin) {
-    // num^T = H_u^T phi(Q)^T with phi(Q) split into hi + lo once per k-step
+    // num^T = H_u^T phi(Q)^T over this wavefront's half of d, phi(Q) split into hi + lo
     float dpart = 0.f;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
@@ -929,9 +1010,9 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
       const bf16x8 bl4 = as_bf16x8(make_uint4(pk_bf16(fl[0], fl[1]), pk_bf16(fl[2], fl[3]),
                                               pk_bf16(fl[4], fl[5]), pk_bf16(fl[6], fl[7])));
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const uint4 ah = rd16(HuHi + t * T::HPB + mt * 1024 + lb);
-        const uint4 al = rd16(HuLo + t * T::HPB + mt * 1024 + lb);
+      for (int mt = 0; mt < HT; ++mt) {
+        const uint4 ah = rd16(HuHi + t * T::HPB + (own0 + mt) * 1024 + lb);
+        const uint4 al = rd16(HuLo + t * T::HPB + (own0 + mt) * 1024 + lb);
         acc_n[mt] = mfma(as_bf16x8(ah), bh4, acc_n[mt]);
         acc_n[mt] = mfma(as_bf16x8(ah), bl4, acc_n[mt]);
         acc_n[mt] = mfma(as_bf16x8(al), bh4, acc_n[mt]);
@@ -944,18 +1025,21 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   if (q < N) {
     const size_t orow = ((size_t)bh * N + q) * D;
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
+    for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = ws_l * acc_o[mt][4 * i4 + r] + wl_den * acc_n[mt][4 * i4 + r];
+        for (int r = 0; r < 4; ++r) o[r] = ws_l * acc_o[own0 + mt][4 * i4 + r] + wl_den * acc_n[mt][4 * i4 + r];
         uint2 wv;
         wv.x = pk_bf16(o[0], o[1]);
         wv.y = pk_bf16(o[2], o[3]);
-        *reinterpret_cast<uint2*>(O + orow + 32 * mt + 8 * i4 + 4 * hi) = wv;
+        *reinterpret_cast<uint2*>(O + orow + 32 * (own0 + mt) + 8 * i4 + 4 * hi) = wv;
       }
   }
+  };
+  if (grp == 0) body(IntTag<0>{});
+  else body(IntTag<1>{});
 }
 
 }  // namespace
