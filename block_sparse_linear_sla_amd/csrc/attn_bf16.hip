@@ -886,71 +886,102 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   else run_loop(make_work(g_tag, IntTag<0>{}, IntTag<0>{}));
 
   // ---- epilogue: swap halves of the partials within each query slice
-  constexpr int HT = D / 64;  // O tiles per half of d
-  constexpr int own0 = G * HT;  // first O tile this wavefront finishes
+  constexpr int HT = D / 64;     // O tiles per half of d
+  constexpr int own0 = G * HT;   // first O tile this wavefront finishes
+  constexpr int NTQ = D / 16;    // k-steps of phi(Q)
+  constexpr int TQ0 = G * (NTQ / 2);                        // the phi(Q) k-steps this wavefront computes
+  constexpr int PQB = (NTQ / 2) * 2 * 1024 + 256;           // its shared phi(Q) hi / lo fragments + dpart
+  constexpr int PQ_S2 = STAGE / PQB, PQ_T = (STAGE - HU_HALF) / PQB;
+  constexpr bool PQ_SHARE = PQ_S2 + 2 * PQ_T >= NWT;         // else each wavefront computes all of phi(Q)
+  auto pq_slot = [&](int k) -> char* {  // phi(Q) share slot of wavefront (k / 2, group k % 2)
+    if (k < PQ_S2) return st2 + k * PQB;
+    k -= PQ_S2;
+    if (k < PQ_T) return st0 + HU_HALF + k * PQB;
+    k -= PQ_T;
+    return st1 + HU_HALF + k * PQB;
+  };
+  // (A) hand the partner the halves it finishes: O tiles and (m, l) of the
+  // softmax partial, G tiles (bf16); group 0 also sets z_u = z - g
   {
-    char* sx = (wq / PPS == 0 ? st0 : st1) + (wq % PPS) * 2 * SXB;
-    float* mine = reinterpret_cast<float*>(sx + G * SXB);        // written by this wavefront
-    uint16_t* gx = reinterpret_cast<uint16_t*>(st2 + wq * 2 * GXB + G * GXB);
+    char* sx = (wq / (PPS > 0 ? PPS : 1) == 0 ? st0 : st1) + (wq % (PPS > 0 ? PPS : 1)) * 2 * SXB;
     if (LOADK) {
+      uint4* mine = reinterpret_cast<uint4*>(sx + G * SXB);
 #pragma unroll
       for (int t = 0; t < HT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) mine[(16 * t + e) * 64 + lane] = acc_o[(1 - G) * HT + t][e];
-      mine[16 * HT * 64 + lane] = sm.m;
-      mine[16 * HT * 64 + 64 + lane] = sm.l;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x16& a = acc_o[(1 - G) * HT + t];
+          mine[(4 * t + e4) * 64 + lane] = make_uint4(__float_as_uint(a[4 * e4]), __float_as_uint(a[4 * e4 + 1]),
+                                                      __float_as_uint(a[4 * e4 + 2]), __float_as_uint(a[4 * e4 + 3]));
+        }
+      reinterpret_cast<float2*>(sx + G * SXB + 16 * HT * 64 * 4)[lane] = make_float2(sm.m, sm.l);
     }
     if (lin && (TPW >= 2 || G == 1)) {
+      uint4* gx = reinterpret_cast<uint4*>(st2 + wq * 2 * GXB + G * GXB);
       const int u0 = TPW >= 2 ? (1 - G) * GXT : 0;  // first G tile the partner finishes
 #pragma unroll
       for (int t = 0; t < GXT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2)
-          *reinterpret_cast<uint32_t*>(gx + ((16 * t + e) * 64 + 2 * lane)) =
-              pk_bf16(acc_g[u0 + t][e], acc_g[u0 + t][e + 1]);
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const f32x16& a = acc_g[u0 + t];
+          gx[(2 * t + h8) * 64 + lane] =
+              make_uint4(pk_bf16(a[8 * h8], a[8 * h8 + 1]), pk_bf16(a[8 * h8 + 2], a[8 * h8 + 3]),
+                         pk_bf16(a[8 * h8 + 4], a[8 * h8 + 5]), pk_bf16(a[8 * h8 + 6], a[8 * h8 + 7]));
+        }
     }
+    if (lin && G == 0 && zd < D) zu[zd] = Hh[D * D + zd] - gsum;
   }
   __syncthreads();
-  float m_all, l_all;
+  // (B) merge the partner's halves into this wavefront's halves
+  float l_all = 0.f;
   {
-    const char* sx = (wq / PPS == 0 ? st0 : st1) + (wq % PPS) * 2 * SXB;
-    const float* theirs = reinterpret_cast<const float*>(sx + (1 - G) * SXB);
-    const uint16_t* gx = reinterpret_cast<const uint16_t*>(st2 + wq * 2 * GXB + (1 - G) * GXB);
-    l_all = 0.f;
-    m_all = -INFINITY;
+    const char* sx = (wq / (PPS > 0 ? PPS : 1) == 0 ? st0 : st1) + (wq % (PPS > 0 ? PPS : 1)) * 2 * SXB;
     if (LOADK) {
-      const float m1 = theirs[16 * HT * 64 + lane], l1 = theirs[16 * HT * 64 + 64 + lane];
-      const float m = fmaxf(sm.m, m1);
+      const uint4* theirs = reinterpret_cast<const uint4*>(sx + (1 - G) * SXB);
+      const float2 ml = reinterpret_cast<const float2*>(sx + (1 - G) * SXB + 16 * HT * 64 * 4)[lane];
+      const float m = fmaxf(sm.m, ml.x);
       float c0 = 0.f, c1 = 0.f;
       if (m != -INFINITY) {
         c0 = __builtin_amdgcn_exp2f((sm.m - m) * scale_log2);
-        c1 = __builtin_amdgcn_exp2f((m1 - m) * scale_log2);
+        c1 = __builtin_amdgcn_exp2f((ml.x - m) * scale_log2);
       }
-      l_all = sm.l * c0 + l1 * c1;
-      m_all = m;
+      l_all = sm.l * c0 + ml.y * c1;
 #pragma unroll
       for (int t = 0; t < HT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          acc_o[own0 + t][e] = acc_o[own0 + t][e] * c0 + theirs[(16 * t + e) * 64 + lane] * c1;
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const uint4 v = theirs[(4 * t + e4) * 64 + lane];
+          f32x16& a = acc_o[own0 + t];
+          a[4 * e4] = a[4 * e4] * c0 + __uint_as_float(v.x) * c1;
+          a[4 * e4 + 1] = a[4 * e4 + 1] * c0 + __uint_as_float(v.y) * c1;
+          a[4 * e4 + 2] = a[4 * e4 + 2] * c0 + __uint_as_float(v.z) * c1;
+          a[4 * e4 + 3] = a[4 * e4 + 3] * c0 + __uint_as_float(v.w) * c1;
+        }
     }
     if (lin && (TPW >= 2 || G == 0)) {
+      const uint4* gx = reinterpret_cast<const uint4*>(st2 + wq * 2 * GXB + (1 - G) * GXB);
       const int u0 = TPW >= 2 ? G * GXT : 0;
 #pragma unroll
       for (int t = 0; t < GXT; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const uint32_t pr = *reinterpret_cast<const uint32_t*>(gx + ((16 * t + e) * 64 + 2 * lane));
-          acc_g[u0 + t][e] += bf2f(pr & 0xffffu);
-          acc_g[u0 + t][e + 1] += bf2f(pr >> 16);
+        for (int h8 = 0; h8 < 2; ++h8) {
+          const uint4 v = gx[(2 * t + h8) * 64 + lane];
+          f32x16& a = acc_g[u0 + t];
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            a[8 * h8 + 2 * c] += bf2f(w4[c] & 0xffffu);
+            a[8 * h8 + 2 * c + 1] += bf2f(w4[c] >> 16);
+          }
         }
     }
   }
-  (void)m_all;
   __syncthreads();  // exchange areas read; stages 0 / 1 take H_u
+  // (C) H_u^T = (H - G)^T for this wavefront's G tiles as hi + lo bf16 planes
+  // (rows d_v, 16-wide d_k slices), and phi(Q) (hi + lo) of its k-steps
+  uint4 qh[NTQ], ql[NTQ];
+  float dpart = 0.f;
   if (lin) {
-    if (G == 0 && zd < D) zu[zd] = Hh[D * D + zd] - gsum;
-    // H_u^T = (H - G)^T as hi + lo bf16 planes (rows d_v, 16-wide d_k slices)
 #pragma unroll
     for (int t = 0; t < GXT; ++t) {
       if (TPW < 2 && G != 0) break;
@@ -978,24 +1009,12 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
         *reinterpret_cast<uint2*>(HuLo + off) = wv;
       }
     }
-    __syncthreads();  // H_u^T and z_u complete
-  }
-
-  float inv_l = 0.f;
-  if (do_s) {
-    const float lt = l_all + __shfl_xor(l_all, 32);
-    inv_l = lt > 0.f ? 1.f / lt : 0.f;
-  }
-  f32x16 acc_n[HT];
-#pragma unroll
-  for (int t = 0; t < HT; ++t) acc_n[t] = f32x16{};
-  float den = 1.f;
-  if (lin) {
-    // num^T = H_u^T phi(Q)^T over this wavefront's half of d, phi(Q) split into hi + lo
-    float dpart = 0.f;
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
+    // phi(Q) of k-step t: 8 values per lane, split into bf16 hi + lo; dpart = phi(Q) . z_u
+    auto phiq = [&](int t) __attribute__((always_inline)) {
       const uint4 qv = __builtin_bit_cast(uint4, qf[t]);
+      const float4 z0 = *reinterpret_cast<const float4*>(zu + 16 * t + 8 * hi);
+      const float4 z1 = *reinterpret_cast<const float4*>(zu + 16 * t + 8 * hi + 4);
+      const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
       float f[8], fl[8];
       uint32_t fh[8];
 #pragma unroll
@@ -1003,38 +1022,86 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
         f[e] = phi(bf2f(elem(qv, e)));
         fh[e] = pk_bf16(f[e], 0.f) & 0xffffu;
         fl[e] = f[e] - bf2f(fh[e]);
-        dpart = fmaf(f[e], zu[16 * t + 8 * hi + e], dpart);
+        dpart = fmaf(f[e], zz[e], dpart);
       }
-      const bf16x8 bh4 = as_bf16x8(make_uint4(fh[0] | (fh[1] << 16), fh[2] | (fh[3] << 16),
-                                              fh[4] | (fh[5] << 16), fh[6] | (fh[7] << 16)));
-      const bf16x8 bl4 = as_bf16x8(make_uint4(pk_bf16(fl[0], fl[1]), pk_bf16(fl[2], fl[3]),
-                                              pk_bf16(fl[4], fl[5]), pk_bf16(fl[6], fl[7])));
+      qh[t] = make_uint4(fh[0] | (fh[1] << 16), fh[2] | (fh[3] << 16), fh[4] | (fh[5] << 16), fh[6] | (fh[7] << 16));
+      ql[t] = make_uint4(pk_bf16(fl[0], fl[1]), pk_bf16(fl[2], fl[3]), pk_bf16(fl[4], fl[5]), pk_bf16(fl[6], fl[7]));
+    };
+    if (PQ_SHARE) {
+      uint4* sh = reinterpret_cast<uint4*>(pq_slot(2 * wq + G));
+#pragma unroll
+      for (int i = 0; i < NTQ / 2; ++i) {
+        phiq(TQ0 + i);
+        sh[(2 * i) * 64 + lane] = qh[TQ0 + i];
+        sh[(2 * i + 1) * 64 + lane] = ql[TQ0 + i];
+      }
+      reinterpret_cast<float*>(pq_slot(2 * wq + G) + (NTQ / 2) * 2 * 1024)[lane] = dpart;
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t) phiq(t);
+    }
+    __syncthreads();  // H_u^T and the shared phi(Q) complete
+  }
+
+  float inv_l = 0.f;
+  if (do_s) {
+    const float lt = l_all + __shfl_xor(l_all, 32);
+    inv_l = lt > 0.f ? 1.f / lt : 0.f;
+  }
+  // (D) num^T = H_u^T phi(Q)^T over this wavefront's half of d
+  f32x16 acc_n[HT];
+#pragma unroll
+  for (int t = 0; t < HT; ++t) acc_n[t] = f32x16{};
+  float den = 1.f;
+  if (lin) {
+    if (PQ_SHARE) {
+      const uint4* sh = reinterpret_cast<const uint4*>(pq_slot(2 * wq + (1 - G)));
+      constexpr int TP0 = (1 - G) * (NTQ / 2);
+#pragma unroll
+      for (int i = 0; i < NTQ / 2; ++i) {
+        qh[TP0 + i] = sh[(2 * i) * 64 + lane];
+        ql[TP0 + i] = sh[(2 * i + 1) * 64 + lane];
+      }
+      dpart += reinterpret_cast<const float*>(pq_slot(2 * wq + (1 - G)) + (NTQ / 2) * 2 * 1024)[lane];
+    }
+#pragma unroll
+    for (int t = 0; t < NTQ; ++t) {
 #pragma unroll
       for (int mt = 0; mt < HT; ++mt) {
         const uint4 ah = rd16(HuHi + t * T::HPB + (own0 + mt) * 1024 + lb);
         const uint4 al = rd16(HuLo + t * T::HPB + (own0 + mt) * 1024 + lb);
-        acc_n[mt] = mfma(as_bf16x8(ah), bh4, acc_n[mt]);
-        acc_n[mt] = mfma(as_bf16x8(ah), bl4, acc_n[mt]);
-        acc_n[mt] = mfma(as_bf16x8(al), bh4, acc_n[mt]);
+        acc_n[mt] = mfma(as_bf16x8(ah), as_bf16x8(qh[t]), acc_n[mt]);
+        acc_n[mt] = mfma(as_bf16x8(ah), as_bf16x8(ql[t]), acc_n[mt]);
+        acc_n[mt] = mfma(as_bf16x8(al), as_bf16x8(qh[t]), acc_n[mt]);
       }
     }
     den = dpart + __shfl_xor(dpart, 32);
   }
   const float wl_den = lin ? wl_ / den : 0.f;
   const float ws_l = ws_ * inv_l;
+  // each 16-byte store holds 8 consecutive d of one query: lanes l and l^32
+  // hold the two 4-d halves of every 8-d chunk and swap one of them
   if (q < N) {
     const size_t orow = ((size_t)bh * N + q) * D;
 #pragma unroll
     for (int mt = 0; mt < HT; ++mt)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        float o[4];
+      for (int j = 0; j < 2; ++j) {
+        uint2 pv[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = ws_l * acc_o[own0 + mt][4 * i4 + r] + wl_den * acc_n[mt][4 * i4 + r];
-        uint2 wv;
-        wv.x = pk_bf16(o[0], o[1]);
-        wv.y = pk_bf16(o[2], o[3]);
-        *reinterpret_cast<uint2*>(O + orow + 32 * (own0 + mt) + 8 * i4 + 4 * hi) = wv;
+        for (int c = 0; c < 2; ++c) {
+          const int i4 = 2 * j + c;
+          float o[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[r] = ws_l * acc_o[own0 + mt][4 * i4 + r] + wl_den * acc_n[mt][4 * i4 + r];
+          pv[c] = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
+        }
+        // lane hi = 0 keeps chunk i4 = 2j (needs the partner's pv[0]); hi = 1 keeps 2j + 1 (needs pv[1])
+        const uint2 send = hi ? pv[0] : pv[1];
+        const uint2 recv = make_uint2(__shfl_xor(send.x, 32), __shfl_xor(send.y, 32));
+        const uint4 outv = hi ? make_uint4(recv.x, recv.y, pv[1].x, pv[1].y)
+                              : make_uint4(pv[0].x, pv[0].y, recv.x, recv.y);
+        *reinterpret_cast<uint4*>(O + orow + 32 * (own0 + mt) + 16 * j + 8 * hi) = outv;
       }
   }
   };
