@@ -9,33 +9,31 @@
 //
 // Two kernels:
 //
-// prep_kernel (one workgroup per chunk of key blocks of one head) streams K and
-//   V once and writes, per head, V^T and phi(K)^T as [d, Nk*bk] bf16 (keys past
-//   N zero), the per-key-block column sums of phi(K) (float32), and partial
-//   linear totals H = sum_u phi(k_u)^T v_u, z = sum_u phi(k_u) (phi(K) split
-//   into hi + lo bf16 so the totals keep ~16 mantissa bits).  Within every 16
-//   keys the transposed tiles store key offset o at position o with bits 2 and
-//   3 swapped (see below).
+// prep_kernel (linear branch only; one workgroup per chunk of key blocks of one
+//   head) streams K and V once and writes phi(K) = elu(K) + 1 as bf16 in the
+//   layout of K, the per-key-block column sums of phi(K) (float32), and the
+//   chunk's partial linear totals H = sum_u phi(k_u)^T v_u, z = sum_u phi(k_u)
+//   (phi split into hi + lo bf16 so the totals keep ~16 mantissa bits).
 //
-// attn_kernel (one workgroup per mask row = (b, h, query block of BQ rows),
-//   BQ/32 wavefronts of 32 query rows each) walks the row's key blocks.  The
-//   K tile, the V^T tile and (linear branch) the phi(K)^T tile of a block go
-//   straight from global memory to LDS (global_load_lds, 16 bytes per lane);
-//   16-byte chunks are XOR-swizzled by row so the matrix-core operand reads are
-//   free of bank conflicts.  Sparse and dense modes double-buffer the tiles.
+// attn_kernel / fused_kernel (one workgroup per mask row = (b, h, query block
+//   of BQ rows)) walk the row's key blocks in units of 64 keys.  The K, V and
+//   (linear branch) phi(K) tiles of a unit go straight from global memory to
+//   LDS (buffer loads with an LDS destination, 16 bytes per lane), row-major
+//   with 16-byte chunks XOR-swizzled by key so the operand reads are free of
+//   bank conflicts.
 //
 // Matrix-core formulation (v_mfma_f32_32x32x16_bf16; lane l supplies operand
 // row / column l%32 and a k-slice 8*(l/32) .. +7; accumulator element i of
 // lane l is row 8*(i/4) + 4*(l/32) + i%4, column l%32):
 //   S^T  (keys x queries)  = K . Q^T           A = K tile, B = Q (registers)
-//   O^T  (d x queries)    += V^T . P^T          A = V^T tile, B = P (registers)
-//   G    (d x d)          += phi(K)^T . V       A = phi(K)^T tile, B = V^T tile
+//   O^T  (d x queries)    += V^T . P^T          A = V^T (transposed read), B = P (registers)
+//   G    (d x d)          += phi(K)^T . V       A = phi(K)^T, B = V^T (transposed reads)
 // With queries on the lane axis of S^T and O^T, each lane's softmax state is
 // its own query's: the row max / sum need one exchange with lane l^32 and the
 // rescale of O is lane-local.  The S^T accumulator of a lane lists keys in the
-// order (0-3, 8-11 | 4-7, 12-15) of every 16, which is exactly the k-slice
-// order of the P operand once bits 2 and 3 of the key offset are swapped in
-// the transposed tiles - so P goes from accumulator to operand in registers.
+// order (0-3, 8-11 | 4-7, 12-15) of every 16, and the V^T / phi(K)^T operands
+// are read in that same key order with ds_read_b64_tr_b16 (two 4-key reads per
+// operand), so P goes from accumulator to operand in registers.
 //
 // Linear branch: H_u = H - G and z_u = z - g, where G and g are the sums over
 // the row's listed blocks, so O_l = phi(Q) H_u / phi(Q) z_u; phi(Q) H_u is a
@@ -49,6 +47,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int I>
@@ -83,172 +82,9 @@ __device__ __forceinline__ long long xcd_row(long long b, long long R) {
   return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
 }
 
-// Position of key offset o inside its 16-key group in the transposed tiles.
-__device__ __forceinline__ int kperm(int o) { return (o & ~12) | ((o & 4) << 1) | ((o & 8) >> 1); }
-
 __device__ __forceinline__ uint32_t elem(const uint4& v, int e) {
   const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
   return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// ------------------------------------------------------------------ prep
-template <int D, int BK>
-struct PrepCfg {
-  static constexpr int NT = 256;
-  static constexpr int VST = BK + 8;                    // padded LDS row stride (elements)
-  static constexpr int PAIRS = (BK / 4) * (D / 8);      // (4-key group, 8-d chunk) pairs
-  static constexpr int ST = (PAIRS + NT - 1) / NT;
-  static constexpr int TILE = D * VST * 2;              // bytes of one transposed tile
-  static constexpr int TT = (D / 32) * (D / 32);
-  static constexpr int TPW = (TT + 3) / 4;              // G tiles per wavefront
-};
-
-// LIN = false: only V^T is written (sparse / dense callers).
-template <int D, int BK, bool LIN>
-__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ K,
-                                                   const uint16_t* __restrict__ V,
-                                                   const float* __restrict__ alpha, int H, int N,
-                                                   int Nk, int chunk_blocks, int nchunk,
-                                                   uint16_t* __restrict__ vt_g, uint16_t* __restrict__ pk_g,
-                                                   float* __restrict__ zblk, float* __restrict__ hpart) {
-  using C = PrepCfg<D, BK>;
-  __shared__ __attribute__((aligned(16))) char smem[3 * C::TILE + (BK / 4) * D * 4];
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Pk = reinterpret_cast<uint16_t*>(smem + C::TILE);
-  uint16_t* PkLo = reinterpret_cast<uint16_t*>(smem + 2 * C::TILE);
-  float* zred = reinterpret_cast<float*>(smem + 3 * C::TILE);  // [BK/4][D]
-
-  const long long bh = blockIdx.x / nchunk;
-  const int chunk = blockIdx.x % nchunk;
-  const bool lin = LIN && !(alpha != nullptr && alpha[bh % H] == 1.f);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const size_t npad = (size_t)Nk * BK;
-  const uint16_t* Kb = K + (size_t)bh * N * D;
-  const uint16_t* Vb = V + (size_t)bh * N * D;
-  const int jb = chunk * chunk_blocks, je = min(Nk, jb + chunk_blocks);
-
-  f32x16 acc_g[C::TPW];
-#pragma unroll
-  for (int t = 0; t < C::TPW; ++t) acc_g[t] = f32x16{};
-  float zpart = 0.f;
-
-  // Block j's K/V chunks are fetched into registers while block j-1 is being
-  // transposed, copied out and multiplied (two register buffers).
-  auto fetch = [&](int j, uint4 (&kr_)[C::ST][4], uint4 (&vr_)[C::ST][4]) __attribute__((always_inline)) {
-    const int key0 = j * BK;
-#pragma unroll
-    for (int s = 0; s < C::ST; ++s) {
-      const int pi = tid + C::NT * s;
-      const int c = pi % (D / 8), g = pi / (D / 8);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int key = key0 + 4 * g + u;
-        const bool ok = pi < C::PAIRS && key < N;
-        const size_t off = (size_t)key * D + c * 8;
-        vr_[s][u] = ok ? *reinterpret_cast<const uint4*>(Vb + off) : make_uint4(0, 0, 0, 0);
-        kr_[s][u] = (ok && lin) ? *reinterpret_cast<const uint4*>(Kb + off) : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  auto process = [&](int j, const uint4 (&kr)[C::ST][4], const uint4 (&vr)[C::ST][4]) __attribute__((always_inline)) {
-    const int key0 = j * BK;
-    __syncthreads();  // previous block's tiles fully consumed
-#pragma unroll
-    for (int s = 0; s < C::ST; ++s) {
-      const int pi = tid + C::NT * s;
-      if (pi >= C::PAIRS) continue;
-      const int c = pi % (D / 8), g = pi / (D / 8);
-      const int pos = ((4 * g) & ~15) + kperm((4 * g) & 15);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint2 wv;
-        wv.x = elem(vr[s][0], e) | (elem(vr[s][1], e) << 16);
-        wv.y = elem(vr[s][2], e) | (elem(vr[s][3], e) << 16);
-        *reinterpret_cast<uint2*>(Vt + (c * 8 + e) * C::VST + pos) = wv;
-      }
-      if (lin) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float f[4], lo[4];
-          uint32_t hb[4];
-          float zs = 0.f;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const bool ok = key0 + 4 * g + u < N;
-            f[u] = ok ? phi(bf2f(elem(kr[s][u], e))) : 0.f;
-            zs += f[u];
-            hb[u] = pk_bf16(f[u], 0.f) & 0xffffu;
-            lo[u] = f[u] - bf2f(hb[u]);
-          }
-          zred[g * D + c * 8 + e] = zs;
-          uint2 wv;
-          wv.x = hb[0] | (hb[1] << 16);
-          wv.y = hb[2] | (hb[3] << 16);
-          *reinterpret_cast<uint2*>(Pk + (c * 8 + e) * C::VST + pos) = wv;
-          wv.x = pk_bf16(lo[0], lo[1]);
-          wv.y = pk_bf16(lo[2], lo[3]);
-          *reinterpret_cast<uint2*>(PkLo + (c * 8 + e) * C::VST + pos) = wv;
-        }
-      }
-    }
-    __syncthreads();
-    // copy the transposed tiles out: row d has BK keys = BK/8 chunks of 16 B
-    for (int e = tid; e < D * (BK / 8); e += C::NT) {
-      const int d = e / (BK / 8), ch = e % (BK / 8);
-      const size_t go = ((size_t)bh * D + d) * npad + key0 + ch * 8;
-      *reinterpret_cast<uint4*>(vt_g + go) = *reinterpret_cast<const uint4*>(Vt + d * C::VST + ch * 8);
-      if (lin) *reinterpret_cast<uint4*>(pk_g + go) = *reinterpret_cast<const uint4*>(Pk + d * C::VST + ch * 8);
-    }
-    if (lin) {
-      if (tid < D) {
-        float z = 0.f;
-#pragma unroll
-        for (int g = 0; g < BK / 4; ++g) z += zred[g * D + tid];
-        zblk[((size_t)bh * Nk + j) * D + tid] = z;
-        zpart += z;
-      }
-      // G += phi(K)^T V (hi and lo parts of phi)
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-#pragma unroll
-        for (int u = 0; u < C::TPW; ++u) {
-          const int tix = w * C::TPW + u;
-          if (tix >= C::TT) continue;
-          const int mt = tix / (D / 32), nt = tix % (D / 32);
-          const uint4 ah = *reinterpret_cast<const uint4*>(Pk + (32 * mt + l32) * C::VST + 16 * s + 8 * hi);
-          const uint4 al = *reinterpret_cast<const uint4*>(PkLo + (32 * mt + l32) * C::VST + 16 * s + 8 * hi);
-          const uint4 bv = *reinterpret_cast<const uint4*>(Vt + (32 * nt + l32) * C::VST + 16 * s + 8 * hi);
-          acc_g[u] = mfma(as_bf16x8(ah), as_bf16x8(bv), acc_g[u]);
-          acc_g[u] = mfma(as_bf16x8(al), as_bf16x8(bv), acc_g[u]);
-        }
-      }
-    }
-  };
-  uint4 ka[C::ST][4], va[C::ST][4], kb2[C::ST][4], vb2[C::ST][4];
-  if (jb < je) fetch(jb, ka, va);
-  for (int j = jb; j < je; j += 2) {
-    if (j + 1 < je) fetch(j + 1, kb2, vb2);
-    process(j, ka, va);
-    if (j + 1 < je) {
-      if (j + 2 < je) fetch(j + 2, ka, va);
-      process(j + 1, kb2, vb2);
-    }
-  }
-  if (!lin) return;
-  float* out = hpart + ((size_t)bh * nchunk + chunk) * (D * D + D);
-#pragma unroll
-  for (int u = 0; u < C::TPW; ++u) {
-    const int tix = w * C::TPW + u;
-    if (tix >= C::TT) continue;
-    const int mt = tix / (D / 32), nt = tix % (D / 32);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int dk = 32 * mt + 8 * (i >> 2) + 4 * hi + (i & 3);
-      out[dk * D + 32 * nt + l32] = acc_g[u][i];
-    }
-  }
-  if (tid < D) out[D * D + tid] = zpart;
 }
 
 // ------------------------------------------------------------------ attention
@@ -257,46 +93,71 @@ constexpr int KU = 64;                 // keys per attention unit; a listed bloc
 
 // LDS tile layouts of one 64-key unit.  Every direct load instruction brings
 // 64 x 16 bytes that land in LDS in lane order, so a tile is stored as rows of
-// whole 128-byte global lines and each load covers 8 complete lines.  Inside
-// a row the 16-byte chunks are XOR-swizzled by the row index, so the 16 rows
-// that a 16-lane group reads for one MFMA operand hit 16 distinct 16-byte bank
-// groups:
-//   K tile     [D/64][64 keys][128 B]  chunk c of key r stored at c ^ ((r >> 1) & 7)
-//   V^T tile   [D][128 B]              chunk c of row d stored at c ^ ((d >> 1) & 7)
-//   phi(K)^T tile: as V^T
+// whole 128-byte global lines - [D/64 halves][64 keys][128 B], row-major like
+// K, V and phi(K) in memory - and each load covers 8 complete lines.  Inside a
+// row the 16-byte chunks are XOR-swizzled by the key:
+//   K tiles       chunk c of key r at c ^ swk(r) = c ^ ((r >> 1) & 7): the 16
+//                 keys that a 16-lane group reads for one S operand hit 16
+//                 distinct bank groups;
+//   V, phi(K)     chunk c of key r at c ^ swv(r) = c ^ (4 ((r >> 1) & 1)): the
+//                 4 keys x 32 bytes that a 16-lane group reads with one
+//                 transposed read hit distinct banks.
 // H_u^T (written with ordinary LDS stores after the loop) keeps a "plane"
 // layout: every 16-element k-slice is a plane of 32 bytes per row, the two
 // 16-byte halves swapped when bit 3 of the row is set.
 template <int D>
 struct Tiles {
-  static constexpr int KHALF = KU * 128;       // bytes of one 64-d half of the K tile
-  static constexpr int KT_BYTES = KU * D * 2;  // K tile
-  static constexpr int VT_BYTES = D * KU * 2;  // V^T (or phi(K)^T) tile
+  static constexpr int KHALF = KU * 128;       // bytes of one 64-d half of a tile
+  static constexpr int KT_BYTES = KU * D * 2;  // one [64 keys x D] tile
   static constexpr int HPB = D * 32;           // bytes of one H_u^T plane (16 d_k)
 };
+
+__device__ __forceinline__ int swk(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swv(int r) { return 4 * ((r >> 1) & 1); }
 
 __device__ __forceinline__ int lane_base(int lane) {
   const int l32 = lane & 31, hi = lane >> 5;
   return l32 * 32 + 16 * (hi ^ ((l32 >> 3) & 1));
 }
 
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
+// of the 4-element pieces addressed by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.
+__device__ __forceinline__ s16x4 tr16(const char* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+}
+
 // Per-lane byte offsets of the MFMA operand reads (lane l: row l%32 of a
-// 32-row tile, k-slice half l/32): the 16-wide k-step t of 32 rows of 128 bytes
-// is at off[t].  K: d-step t of key subtile kt at (t/4) KHALF + 4096 kt +
-// off[t%4]; V^T / phi(K)^T: key plane pl of row tile dt at 4096 dt + off[pl].
+// 32-row tile, k-slice half l/32).
+//   K (S operand): the 16-wide d step t of key subtile kt at (t/4) KHALF +
+//     4096 kt + off[t%4] (one 16-byte read).
+//   V^T / phi(K)^T (transposed reads of a row-major tile): rows d = 32 dt +
+//     l%32, the 8 keys of key plane pl in the order 4h + {0..3}, 4h + 8 +
+//     {0..3} (h = l/32).  Lanes 4m .. 4m+3 of a 16-lane group address key
+//     4h + m (+ 8 for the second read) and 4 consecutive d each, so lane i
+//     receives d = base + i across the 4 keys.
 template <int D>
 struct ReadPlan {
-  int off[4];
+  int off[4], tro[2];
   __device__ __forceinline__ explicit ReadPlan(int lane) {
     const int l32 = lane & 31, hi = lane >> 5;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) off[t] = l32 * 128 + 16 * ((2 * t + hi) ^ ((l32 >> 1) & 7));
+    for (int t = 0; t < 4; ++t) off[t] = l32 * 128 + 16 * ((2 * t + hi) ^ swk(l32));
+    const int i = lane & 15, g2 = (lane >> 4) & 1, kl = 4 * hi + (i >> 2);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {  // d offset 32 p inside a 64-d half
+      const int d = 32 * p + 16 * g2 + 4 * (i & 3);
+      tro[p] = kl * 128 + 16 * ((d >> 3) ^ swv(kl)) + 8 * ((d >> 2) & 1);
+    }
   }
   __device__ __forceinline__ const char* kp(const char* Ks, int kt, int t) const {
     return Ks + (t / 4) * Tiles<D>::KHALF + kt * 4096 + off[t % 4];
   }
-  __device__ __forceinline__ const char* vp(const char* Vt, int dt, int pl) const {
-    return Vt + dt * 4096 + off[pl];
+  __device__ __forceinline__ bf16x8 vt(const char* Vs, int dt, int pl) const {
+    // dt may be a wave-uniform runtime value: select rather than index
+    const char* b = Vs + (dt / 2) * Tiles<D>::KHALF + pl * 16 * 128 + ((dt & 1) ? tro[1] : tro[0]);
+    const s16x4 a = tr16(b), c = tr16(b + 8 * 128);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, c, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 };
 
@@ -331,45 +192,37 @@ __device__ __forceinline__ void b2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
 // Direct loads of one unit's tiles into LDS, split over NWL wavefronts.  Load
 // slot u of a tile fills the 1 KB at tile + 1024 u (8 rows of 128 bytes, in
 // the swizzled layouts above): lane l brings the 16-byte chunk that belongs at
-// position l.  Each load is a per-head buffer resource, the unit's byte
-// offset (scalar) and a per-lane byte offset fixed for the kernel.  K rows
-// past N read as zeros (their scores are masked); V^T / phi(K)^T are zero past N.
+// position l.  Each load is a per-head buffer resource over a row-major
+// [N, D] array, the unit's byte offset (scalar) and a per-lane byte offset
+// fixed for the kernel; rows past N read as zeros.
 template <int D, int NWL>
 struct LoadPlan {
   using T = Tiles<D>;
-  static constexpr int NK = T::KT_BYTES / 1024 / NWL;   // K slots per wavefront
-  static constexpr int NV = T::VT_BYTES / 1024 / NWL;   // V^T (or phi(K)^T) slots per wavefront
-  static_assert(NK * NWL * 1024 == T::KT_BYTES && NV * NWL * 1024 == T::VT_BYTES, "tile split");
-  uint32_t koff[NK], voff[NV];
+  static constexpr int NK = T::KT_BYTES / 1024 / NWL;   // slots per wavefront and tile
+  static_assert(NK * NWL * 1024 == T::KT_BYTES, "tile split");
+  uint32_t koff[NK], roff[NK];
   int w;
 
-  __device__ __forceinline__ LoadPlan(int w_, int lane, size_t npad) : w(w_) {
+  __device__ __forceinline__ LoadPlan(int w_, int lane) : w(w_) {
 #pragma unroll
     for (int ii = 0; ii < NK; ++ii) {
       const int u = w + NWL * ii;
       const int hd = u / 8, key = 8 * (u % 8) + (lane >> 3);
-      const int c = (lane & 7) ^ ((key >> 1) & 7);
-      koff[ii] = (uint32_t)(key * D * 2 + hd * 128 + 16 * c);
-    }
-#pragma unroll
-    for (int ii = 0; ii < NV; ++ii) {
-      const int u = w + NWL * ii;
-      const int d = 8 * u + (lane >> 3);
-      const int c = (lane & 7) ^ ((d >> 1) & 7);
-      voff[ii] = (uint32_t)((size_t)d * npad * 2 + 16 * c);
+      koff[ii] = (uint32_t)(key * D * 2 + hd * 128 + 16 * ((lane & 7) ^ swk(key)));
+      roff[ii] = (uint32_t)(key * D * 2 + hd * 128 + 16 * ((lane & 7) ^ swv(key)));
     }
   }
-  // K tile of the unit starting at key key0 (K of one head as a buffer)
+  // K tile (S operand layout) of the unit starting at key key0
   __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int key0, char* dst) const {
     const uint32_t soff = (uint32_t)key0 * (D * 2);
 #pragma unroll
     for (int ii = 0; ii < NK; ++ii) b2lds16(rk, koff[ii], soff, dst + 1024 * (w + NWL * ii));
   }
-  // transposed [d, npad] tile (V^T or phi(K)^T of one head) of the unit at key0
-  __device__ __forceinline__ void load_t(__amdgpu_buffer_rsrc_t rt, int key0, char* dst) const {
-    const uint32_t soff = (uint32_t)key0 * 2;
+  // V or phi(K) tile (transposed-read layout) of the unit starting at key key0
+  __device__ __forceinline__ void load_r(__amdgpu_buffer_rsrc_t rr, int key0, char* dst) const {
+    const uint32_t soff = (uint32_t)key0 * (D * 2);
 #pragma unroll
-    for (int ii = 0; ii < NV; ++ii) b2lds16(rt, voff[ii], soff, dst + 1024 * (w + NWL * ii));
+    for (int ii = 0; ii < NK; ++ii) b2lds16(rr, roff[ii], soff, dst + 1024 * (w + NWL * ii));
   }
 };
 
@@ -448,9 +301,9 @@ __device__ __forceinline__ void softmax_pv(const char* Vc, f32x16 (&sc)[2], f32x
                                            float scale_log2, float thr8) {
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
   // V^T fragments of the first key plane, read now so they land during the max
-  uint4 vf[D / 32];
+  bf16x8 vf[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) vf[dt] = rd16(rp.vp(Vc, dt, 0));
+  for (int dt = 0; dt < D / 32; ++dt) vf[dt] = rp.vt(Vc, dt, 0);
   if (lim < KU) {
     const int limh = lim - 4 * hi;  // key offset of element i of subtile h2: 32 h2 + 8 (i/4) + 4 hi + i%4
 #pragma unroll
@@ -488,9 +341,9 @@ __device__ __forceinline__ void softmax_pv(const char* Vc, f32x16 (&sc)[2], f32x
     const bf16x8 bp = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const uint4 a = vf[dt];
-      if (s4 + 1 < 4) vf[dt] = rd16(rp.vp(Vc, dt, s4 + 1));  // next key plane, one k-step ahead
-      acc_o[dt] = mfma(as_bf16x8(a), bp, acc_o[dt]);
+      const bf16x8 a = vf[dt];
+      if (s4 + 1 < 4) vf[dt] = rp.vt(Vc, dt, s4 + 1);  // next key plane, one k-step ahead
+      acc_o[dt] = mfma(a, bp, acc_o[dt]);
     }
   }
 }
@@ -504,13 +357,13 @@ __device__ __forceinline__ void softmax_pv(const char* Vc, f32x16 (&sc)[2], f32x
 // of loads fixed.
 template <int D, int BQ, int SUB, int MODE>
 __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const int* __restrict__ row_ptr, const int* __restrict__ col_idx, uint16_t* __restrict__ O, int N,
     int Nq, int Nk, float scale_log2) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
   using LP = LoadPlan<D, NW>;
-  constexpr int STAGE = T::KT_BYTES + T::VT_BYTES;
+  constexpr int STAGE = 2 * T::KT_BYTES;
   static_assert(2 * STAGE <= LDS_BYTES / 2, "two workgroups per compute unit");
   // Two distinct LDS arrays: the compiler can then tell the loads into one
   // stage from the operand reads of the other.
@@ -524,7 +377,6 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
   const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
   const long long bh = row / Nq;
   const int qi = (int)(row % Nq);
-  const size_t npad = (size_t)Nk * SUB * KU;
   int nsel, base = 0;
   if (MODE == MODE_DENSE) {
     nsel = Nk;
@@ -534,7 +386,7 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
   }
   const int nunits = nsel * SUB;
   const uint16_t* Kb = K + (size_t)bh * N * D;
-  const uint16_t* Vtb = vt_g + (size_t)bh * D * npad;
+  const uint16_t* Vb = V + (size_t)bh * N * D;
   const int q = qi * BQ + 32 * w + l32;
   bf16x8 qf[D / 16];
   load_q<D>(Q, bh, q, N, hi, qf);
@@ -543,9 +395,9 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
   for (int t = 0; t < D / 32; ++t) acc_o[t] = f32x16{};
   Softmax sm;
   const float thr8 = 8.f / scale_log2;
-  const LP lp(w, lane, npad);
+  const LP lp(w, lane);
   const auto rk = buf_rsrc(Kb, (uint32_t)((size_t)N * D * 2));
-  const auto rv = buf_rsrc(Vtb, (uint32_t)((size_t)D * npad * 2));
+  const auto rv = buf_rsrc(Vb, (uint32_t)((size_t)N * D * 2));
 
   // first key of unit x (clamped to the row's last unit)
   auto key0 = [&](int x) {
@@ -555,7 +407,7 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_kernel(
   };
   auto issue = [&](int k0x, char* sb) __attribute__((always_inline)) {
     lp.load_k(rk, k0x, sb);
-    lp.load_t(rv, k0x, sb + T::KT_BYTES);
+    lp.load_r(rv, k0x, sb + T::KT_BYTES);
   };
   // kcur: first key of the unit being computed.  The next unit's column index
   // is read before the barrier, whose wait absorbs the scalar load, so the
@@ -635,12 +487,144 @@ struct GTiles {
 // B operand of a G tile: the V^T fragment of column tile nt (a register array
 // index, so a constant nt folds and a wave-uniform one selects).
 template <int D>
-__device__ __forceinline__ uint4 pick_frag(const uint4 (&vf)[D / 32], int nt) {
-  uint4 b = vf[0];
+__device__ __forceinline__ bf16x8 pick_frag(const bf16x8 (&vf)[D / 32], int nt) {
+  bf16x8 b = vf[0];
 #pragma unroll
   for (int c = 1; c < D / 32; ++c)
     if (nt == c) b = vf[c];
   return b;
+}
+
+// Linear-branch preparation of one head's chunk of key blocks (one
+// workgroup, four wavefronts): phi(K) = elu(K) + 1 rounded to bf16 in the
+// layout of K (keys below N), the column sums of phi(K) over every key block
+// (float32), and the chunk's partial totals H = sum_u phi(k_u)^T v_u and
+// z = sum_u phi(k_u).  64-key units of K and V stream through two LDS stages
+// (row-major tiles in the transposed-read layout).  Wavefront w owns the G
+// tiles of the attention kernels' split (the d_k row tile mt = GTiles::mt(w, .)):
+// its phi(K)^T operand is read transposed from the K tile with phi applied in
+// fp32 and split into bf16 hi + lo (H keeps ~16 mantissa bits), and the V^T
+// operand is read transposed from the V tile.  Heads whose alpha is exactly 1
+// are skipped when alpha is given.
+template <int D, int BK>
+__global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ K,
+                                                   const uint16_t* __restrict__ V,
+                                                   const float* __restrict__ alpha, int H, int N, int Nk,
+                                                   int chunk_blocks, int nchunk, uint16_t* __restrict__ pk_g,
+                                                   float* __restrict__ zblk, float* __restrict__ hpart) {
+  using T = Tiles<D>;
+  using LP = LoadPlan<D, 4>;
+  constexpr int SUB = BK / KU;                  // units per key block
+  constexpr int TT = (D / 32) * (D / 32);
+  constexpr int TPW = TT / 4;                   // H tiles per wavefront
+  using GT = GTiles<D, TPW>;
+  constexpr int PCH = KU * (D / 8) / 256;       // 16-byte phi(K) chunks per thread and unit
+  __shared__ __attribute__((aligned(16))) char k0[T::KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char k1[T::KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char v0[T::KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char v1[T::KT_BYTES];
+
+  const long long bh = blockIdx.x / nchunk;
+  const int chunk = blockIdx.x % nchunk;
+  if (alpha != nullptr && alpha[bh % H] == 1.f) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const ReadPlan<D> rdp(lane);
+  const LP lp(w, lane);
+  const uint16_t* Kb = K + (size_t)bh * N * D;
+  const uint16_t* Vb = V + (size_t)bh * N * D;
+  uint16_t* Pb = pk_g + (size_t)bh * N * D;
+  const auto rk = buf_rsrc(Kb, (uint32_t)((size_t)N * D * 2));
+  const auto rv = buf_rsrc(Vb, (uint32_t)((size_t)N * D * 2));
+  const int jb = chunk * chunk_blocks, je = min(Nk, jb + chunk_blocks);
+  const int nun = max(0, je - jb) * SUB;        // units of the chunk
+  const int mt = GT::mt(w, 0);                  // the d_k row tile of this wavefront
+  const bool zown = TPW >= D / 32 || GT::nt(w, 0) == 0;  // one wavefront per row tile keeps z
+
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+  float zblock = 0.f, zpart = 0.f;
+
+  auto step = [&](int x, const char* ks, const char* vs, char* nks, char* nvs) __attribute__((always_inline)) {
+    wait_vm<0>();     // this wavefront's loads of unit x have landed
+    __syncthreads();  // ... and every wavefront's; unit x-1 consumed
+    if (x + 1 < nun) {
+      const int kn = (jb * SUB + x + 1) * KU;
+      lp.load_r(rk, kn, nks);
+      lp.load_r(rv, kn, nvs);
+    }
+    const int key0 = (jb * SUB + x) * KU;
+    const int lim = min(KU, N - key0);          // keys of the unit below N
+    // phi(K) rows to global memory
+#pragma unroll
+    for (int c = 0; c < PCH; ++c) {
+      const int ch = tid + 256 * c;
+      const int r = ch / (D / 8), cc = ch % (D / 8);
+      const uint4 kv = rd16(ks + (cc >> 3) * T::KHALF + r * 128 + 16 * ((cc & 7) ^ swv(r)));
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pk_bf16(phi(bf2f(elem(kv, 2 * e))), phi(bf2f(elem(kv, 2 * e + 1))));
+      if (r < lim) *reinterpret_cast<uint4*>(Pb + (size_t)(key0 + r) * D + 8 * cc) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    // H += phi(K)^T V (hi + lo) and z over the 4 key planes of the unit
+#pragma unroll
+    for (int pl = 0; pl < KU / 16; ++pl) {
+      const uint4 kt = __builtin_bit_cast(uint4, rdp.vt(ks, mt, pl));
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // element e of the fragment is key 16 pl + 4 hi + (e & 3) + 8 (e >> 2) of the unit
+        const int key = 16 * pl + 4 * hi + (e & 3) + 8 * (e >> 2);
+        f[e] = key < lim ? phi(bf2f(elem(kt, e))) : 0.f;
+        zblock += f[e];
+      }
+      uint32_t fh[4], fl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        fh[e] = pk_bf16(f[2 * e], f[2 * e + 1]);
+        fl[e] = pk_bf16(f[2 * e] - bf2f(fh[e] & 0xffffu), f[2 * e + 1] - bf2f(fh[e] >> 16));
+      }
+      const bf16x8 ah = as_bf16x8(make_uint4(fh[0], fh[1], fh[2], fh[3]));
+      const bf16x8 al = as_bf16x8(make_uint4(fl[0], fl[1], fl[2], fl[3]));
+#pragma unroll
+      for (int u = 0; u < TPW; ++u) {
+        const bf16x8 b = rdp.vt(vs, GT::nt(w, u), pl);
+        acc[u] = mfma(ah, b, acc[u]);
+        acc[u] = mfma(al, b, acc[u]);
+      }
+    }
+    if ((x + 1) % SUB == 0) {  // the key block ends: its phi(K) column sums
+      const float zb = zblock + __shfl_xor(zblock, 32);
+      if (zown && hi == 0) zblk[((size_t)bh * Nk + jb + x / SUB) * D + 32 * mt + l32] = zb;
+      zpart += zb;
+      zblock = 0.f;
+    }
+  };
+  if (nun > 0) {
+    lp.load_r(rk, jb * SUB * KU, k0);
+    lp.load_r(rv, jb * SUB * KU, v0);
+  }
+  int x = 0;
+  for (; x + 2 <= nun; x += 2) {
+    step(x, k0, v0, k1, v1);
+    step(x + 1, k1, v1, k0, v0);
+  }
+  if (x < nun) step(x, k0, v0, k1, v1);
+  wait_vm<0>();
+
+  float* out = hpart + ((size_t)bh * nchunk + chunk) * (D * D + D);
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int nt = GT::nt(w, u);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int dk = 32 * mt + 8 * (i >> 2) + 4 * hi + (i & 3);
+      out[dk * D + 32 * nt + l32] = acc[u][i];
+    }
+  }
+  if (zown && hi == 0) out[D * D + 32 * mt + l32] = zpart;
 }
 
 // One fused-kernel wavefront's share of a unit: keys [32 KT, 32 KT + 32),
@@ -656,18 +640,18 @@ __device__ __forceinline__ void fused_half(const char* Vt, const char* Pk, f32x1
                                            int hi, int lim, float scale_log2, float thr8) {
   using GT = GTiles<D, TPW>;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  uint4 vf[2][D / 32];
+  bf16x8 vf[2][D / 32];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) vf[j][dt] = rd16(rp.vp(Vt, dt, 2 * KT + j));
+    for (int dt = 0; dt < D / 32; ++dt) vf[j][dt] = rp.vt(Vt, dt, 2 * KT + j);
   if (DO_G) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
-        const uint4 a = rd16(rp.vp(Pk, GT::mt(wq, u), 2 * KT + j));
-        acc_g[u] = mfma(as_bf16x8(a), as_bf16x8(pick_frag<D>(vf[j], GT::nt(wq, u))), acc_g[u]);
+        const bf16x8 a = rp.vt(Pk, GT::mt(wq, u), 2 * KT + j);
+        acc_g[u] = mfma(a, pick_frag<D>(vf[j], GT::nt(wq, u)), acc_g[u]);
       }
   }
   if (!DO_S) return;
@@ -704,7 +688,7 @@ __device__ __forceinline__ void fused_half(const char* Vt, const char* Pk, f32x1
     }
     const bf16x8 bp = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] = mfma(as_bf16x8(vf[j][dt]), bp, acc_o[dt]);
+    for (int dt = 0; dt < D / 32; ++dt) acc_o[dt] = mfma(vf[j][dt], bp, acc_o[dt]);
   }
 }
 
@@ -723,7 +707,7 @@ __device__ __forceinline__ void fused_half(const char* Vt, const char* Pk, f32x1
 // phi(Q) for its half of d and mixes the branches into the output.
 template <int D, int BQ, int SUB, int MODE>
 __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ vt_g,
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ pk_g, const float* __restrict__ zblk, const int* __restrict__ row_ptr,
     const int* __restrict__ col_idx, const float* __restrict__ alpha, const float* __restrict__ htot,
     uint16_t* __restrict__ O, int H, int N, int Nq, int Nk, float scale_log2) {
@@ -737,8 +721,8 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   using LP = LoadPlan<D, NWT>;
   constexpr bool LOADK = MODE != MODE_LINEAR;    // the softmax branch needs K
   constexpr int OFF_V = LOADK ? T::KT_BYTES : 0; // V^T tile
-  constexpr int OFF_P = OFF_V + T::VT_BYTES;     // phi(K)^T tile
-  constexpr int OFF_Z = OFF_P + T::VT_BYTES;     // sum of phi(k) over the block's keys
+  constexpr int OFF_P = OFF_V + T::KT_BYTES;     // phi(K) tile
+  constexpr int OFF_Z = OFF_P + T::KT_BYTES;     // sum of phi(k) over the block's keys
   constexpr int STAGE = OFF_Z + D * 4;
   constexpr int HU_HALF = D * D * 2;             // H_u^T hi (or lo) part, bf16
   constexpr int NS = 3;
@@ -752,7 +736,7 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
                 "epilogue areas");
   // direct loads per unit of each wavefront; the last wavefront also brings
   // the block's phi sums (D floats, D/64 four-byte loads)
-  constexpr int NL = (LOADK ? LP::NK : 0) + 2 * LP::NV;
+  constexpr int NL = (LOADK ? LP::NK : 0) + 2 * LP::NK;
   constexpr int NLZ = NL + D / 64;
   static_assert((NS - 1) * NLZ < 64, "vmcnt");
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
@@ -773,7 +757,6 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   const long long bh = row / Nq;
   const int qi = (int)(row % Nq);
   const int h = (int)(bh % H);
-  const size_t npad = (size_t)Nk * SUB * KU;
   const int base = row_ptr[row];
   const int nsel = row_ptr[row + 1] - base;
   float ws_, wl_;
@@ -789,14 +772,14 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   const int nunits = (do_s || lin) ? nsel * SUB : 0;
 
   const uint16_t* Kb = K + (size_t)bh * N * D;
-  const uint16_t* Vtb = vt_g + (size_t)bh * D * npad;
-  const uint16_t* Pkb = pk_g + (size_t)bh * D * npad;
+  const uint16_t* Vb = V + (size_t)bh * N * D;
+  const uint16_t* Pkb = pk_g + (size_t)bh * N * D;
   const float* Zb = zblk + (size_t)bh * Nk * D;
   const float* Hh = htot + (size_t)bh * (D * D + D);
-  const LP lp(w, lane, npad);
+  const LP lp(w, lane);
   const auto rk = buf_rsrc(Kb, (uint32_t)((size_t)N * D * 2));
-  const auto rv = buf_rsrc(Vtb, (uint32_t)((size_t)D * npad * 2));
-  const auto rp = buf_rsrc(Pkb, (uint32_t)((size_t)D * npad * 2));
+  const auto rv = buf_rsrc(Vb, (uint32_t)((size_t)N * D * 2));
+  const auto rp = buf_rsrc(Pkb, (uint32_t)((size_t)N * D * 2));
   const auto rz = buf_rsrc(Zb, (uint32_t)((size_t)Nk * D * 4));
 
   auto stage = [&](int i) -> char* {
@@ -812,8 +795,8 @@ __global__ __launch_bounds__(BQ / 32 * 128, 1) void fused_kernel(
   auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
     const int k0x = key0(x);
     if (LOADK) lp.load_k(rk, k0x, sb);
-    lp.load_t(rv, k0x, sb + OFF_V);
-    lp.load_t(rp, k0x, sb + OFF_P);
+    lp.load_r(rv, k0x, sb + OFF_V);
+    lp.load_r(rp, k0x, sb + OFF_P);
     if (zwave) {
       const uint32_t zoff = (uint32_t)blk_of(x) * (D * 4);
 #pragma unroll
@@ -1135,36 +1118,30 @@ hipError_t launch_summary_reduce(const float* hpart, const float* alpha, int H, 
 namespace {
 
 template <int D, int BK>
-hipError_t prep_dispatch(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
-                         char* ws, const WsLayout& L, hipStream_t st) {
+hipError_t prep_dispatch(const Shape& s, const void* K, const void* V, const float* alpha, char* ws,
+                         const WsLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H;
   const dim3 grid((unsigned)(BH * L.nchunk)), block(256);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + L.vt);
   uint16_t* pk = reinterpret_cast<uint16_t*>(ws + L.pk);
   float* zb = reinterpret_cast<float*>(ws + L.zblk);
   float* hpart = reinterpret_cast<float*>(ws + L.hpart);
-  const uint16_t* k = static_cast<const uint16_t*>(K);
-  const uint16_t* v = static_cast<const uint16_t*>(V);
-  if (lin)
-    hipLaunchKernelGGL((prep_kernel<D, BK, true>), grid, block, 0, st, k, v, alpha, s.H, s.N, s.Nk,
-                       L.chunk_blocks, L.nchunk, vt, pk, zb, hpart);
-  else
-    hipLaunchKernelGGL((prep_kernel<D, BK, false>), grid, block, 0, st, k, v, alpha, s.H, s.N, s.Nk,
-                       L.chunk_blocks, L.nchunk, vt, pk, zb, hpart);
+  hipLaunchKernelGGL((prep_kernel<D, BK>), grid, block, 0, st, static_cast<const uint16_t*>(K),
+                     static_cast<const uint16_t*>(V), alpha, s.H, s.N, s.Nk, L.chunk_blocks, L.nchunk, pk,
+                     zb, hpart);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !lin) return e;
+  if (e != hipSuccess) return e;
   return launch_summary_reduce(hpart, alpha, s.H, BH, L.nchunk, D * D + D,
                                reinterpret_cast<float*>(ws + L.htot), st);
 }
 
 template <int D, int BQ, int SUB>
-hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K, const int32_t* rp,
-                         const int32_t* ci, const float* alpha, const char* ws, const WsLayout& L,
-                         void* O, hipStream_t st) {
+hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
+                         const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
+                         const WsLayout& L, void* O, hipStream_t st) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
-  const uint16_t* vt = reinterpret_cast<const uint16_t*>(ws + L.vt);
+  const uint16_t* vt = static_cast<const uint16_t*>(V);
   const uint16_t* pk = reinterpret_cast<const uint16_t*>(ws + L.pk);
   const float* zb = reinterpret_cast<const float*>(ws + L.zblk);
   const float* ht = reinterpret_cast<const float*>(ws + L.htot);
@@ -1195,19 +1172,20 @@ hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K
 
 hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
                             char* ws, const WsLayout& L, hipStream_t st) {
-  if (s.d == 128 && s.bk == 64) return prep_dispatch<128, 64>(s, lin, K, V, alpha, ws, L, st);
-  if (s.d == 128 && s.bk == 128) return prep_dispatch<128, 128>(s, lin, K, V, alpha, ws, L, st);
-  if (s.d == 64 && s.bk == 64) return prep_dispatch<64, 64>(s, lin, K, V, alpha, ws, L, st);
-  if (s.d == 64 && s.bk == 128) return prep_dispatch<64, 128>(s, lin, K, V, alpha, ws, L, st);
+  if (!lin) return hipSuccess;  // the softmax kernels read K and V as they are
+  if (s.d == 128 && s.bk == 64) return prep_dispatch<128, 64>(s, K, V, alpha, ws, L, st);
+  if (s.d == 128 && s.bk == 128) return prep_dispatch<128, 128>(s, K, V, alpha, ws, L, st);
+  if (s.d == 64 && s.bk == 64) return prep_dispatch<64, 64>(s, K, V, alpha, ws, L, st);
+  if (s.d == 64 && s.bk == 128) return prep_dispatch<64, 128>(s, K, V, alpha, ws, L, st);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K,
+hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
                             const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
                             const WsLayout& L, void* O, hipStream_t st) {
 #define SLA_ATTN(DD, QQ, KK)                                                  \
   if (s.d == DD && s.bq == QQ && s.bk == KK)                                  \
-    return attn_dispatch<DD, QQ, KK / 64>(s, mode, Q, K, rp, ci, alpha, ws, L, O, st);
+    return attn_dispatch<DD, QQ, KK / 64>(s, mode, Q, K, V, rp, ci, alpha, ws, L, O, st);
   SLA_ATTN(128, 128, 64)
   SLA_ATTN(128, 128, 128)
   SLA_ATTN(128, 64, 64)

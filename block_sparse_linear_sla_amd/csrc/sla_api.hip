@@ -39,9 +39,7 @@ WsLayout ws_layout(const Shape& s, bool router) {
   L.khat = router ? take(BH * s.Nk * s.d * sizeof(double)) : 0;
   L.S = take(BH * s.Nq * s.Nk * sizeof(double));
   const bool bf = s.dtype == SLA_BF16;
-  const size_t npad = (size_t)s.Nk * s.bk;
-  L.vt = bf ? take(BH * s.d * npad * 2) : 0;
-  L.pk = bf ? take(BH * s.d * npad * 2) : 0;
+  L.pk = bf ? take(BH * (size_t)s.N * s.d * 2) : 0;
   L.zblk = bf ? take(BH * s.Nk * s.d * sizeof(float)) : 0;
   L.counts = take((size_t)s.R() * sizeof(int32_t));
   L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
@@ -98,7 +96,7 @@ hipError_t run_prep(const Shape& s, bool lin, const void* K, const void* V, cons
 hipError_t run_attn(const Shape& s, Mode m, const void* Q, const void* K, const void* V,
                     const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
                     const WsLayout& L, void* O, hipStream_t st) {
-  if (s.dtype == SLA_BF16) return sla::launch_attn_bf16(s, m, Q, K, rp, ci, alpha, ws, L, O, st);
+  if (s.dtype == SLA_BF16) return sla::launch_attn_bf16(s, m, Q, K, V, rp, ci, alpha, ws, L, O, st);
   return sla::launch_attn_f32(s, m, Q, K, V, rp, ci, alpha,
                               reinterpret_cast<const float*>(ws + L.htot), O, st);
 }
