@@ -39,8 +39,7 @@ WsLayout ws_layout(const Shape& s, bool router) {
   L.khat = router ? take(BH * s.Nk * s.d * sizeof(double)) : 0;
   L.S = take(BH * s.Nq * s.Nk * sizeof(double));
   const bool bf = s.dtype == SLA_BF16;
-  L.pk = bf ? take(BH * (size_t)s.N * s.d * 2) : 0;
-  L.zblk = bf ? take(BH * s.Nk * s.d * sizeof(float)) : 0;
+  L.pk = bf ? take(BH * (size_t)s.Nk * s.bk * s.d * 2) : 0;
   L.counts = take((size_t)s.R() * sizeof(int32_t));
   L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
   L.total = off;

@@ -25,8 +25,7 @@ struct WsLayout {
   size_t bits;         // uint32 [R * words]
   size_t hpart;        // linear summary partials, float [B*H*nchunk*(d*d + d)]
   size_t htot;         // linear summaries, float [B*H*(d*d + d)]
-  size_t pk;           // bf16 path: phi(K), bf16 [B*H*N*d] (the layout of K)
-  size_t zblk;         // bf16 path: per-key-block sums of phi(K), float [B*H*Nk*d]
+  size_t pk;           // bf16 path: phi(K), bf16 [B*H][d/32][Nk*bk][32] (keys >= N zero)
   size_t total;
   int nchunk;          // key-block chunks per head in the summary pass
   int chunk_blocks;    // key blocks per chunk
@@ -47,8 +46,8 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
                        const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
                        double* logits_out, char* ws, const WsLayout& L, hipStream_t st);
 
-// attn_bf16.hip: the K/V preparation pass for the linear branch (phi(K),
-// per-block phi(K) sums and the per-head linear totals; nothing without lin;
+// attn_bf16.hip: the K/V preparation pass for the linear branch (phi(K) in
+// 32-wide d slices and the per-head linear totals; nothing without lin;
 // heads whose alpha is exactly 1 are skipped when alpha is given) and the
 // attention kernels.
 hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
