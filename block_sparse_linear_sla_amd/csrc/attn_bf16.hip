@@ -280,14 +280,17 @@ struct PhiPlan {
     return cat_tr(b, b + 512);
   }
 };
-template <int MTN>
+// Half HF (key planes 2 HF, 2 HF + 1) of a wavefront's phi(K) region for the
+// unit starting at key key0: MTN x 2 loads.
+template <int MTN, int HF>
 __device__ __forceinline__ void load_phi(__amdgpu_buffer_rsrc_t r, int mt0, int Npad, int key0, int lane,
                                          char* reg) {
 #pragma unroll
   for (int m = 0; m < MTN; ++m) {
     const uint32_t soff = (uint32_t)((mt0 + m) * Npad + key0) * 64u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b2lds16(r, (uint32_t)(16 * lane + 1024 * j), soff, reg + m * 4096 + 1024 * j);
+    for (int j = 2 * HF; j < 2 * HF + 2; ++j)
+      b2lds16(r, (uint32_t)(16 * lane + 1024 * j), soff, reg + m * 4096 + 1024 * j);
   }
 }
 
@@ -471,25 +474,25 @@ __device__ __forceinline__ void softmax_half(f32x16& sc, bf16x8 (&bp)[2], f32x16
 //   DO_S: O^T += V^T P^T (bp: the P operands of those planes);
 //   DO_G: G += phi(K)^T V for the wavefront's G tiles (the V^T fragments of
 //         P V as the B operand) and, for the wavefront that keeps them, the
-//         column sums g of its phi(K) row tiles.  The phi(K)^T fragments come
-//         from the wavefront's private region one plane ahead: pf holds plane
-//         PL0's on entry (read here when PL0 is 0) and the next plane's on
-//         exit.  Once the last plane's fragments are in registers, refill()
-//         hands the region to the next unit's load.
-template <int D, int NW, bool DO_S, bool DO_G, int PL0, int PL1, class Refill>
+//         column sums g of its phi(K) row tiles.  The phi(K)^T fragments of
+//         these planes come from the wavefront's private region, one plane
+//         ahead: ready() runs before the first read (it waits for the
+//         region's load), refill() after the last (it hands that part of the
+//         region to the next unit's load).
+template <int D, int NW, bool DO_S, bool DO_G, int PL0, int PL1, class Ready, class Refill>
 __device__ __forceinline__ void pv_g(const char* Vc, const char* Ph, const PhiPlan& pp,
                                      const bf16x8 (&bp)[PL1 - PL0], f32x16 (&acc_o)[D / 32],
                                      f32x16 (&acc_g)[GSplit<D, NW>::TPW], float (&gs)[GSplit<D, NW>::MTN],
-                                     bf16x8 (&pf)[GSplit<D, NW>::MTN], const ReadPlan<D>& rp, int w,
-                                     Refill&& refill) {
+                                     const ReadPlan<D>& rp, int w, Ready&& ready, Refill&& refill) {
   using GS = GSplit<D, NW>;
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  bf16x8 vf[D / 32];
+  bf16x8 vf[D / 32], pf[GS::MTN];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) vf[dt] = rp.vt(Vc, dt, PL0);
-  if (DO_G && PL0 == 0) {
+  if (DO_G) {
+    ready();
 #pragma unroll
-    for (int m = 0; m < GS::MTN; ++m) pf[m] = pp.read(Ph, m, 0);
+    for (int m = 0; m < GS::MTN; ++m) pf[m] = pp.read(Ph, m, PL0);
   }
   const bool zw = GS::zown(w);
 #pragma unroll
@@ -499,9 +502,9 @@ __device__ __forceinline__ void pv_g(const char* Vc, const char* Ph, const PhiPl
 #pragma unroll
       for (int m = 0; m < GS::MTN; ++m) {
         pc[m] = pf[m];
-        if (s4 + 1 < 4) pf[m] = pp.read(Ph, m, s4 + 1);
+        if (s4 + 1 < PL1) pf[m] = pp.read(Ph, m, s4 + 1);
       }
-      if (s4 == 3) refill();
+      if (s4 + 1 == PL1) refill();
       if (zw) {
 #pragma unroll
         for (int m = 0; m < GS::MTN; ++m) {
@@ -793,45 +796,66 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
     // index is read before the barrier, whose wait absorbs the scalar load, so
     // the LDS-read waits inside the step count LDS reads only.
     int kcur = key0(0);
+    // Direct loads of a wavefront, in issue order per unit b: K | V of unit
+    // b+1 at the top (NKV instructions), then (linear branch) the two halves
+    // of its phi(K) region for unit b+1 (NPH each), each as soon as the
+    // current unit's fragments of that half are in registers.  The vmcnt
+    // waits below count exactly those.
+    constexpr int NPH = 2 * GS::MTN;
+    auto wait_kv = [&]() __attribute__((always_inline)) {  // K | V of the current unit
+      if (G_) wait_vm<2 * NPH>();
+      else wait_vm<0>();
+    };
+    auto wait_phi = [&]() __attribute__((always_inline)) {  // the next phi half of the current unit
+      if (do_s) wait_vm<2 * LP::NK + NPH>();
+      else wait_vm<LP::NK + NPH>();
+    };
     auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
       const int knext = key0(b + 1);
-      wait_vm<0>();     // this wavefront's loads of unit b have landed
+      wait_kv();        // this wavefront's K | V loads of unit b have landed
       __syncthreads();  // ... and every wavefront's; unit b-1 consumed
       issue(knext, nxt);
       const int lim = min(KU, N - kcur);
       const int ln = G_ ? opaque(lane) : lane;
       const PhiPlan pp(ln);
-      auto refill = [&]() __attribute__((always_inline)) {
-        // the last phi(K) fragments are read: the region takes the next unit's
-        wait_lds();
-        load_phi<GS::MTN>(rph, mt0, Npad, knext, ln, myphi);
+      auto refill0 = [&]() __attribute__((always_inline)) {
+        wait_lds();  // planes 0, 1 of the region are in registers
+        load_phi<GS::MTN, 0>(rph, mt0, Npad, knext, ln, myphi);
       };
-      bf16x8 pf[GS::MTN];
+      auto refill1 = [&]() __attribute__((always_inline)) {
+        wait_lds();  // planes 2, 3 as well
+        load_phi<GS::MTN, 1>(rph, mt0, Npad, knext, ln, myphi);
+      };
+      const char* Vc = cur + T::KT_BYTES;
       if (S_ && G_) {
         // both branches: the unit as two 32-key halves (S, softmax, products),
         // which keeps half of the score and P registers live
         f32x16 s0 = score_half<D, 0, 4>(cur, qf, rdp);
         bf16x8 bp0[2];
         softmax_half<D, 0>(s0, bp0, acc_o, sm, hi, lim, scale_log2, thr8);
-        pv_g<D, NW, true, true, 0, 2>(cur + T::KT_BYTES, myphi, pp, bp0, acc_o, acc_g, gs, pf, rdp, w, refill);
+        pv_g<D, NW, true, true, 0, 2>(Vc, myphi, pp, bp0, acc_o, acc_g, gs, rdp, w, wait_phi, refill0);
         f32x16 s1 = score_half<D, 1, 4>(cur, qf, rdp);
         bf16x8 bp1[2];
         softmax_half<D, 1>(s1, bp1, acc_o, sm, hi, lim, scale_log2, thr8);
-        pv_g<D, NW, true, true, 2, 4>(cur + T::KT_BYTES, myphi, pp, bp1, acc_o, acc_g, gs, pf, rdp, w, refill);
+        pv_g<D, NW, true, true, 2, 4>(Vc, myphi, pp, bp1, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
       } else if (S_) {
         f32x16 sc[2];
         score_unit<D, 4>(cur, qf, rdp, sc);
         bf16x8 bp[4];
         softmax_p<D>(sc, bp, acc_o, sm, hi, lim, scale_log2, thr8);
-        pv_g<D, NW, true, false, 0, 4>(cur + T::KT_BYTES, myphi, pp, bp, acc_o, acc_g, gs, pf, rdp, w, refill);
+        pv_g<D, NW, true, false, 0, 4>(Vc, myphi, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
       } else if (G_) {
-        bf16x8 bp[4];
-        pv_g<D, NW, false, true, 0, 4>(cur + T::KT_BYTES, myphi, pp, bp, acc_o, acc_g, gs, pf, rdp, w, refill);
+        bf16x8 bp[2];
+        pv_g<D, NW, false, true, 0, 2>(Vc, myphi, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill0);
+        pv_g<D, NW, false, true, 2, 4>(Vc, myphi, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
       }
       kcur = knext;
     };
     issue(kcur, st0);
-    if (G_) load_phi<GS::MTN>(rph, mt0, Npad, kcur, lane, myphi);
+    if (G_) {
+      load_phi<GS::MTN, 0>(rph, mt0, Npad, kcur, lane, myphi);
+      load_phi<GS::MTN, 1>(rph, mt0, Npad, kcur, lane, myphi);
+    }
     int b = 0;
     for (; b + 2 <= nunits; b += 2) {
       step(b, st0, st1);

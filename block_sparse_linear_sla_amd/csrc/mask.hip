@@ -144,67 +144,77 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const double* __restri
 }
 
 // S[bh, i, j] = qh[bh, i, :] . kh[bh, j, :] / sqrt(D) on the float64 matrix
-// cores (v_mfma_f64_16x16x4f64: lane l supplies A row l%16 / B column l%16 at
-// k = l/16; accumulator element i of lane l is row 4*i + l/16, column l%16).
-// 64x64 tile per workgroup, a 32x32 quarter (2x2 MFMA blocks) per wavefront,
-// operands staged in LDS 32 k at a time.
+// cores (v_mfma_f64_16x16x4f64: lane l supplies A row l%16 / B column l%16 and
+// one k per step; accumulator element i of lane l is row 4*i + l/16, column
+// l%16).  One workgroup per 32 x 32 tile of S (2 x 2 MFMA blocks); its four
+// wavefronts split the contraction into quarters of D/4, each loading its
+// operands for the whole quarter at once straight into registers (lane (r,
+// g) = (l%16, l/16) reads D/16 consecutive k of row r and supplies them at
+// successive steps; the order of the contraction is permuted the same way for
+// both operands).  The four partial tiles are summed in a fixed order through
+// LDS.  Workgroups are mapped so that each XCD walks a contiguous range of
+// heads, whose pooled vectors then stay in its L2.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void score_kernel(const double* __restrict__ qh,
                                                          const double* __restrict__ kh,
-                                                         double* __restrict__ S, int Nq, int Nk) {
-  constexpr int T = 64, KC = 32, LD = KC + 1;
-  __shared__ double As[T * LD];
-  __shared__ double Bs[T * LD];
-  const long long bh = blockIdx.z;
-  const int i0 = blockIdx.y * T, j0 = blockIdx.x * T;
-  const double* qb = qh + (size_t)bh * Nq * D;
-  const double* kb = kh + (size_t)bh * Nk * D;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wr = w >> 1, wc = w & 1;
-  const int l16 = lane & 15, kq = lane >> 4;
-  f64x4 acc[2][2];
+                                                         double* __restrict__ S, int Nq, int Nk,
+                                                         int tiles_j, int tiles) {
+  static_assert(kThreads == 256, "four wavefronts per tile");
+  constexpr int KL = D / 16;  // k per lane (and MFMA steps per wavefront)
+  __shared__ f64x4 part[4][4][64];  // [wavefront][MFMA block][lane]
+  const int lane = threadIdx.x & 63, kq = threadIdx.x >> 6;
+  // XCD-contiguous order of the workgroups (dispatch is round-robin over 8 XCDs)
+  const long long nb = gridDim.x, b = blockIdx.x;
+  const long long q8 = nb / 8, r8 = nb % 8, x = b % 8, loc = b / 8;
+  const long long wg = x < r8 ? x * (q8 + 1) + loc : r8 * (q8 + 1) + (x - r8) * q8 + loc;
+  const long long bh = wg / tiles;
+  const int t = (int)(wg % tiles);
+  const int i0 = (t / tiles_j) * 32, j0 = (t % tiles_j) * 32;
+  const int r = lane & 15, g = lane >> 4;
+  const int k0 = kq * (D / 4) + g * KL;
+  double a[2][KL], bv[2][KL];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int h = 0; h < 2; ++h) {
+    const bool ia = i0 + 16 * h + r < Nq, jb = j0 + 16 * h + r < Nk;
+    const double2* qa = reinterpret_cast<const double2*>(qh + ((size_t)bh * Nq + (ia ? i0 + 16 * h + r : 0)) * D + k0);
+    const double2* kb = reinterpret_cast<const double2*>(kh + ((size_t)bh * Nk + (jb ? j0 + 16 * h + r : 0)) * D + k0);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int kc = 0; kc < D; kc += KC) {
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < (T * KC) / kThreads; ++u) {
-      const int e = tid + kThreads * u;
-      const int r = e / KC, kk = e % KC;
-      As[r * LD + kk] = (i0 + r < Nq) ? qb[(size_t)(i0 + r) * D + kc + kk] : 0.0;
-      Bs[r * LD + kk] = (j0 + r < Nk) ? kb[(size_t)(j0 + r) * D + kc + kk] : 0.0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int s = 0; s < KC / 4; ++s) {
-      const int kk = 4 * s + kq;
-      double av[2], bv[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) av[a] = As[(32 * wr + 16 * a + l16) * LD + kk];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) bv[b] = Bs[(32 * wc + 16 * b + l16) * LD + kk];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[a], bv[b], acc[a][b], 0, 0, 0);
+    for (int s = 0; s < KL / 2; ++s) {
+      const double2 x2 = qa[s], y2 = kb[s];
+      a[h][2 * s] = ia ? x2.x : 0.0;
+      a[h][2 * s + 1] = ia ? x2.y : 0.0;
+      bv[h][2 * s] = jb ? y2.x : 0.0;
+      bv[h][2 * s + 1] = jb ? y2.y : 0.0;
     }
   }
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) acc[h][c] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int s = 0; s < KL; ++s)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) acc[h][c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[h][s], bv[c][s], acc[h][c], 0, 0, 0);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) part[kq][2 * h + c][lane] = acc[h][c];
+  __syncthreads();
+  // wavefront kq finishes MFMA block kq: the quarters summed in order 0..3
+  const f64x4 sum = ((part[0][kq][lane] + part[1][kq][lane]) + part[2][kq][lane]) + part[3][kq][lane];
   const double sd = sqrt((double)D);
+  const int h = kq >> 1, c = kq & 1;
+  const int j = j0 + 16 * c + r;
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int j = j0 + 32 * wc + 16 * b + l16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i0 + 32 * wr + 16 * a + 4 * i + kq;
-        if (r < Nq && j < Nk) S[((size_t)bh * Nq + r) * Nk + j] = acc[a][b][i] / sd;
-      }
-    }
+  for (int e = 0; e < 4; ++e) {
+    const int row = i0 + 16 * h + 4 * e + g;
+    if (row < Nq && j < Nk) S[((size_t)bh * Nq + row) * Nk + j] = sum[e] / sd;
+  }
 }
 
 __device__ __forceinline__ double wave_max(double v) {
@@ -262,7 +272,7 @@ __device__ __forceinline__ T wave_incl_scan(T v, int lane) {
 // valid elements with a strictly larger key, and the number of elements with
 // exactly that key.  BYMASS: weight = fixed-point mass, else weight = 1.
 template <int E, bool BYMASS>
-__device__ void radix_cut(const unsigned long long (&key)[E], unsigned valid_bits,
+__device__ void radix_cut(const unsigned long long (&key)[E], unsigned long long valid_bits,
                           unsigned long long target, unsigned* hcnt, unsigned long long* hmass,
                           int lane, unsigned long long& cut_key, unsigned& above_cnt,
                           unsigned long long& above_w, unsigned& tie_cnt) {
@@ -281,7 +291,7 @@ __device__ void radix_cut(const unsigned long long (&key)[E], unsigned valid_bit
     // clears above land before these atomics and the reads below.
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const bool in = ((valid_bits >> e) & 1u) && (pass == 0 || (key[e] >> (shift + 8)) == prefix);
+      const bool in = ((valid_bits >> e) & 1ull) && (pass == 0 || (key[e] >> (shift + 8)) == prefix);
       if (in) {
         const int bin = (int)((key[e] >> shift) & 255ull);
         atomicAdd(&hcnt[bin], 1u);
@@ -334,7 +344,7 @@ __device__ void radix_cut(const unsigned long long (&key)[E], unsigned valid_bit
       bool has = false;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const bool m = ((valid_bits >> e) & 1u) && (key[e] >> shift) == prefix;
+        const bool m = ((valid_bits >> e) & 1ull) && (key[e] >> shift) == prefix;
         mine = m ? key[e] : mine;
         has = has || m;
       }
@@ -344,6 +354,59 @@ __device__ void radix_cut(const unsigned long long (&key)[E], unsigned valid_bit
     }
   }
   cut_key = prefix;
+}
+
+// Largest 64-bit value over the wavefront, in every lane: quad exchanges and
+// row mirrors (DPP), then the 16- and 32-lane swaps.  Each step takes the
+// larger of the own value and the partner's, so every lane ends with the
+// same maximum.
+__device__ __forceinline__ void max_u64_step(uint32_t& lo, uint32_t& hi, uint32_t plo, uint32_t phi) {
+  const bool gt = phi > hi || (phi == hi && plo > lo);
+  lo = gt ? plo : lo;
+  hi = gt ? phi : hi;
+}
+template <int CTRL>
+__device__ __forceinline__ void max_u64_dpp(uint32_t& lo, uint32_t& hi) {
+  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xF, 0xF, false);
+  const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xF, 0xF, false);
+  max_u64_step(lo, hi, plo, phi);
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  max_u64_dpp<0xB1>(lo, hi);   // quad_perm [1, 0, 3, 2]
+  max_u64_dpp<0x4E>(lo, hi);   // quad_perm [2, 3, 0, 1]
+  max_u64_dpp<0x141>(lo, hi);  // row_half_mirror: the other quad of each 8
+  max_u64_dpp<0x140>(lo, hi);  // row_mirror: the other 8 of each 16
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    max_u64_step(lo, hi, a[0], b[0]);  // one of the two outputs is the own value,
+    max_u64_step(lo, hi, a[1], b[1]);  // the other the neighbouring row's
+  }
+  {
+    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    max_u64_step(lo, hi, a[0], b[0]);
+    max_u64_step(lo, hi, a[1], b[1]);
+  }
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Largest 32-bit value over the wavefront, in every lane (same exchange
+// pattern as wave_max_u64; each DPP step folds into one v_max_u32).
+template <int CTRL>
+__device__ __forceinline__ uint32_t max_u32_dpp(uint32_t v) {
+  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max_u32_dpp<0xB1>(v);
+  v = max_u32_dpp<0x4E>(v);
+  v = max_u32_dpp<0x141>(v);
+  v = max_u32_dpp<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
 }
 
 template <int E>
@@ -360,28 +423,126 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   const double* srow = S + (size_t)row * Nk;
 
   double sv[E];
-  unsigned valid_bits = 0;
+  unsigned long long valid_bits = 0;
   double mx = -INFINITY;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = lane + 64 * e;
     const bool ok = j < Nk;
     sv[e] = ok ? srow[j] : -INFINITY;
-    valid_bits |= (ok ? 1u : 0u) << e;
+    valid_bits |= (ok ? 1ull : 0ull) << e;
     mx = fmax(mx, sv[e]);
   }
   mx = wave_max(mx);
   double z = 0.0;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if ((valid_bits >> e) & 1u) z += exp(sv[e] - mx);
+  for (int e = 0; e < E; ++e) {
+    sv[e] = ((valid_bits >> e) & 1ull) ? exp(sv[e] - mx) : 0.0;
+    z += sv[e];
+  }
   z = wave_sum(z);
   unsigned long long key[E];
 #pragma unroll
   for (int e = 0; e < E; ++e)
-    key[e] = ((valid_bits >> e) & 1u) ? (unsigned long long)__double_as_longlong(exp(sv[e] - mx) / z) : 0ull;
+    key[e] = ((valid_bits >> e) & 1ull) ? (unsigned long long)__double_as_longlong(sv[e] / z) : 0ull;
 
   const int kk = min(k, Nk);
+  const unsigned long long target = p > 0.0 ? (unsigned long long)ceil(p * kMassScale) : 0ull;
+  unsigned long long tot = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((valid_bits >> e) & 1ull) tot += mass_of(key[e]);
+  tot = __shfl(wave_incl_scan(tot, lane), 63);
+  const bool p_never = p > 0.0 && tot < target;  // p is never reached: every block
+
+  // Fast path: take the blocks one at a time in the selection order (largest
+  // P first, ties to the lower block index) until both the count reaches k
+  // and the mass reaches p; the taken prefix is then exactly the first
+  // max(k, kp).  Used while that prefix is short and a row has at most 1024
+  // blocks (E <= 16, for registers); the rest take the radix descent below.
+  constexpr int kFastMax = 64;
+  if (E <= 16 && !p_never && kk < Nk) {
+    // key + 1 of the untaken blocks as high / low words, 0 for none (the P
+    // bit patterns are below 2^62); a taken block's words become 0
+    uint32_t kh[E], kl[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const unsigned long long m = ((valid_bits >> e) & 1ull) ? key[e] + 1ull : 0ull;
+      kh[e] = (uint32_t)(m >> 32);
+      kl[e] = (uint32_t)m;
+    }
+    unsigned long long taken = 0ull;
+    unsigned long long mass = 0;  // wave-uniform
+    int n = 0;
+    bool done = true;
+    while (n < kk || (p > 0.0 && mass < target)) {
+      if (n == kFastMax) {
+        done = false;
+        break;
+      }
+      // the largest high word, then the blocks that hold it
+      uint32_t h = kh[0];
+#pragma unroll
+      for (int e = 1; e < E; ++e) h = max(h, kh[e]);
+      const uint32_t th = wave_max_u32(h);
+      unsigned hit = 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e) hit |= (kh[e] == th ? 1u : 0u) << e;
+      uint32_t tl;
+      const unsigned long long hl = __ballot(hit != 0u);
+      if (__ballot(__popc(hit) > 1) != 0ull || __popcll(hl) > 1) {
+        // several blocks share it: the largest low word among them
+        uint32_t l = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) l = ((hit >> e) & 1u) ? max(l, kl[e]) : l;
+        tl = wave_max_u32(l);
+        unsigned h2 = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) h2 |= (((hit >> e) & 1u) && kl[e] == tl ? 1u : 0u) << e;
+        hit = h2;
+      } else {
+        // a single block: its low word, read from its lane
+        uint32_t l = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) l = ((hit >> e) & 1u) ? kl[e] : l;
+        tl = (uint32_t)__builtin_amdgcn_readlane((int)l, __ffsll((long long)hl) - 1);
+      }
+      // the first block of this lane holding the maximum (the lower index on
+      // equal keys), the lowest such lane in the wavefront
+      const int ef = __ffs(hit) - 1;
+      const unsigned long long tm = __ballot(hit != 0u);
+      int owner = __ffsll((long long)tm) - 1;
+      if (__popcll(tm) > 1) {
+        const int jmin = wave_min_int(hit != 0u ? lane + 64 * ef : 0x7fffffff);
+        owner = jmin & 63;
+      }
+      if (lane == owner) {
+        taken |= 1ull << ef;
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (e == ef) {
+            kh[e] = 0u;
+            kl[e] = 0u;
+          }
+      }
+      const unsigned long long top = (((unsigned long long)th << 32) | tl) - 1ull;
+      mass += mass_of(top);
+      ++n;
+    }
+    if (done) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const unsigned long long sm = __ballot((taken >> e) & 1ull);
+        if (lane == 0) {
+          if (2 * e < W) bits[(size_t)row * W + 2 * e] = (uint32_t)(sm & 0xffffffffull);
+          if (2 * e + 1 < W) bits[(size_t)row * W + 2 * e + 1] = (uint32_t)(sm >> 32);
+        }
+      }
+      if (lane == 0) counts[row] = n;
+      return;
+    }
+  }
+
   unsigned long long kkey = 0, kw = 0, pkey = 0, pw = 0;
   unsigned kabove = 0, ktie = 0, pabove = 0, ptie = 0;
   // Top-k cut (the kk-th element in the order)
@@ -390,13 +551,7 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   // Top-p cut (the element whose cumulative mass first reaches p)
   int kp = 0;
   if (p > 0.0) {
-    const unsigned long long target = (unsigned long long)ceil(p * kMassScale);
-    unsigned long long tot = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if ((valid_bits >> e) & 1u) tot += mass_of(key[e]);
-    tot = __shfl(wave_incl_scan(tot, lane), 63);
-    if (tot < target) {
+    if (p_never) {
       kp = Nk;  // p is never reached: every block
     } else {
       radix_cut<E, true>(key, valid_bits, target, hcnt, hmass, lane, pkey, pabove, pw, ptie);
@@ -415,7 +570,7 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   int ties_before = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool valid = (valid_bits >> e) & 1u;
+    const bool valid = (valid_bits >> e) & 1ull;
     const bool gt = valid && nsel > 0 && key[e] > ckey;
     const bool eq = valid && nsel > 0 && key[e] == ckey;
     const unsigned long long eqm = __ballot(eq);
@@ -547,11 +702,12 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
     kh = khat;
   }
 
-  const dim3 gscore((unsigned)((s.Nk + 63) / 64), (unsigned)((s.Nq + 63) / 64), (unsigned)BH);
+  const int tiles_j = (s.Nk + 31) / 32, tiles = ((s.Nq + 31) / 32) * tiles_j;
+  const dim3 gscore((unsigned)(BH * tiles));
   if (s.d == 128)
-    hipLaunchKernelGGL((score_kernel<128>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk);
+    hipLaunchKernelGGL((score_kernel<128>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk, tiles_j, tiles);
   else
-    hipLaunchKernelGGL((score_kernel<64>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk);
+    hipLaunchKernelGGL((score_kernel<64>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk, tiles_j, tiles);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   int E = 1;
