@@ -25,6 +25,11 @@ SMALL = [
     ("bf16-topk-only", "bf16", 1500, 128, 128, 64, 0.25, 0.0, False),
     ("bf16-full", "bf16", 700, 128, 128, 64, 1.0, 0.5, False),
     ("bf16-p1", "bf16", 1500, 128, 128, 64, 0.0, 1.0, False),
+    # more than 64 kept blocks per row: the one-at-a-time selection hands over
+    # to the radix descent
+    ("bf16-long-prefix", "bf16", 8192, 128, 128, 64, 0.6, 0.5, False),
+    # Top-p decides the count (k = 1)
+    ("bf16-p-dominant", "bf16", 3000, 128, 128, 64, 0.02, 0.95, False),
 ]
 
 
