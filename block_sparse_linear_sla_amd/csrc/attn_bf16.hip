@@ -553,7 +553,8 @@ __device__ __forceinline__ void pv_g(const char* Vc, const char* Ph, const PhiPl
 // Linear-branch preparation of one head's chunk of key blocks (one
 // workgroup, four wavefronts): phi(K) = elu(K) + 1 rounded to bf16 into the
 // [d/32][Npad][32] array (zero for keys >= N), and the chunk's partial totals
-// H = sum_u phi(k_u)^T v_u and z = sum_u phi(k_u).  64-key units of K and V
+// H = sum_u phi(k_u)^T v_u (in MFMA fragment order: 32 x 32 tile (mt, nt),
+// lane, accumulator element) and z = sum_u phi(k_u).  64-key units of K and V
 // stream through two LDS stages.  Wavefront w owns the G tiles of the
 // attention kernel's split (GSplit<D, 4>): its phi(K)^T operand is read
 // transposed from the K tile with phi applied in fp32 and split into bf16 hi
@@ -667,15 +668,15 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   if (x < nun) step(x, k0, v0, k1, v1);
   wait_vm<0>();
 
+  // H in MFMA fragment order (tile (mt, nt), lane, accumulator element): the
+  // order in which the attention kernel's epilogue holds G
   float* out = hpart + ((size_t)bh * nchunk + chunk) * (D * D + D);
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
-    const int nt = GS::nt(w, u), mu = mt + GS::m(u);
+    const int tile = (mt + GS::m(u)) * GS::NCT + GS::nt(w, u);
+    float4* o4 = reinterpret_cast<float4*>(out + ((size_t)tile * 64 + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int dk = 32 * mu + 8 * (i >> 2) + 4 * hi + (i & 3);
-      out[dk * D + 32 * nt + l32] = acc[u][i];
-    }
+    for (int c = 0; c < 4; ++c) o4[c] = make_float4(acc[u][4 * c], acc[u][4 * c + 1], acc[u][4 * c + 2], acc[u][4 * c + 3]);
   }
   // column sums of phi(K) over the chunk for this wavefront's row tile
   const float zt = zpart + __shfl_xor(zpart, 32);
@@ -886,9 +887,21 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
   char* HuLo = st1;
   float* zu = reinterpret_cast<float*>(phr);
   if (LIN) {
+    const float* Hh = htot + (size_t)bh * (D * D + D);
+    // this wavefront's tiles of H (fragment order, as G is held), loaded
+    // before the barrier so that the wait covers their latency
+    float4 hf[GS::TPW][4];
+    if (lin) {
+#pragma unroll
+      for (int u = 0; u < GS::TPW; ++u) {
+        const int tile = (mt0 + GS::m(u)) * GS::NCT + GS::nt(w, u);
+        const float4* h4 = reinterpret_cast<const float4*>(Hh + ((size_t)tile * 64 + lane) * 16);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) hf[u][c] = h4[c];
+      }
+    }
     __syncthreads();  // every wavefront is done with the stages and its phi(K) region
     if (lin) {
-      const float* Hh = htot + (size_t)bh * (D * D + D);
       // H_u^T = (H - G)^T for this wavefront's G tiles as hi + lo bf16 planes
       // (rows d_v, 16-wide d_k slices)
 #pragma unroll
@@ -898,11 +911,12 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const int dk = 32 * mt + 8 * i4 + 4 * hi;
+          const float hq[4] = {hf[u][i4].x, hf[u][i4].y, hf[u][i4].z, hf[u][i4].w};
           float hv[4], lv[4];
           uint32_t hb[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            hv[r] = Hh[(dk + r) * D + dv] - acc_g[u][4 * i4 + r];
+            hv[r] = hq[r] - acc_g[u][4 * i4 + r];
             hb[r] = pk_bf16(hv[r], 0.f) & 0xffffu;
             lv[r] = hv[r] - bf2f(hb[r]);
           }
@@ -926,28 +940,35 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
         }
       }
     }
+    // phi(Q) of every k-step: 8 values per lane, split into bf16 hi + lo
+    float fq[LIN ? NTQ : 1][8];
+    if (lin && qw) {
+#pragma unroll
+      for (int t = 0; t < NTQ; ++t) {
+        const uint4 qv = __builtin_bit_cast(uint4, qf[t]);
+        uint32_t fh[8];
+        float fl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          fq[t][e] = phi(bf2f(elem(qv, e)));
+          fh[e] = pk_bf16(fq[t][e], 0.f) & 0xffffu;
+          fl[e] = fq[t][e] - bf2f(fh[e]);
+        }
+        qh[t] = make_uint4(fh[0] | (fh[1] << 16), fh[2] | (fh[3] << 16), fh[4] | (fh[5] << 16), fh[6] | (fh[7] << 16));
+        ql[t] = make_uint4(pk_bf16(fl[0], fl[1]), pk_bf16(fl[2], fl[3]), pk_bf16(fl[4], fl[5]), pk_bf16(fl[6], fl[7]));
+      }
+    }
     __syncthreads();  // H_u^T and z_u complete
     if (lin && qw) {
-      // phi(Q) of every k-step: 8 values per lane, split into bf16 hi + lo;
       // den = phi(Q) . z_u (this lane's half of d, then the pair sum)
       float dpart = 0.f;
 #pragma unroll
       for (int t = 0; t < NTQ; ++t) {
-        const uint4 qv = __builtin_bit_cast(uint4, qf[t]);
         const float4 z0 = *reinterpret_cast<const float4*>(zu + 16 * t + 8 * hi);
         const float4 z1 = *reinterpret_cast<const float4*>(zu + 16 * t + 8 * hi + 4);
         const float zz[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
-        float f[8], fl[8];
-        uint32_t fh[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          f[e] = phi(bf2f(elem(qv, e)));
-          fh[e] = pk_bf16(f[e], 0.f) & 0xffffu;
-          fl[e] = f[e] - bf2f(fh[e]);
-          dpart = fmaf(f[e], zz[e], dpart);
-        }
-        qh[t] = make_uint4(fh[0] | (fh[1] << 16), fh[2] | (fh[3] << 16), fh[4] | (fh[5] << 16), fh[6] | (fh[7] << 16));
-        ql[t] = make_uint4(pk_bf16(fl[0], fl[1]), pk_bf16(fl[2], fl[3]), pk_bf16(fl[4], fl[5]), pk_bf16(fl[6], fl[7]));
+        for (int e = 0; e < 8; ++e) dpart = fmaf(fq[t][e], zz[e], dpart);
       }
       const float den = dpart + __shfl_xor(dpart, 32);
       wl_den = wl_ / den;
@@ -956,22 +977,27 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
   if (!qw) return;
   const int lb = lane_base(lane);
   const size_t orow = ((size_t)bh * N + min(q, N - 1)) * D;
-  // Output tile mt (32 d): O = ws_l O_s + wl_den num, num^T = H_u^T phi(Q)^T.
-  // Each 16-byte store holds 8 consecutive d of one query: lanes l and l^32
-  // hold the two 4-d halves of every 8-d chunk and swap one of them.
+  // O = ws_l O_s + wl_den num, num^T = H_u^T phi(Q)^T (the D/32 output tiles
+  // accumulated together).  Each 16-byte store holds 8 consecutive d of one
+  // query: lanes l and l^32 hold the two 4-d halves of every 8-d chunk and
+  // swap one of them.
+  f32x16 acc_n[LIN ? D / 32 : 1];
 #pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) {
-    f32x16 acc_n = f32x16{};
-    if (LIN && lin) {
+  for (int mt = 0; mt < (LIN ? D / 32 : 1); ++mt) acc_n[mt] = f32x16{};
+  if (LIN && lin) {
 #pragma unroll
-      for (int t = 0; t < NTQ; ++t) {
+    for (int t = 0; t < NTQ; ++t)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
         const uint4 ah = rd16(HuHi + t * T::HPB + mt * 1024 + lb);
         const uint4 al = rd16(HuLo + t * T::HPB + mt * 1024 + lb);
-        acc_n = mfma(as_bf16x8(ah), as_bf16x8(qh[t]), acc_n);
-        acc_n = mfma(as_bf16x8(ah), as_bf16x8(ql[t]), acc_n);
-        acc_n = mfma(as_bf16x8(al), as_bf16x8(qh[t]), acc_n);
+        acc_n[mt] = mfma(as_bf16x8(ah), as_bf16x8(qh[t]), acc_n[mt]);
+        acc_n[mt] = mfma(as_bf16x8(ah), as_bf16x8(ql[t]), acc_n[mt]);
+        acc_n[mt] = mfma(as_bf16x8(al), as_bf16x8(qh[t]), acc_n[mt]);
       }
-    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint2 pv[2];
@@ -982,7 +1008,7 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           o[r] = ws_l * acc_o[mt][4 * i4 + r];
-          if (LIN) o[r] = fmaf(wl_den, acc_n[4 * i4 + r], o[r]);
+          if (LIN) o[r] = fmaf(wl_den, acc_n[LIN ? mt : 0][4 * i4 + r], o[r]);
         }
         pv[c] = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
       }

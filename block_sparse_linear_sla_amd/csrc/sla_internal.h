@@ -24,7 +24,9 @@ struct WsLayout {
   size_t counts;       // int32 [R]
   size_t bits;         // uint32 [R * words]
   size_t hpart;        // linear summary partials, float [B*H*nchunk*(d*d + d)]
-  size_t htot;         // linear summaries, float [B*H*(d*d + d)]
+  size_t htot;         // linear summaries, float [B*H*(d*d + d)]: H then z; the
+                       // bf16 path keeps H in MFMA fragment order (32 x 32 tile
+                       // (mt, nt), lane, element), the fp32 path row-major
   size_t pk;           // bf16 path: phi(K), bf16 [B*H][d/32][Nk*bk][32] (keys >= N zero)
   size_t total;
   int nchunk;          // key-block chunks per head in the summary pass
