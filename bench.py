@@ -33,7 +33,7 @@ METRIC = "dense-equivalent attention TFLOPS + speedup vs dense at 97% sparsity, 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 FUSED_SRC = os.path.join(ROOT, "block_sparse_linear_sla_amd", "csrc", "attn_bf16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_kernel_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_fused_traffic.json")
 
 
 def parse():
@@ -195,7 +195,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": fused_flops / (st_fused * 1e-3) / 1e12,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": fused_flops / (st_fused * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                     "traffic": stored_traffic(), "kernel": f"fused_kernel<d={wl.d},bq={wl.bq},bk={wl.bk}>",
+                     "traffic": stored_traffic(), "kernel": f"attn_kernel<d={wl.d},bq={wl.bq},bk={wl.bk},fused>",
                      "flops_per_launch": fused_flops, "ms_per_launch": st_fused},
         "mask_roofline": {"bound": "hbm", "achieved": mask_bytes / (st_mask * 1e-3) / 1e9,
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -134,10 +134,10 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
  * sla_kv_prepare: one pass over K and V that leaves in the workspace what the
  * fused stage reads: the per-head linear-attention totals H = sum_u phi(k_u)^T
  * v_u ([d, d]) and z = sum_u phi(k_u) ([d]) over every key (float32) and, for
- * bf16, phi(K) in the layout of K ([B, H, N, d] bf16) plus per-key-block sums
- * of phi(K).  V is not copied: the attention kernels read V and K as the
- * caller passed them.  alpha (DEVICE fp32 [H]) may be NULL; heads whose alpha
- * is exactly 1 skip the pass when it is given.
+ * bf16, phi(K) in 32-wide d slices (bf16 [B, H, d/32, Nk*bk, 32], keys past N
+ * zero).  V is not copied: the attention kernels read V and K as the caller
+ * passed them.  alpha (DEVICE fp32 [H]) may be NULL; heads whose alpha is
+ * exactly 1 skip the pass when it is given.
  *
  * sla_fused_fwd: O = alpha_h * O_s + (1 - alpha_h) * O_l over the given mask,
  * with O_l = phi(q) (H - G) / phi(q) (z - g), where G, g are the same sums
