@@ -555,12 +555,14 @@ __device__ __forceinline__ void pv_g(const char* Vc, const char* Ph, const PhiPl
 // [d/32][Npad][32] array (zero for keys >= N), and the chunk's partial totals
 // H = sum_u phi(k_u)^T v_u (in MFMA fragment order: 32 x 32 tile (mt, nt),
 // lane, accumulator element) and z = sum_u phi(k_u).  64-key units of K and V
-// stream through two LDS stages.  Wavefront w owns the G tiles of the
-// attention kernel's split (GSplit<D, 4>): its phi(K)^T operand is read
-// transposed from the K tile with phi applied in fp32 and split into bf16 hi
-// + lo (H keeps ~16 mantissa bits), and the V^T operand is read transposed
-// from the V tile.  Heads whose alpha is exactly 1 are skipped when alpha is
-// given.
+// stream through two LDS stages.  Each thread converts its 16-byte chunks of
+// the unit's K tile once: phi goes to global memory, and its bf16 hi part
+// replaces K in the tile while the lo part (phi - hi, bf16) goes to a second
+// tile of the same layout, so H keeps ~16 mantissa bits.  After a barrier,
+// wavefront w accumulates the G tiles of the attention kernel's split
+// (GSplit<D, 4>) from transposed reads of both phi tiles and of the V tile,
+// and the column sums z with v_dot2 over the same fragments.  Heads whose
+// alpha is exactly 1 are skipped when alpha is given.
 template <int D, int BK>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ K,
                                                    const uint16_t* __restrict__ V,
@@ -573,11 +575,12 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   static_assert(GS::MTN == 1, "one row tile per wavefront");
   constexpr int SUB = BK / KU;                  // units per key block
   constexpr int TPW = GS::TPW;
-  constexpr int PCH = KU * (D / 8) / 256;       // 16-byte phi(K) chunks per thread and unit
+  constexpr int PCH = KU * (D / 8) / 256;       // 16-byte K chunks per thread and unit
   __shared__ __attribute__((aligned(16))) char k0[T::KT_BYTES];
   __shared__ __attribute__((aligned(16))) char k1[T::KT_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[T::KT_BYTES];
   __shared__ __attribute__((aligned(16))) char v1[T::KT_BYTES];
+  __shared__ __attribute__((aligned(16))) char plo[T::KT_BYTES];
 
   const long long bh = blockIdx.x / nchunk;
   const int chunk = blockIdx.x % nchunk;
@@ -597,15 +600,16 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   const int nun = max(0, je - jb) * SUB;        // units of the chunk
   const int mt = GS::mt0(w);                    // the d_k row tile of this wavefront
   const bool zown = GS::zown(w);
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   f32x16 acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
   float zpart = 0.f;
 
-  auto step = [&](int x, const char* ks, const char* vs, char* nks, char* nvs) __attribute__((always_inline)) {
+  auto step = [&](int x, char* ks, const char* vs, char* nks, char* nvs) __attribute__((always_inline)) {
     wait_vm<0>();     // this wavefront's loads of unit x have landed
-    __syncthreads();  // ... and every wavefront's; unit x-1 consumed
+    __syncthreads();  // ... and every wavefront's; unit x-1 consumed (its phi tiles read)
     if (x + 1 < nun) {
       const int kn = (jb * SUB + x + 1) * KU;
       lp.load(rk, kn, nks);
@@ -613,41 +617,45 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
     }
     const int key0 = (jb * SUB + x) * KU;
     const int lim = min(KU, N - key0);          // keys of the unit below N
-    // phi(K) into the [d/32][Npad][32] array: thread chunk ch is d slice ch /
-    // 256, key (ch / 4) % 64, 8 d at 8 (ch % 4) - consecutive threads write
-    // consecutive 16 bytes
+    // thread chunk ch: d slice ch / 256, key (ch / 4) % 64, 8 d at 8 (ch % 4);
+    // consecutive threads write consecutive 16 bytes of the phi(K) array
 #pragma unroll
     for (int c = 0; c < PCH; ++c) {
       const int ch = tid + 256 * c;
       const int dt = ch / (4 * KU), r = (ch / 4) % KU, c4 = ch % 4;
       const int cc = 4 * dt + c4;               // 16-byte chunk of the key row
-      const uint4 kv = rd16(ks + (cc >> 3) * T::KHALF + r * 128 + 16 * ((cc & 7) ^ sw(r)));
-      uint32_t o[4];
+      char* at = ks + (cc >> 3) * T::KHALF + r * 128 + 16 * ((cc & 7) ^ sw(r));
+      const uint4 kv = rd16(at);
+      uint32_t oh[4], ol[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = pk_bf16(phi(bf2f(elem(kv, 2 * e))), phi(bf2f(elem(kv, 2 * e + 1))));
-      const uint4 ov = r < lim ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(Pb + ((size_t)dt * Npad + key0 + r) * 32 + 8 * c4) = ov;
+      for (int e = 0; e < 4; ++e) {
+        float f0 = phi(bf2f(elem(kv, 2 * e))), f1 = phi(bf2f(elem(kv, 2 * e + 1)));
+        if (r >= lim) f0 = f1 = 0.f;
+        oh[e] = pk_bf16(f0, f1);
+        ol[e] = pk_bf16(f0 - bf2f(oh[e] & 0xffffu), f1 - bf2f(oh[e] >> 16));
+      }
+      const uint4 hv = make_uint4(oh[0], oh[1], oh[2], oh[3]);
+      *reinterpret_cast<uint4*>(Pb + ((size_t)dt * Npad + key0 + r) * 32 + 8 * c4) = hv;
+      *reinterpret_cast<uint4*>(at) = hv;  // this thread's own chunk: no other thread touches it
+      *reinterpret_cast<uint4*>(plo + (at - ks)) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
     }
+    __syncthreads();  // both phi tiles complete
     // H += phi(K)^T V (hi + lo) and z over the 4 key planes of the unit
 #pragma unroll
     for (int pl = 0; pl < KU / 16; ++pl) {
-      const uint4 kt = __builtin_bit_cast(uint4, rdp.vt(ks, mt, pl));
-      float f[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        // element e of the fragment is key 16 pl + 4 hi + (e & 3) + 8 (e >> 2) of the unit
-        const int key = 16 * pl + 4 * hi + (e & 3) + 8 * (e >> 2);
-        f[e] = key < lim ? phi(bf2f(elem(kt, e))) : 0.f;
-        zpart += f[e];
+      const bf16x8 ah = rdp.vt(ks, mt, pl);
+      const bf16x8 al = rdp.vt(plo, mt, pl);
+      if (zown) {
+        const uint4 h4 = __builtin_bit_cast(uint4, ah), l4 = __builtin_bit_cast(uint4, al);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.x), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.y), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.z), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.w), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.x), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.y), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.z), ones, zpart, false);
+        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.w), ones, zpart, false);
       }
-      uint32_t fh[4], fl[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        fh[e] = pk_bf16(f[2 * e], f[2 * e + 1]);
-        fl[e] = pk_bf16(f[2 * e] - bf2f(fh[e] & 0xffffu), f[2 * e + 1] - bf2f(fh[e] >> 16));
-      }
-      const bf16x8 ah = as_bf16x8(make_uint4(fh[0], fh[1], fh[2], fh[3]));
-      const bf16x8 al = as_bf16x8(make_uint4(fl[0], fl[1], fl[2], fl[3]));
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const bf16x8 b = rdp.vt(vs, GS::nt(w, u), pl);
