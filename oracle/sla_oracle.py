@@ -199,6 +199,66 @@ def mask(Q, K, bq: int, bk: int, k_frac: float, p: float, Wq=None, Wk=None,
     return row_ptr, col_idx, meta
 
 
+# ---------------------------------------------------------------- SoftTop-k
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """Logistic function 1 / (1 + exp(-x)), evaluated without overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+
+
+def soft_topk_row(S_row: np.ndarray, k: int, T: float) -> Tuple[np.ndarray, float]:
+    """SoftTop-k of one row of pooled logits [SLA2 §四: in the router's first
+    training stage the hard Top-k is replaced by a SoftTop-k made of a sigmoid
+    with a temperature, which lets gradients through].
+
+    Reading (the pages name only the sigmoid and the temperature): the soft
+    weight of block j is M_j = sigmoid((S_j - tau) / T), with the one threshold
+    tau for which the weights sum to k, so the soft mask keeps k blocks' worth
+    of weight and tends to the hard Top-k indicator as T -> 0.  k = 0 gives all
+    zeros and k = Nk all ones (tau = +inf / -inf).  tau is found by bisection
+    on the decreasing function f(tau) = sum_j sigmoid((S_j - tau) / T) - k,
+    run until the bracket stops shrinking.  Returns (M, tau)."""
+    S_row = np.asarray(S_row, dtype=np.float64)
+    Nk = len(S_row)
+    if k <= 0:
+        return np.zeros(Nk), math.inf
+    if k >= Nk:
+        return np.ones(Nk), -math.inf
+    lo = float(S_row.min()) - 80.0 * T   # f(lo) > 0: every weight ~ 1
+    hi = float(S_row.max()) + 80.0 * T   # f(hi) < 0: every weight ~ 0
+    while True:
+        mid = 0.5 * (lo + hi)
+        if mid <= lo or mid >= hi:
+            break
+        if sigmoid((S_row - mid) / T).sum() > k:
+            lo = mid
+        else:
+            hi = mid
+    tau = 0.5 * (lo + hi)
+    return sigmoid((S_row - tau) / T), tau
+
+
+def soft_topk(Q, K, bq: int, bk: int, k_frac: float, T: float, Wq=None, Wk=None) -> np.ndarray:
+    """SoftTop-k mask of every (b, h, query block): [B, H, Nq, Nk] weights from
+    the pooled (and optionally routed) block logits, k = ceil(k_frac * Nk)
+    as for the hard mask."""
+    Q = as_f64(Q)
+    K = as_f64(K)
+    Wq = None if Wq is None else as_f64(Wq)
+    Wk = None if Wk is None else as_f64(Wk)
+    B, H, N, d = Q.shape
+    Nq, Nk = n_blocks(N, bq), n_blocks(N, bk)
+    k = k_from_frac(k_frac, Nk)
+    M = np.empty((B, H, Nq, Nk))
+    for b in range(B):
+        for h in range(H):
+            S = block_scores(route(pool(Q[b, h], bq), Wq), route(pool(K[b, h], bk), Wk))
+            for i in range(Nq):
+                M[b, h, i], _ = soft_topk_row(S[i], k, T)
+    return M
+
+
 # ---------------------------------------------------------------- branches
 def _keys_of(blocks: Iterable[int], bk: int, N: int) -> np.ndarray:
     """Token indices of the given key blocks (partial last block clipped)."""
