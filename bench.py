@@ -221,8 +221,8 @@ def main():
         res["dense_TFLOPS"] = dense_flops / (t_dense * 1e-3) / 1e12
         res["speedup_vs_dense"] = t_dense / ms_step
 
-    # the sparse branch alone (sla_sparse_fwd: V transpose + sparse kernel) on
-    # this step's mask, for the executed-block rate of the attention kernel
+    # the sparse branch alone (sla_sparse_fwd) on this step's mask, for the
+    # executed-block rate of the attention kernel
     S.sla_sparse_fwd(q, k, v, wl.bq, wl.bk, rp, ci, out=out, ws=ws)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -234,6 +234,19 @@ def main():
     t_sp = e0.elapsed_time(e1) / args.steps
     res["sparse_fwd_ms"] = t_sp
     res["sparse_fwd_executed_TFLOPS"] = pair_flops * nnz / (t_sp * 1e-3) / 1e12
+
+    # SoftTop-k weights of every mask row (pool + logits + threshold solve),
+    # the router-training form of the selection, at temperature 0.5
+    msoft = torch.empty((wl.B, wl.H, wl.Nq, wl.Nk), dtype=torch.float32, device=dev)
+    S.sla_soft_topk(q, k, wl.bq, wl.bk, wl.k_frac, 0.5, wq, wk, out=msoft, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        S.sla_soft_topk(q, k, wl.bq, wl.bk, wl.k_frac, 0.5, wq, wk, out=msoft, ws=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    res["soft_topk_ms"] = e0.elapsed_time(e1) / args.steps
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * (1 << 20) // 4

@@ -23,7 +23,7 @@ LIB_PATH = os.environ.get("SLA_LIB", os.path.join(_HERE, "libsla.so"))
 SLA_F32, SLA_BF16 = 0, 1
 STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
           -3: "SLA_ERR_WORKSPACE", -4: "SLA_ERR_CAPACITY", -5: "SLA_ERR_HIP"}
-EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_sparse_fwd",
+EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_soft_topk", "sla_sparse_fwd",
            "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
            "sla_dense_fwd", "sla_status_string")
 
@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.sla_mask_capacity.argtypes = [P]
         L.sla_mask_capacity.restype = ctypes.c_int64
         L.sla_mask.argtypes = [P, S, vp, vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
+        L.sla_soft_topk.argtypes = [P, S, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_linear_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_attn_fwd.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
@@ -71,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
-        for fn in ("sla_mask", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
+        for fn in ("sla_mask", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
                    "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -154,6 +155,20 @@ def sla_mask(q, k, bq: int, bk: int, k_frac: float, p: float, wq=None, wk=None,
                                       _ptr(rp), _ptr(ci), ci.numel(), _ptr(logits), _ptr(w),
                                       w.numel(), _stream()))
     return (rp, ci, logits) if return_logits else (rp, ci)
+
+
+def sla_soft_topk(q, k, bq: int, bk: int, k_frac: float, T: float, wq=None, wk=None,
+                  out: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """SoftTop-k weights, float32 [B, H, Nq, Nk] (rows sum to ceil(k_frac * Nk))."""
+    _need(q, k, like=q)
+    prob, sel = problem(q, bq, bk), select(k_frac, 0.0, wq, wk)
+    B, H = q.shape[:2]
+    Nq, Nk = -(-q.shape[2] // bq), -(-q.shape[2] // bk)
+    m = out if out is not None else torch.empty((B, H, Nq, Nk), dtype=torch.float32, device=q.device)
+    w = ws if ws is not None else workspace(prob, sel, q.device)
+    _check("sla_soft_topk", lib().sla_soft_topk(ctypes.byref(prob), ctypes.byref(sel), float(T), _ptr(q),
+                                                _ptr(k), _ptr(m), _ptr(w), w.numel(), _stream()))
+    return m
 
 
 def sla_sparse_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None, ws=None):

@@ -22,6 +22,8 @@
 //             and Top-p cut points, n = max(k, kp), bitmask of the kept blocks
 //   scan      one workgroup: exclusive scan of the per-row counts -> row_ptr
 //   emit      one wavefront per row: bitmask -> ascending col_idx
+#include <cfloat>
+
 #include "sla_internal.h"
 
 namespace sla {
@@ -586,6 +588,77 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   if (lane == 0) counts[row] = nsel;
 }
 
+// ---------------------------------------------------------------- SoftTop-k
+// One wavefront per mask row: M_j = sigmoid((S_j - tau) / T) with tau such
+// that the weights of the row sum to k [SLA2 write-up §四: a sigmoid with a
+// temperature replaces the hard Top-k in the router's first training stage].
+// tau by a safeguarded Newton iteration on f(tau) = sum_j sigmoid((S_j -
+// tau)/T) - k, decreasing in tau with f'(tau) = -sum_j M_j (1 - M_j) / T,
+// inside a bisection bracket that starts where every weight is ~1 (f > 0)
+// and ~0 (f < 0).  float64 throughout; the weights are written as float32.
+__device__ __forceinline__ double sigmoid_f64(double x) {
+  const double e = exp(-fabs(x));
+  return x >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict__ S, long long R, int Nk,
+                                                        int k, double T, float* __restrict__ M) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= R) return;  // whole wavefront; the kernel has no barrier
+  const double* srow = S + (size_t)row * Nk;
+  float* mrow = M + (size_t)row * Nk;
+  double sv[E];
+  double lo_s = INFINITY, hi_s = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    sv[e] = j < Nk ? srow[j] : 0.0;
+    if (j < Nk) {
+      lo_s = fmin(lo_s, sv[e]);
+      hi_s = fmax(hi_s, sv[e]);
+    }
+  }
+  lo_s = -wave_max(-lo_s);
+  hi_s = wave_max(hi_s);
+  if (k <= 0 || k >= Nk) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int j = lane + 64 * e;
+      if (j < Nk) mrow[j] = k <= 0 ? 0.f : 1.f;
+    }
+    return;
+  }
+  double lo = lo_s - 80.0 * T, hi = hi_s + 80.0 * T;  // f(lo) > 0 > f(hi)
+  double tau = 0.5 * (lo + hi);
+  const double inv_t = 1.0 / T;
+  for (int it = 0; it < 200; ++it) {  // uniform: every lane sees the same sums
+    double f = 0.0, g = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (lane + 64 * e < Nk) {
+        const double m = sigmoid_f64((sv[e] - tau) * inv_t);
+        f += m;
+        g += m * (1.0 - m);
+      }
+    }
+    f = wave_sum(f) - (double)k;
+    g = wave_sum(g) * inv_t;
+    if (f == 0.0) break;
+    if (f > 0.0) lo = tau; else hi = tau;
+    const double nt = g > 0.0 ? tau + f / g : 0.5 * (lo + hi);
+    const double next = (nt > lo && nt < hi) ? nt : 0.5 * (lo + hi);
+    if (next == tau || hi - lo <= 4.0 * DBL_EPSILON * fmax(fabs(lo), fabs(hi))) break;
+    tau = next;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    if (j < Nk) mrow[j] = (float)sigmoid_f64((sv[e] - tau) * inv_t);
+  }
+}
+
 // Exclusive scan of counts[R] into row_ptr[R + 1] with one workgroup.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts, long long R,
                                                     int* __restrict__ row_ptr) {
@@ -654,17 +727,14 @@ hipError_t launch_select(const double* S, long long R, int Nk, int k, double p, 
 
 }  // namespace
 
-hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const float* Wk,
-                       const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
-                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st) {
+namespace {
+
+// Pooling, optional router and the pooled logits S [B, H, Nq, Nk] (float64).
+hipError_t launch_scores(const Shape& s, const float* Wq, const float* Wk, const void* Q, const void* K,
+                         double* S, char* ws, const WsLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H;
-  const long long R = s.R();
   double* qbar = reinterpret_cast<double*>(ws + L.qbar);
   double* kbar = reinterpret_cast<double*>(ws + L.kbar);
-  double* S = logits_out ? logits_out : reinterpret_cast<double*>(ws + L.S);
-  int* counts = reinterpret_cast<int*>(ws + L.counts);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
-  const int W = s.words();
 
   const dim3 gpool((unsigned)(BH * (s.Nq + s.Nk)));
 #define SLA_POOL(T, DD)                                                                          \
@@ -708,7 +778,48 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
     hipLaunchKernelGGL((score_kernel<128>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk, tiles_j, tiles);
   else
     hipLaunchKernelGGL((score_kernel<64>), gscore, dim3(kThreads), 0, st, qh, kh, S, s.Nq, s.Nk, tiles_j, tiles);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int E>
+hipError_t launch_soft(const double* S, long long R, int Nk, int k, double T, float* M, hipStream_t st) {
+  hipLaunchKernelGGL((soft_topk_kernel<E>), dim3((unsigned)((R + 3) / 4)), dim3(kThreads), 0, st, S, R, Nk,
+                     k, T, M);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_soft_topk(const Shape& s, int k, double T, const float* Wq, const float* Wk,
+                            const void* Q, const void* K, float* M, char* ws, const WsLayout& L,
+                            hipStream_t st) {
+  double* S = reinterpret_cast<double*>(ws + L.S);
+  hipError_t e = launch_scores(s, Wq, Wk, Q, K, S, ws, L, st);
+  if (e != hipSuccess) return e;
+  const long long R = s.R();
+  int E = 1;
+  while (64 * E < s.Nk) E <<= 1;
+  switch (E) {
+    case 1: return launch_soft<1>(S, R, s.Nk, k, T, M, st);
+    case 2: return launch_soft<2>(S, R, s.Nk, k, T, M, st);
+    case 4: return launch_soft<4>(S, R, s.Nk, k, T, M, st);
+    case 8: return launch_soft<8>(S, R, s.Nk, k, T, M, st);
+    case 16: return launch_soft<16>(S, R, s.Nk, k, T, M, st);
+    case 32: return launch_soft<32>(S, R, s.Nk, k, T, M, st);
+    default: return launch_soft<64>(S, R, s.Nk, k, T, M, st);
+  }
+}
+
+hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const float* Wk,
+                       const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
+                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st) {
+  const long long R = s.R();
+  double* S = logits_out ? logits_out : reinterpret_cast<double*>(ws + L.S);
+  int* counts = reinterpret_cast<int*>(ws + L.counts);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+  const int W = s.words();
+  hipError_t e = launch_scores(s, Wq, Wk, Q, K, S, ws, L, st);
+  if (e != hipSuccess) return e;
 
   int E = 1;
   while (64 * E < s.Nk) E <<= 1;

@@ -134,6 +134,21 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
                                      static_cast<hipStream_t>(stream)));
 }
 
+int sla_soft_topk(const sla_problem* prob, const sla_select* sel, float T, const void* Q, const void* K,
+                  float* M, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  int k;
+  if ((rc = check_select(sel, &k, s)) != SLA_OK) return rc;
+  if (!(T > 0.f) || !isfinite(T)) return SLA_ERR_INVALID_ARG;
+  if (Q == nullptr || K == nullptr || M == nullptr) return SLA_ERR_INVALID_ARG;
+  const WsLayout L = sla::ws_layout(s, sel->Wq != nullptr);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_soft_topk(s, k, (double)T, sel->Wq, sel->Wk, Q, K, M,
+                                          static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
 int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
                    const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* ws,
                    size_t ws_bytes, void* stream) {

@@ -48,6 +48,12 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
                        const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
                        double* logits_out, char* ws, const WsLayout& L, hipStream_t st);
 
+// mask.hip: the SoftTop-k weights [B*H*Nq, Nk] (float32) from the pooled
+// (and optionally routed) logits.
+hipError_t launch_soft_topk(const Shape& s, int k, double T, const float* Wq, const float* Wk,
+                            const void* Q, const void* K, float* M, char* ws, const WsLayout& L,
+                            hipStream_t st);
+
 // attn_bf16.hip: the K/V preparation pass for the linear branch (phi(K) in
 // 32-wide d slices and the per-head linear totals; nothing without lin;
 // heads whose alpha is exactly 1 are skipped when alpha is given) and the

@@ -91,6 +91,20 @@ size_t sla_workspace_bytes(const sla_problem* prob, const sla_select* sel);
  * mask calls require), or -1 on invalid arguments. */
 int64_t sla_mask_capacity(const sla_problem* prob);
 
+/* SoftTop-k weights of every mask row (SLA2 write-up §四: in the router's
+ * first training stage the hard Top-k is replaced by a sigmoid with a
+ * temperature).  For row i of the pooled (and, with sel->Wq / Wk, routed)
+ * logits S: M_ij = sigmoid((S_ij - tau_i) / T), with tau_i the threshold at
+ * which the row's weights sum to k = ceil(k_frac * Nk); k = 0 gives zeros and
+ * k = Nk ones.  sel->p is not used.
+ *   T       temperature, finite and > 0
+ *   Q, K    inputs [B, H, N, d]
+ *   M       out, DEVICE float32 [B*H*Nq, Nk] (rows in (b, h, i) order)
+ *   ws      workspace (>= sla_workspace_bytes(prob, sel))
+ * Returns SLA_ERR_INVALID_ARG for T <= 0, non-finite T or a NULL pointer. */
+int sla_soft_topk(const sla_problem* prob, const sla_select* sel, float T, const void* Q, const void* K,
+                  float* M, void* ws, size_t ws_bytes, void* stream);
+
 /* Build the block mask (SpargeAttention2 write-up §一, §四).
  *   Q, K          inputs [B, H, N, d]
  *   row_ptr       out, int32 [B*H*Nq + 1]; row_ptr[R] is the number of entries

@@ -145,3 +145,27 @@ def test_workspace_grows_with_router():
     a = L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(S.Select(0.03, 0.6, None, None)))
     b = L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(S.Select(0.03, 0.6, FAKE, FAKE)))
     assert b > a > 0
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, float("nan"), float("inf")])
+def test_soft_topk_temperature(T):
+    L = S.lib()
+    p = prob()
+    sel = S.Select(0.1, 0.0, None, None)
+    assert L.sla_soft_topk(ctypes.byref(p), ctypes.byref(sel), T, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                           None) == INVALID
+
+
+def test_soft_topk_null_and_workspace():
+    L = S.lib()
+    p = prob()
+    sel = S.Select(0.1, 0.0, None, None)
+    assert L.sla_soft_topk(ctypes.byref(p), ctypes.byref(sel), 0.5, None, FAKE, FAKE, FAKE, 1 << 40,
+                           None) == INVALID
+    assert L.sla_soft_topk(ctypes.byref(p), ctypes.byref(sel), 0.5, FAKE, FAKE, None, FAKE, 1 << 40,
+                           None) == INVALID
+    assert L.sla_soft_topk(ctypes.byref(p), ctypes.byref(sel), 0.5, FAKE, FAKE, FAKE, FAKE, 16,
+                           None) == WORKSPACE
+    bad = S.Select(1.5, 0.0, None, None)
+    assert L.sla_soft_topk(ctypes.byref(p), ctypes.byref(bad), 0.5, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                           None) == INVALID
