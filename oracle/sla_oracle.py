@@ -379,3 +379,140 @@ def assemble(blocks: Dict, B: int, H: int, N: int, d: int, bq: int) -> np.ndarra
         s, e = block_range(i, bq, N)
         out[b, h, s:e] = v
     return out
+
+
+# ------------------------------------------------------- 8-bit sparse branch
+# [SLA2 §三]: the sparse branch runs with the query, key, attention-probability
+# and value matrices held as 8-bit integers; values are scaled into the 8-bit
+# range, the products are formed there, and the results are scaled back.  The
+# pages fix neither the scale granularity nor the rounding; the readings taken
+# here (listed in the design doc) are:
+#
+# * symmetric codes in [-127, 127], code = round-half-even(x * (127 / amax)),
+#   the reciprocal and the product each rounded to float32, scale = amax / 127
+#   (float32); amax = 0 gives scale 0 and zero codes;
+# * Q per query block and K per key block (one scale per block of each head),
+#   V per channel over the whole sequence of a head (one scale per d index);
+# * scores I = q8 . k8 exactly (integers), S = fl32(I * c) with
+#   c = fl32(fl32(sq * sk) * fl32(1 / sqrt(d)));  m = the row's maximum S over
+#   its selected keys;
+# * P codes in [0, 127]: round-half-even(127 exp(S - m)), the value taken in
+#   float32 as exp2(fma(I, a, -b)) with a = fl32(c log2 e) and
+#   b = fl32(fl32(m log2 e) - log2 127) (a code is an integer decided by
+#   floating point, so it is decided in the precision the kernel uses);
+# * O = sv * (sum_j code_j v8_j) / (sum_j code_j): numerator and denominator
+#   are exact integers; a row with no selected block gives 0.
+_F32 = np.float32
+_LOG2E_F32 = _F32(math.log2(math.e))
+_LOG2_127_F32 = _F32(math.log2(127.0))
+
+
+def _as_f32_exact(x) -> np.ndarray:
+    """Stored bf16 / fp32 values as float32 (exact: both fit)."""
+    a = as_f64(x)
+    f = a.astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), a), "input not representable in float32"
+    return f
+
+
+def quant_codes(x32: np.ndarray, amax: np.float32) -> Tuple[np.ndarray, np.float32]:
+    """Symmetric 8-bit codes of float32 values x32 sharing one absolute maximum
+    amax, and their scale: code = rint(x * fl32(127 / amax)) in [-127, 127],
+    scale = fl32(amax / 127) (zero codes and scale when amax is 0)."""
+    amax = _F32(amax)
+    if amax == 0:
+        return np.zeros(x32.shape, dtype=np.int8), _F32(0.0)
+    r = _F32(_F32(127.0) / amax)
+    c = np.rint((x32 * r).astype(np.float32))
+    return np.clip(c, -127, 127).astype(np.int8), _F32(amax / _F32(127.0))
+
+
+def quantize_blocks(X, b: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-block codes of X [B, H, N, d]: one scale per (b, h, block of b rows)
+    over the block's valid rows and every d.  Returns (codes int8 [B, H, N, d],
+    scales float32 [B, H, ceil(N / b)])."""
+    X = _as_f32_exact(X)
+    B, H, N, d = X.shape
+    nb = n_blocks(N, b)
+    codes = np.zeros((B, H, N, d), dtype=np.int8)
+    scales = np.zeros((B, H, nb), dtype=np.float32)
+    for bb in range(B):
+        for h in range(H):
+            for i in range(nb):
+                s, e = block_range(i, b, N)
+                blk = X[bb, h, s:e]
+                codes[bb, h, s:e], scales[bb, h, i] = quant_codes(blk, np.abs(blk).max())
+    return codes, scales
+
+
+def quantize_channels(V) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-channel codes of V [B, H, N, d]: one scale per (b, h, d index) over
+    all N rows.  Returns (codes int8 [B, H, N, d], scales float32 [B, H, d])."""
+    V = _as_f32_exact(V)
+    B, H, N, d = V.shape
+    codes = np.zeros((B, H, N, d), dtype=np.int8)
+    scales = np.zeros((B, H, d), dtype=np.float32)
+    for bb in range(B):
+        for h in range(H):
+            for c in range(d):
+                col = V[bb, h, :, c]
+                codes[bb, h, :, c], scales[bb, h, c] = quant_codes(col, np.abs(col).max())
+    return codes, scales
+
+
+def quantize_i8(Q, K, V, bq: int, bk: int) -> Dict:
+    """The 8-bit inputs of the sparse branch [SLA2 §三]: Q per query block,
+    K per key block, V per channel."""
+    q8, sq = quantize_blocks(Q, bq)
+    k8, sk = quantize_blocks(K, bk)
+    v8, sv = quantize_channels(V)
+    return {"q8": q8, "sq": sq, "k8": k8, "sk": sk, "v8": v8, "sv": sv}
+
+
+def p_codes(I: np.ndarray, c: np.ndarray, m: np.float32) -> np.ndarray:
+    """8-bit codes round-half-even(127 exp(S - m)) of integer scores I with
+    per-key score scales c (S = fl32(I c)), evaluated in float32 as
+    exp2(fma(I, a, -b)), a = fl32(c log2 e), b = fl32(fl32(m log2 e) - log2 127).
+    The fma is exact in float64 before its one rounding to float32; exp2 is
+    taken in float64 and rounded to float32."""
+    a = (c.astype(np.float32) * _LOG2E_F32).astype(np.float32)
+    b = _F32(_F32(_F32(m) * _LOG2E_F32) - _LOG2_127_F32)
+    t = (I.astype(np.float64) * a.astype(np.float64) - np.float64(b)).astype(np.float32)
+    p = np.exp2(t.astype(np.float64)).astype(np.float32)
+    codes = np.rint(p)
+    assert codes.max(initial=0) <= 127 and codes.min(initial=0) >= 0
+    return codes.astype(np.int64)
+
+
+def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+    """The sparse branch on 8-bit codes [SLA2 §三]: for each query of a row
+    block, integer scores against the keys of its selected blocks, P codes
+    relative to the exact row maximum, and O = sv * sum(code v8) / sum(code)
+    from exact integer sums.  Returns {(b, h, i): [rows_in_block, d]}."""
+    q8, k8, v8 = (qz[k].astype(np.int64) for k in ("q8", "k8", "v8"))
+    sq, sk, sv = qz["sq"], qz["sk"], qz["sv"]
+    B, H, N, d = q8.shape
+    Nq = n_blocks(N, bq)
+    lam = _F32(1.0 / math.sqrt(d))
+    out = {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = [int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]]]
+        s, e = block_range(i, bq, N)
+        if not sel:
+            out[(b, h, i)] = np.zeros((e - s, d))
+            continue
+        keys = _keys_of(sel, bk, N)
+        # per-key score scale c_j = fl32(fl32(sq_i sk_blk(j)) / sqrt(d))
+        c = np.concatenate([np.full(block_range(j, bk, N)[1] - block_range(j, bk, N)[0],
+                                    _F32(_F32(sq[b, h, i] * sk[b, h, j]) * lam), dtype=np.float32)
+                            for j in sel])
+        I = q8[b, h, s:e] @ k8[b, h, keys].T                   # exact integer scores
+        S = (I.astype(np.float32) * c[None, :]).astype(np.float32)
+        o = np.zeros((e - s, d))
+        for t in range(e - s):
+            codes = p_codes(I[t], c, S[t].max())
+            num = codes @ v8[b, h, keys]                       # exact integers
+            o[t] = sv[b, h].astype(np.float64) * num / float(codes.sum())
+        out[(b, h, i)] = o
+    return out
