@@ -25,7 +25,8 @@ STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
           -3: "SLA_ERR_WORKSPACE", -4: "SLA_ERR_CAPACITY", -5: "SLA_ERR_HIP"}
 EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_soft_topk", "sla_sparse_fwd",
            "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
-           "sla_dense_fwd", "sla_status_string")
+           "sla_dense_fwd", "sla_i8_layout_of", "sla_quantize_i8", "sla_sparse_fwd_i8",
+           "sla_status_string")
 
 
 class SlaError(RuntimeError):
@@ -43,6 +44,10 @@ class Problem(ctypes.Structure):
 class Select(ctypes.Structure):
     _fields_ = [("k_frac", ctypes.c_float), ("p", ctypes.c_float),
                 ("Wq", ctypes.c_void_p), ("Wk", ctypes.c_void_p)]
+
+
+class I8Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("q8", "k8", "vt8", "sq", "sk", "sv", "rv", "vpart", "total")]
 
 
 _lib = None
@@ -70,10 +75,14 @@ def lib() -> ctypes.CDLL:
         L.sla_kv_prepare.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_fused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_i8_layout_of.argtypes = [P, ctypes.POINTER(I8Layout)]
+        L.sla_quantize_i8.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_sparse_fwd_i8.argtypes = [P, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
         for fn in ("sla_mask", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
-                   "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd"):
+                   "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd", "sla_i8_layout_of",
+                   "sla_quantize_i8", "sla_sparse_fwd_i8"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -242,3 +251,57 @@ def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None, ws=None):
     _check("sla_dense_fwd", lib().sla_dense_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
                                                 _ptr(w), w.numel(), _stream()))
     return o
+
+
+# ------------------------------------------------------- 8-bit sparse branch
+def sla_i8_layout_of(prob: Problem) -> I8Layout:
+    lay = I8Layout()
+    _check("sla_i8_layout_of", lib().sla_i8_layout_of(ctypes.byref(prob), ctypes.byref(lay)))
+    return lay
+
+
+def sla_quantize_i8(q, k, v, bq: int, bk: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """8-bit codes and scales of Q, K, V in one uint8 buffer (layout from
+    sla_i8_layout_of; i8_views splits it)."""
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    n = sla_i8_layout_of(prob).total
+    buf = out if out is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check("sla_quantize_i8", lib().sla_quantize_i8(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(buf),
+                                                    buf.numel(), _stream()))
+    return buf
+
+
+def sla_sparse_fwd_i8(qbuf: torch.Tensor, like: torch.Tensor, bq: int, bk: int, row_ptr, col_idx,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The 8-bit sparse branch over the codes in qbuf; `like` gives the shape,
+    dtype and device of Q (its data is not read)."""
+    prob = problem(like, bq, bk)
+    o = out if out is not None else torch.empty_like(like)
+    _check("sla_sparse_fwd_i8", lib().sla_sparse_fwd_i8(ctypes.byref(prob), _ptr(qbuf), qbuf.numel(),
+                                                        _ptr(row_ptr), _ptr(col_idx), _ptr(o), _stream()))
+    return o
+
+
+def i8_views(qbuf: torch.Tensor, shape, bq: int, bk: int, dtype=torch.bfloat16) -> dict:
+    """Views of the regions of a quantised buffer: q8 [BH, Nq*bq, d], k8
+    [BH, Nk*bk, d], vt8 [BH, Nk*bk/64, d, 64] (int8), sq [BH, Nq], sk [BH, Nk],
+    sv and rv [BH, d] (float32)."""
+    B, H, N, d = shape
+    prob = Problem(B, H, N, d, bq, bk, SLA_BF16 if dtype == torch.bfloat16 else SLA_F32)
+    lay = sla_i8_layout_of(prob)
+    BH, Nq, Nk = B * H, -(-N // bq), -(-N // bk)
+
+    def region(off, count, dt):
+        nbytes = count * torch.empty((), dtype=dt).element_size()
+        return qbuf[off:off + nbytes].view(dt)
+
+    return {
+        "q8": region(lay.q8, BH * Nq * bq * d, torch.int8).view(BH, Nq * bq, d),
+        "k8": region(lay.k8, BH * Nk * bk * d, torch.int8).view(BH, Nk * bk, d),
+        "vt8": region(lay.vt8, BH * Nk * bk * d, torch.int8).view(BH, Nk * bk // 64, d, 64),
+        "sq": region(lay.sq, BH * Nq, torch.float32).view(BH, Nq),
+        "sk": region(lay.sk, BH * Nk, torch.float32).view(BH, Nk),
+        "sv": region(lay.sv, BH * d, torch.float32).view(BH, d),
+        "rv": region(lay.rv, BH * d, torch.float32).view(BH, d),
+    }

@@ -1,0 +1,573 @@
+// 8-bit sparse branch on gfx950 matrix cores.
+//
+// Source: SLA2 write-up (arXiv:2602.12675) §三: the sparse branch holds Q, K,
+// the attention probabilities P and V as 8-bit integers - values are scaled
+// into the 8-bit range, the products are formed there, and the results are
+// scaled back.  Granularity and rounding are not given there; this file
+// implements (bit for bit where integers are decided):
+//   * codes = round-half-even(x * fl32(127 / amax)) in [-127, 127], scale =
+//     fl32(amax / 127); Q per query block, K per key block, V per channel over
+//     the whole sequence of a head;
+//   * scores I = q8 . k8 (exact int32), S = fl32(I * c), c = fl32(fl32(sq sk)
+//     / sqrt(d)), m = the row's maximum S over its selected keys;
+//   * P codes = round-half-even(exp2(fma(I, a, -b))) with a = fl32(c log2 e),
+//     b = fl32(fl32(m log2 e) - log2 127), i.e. 127 exp(S - m) in float32;
+//   * O = sv * (sum code v8) / (sum code), both sums exact int32.
+//
+// Kernels:
+//   quant_block_kernel  Q or K: one workgroup per block of rows, absolute
+//                       maximum, then codes (row-major [rows padded][d]);
+//   vamax_kernel        V: per-channel maxima of 256-row chunks;
+//   vscale_kernel       V: per-channel scale and reciprocal from the chunks;
+//   quant_v_kernel      V: codes as V^T in 64-key tiles [d][64], keys of
+//                       every 32-key group in the order the P operand holds
+//                       them (key 8a + 4h + b at byte 16h + 4a + b);
+//   attn_i8_kernel      one workgroup of BQ/32 wavefronts per mask row; two
+//                       passes over the row's 64-key units: pass 1 computes
+//                       the integer scores and the exact row maximum, pass 2
+//                       recomputes them, forms the P codes in registers and
+//                       accumulates P V in int32 on the matrix cores.  With
+//                       the maximum known before any code is formed, no
+//                       rescale is ever needed: the output is one int32 sum
+//                       per element, scaled once at the end.
+//
+// Matrix-core formulation (v_mfma_i32_32x32x32_i8; lane l supplies operand
+// row / column l%32 and 16 bytes of the k range, half l/32; accumulator
+// element i of lane l is row 8(i/4) + 4(l/32) + i%4, column l%32):
+//   S^T (keys x queries) = K . Q^T     A = K tile rows, B = Q rows (registers)
+//   O^T (d x queries)   += V^T . P^T   A = V^T tile rows, B = P codes
+// The 16 S^T elements of a lane (one query, keys 8a + 4h + b) become the 16
+// bytes of its P operand in element order, and the V^T tile stores those keys
+// in that order, so P goes from accumulator to operand without a lane move.
+#include <climits>
+#include <math.h>
+
+#include "sla.h"
+#include "sla_internal.h"
+
+namespace sla {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int QROWS = 256;  // rows per chunk of the V channel maxima
+
+// ------------------------------------------------------------------ helpers
+// 16 bytes of input as floats: bf16 (8 values) or fp32 (4 values).
+template <int ES>
+struct Chunk;
+template <>
+struct Chunk<2> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const uint4& v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+    }
+  }
+};
+template <>
+struct Chunk<4> {
+  static constexpr int N = 4;
+  __device__ static void unpack(const uint4& v, float (&x)[4]) {
+    x[0] = __uint_as_float(v.x);
+    x[1] = __uint_as_float(v.y);
+    x[2] = __uint_as_float(v.z);
+    x[3] = __uint_as_float(v.w);
+  }
+};
+
+// symmetric 8-bit code of x with reciprocal scale r, as a byte
+__device__ __forceinline__ uint32_t code8(float x, float r) {
+  const float c = fminf(fmaxf(rintf(x * r), -127.f), 127.f);
+  return (uint32_t)(int)c & 0xffu;
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float m = red[0];
+  for (int i = 1; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
+  return m;
+}
+
+// Workgroups go round-robin over the 8 XCDs (blockIdx % 8), each with its own
+// L2: give every XCD a contiguous range of mask rows, so that adjacent query
+// blocks of a head (which select largely the same key blocks) share an L2.
+__device__ __forceinline__ long long xcd_row(long long b, long long R) {
+  constexpr long long NX = 8;
+  const long long q = R / NX, r = R % NX;
+  const long long x = b % NX, local = b / NX;
+  return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Direct buffer load of 16 bytes per lane into LDS: lane l writes
+// lds_wave_base + 16 l; the byte address is voff + soff in the buffer.
+__device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                        void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, (int)soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their no-wait maxima)
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14)); }
+
+__device__ __forceinline__ uint4 rd16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ i32x16 mfma8(const i32x4& a, const i32x4& b, const i32x16& c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- quantisers
+// Codes of one block of BR rows of X [BH][N][D] (rows past N read as zero),
+// written to codes [BH][Nb * BR][D]; its scale to scales [BH][Nb].
+template <int ES, int D, int BR>
+__global__ __launch_bounds__(256) void quant_block_kernel(const char* __restrict__ X, int N, int Nb,
+                                                          int8_t* __restrict__ codes,
+                                                          float* __restrict__ scales) {
+  using C = Chunk<ES>;
+  constexpr int CH = C::N, CPR = D / CH, NC = BR * CPR / 256;
+  static_assert(NC * 256 == BR * CPR, "chunks per thread");
+  __shared__ float red[4];
+  const long long bh = blockIdx.x / Nb;
+  const int blk = blockIdx.x % Nb;
+  const char* xb = X + (size_t)bh * N * D * ES;
+  float x[NC][CH];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int g = threadIdx.x + 256 * k, r = g / CPR, cc = g % CPR;
+    const int row = blk * BR + r;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < N) v = *reinterpret_cast<const uint4*>(xb + ((size_t)row * D + cc * CH) * ES);
+    C::unpack(v, x[k]);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
+  }
+  amax = block_max(amax, red);
+  const float r = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
+  int8_t* cb = codes + ((size_t)bh * Nb + blk) * BR * D;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const int g = threadIdx.x + 256 * k, rr = g / CPR, cc = g % CPR;
+    uint32_t wv[CH / 4];
+#pragma unroll
+    for (int j = 0; j < CH / 4; ++j)
+      wv[j] = code8(x[k][4 * j], r) | (code8(x[k][4 * j + 1], r) << 8) | (code8(x[k][4 * j + 2], r) << 16) |
+              (code8(x[k][4 * j + 3], r) << 24);
+    int8_t* dst = cb + (size_t)rr * D + cc * CH;
+    if (CH == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0], wv[CH / 4 - 1]);
+    else *reinterpret_cast<uint32_t*>(dst) = wv[0];
+  }
+  if (threadIdx.x == 0) scales[bh * Nb + blk] = __fdiv_rn(amax, 127.f);
+}
+
+// Per-channel absolute maxima of rows [chunk * QROWS, +QROWS) of V.
+template <int ES, int D>
+__global__ __launch_bounds__(256) void vamax_kernel(const char* __restrict__ V, int N, int nchunk,
+                                                    float* __restrict__ vpart) {
+  using C = Chunk<ES>;
+  constexpr int CH = C::N, CPR = D / CH, TR = 256 / CPR;
+  static_assert(TR * CPR == 256, "thread layout");
+  __shared__ float red[TR][D];
+  const long long bh = blockIdx.y;
+  const int ch = blockIdx.x;
+  const int rl = threadIdx.x / CPR, cc = threadIdx.x % CPR;
+  const char* vb = V + (size_t)bh * N * D * ES;
+  float m[CH];
+#pragma unroll
+  for (int e = 0; e < CH; ++e) m[e] = 0.f;
+  const int r1 = min(N, (ch + 1) * QROWS);
+  for (int r = ch * QROWS + rl; r < r1; r += TR) {
+    float x[CH];
+    C::unpack(*reinterpret_cast<const uint4*>(vb + ((size_t)r * D + cc * CH) * ES), x);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) m[e] = fmaxf(m[e], fabsf(x[e]));
+  }
+#pragma unroll
+  for (int e = 0; e < CH; ++e) red[rl][cc * CH + e] = m[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float a = 0.f;
+    for (int t = 0; t < TR; ++t) a = fmaxf(a, red[t][threadIdx.x]);
+    vpart[((size_t)bh * nchunk + ch) * D + threadIdx.x] = a;
+  }
+}
+
+// sv = amax / 127 and rv = 127 / amax (0 when amax is 0) per channel.
+__global__ __launch_bounds__(128) void vscale_kernel(const float* __restrict__ vpart, int nchunk, int D,
+                                                     float* __restrict__ sv, float* __restrict__ rv) {
+  const long long bh = blockIdx.x;
+  const int c = threadIdx.x;
+  if (c >= D) return;
+  float a = 0.f;
+  for (int k = 0; k < nchunk; ++k) a = fmaxf(a, vpart[((size_t)bh * nchunk + k) * D + c]);
+  sv[bh * D + c] = __fdiv_rn(a, 127.f);
+  rv[bh * D + c] = a > 0.f ? __fdiv_rn(127.f, a) : 0.f;
+}
+
+// Codes of one 64-key tile of V, written transposed: vt8 [BH][ntile][D][64],
+// key k of the tile at byte 32 (k / 32) + 16 ((k / 4) % 2) + 4 ((k % 32) / 8)
+// + k % 4 of its channel row (keys past N are zero).
+template <int ES, int D>
+__global__ __launch_bounds__(256) void quant_v_kernel(const char* __restrict__ V, int N, int ntile,
+                                                      const float* __restrict__ rv,
+                                                      int8_t* __restrict__ vt8) {
+  using C = Chunk<ES>;
+  constexpr int CH = C::N, CPR = D / CH;
+  constexpr int RS = 17;  // LDS row stride in words (64 bytes + 4 of padding against bank conflicts)
+  __shared__ uint32_t T[D * RS];
+  const long long bh = blockIdx.y;
+  const int tile = blockIdx.x;
+  const char* vb = V + (size_t)bh * N * D * ES;
+  const float* rvh = rv + bh * D;
+  for (int wi = threadIdx.x; wi < 16 * CPR; wi += 256) {
+    const int kq = wi / CPR, cc = wi % CPR;  // keys 4 kq .. 4 kq + 3, channels cc CH ..
+    float x[4][CH];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = tile * 64 + 4 * kq + j;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (key < N) v = *reinterpret_cast<const uint4*>(vb + ((size_t)key * D + cc * CH) * ES);
+      C::unpack(v, x[j]);
+    }
+    const int k = 4 * kq;
+    const int word = 8 * (k >> 5) + 4 * ((k >> 2) & 1) + ((k & 31) >> 3);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int c = cc * CH + e;
+      const float r = rvh[c];
+      T[c * RS + word] = code8(x[0][e], r) | (code8(x[1][e], r) << 8) | (code8(x[2][e], r) << 16) |
+                         (code8(x[3][e], r) << 24);
+    }
+  }
+  __syncthreads();
+  uint32_t* dst = reinterpret_cast<uint32_t*>(vt8 + ((size_t)bh * ntile + tile) * D * 64);
+  for (int g = threadIdx.x; g < D * 16; g += 256) dst[g] = T[(g >> 4) * RS + (g & 15)];
+}
+
+// ---------------------------------------------------------------- attention
+// LDS layout of a unit (64 keys): the K tile, rows of D bytes with 16-byte
+// chunk c of key r at c ^ swk(r), then the V^T tile, rows of 64 bytes with
+// chunk e of channel c at e ^ swv(c).  The 16 lanes that read one operand
+// chunk from 16 consecutive rows then hit 16 distinct groups of 4 banks.
+template <int D>
+struct I8Tiles {
+  static constexpr int KT = 64 * D;   // bytes of the K tile
+  static constexpr int VT = D * 64;   // bytes of the V^T tile
+  static constexpr int CPR = D / 16;  // 16-byte chunks per K row
+  static constexpr int KSH = CPR == 8 ? 1 : 2;
+  __device__ static int swk(int r) { return (r >> KSH) & (CPR - 1); }
+  __device__ static int swv(int c) { return (c >> 2) & 3; }
+};
+
+// Direct loads of a unit's tiles, split over NW wavefronts: load slot u fills
+// the 1 KB at tile + 1024 u, lane l the 16 bytes at 16 l, from the chunk that
+// belongs there in the swizzled layout.  K and V^T tiles of the unit starting
+// at key key0 both begin at byte key0 * D of their per-head arrays.
+template <int D, int NW>
+struct I8Load {
+  using TT = I8Tiles<D>;
+  static constexpr int NK = TT::KT / 1024 / NW;
+  static_assert(NK * NW * 1024 == TT::KT, "tile split");
+  uint32_t kv[NK], vv[NK];
+  int w;
+  __device__ __forceinline__ I8Load(int w_, int lane) : w(w_) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int o = 1024 * (w + NW * i) + 16 * lane;
+      const int r = o / D, pk = (o % D) / 16;
+      kv[i] = (uint32_t)(r * D + 16 * (pk ^ TT::swk(r)));
+      const int c = o / 64, pv = (o % 64) / 16;
+      vv[i] = (uint32_t)(c * 64 + 16 * (pv ^ TT::swv(c)));
+    }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0,
+                                       bool with_v, char* dst) const {
+    const uint32_t soff = (uint32_t)key0 * D;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) b2lds16(rk, kv[i], soff, dst + 1024 * (w + NW * i));
+    if (with_v) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) b2lds16(rv, vv[i], soff, dst + TT::KT + 1024 * (w + NW * i));
+    }
+  }
+};
+
+// S^T of a unit: two 32-key tiles, D/32 k-steps each.
+template <int D>
+__device__ __forceinline__ void score8(const char* Ks, const i32x4 (&qf)[D / 32], const int (&koff)[D / 32],
+                                       i32x16 (&sc)[2]) {
+  constexpr int NT = D / 32;
+  uint4 fr[2 * NT];
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) fr[i] = rd16(Ks + (i / NT) * 32 * D + koff[i % NT]);
+  sc[0] = i32x16{};
+  sc[1] = i32x16{};
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) sc[i / NT] = mfma8(__builtin_bit_cast(i32x4, fr[i]), qf[i % NT], sc[i / NT]);
+}
+
+template <int D, int BQ, int SUB, int OES>
+__global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_i8_kernel(
+    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const int8_t* __restrict__ vt8,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    const int* __restrict__ row_ptr, const int* __restrict__ col_idx, char* __restrict__ O, int N, int Nq,
+    int Nk, float lam, float l2e, float l2_127) {
+  using TT = I8Tiles<D>;
+  constexpr int NW = BQ / 32;
+  constexpr int STAGE = TT::KT + TT::VT;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
+  const long long bh = row / Nq;
+  const int qi = (int)(row % Nq);
+  const int base = row_ptr[row];
+  const int nunits = (row_ptr[row + 1] - base) * SUB;
+  const int Npad = Nk * SUB * 64;
+  const int q = qi * BQ + 32 * w + l32;  // query rows are padded to Nq * BQ
+
+  i32x4 qf[D / 32];
+  const int8_t* qrow = q8 + ((size_t)bh * Nq * BQ + q) * D;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) qf[kk] = *reinterpret_cast<const i32x4*>(qrow + 32 * kk + 16 * hi);
+  int koff[D / 32], voff[2];
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) koff[kk] = l32 * D + 16 * ((2 * kk + hi) ^ TT::swk(l32));
+#pragma unroll
+  for (int g = 0; g < 2; ++g) voff[g] = l32 * 64 + 16 * ((2 * g + hi) ^ TT::swv(l32));
+
+  i32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = i32x16{};
+  uint32_t lsum = 0;  // this lane's sum of P codes
+  if (nunits > 0) {
+    const float sqv = sq[bh * Nq + qi];
+    const float* skh = sk + bh * Nk;
+    const auto rk = buf_rsrc(k8 + (size_t)bh * Npad * D, (uint32_t)Npad * D);
+    const auto rv = buf_rsrc(vt8 + (size_t)bh * Npad * D, (uint32_t)Npad * D);
+    const I8Load<D, NW> lp(w, lane);
+    const int nsteps = 2 * nunits;  // pass 1: steps 0 .. nunits-1, pass 2: the rest
+    float m = -INFINITY, nb = 0.f;
+    auto blk_of = [&](int u) { return col_idx[base + u / SUB]; };
+    auto key0_of = [&](int u, int blk) { return (blk * SUB + u % SUB) * 64; };
+
+    auto step = [&](int s, char* cur, char* nxt) __attribute__((always_inline)) {
+      const bool p2 = s >= nunits;
+      const int u = p2 ? s - nunits : s;
+      const int blk = blk_of(u);
+      const int kcur = key0_of(u, blk);
+      const int s1 = s + 1;
+      const int u1 = s1 >= nunits ? s1 - nunits : s1;
+      const int knext = s1 < nsteps ? key0_of(u1, blk_of(u1)) : 0;
+      const float cu = (sqv * skh[blk]) * lam;  // fl32(fl32(sq sk) / sqrt(d))
+      wait_vm0();       // this wavefront's loads of unit s have landed
+      __syncthreads();  // ... and every wavefront's; unit s-1 consumed
+      if (s1 < nsteps) lp.load(rk, rv, knext, s1 >= nunits, nxt);
+      const int lim = min(64, N - kcur);  // valid keys of the unit
+      i32x16 sc[2];
+      score8<D>(cur, qf, koff, sc);
+      if (!p2) {
+        int im = INT_MIN;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = 32 * kt + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (lim == 64 || key < lim) im = max(im, sc[kt][i]);
+          }
+        if (im != INT_MIN) m = fmaxf(m, (float)im * cu);
+      } else {
+        if (u == 0) {
+          // the row maximum of this query: lanes l and l^32 hold its two key halves
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(m, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+          nb = (m * l2e) - l2_127;  // fl32(fl32(m log2 e) - log2 127); no contraction in this file
+        }
+        const float au = cu * l2e;
+        i32x4 pc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t wd = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * e + j;
+              float t = __builtin_fmaf((float)sc[kt][i], au, -nb);
+              if (lim < 64 && 32 * kt + 8 * e + 4 * hi + j >= lim) t = -INFINITY;
+              wd = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_exp2f(t), j, wd);
+            }
+            pc[kt][e] = (int)wd;
+            lsum = __builtin_amdgcn_udot4(wd, 0x01010101u, lsum, false);
+          }
+        const char* Vs = cur + TT::KT;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int g = 0; g < 2; ++g)
+            acc[dt] = mfma8(__builtin_bit_cast(i32x4, rd16(Vs + dt * 32 * 64 + voff[g])), pc[g], acc[dt]);
+      }
+    };
+    lp.load(rk, rv, key0_of(0, blk_of(0)), false, st0);
+    int s = 0;
+    for (; s + 2 <= nsteps; s += 2) {
+      step(s, st0, st1);
+      step(s + 1, st1, st0);
+    }
+    wait_vm0();  // nsteps is even: no load outlives the loop
+  }
+
+  const uint32_t L = lsum + (uint32_t)__shfl_xor((int)lsum, 32);
+  const float inv = L ? 1.f / (float)L : 0.f;
+  if (q >= N) return;
+  const float* svh = sv + bh * D;
+  char* orow = O + ((size_t)bh * N + q) * D * OES;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int c0 = 32 * dt + 8 * a + 4 * hi;
+      const float4 s4 = *reinterpret_cast<const float4*>(svh + c0);
+      const float sc4[4] = {s4.x, s4.y, s4.z, s4.w};
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = ((float)acc[dt][4 * a + j] * sc4[j]) * inv;
+      if (OES == 4) {
+        *reinterpret_cast<float4*>(orow + c0 * 4) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        // round to nearest even (v_cvt_pk_bf16_f32)
+        const f32x2 lo = {o[0], o[1]}, hi2 = {o[2], o[3]};
+        *reinterpret_cast<uint2*>(orow + c0 * 2) =
+            make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2)));
+      }
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+template <int ES, int D>
+hipError_t quant_dispatch(const Shape& s, const void* Q, const void* K, const void* V, char* qb,
+                          const I8Layout& L, hipStream_t st) {
+  const long long BH = (long long)s.B * s.H;
+  const char* q = static_cast<const char*>(Q);
+  const char* k = static_cast<const char*>(K);
+  const char* v = static_cast<const char*>(V);
+  int8_t* q8 = reinterpret_cast<int8_t*>(qb + L.q8);
+  int8_t* k8 = reinterpret_cast<int8_t*>(qb + L.k8);
+  float* sq = reinterpret_cast<float*>(qb + L.sq);
+  float* sk = reinterpret_cast<float*>(qb + L.sk);
+  if (s.bq == 128)
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 128>), dim3((unsigned)(BH * s.Nq)), dim3(256), 0, st, q, s.N,
+                       s.Nq, q8, sq);
+  else
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 64>), dim3((unsigned)(BH * s.Nq)), dim3(256), 0, st, q, s.N,
+                       s.Nq, q8, sq);
+  // K: one scale per key block of bk rows
+  if (s.bk == 128)
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 128>), dim3((unsigned)(BH * s.Nk)), dim3(256), 0, st, k, s.N,
+                       s.Nk, k8, sk);
+  else
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 64>), dim3((unsigned)(BH * s.Nk)), dim3(256), 0, st, k, s.N,
+                       s.Nk, k8, sk);
+  float* vpart = reinterpret_cast<float*>(qb + L.vpart);
+  float* sv = reinterpret_cast<float*>(qb + L.sv);
+  float* rv = reinterpret_cast<float*>(qb + L.rv);
+  hipLaunchKernelGGL((vamax_kernel<ES, D>), dim3((unsigned)L.vchunks, (unsigned)BH), dim3(256), 0, st, v, s.N,
+                     L.vchunks, vpart);
+  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)BH), dim3(128), 0, st, vpart, L.vchunks, D, sv, rv);
+  const int ntile = s.Nk * s.bk / 64;
+  hipLaunchKernelGGL((quant_v_kernel<ES, D>), dim3((unsigned)ntile, (unsigned)BH), dim3(256), 0, st, v, s.N,
+                     ntile, rv, reinterpret_cast<int8_t*>(qb + L.vt8));
+  return hipGetLastError();
+}
+
+template <int D, int BQ, int SUB>
+hipError_t attn_i8_dispatch(const Shape& s, const char* qb, const I8Layout& L, const int32_t* rp,
+                            const int32_t* ci, void* O, hipStream_t st) {
+  const float lam = (float)(1.0 / sqrt((double)D));
+  const float l2e = (float)log2(M_E);
+  const float l2_127 = (float)log2(127.0);
+  const int8_t* q8 = reinterpret_cast<const int8_t*>(qb + L.q8);
+  const int8_t* k8 = reinterpret_cast<const int8_t*>(qb + L.k8);
+  const int8_t* vt8 = reinterpret_cast<const int8_t*>(qb + L.vt8);
+  const float* sq = reinterpret_cast<const float*>(qb + L.sq);
+  const float* sk = reinterpret_cast<const float*>(qb + L.sk);
+  const float* sv = reinterpret_cast<const float*>(qb + L.sv);
+  const dim3 grid((unsigned)s.R()), block(BQ / 32 * 64);
+  char* o = static_cast<char*>(O);
+  if (s.dtype == SLA_BF16)
+    hipLaunchKernelGGL((attn_i8_kernel<D, BQ, SUB, 2>), grid, block, 0, st, q8, k8, vt8, sq, sk, sv, rp, ci, o,
+                       s.N, s.Nq, s.Nk, lam, l2e, l2_127);
+  else
+    hipLaunchKernelGGL((attn_i8_kernel<D, BQ, SUB, 4>), grid, block, 0, st, q8, k8, vt8, sq, sk, sv, rp, ci, o,
+                       s.N, s.Nq, s.Nk, lam, l2e, l2_127);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+I8Layout i8_layout(const Shape& s) {
+  I8Layout L{};
+  const size_t BH = (size_t)s.B * s.H;
+  const size_t Npad = (size_t)s.Nk * s.bk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  L.vchunks = (s.N + QROWS - 1) / QROWS;
+  L.q8 = take(BH * s.Nq * s.bq * s.d);
+  L.k8 = take(BH * Npad * s.d);
+  L.vt8 = take(BH * Npad * s.d);
+  L.sq = take(BH * s.Nq * sizeof(float));
+  L.sk = take(BH * s.Nk * sizeof(float));
+  L.sv = take(BH * s.d * sizeof(float));
+  L.rv = take(BH * s.d * sizeof(float));
+  L.vpart = take(BH * L.vchunks * s.d * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_quant_i8(const Shape& s, const void* Q, const void* K, const void* V, char* qbuf,
+                           const I8Layout& L, hipStream_t st) {
+  const bool bf = s.dtype == SLA_BF16;
+  if (s.d == 128) return bf ? quant_dispatch<2, 128>(s, Q, K, V, qbuf, L, st) : quant_dispatch<4, 128>(s, Q, K, V, qbuf, L, st);
+  if (s.d == 64) return bf ? quant_dispatch<2, 64>(s, Q, K, V, qbuf, L, st) : quant_dispatch<4, 64>(s, Q, K, V, qbuf, L, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* rp,
+                          const int32_t* ci, void* O, hipStream_t st) {
+#define SLA_I8(DD, QQ, KK) \
+  if (s.d == DD && s.bq == QQ && s.bk == KK) return attn_i8_dispatch<DD, QQ, KK / 64>(s, qbuf, L, rp, ci, O, st);
+  SLA_I8(128, 128, 64)
+  SLA_I8(128, 128, 128)
+  SLA_I8(128, 64, 64)
+  SLA_I8(128, 64, 128)
+  SLA_I8(64, 128, 64)
+  SLA_I8(64, 128, 128)
+  SLA_I8(64, 64, 64)
+  SLA_I8(64, 64, 128)
+#undef SLA_I8
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sla

@@ -239,6 +239,45 @@ int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const v
   return hip_status(run_attn(s, sla::MODE_DENSE, Q, K, V, nullptr, nullptr, nullptr, w, L, O, st));
 }
 
+int sla_i8_layout_of(const sla_problem* prob, sla_i8_layout* layout) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (layout == nullptr) return SLA_ERR_INVALID_ARG;
+  if (s.N > 131072) return SLA_ERR_UNSUPPORTED;
+  const sla::I8Layout L = sla::i8_layout(s);
+  layout->q8 = L.q8; layout->k8 = L.k8; layout->vt8 = L.vt8;
+  layout->sq = L.sq; layout->sk = L.sk; layout->sv = L.sv; layout->rv = L.rv;
+  layout->vpart = L.vpart; layout->total = L.total;
+  return SLA_OK;
+}
+
+int sla_quantize_i8(const sla_problem* prob, const void* Q, const void* K, const void* V, void* qbuf,
+                    size_t qbuf_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.N > 131072) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V) return SLA_ERR_INVALID_ARG;
+  const sla::I8Layout L = sla::i8_layout(s);
+  if (qbuf == nullptr || qbuf_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_quant_i8(s, Q, K, V, static_cast<char*>(qbuf), L,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int sla_sparse_fwd_i8(const sla_problem* prob, const void* qbuf, size_t qbuf_bytes, const int32_t* row_ptr,
+                      const int32_t* col_idx, void* O_s, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.N > 131072) return SLA_ERR_UNSUPPORTED;
+  if (!row_ptr || !col_idx || !O_s) return SLA_ERR_INVALID_ARG;
+  const sla::I8Layout L = sla::i8_layout(s);
+  if (qbuf == nullptr || qbuf_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_attn_i8(s, static_cast<const char*>(qbuf), L, row_ptr, col_idx, O_s,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 const char* sla_status_string(int status) {
   switch (status) {
     case SLA_OK: return "ok";

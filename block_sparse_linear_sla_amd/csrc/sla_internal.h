@@ -35,6 +35,22 @@ struct WsLayout {
 
 WsLayout ws_layout(const Shape& s, bool router);
 
+// Byte offsets of the 8-bit sparse branch buffer (all 256-byte aligned).
+struct I8Layout {
+  size_t q8;     // int8 [B*H][Nq*bq][d], rows >= N zero
+  size_t k8;     // int8 [B*H][Nk*bk][d], rows >= N zero
+  size_t vt8;    // int8 [B*H][Nk*bk/64][d][64]: V^T in 64-key tiles (P operand key order)
+  size_t sq;     // float [B*H][Nq]
+  size_t sk;     // float [B*H][Nk]
+  size_t sv;     // float [B*H][d]
+  size_t rv;     // float [B*H][d]: 127 / amax of each V channel (0 for amax 0)
+  size_t vpart;  // float [B*H][vchunks][d]: channel maxima of 256-row chunks
+  size_t total;
+  int vchunks;
+};
+
+I8Layout i8_layout(const Shape& s);
+
 // Mode of the attention kernels.
 enum Mode : int {
   MODE_SPARSE = 0,  // O = O_s over the CSR row
@@ -65,6 +81,13 @@ hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void
                             const char* ws, const WsLayout& L, void* O, hipStream_t st);
 hipError_t launch_summary_reduce(const float* hpart, const float* alpha, int H, long long BH,
                                  int nchunk, int per, float* htot, hipStream_t st);
+
+// attn_i8.hip: the 8-bit codes and scales of Q, K, V, and the 8-bit sparse
+// branch over them.
+hipError_t launch_quant_i8(const Shape& s, const void* Q, const void* K, const void* V, char* qbuf,
+                           const I8Layout& L, hipStream_t st);
+hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* row_ptr,
+                          const int32_t* col_idx, void* O, hipStream_t st);
 
 // attn_f32.hip: linear totals and attention for float32 inputs.
 hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,

@@ -170,6 +170,50 @@ int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const v
                   void* ws, size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
+/* ---- 8-bit sparse branch (SLA2 write-up §三: the sparse branch holds Q, K,
+ * the attention probabilities P and V as 8-bit integers, scaled into the
+ * 8-bit range and scaled back).  The granularity and rounding, which that
+ * section leaves open, are:
+ *   - symmetric codes in [-127, 127]: code = round-half-even(x * fl32(127 /
+ *     amax)), scale = fl32(amax / 127) (amax = 0: scale 0, codes 0); Q has one
+ *     scale per query block, K one per key block, V one per channel (d index)
+ *     over the whole sequence of a head;
+ *   - integer scores I = q8 . k8, S = fl32(I * c) with c = fl32(fl32(sq * sk)
+ *     * fl32(1 / sqrt(d))), m = the row's largest S over its listed keys;
+ *   - P codes = round-half-even(exp2(fma(I, a, -b))) in [0, 127], a = fl32(c *
+ *     log2 e), b = fl32(fl32(m * log2 e) - log2 127): 127 exp(S - m) taken in
+ *     float32 (exp2 by the hardware instruction, within an ulp);
+ *   - O_s = sv * (sum_j code_j v8_j) / (sum_j code_j) from exact int32 sums;
+ *     a row with no listed block gives 0.
+ *
+ * The quantised buffer (caller-owned device memory, qbuf_bytes >= total):
+ *   q8     int8  [B*H][Nq*bq][d]   row-major, rows >= N zero
+ *   k8     int8  [B*H][Nk*bk][d]   row-major, rows >= N zero
+ *   vt8    int8  [B*H][Nk*bk/64][d][64]   V^T in tiles of 64 keys: key k of a
+ *                tile sits at byte 32(k/32) + 16((k/4)%2) + 4((k%32)/8) + k%4
+ *                of its channel's 64-byte row (keys >= N zero)
+ *   sq     float [B*H][Nq],  sk float [B*H][Nk],  sv float [B*H][d]
+ *   rv     float [B*H][d]    127 / amax per V channel (0 for amax 0)
+ *   vpart  float [B*H][ceil(N/256)][d]   channel maxima of 256-row chunks
+ * at the byte offsets sla_i8_layout_of returns (each 256-byte aligned).
+ * Supported as for the other calls, and N <= 131072 (the int32 sums then
+ * cannot overflow).  Inputs must be finite. */
+typedef struct {
+  size_t q8, k8, vt8, sq, sk, sv, rv, vpart, total;
+} sla_i8_layout;
+
+/* Offsets and total size of the quantised buffer for this problem. */
+int sla_i8_layout_of(const sla_problem* prob, sla_i8_layout* layout);
+
+/* Quantise Q, K, V (problem dtype) into qbuf. */
+int sla_quantize_i8(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                    void* qbuf, size_t qbuf_bytes, void* stream);
+
+/* The sparse branch on the codes in qbuf (as left by sla_quantize_i8), over
+ * the CSR mask; writes O_s [B, H, N, d] in the problem dtype. */
+int sla_sparse_fwd_i8(const sla_problem* prob, const void* qbuf, size_t qbuf_bytes,
+                      const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
+
 const char* sla_status_string(int status);
 
 #ifdef __cplusplus

@@ -484,23 +484,26 @@ def p_codes(I: np.ndarray, c: np.ndarray, m: np.float32) -> np.ndarray:
     return codes.astype(np.int64)
 
 
-def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, with_sums: bool = False):
     """The sparse branch on 8-bit codes [SLA2 §三]: for each query of a row
     block, integer scores against the keys of its selected blocks, P codes
     relative to the exact row maximum, and O = sv * sum(code v8) / sum(code)
-    from exact integer sums.  Returns {(b, h, i): [rows_in_block, d]}."""
+    from exact integer sums.  Returns {(b, h, i): [rows_in_block, d]}, and with
+    with_sums also {(b, h, i): sum of the P codes per query} (0 for an empty
+    row)."""
     q8, k8, v8 = (qz[k].astype(np.int64) for k in ("q8", "k8", "v8"))
     sq, sk, sv = qz["sq"], qz["sk"], qz["sv"]
     B, H, N, d = q8.shape
     Nq = n_blocks(N, bq)
     lam = _F32(1.0 / math.sqrt(d))
-    out = {}
+    out, sums = {}, {}
     for (b, h, i) in _rows(B, H, Nq, rows):
         r = (b * H + h) * Nq + i
         sel = [int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]]]
         s, e = block_range(i, bq, N)
         if not sel:
             out[(b, h, i)] = np.zeros((e - s, d))
+            sums[(b, h, i)] = np.zeros(e - s, dtype=np.int64)
             continue
         keys = _keys_of(sel, bk, N)
         # per-key score scale c_j = fl32(fl32(sq_i sk_blk(j)) / sqrt(d))
@@ -510,9 +513,12 @@ def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None) ->
         I = q8[b, h, s:e] @ k8[b, h, keys].T                   # exact integer scores
         S = (I.astype(np.float32) * c[None, :]).astype(np.float32)
         o = np.zeros((e - s, d))
+        L = np.zeros(e - s, dtype=np.int64)
         for t in range(e - s):
             codes = p_codes(I[t], c, S[t].max())
             num = codes @ v8[b, h, keys]                       # exact integers
-            o[t] = sv[b, h].astype(np.float64) * num / float(codes.sum())
+            L[t] = codes.sum()
+            o[t] = sv[b, h].astype(np.float64) * num / float(L[t])
         out[(b, h, i)] = o
-    return out
+        sums[(b, h, i)] = L
+    return (out, sums) if with_sums else out

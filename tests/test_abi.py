@@ -21,7 +21,7 @@ FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(sla_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(sla_[a-z_0-9]+)\s*\(", text, re.M)))
 
 
 def test_exports_match_header():
@@ -169,3 +169,43 @@ def test_soft_topk_null_and_workspace():
     bad = S.Select(1.5, 0.0, None, None)
     assert L.sla_soft_topk(ctypes.byref(p), ctypes.byref(bad), 0.5, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                            None) == INVALID
+
+
+def test_i8_layout_and_limits():
+    L = S.lib()
+    p = prob(N=1000, d=128, bq=128, bk=64, dtype=S.SLA_BF16)
+    lay = S.I8Layout()
+    assert L.sla_i8_layout_of(ctypes.byref(p), ctypes.byref(lay)) == 0
+    BH, Nq, Nk = 2, 8, 16
+    sizes = [("q8", BH * Nq * 128 * 128), ("k8", BH * Nk * 64 * 128), ("vt8", BH * Nk * 64 * 128),
+             ("sq", BH * Nq * 4), ("sk", BH * Nk * 4), ("sv", BH * 128 * 4), ("rv", BH * 128 * 4),
+             ("vpart", BH * 4 * 128 * 4)]
+    off = 0
+    for name, n in sizes:  # regions in order, each 256-byte aligned, no overlap
+        assert getattr(lay, name) == off, name
+        off = (off + n + 255) // 256 * 256
+    assert lay.total == off
+    assert L.sla_i8_layout_of(ctypes.byref(p), None) == INVALID
+    big = prob(N=131073, H=1, d=64, bk=128)
+    assert L.sla_i8_layout_of(ctypes.byref(big), ctypes.byref(lay)) == UNSUPPORTED
+    assert L.sla_quantize_i8(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    assert L.sla_sparse_fwd_i8(ctypes.byref(big), FAKE, 1 << 40, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    bad = prob(d=96)
+    assert L.sla_quantize_i8(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+
+
+def test_i8_null_and_buffer_checks():
+    L = S.lib()
+    p = prob(dtype=S.SLA_BF16)
+    lay = S.I8Layout()
+    assert L.sla_i8_layout_of(ctypes.byref(p), ctypes.byref(lay)) == 0
+    n = lay.total
+    for args in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
+        assert L.sla_quantize_i8(ctypes.byref(p), *args, FAKE, n, None) == INVALID
+    assert L.sla_quantize_i8(ctypes.byref(p), FAKE, FAKE, FAKE, None, n, None) == WORKSPACE
+    assert L.sla_quantize_i8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, n - 1, None) == WORKSPACE
+    for args in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
+        assert L.sla_sparse_fwd_i8(ctypes.byref(p), FAKE, n, *args, None) == INVALID
+    assert L.sla_sparse_fwd_i8(ctypes.byref(p), None, n, FAKE, FAKE, FAKE, None) == WORKSPACE
+    assert L.sla_sparse_fwd_i8(ctypes.byref(p), FAKE, n - 1, FAKE, FAKE, FAKE, None) == WORKSPACE
+    assert L.sla_sparse_fwd_i8(None, FAKE, n, FAKE, FAKE, FAKE, None) == INVALID
