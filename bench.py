@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "dense-equivalent attention TFLOPS + speedup vs dense at 97% sparsity, N=32760"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_I8_TOPS = 5000.0          # MI355X dense int8 matrix peak
 FUSED_SRC = os.path.join(ROOT, "block_sparse_linear_sla_amd", "csrc", "attn_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_fused_traffic.json")
 
@@ -234,6 +235,31 @@ def main():
     t_sp = e0.elapsed_time(e1) / args.steps
     res["sparse_fwd_ms"] = t_sp
     res["sparse_fwd_executed_TFLOPS"] = pair_flops * nnz / (t_sp * 1e-3) / 1e12
+
+    # the 8-bit sparse branch on the same mask: quantisation of Q, K, V, then
+    # the two-pass int8 kernel; its algorithmic rate (4 bq bk d operations per
+    # executed pair) is priced against the int8 matrix peak
+    if wl.dtype == "bf16":
+        qbuf = S.sla_quantize_i8(q, k, v, wl.bq, wl.bk)
+        S.sla_sparse_fwd_i8(qbuf, q, wl.bq, wl.bk, rp, ci, out=out)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(args.steps):
+            S.sla_quantize_i8(q, k, v, wl.bq, wl.bk, out=qbuf)
+        e[1].record()
+        for _ in range(args.steps):
+            S.sla_sparse_fwd_i8(qbuf, q, wl.bq, wl.bk, rp, ci, out=out)
+        e[2].record()
+        torch.cuda.synchronize()
+        t_q = e[0].elapsed_time(e[1]) / args.steps
+        t_i8 = e[1].elapsed_time(e[2]) / args.steps
+        i8_ops = pair_flops * nnz
+        res["i8"] = {"quantize_ms": t_q, "sparse_fwd_i8_ms": t_i8,
+                     "achieved": i8_ops / (t_i8 * 1e-3) / 1e12, "peak": PEAK_I8_TOPS, "unit": "TOP/s",
+                     "frac": i8_ops / (t_i8 * 1e-3) / 1e12 / PEAK_I8_TOPS,
+                     "kernel": f"attn_i8_kernel<d={wl.d},bq={wl.bq},bk={wl.bk}>",
+                     "vs_bf16_sparse": t_sp / t_i8, "with_quantize_vs_bf16_sparse": t_sp / (t_q + t_i8)}
 
     # SoftTop-k weights of every mask row (pool + logits + threshold solve),
     # the router-training form of the selection, at temperature 0.5

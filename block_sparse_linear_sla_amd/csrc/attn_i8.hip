@@ -24,9 +24,11 @@
 //                       them (key 8a + 4h + b at byte 16h + 4a + b);
 //   attn_i8_kernel      one workgroup of BQ/32 wavefronts per mask row; two
 //                       passes over the row's 64-key units: pass 1 computes
-//                       the integer scores and the exact row maximum, pass 2
-//                       recomputes them, forms the P codes in registers and
-//                       accumulates P V in int32 on the matrix cores.  With
+//                       the integer scores and the exact row maximum (two
+//                       units per step), pass 2 recomputes them, forms the P
+//                       codes in registers and accumulates P V in int32 on
+//                       the matrix cores (tiles loaded two steps ahead into a
+//                       ring of three LDS stages).  With
 //                       the maximum known before any code is formed, no
 //                       rescale is ever needed: the output is one int32 sum
 //                       per element, scaled once at the end.
@@ -55,6 +57,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int QROWS = 256;  // rows per chunk of the V channel maxima
+
+template <int I>
+struct IntTag {
+  static constexpr int value = I;
+};
 
 // ------------------------------------------------------------------ helpers
 // 16 bytes of input as floats: bf16 (8 values) or fp32 (4 values).
@@ -121,10 +128,24 @@ __device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, (int)soff, 0, 0);
 }
 
-// s_waitcnt vmcnt(0) alone (expcnt and lgkmcnt at their no-wait maxima)
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8) | (0 << 14)); }
+// s_waitcnt on the vector-memory counter alone (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt at their no-wait maxima).  Direct loads
+// to LDS count on vmcnt in issue order.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ uint4 rd16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// v itself, opaque to the optimiser: per-lane offsets derived from it are
+// recomputed where they are used instead of being kept live (or spilled)
+// across the loop.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 __device__ __forceinline__ i32x16 mfma8(const i32x4& a, const i32x4& b, const i32x16& c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
@@ -294,30 +315,45 @@ struct I8Load {
       vv[i] = (uint32_t)(c * 64 + 16 * (pv ^ TT::swv(c)));
     }
   }
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int key0,
-                                       bool with_v, char* dst) const {
-    const uint32_t soff = (uint32_t)key0 * D;
+  // the K tile of the unit at key0 into dst (NK loads per wavefront)
+  __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t rk, int key0, char* dst) const {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) b2lds16(rk, kv[i], soff, dst + 1024 * (w + NW * i));
-    if (with_v) {
+    for (int i = 0; i < NK; ++i) b2lds16(rk, kv[i], (uint32_t)key0 * D, dst + 1024 * (w + NW * i));
+  }
+  // its V^T tile into dst (NK loads per wavefront)
+  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t rv, int key0, char* dst) const {
 #pragma unroll
-      for (int i = 0; i < NK; ++i) b2lds16(rv, vv[i], soff, dst + TT::KT + 1024 * (w + NW * i));
-    }
+    for (int i = 0; i < NK; ++i) b2lds16(rv, vv[i], (uint32_t)key0 * D, dst + 1024 * (w + NW * i));
   }
 };
 
-// S^T of a unit: two 32-key tiles, D/32 k-steps each.
-template <int D>
-__device__ __forceinline__ void score8(const char* Ks, const i32x4 (&qf)[D / 32], const int (&koff)[D / 32],
-                                       i32x16 (&sc)[2]) {
+// S^T of one 32-key tile of a unit (D/32 k-steps), the K fragments read PF
+// matrix ops ahead of their use (a rolling window of PF registers), in an
+// order pinned with sched_group_barrier so that the LDS latency stays hidden
+// behind the matrix ops already issued.
+template <int D, int PF>
+__device__ __forceinline__ i32x16 score_tile(const char* Kt, const i32x4 (&qf)[D / 32],
+                                             const int (&koff)[D / 32]) {
   constexpr int NT = D / 32;
-  uint4 fr[2 * NT];
+  static_assert(PF <= NT, "prefetch window");
+  uint4 fr[PF];
 #pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) fr[i] = rd16(Ks + (i / NT) * 32 * D + koff[i % NT]);
-  sc[0] = i32x16{};
-  sc[1] = i32x16{};
+  for (int i = 0; i < PF; ++i) fr[i] = rd16(Kt + koff[i]);
+  i32x16 sc = i32x16{};
 #pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) sc[i / NT] = mfma8(__builtin_bit_cast(i32x4, fr[i]), qf[i % NT], sc[i / NT]);
+  for (int i = 0; i < NT; ++i) {
+    const uint4 a = fr[i % PF];
+    if (i + PF < NT) fr[i % PF] = rd16(Kt + koff[i + PF]);
+    sc = mfma8(__builtin_bit_cast(i32x4, a), qf[i], sc);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // PF LDS reads
+#pragma unroll
+  for (int i = 0; i + PF < NT; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix op
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  return sc;
 }
 
 template <int D, int BQ, int SUB, int OES>
@@ -329,8 +365,11 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_i8_kernel(
   using TT = I8Tiles<D>;
   constexpr int NW = BQ / 32;
   constexpr int STAGE = TT::KT + TT::VT;
+  // three distinct stage arrays, so the compiler can tell the loads into one
+  // from the operand reads of another
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -362,76 +401,119 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_i8_kernel(
     const float* skh = sk + bh * Nk;
     const auto rk = buf_rsrc(k8 + (size_t)bh * Npad * D, (uint32_t)Npad * D);
     const auto rv = buf_rsrc(vt8 + (size_t)bh * Npad * D, (uint32_t)Npad * D);
-    const I8Load<D, NW> lp(w, lane);
-    const int nsteps = 2 * nunits;  // pass 1: steps 0 .. nunits-1, pass 2: the rest
+    using LP = I8Load<D, NW>;
+    // Steps: pass 1 scores the K tiles of two units per step (n1 steps),
+    // pass 2 takes one unit's K and V^T tiles per step.  Every step loads two
+    // tiles (the second K tile of an odd last pass-1 step repeats the first),
+    // so each step issues 2 NK loads per wavefront, two steps ahead of use
+    // into a ring of three stages.
+    const int n1 = (nunits + 1) >> 1;
+    const int nsteps = n1 + nunits;
     float m = -INFINITY, nb = 0.f;
     auto blk_of = [&](int u) { return col_idx[base + u / SUB]; };
     auto key0_of = [&](int u, int blk) { return (blk * SUB + u % SUB) * 64; };
-
-    auto step = [&](int s, char* cur, char* nxt) __attribute__((always_inline)) {
-      const bool p2 = s >= nunits;
-      const int u = p2 ? s - nunits : s;
+    auto issue = [&](int s, char* dst) __attribute__((always_inline)) {
+      const LP lp(w, opaque(lane));
+      if (s < n1) {
+        const int u0 = 2 * s, u1 = min(2 * s + 1, nunits - 1);
+        lp.load_k(rk, key0_of(u0, blk_of(u0)), dst);
+        lp.load_k(rk, key0_of(u1, blk_of(u1)), dst + TT::KT);
+      } else {
+        const int u = s - n1;
+        const int k0 = key0_of(u, blk_of(u));
+        lp.load_k(rk, k0, dst);
+        lp.load_v(rv, k0, dst + TT::KT);
+      }
+    };
+    constexpr int PF = D == 128 ? 2 : 1;
+    // pass 1 on the K tile of unit u: this lane's largest score.  MASK: the
+    // unit runs past N (only the last unit of a sequence), keys at offset
+    // >= lim do not exist; the common case carries no per-element test.
+    auto pass1_unit = [&](const char* Ks, int u) __attribute__((always_inline)) {
       const int blk = blk_of(u);
-      const int kcur = key0_of(u, blk);
-      const int s1 = s + 1;
-      const int u1 = s1 >= nunits ? s1 - nunits : s1;
-      const int knext = s1 < nsteps ? key0_of(u1, blk_of(u1)) : 0;
-      const float cu = (sqv * skh[blk]) * lam;  // fl32(fl32(sq sk) / sqrt(d))
-      wait_vm0();       // this wavefront's loads of unit s have landed
-      __syncthreads();  // ... and every wavefront's; unit s-1 consumed
-      if (s1 < nsteps) lp.load(rk, rv, knext, s1 >= nunits, nxt);
-      const int lim = min(64, N - kcur);  // valid keys of the unit
-      i32x16 sc[2];
-      score8<D>(cur, qf, koff, sc);
-      if (!p2) {
+      const int lim = min(64, N - key0_of(u, blk));  // valid keys of the unit
+      const float cu = (sqv * skh[blk]) * lam;        // fl32(fl32(sq sk) / sqrt(d))
+      auto body = [&](auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value != 0;
+        const int limh = lim - 4 * hi;  // element i of tile kt is key 32 kt + 8 (i/4) + 4 hi + i%4
         int im = INT_MIN;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) {
+          const i32x16 sc = score_tile<D, PF>(Ks + kt * 32 * D, qf, koff);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = 32 * kt + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (lim == 64 || key < lim) im = max(im, sc[kt][i]);
+          for (int i = 0; i < 16; i += 2) {
+            const int a = (!MASK || 32 * kt + 8 * (i >> 2) + (i & 3) < limh) ? sc[i] : INT_MIN;
+            const int b = (!MASK || 32 * kt + 8 * (i >> 2) + (i & 3) + 1 < limh) ? sc[i + 1] : INT_MIN;
+            im = max(im, max(a, b));  // v_max3_i32
           }
-        if (im != INT_MIN) m = fmaxf(m, (float)im * cu);
-      } else {
-        if (u == 0) {
-          // the row maximum of this query: lanes l and l^32 hold its two key halves
-          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-          m = fmaxf(m, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
-          nb = (m * l2e) - l2_127;  // fl32(fl32(m log2 e) - log2 127); no contraction in this file
         }
-        const float au = cu * l2e;
-        i32x4 pc[2];
+        if (im != INT_MIN) m = fmaxf(m, (float)im * cu);
+      };
+      if (lim < 64) body(IntTag<1>{});
+      else body(IntTag<0>{});
+    };
+    // pass 2 on unit u (K tile at cur, V^T tile after it), one 32-key tile at
+    // a time: scores, P codes (the B operand), then its share of P V
+    auto pass2_unit = [&](const char* cur, int u) __attribute__((always_inline)) {
+      if (u == 0) {
+        // the row maximum of this query: lanes l and l^32 hold its two key halves
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(m, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+        nb = (m * l2e) - l2_127;  // fl32(fl32(m log2 e) - log2 127); no contraction in this file
+      }
+      const int blk = blk_of(u);
+      const int lim = min(64, N - key0_of(u, blk));
+      const float au = ((sqv * skh[blk]) * lam) * l2e;
+      const char* Vs = cur + TT::KT;
+      auto body = [&](auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value != 0;
+        const int limh = lim - 4 * hi;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < 2; ++kt) {
+          const i32x16 sc = score_tile<D, PF>(cur + kt * 32 * D, qf, koff);
+          i32x4 pc;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             uint32_t wd = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int i = 4 * e + j;
-              float t = __builtin_fmaf((float)sc[kt][i], au, -nb);
-              if (lim < 64 && 32 * kt + 8 * e + 4 * hi + j >= lim) t = -INFINITY;
+              float t = __builtin_fmaf((float)sc[4 * e + j], au, -nb);
+              if (MASK && 32 * kt + 8 * e + j >= limh) t = -INFINITY;
               wd = __builtin_amdgcn_cvt_pk_u8_f32(__builtin_amdgcn_exp2f(t), j, wd);
             }
-            pc[kt][e] = (int)wd;
+            pc[e] = (int)wd;
             lsum = __builtin_amdgcn_udot4(wd, 0x01010101u, lsum, false);
           }
-        const char* Vs = cur + TT::KT;
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-          for (int g = 0; g < 2; ++g)
-            acc[dt] = mfma8(__builtin_bit_cast(i32x4, rd16(Vs + dt * 32 * 64 + voff[g])), pc[g], acc[dt]);
+          for (int dt = 0; dt < D / 32; ++dt)
+            acc[dt] = mfma8(__builtin_bit_cast(i32x4, rd16(Vs + dt * 32 * 64 + voff[kt])), pc, acc[dt]);
+        }
+      };
+      if (lim < 64) body(IntTag<1>{});
+      else body(IntTag<0>{});
+    };
+    auto step = [&](int s, const char* cur, char* ahead) __attribute__((always_inline)) {
+      if (s + 1 < nsteps) wait_vm<2 * LP::NK>();  // step s landed; step s+1 may be in flight
+      else wait_vm<0>();
+      __syncthreads();  // every wavefront's loads of step s landed; step s-1 consumed
+      if (s + 2 < nsteps) issue(s + 2, ahead);
+      if (s < n1) {
+        pass1_unit(cur, 2 * s);
+        if (2 * s + 1 < nunits) pass1_unit(cur + TT::KT, 2 * s + 1);
+      } else {
+        pass2_unit(cur, s - n1);
       }
     };
-    lp.load(rk, rv, key0_of(0, blk_of(0)), false, st0);
+    issue(0, st0);
+    if (nsteps > 1) issue(1, st1);
     int s = 0;
-    for (; s + 2 <= nsteps; s += 2) {
-      step(s, st0, st1);
+    for (; s + 3 <= nsteps; s += 3) {
+      step(s, st0, st2);
       step(s + 1, st1, st0);
+      step(s + 2, st2, st1);
     }
-    wait_vm0();  // nsteps is even: no load outlives the loop
+    if (s < nsteps) step(s, st0, st2);
+    if (s + 1 < nsteps) step(s + 1, st1, st0);
   }
 
   const uint32_t L = lsum + (uint32_t)__shfl_xor((int)lsum, 32);
