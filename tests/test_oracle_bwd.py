@@ -1,0 +1,82 @@
+"""Pins of the oracle's sparse-branch backward and alpha gradient: central
+finite differences of the forward definition on a tiny ragged case (every
+input element), the full-mask case against dense attention's gradient through
+torch's scaled_dot_product_attention in float64, rows with no selected block,
+and the alpha gradient against a finite difference of the mixed output."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sla_oracle as O
+
+
+def _tiny(seed=0, N=11, d=4, bq=4, bk=3):
+    rng = np.random.default_rng(seed)
+    Q, K, V, dO = (rng.normal(size=(1, 2, N, d)) for _ in range(4))
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp, ci = [0], []
+    for r in range(2 * Nq):
+        sel = [j for j in range(Nk) if rng.random() < 0.5] if r != 1 else []
+        ci.extend(sel)
+        rp.append(len(ci))
+    return Q, K, V, dO, np.array(rp), np.array(ci, dtype=np.int64), bq, bk
+
+
+def _loss(Q, K, V, dO, rp, ci, bq, bk):
+    out = O.sparse_branch(Q, K, V, bq, bk, rp, ci)
+    N = Q.shape[2]
+    return sum(float((o * dO[b, h, slice(*O.block_range(i, bq, N))]).sum()) for (b, h, i), o in out.items())
+
+
+def test_finite_differences_every_element():
+    Q, K, V, dO, rp, ci, bq, bk = _tiny()
+    g = O.sparse_branch_backward(Q, K, V, bq, bk, rp, ci, dO)
+    eps = 1e-6
+    for name, X in (("dQ", Q), ("dK", K), ("dV", V)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[idx] += eps
+            Xm[idx] -= eps
+            args = {"dQ": (Xp, K, V), "dK": (Q, Xp, V), "dV": (Q, K, Xp)}[name]
+            argm = {"dQ": (Xm, K, V), "dK": (Q, Xm, V), "dV": (Q, K, Xm)}[name]
+            num[idx] = (_loss(*args, dO, rp, ci, bq, bk) - _loss(*argm, dO, rp, ci, bq, bk)) / (2 * eps)
+        np.testing.assert_allclose(g[name], num, atol=1e-7, rtol=1e-6, err_msg=name)
+
+
+def test_empty_row_contributes_nothing():
+    Q, K, V, dO, rp, ci, bq, bk = _tiny(seed=1)
+    g = O.sparse_branch_backward(Q, K, V, bq, bk, rp, ci, dO)
+    # row r = 1 is (b 0, h 0, query block 1) and selects nothing
+    assert not g["dQ"][0, 0, 4:8].any()
+    dO2 = dO.copy()
+    dO2[0, 0, 4:8] = 123.0    # its upstream gradient has no effect anywhere
+    g2 = O.sparse_branch_backward(Q, K, V, bq, bk, rp, ci, dO2)
+    for k in g:
+        np.testing.assert_array_equal(g[k], g2[k])
+
+
+def test_full_mask_is_dense_gradient():
+    rng = np.random.default_rng(2)
+    N, d, bq, bk = 37, 8, 8, 16
+    Q, K, V, dO = (rng.normal(size=(1, 2, N, d)) for _ in range(4))
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp = np.arange(0, 2 * Nq + 1) * Nk
+    ci = np.tile(np.arange(Nk), 2 * Nq)
+    g = O.sparse_branch_backward(Q, K, V, bq, bk, rp, ci, dO)
+    q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+    torch.nn.functional.scaled_dot_product_attention(q, k, v).backward(torch.tensor(dO))
+    for name, t in (("dQ", q), ("dK", k), ("dV", v)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), atol=1e-12, err_msg=name)
+
+
+def test_alpha_gradient_finite_difference():
+    Q, K, V, dO, rp, ci, bq, bk = _tiny(seed=3)
+    Os = O.assemble(O.sparse_branch(Q, K, V, bq, bk, rp, ci), 1, 2, 11, 4, bq)
+    Ol = O.assemble(O.linear_branch(Q, K, V, bq, bk, rp, ci), 1, 2, 11, 4, bq)
+    ga = O.alpha_grad(dO, Os, Ol)
+    for h in range(2):
+        def loss(a):
+            return float((dO[:, h] * O.combine(Os[:, h], Ol[:, h], a)).sum())
+        num = (loss(0.3 + 1e-6) - loss(0.3 - 1e-6)) / 2e-6
+        assert ga[h] == pytest.approx(num, abs=1e-7)
