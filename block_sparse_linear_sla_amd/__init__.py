@@ -26,6 +26,7 @@ STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
 EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_soft_topk", "sla_sparse_fwd",
            "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
            "sla_dense_fwd", "sla_i8_layout_of", "sla_quantize_i8", "sla_sparse_fwd_i8",
+           "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_alpha_grad",
            "sla_status_string")
 
 
@@ -78,11 +79,15 @@ def lib() -> ctypes.CDLL:
         L.sla_i8_layout_of.argtypes = [P, ctypes.POINTER(I8Layout)]
         L.sla_quantize_i8.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_sparse_fwd_i8.argtypes = [P, vp, ctypes.c_size_t, vp, vp, vp, vp]
+        L.sla_bwd_workspace_bytes.argtypes = [P]
+        L.sla_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.sla_sparse_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_alpha_grad.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
         for fn in ("sla_mask", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
                    "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd", "sla_i8_layout_of",
-                   "sla_quantize_i8", "sla_sparse_fwd_i8"):
+                   "sla_quantize_i8", "sla_sparse_fwd_i8", "sla_sparse_bwd", "sla_alpha_grad"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -305,3 +310,37 @@ def i8_views(qbuf: torch.Tensor, shape, bq: int, bk: int, dtype=torch.bfloat16) 
         "sv": region(lay.sv, BH * d, torch.float32).view(BH, d),
         "rv": region(lay.rv, BH * d, torch.float32).view(BH, d),
     }
+
+
+# ------------------------------------------------------------------ backward
+def sla_bwd_workspace_bytes(prob: Problem) -> int:
+    return int(lib().sla_bwd_workspace_bytes(ctypes.byref(prob)))
+
+
+def bwd_workspace(prob: Problem, device=None) -> torch.Tensor:
+    n = sla_bwd_workspace_bytes(prob)
+    if n == 0:
+        raise ValueError("invalid problem")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sla_sparse_bwd(q, k, v, do_s, bq: int, bk: int, row_ptr, col_idx, ws=None, out=None):
+    """Gradient of sum(O_s * dO_s) with the mask fixed: returns (dQ, dK, dV)."""
+    _need(q, k, v, do_s, like=q)
+    prob = problem(q, bq, bk)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    w = ws if ws is not None else bwd_workspace(prob, q.device)
+    _check("sla_sparse_bwd", lib().sla_sparse_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do_s), _ptr(row_ptr), _ptr(col_idx), _ptr(dq), _ptr(dk),
+                                                  _ptr(dv), _ptr(w), w.numel(), _stream()))
+    return dq, dk, dv
+
+
+def sla_alpha_grad(do, o_s, o_l, bq: int = 128, bk: int = 64, ws=None) -> torch.Tensor:
+    """d/d alpha of sum(O * dO), O = alpha_h O_s + (1 - alpha_h) O_l: float32 [H]."""
+    _need(do, o_s, o_l, like=do)
+    prob = problem(do, bq, bk)
+    da = torch.empty(do.shape[1], dtype=torch.float32, device=do.device)
+    w = ws if ws is not None else bwd_workspace(prob, do.device)
+    _check("sla_alpha_grad", lib().sla_alpha_grad(ctypes.byref(prob), _ptr(do), _ptr(o_s), _ptr(o_l), _ptr(da),
+                                                  _ptr(w), w.numel(), _stream()))
+    return da

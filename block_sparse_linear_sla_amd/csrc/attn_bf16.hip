@@ -42,200 +42,10 @@
 // the row's listed blocks, so O_l = phi(Q) H_u / phi(Q) z_u; phi(Q) H_u is a
 // hi + lo split product (three bf16 MFMAs), again ~16 mantissa bits.
 #include "sla_internal.h"
+#include "bf16_tiles.h"
 
 namespace sla {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int I>
-struct IntTag {
-  static constexpr int value = I;
-};
-
-__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-// two floats -> packed bf16 pair (round to nearest even, v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-
-// Workgroups are dispatched round-robin over the 8 XCDs (blockIdx % 8), each
-// XCD with its own L2.  Map them so that every XCD walks a contiguous range of
-// mask rows: adjacent query blocks of a head select largely the same key
-// blocks, so their K / V tiles are then shared in one L2.
-__device__ __forceinline__ long long xcd_row(long long b, long long R) {
-  constexpr long long NX = 8;
-  const long long q = R / NX, r = R % NX;
-  const long long x = b % NX, local = b / NX;
-  return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
-}
-
-__device__ __forceinline__ uint32_t elem(const uint4& v, int e) {
-  const uint32_t w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// ------------------------------------------------------------------ attention
-constexpr int LDS_BYTES = 160 * 1024;  // LDS of one gfx950 compute unit
-constexpr int KU = 64;                 // keys per attention unit; a listed block of BK keys is BK/64 units
-
-// LDS tile layout of one 64-key unit of K or V.  Every direct load instruction
-// brings 64 x 16 bytes that land in LDS in lane order, so a tile is stored as
-// rows of whole 128-byte global lines - [D/64 halves][64 keys][128 B],
-// row-major as in memory - and each load covers 8 complete lines.  Inside a
-// row, 16-byte chunk c of key r sits at c ^ sw(r), sw(r) = f((r >> 1) & 7)
-// with f(b) = 4 (b & 1) + (b >> 1):
-//   * the 16 keys that a 16-lane group reads for one S operand (one chunk
-//     each) hit 16 distinct bank groups (f is a permutation of 0..7);
-//   * the 4 keys x 64 bytes of one transposed read by 32 lanes hit 64
-//     distinct banks (keys r and r + 2 differ in bit 2 of sw).
-// H_u^T (written with ordinary LDS stores after the loop) keeps a "plane"
-// layout: every 16-element k-slice is a plane of 32 bytes per row, the two
-// 16-byte halves swapped when bit 3 of the row is set.
-template <int D>
-struct Tiles {
-  static constexpr int KHALF = KU * 128;       // bytes of one 64-d half of a tile
-  static constexpr int KT_BYTES = KU * D * 2;  // one [64 keys x D] tile
-  static constexpr int HPB = D * 32;           // bytes of one H_u^T plane (16 d_k)
-};
-
-__device__ __forceinline__ int sw(int r) {
-  const int b = (r >> 1) & 7;
-  return ((b & 1) << 2) | (b >> 1);
-}
-
-__device__ __forceinline__ int lane_base(int lane) {
-  const int l32 = lane & 31, hi = lane >> 5;
-  return l32 * 32 + 16 * (hi ^ ((l32 >> 3) & 1));
-}
-
-// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i%4
-// of the 4-element pieces addressed by lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4.
-__device__ __forceinline__ s16x4 tr16(const char* p) {
-  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-}
-
-__device__ __forceinline__ bf16x8 cat_tr(const char* a, const char* b) {
-  const s16x4 x = tr16(a), y = tr16(b);
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// Per-lane byte offsets of the MFMA operand reads (lane l: row l%32 of a
-// 32-row tile, k-slice half l/32).
-//   K (S operand): the 16-wide d step t of key subtile kt at (t/4) KHALF +
-//     4096 kt + off[t%4] (one 16-byte read).
-//   V^T / phi(K)^T (transposed reads of a row-major tile): rows d = 32 dt +
-//     l%32, the 8 keys of key plane pl in the order 4h + {0..3}, 4h + 8 +
-//     {0..3} (h = l/32).  Lanes 4m .. 4m+3 of a 16-lane group address key
-//     4h + m (+ 8 for the second read, tro[1]) and 4 consecutive d each, so
-//     lane i receives d = base + i across the 4 keys.
-template <int D>
-struct ReadPlan {
-  int off[4], tro[2][2];  // tro[second read][32-d half of a 64-d half]
-  __device__ __forceinline__ explicit ReadPlan(int lane) {
-    const int l32 = lane & 31, hi = lane >> 5;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) off[t] = l32 * 128 + 16 * ((2 * t + hi) ^ sw(l32));
-    const int i = lane & 15, g2 = (lane >> 4) & 1;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int kl = 4 * hi + (i >> 2) + 8 * j;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int d = 32 * p + 16 * g2 + 4 * (i & 3);
-        tro[j][p] = kl * 128 + 16 * ((d >> 3) ^ sw(kl)) + 8 * ((d >> 2) & 1);
-      }
-    }
-  }
-  __device__ __forceinline__ const char* kp(const char* Ks, int kt, int t) const {
-    return Ks + (t / 4) * Tiles<D>::KHALF + kt * 4096 + off[t % 4];
-  }
-  __device__ __forceinline__ bf16x8 vt(const char* Vs, int dt, int pl) const {
-    // dt may be a wave-uniform runtime value: select rather than index
-    const char* b = Vs + (dt / 2) * Tiles<D>::KHALF + pl * 16 * 128;
-    return cat_tr(b + ((dt & 1) ? tro[0][1] : tro[0][0]), b + ((dt & 1) ? tro[1][1] : tro[1][0]));
-  }
-};
-
-__device__ __forceinline__ uint4 rd16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// v itself, opaque to the optimiser: per-lane offsets derived from it are
-// then recomputed where they are used instead of being kept live (or
-// spilled) across a loop.
-__device__ __forceinline__ int opaque(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14, expcnt and lgkmcnt left at their no-wait maxima).  Direct
-// loads to LDS count on vmcnt, in issue order.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-// s_waitcnt lgkmcnt(0) only: every LDS read of this wavefront has returned.
-__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
-
-// Buffer resource over [base, base + bytes) for raw (unstructured) buffer
-// loads; reads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-
-// Direct buffer load of 16 bytes per lane into LDS: lane l writes
-// lds_wave_base + 16 l; the byte address is voff + soff in the buffer.
-__device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
-                                        void* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, (int)soff, 0, 0);
-}
-
-// Direct loads of one unit's K or V tile into LDS, split over NWL wavefronts.
-// Load slot u of a tile fills the 1 KB at tile + 1024 u (8 rows of 128 bytes,
-// in the swizzled layout above): lane l brings the 16-byte chunk that belongs
-// at position l.  Each load is a per-head buffer resource over a row-major
-// [N, D] array, the unit's byte offset (scalar) and a per-lane byte offset
-// fixed for the kernel; rows past N read as zeros.
-template <int D, int NWL>
-struct LoadPlan {
-  using T = Tiles<D>;
-  static constexpr int NK = T::KT_BYTES / 1024 / NWL;   // slots per wavefront and tile
-  static_assert(NK * NWL * 1024 == T::KT_BYTES, "tile split");
-  uint32_t voff[NK];
-  int w;
-
-  __device__ __forceinline__ LoadPlan(int w_, int lane) : w(w_) {
-#pragma unroll
-    for (int ii = 0; ii < NK; ++ii) {
-      const int u = w + NWL * ii;
-      const int hd = u / 8, key = 8 * (u % 8) + (lane >> 3);
-      voff[ii] = (uint32_t)(key * D * 2 + hd * 128 + 16 * ((lane & 7) ^ sw(key)));
-    }
-  }
-  // the tile of the unit starting at key key0
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int key0, char* dst) const {
-    const uint32_t soff = (uint32_t)key0 * (D * 2);
-#pragma unroll
-    for (int ii = 0; ii < NK; ++ii) b2lds16(r, voff[ii], soff, dst + 1024 * (w + NWL * ii));
-  }
-};
 
 // How the D x D tiles of G = phi(K)^T V are split over NW wavefronts: each
 // takes TPW 32 x 32 tiles, MTN whole row tiles (d_k) when it has at least a
@@ -294,15 +104,6 @@ __device__ __forceinline__ void load_phi(__amdgpu_buffer_rsrc_t r, int mt0, int 
   }
 }
 
-// max of v over lanes l and l^32 (v_permlane32_swap exchanges the two halves;
-// taking the max with the own value makes the result independent of which
-// output holds which half)
-__device__ __forceinline__ float pair_max(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __builtin_elementwise_maximum(
-      v, __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1])));
-}
-
 // Running online-softmax state of one query; lanes l and l^32 hold the two
 // key halves of the same query and keep identical m.
 struct Softmax {
@@ -312,73 +113,6 @@ struct Softmax {
   float l;     // this lane's running sum of the (bf16-rounded) P values
   __device__ __forceinline__ Softmax() : m(-INFINITY), thr(-INFINITY), mneg(0.f), l(0.f) {}
 };
-
-// S^T of a whole unit (two 32-key subtiles) with the K fragments read PF
-// MFMAs ahead of their use, so the LDS latency stays hidden behind the
-// matrix ops already issued.
-template <int D, int PF>
-__device__ __forceinline__ void score_unit(const char* Ks, const bf16x8 (&qf)[D / 16], const ReadPlan<D>& rp,
-                                           f32x16 (&s)[2]) {
-  constexpr int NT = D / 16;        // k-steps per subtile
-  constexpr int NI = 2 * NT;        // MFMAs of the unit
-  uint4 fr[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) fr[i] = rd16(rp.kp(Ks, i / NT, i % NT));
-  s[0] = f32x16{};
-  s[1] = f32x16{};
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const uint4 a = fr[i % PF];
-    if (i + PF < NI) fr[i % PF] = rd16(rp.kp(Ks, (i + PF) / NT, (i + PF) % NT));
-    s[i / NT] = mfma(as_bf16x8(a), qf[i % NT], s[i / NT]);
-  }
-  // keep that order: the scheduler would otherwise pull each read down to
-  // just before its MFMA
-  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // PF LDS reads
-#pragma unroll
-  for (int i = 0; i + PF < NI; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
-}
-
-// S^T of the 32-key half KT of a unit (K fragments read PF MFMAs ahead,
-// order pinned as in score_unit).
-template <int D, int KT, int PF>
-__device__ __forceinline__ f32x16 score_half(const char* Ks, const bf16x8 (&qf)[D / 16], const ReadPlan<D>& rp) {
-  constexpr int NT = D / 16;
-  uint4 fr[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) fr[i] = rd16(rp.kp(Ks, KT, i));
-  f32x16 s = f32x16{};
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    const uint4 a = fr[i % PF];
-    if (i + PF < NT) fr[i % PF] = rd16(rp.kp(Ks, KT, i + PF));
-    s = mfma(as_bf16x8(a), qf[i], s);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-  for (int i = 0; i + PF < NT; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
-  return s;
-}
-
-// Q fragments of 32 query rows (B operand of S^T = K Q^T), zero past N.
-template <int D>
-__device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, int N, int hi,
-                                       bf16x8 (&qf)[D / 16]) {
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) {
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (q < N) v = *reinterpret_cast<const uint4*>(Q + ((size_t)bh * N + q) * D + 16 * t + 8 * hi);
-    qf[t] = as_bf16x8(v);
-  }
-}
 
 // Online softmax of one wavefront's scores sc over a unit (two 32-key
 // subtiles) into the P operands bp of its 4 key planes.  One max exchange and

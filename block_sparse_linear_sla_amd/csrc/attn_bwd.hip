@@ -1,0 +1,523 @@
+// Backward of the sparse branch (bf16) on gfx950 matrix cores.
+//
+// Source: SLA2 write-up (arXiv:2602.12675) §一 (the sparse branch: exact
+// softmax attention of each query over the keys of its selected blocks) and
+// §四 (the attention is trained end to end with the block selection fixed per
+// step).  With the mask held fixed, for each (query block i, key block j) pair
+// of the mask and P = softmax over the row's selected keys:
+//   dV_j += P^T dO_i,   dP = dO_i V_j^T,   dS = P o (dP - D_i),
+//   dQ_i += dS K_j / sqrt(d),   dK_j += dS^T Q_i / sqrt(d),
+// with D_t = dO_t . O_t = sum_u P_tu dP_tu per query - the textbook
+// softmax-attention gradient restricted to the listed pairs.  D is formed
+// here from the second form, in float32 with the same P as the gradient
+// (rather than from a rounded forward output, whose error would shift every
+// dS of the row by the same amount).
+//
+// Kernels:
+//   csc_count_kernel / csc_scan_kernel / csc_fill_kernel  the mask's
+//       transpose: for each key block, the query blocks that list it, in
+//       ascending order (one thread per key block binary-searches every
+//       row: deterministic, no atomics);
+//   bwd_dq_kernel    one workgroup per mask row (BQ/32 wavefronts, 32
+//       queries each, queries on the lane axis as in the forward).  Pass A
+//       walks the row's 64-key units with S^T = K Q^T and dP^T = V dO^T for
+//       each query's log-sum-exp and D (online, like the forward's softmax);
+//       pass B recomputes both, forms dS in registers, and accumulates
+//       dQ^T += K^T dS^T with K read transposed (as the forward reads V).
+//       Writes dQ, and the log-sum-exp (base 2) and D of every query for the
+//       next kernel (+inf / 0 past N);
+//   bwd_dkdv_kernel  one workgroup per 64-key unit, walking the query blocks
+//       that list its key block in 64-query units.  Wavefront w keeps the
+//       K and V rows of 32 keys (half w%2) in registers and the dK^T, dV^T
+//       tiles of half w/2 of d: S = Q K^T and dP = dO V^T (queries x keys,
+//       keys on the lane axis), P and dS in registers, then
+//       dV^T += dO^T P and dK^T += Q^T dS with Q and dO read transposed.
+#include "sla.h"
+#include "sla_internal.h"
+#include "bf16_tiles.h"
+
+namespace sla {
+namespace {
+
+// ------------------------------------------------------------ mask transpose
+// first index in the sorted list a[0..n) that is >= x
+__device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// counts[bh * Nk + j] = number of query blocks of head bh whose row lists j
+__global__ __launch_bounds__(256) void csc_count_kernel(const int* __restrict__ row_ptr,
+                                                        const int* __restrict__ col_idx, int Nq, int Nk,
+                                                        long long BH, int* __restrict__ counts) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= BH * Nk) return;
+  const long long bh = t / Nk;
+  const int j = (int)(t % Nk);
+  int c = 0;
+  for (int i = 0; i < Nq; ++i) {
+    const long long r = bh * Nq + i;
+    const int b = row_ptr[r], n = row_ptr[r + 1] - b;
+    const int p = lower_bound(col_idx + b, n, j);
+    c += (p < n && col_idx[b + p] == j) ? 1 : 0;
+  }
+  counts[t] = c;
+}
+
+// col_ptr = exclusive prefix sum of counts (n entries, one workgroup)
+__global__ __launch_bounds__(1024) void csc_scan_kernel(const int* __restrict__ counts, long long n,
+                                                        int* __restrict__ col_ptr) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const long long per = (n + 1023) / 1024;
+  const long long a = t * per, b = min(n, a + per);
+  int s = 0;
+  for (long long x = a; x < b; ++x) s += counts[x];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = t ? part[t - 1] : 0;
+  for (long long x = a; x < b; ++x) {
+    col_ptr[x] = run;
+    run += counts[x];
+  }
+  if (t == 1023) col_ptr[n] = part[1023];
+}
+
+// row_idx[col_ptr[bh * Nk + j] ...] = the query blocks listing j, ascending
+__global__ __launch_bounds__(256) void csc_fill_kernel(const int* __restrict__ row_ptr,
+                                                       const int* __restrict__ col_idx, int Nq, int Nk,
+                                                       long long BH, const int* __restrict__ col_ptr,
+                                                       int* __restrict__ row_idx) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= BH * Nk) return;
+  const long long bh = t / Nk;
+  const int j = (int)(t % Nk);
+  int o = col_ptr[t];
+  for (int i = 0; i < Nq; ++i) {
+    const long long r = bh * Nq + i;
+    const int b = row_ptr[r], n = row_ptr[r + 1] - b;
+    const int p = lower_bound(col_idx + b, n, j);
+    if (p < n && col_idx[b + p] == j) row_idx[o++] = i;
+  }
+}
+
+// ------------------------------------------------------------------ helpers
+// Store the D/32-row-tile accumulators acc (rows d = 32 (T0 + t) + ..., one
+// column per lane: this lane's row `row`) times scale as bf16, NT tiles.
+// Each 16-byte store holds 8 consecutive d of one row: lanes l and l^32 hold
+// the two 4-d halves of every 8-d chunk and swap one of them.
+template <int NT>
+__device__ __forceinline__ void store_T(const f32x16 (&acc)[NT], float scale, uint16_t* dst, int d0, bool valid,
+                                        int hi) {
+#pragma unroll
+  for (int mt = 0; mt < NT; ++mt) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint2 pv[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int i4 = 2 * j + c;
+        pv[c] = make_uint2(pk_bf16(scale * acc[mt][4 * i4], scale * acc[mt][4 * i4 + 1]),
+                           pk_bf16(scale * acc[mt][4 * i4 + 2], scale * acc[mt][4 * i4 + 3]));
+      }
+      const uint2 send = hi ? pv[0] : pv[1];
+      const uint2 recv = make_uint2(__shfl_xor(send.x, 32), __shfl_xor(send.y, 32));
+      const uint4 outv = hi ? make_uint4(recv.x, recv.y, pv[1].x, pv[1].y)
+                            : make_uint4(pv[0].x, pv[0].y, recv.x, recv.y);
+      if (valid) *reinterpret_cast<uint4*>(dst + d0 + 32 * mt + 16 * j + 8 * hi) = outv;
+    }
+  }
+}
+
+// 16 fp32 values of a 32-key S^T half (element order) into the 2 bf16 P
+// operands of its key planes (the forward's packing)
+__device__ __forceinline__ void pack_planes(const float (&v)[16], bf16x8 (&bp)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[e] = pk_bf16(v[8 * j + 2 * e], v[8 * j + 2 * e + 1]);
+    bp[j] = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int D, int BQ, int SUB>
+__global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const int* __restrict__ row_ptr,
+    const int* __restrict__ col_idx, uint16_t* __restrict__ dQ, float* __restrict__ lse2_out,
+    float* __restrict__ dd_out, int N, int Nq, int Nk, float scale_log2, float inv_sqrt_d) {
+  using T = Tiles<D>;
+  constexpr int NW = BQ / 32;
+  using LP = LoadPlan<D, NW>;
+  constexpr int STAGE = 2 * T::KT_BYTES;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const ReadPlan<D> rdp(lane);
+  const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
+  const long long bh = row / Nq;
+  const int qi = (int)(row % Nq);
+  const int base = row_ptr[row];
+  const int nunits = (row_ptr[row + 1] - base) * SUB;
+  const int q = qi * BQ + 32 * w + (lane & 31);
+  const bool qv = q < N;
+
+  bf16x8 qf[D / 16], df[D / 16];
+  load_q<D>(Q, bh, q, N, hi, qf);
+  load_q<D>(dO, bh, q, N, hi, df);
+  float dd = 0.f;  // D of this query (after pass A)
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  float lse2 = INFINITY;  // log2-sum-exp of the scaled scores; +inf: no key (P = 0)
+  if (nunits > 0) {
+    const auto rk = buf_rsrc(K + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    const auto rv = buf_rsrc(V + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    auto key0 = [&](int x) {
+      const int u = x % nunits;  // pass A units, then pass B units
+      return (col_idx[base + u / SUB] * SUB + u % SUB) * KU;
+    };
+    const int nsteps = 2 * nunits;
+    // pass A: running max (raw scores), sum of exp2 and sum of exp2 * dP
+    float m = -INFINITY, l = 0.f, dn = 0.f;
+    auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
+      const LP lp(w, opaque(lane));
+      const int k0 = key0(x);
+      lp.load(rk, k0, sb);
+      lp.load(rv, k0, sb + T::KT_BYTES);
+    };
+    auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+      const int kcur = key0(x);
+      wait_vm<0>();
+      __syncthreads();
+      if (x + 1 < nsteps) issue(x + 1, nxt);
+      const int lim = min(KU, N - kcur);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int limh = lim - 32 * kt - 4 * hi;  // element i: key 32 kt + 8 (i/4) + 4 hi + i%4
+        f32x16 s = kt == 0 ? score_half<D, 0, 2>(cur, qf, rdp) : score_half<D, 1, 2>(cur, qf, rdp);
+        if (lim < KU) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= limh) s[i] = -INFINITY;
+        }
+        const f32x16 dp = kt == 0 ? score_half<D, 0, 2>(cur + T::KT_BYTES, df, rdp)
+                                  : score_half<D, 1, 2>(cur + T::KT_BYTES, df, rdp);
+        if (x < nunits) {
+          // pass A: online max, sum and P-weighted sum of dP (this lane's keys)
+          float mx = s[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+          const float mn = fmaxf(m, mx);
+          if (mn != -INFINITY) {
+            float sl = 0.f, sd = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const float e = __builtin_amdgcn_exp2f((s[i] - mn) * scale_log2);
+              sl += e;
+              sd = fmaf(e, dp[i], sd);
+            }
+            const float c = __builtin_amdgcn_exp2f((m - mn) * scale_log2);
+            l = l * c + sl;
+            dn = dn * c + sd;
+            m = mn;
+          }
+        } else {
+          if (x == nunits && kt == 0) {
+            // the query's log2-sum-exp and D over both key halves (lanes l, l^32)
+            const float M = pair_max(m);
+            const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - M) * scale_log2);
+            const float L = l * c + __shfl_xor(l * c, 32);
+            const float Dn = dn * c + __shfl_xor(dn * c, 32);
+            lse2 = M * scale_log2 + __log2f(L);
+            dd = Dn / L;
+          }
+          float ds[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lse2));
+            ds[i] = p * (dp[i] - dd);
+          }
+          bf16x8 bp[2];
+          pack_planes(ds, bp);
+          // dQ^T += K^T dS^T over this half's two key planes
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(rdp.vt(cur, dt, 2 * kt + pl), bp[pl], acc[dt]);
+        }
+        // one 32-key half at a time: keeps the two halves' scores from being live together
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    issue(0, st0);
+    int x = 0;
+    for (; x + 2 <= nsteps; x += 2) {
+      step(x, st0, st1);
+      step(x + 1, st1, st0);
+    }
+    wait_vm<0>();  // nsteps is even
+  }
+  const size_t qrow = (size_t)bh * N + min(q, N - 1);
+  store_T<D / 32>(acc, inv_sqrt_d, dQ + qrow * D, 0, qv, hi);
+  if (hi == 0) {
+    const size_t r = (size_t)row * BQ + 32 * w + (lane & 31);
+    lse2_out[r] = qv ? lse2 : INFINITY;
+    dd_out[r] = qv ? dd : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int D, int BQ, int SUB>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const int* __restrict__ col_ptr, const int* __restrict__ row_idx,
+    const float* __restrict__ lse2, const float* __restrict__ ddv, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int N, int Nq, int Nk, float scale_log2, float inv_sqrt_d) {
+  using T = Tiles<D>;
+  using LP = LoadPlan<D, 4>;
+  constexpr int STAGE = 2 * T::KT_BYTES;  // Q and dO tiles of 64 queries
+  constexpr int NDT = D / 64;             // 32-row d tiles per wavefront (half of d)
+  constexpr int QU = BQ / KU;             // 64-query units per query block
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const int kh = w & 1, dh = w >> 1;  // key half (32 keys), d half of the accumulators
+  const ReadPlan<D> rdp(lane);
+  const long long unit = xcd_row(blockIdx.x, (long long)gridDim.x);  // (bh, key block, 64-key part)
+  const long long bh = unit / ((long long)Nk * SUB);
+  const int ku = (int)(unit % ((long long)Nk * SUB));
+  const int j = ku / SUB;
+  const int key = ku * KU + 32 * kh + (lane & 31);
+  const bool kv = key < N;
+  const long long col = bh * Nk + j;
+  const int cb = col_ptr[col];
+  const int nunits = (col_ptr[col + 1] - cb) * QU;
+
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_q<D>(K, bh, key, N, hi, kf);
+  load_q<D>(V, bh, key, N, hi, vf);
+  f32x16 adv[NDT], adk[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    adv[t] = f32x16{};
+    adk[t] = f32x16{};
+  }
+  if (nunits > 0) {
+    const auto rq = buf_rsrc(Q + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    const auto rg = buf_rsrc(dO + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    // first query of unit x, and its mask row (for the per-query terms)
+    auto qrow_of = [&](int x) { return row_idx[cb + x / QU]; };
+    auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
+      const LP lp(w, opaque(lane));
+      const int q0 = qrow_of(x) * BQ + (x % QU) * KU;
+      lp.load(rq, q0, sb);
+      lp.load(rg, q0, sb + T::KT_BYTES);
+    };
+    auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+      const int qb = qrow_of(x);
+      const size_t r0 = ((size_t)(bh * Nq + qb)) * BQ + (x % QU) * KU;  // per-query terms of the unit
+      wait_vm<0>();
+      __syncthreads();
+      if (x + 1 < nunits) issue(x + 1, nxt);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        // S and dP of 32 queries x this wavefront's 32 keys (element i: query
+        // 32 qt + 8 (i/4) + 4 hi + i%4 of the unit, key = this lane's)
+        const f32x16 s = qt == 0 ? score_half<D, 0, 4>(cur, kf, rdp) : score_half<D, 1, 4>(cur, kf, rdp);
+        const f32x16 dp = qt == 0 ? score_half<D, 0, 4>(cur + T::KT_BYTES, vf, rdp)
+                                  : score_half<D, 1, 4>(cur + T::KT_BYTES, vf, rdp);
+        float pv[16], ds[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const size_t ro = r0 + 32 * qt + 8 * a + 4 * hi;
+          const float4 L4 = *reinterpret_cast<const float4*>(lse2 + ro);
+          const float4 D4 = *reinterpret_cast<const float4*>(ddv + ro);
+          const float Lq[4] = {L4.x, L4.y, L4.z, L4.w}, Dq[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int i = 4 * a + c;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -Lq[c]));
+            pv[i] = p;
+            ds[i] = p * (dp[i] - Dq[c]);
+          }
+        }
+        bf16x8 bp[2], bs[2];
+        pack_planes(pv, bp);
+        pack_planes(ds, bs);
+        // dV^T += dO^T P and dK^T += Q^T dS over this half's two query planes,
+        // d rows of this wavefront's half
+#pragma unroll
+        for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) {
+            adv[t] = mfma(rdp.vt(cur + T::KT_BYTES, NDT * dh + t, 2 * qt + pl), bp[pl], adv[t]);
+            adk[t] = mfma(rdp.vt(cur, NDT * dh + t, 2 * qt + pl), bs[pl], adk[t]);
+          }
+      }
+    };
+    issue(0, st0);
+    int x = 0;
+    for (; x + 2 <= nunits; x += 2) {
+      step(x, st0, st1);
+      step(x + 1, st1, st0);
+    }
+    if (x < nunits) step(x, st0, st1);
+    wait_vm<0>();
+  }
+  const size_t krow = ((size_t)bh * N + min(key, N - 1)) * D;
+  store_T<NDT>(adv, 1.f, dV + krow, 32 * NDT * dh, kv, hi);
+  store_T<NDT>(adk, inv_sqrt_d, dK + krow, 32 * NDT * dh, kv, hi);
+}
+
+// ------------------------------------------------------------------ d alpha
+// Partial sums of dO . (O_s - O_l) over chunks of one (b, h) slice: each
+// workgroup sums ACH elements in float64 (fixed order: thread-strided, then a
+// tree), one partial per (bh, chunk).
+constexpr int ACH = 65536;
+template <int ES>
+__global__ __launch_bounds__(256) void alpha_part_kernel(const char* __restrict__ dO, const char* __restrict__ Os,
+                                                         const char* __restrict__ Ol, long long per, int nch,
+                                                         double* __restrict__ part) {
+  __shared__ double red[256];
+  const long long bh = blockIdx.y;
+  const long long a = (long long)blockIdx.x * ACH, b = min(per, a + ACH);
+  double acc = 0.0;
+  for (long long e = a + threadIdx.x; e < b; e += 256) {
+    const size_t o = (size_t)(bh * per + e);
+    float g, x, y;
+    if (ES == 2) {
+      g = bf2f(reinterpret_cast<const uint16_t*>(dO)[o]);
+      x = bf2f(reinterpret_cast<const uint16_t*>(Os)[o]);
+      y = bf2f(reinterpret_cast<const uint16_t*>(Ol)[o]);
+    } else {
+      g = reinterpret_cast<const float*>(dO)[o];
+      x = reinterpret_cast<const float*>(Os)[o];
+      y = reinterpret_cast<const float*>(Ol)[o];
+    }
+    acc += (double)g * ((double)x - (double)y);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[bh * nch + blockIdx.x] = red[0];
+}
+
+// dalpha[h] = sum over b and chunks, in order
+__global__ __launch_bounds__(64) void alpha_sum_kernel(const double* __restrict__ part, int B, int H, int nch,
+                                                       float* __restrict__ dalpha) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= H) return;
+  double s = 0.0;
+  for (int b = 0; b < B; ++b)
+    for (int c = 0; c < nch; ++c) s += part[((long long)b * H + h) * nch + c];
+  dalpha[h] = (float)s;
+}
+
+template <int D, int BQ, int SUB>
+hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV,
+                        char* ws, const BwdLayout& L, hipStream_t st) {
+  const long long BH = (long long)s.B * s.H;
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  const float isd = 1.f / sqrtf((float)D);
+  int* counts = reinterpret_cast<int*>(ws + L.counts);
+  int* col_ptr = reinterpret_cast<int*>(ws + L.col_ptr);
+  int* row_idx = reinterpret_cast<int*>(ws + L.row_idx);
+  float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  float* ddv = reinterpret_cast<float*>(ws + L.dd);
+  const unsigned ncol = (unsigned)((BH * s.Nk + 255) / 256);
+  hipLaunchKernelGGL(csc_count_kernel, dim3(ncol), dim3(256), 0, st, rp, ci, s.Nq, s.Nk, BH, counts);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, col_ptr);
+  hipLaunchKernelGGL(csc_fill_kernel, dim3(ncol), dim3(256), 0, st, rp, ci, s.Nq, s.Nk, BH, col_ptr, row_idx);
+  const uint16_t* q = static_cast<const uint16_t*>(Q);
+  const uint16_t* k = static_cast<const uint16_t*>(K);
+  const uint16_t* v = static_cast<const uint16_t*>(V);
+  const uint16_t* g = static_cast<const uint16_t*>(dO);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, q, k, v,
+                     g, rp, ci, static_cast<uint16_t*>(dQ), lse2, ddv, s.N,
+                     s.Nq, s.Nk, sl2, isd);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, q, k, v,
+                     g, col_ptr, row_idx, lse2, ddv, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
+                     s.N, s.Nq, s.Nk, sl2, isd);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdLayout bwd_layout(const Shape& s) {
+  BwdLayout L{};
+  const size_t BH = (size_t)s.B * s.H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  L.counts = take(BH * s.Nk * sizeof(int));
+  L.col_ptr = take((BH * s.Nk + 1) * sizeof(int));
+  L.row_idx = take(BH * (size_t)s.Nq * s.Nk * sizeof(int));
+  L.lse2 = take((size_t)s.R() * s.bq * sizeof(float));
+  L.dd = take((size_t)s.R() * s.bq * sizeof(float));
+  L.achunks = (int)(((long long)s.N * s.d + ACH - 1) / ACH);
+  L.apart = take(BH * L.achunks * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
+                             char* ws, const BwdLayout& L, hipStream_t st) {
+  const long long BH = (long long)s.B * s.H, per = (long long)s.N * s.d;
+  double* part = reinterpret_cast<double*>(ws + L.apart);
+  const dim3 grid((unsigned)L.achunks, (unsigned)BH);
+  const char* g = static_cast<const char*>(dO);
+  const char* x = static_cast<const char*>(Os);
+  const char* y = static_cast<const char*>(Ol);
+  if (s.dtype == SLA_BF16)
+    hipLaunchKernelGGL(alpha_part_kernel<2>, grid, dim3(256), 0, st, g, x, y, per, L.achunks, part);
+  else
+    hipLaunchKernelGGL(alpha_part_kernel<4>, grid, dim3(256), 0, st, g, x, y, per, L.achunks, part);
+  hipLaunchKernelGGL(alpha_sum_kernel, dim3((unsigned)((s.H + 63) / 64)), dim3(64), 0, st, part, s.B, s.H,
+                     L.achunks, dalpha);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV,
+                             char* ws, const BwdLayout& L, hipStream_t st) {
+#define SLA_BWD(DD, QQ, KK) \
+  if (s.d == DD && s.bq == QQ && s.bk == KK) return bwd_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, ws, L, st);
+  SLA_BWD(128, 128, 64)
+  SLA_BWD(128, 128, 128)
+  SLA_BWD(128, 64, 64)
+  SLA_BWD(128, 64, 128)
+  SLA_BWD(64, 128, 64)
+  SLA_BWD(64, 128, 128)
+  SLA_BWD(64, 64, 64)
+  SLA_BWD(64, 64, 128)
+#undef SLA_BWD
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sla

@@ -278,6 +278,38 @@ int sla_sparse_fwd_i8(const sla_problem* prob, const void* qbuf, size_t qbuf_byt
                                         static_cast<hipStream_t>(stream)));
 }
 
+size_t sla_bwd_workspace_bytes(const sla_problem* prob) {
+  Shape s;
+  if (check_problem(prob, &s) != SLA_OK) return 0;
+  return sla::bwd_layout(s).total;
+}
+
+int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_s,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
+                   void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !dO_s || !row_ptr || !col_idx || !dQ || !dK || !dV) return SLA_ERR_INVALID_ARG;
+  const sla::BwdLayout L = sla::bwd_layout(s);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_sparse_bwd(s, Q, K, V, dO_s, row_ptr, col_idx, dQ, dK, dV,
+                                           static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
+int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,
+                   void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (!dO || !O_s || !O_l || !dalpha) return SLA_ERR_INVALID_ARG;
+  const sla::BwdLayout L = sla::bwd_layout(s);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_alpha_grad(s, dO, O_s, O_l, dalpha, static_cast<char*>(ws), L,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 const char* sla_status_string(int status) {
   switch (status) {
     case SLA_OK: return "ok";

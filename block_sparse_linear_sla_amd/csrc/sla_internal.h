@@ -51,6 +51,20 @@ struct I8Layout {
 
 I8Layout i8_layout(const Shape& s);
 
+// Byte offsets of the sparse-branch backward workspace (256-byte aligned).
+struct BwdLayout {
+  size_t counts;   // int32 [B*H*Nk]: query blocks listing each key block
+  size_t col_ptr;  // int32 [B*H*Nk + 1]: the mask's transpose (CSC)
+  size_t row_idx;  // int32 [B*H*Nq*Nk]: query block indices, ascending per column
+  size_t lse2;     // float [R*bq]: log2-sum-exp of the scaled scores per query (+inf past N)
+  size_t dd;       // float [R*bq]: D = dO . O per query (0 past N)
+  size_t apart;    // double [B*H][achunks]: partial sums of the alpha gradient
+  size_t total;
+  int achunks;     // chunks of 65536 elements per (b, h) slice
+};
+
+BwdLayout bwd_layout(const Shape& s);
+
 // Mode of the attention kernels.
 enum Mode : int {
   MODE_SPARSE = 0,  // O = O_s over the CSR row
@@ -88,6 +102,12 @@ hipError_t launch_quant_i8(const Shape& s, const void* Q, const void* K, const v
                            const I8Layout& L, hipStream_t st);
 hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* row_ptr,
                           const int32_t* col_idx, void* O, hipStream_t st);
+
+// attn_bwd.hip: gradient of the sparse branch (bf16) with the mask fixed.
+hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
+                             void* dV, char* ws, const BwdLayout& L, hipStream_t st);
+hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
+                             char* ws, const BwdLayout& L, hipStream_t st);
 
 // attn_f32.hip: linear totals and attention for float32 inputs.
 hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,

@@ -214,6 +214,31 @@ int sla_quantize_i8(const sla_problem* prob, const void* Q, const void* K, const
 int sla_sparse_fwd_i8(const sla_problem* prob, const void* qbuf, size_t qbuf_bytes,
                       const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
 
+/* ---- Backward of the sparse branch, mask fixed (SLA2 write-up §一 for the
+ * branch, §四 for training the attention end to end with the selection fixed
+ * per step).  For L = sum(O_s * dO_s), with P the softmax over each row's
+ * listed keys and D_t = dO_s[t] . O_s[t] = sum_u P_tu dP_tu:
+ *   dV = P^T dO_s,  dP = dO_s V^T,  dS = P o (dP - D),  dQ = dS K / sqrt(d),
+ *   dK = dS^T Q / sqrt(d)   over the listed (query block, key block) pairs.
+ * D is formed from its second expression in float32 (the forward output is
+ * not needed).  bf16 only (SLA_ERR_UNSUPPORTED for fp32).  dO_s is the
+ * gradient reaching O_s (alpha_h dO for the mixed output).  Outputs dQ, dK,
+ * dV [B, H, N, d] bf16
+ * (every element written; rows of keys no row lists get 0).  Needs a
+ * workspace of sla_bwd_workspace_bytes (the mask's transpose, per-query
+ * terms).  Deterministic: no atomics. */
+size_t sla_bwd_workspace_bytes(const sla_problem* prob);
+int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_s, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
+                   void* dV, void* ws, size_t ws_bytes, void* stream);
+
+/* Gradient of sum(O * dO) with respect to alpha for O = alpha_h O_s +
+ * (1 - alpha_h) O_l (SLA2 write-up §二): dalpha[h] = sum over the head's
+ * tokens of dO . (O_s - O_l), float64 partial sums in a fixed order, written
+ * as float32 [H] (DEVICE).  dO, O_s, O_l in the problem dtype.  Needs the
+ * sla_bwd_workspace_bytes workspace. */
+int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,
+                   void* ws, size_t ws_bytes, void* stream);
+
 const char* sla_status_string(int status);
 
 #ifdef __cplusplus

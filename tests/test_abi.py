@@ -209,3 +209,24 @@ def test_i8_null_and_buffer_checks():
     assert L.sla_sparse_fwd_i8(ctypes.byref(p), None, n, FAKE, FAKE, FAKE, None) == WORKSPACE
     assert L.sla_sparse_fwd_i8(ctypes.byref(p), FAKE, n - 1, FAKE, FAKE, FAKE, None) == WORKSPACE
     assert L.sla_sparse_fwd_i8(None, FAKE, n, FAKE, FAKE, FAKE, None) == INVALID
+
+
+def test_bwd_checks():
+    L = S.lib()
+    p32 = prob()
+    p16 = prob(dtype=S.SLA_BF16)
+    n = L.sla_bwd_workspace_bytes(ctypes.byref(p16))
+    assert n > 0 and L.sla_bwd_workspace_bytes(None) == 0
+    args = [FAKE] * 9
+    assert L.sla_sparse_bwd(ctypes.byref(p32), *args, FAKE, n, None) == UNSUPPORTED
+    for i in range(9):
+        a = list(args)
+        a[i] = None
+        assert L.sla_sparse_bwd(ctypes.byref(p16), *a, FAKE, n, None) == INVALID, i
+    assert L.sla_sparse_bwd(ctypes.byref(p16), *args, None, n, None) == WORKSPACE
+    assert L.sla_sparse_bwd(ctypes.byref(p16), *args, FAKE, n - 1, None) == WORKSPACE
+    for i in range(4):
+        a = [FAKE] * 4
+        a[i] = None
+        assert L.sla_alpha_grad(ctypes.byref(p32), *a, FAKE, n, None) == INVALID, i
+    assert L.sla_alpha_grad(ctypes.byref(p16), FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == WORKSPACE
