@@ -261,6 +261,33 @@ def main():
                      "kernel": f"attn_i8_kernel<d={wl.d},bq={wl.bq},bk={wl.bk}>",
                      "vs_bf16_sparse": t_sp / t_i8, "with_quantize_vs_bf16_sparse": t_sp / (t_q + t_i8)}
 
+    # the sparse branch's backward (mask fixed) on this step's mask: the mask
+    # transpose, the dQ pass and the dK/dV pass.  Algorithmic work: the five
+    # matrix products of a softmax-attention gradient per executed pair
+    # (S, dP, dV, dQ, dK: 10 bq bk d), priced against the bf16 matrix peak
+    if wl.dtype == "bf16":
+        dO = torch.randn_like(q)
+        bws = S.bwd_workspace(S.problem(q, wl.bq, wl.bk), dev)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        S.sla_sparse_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(args.steps):
+            S.sla_sparse_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
+        e[1].record()
+        for _ in range(args.steps):
+            S.sla_alpha_grad(dO, out, grads[0], wl.bq, wl.bk, ws=bws)
+        e[2].record()
+        torch.cuda.synchronize()
+        t_b = e[0].elapsed_time(e[1]) / args.steps
+        bwd_flops = 10.0 * wl.bq * wl.bk * wl.d * nnz
+        res["bwd"] = {"sparse_bwd_ms": t_b, "alpha_grad_ms": e[1].elapsed_time(e[2]) / args.steps,
+                      "achieved": bwd_flops / (t_b * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": bwd_flops / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                      "kernels": "csc_count/scan/fill + bwd_dq_kernel + bwd_dkdv_kernel",
+                      "vs_sparse_fwd": t_b / t_sp}
+
     # SoftTop-k weights of every mask row (pool + logits + threshold solve),
     # the router-training form of the selection, at temperature 0.5
     msoft = torch.empty((wl.B, wl.H, wl.Nq, wl.Nk), dtype=torch.float32, device=dev)

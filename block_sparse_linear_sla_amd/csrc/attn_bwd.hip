@@ -14,10 +14,11 @@
 // dS of the row by the same amount).
 //
 // Kernels:
-//   csc_count_kernel / csc_scan_kernel / csc_fill_kernel  the mask's
-//       transpose: for each key block, the query blocks that list it, in
-//       ascending order (one thread per key block binary-searches every
-//       row: deterministic, no atomics);
+//   csc_bits_kernel / csc_count_kernel / csc_scan_kernel / csc_fill_kernel
+//       the mask's transpose: the rows as bitmasks (one thread per row),
+//       then for each key block the query blocks that list it, in ascending
+//       order (one thread per key block reads its bit of every row:
+//       deterministic, no atomics);
 //   bwd_dq_kernel    one workgroup per mask row (BQ/32 wavefronts, 32
 //       queries each, queries on the lane axis as in the forward).  Pass A
 //       walks the row's 64-key units with S^T = K Q^T and dP^T = V dO^T for
@@ -40,32 +41,32 @@ namespace sla {
 namespace {
 
 // ------------------------------------------------------------ mask transpose
-// first index in the sorted list a[0..n) that is >= x
-__device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1;
-    else hi = mid;
+// bits[r][w]: bit j%32 of word j/32 set when row r lists key block j (one
+// thread per row writes all of its row's words)
+__global__ __launch_bounds__(256) void csc_bits_kernel(const int* __restrict__ row_ptr,
+                                                       const int* __restrict__ col_idx, long long R, int words,
+                                                       uint32_t* __restrict__ bits) {
+  const long long r = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (r >= R) return;
+  uint32_t* row = bits + r * words;
+  for (int x = 0; x < words; ++x) row[x] = 0u;
+  for (int p = row_ptr[r]; p < row_ptr[r + 1]; ++p) {
+    const int j = col_idx[p];
+    row[j >> 5] |= 1u << (j & 31);
   }
-  return lo;
 }
 
 // counts[bh * Nk + j] = number of query blocks of head bh whose row lists j
-__global__ __launch_bounds__(256) void csc_count_kernel(const int* __restrict__ row_ptr,
-                                                        const int* __restrict__ col_idx, int Nq, int Nk,
-                                                        long long BH, int* __restrict__ counts) {
+// (one thread per key block; the 32 threads of a word read it together)
+__global__ __launch_bounds__(256) void csc_count_kernel(const uint32_t* __restrict__ bits, int Nq, int Nk,
+                                                        int words, long long BH, int* __restrict__ counts) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= BH * Nk) return;
   const long long bh = t / Nk;
   const int j = (int)(t % Nk);
+  const uint32_t* b = bits + bh * Nq * words + (j >> 5);
   int c = 0;
-  for (int i = 0; i < Nq; ++i) {
-    const long long r = bh * Nq + i;
-    const int b = row_ptr[r], n = row_ptr[r + 1] - b;
-    const int p = lower_bound(col_idx + b, n, j);
-    c += (p < n && col_idx[b + p] == j) ? 1 : 0;
-  }
+  for (int i = 0; i < Nq; ++i) c += (b[(size_t)i * words] >> (j & 31)) & 1u;
   counts[t] = c;
 }
 
@@ -95,21 +96,17 @@ __global__ __launch_bounds__(1024) void csc_scan_kernel(const int* __restrict__ 
 }
 
 // row_idx[col_ptr[bh * Nk + j] ...] = the query blocks listing j, ascending
-__global__ __launch_bounds__(256) void csc_fill_kernel(const int* __restrict__ row_ptr,
-                                                       const int* __restrict__ col_idx, int Nq, int Nk,
-                                                       long long BH, const int* __restrict__ col_ptr,
+__global__ __launch_bounds__(256) void csc_fill_kernel(const uint32_t* __restrict__ bits, int Nq, int Nk,
+                                                       int words, long long BH, const int* __restrict__ col_ptr,
                                                        int* __restrict__ row_idx) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
   if (t >= BH * Nk) return;
   const long long bh = t / Nk;
   const int j = (int)(t % Nk);
+  const uint32_t* b = bits + bh * Nq * words + (j >> 5);
   int o = col_ptr[t];
-  for (int i = 0; i < Nq; ++i) {
-    const long long r = bh * Nq + i;
-    const int b = row_ptr[r], n = row_ptr[r + 1] - b;
-    const int p = lower_bound(col_idx + b, n, j);
-    if (p < n && col_idx[b + p] == j) row_idx[o++] = i;
-  }
+  for (int i = 0; i < Nq; ++i)
+    if ((b[(size_t)i * words] >> (j & 31)) & 1u) row_idx[o++] = i;
 }
 
 // ------------------------------------------------------------------ helpers
@@ -399,23 +396,27 @@ template <int ES>
 __global__ __launch_bounds__(256) void alpha_part_kernel(const char* __restrict__ dO, const char* __restrict__ Os,
                                                          const char* __restrict__ Ol, long long per, int nch,
                                                          double* __restrict__ part) {
+  constexpr int VE = 16 / ES;  // elements per 16-byte load (per is a multiple: d is 64 or 128)
   __shared__ double red[256];
   const long long bh = blockIdx.y;
   const long long a = (long long)blockIdx.x * ACH, b = min(per, a + ACH);
   double acc = 0.0;
-  for (long long e = a + threadIdx.x; e < b; e += 256) {
-    const size_t o = (size_t)(bh * per + e);
-    float g, x, y;
+  for (long long e = a + (long long)threadIdx.x * VE; e < b; e += 256 * VE) {
+    const size_t o = (size_t)(bh * per + e) * ES;
+    const uint4 g4 = *reinterpret_cast<const uint4*>(dO + o);
+    const uint4 x4 = *reinterpret_cast<const uint4*>(Os + o);
+    const uint4 y4 = *reinterpret_cast<const uint4*>(Ol + o);
     if (ES == 2) {
-      g = bf2f(reinterpret_cast<const uint16_t*>(dO)[o]);
-      x = bf2f(reinterpret_cast<const uint16_t*>(Os)[o]);
-      y = bf2f(reinterpret_cast<const uint16_t*>(Ol)[o]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        acc += (double)bf2f(elem(g4, k)) * ((double)bf2f(elem(x4, k)) - (double)bf2f(elem(y4, k)));
     } else {
-      g = reinterpret_cast<const float*>(dO)[o];
-      x = reinterpret_cast<const float*>(Os)[o];
-      y = reinterpret_cast<const float*>(Ol)[o];
+      const float g[4] = {__uint_as_float(g4.x), __uint_as_float(g4.y), __uint_as_float(g4.z), __uint_as_float(g4.w)};
+      const float x[4] = {__uint_as_float(x4.x), __uint_as_float(x4.y), __uint_as_float(x4.z), __uint_as_float(x4.w)};
+      const float y[4] = {__uint_as_float(y4.x), __uint_as_float(y4.y), __uint_as_float(y4.z), __uint_as_float(y4.w)};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += (double)g[k] * ((double)x[k] - (double)y[k]);
     }
-    acc += (double)g * ((double)x - (double)y);
   }
   red[threadIdx.x] = acc;
   __syncthreads();
@@ -448,10 +449,15 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   int* row_idx = reinterpret_cast<int*>(ws + L.row_idx);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* ddv = reinterpret_cast<float*>(ws + L.dd);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+  const int words = s.words();
   const unsigned ncol = (unsigned)((BH * s.Nk + 255) / 256);
-  hipLaunchKernelGGL(csc_count_kernel, dim3(ncol), dim3(256), 0, st, rp, ci, s.Nq, s.Nk, BH, counts);
+  hipLaunchKernelGGL(csc_bits_kernel, dim3((unsigned)((s.R() + 255) / 256)), dim3(256), 0, st, rp, ci, s.R(), words,
+                     bits);
+  hipLaunchKernelGGL(csc_count_kernel, dim3(ncol), dim3(256), 0, st, bits, s.Nq, s.Nk, words, BH, counts);
   hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, col_ptr);
-  hipLaunchKernelGGL(csc_fill_kernel, dim3(ncol), dim3(256), 0, st, rp, ci, s.Nq, s.Nk, BH, col_ptr, row_idx);
+  hipLaunchKernelGGL(csc_fill_kernel, dim3(ncol), dim3(256), 0, st, bits, s.Nq, s.Nk, words, BH, col_ptr,
+                     row_idx);
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
   const uint16_t* v = static_cast<const uint16_t*>(V);
@@ -476,6 +482,7 @@ BwdLayout bwd_layout(const Shape& s) {
     off = (off + bytes + 255) & ~(size_t)255;
     return o;
   };
+  L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
   L.counts = take(BH * s.Nk * sizeof(int));
   L.col_ptr = take((BH * s.Nk + 1) * sizeof(int));
   L.row_idx = take(BH * (size_t)s.Nq * s.Nk * sizeof(int));

@@ -53,6 +53,7 @@ I8Layout i8_layout(const Shape& s);
 
 // Byte offsets of the sparse-branch backward workspace (256-byte aligned).
 struct BwdLayout {
+  size_t bits;     // uint32 [R * words]: the mask's rows as bitmasks
   size_t counts;   // int32 [B*H*Nk]: query blocks listing each key block
   size_t col_ptr;  // int32 [B*H*Nk + 1]: the mask's transpose (CSC)
   size_t row_idx;  // int32 [B*H*Nq*Nk]: query block indices, ascending per column
