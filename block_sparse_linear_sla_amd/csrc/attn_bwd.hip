@@ -17,8 +17,9 @@
 //   csc_bits_kernel / csc_count_kernel / csc_scan_kernel / csc_fill_kernel
 //       the mask's transpose: the rows as bitmasks (one thread per row),
 //       then for each key block the query blocks that list it, in ascending
-//       order (one thread per key block reads its bit of every row:
-//       deterministic, no atomics);
+//       order (one thread per key block and 64-row chunk reads its bit of
+//       each row; column totals are scanned, and a chunk's rows go after
+//       those of the column's earlier chunks: deterministic, no atomics);
 //   bwd_dq_kernel    one workgroup per mask row (BQ/32 wavefronts, 32
 //       queries each, queries on the lane axis as in the forward).  Pass A
 //       walks the row's 64-key units with S^T = K Q^T and dP^T = V dO^T for
@@ -56,56 +57,79 @@ __global__ __launch_bounds__(256) void csc_bits_kernel(const int* __restrict__ r
   }
 }
 
-// counts[bh * Nk + j] = number of query blocks of head bh whose row lists j
-// (one thread per key block; the 32 threads of a word read it together)
+// The transpose works on (column, chunk) cells: column c = bh * Nk + j, chunk
+// k = rows [64 k, 64 k + 64) of the head.  counts[c * nch + k] = rows of the
+// chunk that list j (one thread per cell; the 32 threads of a bitmask word
+// read it together).
+constexpr int CROWS = 64;
 __global__ __launch_bounds__(256) void csc_count_kernel(const uint32_t* __restrict__ bits, int Nq, int Nk,
-                                                        int words, long long BH, int* __restrict__ counts) {
+                                                        int words, int nch, long long BH,
+                                                        int* __restrict__ counts) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= BH * Nk) return;
-  const long long bh = t / Nk;
-  const int j = (int)(t % Nk);
+  if (t >= BH * Nk * nch) return;
+  const int k = (int)(t % nch);
+  const long long c = t / nch;
+  const long long bh = c / Nk;
+  const int j = (int)(c % Nk);
   const uint32_t* b = bits + bh * Nq * words + (j >> 5);
-  int c = 0;
-  for (int i = 0; i < Nq; ++i) c += (b[(size_t)i * words] >> (j & 31)) & 1u;
-  counts[t] = c;
+  int n = 0;
+  const int i1 = min(Nq, (k + 1) * CROWS);
+  for (int i = k * CROWS; i < i1; ++i) n += (b[(size_t)i * words] >> (j & 31)) & 1u;
+  counts[t] = n;
 }
 
-// col_ptr = exclusive prefix sum of counts (n entries, one workgroup)
-__global__ __launch_bounds__(1024) void csc_scan_kernel(const int* __restrict__ counts, long long n,
+// col_ptr = exclusive prefix sum of the column totals (each the sum of the
+// column's nch cell counts; n columns, one workgroup): 1024 consecutive
+// columns per pass, a shuffle scan within each wavefront, then one across the
+// 16 wavefronts, plus the carry of the earlier passes
+__global__ __launch_bounds__(1024) void csc_scan_kernel(const int* __restrict__ counts, long long n, int nch,
                                                         int* __restrict__ col_ptr) {
-  __shared__ int part[1024];
-  const int t = threadIdx.x;
-  const long long per = (n + 1023) / 1024;
-  const long long a = t * per, b = min(n, a + per);
-  int s = 0;
-  for (long long x = a; x < b; ++x) s += counts[x];
-  part[t] = s;
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  if (t == 0) carry = 0;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = t >= off ? part[t - off] : 0;
+  for (long long base = 0; base < n; base += 1024) {
+    const long long x = base + t;
+    int v = 0;
+    if (x < n)
+      for (int k = 0; k < nch; ++k) v += counts[x * nch + k];
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wv] = incl;
     __syncthreads();
-    part[t] += v;
+    int wpre = 0;
+    for (int u = 0; u < wv; ++u) wpre += wsum[u];
+    const int c0 = carry;
+    if (x < n) col_ptr[x] = c0 + wpre + incl - v;
+    __syncthreads();  // every thread has read wsum and carry
+    if (t == 1023) carry = c0 + wpre + incl;
     __syncthreads();
   }
-  int run = t ? part[t - 1] : 0;
-  for (long long x = a; x < b; ++x) {
-    col_ptr[x] = run;
-    run += counts[x];
-  }
-  if (t == 1023) col_ptr[n] = part[1023];
+  if (t == 0) col_ptr[n] = carry;
 }
 
-// row_idx[col_ptr[bh * Nk + j] ...] = the query blocks listing j, ascending
+// row_idx[...] = the rows of cell (c, k) that list j, ascending, starting
+// after the column's earlier cells
 __global__ __launch_bounds__(256) void csc_fill_kernel(const uint32_t* __restrict__ bits, int Nq, int Nk,
-                                                       int words, long long BH, const int* __restrict__ col_ptr,
-                                                       int* __restrict__ row_idx) {
+                                                       int words, int nch, long long BH,
+                                                       const int* __restrict__ counts,
+                                                       const int* __restrict__ col_ptr, int* __restrict__ row_idx) {
   const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= BH * Nk) return;
-  const long long bh = t / Nk;
-  const int j = (int)(t % Nk);
+  if (t >= BH * Nk * nch) return;
+  const int k = (int)(t % nch);
+  const long long c = t / nch;
+  const long long bh = c / Nk;
+  const int j = (int)(c % Nk);
+  int o = col_ptr[c];
+  for (int k2 = 0; k2 < k; ++k2) o += counts[c * nch + k2];
   const uint32_t* b = bits + bh * Nq * words + (j >> 5);
-  int o = col_ptr[t];
-  for (int i = 0; i < Nq; ++i)
+  const int i1 = min(Nq, (k + 1) * CROWS);
+  for (int i = k * CROWS; i < i1; ++i)
     if ((b[(size_t)i * words] >> (j & 31)) & 1u) row_idx[o++] = i;
 }
 
@@ -451,13 +475,15 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   float* ddv = reinterpret_cast<float*>(ws + L.dd);
   uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
   const int words = s.words();
-  const unsigned ncol = (unsigned)((BH * s.Nk + 255) / 256);
+  const int nch = (s.Nq + CROWS - 1) / CROWS;
+  const long long ncell = BH * s.Nk * nch;
+  const unsigned gcell = (unsigned)((ncell + 255) / 256);
   hipLaunchKernelGGL(csc_bits_kernel, dim3((unsigned)((s.R() + 255) / 256)), dim3(256), 0, st, rp, ci, s.R(), words,
                      bits);
-  hipLaunchKernelGGL(csc_count_kernel, dim3(ncol), dim3(256), 0, st, bits, s.Nq, s.Nk, words, BH, counts);
-  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, col_ptr);
-  hipLaunchKernelGGL(csc_fill_kernel, dim3(ncol), dim3(256), 0, st, bits, s.Nq, s.Nk, words, BH, col_ptr,
-                     row_idx);
+  hipLaunchKernelGGL(csc_count_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, nch, col_ptr);
+  hipLaunchKernelGGL(csc_fill_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts,
+                     col_ptr, row_idx);
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
   const uint16_t* v = static_cast<const uint16_t*>(V);
@@ -483,7 +509,8 @@ BwdLayout bwd_layout(const Shape& s) {
     return o;
   };
   L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
-  L.counts = take(BH * s.Nk * sizeof(int));
+  const size_t ncell = BH * s.Nk * (size_t)((s.Nq + CROWS - 1) / CROWS);
+  L.counts = take(ncell * sizeof(int));
   L.col_ptr = take((BH * s.Nk + 1) * sizeof(int));
   L.row_idx = take(BH * (size_t)s.Nq * s.Nk * sizeof(int));
   L.lse2 = take((size_t)s.R() * s.bq * sizeof(float));

@@ -17,7 +17,7 @@
 // Kernels:
 //   quant_block_kernel  Q or K: one workgroup per block of rows, absolute
 //                       maximum, then codes (row-major [rows padded][d]);
-//   vamax_kernel        V: per-channel maxima of 256-row chunks;
+//   vamax_kernel        V: per-channel maxima of 1024-row chunks;
 //   vscale_kernel       V: per-channel scale and reciprocal from the chunks;
 //   quant_v_kernel      V: codes as V^T in 64-key tiles [d][64], keys of
 //                       every 32-key group in the order the P operand holds
@@ -56,7 +56,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int QROWS = 256;  // rows per chunk of the V channel maxima
+constexpr int QROWS = 1024;  // rows per chunk of the V channel maxima
 
 template <int I>
 struct IntTag {

@@ -44,7 +44,7 @@ struct I8Layout {
   size_t sk;     // float [B*H][Nk]
   size_t sv;     // float [B*H][d]
   size_t rv;     // float [B*H][d]: 127 / amax of each V channel (0 for amax 0)
-  size_t vpart;  // float [B*H][vchunks][d]: channel maxima of 256-row chunks
+  size_t vpart;  // float [B*H][vchunks][d]: channel maxima of 1024-row chunks
   size_t total;
   int vchunks;
 };
@@ -54,7 +54,7 @@ I8Layout i8_layout(const Shape& s);
 // Byte offsets of the sparse-branch backward workspace (256-byte aligned).
 struct BwdLayout {
   size_t bits;     // uint32 [R * words]: the mask's rows as bitmasks
-  size_t counts;   // int32 [B*H*Nk]: query blocks listing each key block
+  size_t counts;   // int32 [B*H*Nk*ceil(Nq/64)]: rows listing each key block, per 64-row chunk
   size_t col_ptr;  // int32 [B*H*Nk + 1]: the mask's transpose (CSC)
   size_t row_idx;  // int32 [B*H*Nq*Nk]: query block indices, ascending per column
   size_t lse2;     // float [R*bq]: log2-sum-exp of the scaled scores per query (+inf past N)

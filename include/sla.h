@@ -194,7 +194,7 @@ int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const v
  *                of its channel's 64-byte row (keys >= N zero)
  *   sq     float [B*H][Nq],  sk float [B*H][Nk],  sv float [B*H][d]
  *   rv     float [B*H][d]    127 / amax per V channel (0 for amax 0)
- *   vpart  float [B*H][ceil(N/256)][d]   channel maxima of 256-row chunks
+ *   vpart  float [B*H][ceil(N/1024)][d]   channel maxima of 1024-row chunks
  * at the byte offsets sla_i8_layout_of returns (each 256-byte aligned).
  * Supported as for the other calls, and N <= 131072 (the int32 sums then
  * cannot overflow).  Inputs must be finite. */

@@ -179,7 +179,7 @@ def test_i8_layout_and_limits():
     BH, Nq, Nk = 2, 8, 16
     sizes = [("q8", BH * Nq * 128 * 128), ("k8", BH * Nk * 64 * 128), ("vt8", BH * Nk * 64 * 128),
              ("sq", BH * Nq * 4), ("sk", BH * Nk * 4), ("sv", BH * 128 * 4), ("rv", BH * 128 * 4),
-             ("vpart", BH * 4 * 128 * 4)]
+             ("vpart", BH * 1 * 128 * 4)]
     off = 0
     for name, n in sizes:  # regions in order, each 256-byte aligned, no overlap
         assert getattr(lay, name) == off, name
