@@ -31,9 +31,12 @@
 //   bwd_dkdv_kernel  one workgroup per 64-key unit, walking the query blocks
 //       that list its key block in 64-query units.  Wavefront w keeps the
 //       K and V rows of 32 keys (half w%2) in registers and the dK^T, dV^T
-//       tiles of half w/2 of d: S = Q K^T and dP = dO V^T (queries x keys,
-//       keys on the lane axis), P and dS in registers, then
-//       dV^T += dO^T P and dK^T += Q^T dS with Q and dO read transposed.
+//       tiles of half w/2 of d.  Per unit it forms S = Q K^T and dP = dO V^T
+//       (queries x keys, keys on the lane axis) for half w/2 of the queries,
+//       P and dS in registers, swaps those operands with the wavefront that
+//       shares its keys (through LDS), then accumulates dV^T += dO^T P and
+//       dK^T += Q^T dS over all of the unit's queries with Q and dO read
+//       transposed.
 #include "sla.h"
 #include "sla_internal.h"
 #include "bf16_tiles.h"
@@ -317,13 +320,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   constexpr int STAGE = 2 * T::KT_BYTES;  // Q and dO tiles of 64 queries
   constexpr int NDT = D / 64;             // 32-row d tiles per wavefront (half of d)
   constexpr int QU = BQ / KU;             // 64-query units per query block
+  constexpr int XCH = 4 * 64 * 16;        // one wavefront's P and dS operands (2 planes each)
+  static_assert(2 * (2 * STAGE + 4 * XCH) <= LDS_BYTES, "two workgroups per compute unit");
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint4 xch[4][4][64];  // [wavefront][operand][lane]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hi = lane >> 5;
-  const int kh = w & 1, dh = w >> 1;  // key half (32 keys), d half of the accumulators
+  // key half kh (32 keys); wavefront pair (kh, 0), (kh, 1) share those keys:
+  // each scores half dh of every unit's queries and accumulates half dh of d
+  const int kh = w & 1, dh = w >> 1;
+  const int partner = w ^ 2;
   const ReadPlan<D> rdp(lane);
   const long long unit = xcd_row(blockIdx.x, (long long)gridDim.x);  // (bh, key block, 64-key part)
   const long long bh = unit / ((long long)Nk * SUB);
@@ -355,47 +364,73 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
       lp.load(rq, q0, sb);
       lp.load(rg, q0, sb + T::KT_BYTES);
     };
+    // S and dP of this wavefront's 32 queries (half QH of the unit) x its 32
+    // keys (element i: query 32 QH + 8 (i/4) + 4 hi + i%4, key = this
+    // lane's); P and dS packed as the B operands of query planes 2 QH, 2 QH + 1
+    auto score = [&](const char* cur, size_t r0, bf16x8 (&bp)[2], bf16x8 (&bs)[2], auto qh_tag)
+        __attribute__((always_inline)) {
+      constexpr int QH = decltype(qh_tag)::value;
+      const f32x16 s = score_half<D, QH, 4>(cur, kf, rdp);
+      const f32x16 dp = score_half<D, QH, 4>(cur + T::KT_BYTES, vf, rdp);
+      float pv[16], ds[16];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const size_t ro = r0 + 32 * QH + 8 * a + 4 * hi;
+        const float4 L4 = *reinterpret_cast<const float4*>(lse2 + ro);
+        const float4 D4 = *reinterpret_cast<const float4*>(ddv + ro);
+        const float Lq[4] = {L4.x, L4.y, L4.z, L4.w}, Dq[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 4 * a + c;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -Lq[c]));
+          pv[i] = p;
+          ds[i] = p * (dp[i] - Dq[c]);
+        }
+      }
+      pack_planes(pv, bp);
+      pack_planes(ds, bs);
+    };
     auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
       const int qb = qrow_of(x);
       const size_t r0 = ((size_t)(bh * Nq + qb)) * BQ + (x % QU) * KU;  // per-query terms of the unit
       wait_vm<0>();
-      __syncthreads();
+      __syncthreads();  // the unit's tiles landed; the previous unit's exchange consumed
       if (x + 1 < nunits) issue(x + 1, nxt);
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        // S and dP of 32 queries x this wavefront's 32 keys (element i: query
-        // 32 qt + 8 (i/4) + 4 hi + i%4 of the unit, key = this lane's)
-        const f32x16 s = qt == 0 ? score_half<D, 0, 4>(cur, kf, rdp) : score_half<D, 1, 4>(cur, kf, rdp);
-        const f32x16 dp = qt == 0 ? score_half<D, 0, 4>(cur + T::KT_BYTES, vf, rdp)
-                                  : score_half<D, 1, 4>(cur + T::KT_BYTES, vf, rdp);
-        float pv[16], ds[16];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const size_t ro = r0 + 32 * qt + 8 * a + 4 * hi;
-          const float4 L4 = *reinterpret_cast<const float4*>(lse2 + ro);
-          const float4 D4 = *reinterpret_cast<const float4*>(ddv + ro);
-          const float Lq[4] = {L4.x, L4.y, L4.z, L4.w}, Dq[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int i = 4 * a + c;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -Lq[c]));
-            pv[i] = p;
-            ds[i] = p * (dp[i] - Dq[c]);
-          }
-        }
+      // all operand indices below are compile-time (a runtime index would put
+      // the operand array in scratch memory)
+      auto body = [&](auto qh_tag) __attribute__((always_inline)) {
+        constexpr int QH = decltype(qh_tag)::value;
+        constexpr int OWN = 2 * QH, OTH = 2 - OWN;
+        bf16x8 op[2][4];  // [P, dS][query plane 0..3]
         bf16x8 bp[2], bs[2];
-        pack_planes(pv, bp);
-        pack_planes(ds, bs);
-        // dV^T += dO^T P and dK^T += Q^T dS over this half's two query planes,
-        // d rows of this wavefront's half
+        score(cur, r0, bp, bs, qh_tag);
+        op[0][OWN] = bp[0];
+        op[0][OWN + 1] = bp[1];
+        op[1][OWN] = bs[0];
+        op[1][OWN + 1] = bs[1];
+        // hand this half's operands to the partner, take the partner's half
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl) xch[w][2 * o + pl][lane] = __builtin_bit_cast(uint4, op[o][OWN + pl]);
+        __syncthreads();
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+            op[o][OTH + pl] = __builtin_bit_cast(bf16x8, xch[partner][2 * o + pl][lane]);
+        // dV^T += dO^T P and dK^T += Q^T dS over the unit's four query
+        // planes, d rows of this wavefront's half
+#pragma unroll
+        for (int pl = 0; pl < 4; ++pl)
 #pragma unroll
           for (int t = 0; t < NDT; ++t) {
-            adv[t] = mfma(rdp.vt(cur + T::KT_BYTES, NDT * dh + t, 2 * qt + pl), bp[pl], adv[t]);
-            adk[t] = mfma(rdp.vt(cur, NDT * dh + t, 2 * qt + pl), bs[pl], adk[t]);
+            adv[t] = mfma(rdp.vt(cur + T::KT_BYTES, NDT * QH + t, pl), op[0][pl], adv[t]);
+            adk[t] = mfma(rdp.vt(cur, NDT * QH + t, pl), op[1][pl], adk[t]);
           }
-      }
+      };
+      if (dh == 0) body(IntTag<0>{});
+      else body(IntTag<1>{});
     };
     issue(0, st0);
     int x = 0;
