@@ -595,7 +595,59 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
 // tau by a safeguarded Newton iteration on f(tau) = sum_j sigmoid((S_j -
 // tau)/T) - k, decreasing in tau with f'(tau) = -sum_j M_j (1 - M_j) / T,
 // inside a bisection bracket that starts where every weight is ~1 (f > 0)
-// and ~0 (f < 0).  float64 throughout; the weights are written as float32.
+// and ~0 (f < 0).  The iteration first runs in float32 (hardware
+// exponential) to a starting point; plain float64 Newton steps from there
+// converge quadratically (the safeguarded float64 iteration takes over if
+// they do not settle), and the weights are written as float32.
+// Wavefront sums through DPP butterflies (quad_perm [1,0,3,2] and [2,3,0,1],
+// row_half_mirror, row_mirror) and the 16- and 32-lane permlane swaps, as in
+// wave_max_u64: every step adds a lane's value to its partner's, and the
+// partner adds the same two numbers, so all 64 lanes end with bit-identical
+// sums (the iteration below branches on them) at a few cycles per step.
+template <int CTRL>
+__device__ __forceinline__ float add_f32_dpp(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = add_f32_dpp<0xB1>(v);
+  v = add_f32_dpp<0x4E>(v);
+  v = add_f32_dpp<0x141>(v);
+  v = add_f32_dpp<0x140>(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ double add_f64_dpp(double v) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return v + __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double f64_of(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = add_f64_dpp<0xB1>(v);
+  v = add_f64_dpp<0x4E>(v);
+  v = add_f64_dpp<0x141>(v);
+  v = add_f64_dpp<0x140>(v);
+  {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = f64_of(a[0], b[0]) + f64_of(a[1], b[1]);
+  }
+  {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    v = f64_of(a[0], b[0]) + f64_of(a[1], b[1]);
+  }
+  return v;
+}
+
 __device__ __forceinline__ double sigmoid_f64(double x) {
   const double e = exp(-fabs(x));
   return x >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
@@ -633,7 +685,70 @@ __global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict
   double lo = lo_s - 80.0 * T, hi = hi_s + 80.0 * T;  // f(lo) > 0 > f(hi)
   double tau = 0.5 * (lo + hi);
   const double inv_t = 1.0 / T;
-  for (int it = 0; it < 200; ++it) {  // uniform: every lane sees the same sums
+  {
+    // float32 phase: sigmoid(x) = 1 / (1 + 2^(-x log2 e)); stops once the
+    // bracket or the step is at float32 resolution
+    float l32 = (float)lo, h32 = (float)hi, t32 = (float)tau;
+    const float it32 = (float)inv_t;
+    for (int it = 0; it < 96; ++it) {
+      float f = 0.f, g = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (lane + 64 * e < Nk) {
+          const float x = ((float)sv[e] - t32) * it32;
+          const float m = 1.f / (1.f + __builtin_amdgcn_exp2f(-1.44269504f * x));
+          f += m;
+          g += m * (1.f - m);
+        }
+      }
+      f = wave_sum_f32(f) - (float)k;
+      g = wave_sum_f32(g) * it32;
+      if (f == 0.f) break;
+      if (f > 0.f) l32 = t32; else h32 = t32;
+      const float nt = g > 0.f ? t32 + f / g : 0.5f * (l32 + h32);
+      const float next = (nt > l32 && nt < h32) ? nt : 0.5f * (l32 + h32);
+      const bool done = next == t32 || h32 - l32 <= 1e-6f * fmaxf(fabsf(l32), fabsf(h32));
+      t32 = next;
+      if (done) break;
+    }
+    if ((double)t32 > lo && (double)t32 < hi) tau = (double)t32;
+  }
+  // float64 Newton from the float32 root (quadratic convergence: a few
+  // steps); if it has not settled after 10, the safeguarded iteration below
+  // starts again from the whole bracket
+  bool done = false;
+  {
+    double t = tau;
+    for (int it = 0; it < 10; ++it) {
+      double f = 0.0, g = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (lane + 64 * e < Nk) {
+          const double m = sigmoid_f64((sv[e] - t) * inv_t);
+          f += m;
+          g += m * (1.0 - m);
+        }
+      }
+      f = wave_sum_f64(f) - (double)k;
+      g = wave_sum_f64(g) * inv_t;
+      if (f == 0.0) {
+        done = true;
+        break;
+      }
+      if (!(g > 0.0)) break;
+      const double next = t + f / g;
+      if (!(next > lo && next < hi)) break;
+      const bool tiny = fabs(next - t) <= 4.0 * DBL_EPSILON * fmax(fabs(t), T);
+      t = next;
+      if (tiny) {
+        done = true;
+        break;
+      }
+    }
+    if (done) tau = t;
+    else tau = 0.5 * (lo + hi);
+  }
+  for (int it = 0; it < 200 && !done; ++it) {  // uniform: every lane sees the same sums
     double f = 0.0, g = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
@@ -643,8 +758,8 @@ __global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict
         g += m * (1.0 - m);
       }
     }
-    f = wave_sum(f) - (double)k;
-    g = wave_sum(g) * inv_t;
+    f = wave_sum_f64(f) - (double)k;
+    g = wave_sum_f64(g) * inv_t;
     if (f == 0.0) break;
     if (f > 0.0) lo = tau; else hi = tau;
     const double nt = g > 0.0 ? tau + f / g : 0.5 * (lo + hi);
