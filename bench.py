@@ -112,8 +112,8 @@ def cpu_baseline(x, rows_budget_s: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards over (batch, head) with no communication; see DESIGN.md)",
+        print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards over (batch, head) with no communication between GPUs)",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np

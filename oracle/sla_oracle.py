@@ -20,7 +20,7 @@ Sources (cited by short key):
 * [FM]  - the feature map phi(x) = elu(x) + 1 of Katharopoulos et al. 2020,
   "Transformers are RNNs", used for the linear branch.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
 
 * pooled scores use the attention scale 1/sqrt(d); P is a row softmax;
 * k = ceil(k_frac * Nk - 1e-9) from float32 k_frac widened to float64;
@@ -162,7 +162,7 @@ def mask(Q, K, bq: int, bk: int, k_frac: float, p: float, Wq=None, Wk=None,
     Q, K: [B, H, N, d].  Rows are ordered (b, h, i); column indices ascending.
     Returns (row_ptr int64 [R+1], col_idx int64 [nnz], info) where info holds,
     per row, the logits S, the probabilities P, the order, the cumulative sums
-    and the counts (used to judge blocks that sit on the selection cut).
+    and the counts (used to excuse blocks that sit on the selection cut).
     [SA2 §四: pool -> hybrid select on the pooled map -> block-level mask
     marking each block important or negligible.]
     """
@@ -386,7 +386,7 @@ def assemble(blocks: Dict, B: int, H: int, N: int, d: int, bq: int) -> np.ndarra
 # and value matrices held as 8-bit integers; values are scaled into the 8-bit
 # range, the products are formed there, and the results are scaled back.  The
 # pages fix neither the scale granularity nor the rounding; the readings taken
-# here (listed in the design doc) are:
+# here are:
 #
 # * symmetric codes in [-127, 127], code = round-half-even(x * (127 / amax)),
 #   the reciprocal and the product each rounded to float32, scale = amax / 127
