@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsla.so")
-SOURCES = ["sla_api.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip", "attn_i8.hip", "attn_bwd.hip"]
+SOURCES = ["sla_api.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip", "attn_i8.hip", "attn_bwd.hip", "attn_bwd_lin.hip"]
 # per-source extra flags: the attention kernels keep their matrix accumulators
 # in ordinary VGPRs (their softmax reads them every step), so the compiler is
 # told to use the VGPR form of the MFMA instructions there.  The 8-bit file
@@ -25,6 +25,7 @@ SOURCES = ["sla_api.hip", "mask.hip", "attn_bf16.hip", "attn_f32.hip", "attn_i8.
 # written, so it is built without floating-point contraction.
 EXTRA = {"attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "attn_bwd_lin.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
          "attn_i8.hip": ["-ffp-contract=off", "-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = os.environ.get("SLA_OFFLOAD_ARCH", "gfx950")
 

@@ -164,18 +164,6 @@ __device__ __forceinline__ void store_T(const f32x16 (&acc)[NT], float scale, ui
   }
 }
 
-// 16 fp32 values of a 32-key S^T half (element order) into the 2 bf16 P
-// operands of its key planes (the forward's packing)
-__device__ __forceinline__ void pack_planes(const float (&v)[16], bf16x8 (&bp)[2]) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    uint32_t pw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pw[e] = pk_bf16(v[8 * j + 2 * e], v[8 * j + 2 * e + 1]);
-    bp[j] = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
-  }
-}
-
 // ------------------------------------------------------------------ dQ
 template <int D, int BQ, int SUB>
 __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
@@ -503,22 +491,12 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   const long long BH = (long long)s.B * s.H;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const float isd = 1.f / sqrtf((float)D);
-  int* counts = reinterpret_cast<int*>(ws + L.counts);
-  int* col_ptr = reinterpret_cast<int*>(ws + L.col_ptr);
-  int* row_idx = reinterpret_cast<int*>(ws + L.row_idx);
+  const int* col_ptr = reinterpret_cast<const int*>(ws + L.col_ptr);
+  const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* ddv = reinterpret_cast<float*>(ws + L.dd);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
-  const int words = s.words();
-  const int nch = (s.Nq + CROWS - 1) / CROWS;
-  const long long ncell = BH * s.Nk * nch;
-  const unsigned gcell = (unsigned)((ncell + 255) / 256);
-  hipLaunchKernelGGL(csc_bits_kernel, dim3((unsigned)((s.R() + 255) / 256)), dim3(256), 0, st, rp, ci, s.R(), words,
-                     bits);
-  hipLaunchKernelGGL(csc_count_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts);
-  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, nch, col_ptr);
-  hipLaunchKernelGGL(csc_fill_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts,
-                     col_ptr, row_idx);
+  hipError_t e = launch_csc(s, rp, ci, ws, L, st);
+  if (e != hipSuccess) return e;
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
   const uint16_t* v = static_cast<const uint16_t*>(V);
@@ -533,6 +511,26 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
 }
 
 }  // namespace
+
+hipError_t launch_csc(const Shape& s, const int32_t* rp, const int32_t* ci, char* ws, const BwdLayout& L,
+                      hipStream_t st) {
+  const long long BH = (long long)s.B * s.H;
+  int* counts = reinterpret_cast<int*>(ws + L.counts);
+  int* col_ptr = reinterpret_cast<int*>(ws + L.col_ptr);
+  int* row_idx = reinterpret_cast<int*>(ws + L.row_idx);
+  uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
+  const int words = s.words();
+  const int nch = (s.Nq + CROWS - 1) / CROWS;
+  const long long ncell = BH * s.Nk * nch;
+  const unsigned gcell = (unsigned)((ncell + 255) / 256);
+  hipLaunchKernelGGL(csc_bits_kernel, dim3((unsigned)((s.R() + 255) / 256)), dim3(256), 0, st, rp, ci, s.R(), words,
+                     bits);
+  hipLaunchKernelGGL(csc_count_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, nch, col_ptr);
+  hipLaunchKernelGGL(csc_fill_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts,
+                     col_ptr, row_idx);
+  return hipGetLastError();
+}
 
 BwdLayout bwd_layout(const Shape& s) {
   BwdLayout L{};
@@ -552,6 +550,22 @@ BwdLayout bwd_layout(const Shape& s) {
   L.dd = take((size_t)s.R() * s.bq * sizeof(float));
   L.achunks = (int)(((long long)s.N * s.d + ACH - 1) / ACH);
   L.apart = take(BH * L.achunks * sizeof(double));
+  // linear branch
+  const size_t rows = BH * (size_t)s.N * s.d;
+  const size_t per = (size_t)s.d * s.d + s.d;
+  L.lchunks = (s.N + LROWS - 1) / LROWS;
+  L.phiq = take(rows * 2);
+  L.phik = take(rows * 2);
+  L.U = take(rows * sizeof(float));
+  L.Yv = take(rows * sizeof(float));
+  L.Yk = take(rows * sizeof(float));
+  L.t1 = take((size_t)s.R() * s.bq * sizeof(float));
+  L.t2 = take((size_t)s.R() * s.bq * sizeof(float));
+  L.invden = take((size_t)s.R() * s.bq * sizeof(float));
+  L.dt = take((size_t)s.R() * s.bq * sizeof(float));
+  L.tot_h = take(BH * per * sizeof(float));
+  L.tot_m = take(BH * per * sizeof(float));
+  L.lpart = take(BH * L.lchunks * per * sizeof(float));
   L.total = off;
   return L;
 }

@@ -1,0 +1,602 @@
+// Backward of the linear branch (bf16) on gfx950.
+//
+// Source: SLA2 write-up (arXiv:2602.12675) §一 (the linear branch: linear
+// attention, phi = elu + 1, over the keys of the blocks a row does not
+// select), §二 (its output is normalised over those keys) and §四 (training
+// with the selection fixed per step).  For a query t of row block i with
+// unselected key set U, a = phi(q_t), w_u = a . phi(k_u), den = sum_U w_u,
+// O_l = sum_U w_u v_u / den and h the gradient reaching O_l:
+//   P~_u = w_u / den,  D~ = h . O_l,  dw_u = (h . v_u - D~) / den,
+//   da = sum_U dw_u phi(k_u),  dq = phi'(q) o da,
+//   dv_u = sum_{t: u in U_t} P~_tu h_t,  dphi(k_u) = sum_{t: u in U_t} dw_tu a_t.
+// Every sum over U is the sum over all keys minus the sum over the row's
+// listed blocks, as in the forward: with H = sum_u phi(k_u) v_u^T, z =
+// sum_u phi(k_u), M = sum_t a_t (h_t / den_t)^T and m = sum_t (D~_t / den_t) a_t,
+//   den = a . z - sum_sel w,   den D~ = a^T H h - sum_sel w (h . v),
+//   da  = (H h - D~ z - sum_sel (h . v_u - D~) phi(k_u)) / den,
+//   dv_u = M^T phi(k_u) - sum_sel P~ h,   dphi(k_u) = M v_u - m - sum_sel dw a.
+// The listed-pair sums run on the matrix cores in the same row (CSR) and
+// column (CSC) walks as the sparse branch's gradient, with phi(K) in place
+// of K and no exponential; the totals are float32 products per head.
+// A row whose blocks are all listed has no linear branch: its den, D~ and
+// gradient contributions are 0.
+//
+// Kernels:
+//   lin_phi_kernel     phi(Q), phi(K) as bf16 rows (the matrix-core tiles);
+//   lin_outer_kernel   chunk partials of R = sum_t x_t y_t^T and s = sum_t
+//                      c_t x_t per head (x = phi(rows), y = rows times a per-row
+//                      scale) - (H, z) and (M, m); summed by the chunk reduction;
+//   lin_rowvec_kernel  y_t = R x_t per row: H h (and a . z, a . H h) per query,
+//                      M^T phi(k) and M v - m per key;
+//   lin_dq_kernel      per mask row: pass A sums w and w (h . v) over the listed
+//                      units (den, D~), pass B accumulates phi(K)^T (h . v - D~),
+//                      then dq from the totals;
+//   lin_dkdv_kernel    per 64-key unit over the rows that list it: P~ and dw in
+//                      registers, dV^T += h^T P~ and dphi^T += phi(Q)^T dw, then
+//                      dk, dv from the totals.
+#include "sla.h"
+#include "sla_internal.h"
+#include "bf16_tiles.h"
+
+namespace sla {
+namespace {
+
+__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+// 8 bf16 of a uint4 as floats
+__device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = bf2f(elem(v, e));
+}
+
+// 4 consecutive bf16 at p: write (or add to what is there) the 4 values
+__device__ __forceinline__ void put4(uint16_t* p, const float (&v)[4], bool add) {
+  float o[4] = {v[0], v[1], v[2], v[3]};
+  if (add) {
+    const uint2 old = *reinterpret_cast<const uint2*>(p);
+    o[0] += bf2f(old.x & 0xffffu);
+    o[1] += bf2f(old.x >> 16);
+    o[2] += bf2f(old.y & 0xffffu);
+    o[3] += bf2f(old.y >> 16);
+  }
+  *reinterpret_cast<uint2*>(p) = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
+}
+
+// ------------------------------------------------------------------ phi rows
+__global__ __launch_bounds__(256) void lin_phi_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                      long long n8, uint16_t* __restrict__ A,
+                                                      uint16_t* __restrict__ F) {
+  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= 2 * n8) return;
+  const bool isk = t >= n8;
+  const long long o = isk ? t - n8 : t;
+  const uint4 v = reinterpret_cast<const uint4*>(isk ? K : Q)[o];
+  float x[8];
+  unpack8(v, x);
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = pk_bf16(phi(x[2 * e]), phi(x[2 * e + 1]));
+  reinterpret_cast<uint4*>(isk ? F : A)[o] = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// ------------------------------------------------------------------ totals
+// Partials over rows [chunk * LROWS, ...) of one head: R = sum_t phi(x_t) (ys_t
+// y_t)^T (D x D, row-major) and s = sum_t ss_t phi(x_t), with ys = 1 / den and
+// ss = D~ / den from the per-query arrays [bh * QP + t] (both 1 when inv is
+// null).  Thread (tr, tc) owns RB x RB outputs.
+template <int D>
+__global__ __launch_bounds__(256) void lin_outer_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
+                                                        const float* __restrict__ inv, const float* __restrict__ dtq,
+                                                        int N, long long QP, int nchunk, float* __restrict__ part) {
+  constexpr int RB = D / 16, SC = 32, CPR = D / 8;
+  __shared__ float xs[SC][D];
+  __shared__ float yv[SC][D];
+  __shared__ float sw[SC];
+  const long long bh = blockIdx.y;
+  const int chunk = blockIdx.x;
+  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;
+  const int r0 = chunk * LROWS, r1 = min(N, r0 + LROWS);
+  float acc[RB][RB], sacc[RB];
+#pragma unroll
+  for (int a = 0; a < RB; ++a) {
+    sacc[a] = 0.f;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) acc[a][b] = 0.f;
+  }
+  for (int t0 = r0; t0 < r1; t0 += SC) {
+    __syncthreads();  // the previous sub-chunk is consumed
+    for (int g = threadIdx.x; g < SC * CPR; g += 256) {
+      const int rr = g / CPR, cc = g % CPR, t = t0 + rr;
+      float x[8], y[8];
+      if (t < r1) {
+        const size_t o = ((size_t)bh * N + t) * D + cc * 8;
+        unpack8(*reinterpret_cast<const uint4*>(X + o), x);
+        unpack8(*reinterpret_cast<const uint4*>(Y + o), y);
+        const float sy = inv ? inv[bh * QP + t] : 1.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = phi(x[e]);
+          y[e] *= sy;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = y[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xs[rr][cc * 8 + e] = x[e];
+        yv[rr][cc * 8 + e] = y[e];
+      }
+      if (cc == 0) sw[rr] = t < r1 ? (inv ? dtq[bh * QP + t] * inv[bh * QP + t] : 1.f) : 0.f;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < SC; ++rr) {
+      float xr[RB], yc[RB];
+#pragma unroll
+      for (int a = 0; a < RB; ++a) {
+        xr[a] = xs[rr][tr * RB + a];
+        yc[a] = yv[rr][tc * RB + a];
+      }
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+#pragma unroll
+        for (int b = 0; b < RB; ++b) acc[a][b] = fmaf(xr[a], yc[b], acc[a][b]);
+      if (tc == 0) {
+        const float c = sw[rr];
+#pragma unroll
+        for (int a = 0; a < RB; ++a) sacc[a] = fmaf(xr[a], c, sacc[a]);
+      }
+    }
+  }
+  const size_t per = (size_t)D * D + D;
+  float* out = part + ((size_t)bh * nchunk + chunk) * per;
+#pragma unroll
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int b = 0; b < RB; ++b) out[(tr * RB + a) * D + tc * RB + b] = acc[a][b];
+  if (tc == 0) {
+#pragma unroll
+    for (int a = 0; a < RB; ++a) out[D * D + tr * RB + a] = sacc[a];
+  }
+}
+
+// y_t = R x_t for 64 rows of one head (R [D x D] row-major from tot, the
+// vector part s after it):
+//   MODE 0 (per query): x = h rows, y[r] = sum_c H[r][c] x[c] -> U; also
+//          t1 = phi(q) . z and t2 = phi(q) . y;
+//   MODE 1 (per key):   x = phi(k) rows, y[c] = sum_r M[r][c] x[r] -> Yv;
+//   MODE 2 (per key):   x = v rows, y[r] = sum_c M[r][c] x[c] - m[r] -> Yk.
+// LDS holds R^T or R so that y[o] = sum_i RT[i][o] x[i], and X^T.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void lin_rowvec_kernel(const uint16_t* __restrict__ X, const float* __restrict__ tot,
+                                                         const uint16_t* __restrict__ Qraw, int N, long long QP,
+                                                         float* __restrict__ out, float* __restrict__ t1,
+                                                         float* __restrict__ t2) {
+  constexpr int OB = D / 16, ROWS = 64, CPR = D / 8;
+  __shared__ float RT[D][D];
+  __shared__ float XT[D][ROWS];
+  const long long bh = blockIdx.y;
+  const int row0 = blockIdx.x * ROWS;
+  const float* R = tot + (size_t)bh * ((size_t)D * D + D);
+  for (int g = threadIdx.x; g < D * D; g += 256) {
+    const int a = g / D, b = g % D;  // R[a][b]
+    if (MODE == 1) RT[a][b] = R[g];
+    else RT[b][a] = R[g];
+  }
+  for (int g = threadIdx.x; g < ROWS * CPR; g += 256) {
+    const int rr = g / CPR, cc = g % CPR, t = row0 + rr;
+    float x[8];
+    if (t < N) {
+      unpack8(*reinterpret_cast<const uint4*>(X + ((size_t)bh * N + t) * D + cc * 8), x);
+      if (MODE == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = phi(x[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) XT[cc * 8 + e][rr] = x[e];
+  }
+  __syncthreads();
+  const int rg = threadIdx.x / 16, og = threadIdx.x % 16;
+  float acc[4][OB];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < OB; ++b) acc[a][b] = 0.f;
+  for (int i = 0; i < D; ++i) {
+    float xr[4], rc[OB];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) xr[a] = XT[i][rg * 4 + a];
+#pragma unroll
+    for (int b = 0; b < OB; ++b) rc[b] = RT[i][og * OB + b];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < OB; ++b) acc[a][b] = fmaf(rc[b], xr[a], acc[a][b]);
+  }
+  const float* sv = R + (size_t)D * D;  // z (MODE 0) or m (MODE 2)
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int t = row0 + rg * 4 + a;
+    float p1 = 0.f, p2 = 0.f;
+    if (t < N) {
+      float* o = out + ((size_t)bh * N + t) * D + og * OB;
+#pragma unroll
+      for (int b = 0; b < OB; ++b) {
+        float y = acc[a][b];
+        if (MODE == 2) y -= sv[og * OB + b];
+        o[b] = y;
+      }
+      if (MODE == 0) {
+        const uint16_t* qr = Qraw + ((size_t)bh * N + t) * D + og * OB;
+#pragma unroll
+        for (int b = 0; b < OB; ++b) {
+          const float aq = phi(bf2f(qr[b]));
+          p1 = fmaf(aq, sv[og * OB + b], p1);
+          p2 = fmaf(aq, acc[a][b], p2);
+        }
+      }
+    }
+    if (MODE == 0) {
+      // the 16 threads of a row group are consecutive lanes of one wavefront
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) {
+        p1 += __shfl_xor(p1, off);
+        p2 += __shfl_xor(p2, off);
+      }
+      if (og == 0 && t < N) {
+        t1[bh * QP + t] = p1;
+        t2[bh * QP + t] = p2;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dq
+template <int D, int BQ, int SUB>
+__global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ G, const uint16_t* __restrict__ Qraw, const int* __restrict__ row_ptr,
+    const int* __restrict__ col_idx, const float* __restrict__ U, const float* __restrict__ t1,
+    const float* __restrict__ t2, const float* __restrict__ tot_h, float* __restrict__ invden_out,
+    float* __restrict__ dt_out, uint16_t* __restrict__ dQ, int add, int N, int Nq, int Nk) {
+  using T = Tiles<D>;
+  constexpr int NW = BQ / 32;
+  using LP = LoadPlan<D, NW>;
+  constexpr int STAGE = 2 * T::KT_BYTES;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const ReadPlan<D> rdp(lane);
+  const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
+  const long long bh = row / Nq;
+  const int qi = (int)(row % Nq);
+  const int base = row_ptr[row];
+  const int nsel = row_ptr[row + 1] - base;
+  const int nunits = nsel * SUB;
+  const int q = qi * BQ + 32 * w + (lane & 31);
+  const bool qv = q < N;
+  const size_t qidx = (size_t)row * BQ + 32 * w + (lane & 31);  // per-query arrays
+
+  bf16x8 af[D / 16], hf[D / 16];
+  load_q<D>(A, bh, q, N, hi, af);
+  load_q<D>(G, bh, q, N, hi, hf);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+  float sw = 0.f, swh = 0.f;  // this lane's sums of w and w (h . v) over its listed keys
+  float inv = 0.f, dtv = 0.f;  // 1 / den and D~ (0 for a row without a linear branch)
+  auto settle = [&]() {
+    const float SW = sw + __shfl_xor(sw, 32), SWH = swh + __shfl_xor(swh, 32);
+    const float den = (qv ? t1[qidx] : 0.f) - SW;
+    const float X = (qv ? t2[qidx] : 0.f) - SWH;
+    if (qv && nsel < Nk && den > 0.f) {
+      inv = 1.f / den;
+      dtv = X * inv;
+    }
+  };
+  if (nunits > 0) {
+    const auto rf = buf_rsrc(F + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    const auto rv = buf_rsrc(V + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    auto key0 = [&](int x) {
+      const int u = x % nunits;
+      return (col_idx[base + u / SUB] * SUB + u % SUB) * KU;
+    };
+    const int nsteps = 2 * nunits;
+    auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
+      const LP lp(w, opaque(lane));
+      const int k0 = key0(x);
+      lp.load(rf, k0, sb);
+      lp.load(rv, k0, sb + T::KT_BYTES);
+    };
+    auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+      wait_vm<0>();
+      __syncthreads();
+      if (x + 1 < nsteps) issue(x + 1, nxt);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        // keys past N read as zero rows of phi(K) and V (buffer loads past the
+        // head's range return 0), so they add nothing to either pass
+        const f32x16 s = kt == 0 ? score_half<D, 0, 2>(cur, af, rdp) : score_half<D, 1, 2>(cur, af, rdp);
+        const f32x16 dp = kt == 0 ? score_half<D, 0, 2>(cur + T::KT_BYTES, hf, rdp)
+                                  : score_half<D, 1, 2>(cur + T::KT_BYTES, hf, rdp);
+        if (x < nunits) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            sw += s[i];
+            swh = fmaf(s[i], dp[i], swh);
+          }
+        } else {
+          if (x == nunits && kt == 0) settle();
+          float c[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) c[i] = dp[i] - dtv;
+          bf16x8 bp[2];
+          pack_planes(c, bp);
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+            for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(rdp.vt(cur, dt, 2 * kt + pl), bp[pl], acc[dt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    issue(0, st0);
+    int x = 0;
+    for (; x + 2 <= nsteps; x += 2) {
+      step(x, st0, st1);
+      step(x + 1, st1, st0);
+    }
+    wait_vm<0>();
+  }
+  if (nunits == 0) settle();
+  if (hi == 0) {
+    invden_out[qidx] = inv;
+    dt_out[qidx] = dtv;
+  }
+  if (!qv) return;
+  // da = (U - D~ z - acc) / den; dq = phi'(q) o da (element i of tile dt:
+  // d = 32 dt + 8 (i/4) + 4 hi + i%4)
+  const size_t qrow = ((size_t)bh * N + q) * D;
+  const float* z = tot_h + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hi;
+      const float4 u4 = *reinterpret_cast<const float4*>(U + qrow + d0);
+      const float4 z4 = *reinterpret_cast<const float4*>(z + d0);
+      const uint2 q2 = *reinterpret_cast<const uint2*>(Qraw + qrow + d0);
+      const float uu[4] = {u4.x, u4.y, u4.z, u4.w}, zz[4] = {z4.x, z4.y, z4.z, z4.w};
+      const float qq[4] = {bf2f(q2.x & 0xffffu), bf2f(q2.x >> 16), bf2f(q2.y & 0xffffu), bf2f(q2.y >> 16)};
+      float o[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = dphi(qq[c]) * ((uu[c] - dtv * zz[c] - acc[dt][4 * a + c]) * inv);
+      put4(dQ + qrow + d0, o, add != 0);
+    }
+}
+
+// ------------------------------------------------------------------ dk, dv
+template <int D, int BQ, int SUB>
+__global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ G, const uint16_t* __restrict__ Kraw, const int* __restrict__ col_ptr,
+    const int* __restrict__ row_idx, const float* __restrict__ invden, const float* __restrict__ dtq,
+    const float* __restrict__ Yv, const float* __restrict__ Yk, uint16_t* __restrict__ dK,
+    uint16_t* __restrict__ dV, int add, int N, int Nq, int Nk) {
+  using T = Tiles<D>;
+  using LP = LoadPlan<D, 4>;
+  constexpr int STAGE = 2 * T::KT_BYTES;  // phi(Q) and h tiles of 64 queries
+  constexpr int NDT = D / 64;
+  constexpr int QU = BQ / KU;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) uint4 xch[4][4][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hi = lane >> 5;
+  const int kh = w & 1, dh = w >> 1;
+  const int partner = w ^ 2;
+  const ReadPlan<D> rdp(lane);
+  const long long unit = xcd_row(blockIdx.x, (long long)gridDim.x);
+  const long long bh = unit / ((long long)Nk * SUB);
+  const int ku = (int)(unit % ((long long)Nk * SUB));
+  const int j = ku / SUB;
+  const int key = ku * KU + 32 * kh + (lane & 31);
+  const bool kv = key < N;
+  const long long col = bh * Nk + j;
+  const int cb = col_ptr[col];
+  const int nunits = (col_ptr[col + 1] - cb) * QU;
+
+  bf16x8 ff[D / 16], vf[D / 16];
+  load_q<D>(F, bh, key, N, hi, ff);
+  load_q<D>(V, bh, key, N, hi, vf);
+  f32x16 adv[NDT], adk[NDT];
+#pragma unroll
+  for (int t = 0; t < NDT; ++t) {
+    adv[t] = f32x16{};
+    adk[t] = f32x16{};
+  }
+  if (nunits > 0) {
+    const auto ra = buf_rsrc(A + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    const auto rg = buf_rsrc(G + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+    auto qrow_of = [&](int x) { return row_idx[cb + x / QU]; };
+    auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
+      const LP lp(w, opaque(lane));
+      const int q0 = qrow_of(x) * BQ + (x % QU) * KU;
+      lp.load(ra, q0, sb);
+      lp.load(rg, q0, sb + T::KT_BYTES);
+    };
+    auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+      const int qb = qrow_of(x);
+      const size_t r0 = ((size_t)(bh * Nq + qb)) * BQ + (x % QU) * KU;
+      wait_vm<0>();
+      __syncthreads();
+      if (x + 1 < nunits) issue(x + 1, nxt);
+      auto body = [&](auto qh_tag) __attribute__((always_inline)) {
+        constexpr int QH = decltype(qh_tag)::value;
+        constexpr int OWN = 2 * QH, OTH = 2 - OWN;
+        // w and h . v of this wavefront's 32 queries x its 32 keys (element
+        // i: query 32 QH + 8 (i/4) + 4 hi + i%4); P~ = w / den, dw = (h . v - D~) / den
+        const f32x16 s = score_half<D, QH, 4>(cur, ff, rdp);
+        const f32x16 dp = score_half<D, QH, 4>(cur + T::KT_BYTES, vf, rdp);
+        float pv[16], ds[16];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const size_t ro = r0 + 32 * QH + 8 * a + 4 * hi;
+          const float4 I4 = *reinterpret_cast<const float4*>(invden + ro);
+          const float4 D4 = *reinterpret_cast<const float4*>(dtq + ro);
+          const float Iq[4] = {I4.x, I4.y, I4.z, I4.w}, Dq[4] = {D4.x, D4.y, D4.z, D4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int i = 4 * a + c;
+            pv[i] = s[i] * Iq[c];
+            ds[i] = (dp[i] - Dq[c]) * Iq[c];
+          }
+        }
+        bf16x8 op[2][4];
+        bf16x8 bp[2], bs[2];
+        pack_planes(pv, bp);
+        pack_planes(ds, bs);
+        op[0][OWN] = bp[0];
+        op[0][OWN + 1] = bp[1];
+        op[1][OWN] = bs[0];
+        op[1][OWN + 1] = bs[1];
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl) xch[w][2 * o + pl][lane] = __builtin_bit_cast(uint4, op[o][OWN + pl]);
+        __syncthreads();
+#pragma unroll
+        for (int o = 0; o < 2; ++o)
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+            op[o][OTH + pl] = __builtin_bit_cast(bf16x8, xch[partner][2 * o + pl][lane]);
+#pragma unroll
+        for (int pl = 0; pl < 4; ++pl)
+#pragma unroll
+          for (int t = 0; t < NDT; ++t) {
+            adv[t] = mfma(rdp.vt(cur + T::KT_BYTES, NDT * QH + t, pl), op[0][pl], adv[t]);
+            adk[t] = mfma(rdp.vt(cur, NDT * QH + t, pl), op[1][pl], adk[t]);
+          }
+      };
+      if (dh == 0) body(IntTag<0>{});
+      else body(IntTag<1>{});
+    };
+    issue(0, st0);
+    int x = 0;
+    for (; x + 2 <= nunits; x += 2) {
+      step(x, st0, st1);
+      step(x + 1, st1, st0);
+    }
+    if (x < nunits) step(x, st0, st1);
+    wait_vm<0>();
+  }
+  if (!kv) return;
+  // dv = Yv - acc_v; dphi = Yk - acc_k; dk = phi'(k) o dphi (element i of tile
+  // t: d = 32 (NDT dh + t) + 8 (i/4) + 4 hi + i%4)
+  const size_t krow = ((size_t)bh * N + key) * D;
+#pragma unroll
+  for (int t = 0; t < NDT; ++t)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * (NDT * dh + t) + 8 * a + 4 * hi;
+      const float4 yv = *reinterpret_cast<const float4*>(Yv + krow + d0);
+      const float4 yk = *reinterpret_cast<const float4*>(Yk + krow + d0);
+      const uint2 k2 = *reinterpret_cast<const uint2*>(Kraw + krow + d0);
+      const float YV[4] = {yv.x, yv.y, yv.z, yv.w}, YK[4] = {yk.x, yk.y, yk.z, yk.w};
+      const float kk[4] = {bf2f(k2.x & 0xffffu), bf2f(k2.x >> 16), bf2f(k2.y & 0xffffu), bf2f(k2.y >> 16)};
+      float ov[4], ok[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ov[c] = YV[c] - adv[t][4 * a + c];
+        ok[c] = dphi(kk[c]) * (YK[c] - adk[t][4 * a + c]);
+      }
+      put4(dV + krow + d0, ov, add != 0);
+      put4(dK + krow + d0, ok, add != 0);
+    }
+}
+
+template <int D, int BQ, int SUB>
+hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const void* Vv, const void* dOv,
+                        const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool add, char* ws,
+                        const BwdLayout& L, hipStream_t st) {
+  const long long BH = (long long)s.B * s.H;
+  const long long QP = (long long)s.Nq * s.bq;  // per-query arrays: [bh * QP + t]
+  const uint16_t* Q = static_cast<const uint16_t*>(Qv);
+  const uint16_t* K = static_cast<const uint16_t*>(Kv);
+  const uint16_t* V = static_cast<const uint16_t*>(Vv);
+  const uint16_t* G = static_cast<const uint16_t*>(dOv);
+  uint16_t* A = reinterpret_cast<uint16_t*>(ws + L.phiq);
+  uint16_t* F = reinterpret_cast<uint16_t*>(ws + L.phik);
+  float* U = reinterpret_cast<float*>(ws + L.U);
+  float* Yv = reinterpret_cast<float*>(ws + L.Yv);
+  float* Yk = reinterpret_cast<float*>(ws + L.Yk);
+  float* t1 = reinterpret_cast<float*>(ws + L.t1);
+  float* t2 = reinterpret_cast<float*>(ws + L.t2);
+  float* invden = reinterpret_cast<float*>(ws + L.invden);
+  float* dtq = reinterpret_cast<float*>(ws + L.dt);
+  float* tot_h = reinterpret_cast<float*>(ws + L.tot_h);
+  float* tot_m = reinterpret_cast<float*>(ws + L.tot_m);
+  float* part = reinterpret_cast<float*>(ws + L.lpart);
+  const int per = D * D + D;
+  hipError_t e = launch_csc(s, rp, ci, ws, L, st);
+  if (e != hipSuccess) return e;
+  const long long n8 = BH * s.N * D / 8;
+  hipLaunchKernelGGL(lin_phi_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256), 0, st, Q, K, n8, A, F);
+  // H, z
+  hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, K, V,
+                     (const float*)nullptr, (const float*)nullptr, s.N, QP, L.lchunks, part);
+  if ((e = launch_summary_reduce(part, nullptr, s.H, BH, L.lchunks, per, tot_h, st)) != hipSuccess) return e;
+  // H h, phi(q).z, phi(q).H h per query
+  const dim3 grow((unsigned)((s.N + 63) / 64), (unsigned)BH);
+  hipLaunchKernelGGL((lin_rowvec_kernel<D, 0>), grow, dim3(256), 0, st, G, tot_h, Q, s.N, QP, U, t1, t2);
+  // rows: den, D~ and dq
+  hipLaunchKernelGGL((lin_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, A, F, V, G, Q,
+                     rp, ci, U, t1, t2, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, s.N, s.Nq,
+                     s.Nk);
+  // M = sum a (h / den)^T, m = sum (D~ / den) a
+  hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, Q, G, invden,
+                     dtq, s.N, QP, L.lchunks, part);
+  if ((e = launch_summary_reduce(part, nullptr, s.H, BH, L.lchunks, per, tot_m, st)) != hipSuccess) return e;
+  // M^T phi(k), M v - m per key
+  hipLaunchKernelGGL((lin_rowvec_kernel<D, 1>), grow, dim3(256), 0, st, K, tot_m, (const uint16_t*)nullptr, s.N, QP,
+                     Yv, (float*)nullptr, (float*)nullptr);
+  hipLaunchKernelGGL((lin_rowvec_kernel<D, 2>), grow, dim3(256), 0, st, V, tot_m, (const uint16_t*)nullptr, s.N, QP,
+                     Yk, (float*)nullptr, (float*)nullptr);
+  // keys: dk, dv
+  const int* col_ptr = reinterpret_cast<const int*>(ws + L.col_ptr);
+  const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
+  hipLaunchKernelGGL((lin_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, A, F, V, G,
+                     K, col_ptr, row_idx, invden, dtq, Yv, Yk, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
+                     add ? 1 : 0, s.N, s.Nq, s.Nk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_linear_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                             const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool accumulate,
+                             char* ws, const BwdLayout& L, hipStream_t st) {
+#define SLA_LBWD(DD, QQ, KK) \
+  if (s.d == DD && s.bq == QQ && s.bk == KK) return lin_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, accumulate, ws, L, st);
+  SLA_LBWD(128, 128, 64)
+  SLA_LBWD(128, 128, 128)
+  SLA_LBWD(128, 64, 64)
+  SLA_LBWD(128, 64, 128)
+  SLA_LBWD(64, 128, 64)
+  SLA_LBWD(64, 128, 128)
+  SLA_LBWD(64, 64, 64)
+  SLA_LBWD(64, 64, 128)
+#undef SLA_LBWD
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sla

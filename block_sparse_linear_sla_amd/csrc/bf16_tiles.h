@@ -279,5 +279,17 @@ __device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, i
   }
 }
 
+// 16 fp32 values of a 32-key S^T half (element order) into the 2 bf16 P
+// operands of its key planes (plane j: elements 8 j .. 8 j + 7)
+__device__ __forceinline__ void pack_planes(const float (&v)[16], bf16x8 (&bp)[2]) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[e] = pk_bf16(v[8 * j + 2 * e], v[8 * j + 2 * e + 1]);
+    bp[j] = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+  }
+}
+
 }  // namespace
 }  // namespace sla

@@ -298,6 +298,20 @@ int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const 
                                            static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
 }
 
+int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_l,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV, int accumulate,
+                   void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !dO_l || !row_ptr || !col_idx || !dQ || !dK || !dV) return SLA_ERR_INVALID_ARG;
+  const sla::BwdLayout L = sla::bwd_layout(s);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_linear_bwd(s, Q, K, V, dO_l, row_ptr, col_idx, dQ, dK, dV, accumulate != 0,
+                                           static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
 int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,
                    void* ws, size_t ws_bytes, void* stream) {
   Shape s;

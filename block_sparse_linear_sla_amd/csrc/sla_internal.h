@@ -60,9 +60,18 @@ struct BwdLayout {
   size_t lse2;     // float [R*bq]: log2-sum-exp of the scaled scores per query (+inf past N)
   size_t dd;       // float [R*bq]: D = dO . O per query (0 past N)
   size_t apart;    // double [B*H][achunks]: partial sums of the alpha gradient
+  // linear-branch backward
+  size_t phiq, phik;    // bf16 [B*H][N][d]: phi(Q), phi(K)
+  size_t U, Yv, Yk;     // float [B*H][N][d]: H h per query; M^T phi(k), M v - m per key
+  size_t t1, t2;        // float [R*bq]: phi(q).z and phi(q).(H h) per query
+  size_t invden, dt;    // float [R*bq]: 1 / linear denominator and h.O_l per query (0 where undefined)
+  size_t tot_h, tot_m;  // float [B*H][d*d + d]: (H, z) and (M, m), row-major
+  size_t lpart;         // float [B*H][lchunks][d*d + d]: chunk partials of those totals
   size_t total;
   int achunks;     // chunks of 65536 elements per (b, h) slice
+  int lchunks;     // chunks of LROWS rows per head for the linear totals
 };
+constexpr int LROWS = 512;
 
 BwdLayout bwd_layout(const Shape& s);
 
@@ -109,6 +118,14 @@ hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const
                              void* dV, char* ws, const BwdLayout& L, hipStream_t st);
 hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
                              char* ws, const BwdLayout& L, hipStream_t st);
+// the mask's transpose (CSC) into the backward workspace
+hipError_t launch_csc(const Shape& s, const int32_t* row_ptr, const int32_t* col_idx, char* ws, const BwdLayout& L,
+                      hipStream_t st);
+// attn_bwd_lin.hip: gradient of the linear branch (bf16) with the mask fixed;
+// accumulate: add to dQ, dK, dV instead of writing them
+hipError_t launch_linear_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                             const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
+                             bool accumulate, char* ws, const BwdLayout& L, hipStream_t st);
 
 // attn_f32.hip: linear totals and attention for float32 inputs.
 hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,

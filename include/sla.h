@@ -231,6 +231,28 @@ size_t sla_bwd_workspace_bytes(const sla_problem* prob);
 int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_s, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
                    void* dV, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Backward of the linear branch, mask fixed (SLA2 write-up §一 for the
+ * branch: phi = elu + 1 linear attention over the keys of the blocks a row
+ * does not select, normalised over those keys; §四 for training with the
+ * selection fixed per step).  For L = sum(O_l * dO_l), a = phi(q_t),
+ * w_tu = a . phi(k_u), den_t = sum over the row's unselected keys of w_tu,
+ * D~_t = dO_l[t] . O_l[t] and dw_tu = (dO_l[t] . v_u - D~_t) / den_t:
+ *   dq_t = phi'(q_t) o sum_u dw_tu phi(k_u),
+ *   dv_u = sum_t (w_tu / den_t) dO_l[t],  dk_u = phi'(k_u) o sum_t dw_tu a_t,
+ * every sum over the (query, key) pairs outside the listed blocks.  Each is
+ * formed as the sum over all pairs (float32 per-head totals) minus the sum
+ * over the listed pairs (bf16 matrix-core tiles, as in the sparse branch's
+ * gradient).  Rows whose blocks are all listed contribute nothing.  bf16 only
+ * (SLA_ERR_UNSUPPORTED for fp32).  dO_l is the gradient reaching O_l
+ * ((1 - alpha_h) dO for the mixed output).  Outputs dQ, dK, dV [B, H, N, d]
+ * bf16, every element written; with accumulate != 0 the results are added to
+ * what the buffers hold (for example the sparse branch's gradient) and
+ * rounded to bf16 once more.  Needs the sla_bwd_workspace_bytes workspace
+ * (its contents on entry are ignored).  Deterministic: no atomics. */
+int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_l,
+                   const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
+                   int accumulate, void* ws, size_t ws_bytes, void* stream);
+
 /* Gradient of sum(O * dO) with respect to alpha for O = alpha_h O_s +
  * (1 - alpha_h) O_l (SLA2 write-up §二): dalpha[h] = sum over the head's
  * tokens of dO . (O_s - O_l), float64 partial sums in a fixed order, written

@@ -569,37 +569,36 @@ def alpha_grad(dO, Os, Ol) -> np.ndarray:
 
 
 # -------------------------------------------------------- linear backward
-def linear_branch_backward(Q, K, V, bq: int, bk: int, row_ptr, col_idx, dO) -> Dict[str, np.ndarray]:
+def linear_branch_backward(Q, K, V, bq: int, bk: int, row_ptr, col_idx, dO, rows=None) -> Dict[str, np.ndarray]:
     """dQ, dK, dV of L = sum(O_l * dO), O_l the linear branch of
     linear_branch() over each row block's unselected keys (mask fixed), as
     the derivative of that definition taken by torch's autograd in float64,
     one row block at a time (rows whose blocks are all selected contribute
-    nothing)."""
+    nothing).  With `rows` (a list of (b, h, i)) only those row blocks are
+    differentiated: their dQ rows are exact, dK and dV hold only their share."""
     import torch
     Qt, Kt, Vt = (torch.tensor(as_f64(x)) for x in (Q, K, V))
     G = torch.tensor(as_f64(dO))
     B, H, N, d = Qt.shape
     Nq, Nk = n_blocks(N, bq), n_blocks(N, bk)
     dQ, dK, dV = torch.zeros_like(Qt), torch.zeros_like(Kt), torch.zeros_like(Vt)
-    for b in range(B):
-        for h in range(H):
-            for i in range(Nq):
-                r = (b * H + h) * Nq + i
-                sel = set(int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]])
-                unsel = [j for j in range(Nk) if j not in sel]
-                if not unsel:
-                    continue
-                keys = torch.tensor(_keys_of(unsel, bk, N))
-                s, e = block_range(i, bq, N)
-                q = Qt[b, h, s:e].clone().requires_grad_(True)
-                k = Kt[b, h, keys].clone().requires_grad_(True)
-                v = Vt[b, h, keys].clone().requires_grad_(True)
-                fq = torch.nn.functional.elu(q) + 1.0
-                fk = torch.nn.functional.elu(k) + 1.0
-                A = fq @ fk.T
-                o = (A @ v) / A.sum(dim=1, keepdim=True)
-                (o * G[b, h, s:e]).sum().backward()
-                dQ[b, h, s:e] += q.grad
-                dK[b, h, keys] += k.grad
-                dV[b, h, keys] += v.grad
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = set(int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]])
+        unsel = [j for j in range(Nk) if j not in sel]
+        if not unsel:
+            continue
+        keys = torch.tensor(_keys_of(unsel, bk, N))
+        s, e = block_range(i, bq, N)
+        q = Qt[b, h, s:e].clone().requires_grad_(True)
+        k = Kt[b, h, keys].clone().requires_grad_(True)
+        v = Vt[b, h, keys].clone().requires_grad_(True)
+        fq = torch.nn.functional.elu(q) + 1.0
+        fk = torch.nn.functional.elu(k) + 1.0
+        A = fq @ fk.T
+        o = (A @ v) / A.sum(dim=1, keepdim=True)
+        (o * G[b, h, s:e]).sum().backward()
+        dQ[b, h, s:e] += q.grad
+        dK[b, h, keys] += k.grad
+        dV[b, h, keys] += v.grad
     return {"dQ": dQ.numpy(), "dK": dK.numpy(), "dV": dV.numpy()}

@@ -1,0 +1,151 @@
+"""GPU parity of the linear-branch backward against the oracle (float64
+autograd of the linear branch over each row block's unselected keys, mask
+fixed).
+
+Bar, derived from the arithmetic: the kernels take bf16 inputs exactly,
+form phi(Q) and phi(K) once as bf16 matrix-core operands (relative 2^-9),
+keep the per-head totals and per-query terms in float32, round the
+listed-pair weights to bf16 where they enter a matrix product (2^-9) and the
+outputs to bf16 (2^-9; once more when accumulating).  These roundings are
+independent from element to element, so, as for the sparse branch, each
+gradient tensor must stay within a relative L1 error of 1e-2 of the exact one
+and every element within 2e-2 of the tensor's largest magnitude.
+
+At the 480p workload's full length the oracle differentiates sampled row
+blocks (their dQ rows are exact), and two identities that hold at any size
+check the rest: dV summed over keys equals dO_l summed over the rows that
+have a linear branch, and rescaling phi(k) for all keys (phi(q_t) for one
+query) leaves O_l unchanged, so sum_u phi(k_u) . dphi(k_u) = 0 per head and
+phi(q_t) . dphi(q_t) = 0 per query, with dphi = grad / phi'."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_linear_sla_amd as S
+import gen
+from oracle import sla_oracle as O
+from tests import _util as U
+from tests.test_gpu_bwd import _compare, _random_csr
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(x, rp, ci, seed):
+    q, k, v = U.dev(x.Q, x.K, x.V)
+    dO = torch.from_numpy(np.random.default_rng(seed).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
+    rpt = torch.from_numpy(rp).int().cuda()
+    cit = torch.from_numpy(ci).int().cuda() if len(ci) else torch.zeros(1, dtype=torch.int32, device="cuda")
+    return q, k, v, dO, rpt, cit
+
+
+CASES = [
+    # name, N, d, bq, bk, density
+    ("ragged-1000", 1000, 128, 128, 64, 0.3),
+    ("d64-bq64-bk128-777", 777, 64, 64, 128, 0.4),
+    ("bq64-bk128-1500", 1500, 128, 64, 128, 0.25),
+    ("d64-600", 600, 64, 128, 64, 0.5),
+    ("sparse-2100", 2100, 128, 128, 64, 0.05),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_linear_bwd_small(case):
+    name, N, d, bq, bk, density = case
+    print(f"[lin-bwd] {name}", flush=True)
+    wl = gen.Workload("adhoc", B=1, H=2, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+                      dtype="bf16", router=False, seed=23)
+    x = gen.make(wl)
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    # row 1 lists nothing (linear over every key), the last row lists every
+    # block (no linear branch)
+    rp, ci = _random_csr(np.random.default_rng(11), 2, Nq, Nk, density, empty_rows={1},
+                         full_rows={2 * Nq - 1})
+    q, k, v, dO, rpt, cit = _inputs(x, rp, ci, seed=6)
+    dq, dk, dv = S.sla_linear_bwd(q, k, v, dO.cuda(), bq, bk, rpt, cit)
+    torch.cuda.synchronize()
+    ref = O.linear_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
+    _compare(dq, ref["dQ"], "dQ")
+    _compare(dk, ref["dK"], "dK")
+    _compare(dv, ref["dV"], "dV")
+    # the fully listed row block has no linear branch: its dQ rows are 0
+    s0 = (Nq - 1) * bq
+    assert not dq[0, 1, s0:].any()
+
+
+def test_linear_bwd_accumulates_onto_sparse():
+    """Both branches into one set of buffers: sparse branch's gradient with
+    alpha dO, then the linear branch's with (1 - alpha) dO added."""
+    N, d, bq, bk, alpha = 900, 128, 128, 64, 0.7
+    print(f"[lin-bwd] accumulate N={N}", flush=True)
+    wl = gen.Workload("adhoc", B=1, H=2, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+                      dtype="bf16", router=False, seed=29)
+    x = gen.make(wl)
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp, ci = _random_csr(np.random.default_rng(12), 2, Nq, Nk, 0.35)
+    q, k, v, dO, rpt, cit = _inputs(x, rp, ci, seed=7)
+    g = dO.cuda()
+    gs = (alpha * g.float()).to(torch.bfloat16)
+    gl = ((1 - alpha) * g.float()).to(torch.bfloat16)
+    ws = S.bwd_workspace(S.problem(q, bq, bk), q.device)
+    out = S.sla_sparse_bwd(q, k, v, gs, bq, bk, rpt, cit, ws=ws)
+    S.sla_linear_bwd(q, k, v, gl, bq, bk, rpt, cit, ws=ws, out=out, accumulate=True)
+    torch.cuda.synchronize()
+    rs = O.sparse_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, gs.cpu())
+    rl = O.linear_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, gl.cpu())
+    for t, n in zip(out, ("dQ", "dK", "dV")):
+        _compare(t, rs[n] + rl[n], n)
+
+
+def _dphi_inv(x):
+    """1 / phi'(x) for phi = elu + 1, float64."""
+    return np.where(x > 0, 1.0, np.exp(-np.minimum(x, 0.0)))
+
+
+def test_linear_bwd_480p_two_heads():
+    """The 480p SLA2 workload at full length (N = 32760) on two heads with the
+    library's own mask: sampled row blocks against the oracle, identities for
+    the rest."""
+    wl = gen.WORKLOADS["video480p-sla2-N32760"]
+    print(f"[lin-bwd] {wl.name}, 2 heads", flush=True)
+    x = gen.make(wl, heads=2)
+    q, k, v = U.dev(x.Q, x.K, x.V)
+    rp_t, ci_t = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    rp, ci = U.csr(rp_t, ci_t)
+    dO = torch.from_numpy(np.random.default_rng(8).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
+    dq, dk, dv = S.sla_linear_bwd(q, k, v, dO.cuda(), wl.bq, wl.bk, rp_t, ci_t)
+    torch.cuda.synchronize()
+    B, H, N, d = x.Q.shape
+    Nq = O.n_blocks(N, wl.bq)
+    rows = [(0, 0, 0), (0, 0, Nq // 2), (0, 1, 77), (0, 1, Nq - 1)]
+    ref = O.linear_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
+    for (b, h, i) in rows:
+        s, e = i * wl.bq, min(N, (i + 1) * wl.bq)
+        _compare(dq[b, h, s:e], ref["dQ"][b, h, s:e], f"dQ rows of block {i}, head {h}")
+    Qd, Kd = O.as_f64(x.Q), O.as_f64(x.K)
+    G = O.as_f64(dO)
+    dqd, dkd, dvd = (t.cpu().double().numpy() for t in (dq, dk, dv))
+    for h in range(H):
+        # dV sums to dO over the rows with a linear branch
+        has = np.zeros(N, dtype=bool)
+        for i in range(Nq):
+            r = h * Nq + i
+            if rp[r + 1] - rp[r] < O.n_blocks(N, wl.bk):
+                has[i * wl.bq:(i + 1) * wl.bq] = True
+        want = G[0, h][has].sum(0)
+        got = dvd[0, h].sum(0)
+        scale = np.abs(G[0, h][has]).sum(0).max()
+        err = np.abs(got - want).max() / scale
+        print(f"  head {h}: sum dV vs sum dO_l: {err:.3g} of sum|dO_l|")
+        assert err <= 1e-2
+        # sum_u phi(k_u) . dphi(k_u) = 0
+        pk = O.phi(Kd[0, h])
+        terms = pk * dkd[0, h] * _dphi_inv(Kd[0, h])
+        rel = abs(terms.sum()) / np.abs(terms).sum()
+        print(f"  head {h}: sum phi(k) . dphi(k): {rel:.3g} of sum |terms|")
+        assert rel <= 1e-2
+        # phi(q_t) . dphi(q_t) = 0 per query
+        pq = O.phi(Qd[0, h])
+        tq = pq * dqd[0, h] * _dphi_inv(Qd[0, h])
+        relq = np.abs(tq.sum(1)) / np.maximum(np.abs(tq).sum(1), 1e-30)
+        print(f"  head {h}: per-query phi(q) . dphi(q): max {relq.max():.3g}, mean {relq.mean():.3g}")
+        assert relq.mean() <= 2e-2
