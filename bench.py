@@ -271,7 +271,9 @@ def main():
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
         S.sla_sparse_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
         torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        S.sla_linear_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads, accumulate=True)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         e[0].record()
         for _ in range(args.steps):
             S.sla_sparse_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
@@ -279,14 +281,23 @@ def main():
         for _ in range(args.steps):
             S.sla_alpha_grad(dO, out, grads[0], wl.bq, wl.bk, ws=bws)
         e[2].record()
+        for _ in range(args.steps):
+            S.sla_linear_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads, accumulate=True)
+        e[3].record()
         torch.cuda.synchronize()
         t_b = e[0].elapsed_time(e[1]) / args.steps
+        t_lb = e[2].elapsed_time(e[3]) / args.steps
         bwd_flops = 10.0 * wl.bq * wl.bk * wl.d * nnz
         res["bwd"] = {"sparse_bwd_ms": t_b, "alpha_grad_ms": e[1].elapsed_time(e[2]) / args.steps,
                       "achieved": bwd_flops / (t_b * 1e-3) / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                       "frac": bwd_flops / (t_b * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                       "kernels": "csc_count/scan/fill + bwd_dq_kernel + bwd_dkdv_kernel",
-                      "vs_sparse_fwd": t_b / t_sp}
+                      "vs_sparse_fwd": t_b / t_sp,
+                      # the linear branch's backward, accumulated onto the sparse
+                      # branch's: mask transpose, phi tiles, the four per-head
+                      # float32 products and the listed-pair row and column walks
+                      "linear_bwd_ms": t_lb,
+                      "linear_kernels": "lin_phi + lin_outer x2 + lin_rowvec x3 + lin_dq + lin_dkdv"}
 
     # SoftTop-k weights of every mask row (pool + logits + threshold solve),
     # the router-training form of the selection, at temperature 0.5

@@ -559,8 +559,7 @@ BwdLayout bwd_layout(const Shape& s) {
   L.U = take(rows * sizeof(float));
   L.Yv = take(rows * sizeof(float));
   L.Yk = take(rows * sizeof(float));
-  L.t1 = take((size_t)s.R() * s.bq * sizeof(float));
-  L.t2 = take((size_t)s.R() * s.bq * sizeof(float));
+  L.rsplit = take(BH * (size_t)(s.d / 32) * (s.d / 16) * 2 * 64 * 16);
   L.invden = take((size_t)s.R() * s.bq * sizeof(float));
   L.dt = take((size_t)s.R() * s.bq * sizeof(float));
   L.tot_h = take(BH * per * sizeof(float));

@@ -26,10 +26,12 @@
 //   lin_outer_kernel   chunk partials of R = sum_t x_t y_t^T and s = sum_t
 //                      c_t x_t per head (x = phi(rows), y = rows times a per-row
 //                      scale) - (H, z) and (M, m); summed by the chunk reduction;
-//   lin_rowvec_kernel  y_t = R x_t per row: H h (and a . z, a . H h) per query,
+//   lin_split_kernel   a total as hi + lo bf16 matrix-core fragments;
+//   lin_rowvec_kernel  y_t = R x_t per row on the matrix cores: H h per query,
 //                      M^T phi(k) and M v - m per key;
 //   lin_dq_kernel      per mask row: pass A sums w and w (h . v) over the listed
-//                      units (den, D~), pass B accumulates phi(K)^T (h . v - D~),
+//                      units, then den = a . z - sum w and den D~ = a . H h -
+//                      sum w (h . v); pass B accumulates phi(K)^T (h . v - D~);
 //                      then dq from the totals;
 //   lin_dkdv_kernel    per 64-key unit over the rows that list it: P~ and dw in
 //                      registers, dV^T += h^T P~ and dphi^T += phi(Q)^T dw, then
@@ -160,96 +162,97 @@ __global__ __launch_bounds__(256) void lin_outer_kernel(const uint16_t* __restri
   }
 }
 
-// y_t = R x_t for 64 rows of one head (R [D x D] row-major from tot, the
-// vector part s after it):
-//   MODE 0 (per query): x = h rows, y[r] = sum_c H[r][c] x[c] -> U; also
-//          t1 = phi(q) . z and t2 = phi(q) . y;
-//   MODE 1 (per key):   x = phi(k) rows, y[c] = sum_r M[r][c] x[r] -> Yv;
-//   MODE 2 (per key):   x = v rows, y[r] = sum_c M[r][c] x[c] - m[r] -> Yk.
-// LDS holds R^T or R so that y[o] = sum_i RT[i][o] x[i], and X^T.
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void lin_rowvec_kernel(const uint16_t* __restrict__ X, const float* __restrict__ tot,
-                                                         const uint16_t* __restrict__ Qraw, int N, long long QP,
-                                                         float* __restrict__ out, float* __restrict__ t1,
-                                                         float* __restrict__ t2) {
-  constexpr int OB = D / 16, ROWS = 64, CPR = D / 8;
-  __shared__ float RT[D][D];
-  __shared__ float XT[D][ROWS];
+// One head's D x D total R (row-major in tot) as the B operands of y_t = R' x_t
+// on the matrix cores, R' = R (TRANS = 0: y[o] = sum_i R[o][i] x[i]) or R^T
+// (TRANS = 1: y[o] = sum_i R[i][o] x[i]).  Fragment (dt, kk) of lane l holds
+// R'[o][i] for o = 32 dt + l % 32 and i = 16 kk + 8 (l / 32) + 0..7, each
+// value split as hi = bf16(x) and lo = bf16(x - hi), so that the two
+// bf16 products keep R to about 2^-17 relative.  Layout: uint4
+// [bh][(dt * D/16 + kk) * 2 + part][lane].
+template <int D>
+__global__ __launch_bounds__(256) void lin_split_kernel(const float* __restrict__ tot, int trans,
+                                                        uint4* __restrict__ frag) {
+  constexpr int NKK = D / 16, PER_HEAD = (D / 32) * NKK * 64;
   const long long bh = blockIdx.y;
-  const int row0 = blockIdx.x * ROWS;
+  const int g = blockIdx.x * 256 + threadIdx.x;  // (dt, kk, lane)
+  if (g >= PER_HEAD) return;
+  const int lane = g & 63, f = g >> 6;
+  const int dt = f / NKK, kk = f % NKK;
+  const int o = 32 * dt + (lane & 31), i0 = 16 * kk + 8 * (lane >> 5);
   const float* R = tot + (size_t)bh * ((size_t)D * D + D);
-  for (int g = threadIdx.x; g < D * D; g += 256) {
-    const int a = g / D, b = g % D;  // R[a][b]
-    if (MODE == 1) RT[a][b] = R[g];
-    else RT[b][a] = R[g];
-  }
-  for (int g = threadIdx.x; g < ROWS * CPR; g += 256) {
-    const int rr = g / CPR, cc = g % CPR, t = row0 + rr;
-    float x[8];
-    if (t < N) {
-      unpack8(*reinterpret_cast<const uint4*>(X + ((size_t)bh * N + t) * D + cc * 8), x);
-      if (MODE == 1) {
+  uint32_t h[4], l[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = phi(x[e]);
-      }
-    } else {
+  for (int e = 0; e < 4; ++e) {
+    float x[2], hf[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    for (int c = 0; c < 2; ++c) {
+      const int i = i0 + 2 * e + c;
+      x[c] = trans ? R[(size_t)i * D + o] : R[(size_t)o * D + i];
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) XT[cc * 8 + e][rr] = x[e];
+    h[e] = pk_bf16(x[0], x[1]);
+    hf[0] = bf2f(h[e] & 0xffffu);
+    hf[1] = bf2f(h[e] >> 16);
+    l[e] = pk_bf16(x[0] - hf[0], x[1] - hf[1]);
   }
+  uint4* dst = frag + (size_t)bh * 2 * PER_HEAD + (size_t)(2 * f) * 64 + lane;
+  dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+  dst[64] = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// y_t = R' x_t for the rows of one head, on the matrix cores (x bf16 rows,
+// R' from lin_split_kernel, float32 results [bh][N][D]):
+//   MODE 0: x = dO_l rows, R' = H  -> U = H h per query;
+//   MODE 1: x = phi(k) rows, R' = M^T -> M^T phi(k) per key;
+//   MODE 2: x = v rows, R' = M, minus m (the vector part of tot) -> M v - m.
+// Each wavefront takes 32-row groups: A = the rows' fragments (16 bytes per
+// lane and k step, straight from HBM), B = the fragments staged in LDS once
+// per workgroup; lane l of the result holds column o = 32 dt + l % 32 of
+// rows 8 (i/4) + 4 (l/32) + i%4, so a store covers 32 consecutive floats of a row.
+constexpr int RV_GPW = 2;  // 32-row groups per wavefront
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void lin_rowvec_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ frag,
+                                                         const float* __restrict__ tot, int N,
+                                                         float* __restrict__ out) {
+  constexpr int NDT = D / 32, NKK = D / 16, NF = NDT * NKK * 2;
+  __shared__ uint4 bfr[NF * 64];
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long bh = blockIdx.y;
+  const uint4* src = frag + (size_t)bh * NF * 64;
+  for (int g = tid; g < NF * 64; g += 256) bfr[g] = src[g];
   __syncthreads();
-  const int rg = threadIdx.x / 16, og = threadIdx.x % 16;
-  float acc[4][OB];
+  const float* mv = tot + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
+#pragma unroll 1
+  for (int grp = 0; grp < RV_GPW; ++grp) {
+    const int t0 = (blockIdx.x * 4 * RV_GPW + grp * 4 + w) * 32;
+    if (t0 >= N) break;
+    const int t = t0 + (lane & 31);
+    bf16x8 a[NKK];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < OB; ++b) acc[a][b] = 0.f;
-  for (int i = 0; i < D; ++i) {
-    float xr[4], rc[OB];
-#pragma unroll
-    for (int a = 0; a < 4; ++a) xr[a] = XT[i][rg * 4 + a];
-#pragma unroll
-    for (int b = 0; b < OB; ++b) rc[b] = RT[i][og * OB + b];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int b = 0; b < OB; ++b) acc[a][b] = fmaf(rc[b], xr[a], acc[a][b]);
-  }
-  const float* sv = R + (size_t)D * D;  // z (MODE 0) or m (MODE 2)
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int t = row0 + rg * 4 + a;
-    float p1 = 0.f, p2 = 0.f;
-    if (t < N) {
-      float* o = out + ((size_t)bh * N + t) * D + og * OB;
-#pragma unroll
-      for (int b = 0; b < OB; ++b) {
-        float y = acc[a][b];
-        if (MODE == 2) y -= sv[og * OB + b];
-        o[b] = y;
-      }
-      if (MODE == 0) {
-        const uint16_t* qr = Qraw + ((size_t)bh * N + t) * D + og * OB;
-#pragma unroll
-        for (int b = 0; b < OB; ++b) {
-          const float aq = phi(bf2f(qr[b]));
-          p1 = fmaf(aq, sv[og * OB + b], p1);
-          p2 = fmaf(aq, acc[a][b], p2);
-        }
-      }
+    for (int kk = 0; kk < NKK; ++kk) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (t < N) v = *reinterpret_cast<const uint4*>(X + ((size_t)bh * N + t) * D + 16 * kk + 8 * hi);
+      a[kk] = as_bf16x8(v);
     }
-    if (MODE == 0) {
-      // the 16 threads of a row group are consecutive lanes of one wavefront
+    f32x16 acc[NDT];
 #pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) {
-        p1 += __shfl_xor(p1, off);
-        p2 += __shfl_xor(p2, off);
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const uint4* fb = bfr + (size_t)(2 * (dt * NKK + kk)) * 64 + lane;
+        acc[dt] = mfma(a[kk], as_bf16x8(fb[0]), acc[dt]);
+        acc[dt] = mfma(a[kk], as_bf16x8(fb[64]), acc[dt]);
       }
-      if (og == 0 && t < N) {
-        t1[bh * QP + t] = p1;
-        t2[bh * QP + t] = p2;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int o = 32 * dt + (lane & 31);
+      const float sub = MODE == 2 ? mv[o] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = t0 + 8 * (i >> 2) + 4 * hi + (i & 3);
+        if (r < N) out[((size_t)bh * N + r) * D + o] = acc[dt][i] - sub;
       }
     }
   }
@@ -260,8 +263,8 @@ template <int D, int BQ, int SUB>
 __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Qraw, const int* __restrict__ row_ptr,
-    const int* __restrict__ col_idx, const float* __restrict__ U, const float* __restrict__ t1,
-    const float* __restrict__ t2, const float* __restrict__ tot_h, float* __restrict__ invden_out,
+    const int* __restrict__ col_idx, const float* __restrict__ U, const float* __restrict__ tot_h,
+    float* __restrict__ invden_out,
     float* __restrict__ dt_out, uint16_t* __restrict__ dQ, int add, int N, int Nq, int Nk) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
@@ -292,10 +295,34 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
   float sw = 0.f, swh = 0.f;  // this lane's sums of w and w (h . v) over its listed keys
   float inv = 0.f, dtv = 0.f;  // 1 / den and D~ (0 for a row without a linear branch)
+  const size_t qrow = ((size_t)bh * N + (qv ? q : 0)) * D;
+  const float* z = tot_h + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
+  // phi(q) . z and phi(q) . (H h) over this lane's half of d (the 8-d slices
+  // 16 t + 8 hi of its fragments); the two halves are added in settle
+  float p1 = 0.f, p2 = 0.f;
+  if (qv) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const int d0 = 16 * t + 8 * hi;
+      const uint4 av = __builtin_bit_cast(uint4, af[t]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float4 u4 = *reinterpret_cast<const float4*>(U + qrow + d0 + 4 * c);
+        const float4 z4 = *reinterpret_cast<const float4*>(z + d0 + 4 * c);
+        const float uu[4] = {u4.x, u4.y, u4.z, u4.w}, zz[4] = {z4.x, z4.y, z4.z, z4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float ae = bf2f(elem(av, 4 * c + e));
+          p1 = fmaf(ae, zz[e], p1);
+          p2 = fmaf(ae, uu[e], p2);
+        }
+      }
+    }
+  }
   auto settle = [&]() {
     const float SW = sw + __shfl_xor(sw, 32), SWH = swh + __shfl_xor(swh, 32);
-    const float den = (qv ? t1[qidx] : 0.f) - SW;
-    const float X = (qv ? t2[qidx] : 0.f) - SWH;
+    const float den = p1 + __shfl_xor(p1, 32) - SW;
+    const float X = p2 + __shfl_xor(p2, 32) - SWH;
     if (qv && nsel < Nk && den > 0.f) {
       inv = 1.f / den;
       dtv = X * inv;
@@ -304,36 +331,33 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   if (nunits > 0) {
     const auto rf = buf_rsrc(F + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
     const auto rv = buf_rsrc(V + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
-    auto key0 = [&](int x) {
-      const int u = x % nunits;
-      return (col_idx[base + u / SUB] * SUB + u % SUB) * KU;
-    };
-    const int nsteps = 2 * nunits;
     auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
       const LP lp(w, opaque(lane));
-      const int k0 = key0(x);
+      const int k0 = (col_idx[base + x / SUB] * SUB + x % SUB) * KU;
       lp.load(rf, k0, sb);
       lp.load(rv, k0, sb + T::KT_BYTES);
     };
-    auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+    // keys past N read as zero rows of phi(K) and V (buffer loads past the
+    // head's range return 0), so they add nothing to either pass
+    auto step = [&](auto pass, int x, char* cur, char* nxt) __attribute__((always_inline)) {
+      constexpr int PASS = decltype(pass)::value;
       wait_vm<0>();
       __syncthreads();
-      if (x + 1 < nsteps) issue(x + 1, nxt);
+      if (x + 1 < nunits) issue(x + 1, nxt);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        // keys past N read as zero rows of phi(K) and V (buffer loads past the
-        // head's range return 0), so they add nothing to either pass
-        const f32x16 s = kt == 0 ? score_half<D, 0, 2>(cur, af, rdp) : score_half<D, 1, 2>(cur, af, rdp);
         const f32x16 dp = kt == 0 ? score_half<D, 0, 2>(cur + T::KT_BYTES, hf, rdp)
                                   : score_half<D, 1, 2>(cur + T::KT_BYTES, hf, rdp);
-        if (x < nunits) {
+        if (PASS == 0) {
+          // pass A: w and w (h . v) summed over this lane's keys
+          const f32x16 s = kt == 0 ? score_half<D, 0, 2>(cur, af, rdp) : score_half<D, 1, 2>(cur, af, rdp);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             sw += s[i];
             swh = fmaf(s[i], dp[i], swh);
           }
         } else {
-          if (x == nunits && kt == 0) settle();
+          // pass B: phi(K)^T (h . v - D~) over this half's two key planes
           float c[16];
 #pragma unroll
           for (int i = 0; i < 16; ++i) c[i] = dp[i] - dtv;
@@ -347,15 +371,23 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    issue(0, st0);
-    int x = 0;
-    for (; x + 2 <= nsteps; x += 2) {
-      step(x, st0, st1);
-      step(x + 1, st1, st0);
-    }
-    wait_vm<0>();
+    auto run = [&](auto pass) __attribute__((always_inline)) {
+      issue(0, st0);
+      int x = 0;
+      for (; x + 2 <= nunits; x += 2) {
+        step(pass, x, st0, st1);
+        step(pass, x + 1, st1, st0);
+      }
+      if (x < nunits) step(pass, x, st0, st1);
+      wait_vm<0>();
+      __syncthreads();  // every wavefront is done with both stages
+    };
+    run(IntTag<0>{});
+    settle();
+    run(IntTag<1>{});
+  } else {
+    settle();
   }
-  if (nunits == 0) settle();
   if (hi == 0) {
     invden_out[qidx] = inv;
     dt_out[qidx] = dtv;
@@ -363,8 +395,6 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   if (!qv) return;
   // da = (U - D~ z - acc) / den; dq = phi'(q) o da (element i of tile dt:
   // d = 32 dt + 8 (i/4) + 4 hi + i%4)
-  const size_t qrow = ((size_t)bh * N + q) * D;
-  const float* z = tot_h + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -539,8 +569,7 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   float* U = reinterpret_cast<float*>(ws + L.U);
   float* Yv = reinterpret_cast<float*>(ws + L.Yv);
   float* Yk = reinterpret_cast<float*>(ws + L.Yk);
-  float* t1 = reinterpret_cast<float*>(ws + L.t1);
-  float* t2 = reinterpret_cast<float*>(ws + L.t2);
+  uint4* frag = reinterpret_cast<uint4*>(ws + L.rsplit);
   float* invden = reinterpret_cast<float*>(ws + L.invden);
   float* dtq = reinterpret_cast<float*>(ws + L.dt);
   float* tot_h = reinterpret_cast<float*>(ws + L.tot_h);
@@ -555,22 +584,23 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, K, V,
                      (const float*)nullptr, (const float*)nullptr, s.N, QP, L.lchunks, part);
   if ((e = launch_summary_reduce(part, nullptr, s.H, BH, L.lchunks, per, tot_h, st)) != hipSuccess) return e;
-  // H h, phi(q).z, phi(q).H h per query
-  const dim3 grow((unsigned)((s.N + 63) / 64), (unsigned)BH);
-  hipLaunchKernelGGL((lin_rowvec_kernel<D, 0>), grow, dim3(256), 0, st, G, tot_h, Q, s.N, QP, U, t1, t2);
+  // H h per query
+  const dim3 gsplit((unsigned)((D / 32 * D / 16 * 64 + 255) / 256), (unsigned)BH);
+  const dim3 grow((unsigned)((s.N + 4 * RV_GPW * 32 - 1) / (4 * RV_GPW * 32)), (unsigned)BH);
+  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_h, 0, frag);
+  hipLaunchKernelGGL((lin_rowvec_kernel<D, 0>), grow, dim3(256), 0, st, G, frag, tot_h, s.N, U);
   // rows: den, D~ and dq
   hipLaunchKernelGGL((lin_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, A, F, V, G, Q,
-                     rp, ci, U, t1, t2, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, s.N, s.Nq,
-                     s.Nk);
+                     rp, ci, U, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, s.N, s.Nq, s.Nk);
   // M = sum a (h / den)^T, m = sum (D~ / den) a
   hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, Q, G, invden,
                      dtq, s.N, QP, L.lchunks, part);
   if ((e = launch_summary_reduce(part, nullptr, s.H, BH, L.lchunks, per, tot_m, st)) != hipSuccess) return e;
   // M^T phi(k), M v - m per key
-  hipLaunchKernelGGL((lin_rowvec_kernel<D, 1>), grow, dim3(256), 0, st, K, tot_m, (const uint16_t*)nullptr, s.N, QP,
-                     Yv, (float*)nullptr, (float*)nullptr);
-  hipLaunchKernelGGL((lin_rowvec_kernel<D, 2>), grow, dim3(256), 0, st, V, tot_m, (const uint16_t*)nullptr, s.N, QP,
-                     Yk, (float*)nullptr, (float*)nullptr);
+  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_m, 1, frag);
+  hipLaunchKernelGGL((lin_rowvec_kernel<D, 1>), grow, dim3(256), 0, st, F, frag, tot_m, s.N, Yv);
+  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_m, 0, frag);
+  hipLaunchKernelGGL((lin_rowvec_kernel<D, 2>), grow, dim3(256), 0, st, V, frag, tot_m, s.N, Yk);
   // keys: dk, dv
   const int* col_ptr = reinterpret_cast<const int*>(ws + L.col_ptr);
   const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
