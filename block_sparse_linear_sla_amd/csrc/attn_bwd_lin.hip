@@ -24,8 +24,8 @@
 // Kernels:
 //   lin_phi_kernel     phi(Q), phi(K) as bf16 rows (the matrix-core tiles);
 //   lin_outer_kernel   chunk partials of R = sum_t x_t y_t^T and s = sum_t
-//                      c_t x_t per head (x = phi(rows), y = rows times a per-row
-//                      scale) - (H, z) and (M, m); summed by the chunk reduction;
+//                      e_t x_t per head on the matrix cores - (H, z) and (M, m);
+//                      summed by the chunk reduction;
 //   lin_split_kernel   a total as hi + lo bf16 matrix-core fragments;
 //   lin_rowvec_kernel  y_t = R x_t per row on the matrix cores: H h per query,
 //                      M^T phi(k) and M v - m per key;
@@ -82,84 +82,120 @@ __global__ __launch_bounds__(256) void lin_phi_kernel(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------------------ totals
-// Partials over rows [chunk * LROWS, ...) of one head: R = sum_t phi(x_t) (ys_t
-// y_t)^T (D x D, row-major) and s = sum_t ss_t phi(x_t), with ys = 1 / den and
-// ss = D~ / den from the per-query arrays [bh * QP + t] (both 1 when inv is
-// null).  Thread (tr, tc) owns RB x RB outputs.
+// Partials over rows [chunk * LROWS, ...) of one head, on the matrix cores:
+// R = sum_t (c_t phi(x_t)) y_t^T (D x D, row-major) and s = sum_t e_t c_t
+// phi(x_t), x and y bf16 rows (x = K, y = V: H and z, c = e = 1; x = Q,
+// y = dO_l: M and m, c = 1 / den, e = D~ from the per-query arrays
+// [bh * QP + t], which hold 0 past N).  The 64-row units stream through two
+// LDS stages; both operands are transposed reads of the row-major tiles
+// (row t in the contraction): A = the x^T fragments of the wavefront's row
+// tile of R, turned into c phi(x) in float32 and split into hi + lo bf16
+// (two products, so that the totals keep about 2^-17 relative accuracy), and
+// B = the y^T fragments of its column tiles.  Lanes keep the vector sums of
+// their A elements in float32.
 template <int D>
-__global__ __launch_bounds__(256) void lin_outer_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
-                                                        const float* __restrict__ inv, const float* __restrict__ dtq,
-                                                        int N, long long QP, int nchunk, float* __restrict__ part) {
-  constexpr int RB = D / 16, SC = 32, CPR = D / 8;
-  __shared__ float xs[SC][D];
-  __shared__ float yv[SC][D];
-  __shared__ float sw[SC];
+__global__ __launch_bounds__(256, 2) void lin_outer_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Y,
+                                                           const float* __restrict__ inv,
+                                                           const float* __restrict__ dtq, int N, long long QP,
+                                                           int nchunk, float* __restrict__ part) {
+  using T = Tiles<D>;
+  using LP = LoadPlan<D, 4>;
+  constexpr int NT = D / 32, TPW = NT * NT / 4;
+  constexpr int STAGE = 2 * T::KT_BYTES;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const ReadPlan<D> rdp(lane);
   const long long bh = blockIdx.y;
   const int chunk = blockIdx.x;
-  const int tr = threadIdx.x / 16, tc = threadIdx.x % 16;
-  const int r0 = chunk * LROWS, r1 = min(N, r0 + LROWS);
-  float acc[RB][RB], sacc[RB];
+  const int r0 = chunk * LROWS;
+  const int nun = (min(LROWS, N - r0) + KU - 1) / KU;
+  const int gt0 = w * TPW;  // this wavefront's tiles gt0 .. gt0 + TPW - 1 (one row tile)
+  const int at = gt0 / NT;
+  const bool sown = gt0 % NT == 0;  // keeps the vector sums of row tile at
+  const auto rx = buf_rsrc(X + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+  const auto ry = buf_rsrc(Y + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
+  f32x16 acc[TPW];
 #pragma unroll
-  for (int a = 0; a < RB; ++a) {
-    sacc[a] = 0.f;
+  for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
+  float sp = 0.f;
+  auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
+    const LP lp(w, opaque(lane));
+    lp.load(rx, r0 + x * KU, sb);
+    lp.load(ry, r0 + x * KU, sb + T::KT_BYTES);
+  };
+  auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+    wait_vm<0>();
+    __syncthreads();
+    if (x + 1 < nun) issue(x + 1, nxt);
+    const int t0 = r0 + x * KU;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) acc[a][b] = 0.f;
-  }
-  for (int t0 = r0; t0 < r1; t0 += SC) {
-    __syncthreads();  // the previous sub-chunk is consumed
-    for (int g = threadIdx.x; g < SC * CPR; g += 256) {
-      const int rr = g / CPR, cc = g % CPR, t = t0 + rr;
-      float x[8], y[8];
-      if (t < r1) {
-        const size_t o = ((size_t)bh * N + t) * D + cc * 8;
-        unpack8(*reinterpret_cast<const uint4*>(X + o), x);
-        unpack8(*reinterpret_cast<const uint4*>(Y + o), y);
-        const float sy = inv ? inv[bh * QP + t] : 1.f;
+    for (int pl = 0; pl < 4; ++pl) {
+      // element e of a plane fragment: row 16 pl + 4 hi + e % 4 + 8 (e / 4);
+      // rows past N are zero in the tile, and phi(0) = 1 is cancelled by c = 0
+      // (M) or by the row mask below (H)
+      const uint4 av = __builtin_bit_cast(uint4, rdp.vt(cur, at, pl));
+      float xs[8];
+      if (inv != nullptr) {
+        const size_t tq = (size_t)bh * QP + t0 + 16 * pl + 4 * hi;
+        const float4 i0 = *reinterpret_cast<const float4*>(inv + tq);
+        const float4 i1 = *reinterpret_cast<const float4*>(inv + tq + 8);
+        const float4 e0 = *reinterpret_cast<const float4*>(dtq + tq);
+        const float4 e1 = *reinterpret_cast<const float4*>(dtq + tq + 8);
+        const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[e] = phi(x[e]);
-          y[e] *= sy;
+          xs[e] = phi(bf2f(elem(av, e))) * iv[e];
+          if (sown) sp = fmaf(xs[e], ev[e], sp);
         }
       } else {
+        const int lim = N - (t0 + 16 * pl + 4 * hi);  // element e is a row when e%4 + 8 (e/4) < lim
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = y[e] = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          xs[e] = (e % 4) + 8 * (e / 4) < lim ? phi(bf2f(elem(av, e))) : 0.f;
+          if (sown) sp += xs[e];
+        }
       }
+      uint32_t h[4], l[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xs[rr][cc * 8 + e] = x[e];
-        yv[rr][cc * 8 + e] = y[e];
+      for (int e = 0; e < 4; ++e) {
+        h[e] = pk_bf16(xs[2 * e], xs[2 * e + 1]);
+        l[e] = pk_bf16(xs[2 * e] - bf2f(h[e] & 0xffffu), xs[2 * e + 1] - bf2f(h[e] >> 16));
       }
-      if (cc == 0) sw[rr] = t < r1 ? (inv ? dtq[bh * QP + t] * inv[bh * QP + t] : 1.f) : 0.f;
-    }
-    __syncthreads();
-    for (int rr = 0; rr < SC; ++rr) {
-      float xr[RB], yc[RB];
+      const bf16x8 ah = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+      const bf16x8 al = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
 #pragma unroll
-      for (int a = 0; a < RB; ++a) {
-        xr[a] = xs[rr][tr * RB + a];
-        yc[a] = yv[rr][tc * RB + a];
-      }
-#pragma unroll
-      for (int a = 0; a < RB; ++a)
-#pragma unroll
-        for (int b = 0; b < RB; ++b) acc[a][b] = fmaf(xr[a], yc[b], acc[a][b]);
-      if (tc == 0) {
-        const float c = sw[rr];
-#pragma unroll
-        for (int a = 0; a < RB; ++a) sacc[a] = fmaf(xr[a], c, sacc[a]);
+      for (int u = 0; u < TPW; ++u) {
+        const bf16x8 b = rdp.vt(cur + T::KT_BYTES, (gt0 + u) % NT, pl);
+        acc[u] = mfma(ah, b, acc[u]);
+        acc[u] = mfma(al, b, acc[u]);
       }
     }
+  };
+  if (nun > 0) {
+    issue(0, st0);
+    int x = 0;
+    for (; x + 2 <= nun; x += 2) {
+      step(x, st0, st1);
+      step(x + 1, st1, st0);
+    }
+    if (x < nun) step(x, st0, st1);
+    wait_vm<0>();
   }
+  // element i of tile u: R row 32 at + 8 (i/4) + 4 hi + i%4, column 32 bt + lane % 32
   const size_t per = (size_t)D * D + D;
   float* out = part + ((size_t)bh * nchunk + chunk) * per;
 #pragma unroll
-  for (int a = 0; a < RB; ++a)
+  for (int u = 0; u < TPW; ++u) {
+    const int bt = (gt0 + u) % NT;
 #pragma unroll
-    for (int b = 0; b < RB; ++b) out[(tr * RB + a) * D + tc * RB + b] = acc[a][b];
-  if (tc == 0) {
-#pragma unroll
-    for (int a = 0; a < RB; ++a) out[D * D + tr * RB + a] = sacc[a];
+    for (int i = 0; i < 16; ++i)
+      out[(size_t)(32 * at + 8 * (i >> 2) + 4 * hi + (i & 3)) * D + 32 * bt + (lane & 31)] = acc[u][i];
   }
+  const float st = sp + __shfl_xor(sp, 32);
+  if (sown && hi == 0) out[(size_t)D * D + 32 * at + (lane & 31)] = st;
 }
 
 // One head's D x D total R (row-major in tot) as the B operands of y_t = R' x_t
