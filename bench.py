@@ -297,7 +297,7 @@ def main():
                       # branch's: mask transpose, phi tiles, the four per-head
                       # float32 products and the listed-pair row and column walks
                       "linear_bwd_ms": t_lb,
-                      "linear_kernels": "lin_phi + lin_outer x2 + lin_rowvec x3 + lin_dq + lin_dkdv"}
+                      "linear_kernels": "csc_* + lin_phi + lin_outer x2 + lin_split x3 + lin_dq + lin_dkdv"}
 
     # SoftTop-k weights of every mask row (pool + logits + threshold solve),
     # the router-training form of the selection, at temperature 0.5

@@ -556,10 +556,7 @@ BwdLayout bwd_layout(const Shape& s) {
   L.lchunks = (s.N + LROWS - 1) / LROWS;
   L.phiq = take(rows * 2);
   L.phik = take(rows * 2);
-  L.U = take(rows * sizeof(float));
-  L.Yv = take(rows * sizeof(float));
-  L.Yk = take(rows * sizeof(float));
-  L.rsplit = take(BH * (size_t)(s.d / 32) * (s.d / 16) * 2 * 64 * 16);
+  L.rsplit = take(2 * BH * (size_t)(s.d / 32) * (s.d / 16) * 2 * 64 * 16);
   L.invden = take((size_t)s.R() * s.bq * sizeof(float));
   L.dt = take((size_t)s.R() * s.bq * sizeof(float));
   L.tot_h = take(BH * per * sizeof(float));

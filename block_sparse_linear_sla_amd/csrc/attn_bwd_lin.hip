@@ -27,15 +27,15 @@
 //                      e_t x_t per head on the matrix cores - (H, z) and (M, m);
 //                      summed by the chunk reduction;
 //   lin_split_kernel   a total as hi + lo bf16 matrix-core fragments;
-//   lin_rowvec_kernel  y_t = R x_t per row on the matrix cores: H h per query,
-//                      M^T phi(k) and M v - m per key;
-//   lin_dq_kernel      per mask row: pass A sums w and w (h . v) over the listed
-//                      units, then den = a . z - sum w and den D~ = a . H h -
-//                      sum w (h . v); pass B accumulates phi(K)^T (h . v - D~);
-//                      then dq from the totals;
+//   lin_dq_kernel      per mask row: U = H h on the matrix cores from the
+//                      fragments of H; pass A sums w and w (h . v) over the
+//                      listed units, then den = a . z - sum w and den D~ =
+//                      a . U - sum w (h . v); pass B subtracts phi(K)^T
+//                      (h . v - D~) from U; then dq;
 //   lin_dkdv_kernel    per 64-key unit over the rows that list it: P~ and dw in
 //                      registers, dV^T += h^T P~ and dphi^T += phi(Q)^T dw, then
-//                      dk, dv from the totals.
+//                      dv = M^T phi(k) - dV and dphi = M v - m - dphi with the
+//                      products on the matrix cores from the fragments of M^T, M.
 #include "sla.h"
 #include "sla_internal.h"
 #include "bf16_tiles.h"
@@ -235,77 +235,19 @@ __global__ __launch_bounds__(256) void lin_split_kernel(const float* __restrict_
   dst[64] = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
-// y_t = R' x_t for the rows of one head, on the matrix cores (x bf16 rows,
-// R' from lin_split_kernel, float32 results [bh][N][D]):
-//   MODE 0: x = dO_l rows, R' = H  -> U = H h per query;
-//   MODE 1: x = phi(k) rows, R' = M^T -> M^T phi(k) per key;
-//   MODE 2: x = v rows, R' = M, minus m (the vector part of tot) -> M v - m.
-// Each wavefront takes 32-row groups: A = the rows' fragments (16 bytes per
-// lane and k step, straight from HBM), B = the fragments staged in LDS once
-// per workgroup; lane l of the result holds column o = 32 dt + l % 32 of
-// rows 8 (i/4) + 4 (l/32) + i%4, so a store covers 32 consecutive floats of a row.
-constexpr int RV_GPW = 2;  // 32-row groups per wavefront
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void lin_rowvec_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ frag,
-                                                         const float* __restrict__ tot, int N,
-                                                         float* __restrict__ out) {
-  constexpr int NDT = D / 32, NKK = D / 16, NF = NDT * NKK * 2;
-  __shared__ uint4 bfr[NF * 64];
-  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const long long bh = blockIdx.y;
-  const uint4* src = frag + (size_t)bh * NF * 64;
-  for (int g = tid; g < NF * 64; g += 256) bfr[g] = src[g];
-  __syncthreads();
-  const float* mv = tot + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
-#pragma unroll 1
-  for (int grp = 0; grp < RV_GPW; ++grp) {
-    const int t0 = (blockIdx.x * 4 * RV_GPW + grp * 4 + w) * 32;
-    if (t0 >= N) break;
-    const int t = t0 + (lane & 31);
-    bf16x8 a[NKK];
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < N) v = *reinterpret_cast<const uint4*>(X + ((size_t)bh * N + t) * D + 16 * kk + 8 * hi);
-      a[kk] = as_bf16x8(v);
-    }
-    f32x16 acc[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const uint4* fb = bfr + (size_t)(2 * (dt * NKK + kk)) * 64 + lane;
-        acc[dt] = mfma(a[kk], as_bf16x8(fb[0]), acc[dt]);
-        acc[dt] = mfma(a[kk], as_bf16x8(fb[64]), acc[dt]);
-      }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int o = 32 * dt + (lane & 31);
-      const float sub = MODE == 2 ? mv[o] : 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = t0 + 8 * (i >> 2) + 4 * hi + (i & 3);
-        if (r < N) out[((size_t)bh * N + r) * D + o] = acc[dt][i] - sub;
-      }
-    }
-  }
-}
-
 // ------------------------------------------------------------------ dq
 template <int D, int BQ, int SUB>
 __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Qraw, const int* __restrict__ row_ptr,
-    const int* __restrict__ col_idx, const float* __restrict__ U, const float* __restrict__ tot_h,
+    const int* __restrict__ col_idx, const uint4* __restrict__ fragH, const float* __restrict__ tot_h,
     float* __restrict__ invden_out,
     float* __restrict__ dt_out, uint16_t* __restrict__ dQ, int add, int N, int Nq, int Nk) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
   using LP = LoadPlan<D, NW>;
   constexpr int STAGE = 2 * T::KT_BYTES;
+  constexpr int NDT = D / 32, NKK = D / 16;
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
 
@@ -323,37 +265,50 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   const bool qv = q < N;
   const size_t qidx = (size_t)row * BQ + 32 * w + (lane & 31);  // per-query arrays
 
-  bf16x8 af[D / 16], hf[D / 16];
+  bf16x8 af[NKK], hf[NKK];
   load_q<D>(A, bh, q, N, hi, af);
   load_q<D>(G, bh, q, N, hi, hf);
-  f32x16 acc[D / 32];
+  // acc^T starts as U^T = (H h)^T for this wavefront's queries (H as hi + lo
+  // fragments; element i of tile dt: d = 32 dt + 8 (i/4) + 4 hi + i%4) and
+  // ends as U - sum_sel (h . v - D~) phi(k)
+  f32x16 acc[NDT];
+  {
+    const uint4* fh = fragH + (size_t)bh * (2 * NDT * NKK * 64) + lane;
 #pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    for (int dt = 0; dt < NDT; ++dt) {
+      acc[dt] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int f = 2 * (dt * NKK + kk) * 64;
+        acc[dt] = mfma(as_bf16x8(fh[f]), hf[kk], acc[dt]);
+        acc[dt] = mfma(as_bf16x8(fh[f + 64]), hf[kk], acc[dt]);
+      }
+    }
+  }
   float sw = 0.f, swh = 0.f;  // this lane's sums of w and w (h . v) over its listed keys
   float inv = 0.f, dtv = 0.f;  // 1 / den and D~ (0 for a row without a linear branch)
   const size_t qrow = ((size_t)bh * N + (qv ? q : 0)) * D;
   const float* z = tot_h + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
-  // phi(q) . z and phi(q) . (H h) over this lane's half of d (the 8-d slices
-  // 16 t + 8 hi of its fragments); the two halves are added in settle
+  // phi(q) . z and phi(q) . (H h) over this lane's d of the accumulator
+  // tiles; the two halves (lanes l, l^32) are added in settle
   float p1 = 0.f, p2 = 0.f;
   if (qv) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      const int d0 = 16 * t + 8 * hi;
-      const uint4 av = __builtin_bit_cast(uint4, af[t]);
+    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float4 u4 = *reinterpret_cast<const float4*>(U + qrow + d0 + 4 * c);
-        const float4 z4 = *reinterpret_cast<const float4*>(z + d0 + 4 * c);
-        const float uu[4] = {u4.x, u4.y, u4.z, u4.w}, zz[4] = {z4.x, z4.y, z4.z, z4.w};
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = 32 * dt + 8 * a + 4 * hi;
+        const uint2 q2 = *reinterpret_cast<const uint2*>(Qraw + qrow + d0);
+        const float4 z4 = *reinterpret_cast<const float4*>(z + d0);
+        const float qq[4] = {bf2f(q2.x & 0xffffu), bf2f(q2.x >> 16), bf2f(q2.y & 0xffffu), bf2f(q2.y >> 16)};
+        const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float ae = bf2f(elem(av, 4 * c + e));
-          p1 = fmaf(ae, zz[e], p1);
-          p2 = fmaf(ae, uu[e], p2);
+        for (int c = 0; c < 4; ++c) {
+          const float fq = phi(qq[c]);
+          p1 = fmaf(fq, zz[c], p1);
+          p2 = fmaf(fq, acc[dt][4 * a + c], p2);
         }
       }
-    }
   }
   auto settle = [&]() {
     const float SW = sw + __shfl_xor(sw, 32), SWH = swh + __shfl_xor(swh, 32);
@@ -393,10 +348,10 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
             swh = fmaf(s[i], dp[i], swh);
           }
         } else {
-          // pass B: phi(K)^T (h . v - D~) over this half's two key planes
+          // pass B: acc -= phi(K)^T (h . v - D~) over this half's two key planes
           float c[16];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) c[i] = dp[i] - dtv;
+          for (int i = 0; i < 16; ++i) c[i] = dtv - dp[i];
           bf16x8 bp[2];
           pack_planes(c, bp);
 #pragma unroll
@@ -429,21 +384,19 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
     dt_out[qidx] = dtv;
   }
   if (!qv) return;
-  // da = (U - D~ z - acc) / den; dq = phi'(q) o da (element i of tile dt:
-  // d = 32 dt + 8 (i/4) + 4 hi + i%4)
+  // da = (acc - D~ z) / den; dq = phi'(q) o da
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * dt + 8 * a + 4 * hi;
-      const float4 u4 = *reinterpret_cast<const float4*>(U + qrow + d0);
       const float4 z4 = *reinterpret_cast<const float4*>(z + d0);
       const uint2 q2 = *reinterpret_cast<const uint2*>(Qraw + qrow + d0);
-      const float uu[4] = {u4.x, u4.y, u4.z, u4.w}, zz[4] = {z4.x, z4.y, z4.z, z4.w};
+      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
       const float qq[4] = {bf2f(q2.x & 0xffffu), bf2f(q2.x >> 16), bf2f(q2.y & 0xffffu), bf2f(q2.y >> 16)};
       float o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = dphi(qq[c]) * ((uu[c] - dtv * zz[c] - acc[dt][4 * a + c]) * inv);
+      for (int c = 0; c < 4; ++c) o[c] = dphi(qq[c]) * ((acc[dt][4 * a + c] - dtv * zz[c]) * inv);
       put4(dQ + qrow + d0, o, add != 0);
     }
 }
@@ -454,7 +407,8 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Kraw, const int* __restrict__ col_ptr,
     const int* __restrict__ row_idx, const float* __restrict__ invden, const float* __restrict__ dtq,
-    const float* __restrict__ Yv, const float* __restrict__ Yk, uint16_t* __restrict__ dK,
+    const uint4* __restrict__ fragMT, const uint4* __restrict__ fragM, const float* __restrict__ tot_m,
+    uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, int add, int N, int Nq, int Nk) {
   using T = Tiles<D>;
   using LP = LoadPlan<D, 4>;
@@ -565,29 +519,44 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
     if (x < nunits) step(x, st0, st1);
     wait_vm<0>();
   }
-  if (!kv) return;
-  // dv = Yv - acc_v; dphi = Yk - acc_k; dk = phi'(k) o dphi (element i of tile
-  // t: d = 32 (NDT dh + t) + 8 (i/4) + 4 hi + i%4)
-  const size_t krow = ((size_t)bh * N + key) * D;
+  // dv = M^T phi(k) - acc_v and dphi = M v - m - acc_k, the products with M
+  // on the matrix cores (M^T and M as hi + lo fragments, phi(k) and v from
+  // this lane's key fragments); dk = phi'(k) o dphi.  Element i of tile t:
+  // d = 32 (NDT dh + t) + 8 (i/4) + 4 hi + i%4
+  constexpr int NKK = D / 16;
+  const size_t fb = (size_t)bh * (2 * (D / 32) * NKK * 64) + lane;
+  const float* mv = tot_m + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
+  const size_t krow = ((size_t)bh * N + (kv ? key : 0)) * D;
 #pragma unroll
-  for (int t = 0; t < NDT; ++t)
+  for (int t = 0; t < NDT; ++t) {
+    const int dt = NDT * dh + t;
+    f32x16 yv = f32x16{}, yk = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const size_t f = fb + (size_t)(2 * (dt * NKK + kk)) * 64;
+      yv = mfma(as_bf16x8(fragMT[f]), ff[kk], yv);
+      yv = mfma(as_bf16x8(fragMT[f + 64]), ff[kk], yv);
+      yk = mfma(as_bf16x8(fragM[f]), vf[kk], yk);
+      yk = mfma(as_bf16x8(fragM[f + 64]), vf[kk], yk);
+    }
+    if (!kv) continue;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * (NDT * dh + t) + 8 * a + 4 * hi;
-      const float4 yv = *reinterpret_cast<const float4*>(Yv + krow + d0);
-      const float4 yk = *reinterpret_cast<const float4*>(Yk + krow + d0);
+      const int d0 = 32 * dt + 8 * a + 4 * hi;
+      const float4 m4 = *reinterpret_cast<const float4*>(mv + d0);
       const uint2 k2 = *reinterpret_cast<const uint2*>(Kraw + krow + d0);
-      const float YV[4] = {yv.x, yv.y, yv.z, yv.w}, YK[4] = {yk.x, yk.y, yk.z, yk.w};
-      const float kk[4] = {bf2f(k2.x & 0xffffu), bf2f(k2.x >> 16), bf2f(k2.y & 0xffffu), bf2f(k2.y >> 16)};
+      const float MM[4] = {m4.x, m4.y, m4.z, m4.w};
+      const float kk4[4] = {bf2f(k2.x & 0xffffu), bf2f(k2.x >> 16), bf2f(k2.y & 0xffffu), bf2f(k2.y >> 16)};
       float ov[4], ok[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        ov[c] = YV[c] - adv[t][4 * a + c];
-        ok[c] = dphi(kk[c]) * (YK[c] - adk[t][4 * a + c]);
+        ov[c] = yv[4 * a + c] - adv[t][4 * a + c];
+        ok[c] = dphi(kk4[c]) * (yk[4 * a + c] - MM[c] - adk[t][4 * a + c]);
       }
       put4(dV + krow + d0, ov, add != 0);
       put4(dK + krow + d0, ok, add != 0);
     }
+  }
 }
 
 template <int D, int BQ, int SUB>
@@ -602,10 +571,8 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   const uint16_t* G = static_cast<const uint16_t*>(dOv);
   uint16_t* A = reinterpret_cast<uint16_t*>(ws + L.phiq);
   uint16_t* F = reinterpret_cast<uint16_t*>(ws + L.phik);
-  float* U = reinterpret_cast<float*>(ws + L.U);
-  float* Yv = reinterpret_cast<float*>(ws + L.Yv);
-  float* Yk = reinterpret_cast<float*>(ws + L.Yk);
-  uint4* frag = reinterpret_cast<uint4*>(ws + L.rsplit);
+  uint4* frag0 = reinterpret_cast<uint4*>(ws + L.rsplit);
+  uint4* frag1 = frag0 + (size_t)BH * (2 * (D / 32) * (D / 16) * 64);
   float* invden = reinterpret_cast<float*>(ws + L.invden);
   float* dtq = reinterpret_cast<float*>(ws + L.dt);
   float* tot_h = reinterpret_cast<float*>(ws + L.tot_h);
@@ -620,28 +587,25 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, K, V,
                      (const float*)nullptr, (const float*)nullptr, s.N, QP, L.lchunks, part);
   if ((e = launch_summary_reduce(part, nullptr, s.H, BH, L.lchunks, per, tot_h, st)) != hipSuccess) return e;
-  // H h per query
+  // H as matrix-core fragments for the rows' H h
   const dim3 gsplit((unsigned)((D / 32 * D / 16 * 64 + 255) / 256), (unsigned)BH);
-  const dim3 grow((unsigned)((s.N + 4 * RV_GPW * 32 - 1) / (4 * RV_GPW * 32)), (unsigned)BH);
-  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_h, 0, frag);
-  hipLaunchKernelGGL((lin_rowvec_kernel<D, 0>), grow, dim3(256), 0, st, G, frag, tot_h, s.N, U);
+  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_h, 0, frag0);
   // rows: den, D~ and dq
   hipLaunchKernelGGL((lin_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, A, F, V, G, Q,
-                     rp, ci, U, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, s.N, s.Nq, s.Nk);
-  // M = sum a (h / den)^T, m = sum (D~ / den) a
+                     rp, ci, frag0, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, s.N, s.Nq, s.Nk);
+  // M = sum (phi(q) / den) h^T, m = sum (D~ / den) phi(q)
   hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, Q, G, invden,
                      dtq, s.N, QP, L.lchunks, part);
   if ((e = launch_summary_reduce(part, nullptr, s.H, BH, L.lchunks, per, tot_m, st)) != hipSuccess) return e;
-  // M^T phi(k), M v - m per key
-  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_m, 1, frag);
-  hipLaunchKernelGGL((lin_rowvec_kernel<D, 1>), grow, dim3(256), 0, st, F, frag, tot_m, s.N, Yv);
-  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_m, 0, frag);
-  hipLaunchKernelGGL((lin_rowvec_kernel<D, 2>), grow, dim3(256), 0, st, V, frag, tot_m, s.N, Yk);
+  // M^T and M as fragments for the keys' M^T phi(k) and M v
+  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_m, 1, frag0);
+  hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_m, 0, frag1);
   // keys: dk, dv
   const int* col_ptr = reinterpret_cast<const int*>(ws + L.col_ptr);
   const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
   hipLaunchKernelGGL((lin_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, A, F, V, G,
-                     K, col_ptr, row_idx, invden, dtq, Yv, Yk, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
+                     K, col_ptr, row_idx, invden, dtq, frag0, frag1, tot_m, static_cast<uint16_t*>(dK),
+                     static_cast<uint16_t*>(dV),
                      add ? 1 : 0, s.N, s.Nq, s.Nk);
   return hipGetLastError();
 }

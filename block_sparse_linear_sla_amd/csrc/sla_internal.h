@@ -62,8 +62,7 @@ struct BwdLayout {
   size_t apart;    // double [B*H][achunks]: partial sums of the alpha gradient
   // linear-branch backward
   size_t phiq, phik;    // bf16 [B*H][N][d]: phi(Q), phi(K)
-  size_t U, Yv, Yk;     // float [B*H][N][d]: H h per query; M^T phi(k), M v - m per key
-  size_t rsplit;        // uint4 [B*H][(d/32)(d/16)*2][64]: one total as hi + lo bf16 matrix-core fragments
+  size_t rsplit;        // uint4 2 x [B*H][(d/32)(d/16)*2][64]: two totals as hi + lo bf16 matrix-core fragments
   size_t invden, dt;    // float [R*bq]: 1 / linear denominator and h.O_l per query (0 where undefined)
   size_t tot_h, tot_m;  // float [B*H][d*d + d]: (H, z) and (M, m), row-major
   size_t lpart;         // float [B*H][lchunks][d*d + d]: chunk partials of those totals
