@@ -273,7 +273,9 @@ def main():
         torch.cuda.synchronize()
         S.sla_linear_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads, accumulate=True)
         torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        S.sla_attn_bwd(q, k, v, dO, alpha, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         e[0].record()
         for _ in range(args.steps):
             S.sla_sparse_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
@@ -284,6 +286,9 @@ def main():
         for _ in range(args.steps):
             S.sla_linear_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads, accumulate=True)
         e[3].record()
+        for _ in range(args.steps):
+            S.sla_attn_bwd(q, k, v, dO, alpha, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
+        e[4].record()
         torch.cuda.synchronize()
         t_b = e[0].elapsed_time(e[1]) / args.steps
         t_lb = e[2].elapsed_time(e[3]) / args.steps
@@ -297,6 +302,9 @@ def main():
                       # branch's: mask transpose, phi tiles, the four per-head
                       # float32 products and the listed-pair row and column walks
                       "linear_bwd_ms": t_lb,
+                      # the mixed output's gradient (both branches, mask
+                      # transpose built once): the training backward
+                      "attn_bwd_ms": e[3].elapsed_time(e[4]) / args.steps,
                       "linear_kernels": "csc_* + lin_phi + lin_outer x2 + lin_split x3 + lin_dq + lin_dkdv"}
 
     # SoftTop-k weights of every mask row (pool + logits + threshold solve),

@@ -26,7 +26,7 @@ STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
 EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_soft_topk", "sla_sparse_fwd",
            "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
            "sla_dense_fwd", "sla_i8_layout_of", "sla_quantize_i8", "sla_sparse_fwd_i8",
-           "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_linear_bwd", "sla_alpha_grad",
+           "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_linear_bwd", "sla_attn_bwd", "sla_alpha_grad",
            "sla_status_string")
 
 
@@ -84,13 +84,14 @@ def lib() -> ctypes.CDLL:
         L.sla_sparse_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_linear_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
                                      vp]
+        L.sla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_alpha_grad.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
         for fn in ("sla_mask", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
                    "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd", "sla_i8_layout_of",
                    "sla_quantize_i8", "sla_sparse_fwd_i8", "sla_sparse_bwd", "sla_linear_bwd",
-                   "sla_alpha_grad"):
+                   "sla_attn_bwd", "sla_alpha_grad"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -352,6 +353,21 @@ def sla_linear_bwd(q, k, v, do_l, bq: int, bk: int, row_ptr, col_idx, ws=None, o
     _check("sla_linear_bwd", lib().sla_linear_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do_l),
                                                   _ptr(row_ptr), _ptr(col_idx), _ptr(dq), _ptr(dk), _ptr(dv),
                                                   1 if accumulate else 0, _ptr(w), w.numel(), _stream()))
+    return dq, dk, dv
+
+
+def sla_attn_bwd(q, k, v, do, alpha, bq: int, bk: int, row_ptr, col_idx, ws=None, out=None):
+    """Gradient of sum(O * dO) for O = alpha_h O_s + (1 - alpha_h) O_l with
+    the mask fixed: returns (dQ, dK, dV)."""
+    _need(q, k, v, do, like=q)
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != q.shape[1]:
+        raise ValueError("alpha must be a float32 CUDA tensor of H values")
+    prob = problem(q, bq, bk)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    w = ws if ws is not None else bwd_workspace(prob, q.device)
+    _check("sla_attn_bwd", lib().sla_attn_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                                              _ptr(alpha.contiguous()), _ptr(row_ptr), _ptr(col_idx), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream()))
     return dq, dk, dv
 
 

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int* __restrict__ row_ptr,
     const int* __restrict__ col_idx, uint16_t* __restrict__ dQ, float* __restrict__ lse2_out,
-    float* __restrict__ dd_out, int N, int Nq, int Nk, float scale_log2, float inv_sqrt_d) {
+    float* __restrict__ dd_out, const float* __restrict__ alpha, int H, int N, int Nq, int Nk, float scale_log2,
+    float inv_sqrt_d) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
   using LP = LoadPlan<D, NW>;
@@ -288,7 +289,8 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
     wait_vm<0>();  // nsteps is even
   }
   const size_t qrow = (size_t)bh * N + min(q, N - 1);
-  store_T<D / 32>(acc, inv_sqrt_d, dQ + qrow * D, 0, qv, hi);
+  const float os = alpha != nullptr ? alpha[bh % H] : 1.f;  // the branch's weight in the mixed output
+  store_T<D / 32>(acc, os * inv_sqrt_d, dQ + qrow * D, 0, qv, hi);
   if (hi == 0) {
     const size_t r = (size_t)row * BQ + 32 * w + (lane & 31);
     lse2_out[r] = qv ? lse2 : INFINITY;
@@ -302,7 +304,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int* __restrict__ col_ptr, const int* __restrict__ row_idx,
     const float* __restrict__ lse2, const float* __restrict__ ddv, uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int N, int Nq, int Nk, float scale_log2, float inv_sqrt_d) {
+    uint16_t* __restrict__ dV, const float* __restrict__ alpha, int H, int N, int Nq, int Nk, float scale_log2,
+    float inv_sqrt_d) {
   using T = Tiles<D>;
   using LP = LoadPlan<D, 4>;
   constexpr int STAGE = 2 * T::KT_BYTES;  // Q and dO tiles of 64 queries
@@ -430,8 +433,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     wait_vm<0>();
   }
   const size_t krow = ((size_t)bh * N + min(key, N - 1)) * D;
-  store_T<NDT>(adv, 1.f, dV + krow, 32 * NDT * dh, kv, hi);
-  store_T<NDT>(adk, inv_sqrt_d, dK + krow, 32 * NDT * dh, kv, hi);
+  const float os = alpha != nullptr ? alpha[bh % H] : 1.f;
+  store_T<NDT>(adv, os, dV + krow, 32 * NDT * dh, kv, hi);
+  store_T<NDT>(adk, os * inv_sqrt_d, dK + krow, 32 * NDT * dh, kv, hi);
 }
 
 // ------------------------------------------------------------------ d alpha
@@ -486,8 +490,9 @@ __global__ __launch_bounds__(64) void alpha_sum_kernel(const double* __restrict_
 }
 
 template <int D, int BQ, int SUB>
-hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV,
-                        char* ws, const BwdLayout& L, hipStream_t st) {
+hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* rp,
+                        const int32_t* ci, void* dQ, void* dK, void* dV, const float* alpha, bool csc, char* ws,
+                        const BwdLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const float isd = 1.f / sqrtf((float)D);
@@ -495,18 +500,19 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* ddv = reinterpret_cast<float*>(ws + L.dd);
-  hipError_t e = launch_csc(s, rp, ci, ws, L, st);
-  if (e != hipSuccess) return e;
+  if (csc) {
+    const hipError_t e = launch_csc(s, rp, ci, ws, L, st);
+    if (e != hipSuccess) return e;
+  }
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
   const uint16_t* v = static_cast<const uint16_t*>(V);
   const uint16_t* g = static_cast<const uint16_t*>(dO);
   hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, q, k, v,
-                     g, rp, ci, static_cast<uint16_t*>(dQ), lse2, ddv, s.N,
-                     s.Nq, s.Nk, sl2, isd);
+                     g, rp, ci, static_cast<uint16_t*>(dQ), lse2, ddv, alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, q, k, v,
                      g, col_ptr, row_idx, lse2, ddv, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
-                     s.N, s.Nq, s.Nk, sl2, isd);
+                     alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd);
   return hipGetLastError();
 }
 
@@ -583,10 +589,12 @@ hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, con
   return hipGetLastError();
 }
 
-hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV,
-                             char* ws, const BwdLayout& L, hipStream_t st) {
+hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                             const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, const float* alpha,
+                             bool csc, char* ws, const BwdLayout& L, hipStream_t st) {
 #define SLA_BWD(DD, QQ, KK) \
-  if (s.d == DD && s.bq == QQ && s.bk == KK) return bwd_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, ws, L, st);
+  if (s.d == DD && s.bq == QQ && s.bk == KK) \
+    return bwd_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, alpha, csc, ws, L, st);
   SLA_BWD(128, 128, 64)
   SLA_BWD(128, 128, 128)
   SLA_BWD(128, 64, 64)

@@ -241,8 +241,8 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Qraw, const int* __restrict__ row_ptr,
     const int* __restrict__ col_idx, const uint4* __restrict__ fragH, const float* __restrict__ tot_h,
-    float* __restrict__ invden_out,
-    float* __restrict__ dt_out, uint16_t* __restrict__ dQ, int add, int N, int Nq, int Nk) {
+    float* __restrict__ invden_out, float* __restrict__ dt_out, uint16_t* __restrict__ dQ, int add,
+    const float* __restrict__ alpha, int H, int N, int Nq, int Nk) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
   using LP = LoadPlan<D, NW>;
@@ -384,7 +384,10 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
     dt_out[qidx] = dtv;
   }
   if (!qv) return;
-  // da = (acc - D~ z) / den; dq = phi'(q) o da
+  // da = (acc - D~ z) / den; dq = phi'(q) o da, times the branch's weight in
+  // the mixed output
+  const float os = alpha != nullptr ? 1.f - alpha[bh % H] : 1.f;
+  const float sinv = os * inv;
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -396,7 +399,7 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
       const float qq[4] = {bf2f(q2.x & 0xffffu), bf2f(q2.x >> 16), bf2f(q2.y & 0xffffu), bf2f(q2.y >> 16)};
       float o[4];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] = dphi(qq[c]) * ((acc[dt][4 * a + c] - dtv * zz[c]) * inv);
+      for (int c = 0; c < 4; ++c) o[c] = dphi(qq[c]) * ((acc[dt][4 * a + c] - dtv * zz[c]) * sinv);
       put4(dQ + qrow + d0, o, add != 0);
     }
 }
@@ -408,8 +411,8 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Kraw, const int* __restrict__ col_ptr,
     const int* __restrict__ row_idx, const float* __restrict__ invden, const float* __restrict__ dtq,
     const uint4* __restrict__ fragMT, const uint4* __restrict__ fragM, const float* __restrict__ tot_m,
-    uint16_t* __restrict__ dK,
-    uint16_t* __restrict__ dV, int add, int N, int Nq, int Nk) {
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int add, const float* __restrict__ alpha, int H, int N,
+    int Nq, int Nk) {
   using T = Tiles<D>;
   using LP = LoadPlan<D, 4>;
   constexpr int STAGE = 2 * T::KT_BYTES;  // phi(Q) and h tiles of 64 queries
@@ -527,6 +530,7 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
   const size_t fb = (size_t)bh * (2 * (D / 32) * NKK * 64) + lane;
   const float* mv = tot_m + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
   const size_t krow = ((size_t)bh * N + (kv ? key : 0)) * D;
+  const float os = alpha != nullptr ? 1.f - alpha[bh % H] : 1.f;
 #pragma unroll
   for (int t = 0; t < NDT; ++t) {
     const int dt = NDT * dh + t;
@@ -550,8 +554,8 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
       float ov[4], ok[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        ov[c] = yv[4 * a + c] - adv[t][4 * a + c];
-        ok[c] = dphi(kk4[c]) * (yk[4 * a + c] - MM[c] - adk[t][4 * a + c]);
+        ov[c] = os * (yv[4 * a + c] - adv[t][4 * a + c]);
+        ok[c] = os * dphi(kk4[c]) * (yk[4 * a + c] - MM[c] - adk[t][4 * a + c]);
       }
       put4(dV + krow + d0, ov, add != 0);
       put4(dK + krow + d0, ok, add != 0);
@@ -561,8 +565,8 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
 
 template <int D, int BQ, int SUB>
 hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const void* Vv, const void* dOv,
-                        const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool add, char* ws,
-                        const BwdLayout& L, hipStream_t st) {
+                        const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool add,
+                        const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H;
   const long long QP = (long long)s.Nq * s.bq;  // per-query arrays: [bh * QP + t]
   const uint16_t* Q = static_cast<const uint16_t*>(Qv);
@@ -579,8 +583,8 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   float* tot_m = reinterpret_cast<float*>(ws + L.tot_m);
   float* part = reinterpret_cast<float*>(ws + L.lpart);
   const int per = D * D + D;
-  hipError_t e = launch_csc(s, rp, ci, ws, L, st);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (csc && (e = launch_csc(s, rp, ci, ws, L, st)) != hipSuccess) return e;
   const long long n8 = BH * s.N * D / 8;
   hipLaunchKernelGGL(lin_phi_kernel, dim3((unsigned)((2 * n8 + 255) / 256)), dim3(256), 0, st, Q, K, n8, A, F);
   // H, z
@@ -592,7 +596,8 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   hipLaunchKernelGGL((lin_split_kernel<D>), gsplit, dim3(256), 0, st, tot_h, 0, frag0);
   // rows: den, D~ and dq
   hipLaunchKernelGGL((lin_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, A, F, V, G, Q,
-                     rp, ci, frag0, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, s.N, s.Nq, s.Nk);
+                     rp, ci, frag0, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, alpha, s.H, s.N,
+                     s.Nq, s.Nk);
   // M = sum (phi(q) / den) h^T, m = sum (D~ / den) phi(q)
   hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, Q, G, invden,
                      dtq, s.N, QP, L.lchunks, part);
@@ -605,8 +610,7 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
   hipLaunchKernelGGL((lin_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, A, F, V, G,
                      K, col_ptr, row_idx, invden, dtq, frag0, frag1, tot_m, static_cast<uint16_t*>(dK),
-                     static_cast<uint16_t*>(dV),
-                     add ? 1 : 0, s.N, s.Nq, s.Nk);
+                     static_cast<uint16_t*>(dV), add ? 1 : 0, alpha, s.H, s.N, s.Nq, s.Nk);
   return hipGetLastError();
 }
 
@@ -614,9 +618,10 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
 
 hipError_t launch_linear_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                              const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool accumulate,
-                             char* ws, const BwdLayout& L, hipStream_t st) {
+                             const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st) {
 #define SLA_LBWD(DD, QQ, KK) \
-  if (s.d == DD && s.bq == QQ && s.bk == KK) return lin_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, accumulate, ws, L, st);
+  if (s.d == DD && s.bq == QQ && s.bk == KK) \
+    return lin_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, accumulate, alpha, csc, ws, L, st);
   SLA_LBWD(128, 128, 64)
   SLA_LBWD(128, 128, 128)
   SLA_LBWD(128, 64, 64)

@@ -294,7 +294,7 @@ int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const 
   if (!Q || !K || !V || !dO_s || !row_ptr || !col_idx || !dQ || !dK || !dV) return SLA_ERR_INVALID_ARG;
   const sla::BwdLayout L = sla::bwd_layout(s);
   if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
-  return hip_status(sla::launch_sparse_bwd(s, Q, K, V, dO_s, row_ptr, col_idx, dQ, dK, dV,
+  return hip_status(sla::launch_sparse_bwd(s, Q, K, V, dO_s, row_ptr, col_idx, dQ, dK, dV, nullptr, true,
                                            static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
 }
 
@@ -309,7 +309,26 @@ int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const 
   const sla::BwdLayout L = sla::bwd_layout(s);
   if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
   return hip_status(sla::launch_linear_bwd(s, Q, K, V, dO_l, row_ptr, col_idx, dQ, dK, dV, accumulate != 0,
-                                           static_cast<char*>(ws), L, static_cast<hipStream_t>(stream)));
+                                           nullptr, true, static_cast<char*>(ws), L,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
+                 const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
+                 void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !dO || !alpha || !row_ptr || !col_idx || !dQ || !dK || !dV) return SLA_ERR_INVALID_ARG;
+  const sla::BwdLayout L = sla::bwd_layout(s);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  if (sla::launch_sparse_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, alpha, true, w, L, st) != hipSuccess)
+    return SLA_ERR_HIP;
+  return hip_status(sla::launch_linear_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, true, alpha, false, w, L,
+                                           st));
 }
 
 int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,

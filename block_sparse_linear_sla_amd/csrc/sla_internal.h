@@ -113,18 +113,24 @@ hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, c
                           const int32_t* col_idx, void* O, hipStream_t st);
 
 // attn_bwd.hip: gradient of the sparse branch (bf16) with the mask fixed.
-hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
-                             void* dV, char* ws, const BwdLayout& L, hipStream_t st);
+// alpha (device [H], nullable): the outputs are scaled by alpha_h, the
+// branch's weight in the mixed output; csc: build the mask's transpose into
+// ws first (else it is already there, from a call on the same mask).
+hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
+                             const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
+                             const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st);
 hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
                              char* ws, const BwdLayout& L, hipStream_t st);
 // the mask's transpose (CSC) into the backward workspace
 hipError_t launch_csc(const Shape& s, const int32_t* row_ptr, const int32_t* col_idx, char* ws, const BwdLayout& L,
                       hipStream_t st);
 // attn_bwd_lin.hip: gradient of the linear branch (bf16) with the mask fixed;
-// accumulate: add to dQ, dK, dV instead of writing them
+// accumulate: add to dQ, dK, dV instead of writing them; alpha (nullable):
+// the outputs are scaled by 1 - alpha_h; csc as for the sparse branch.
 hipError_t launch_linear_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                              const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
-                             bool accumulate, char* ws, const BwdLayout& L, hipStream_t st);
+                             bool accumulate, const float* alpha, bool csc, char* ws, const BwdLayout& L,
+                             hipStream_t st);
 
 // attn_f32.hip: linear totals and attention for float32 inputs.
 hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,

@@ -253,6 +253,23 @@ int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const 
                    const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
                    int accumulate, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Backward of the mixed output, mask fixed (SLA2 write-up §二 for
+ * O = alpha_h O_s + (1 - alpha_h) O_l, §四 for training with the selection
+ * fixed per step).  dQ, dK, dV of L = sum(O * dO) with respect to Q, K, V:
+ * the sparse branch's gradient (as sla_sparse_bwd) taken with dO and scaled
+ * by alpha_h, plus the linear branch's (as sla_linear_bwd) taken with dO and
+ * scaled by 1 - alpha_h; both branches' gradients are linear in the
+ * incoming gradient, so the scales are applied to the float32 results.  The
+ * mask's transpose is built once for both.  alpha: float32 [H] (DEVICE),
+ * the forward's mixing ratios.  bf16 only.  Outputs dQ, dK, dV [B, H, N, d]
+ * bf16, every element written (the sparse part rounded to bf16, the linear
+ * part added and rounded again).  Needs the sla_bwd_workspace_bytes
+ * workspace.  The gradient with respect to alpha is sla_alpha_grad's.
+ * Deterministic: no atomics. */
+int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
+                 const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
+                 void* ws, size_t ws_bytes, void* stream);
+
 /* Gradient of sum(O * dO) with respect to alpha for O = alpha_h O_s +
  * (1 - alpha_h) O_l (SLA2 write-up §二): dalpha[h] = sum over the head's
  * tokens of dO . (O_s - O_l), float64 partial sums in a fixed order, written

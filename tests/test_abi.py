@@ -230,3 +230,27 @@ def test_bwd_checks():
         a[i] = None
         assert L.sla_alpha_grad(ctypes.byref(p32), *a, FAKE, n, None) == INVALID, i
     assert L.sla_alpha_grad(ctypes.byref(p16), FAKE, FAKE, FAKE, FAKE, FAKE, n - 1, None) == WORKSPACE
+
+
+def test_linear_and_mixed_bwd_checks():
+    L = S.lib()
+    p32 = prob()
+    p16 = prob(dtype=S.SLA_BF16)
+    n = L.sla_bwd_workspace_bytes(ctypes.byref(p16))
+    lin = [FAKE] * 9
+    assert L.sla_linear_bwd(ctypes.byref(p32), *lin, 0, FAKE, n, None) == UNSUPPORTED
+    for i in range(9):
+        a = list(lin)
+        a[i] = None
+        assert L.sla_linear_bwd(ctypes.byref(p16), *a, 1, FAKE, n, None) == INVALID, i
+    assert L.sla_linear_bwd(ctypes.byref(p16), *lin, 0, None, n, None) == WORKSPACE
+    assert L.sla_linear_bwd(ctypes.byref(p16), *lin, 0, FAKE, n - 1, None) == WORKSPACE
+    assert L.sla_linear_bwd(None, *lin, 0, FAKE, n, None) == INVALID
+    mixed = [FAKE] * 10  # Q, K, V, dO, alpha, row_ptr, col_idx, dQ, dK, dV
+    assert L.sla_attn_bwd(ctypes.byref(p32), *mixed, FAKE, n, None) == UNSUPPORTED
+    for i in range(10):
+        a = list(mixed)
+        a[i] = None
+        assert L.sla_attn_bwd(ctypes.byref(p16), *a, FAKE, n, None) == INVALID, i
+    assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, None, n, None) == WORKSPACE
+    assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, FAKE, n - 1, None) == WORKSPACE

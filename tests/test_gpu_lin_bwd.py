@@ -149,3 +149,31 @@ def test_linear_bwd_480p_two_heads():
         relq = np.abs(tq.sum(1)) / np.maximum(np.abs(tq).sum(1), 1e-30)
         print(f"  head {h}: per-query phi(q) . dphi(q): max {relq.max():.3g}, mean {relq.mean():.3g}")
         assert relq.mean() <= 2e-2
+
+
+@pytest.mark.parametrize("N,d,bq,bk", [(1000, 128, 128, 64), (777, 64, 64, 128)])
+def test_attn_bwd_mixed(N, d, bq, bk):
+    """sla_attn_bwd: alpha_h times the sparse branch's gradient plus
+    (1 - alpha_h) times the linear branch's, both taken with dO, on four heads
+    whose ratios include the two ends (alpha = 1: sparse only; 0: linear only)."""
+    print(f"[lin-bwd] mixed N={N} d={d} bq={bq} bk={bk}", flush=True)
+    H = 4
+    wl = gen.Workload("adhoc", B=1, H=H, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+                      dtype="bf16", router=False, seed=31)
+    x = gen.make(wl)
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp, ci = _random_csr(np.random.default_rng(13), H, Nq, Nk, 0.3, empty_rows={2},
+                         full_rows={H * Nq - 1})
+    q, k, v, dO, rpt, cit = _inputs(x, rp, ci, seed=9)
+    alpha = torch.tensor([0.7, 1.0, 0.0, 0.35], dtype=torch.float32)
+    dq, dk, dv = S.sla_attn_bwd(q, k, v, dO.cuda(), alpha.cuda(), bq, bk, rpt, cit)
+    torch.cuda.synchronize()
+    rs = O.sparse_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
+    rl = O.linear_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
+    a = alpha.double().numpy()[None, :, None, None]
+    for t, n in zip((dq, dk, dv), ("dQ", "dK", "dV")):
+        _compare(t, a * rs[n] + (1 - a) * rl[n], n)
+        # the alpha = 1 head carries the sparse branch's gradient alone, the
+        # alpha = 0 head the linear branch's alone
+        _compare(t[:, 1:2], rs[n][:, 1:2], n + " (alpha 1)")
+        _compare(t[:, 2:3], rl[n][:, 2:3], n + " (alpha 0)")
