@@ -2,17 +2,22 @@
 """Throughput of the sparse + linear attention forward on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input:
-the block mask (sla_mask), the K/V preparation pass (sla_kv_prepare)
-and the fused sparse + linear + alpha-mix kernel (sla_fused_fwd) - the same
-launches as sla_attn_fwd, issued one by one so that HIP events on the launch
-stream bracket each stage.  Inputs are resident in HBM before timing starts.
+the K/V preparation pass (sla_kv_prepare, which also pools K for the mask),
+the block mask (sla_mask_prepared) and the fused sparse + linear + alpha-mix
+kernel (sla_fused_fwd) - the same launches as sla_attn_fwd, issued one by one
+so that HIP events on the launch stream bracket each stage.  Inputs are
+resident in HBM before timing starts.  The untimed warm-up runs 300 steps
+(about 0.2 s): the shader clock of a GPU that was idle takes tens of
+milliseconds of load to settle, and steps timed before that run 10-15%
+slower.
 
 Prints ONE JSON line.  value = dense-equivalent TFLOP/s = 4 B H N^2 d /
 (time per step); the dense bf16 kernel of this library on the same tensors
 gives the speedup.  The roofline object covers the fused kernel (algorithmic
 FLOPs: 4 bq bk d per executed (query block, key block) pair plus 2 bq d^2 per
-query block with a linear branch), the mask roofline the HBM bytes of the mask
-(Q and K read once, the CSR written once).  cpu_baseline times the fp64
+query block with a linear branch), the mask roofline the HBM bytes of the
+standalone mask call sla_mask (Q and K read once, the CSR written once), timed
+in its own leg after the steps.  cpu_baseline times the fp64
 oracle on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
@@ -40,8 +45,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_fused_traffic.json")
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="video480p-sla2-N32760")
     ap.add_argument("--dense-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -143,10 +148,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p, wq, wk, ws=ws, row_ptr=rp, col_idx=ci)
+        S.sla_kv_prepare(k, v, wl.bq, wl.bk, ws, alpha)
         if ev is not None:
             ev[1].record()
-        S.sla_kv_prepare(k, v, wl.bq, wl.bk, ws, alpha)
+        S.sla_mask_prepared(q, k, alpha, wl.bq, wl.bk, wl.k_frac, wl.p, wq, wk, ws=ws, row_ptr=rp, col_idx=ci)
         if ev is not None:
             ev[2].record()
         S.sla_fused_fwd(q, k, v, alpha, wl.bq, wl.bk, rp, ci, ws, out=out)
@@ -164,10 +169,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall / args.steps * 1e3
-    st_mask = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    st_sum = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    st_sum = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    st_maskp = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     st_fused = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     ev_step = sum(e[0].elapsed_time(e[3]) for e in events) / args.steps
+
+    # the standalone mask call (pools Q and K itself), for the mask's HBM roofline
+    rp_m, ci_m = torch.empty_like(rp), torch.empty_like(ci)
+    mask_call = lambda: S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p, wq, wk, ws=ws, row_ptr=rp_m,
+                                   col_idx=ci_m)
+    for _ in range(10):
+        mask_call()
+    torch.cuda.synchronize()
+    em0, em1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    em0.record()
+    for _ in range(args.steps):
+        mask_call()
+    em1.record()
+    torch.cuda.synchronize()
+    st_mask = em0.elapsed_time(em1) / args.steps
+    n_m = int(rp_m[-1])
+    if not (torch.equal(rp_m, rp) and torch.equal(ci_m[:n_m], ci[:n_m])):
+        raise RuntimeError("sla_mask and sla_mask_prepared disagree")
 
     # algorithmic work from the mask this step produced
     counts = np.diff(rp.cpu().numpy().astype(np.int64))
@@ -202,8 +225,8 @@ def main():
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
                           "frac": mask_bytes / (st_mask * 1e-3) / 1e9 / PEAK_HBM_GBS,
                           "bytes_per_call": mask_bytes, "ms_per_call": st_mask},
-        "stage_ms": {"mask": st_mask, "kv_prepare": st_sum, "fused": st_fused,
-                     "events_step": ev_step},
+        "stage_ms": {"kv_prepare": st_sum, "mask_prepared": st_maskp, "fused": st_fused,
+                     "events_step": ev_step, "mask_standalone": st_mask},
         "sparsity": 1.0 - nnz / float(wl.B * wl.H * wl.Nq * wl.Nk), "nnz": nnz,
         "executed_TFLOPS_fused": fused_flops / (st_fused * 1e-3) / 1e12,
     }

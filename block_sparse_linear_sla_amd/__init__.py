@@ -23,7 +23,8 @@ LIB_PATH = os.environ.get("SLA_LIB", os.path.join(_HERE, "libsla.so"))
 SLA_F32, SLA_BF16 = 0, 1
 STATUS = {0: "SLA_OK", -1: "SLA_ERR_INVALID_ARG", -2: "SLA_ERR_UNSUPPORTED",
           -3: "SLA_ERR_WORKSPACE", -4: "SLA_ERR_CAPACITY", -5: "SLA_ERR_HIP"}
-EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_soft_topk", "sla_sparse_fwd",
+EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_mask_prepared", "sla_soft_topk",
+           "sla_sparse_fwd",
            "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
            "sla_dense_fwd", "sla_i8_layout_of", "sla_quantize_i8", "sla_sparse_fwd_i8",
            "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_linear_bwd", "sla_attn_bwd", "sla_alpha_grad",
@@ -68,6 +69,7 @@ def lib() -> ctypes.CDLL:
         L.sla_mask_capacity.argtypes = [P]
         L.sla_mask_capacity.restype = ctypes.c_int64
         L.sla_mask.argtypes = [P, S, vp, vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
+        L.sla_mask_prepared.argtypes = [P, S, vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_size_t, vp]
         L.sla_soft_topk.argtypes = [P, S, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_linear_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -88,7 +90,7 @@ def lib() -> ctypes.CDLL:
         L.sla_alpha_grad.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
-        for fn in ("sla_mask", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
+        for fn in ("sla_mask", "sla_mask_prepared", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
                    "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd", "sla_i8_layout_of",
                    "sla_quantize_i8", "sla_sparse_fwd_i8", "sla_sparse_bwd", "sla_linear_bwd",
                    "sla_attn_bwd", "sla_alpha_grad"):
@@ -173,6 +175,29 @@ def sla_mask(q, k, bq: int, bk: int, k_frac: float, p: float, wq=None, wk=None,
                                       _ptr(rp), _ptr(ci), ci.numel(), _ptr(logits), _ptr(w),
                                       w.numel(), _stream()))
     return (rp, ci, logits) if return_logits else (rp, ci)
+
+
+def sla_mask_prepared(q, k, alpha, bq: int, bk: int, k_frac: float, p: float, wq=None, wk=None,
+                      ws: Optional[torch.Tensor] = None, row_ptr: Optional[torch.Tensor] = None,
+                      col_idx: Optional[torch.Tensor] = None):
+    """sla_mask for a workspace on which sla_kv_prepare(k, v, ..., alpha) has
+    just run (it pooled K for the heads it processed): the same CSR."""
+    _need(q, k, like=q)
+    if not alpha.is_cuda or alpha.dtype != torch.float32 or alpha.numel() != q.shape[1]:
+        raise ValueError("alpha must be a CUDA float32 tensor of H entries")
+    if ws is None:
+        raise ValueError("sla_mask_prepared needs the workspace sla_kv_prepare filled")
+    prob, sel = problem(q, bq, bk), select(k_frac, p, wq, wk)
+    cap = sla_mask_capacity(prob)
+    B, H = q.shape[:2]
+    Nq = -(-q.shape[2] // bq)
+    dev = q.device
+    rp = row_ptr if row_ptr is not None else torch.empty(B * H * Nq + 1, dtype=torch.int32, device=dev)
+    ci = col_idx if col_idx is not None else torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    _check("sla_mask_prepared", lib().sla_mask_prepared(ctypes.byref(prob), ctypes.byref(sel), _ptr(q), _ptr(k),
+                                                        _ptr(alpha), _ptr(rp), _ptr(ci), ci.numel(), _ptr(ws),
+                                                        ws.numel(), _stream()))
+    return rp, ci
 
 
 def sla_soft_topk(q, k, bq: int, bk: int, k_frac: float, T: float, wq=None, wk=None,

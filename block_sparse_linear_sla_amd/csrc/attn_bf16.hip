@@ -289,20 +289,21 @@ __device__ __forceinline__ void pv_g(const char* Vc, const char* Ph, const PhiPl
 // [d/32][Npad][32] array (zero for keys >= N), and the chunk's partial totals
 // H = sum_u phi(k_u)^T v_u (in MFMA fragment order: 32 x 32 tile (mt, nt),
 // lane, accumulator element) and z = sum_u phi(k_u).  64-key units of K and V
-// stream through two LDS stages.  Each thread converts its 16-byte chunks of
-// the unit's K tile once: phi goes to global memory, and its bf16 hi part
-// replaces K in the tile while the lo part (phi - hi, bf16) goes to a second
-// tile of the same layout, so H keeps ~16 mantissa bits.  After a barrier,
-// wavefront w accumulates the G tiles of the attention kernel's split
-// (GSplit<D, 4>) from transposed reads of both phi tiles and of the V tile,
-// and the column sums z with v_dot2 over the same fragments.  Heads whose
-// alpha is exactly 1 are skipped when alpha is given.
+// stream through two LDS stages and are only read there: each thread turns
+// its 16-byte chunks of the unit's K tile into phi for the global array,
+// and wavefront w accumulates the G tiles of the attention kernel's split
+// (GSplit<D, 4>) from transposed reads of the raw K tile (phi applied in
+// float32 and split into hi + lo bf16, so H keeps ~16 mantissa bits) and of
+// the V tile.  The wavefronts that keep z also sum the raw K values of their
+// d rows in float64 (sums of bf16 values, exact in float64) and, with kbar
+// given, write each key block's mean there (the mask's pooled K).  Heads
+// whose alpha is exactly 1 are skipped when alpha is given.
 template <int D, int BK>
 __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ K,
                                                    const uint16_t* __restrict__ V,
                                                    const float* __restrict__ alpha, int H, int N, int Nk,
                                                    int chunk_blocks, int nchunk, uint16_t* __restrict__ pk_g,
-                                                   float* __restrict__ hpart) {
+                                                   float* __restrict__ hpart, double* __restrict__ kbar) {
   using T = Tiles<D>;
   using LP = LoadPlan<D, 4>;
   using GS = GSplit<D, 4>;
@@ -314,7 +315,6 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) char k1[T::KT_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[T::KT_BYTES];
   __shared__ __attribute__((aligned(16))) char v1[T::KT_BYTES];
-  __shared__ __attribute__((aligned(16))) char plo[T::KT_BYTES];
 
   const long long bh = blockIdx.x / nchunk;
   const int chunk = blockIdx.x % nchunk;
@@ -334,16 +334,16 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
   const int nun = max(0, je - jb) * SUB;        // units of the chunk
   const int mt = GS::mt0(w);                    // the d_k row tile of this wavefront
   const bool zown = GS::zown(w);
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
   f32x16 acc[TPW];
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
   float zpart = 0.f;
+  double ksum = 0.0;  // raw K over this lane's keys of the current block, d row 32 mt + l32
 
-  auto step = [&](int x, char* ks, const char* vs, char* nks, char* nvs) __attribute__((always_inline)) {
+  auto step = [&](int x, const char* ks, const char* vs, char* nks, char* nvs) __attribute__((always_inline)) {
     wait_vm<0>();     // this wavefront's loads of unit x have landed
-    __syncthreads();  // ... and every wavefront's; unit x-1 consumed (its phi tiles read)
+    __syncthreads();  // ... and every wavefront's; unit x-1 consumed
     if (x + 1 < nun) {
       const int kn = (jb * SUB + x + 1) * KU;
       lp.load(rk, kn, nks);
@@ -358,44 +358,54 @@ __global__ __launch_bounds__(256) void prep_kernel(const uint16_t* __restrict__ 
       const int ch = tid + 256 * c;
       const int dt = ch / (4 * KU), r = (ch / 4) % KU, c4 = ch % 4;
       const int cc = 4 * dt + c4;               // 16-byte chunk of the key row
-      char* at = ks + (cc >> 3) * T::KHALF + r * 128 + 16 * ((cc & 7) ^ sw(r));
-      const uint4 kv = rd16(at);
-      uint32_t oh[4], ol[4];
+      const uint4 kv = rd16(ks + (cc >> 3) * T::KHALF + r * 128 + 16 * ((cc & 7) ^ sw(r)));
+      uint32_t oh[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float f0 = phi(bf2f(elem(kv, 2 * e))), f1 = phi(bf2f(elem(kv, 2 * e + 1)));
         if (r >= lim) f0 = f1 = 0.f;
         oh[e] = pk_bf16(f0, f1);
-        ol[e] = pk_bf16(f0 - bf2f(oh[e] & 0xffffu), f1 - bf2f(oh[e] >> 16));
       }
-      const uint4 hv = make_uint4(oh[0], oh[1], oh[2], oh[3]);
-      *reinterpret_cast<uint4*>(Pb + ((size_t)dt * Npad + key0 + r) * 32 + 8 * c4) = hv;
-      *reinterpret_cast<uint4*>(at) = hv;  // this thread's own chunk: no other thread touches it
-      *reinterpret_cast<uint4*>(plo + (at - ks)) = make_uint4(ol[0], ol[1], ol[2], ol[3]);
+      *reinterpret_cast<uint4*>(Pb + ((size_t)dt * Npad + key0 + r) * 32 + 8 * c4) =
+          make_uint4(oh[0], oh[1], oh[2], oh[3]);
     }
-    __syncthreads();  // both phi tiles complete
-    // H += phi(K)^T V (hi + lo) and z over the 4 key planes of the unit
+    // H += phi(K)^T V (hi + lo) over the 4 key planes of the unit; element e
+    // of a plane fragment is key 16 pl + 4 hi + e % 4 + 8 (e / 4)
 #pragma unroll
     for (int pl = 0; pl < KU / 16; ++pl) {
-      const bf16x8 ah = rdp.vt(ks, mt, pl);
-      const bf16x8 al = rdp.vt(plo, mt, pl);
-      if (zown) {
-        const uint4 h4 = __builtin_bit_cast(uint4, ah), l4 = __builtin_bit_cast(uint4, al);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.x), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.y), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.z), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, h4.w), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.x), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.y), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.z), ones, zpart, false);
-        zpart = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, l4.w), ones, zpart, false);
+      const uint4 kr = __builtin_bit_cast(uint4, rdp.vt(ks, mt, pl));
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xv = bf2f(elem(kr, e));
+        f[e] = 16 * pl + 4 * hi + (e & 3) + 8 * (e >> 2) < lim ? phi(xv) : 0.f;
+        if (zown) {
+          zpart += f[e];
+          ksum += (double)xv;  // keys past N read as 0
+        }
       }
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[e] = pk_bf16(f[2 * e], f[2 * e + 1]);
+        l[e] = pk_bf16(f[2 * e] - bf2f(h[e] & 0xffffu), f[2 * e + 1] - bf2f(h[e] >> 16));
+      }
+      const bf16x8 ah = as_bf16x8(make_uint4(h[0], h[1], h[2], h[3]));
+      const bf16x8 al = as_bf16x8(make_uint4(l[0], l[1], l[2], l[3]));
 #pragma unroll
       for (int u = 0; u < TPW; ++u) {
         const bf16x8 b = rdp.vt(vs, GS::nt(w, u), pl);
         acc[u] = mfma(ah, b, acc[u]);
         acc[u] = mfma(al, b, acc[u]);
       }
+    }
+    if (x % SUB == SUB - 1) {
+      // the key block is complete: its mean over the valid rows
+      const double t = ksum + __shfl_xor(ksum, 32);
+      const int j = jb + x / SUB;
+      if (kbar != nullptr && zown && hi == 0)
+        kbar[((size_t)bh * Nk + j) * D + 32 * mt + l32] = t / (double)min(BK, N - j * BK);
+      ksum = 0.0;
     }
   };
   if (nun > 0) {
@@ -791,15 +801,16 @@ hipError_t launch_summary_reduce(const float* hpart, const float* alpha, int H, 
 namespace {
 
 template <int D, int BK>
-hipError_t prep_dispatch(const Shape& s, const void* K, const void* V, const float* alpha, char* ws,
-                         const WsLayout& L, hipStream_t st) {
+hipError_t prep_dispatch(const Shape& s, const void* K, const void* V, const float* alpha, bool kmeans,
+                         char* ws, const WsLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H;
   const dim3 grid((unsigned)(BH * L.nchunk)), block(256);
   uint16_t* pk = reinterpret_cast<uint16_t*>(ws + L.pk);
   float* hpart = reinterpret_cast<float*>(ws + L.hpart);
+  double* kbar = kmeans ? reinterpret_cast<double*>(ws + L.kbar) : nullptr;
   hipLaunchKernelGGL((prep_kernel<D, BK>), grid, block, 0, st, static_cast<const uint16_t*>(K),
                      static_cast<const uint16_t*>(V), alpha, s.H, s.N, s.Nk, L.chunk_blocks, L.nchunk, pk,
-                     hpart);
+                     hpart, kbar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_summary_reduce(hpart, alpha, s.H, BH, L.nchunk, D * D + D,
@@ -834,12 +845,12 @@ hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K
 }  // namespace
 
 hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
-                            char* ws, const WsLayout& L, hipStream_t st) {
+                            bool kmeans, char* ws, const WsLayout& L, hipStream_t st) {
   if (!lin) return hipSuccess;  // the softmax kernels read K and V as they are
-  if (s.d == 128 && s.bk == 64) return prep_dispatch<128, 64>(s, K, V, alpha, ws, L, st);
-  if (s.d == 128 && s.bk == 128) return prep_dispatch<128, 128>(s, K, V, alpha, ws, L, st);
-  if (s.d == 64 && s.bk == 64) return prep_dispatch<64, 64>(s, K, V, alpha, ws, L, st);
-  if (s.d == 64 && s.bk == 128) return prep_dispatch<64, 128>(s, K, V, alpha, ws, L, st);
+  if (s.d == 128 && s.bk == 64) return prep_dispatch<128, 64>(s, K, V, alpha, kmeans, ws, L, st);
+  if (s.d == 128 && s.bk == 128) return prep_dispatch<128, 128>(s, K, V, alpha, kmeans, ws, L, st);
+  if (s.d == 64 && s.bk == 64) return prep_dispatch<64, 64>(s, K, V, alpha, kmeans, ws, L, st);
+  if (s.d == 64 && s.bk == 128) return prep_dispatch<64, 128>(s, K, V, alpha, kmeans, ws, L, st);
   return hipErrorInvalidValue;
 }
 

@@ -64,12 +64,14 @@ struct Chunk<uint16_t> {  // bf16 bit patterns
 };
 
 // Mean of the valid rows of one block of Q or K.  Workgroups [0, BH*Nq) pool Q
-// blocks, the rest pool K blocks.  Each thread owns one 16-byte column chunk
+// blocks, the rest pool K blocks (except those of the heads whose kdone value
+// is not exactly 1: the preparation pass has written their means).  Each thread owns one 16-byte column chunk
 // and walks rows with stride RPP; partial sums meet in LDS.
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ Q, const T* __restrict__ K,
                                                         int N, int bq, int bk, int Nq, int Nk,
-                                                        long long BH, double* __restrict__ qbar,
+                                                        long long BH, int H, const float* __restrict__ kdone,
+                                                        double* __restrict__ qbar,
                                                         double* __restrict__ kbar) {
   constexpr int VEC = Chunk<T>::VEC;
   constexpr int TPR = D / VEC;         // threads per row
@@ -87,6 +89,7 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ Q,
   } else {
     wg -= nqb;
     bh = wg / Nk; blk = (int)(wg % Nk); X = K; out = kbar; bs = bk; nb = Nk;
+    if (kdone != nullptr && kdone[bh % H] != 1.f) return;  // pooled by the preparation pass
   }
   const int r0 = blk * bs;
   const int rows = min(bs, N - r0);
@@ -846,7 +849,7 @@ namespace {
 
 // Pooling, optional router and the pooled logits S [B, H, Nq, Nk] (float64).
 hipError_t launch_scores(const Shape& s, const float* Wq, const float* Wk, const void* Q, const void* K,
-                         double* S, char* ws, const WsLayout& L, hipStream_t st) {
+                         double* S, char* ws, const WsLayout& L, hipStream_t st, const float* kdone = nullptr) {
   const long long BH = (long long)s.B * s.H;
   double* qbar = reinterpret_cast<double*>(ws + L.qbar);
   double* kbar = reinterpret_cast<double*>(ws + L.kbar);
@@ -855,7 +858,7 @@ hipError_t launch_scores(const Shape& s, const float* Wq, const float* Wk, const
 #define SLA_POOL(T, DD)                                                                          \
   hipLaunchKernelGGL((pool_kernel<T, DD>), gpool, dim3(kThreads), 0, st,                          \
                      reinterpret_cast<const T*>(Q), reinterpret_cast<const T*>(K), s.N, s.bq,   \
-                     s.bk, s.Nq, s.Nk, BH, qbar, kbar)
+                     s.bk, s.Nq, s.Nk, BH, s.H, kdone, qbar, kbar)
   if (s.dtype == 1) {
     if (s.d == 128) SLA_POOL(uint16_t, 128); else SLA_POOL(uint16_t, 64);
   } else {
@@ -927,13 +930,14 @@ hipError_t launch_soft_topk(const Shape& s, int k, double T, const float* Wq, co
 
 hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const float* Wk,
                        const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
-                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st) {
+                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st,
+                       const float* kdone) {
   const long long R = s.R();
   double* S = logits_out ? logits_out : reinterpret_cast<double*>(ws + L.S);
   int* counts = reinterpret_cast<int*>(ws + L.counts);
   uint32_t* bits = reinterpret_cast<uint32_t*>(ws + L.bits);
   const int W = s.words();
-  hipError_t e = launch_scores(s, Wq, Wk, Q, K, S, ws, L, st);
+  hipError_t e = launch_scores(s, Wq, Wk, Q, K, S, ws, L, st, kdone);
   if (e != hipSuccess) return e;
 
   int E = 1;

@@ -20,7 +20,9 @@ WsLayout ws_layout(const Shape& s, bool router) {
     off = align256(off + bytes);
     return o;
   };
-  // Linear summaries first, so their offsets do not depend on the router.
+  // What the preparation pass writes (linear summaries, phi(K), the pooled K)
+  // comes first, so its offsets do not depend on the router: the pass can run
+  // with either layout, before or after the mask, on the same workspace.
   // The preparation pass runs one workgroup per chunk of key blocks of a head;
   // chunks are sized so the grid is a single round at two workgroups per CU
   // (about 512), which keeps the per-chunk partials few.
@@ -33,13 +35,13 @@ WsLayout ws_layout(const Shape& s, bool router) {
   const size_t per = (size_t)s.d * s.d + s.d;
   L.htot = take(BH * per * sizeof(float));
   L.hpart = take(BH * L.nchunk * per * sizeof(float));
+  const bool bf = s.dtype == SLA_BF16;
+  L.pk = bf ? take(BH * (size_t)s.Nk * s.bk * s.d * 2) : 0;
   L.qbar = take(BH * s.Nq * s.d * sizeof(double));
   L.kbar = take(BH * s.Nk * s.d * sizeof(double));
   L.qhat = router ? take(BH * s.Nq * s.d * sizeof(double)) : 0;
   L.khat = router ? take(BH * s.Nk * s.d * sizeof(double)) : 0;
   L.S = take(BH * s.Nq * s.Nk * sizeof(double));
-  const bool bf = s.dtype == SLA_BF16;
-  L.pk = bf ? take(BH * (size_t)s.Nk * s.bk * s.d * 2) : 0;
   L.counts = take((size_t)s.R() * sizeof(int32_t));
   L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
   L.total = off;
@@ -87,8 +89,8 @@ int check_select(const sla_select* sel, int* k, const Shape& s) {
 int hip_status(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_HIP; }
 
 hipError_t run_prep(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
-                    char* ws, const WsLayout& L, hipStream_t st) {
-  if (s.dtype == SLA_BF16) return sla::launch_prep_bf16(s, lin, K, V, alpha, ws, L, st);
+                    char* ws, const WsLayout& L, hipStream_t st, bool kmeans = false) {
+  if (s.dtype == SLA_BF16) return sla::launch_prep_bf16(s, lin, K, V, alpha, kmeans, ws, L, st);
   return lin ? sla::launch_summary_f32(s, K, V, alpha, ws, L, st) : hipSuccess;
 }
 
@@ -132,6 +134,25 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
   return hip_status(sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx,
                                      block_logits, static_cast<char*>(ws), L,
                                      static_cast<hipStream_t>(stream)));
+}
+
+int sla_mask_prepared(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+                      const float* alpha, int32_t* row_ptr, int32_t* col_idx, int64_t capacity, void* ws,
+                      size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  int k;
+  if ((rc = check_select(sel, &k, s)) != SLA_OK) return rc;
+  if (Q == nullptr || K == nullptr || alpha == nullptr || row_ptr == nullptr || col_idx == nullptr)
+    return SLA_ERR_INVALID_ARG;
+  if (capacity < (int64_t)s.B * s.H * s.Nq * s.Nk) return SLA_ERR_CAPACITY;
+  const WsLayout L = sla::ws_layout(s, sel->Wq != nullptr);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  // the bf16 preparation pass pooled K for the heads it processed
+  return hip_status(sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx, nullptr,
+                                     static_cast<char*>(ws), L, static_cast<hipStream_t>(stream),
+                                     s.dtype == SLA_BF16 ? alpha : nullptr));
 }
 
 int sla_soft_topk(const sla_problem* prob, const sla_select* sel, float T, const void* Q, const void* K,
@@ -193,10 +214,14 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
   if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   char* w = static_cast<char*>(ws);
-  if (sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx, nullptr, w, L,
-                       st) != hipSuccess)
+  // bf16: the preparation pass runs first and also pools K for the heads it
+  // processes (alpha != 1), so the mask reads K only for the others
+  const bool bf = s.dtype == SLA_BF16;
+  if (bf && run_prep(s, true, K, V, alpha, w, L, st, true) != hipSuccess) return SLA_ERR_HIP;
+  if (sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx, nullptr, w, L, st,
+                       bf ? alpha : nullptr) != hipSuccess)
     return SLA_ERR_HIP;
-  if (run_prep(s, true, K, V, alpha, w, L, st) != hipSuccess) return SLA_ERR_HIP;
+  if (!bf && run_prep(s, true, K, V, alpha, w, L, st) != hipSuccess) return SLA_ERR_HIP;
   return hip_status(run_attn(s, sla::MODE_FUSED, Q, K, V, row_ptr, col_idx, alpha, w, L, O, st));
 }
 
@@ -209,7 +234,7 @@ int sla_kv_prepare(const sla_problem* prob, const void* K, const void* V, const 
   const WsLayout L = sla::ws_layout(s, false);
   if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
   return hip_status(run_prep(s, true, K, V, alpha, static_cast<char*>(ws), L,
-                             static_cast<hipStream_t>(stream)));
+                             static_cast<hipStream_t>(stream), true));
 }
 
 int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,

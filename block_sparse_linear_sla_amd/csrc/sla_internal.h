@@ -83,9 +83,13 @@ enum Mode : int {
 };
 
 // mask.hip: pooling, optional router, pooled logits, selection, CSR.
+// kdone (device [H], nullable): the pooled K of every head whose value there
+// is not exactly 1 is already in the workspace (written by the preparation
+// pass), so only Q and the other heads' K are pooled.
 hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const float* Wk,
                        const void* Q, const void* K, int32_t* row_ptr, int32_t* col_idx,
-                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st);
+                       double* logits_out, char* ws, const WsLayout& L, hipStream_t st,
+                       const float* kdone = nullptr);
 
 // mask.hip: the SoftTop-k weights [B*H*Nq, Nk] (float32) from the pooled
 // (and optionally routed) logits.
@@ -95,9 +99,11 @@ hipError_t launch_soft_topk(const Shape& s, int k, double T, const float* Wq, co
 
 // attn_bf16.hip: the K/V preparation pass for the linear branch (phi(K) in
 // 32-wide d slices and the per-head linear totals; nothing without lin;
-// heads whose alpha is exactly 1 are skipped when alpha is given) and the
+// heads whose alpha is exactly 1 are skipped when alpha is given; kmeans:
+// also the pooled K of the heads it processes, for the mask) and the
 // attention kernels.
 hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
+                            bool kmeans,
                             char* ws, const WsLayout& L, hipStream_t st);
 hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,

@@ -134,7 +134,8 @@ int sla_linear_fwd(const sla_problem* prob, const void* Q, const void* K, const 
                    void* ws, size_t ws_bytes, void* stream);
 
 /* The whole forward: mask, then O = alpha_h * O_s + (1 - alpha_h) * O_l
- * (SLA2 write-up §二), written once in the input dtype.
+ * (SLA2 write-up §二), written once in the input dtype (for bf16 the K/V
+ * preparation pass runs first and pools K for the mask; see below).
  *   alpha    DEVICE fp32 [H], each in [0, 1]; a branch whose weight is exactly
  *            0 for a head is not evaluated for that head
  *   row_ptr, col_idx, capacity   the mask, returned as by sla_mask */
@@ -142,8 +143,10 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
                  const void* V, const float* alpha, void* O, int32_t* row_ptr,
                  int32_t* col_idx, int64_t capacity, void* ws, size_t ws_bytes, void* stream);
 
-/* The two stages that follow the mask in sla_attn_fwd, for callers that time
- * or schedule them separately (sla_attn_fwd == sla_mask, then these two).
+/* The stages of sla_attn_fwd, for callers that time or schedule them
+ * separately: sla_attn_fwd == sla_kv_prepare, sla_mask_prepared, then
+ * sla_fused_fwd, on one workspace (sla_mask, sla_kv_prepare, sla_fused_fwd
+ * gives the same mask and output and reads K once more).
  *
  * sla_kv_prepare: one pass over K and V that leaves in the workspace what the
  * fused stage reads: the per-head linear-attention totals H = sum_u phi(k_u)^T
@@ -151,7 +154,16 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
  * bf16, phi(K) in 32-wide d slices (bf16 [B, H, d/32, Nk*bk, 32], keys past N
  * zero).  V is not copied: the attention kernels read V and K as the caller
  * passed them.  alpha (DEVICE fp32 [H]) may be NULL; heads whose alpha is
- * exactly 1 skip the pass when it is given.
+ * exactly 1 skip the pass when it is given.  For bf16 the pass also writes the
+ * mean of every key block of the heads it processes (the mask's pooled K,
+ * float64 sums of the bf16 values) into the workspace.
+ *
+ * sla_mask_prepared: sla_mask (same arguments and outputs, no block_logits)
+ * for a workspace on which sla_kv_prepare has just run with the same K and
+ * alpha: it pools Q and only the K of the heads that pass skipped (alpha
+ * exactly 1; every head for fp32, whose pass writes no key-block means).  The
+ * result is identical to sla_mask's.  Calling it without that pass is
+ * undefined.
  *
  * sla_fused_fwd: O = alpha_h * O_s + (1 - alpha_h) * O_l over the given mask,
  * with O_l = phi(q) (H - G) / phi(q) (z - g), where G, g are the same sums
@@ -160,6 +172,9 @@ int sla_attn_fwd(const sla_problem* prob, const sla_select* sel, const void* Q, 
  * calling it without that is undefined. */
 int sla_kv_prepare(const sla_problem* prob, const void* K, const void* V, const float* alpha,
                    void* ws, size_t ws_bytes, void* stream);
+int sla_mask_prepared(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+                      const float* alpha, int32_t* row_ptr, int32_t* col_idx, int64_t capacity,
+                      void* ws, size_t ws_bytes, void* stream);
 int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
                   const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
                   const void* ws, size_t ws_bytes, void* stream);

@@ -254,3 +254,21 @@ def test_linear_and_mixed_bwd_checks():
         assert L.sla_attn_bwd(ctypes.byref(p16), *a, FAKE, n, None) == INVALID, i
     assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, None, n, None) == WORKSPACE
     assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, FAKE, n - 1, None) == WORKSPACE
+
+
+def test_mask_prepared_checks():
+    L = S.lib()
+    p = prob(dtype=S.SLA_BF16)
+    sel = S.select(0.1, 0.5)
+    n = L.sla_workspace_bytes(ctypes.byref(p), ctypes.byref(sel))
+    cap = L.sla_mask_capacity(ctypes.byref(p))
+    args = [FAKE] * 5  # Q, K, alpha, row_ptr, col_idx
+    for i in range(5):
+        a = list(args)
+        a[i] = None
+        assert L.sla_mask_prepared(ctypes.byref(p), ctypes.byref(sel), *a, cap, FAKE, n, None) == INVALID, i
+    assert L.sla_mask_prepared(ctypes.byref(p), ctypes.byref(sel), *args, cap - 1, FAKE, n, None) == CAPACITY
+    assert L.sla_mask_prepared(ctypes.byref(p), ctypes.byref(sel), *args, cap, None, n, None) == WORKSPACE
+    assert L.sla_mask_prepared(ctypes.byref(p), ctypes.byref(sel), *args, cap, FAKE, n - 1, None) == WORKSPACE
+    assert L.sla_mask_prepared(None, ctypes.byref(sel), *args, cap, FAKE, n, None) == INVALID
+    assert L.sla_mask_prepared(ctypes.byref(p), None, *args, cap, FAKE, n, None) == INVALID

@@ -116,3 +116,44 @@ def test_mask_deterministic():
     b = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
     n = int(a[0][-1])
     assert torch.equal(a[0], b[0]) and torch.equal(a[1][:n], b[1][:n])
+
+
+PREPARED = [
+    # name, dtype, N, d, bq, bk, router, alpha per head (B=2, H=3)
+    ("bf16-ragged-1000", "bf16", 1000, 128, 128, 64, False, (0.7, 1.0, 0.9)),
+    ("bf16-ragged-1001-d64-bk128", "bf16", 1001, 64, 64, 128, False, (0.6, 0.8, 1.0)),
+    ("bf16-router", "bf16", 2000, 128, 128, 64, True, (0.75, 0.6, 0.95)),
+    ("bf16-bk128", "bf16", 4000, 128, 128, 128, False, (1.0, 1.0, 0.5)),
+    ("fp32-ragged-1000", "fp32", 1000, 64, 64, 64, False, (0.5, 1.0, 0.7)),
+]
+
+
+@pytest.mark.parametrize("case", PREPARED, ids=[c[0] for c in PREPARED])
+def test_mask_prepared_matches_mask(case):
+    """sla_kv_prepare pools K for the heads it processes (alpha != 1, bf16);
+    sla_mask_prepared then pools only the rest.  The CSR must be sla_mask's,
+    entry for entry (the key-block means are float64 sums of bf16 values,
+    exact in any order), and sla_attn_fwd, which runs the stages in that
+    order, must give the output of the three separate calls."""
+    name, dtype, N, d, bq, bk, router, alpha = case
+    print(f"[mask-prepared] {name}", flush=True)
+    wl = gen.Workload("adhoc", B=2, H=3, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.6,
+                      dtype=dtype, router=router, alpha=alpha, seed=17)
+    x = gen.make(wl)
+    q, k, v = U.dev(x.Q, x.K, x.V)
+    wq, wk = U.dev(x.Wq, x.Wk)
+    a = torch.tensor(alpha, dtype=torch.float32, device="cuda")
+    prob, sel = S.problem(q, bq, bk), S.select(wl.k_frac, wl.p, wq, wk)
+    ws = S.workspace(prob, sel, q.device)
+    rp0, ci0 = S.sla_mask(q, k, bq, bk, wl.k_frac, wl.p, wq, wk)
+    ws.fill_(0xFF)  # the prepared path must not rely on an earlier sla_mask in this workspace
+    S.sla_kv_prepare(k, v, bq, bk, ws, a)
+    rp1, ci1 = S.sla_mask_prepared(q, k, a, bq, bk, wl.k_frac, wl.p, wq, wk, ws=ws)
+    torch.cuda.synchronize()
+    n = int(rp0[-1])
+    assert torch.equal(rp0, rp1) and torch.equal(ci0[:n], ci1[:n])
+    o3 = S.sla_fused_fwd(q, k, v, a, bq, bk, rp1, ci1, ws)
+    o1, rp2, ci2 = S.sla_attn_fwd(q, k, v, a, bq, bk, wl.k_frac, wl.p, wq, wk)
+    torch.cuda.synchronize()
+    assert torch.equal(rp0, rp2) and torch.equal(ci0[:n], ci2[:n])
+    assert torch.equal(o1, o3)
