@@ -198,9 +198,10 @@ __global__ __launch_bounds__(256, 2) void lin_outer_kernel(const uint16_t* __res
   if (sown && hi == 0) out[(size_t)D * D + 32 * at + (lane & 31)] = st;
 }
 
-// One head's D x D total R (row-major in tot) as the B operands of y_t = R' x_t
-// on the matrix cores, R' = R (TRANS = 0: y[o] = sum_i R[o][i] x[i]) or R^T
-// (TRANS = 1: y[o] = sum_i R[i][o] x[i]).  Fragment (dt, kk) of lane l holds
+// One head's D x D total R (row-major in tot) as matrix-core operand
+// fragments of y_t = R' x_t (the A operand of y^T = R' x^T: rows o, k-slices
+// i), R' = R (TRANS = 0: y[o] = sum_i R[o][i] x[i]) or R^T (TRANS = 1:
+// y[o] = sum_i R[i][o] x[i]).  Fragment (dt, kk) of lane l holds
 // R'[o][i] for o = 32 dt + l % 32 and i = 16 kk + 8 (l / 32) + 0..7, each
 // value split as hi = bf16(x) and lo = bf16(x - hi), so that the two
 // bf16 products keep R to about 2^-17 relative.  Layout: uint4
