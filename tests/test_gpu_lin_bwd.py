@@ -177,3 +177,40 @@ def test_attn_bwd_mixed(N, d, bq, bk):
         # alpha = 0 head the linear branch's alone
         _compare(t[:, 1:2], rs[n][:, 1:2], n + " (alpha 1)")
         _compare(t[:, 2:3], rl[n][:, 2:3], n + " (alpha 0)")
+
+
+def test_attn_bwd_480p_two_heads():
+    """sla_attn_bwd on the 480p workload at full length (two heads, the
+    library's mask, the workload's alpha): dQ of sampled row blocks against
+    alpha times the oracle's sparse-branch gradient plus (1 - alpha) times its
+    linear-branch gradient; and, since every row has both branches there,
+    dV summed over the keys equals dO summed over the queries (each branch's
+    weights over its keys sum to one)."""
+    wl = gen.WORKLOADS["video480p-sla2-N32760"]
+    print(f"[lin-bwd] sla_attn_bwd {wl.name}, 2 heads", flush=True)
+    x = gen.make(wl, heads=2)
+    q, k, v = U.dev(x.Q, x.K, x.V)
+    rp_t, ci_t = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    rp, ci = U.csr(rp_t, ci_t)
+    dO = torch.from_numpy(np.random.default_rng(10).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
+    alpha = x.alpha.float()
+    dq, dk, dv = S.sla_attn_bwd(q, k, v, dO.cuda(), alpha.cuda(), wl.bq, wl.bk, rp_t, ci_t)
+    torch.cuda.synchronize()
+    B, H, N, d = x.Q.shape
+    Nq, Nk = O.n_blocks(N, wl.bq), O.n_blocks(N, wl.bk)
+    counts = np.diff(rp)
+    assert counts.min() > 0 and counts.max() < Nk  # both branches on every row
+    rows = [(0, 0, 3), (0, 1, Nq - 1)]
+    rs = O.sparse_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO)
+    rl = O.linear_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
+    a = alpha.double().numpy()
+    for (b, h, i) in rows:
+        s, e = i * wl.bq, min(N, (i + 1) * wl.bq)
+        ref = a[h] * rs["dQ"][b, h, s:e] + (1 - a[h]) * rl["dQ"][b, h, s:e]
+        _compare(dq[b, h, s:e], ref, f"dQ rows of block {i}, head {h}")
+    G = O.as_f64(dO)
+    dvd = dv.cpu().double().numpy()
+    for h in range(H):
+        err = np.abs(dvd[0, h].sum(0) - G[0, h].sum(0)).max() / np.abs(G[0, h]).sum(0).max()
+        print(f"  head {h}: sum dV vs sum dO: {err:.3g} of sum|dO|")
+        assert err <= 1e-2
