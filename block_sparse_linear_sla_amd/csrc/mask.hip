@@ -16,8 +16,10 @@
 //
 // Pipeline (six launches, no host synchronisation):
 //   pool      one workgroup per (b, h, block) of Q and of K   - HBM bound
-//   router    pooled rows times W                               (optional)
-//   score     per (b, h) 64x64-tiled float64 MFMA product q_hat k_hat^T / sqrt(d)
+//   router    W_q W_k^T, then the pooled Q rows times it           (optional;
+//             (q W_q).(k W_k) taken as (q W_q W_k^T).k)
+//   score     per (b, h) 64x64-tiled float64 MFMA product q_hat k_bar^T / sqrt(d)
+//             (q_hat = q_bar, or q_bar W_q W_k^T with the router)
 //   select    one wavefront per mask row: softmax, radix descent to the Top-k
 //             and Top-p cut points, n = max(k, kp), bitmask of the kept blocks
 //   scan      one workgroup: exclusive scan of the per-row counts -> row_ptr
@@ -116,10 +118,21 @@ __global__ __launch_bounds__(kThreads) void pool_kernel(const T* __restrict__ Q,
   }
 }
 
-// y[m, :] = x[m, :] . W   (row vector times the [D, D] router matrix).
+// W_qk = W_q W_k^T in float64 (row a: one workgroup; column b: one thread).
+// The products of two float32 values are exact in float64.
 template <int D>
+__global__ __launch_bounds__(D) void router_pair_kernel(const float* __restrict__ Wq, const float* __restrict__ Wk,
+                                                        double* __restrict__ Wqk) {
+  const int a = blockIdx.x, b = threadIdx.x;
+  double acc = 0.0;
+  for (int c = 0; c < D; ++c) acc = fma((double)Wq[a * D + c], (double)Wk[b * D + c], acc);
+  Wqk[a * D + b] = acc;
+}
+
+// y[m, :] = x[m, :] . W   (row vector times a [D, D] matrix).
+template <int D, typename TW>
 __global__ __launch_bounds__(kThreads) void router_kernel(const double* __restrict__ x,
-                                                          const float* __restrict__ W,
+                                                          const TW* __restrict__ W,
                                                           double* __restrict__ y, long long M) {
   constexpr int ROWS = 32;
   constexpr int G = kThreads / D;  // row groups
@@ -871,23 +884,23 @@ hipError_t launch_scores(const Shape& s, const float* Wq, const float* Wk, const
   const double* qh = qbar;
   const double* kh = kbar;
   if (Wq != nullptr) {
+    // (q_bar W_q) . (k_bar W_k) = (q_bar W_q W_k^T) . k_bar: one projection,
+    // of the query side (half as many rows as the key side), through the
+    // product of the two matrices
     double* qhat = reinterpret_cast<double*>(ws + L.qhat);
-    double* khat = reinterpret_cast<double*>(ws + L.khat);
-    const long long Mq = BH * s.Nq, Mk = BH * s.Nk;
+    double* wqk = reinterpret_cast<double*>(ws + L.wqk);
+    const long long Mq = BH * s.Nq;
     if (s.d == 128) {
-      hipLaunchKernelGGL((router_kernel<128>), dim3((unsigned)((Mq + 31) / 32)), dim3(kThreads), 0,
-                         st, qbar, Wq, qhat, Mq);
-      hipLaunchKernelGGL((router_kernel<128>), dim3((unsigned)((Mk + 31) / 32)), dim3(kThreads), 0,
-                         st, kbar, Wk, khat, Mk);
+      hipLaunchKernelGGL((router_pair_kernel<128>), dim3(128), dim3(128), 0, st, Wq, Wk, wqk);
+      hipLaunchKernelGGL((router_kernel<128, double>), dim3((unsigned)((Mq + 31) / 32)), dim3(kThreads), 0,
+                         st, qbar, wqk, qhat, Mq);
     } else {
-      hipLaunchKernelGGL((router_kernel<64>), dim3((unsigned)((Mq + 31) / 32)), dim3(kThreads), 0,
-                         st, qbar, Wq, qhat, Mq);
-      hipLaunchKernelGGL((router_kernel<64>), dim3((unsigned)((Mk + 31) / 32)), dim3(kThreads), 0,
-                         st, kbar, Wk, khat, Mk);
+      hipLaunchKernelGGL((router_pair_kernel<64>), dim3(64), dim3(64), 0, st, Wq, Wk, wqk);
+      hipLaunchKernelGGL((router_kernel<64, double>), dim3((unsigned)((Mq + 31) / 32)), dim3(kThreads), 0,
+                         st, qbar, wqk, qhat, Mq);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     qh = qhat;
-    kh = khat;
   }
 
   const int tiles_j = (s.Nk + 31) / 32, tiles = ((s.Nq + 31) / 32) * tiles_j;

@@ -40,7 +40,7 @@ WsLayout ws_layout(const Shape& s, bool router) {
   L.qbar = take(BH * s.Nq * s.d * sizeof(double));
   L.kbar = take(BH * s.Nk * s.d * sizeof(double));
   L.qhat = router ? take(BH * s.Nq * s.d * sizeof(double)) : 0;
-  L.khat = router ? take(BH * s.Nk * s.d * sizeof(double)) : 0;
+  L.wqk = router ? take((size_t)s.d * s.d * sizeof(double)) : 0;
   L.S = take(BH * s.Nq * s.Nk * sizeof(double));
   L.counts = take((size_t)s.R() * sizeof(int32_t));
   L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));

@@ -19,7 +19,8 @@ struct Shape {
 // Byte offsets of the workspace regions (all 256-byte aligned).
 struct WsLayout {
   size_t qbar, kbar;   // pooled means, double [B*H*Nq*d], [B*H*Nk*d]
-  size_t qhat, khat;   // routed pooled vectors (router only), same sizes
+  size_t qhat;         // router only: q_bar W_q W_k^T, double [B*H*Nq*d]
+  size_t wqk;          // router only: W_q W_k^T, double [d*d]
   size_t S;            // pooled logits, double [B*H*Nq*Nk]
   size_t counts;       // int32 [R]
   size_t bits;         // uint32 [R * words]
