@@ -790,29 +790,49 @@ __global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict
   }
 }
 
-// Exclusive scan of counts[R] into row_ptr[R + 1] with one workgroup.
+// Exclusive scan of counts[R] into row_ptr[R + 1] with one workgroup of 1024
+// threads, 4096 counts per pass: each thread loads 4 consecutive counts, the
+// thread totals are scanned within each wavefront (shuffles) and across the 16
+// wavefronts (LDS), and a running carry joins the passes.
 __global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts, long long R,
                                                     int* __restrict__ row_ptr) {
-  __shared__ long long part[1024];
-  const int tid = threadIdx.x;
-  const long long per = (R + 1023) / 1024;
-  const long long b = tid * per, e = min(R, b + per);
-  long long s = 0;
-  for (long long r = b; r < e; ++r) s += counts[r];
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const long long add = (tid >= off) ? part[tid - off] : 0;
+  __shared__ int wtot[16];
+  __shared__ int ttot;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int carry = 0;  // sum of the counts of the earlier passes (the same in every thread)
+  for (long long t0 = 0; t0 < R; t0 += 4096) {
+    const long long i0 = t0 + 4 * (long long)tid;
+    int v[4];
+    if (i0 + 3 < R) {
+      const int4 q = *reinterpret_cast<const int4*>(counts + i0);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = i0 + e < R ? counts[i0 + e] : 0;
+    }
+    const int tsum = v[0] + v[1] + v[2] + v[3];
+    int incl = tsum;  // inclusive scan of the thread totals within the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int up = __shfl_up(incl, off);
+      if (lane >= off) incl += up;
+    }
+    if (lane == 63) wtot[wv] = incl;
     __syncthreads();
-    part[tid] += add;
-    __syncthreads();
+    int before = 0;  // totals of the earlier wavefronts of this pass
+    for (int u = 0; u < wv; ++u) before += wtot[u];
+    if (tid == 1023) ttot = before + incl;
+    int run = carry + before + incl - tsum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e < R) row_ptr[i0 + e] = run;
+      run += v[e];
+    }
+    __syncthreads();  // ttot written; wtot free for the next pass
+    carry += ttot;
+    __syncthreads();  // every thread has read ttot
   }
-  long long run = (tid > 0) ? part[tid - 1] : 0;
-  for (long long r = b; r < e; ++r) {
-    row_ptr[r] = (int)run;
-    run += counts[r];
-  }
-  if (tid == 1023) row_ptr[R] = (int)part[1023];
+  if (tid == 0) row_ptr[R] = carry;
 }
 
 // One wavefront per row: bitmask words -> ascending block indices.
