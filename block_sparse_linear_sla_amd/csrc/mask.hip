@@ -973,15 +973,27 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
   hipError_t e = launch_scores(s, Wq, Wk, Q, K, S, ws, L, st, kdone);
   if (e != hipSuccess) return e;
 
-  int E = 1;
-  while (64 * E < s.Nk) E <<= 1;
+  // blocks per lane: the smallest listed E with 64 E >= Nk (element j of a row
+  // is lane j % 64, slot j / 64; slots past Nk are invalid and cost work)
+  static constexpr int kE[] = {1, 2, 4, 8, 12, 16, 20, 24, 32, 40, 48, 64};
+  int E = 64;
+  for (int c : kE)
+    if (64 * c >= s.Nk) {
+      E = c;
+      break;
+    }
   switch (E) {
     case 1: e = launch_select<1>(S, R, s.Nk, k, p, counts, bits, W, st); break;
     case 2: e = launch_select<2>(S, R, s.Nk, k, p, counts, bits, W, st); break;
     case 4: e = launch_select<4>(S, R, s.Nk, k, p, counts, bits, W, st); break;
     case 8: e = launch_select<8>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 12: e = launch_select<12>(S, R, s.Nk, k, p, counts, bits, W, st); break;
     case 16: e = launch_select<16>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 20: e = launch_select<20>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 24: e = launch_select<24>(S, R, s.Nk, k, p, counts, bits, W, st); break;
     case 32: e = launch_select<32>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 40: e = launch_select<40>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    case 48: e = launch_select<48>(S, R, s.Nk, k, p, counts, bits, W, st); break;
     default: e = launch_select<64>(S, R, s.Nk, k, p, counts, bits, W, st); break;
   }
   if (e != hipSuccess) return e;

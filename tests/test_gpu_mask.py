@@ -30,6 +30,10 @@ SMALL = [
     ("bf16-long-prefix", "bf16", 8192, 128, 128, 64, 0.6, 0.5, False),
     # Top-p decides the count (k = 1)
     ("bf16-p-dominant", "bf16", 3000, 128, 128, 64, 0.02, 0.95, False),
+    # blocks per lane that are not powers of two: Nk = 625 (12 per lane) and
+    # Nk = 1400 (24 per lane)
+    ("bf16-Nk625", "bf16", 40000, 128, 128, 64, 0.05, 0.7, False),
+    ("bf16-Nk1400", "bf16", 89600, 64, 128, 64, 0.03, 0.6, False),
 ]
 
 
