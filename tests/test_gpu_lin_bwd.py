@@ -214,3 +214,27 @@ def test_attn_bwd_480p_two_heads():
         err = np.abs(dvd[0, h].sum(0) - G[0, h].sum(0)).max() / np.abs(G[0, h]).sum(0).max()
         print(f"  head {h}: sum dV vs sum dO: {err:.3g} of sum|dO|")
         assert err <= 1e-2
+
+
+def test_attn_bwd_two_batches():
+    """B = 2: the (b, h) slices of every kernel of the backward (the mask
+    transpose, the row and column walks, the per-head totals) index past the
+    first batch."""
+    N, d, bq, bk = 700, 64, 64, 64
+    print(f"[lin-bwd] mixed B=2 N={N}", flush=True)
+    wl = gen.Workload("adhoc", B=2, H=2, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+                      dtype="bf16", router=False, alpha=(0.8, 0.4), seed=37)
+    x = gen.make(wl)
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp, ci = _random_csr(np.random.default_rng(14), 4, Nq, Nk, 0.3, empty_rows={5},
+                         full_rows={4 * Nq - 1})
+    q, k, v, dO, rpt, cit = _inputs(x, rp, ci, seed=11)
+    alpha = torch.tensor([0.8, 0.4], dtype=torch.float32)
+    dq, dk, dv = S.sla_attn_bwd(q, k, v, dO.cuda(), alpha.cuda(), bq, bk, rpt, cit)
+    torch.cuda.synchronize()
+    rs = O.sparse_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
+    rl = O.linear_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
+    a = alpha.double().numpy()[None, :, None, None]
+    for t, n in zip((dq, dk, dv), ("dQ", "dK", "dV")):
+        _compare(t, a * rs[n] + (1 - a) * rl[n], n)
+        _compare(t[1:], (a * rs[n] + (1 - a) * rl[n])[1:], n + " (second batch)")
