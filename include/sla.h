@@ -1,5 +1,6 @@
 /*
- * sla.h - C interface of the MI355X (gfx950) sparse + linear attention forward.
+ * sla.h - C interface of the MI355X (gfx950) sparse + linear attention: the
+ * forward, its 8-bit sparse branch, the SoftTop-k weights and the backward.
  *
  * The library computes, for attention inputs Q, K, V of shape [B, H, N, d]:
  *
@@ -17,7 +18,10 @@
  *   3. the linear branch: linear attention with phi(x) = elu(x) + 1 over the
  *      keys of the blocks NOT selected (SLA2 write-up §一), and the mix
  *      O = alpha_h * O_sparse + (1 - alpha_h) * O_linear with one alpha per
- *      head (SLA2 write-up §二).
+ *      head (SLA2 write-up §二);
+ *   4. with the mask held fixed, the gradients of both branches, of the mix
+ *      and of alpha (SLA2 write-up §四: training with the selection fixed
+ *      per step), bf16.
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller.  Q, K, V and
