@@ -124,7 +124,8 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
 /* Sparse branch alone (SLA2 write-up §一): O_s[t] = softmax over the keys of the
  * blocks listed in row (b, h, t / bq) of the mask, of q_t . k / sqrt(d), times V.
  * Rows with no selected block are written as 0.  Output O_s [B, H, N, d].
- * Needs the workspace (the bf16 path stages a transposed copy of V there). */
+ * Takes the workspace like the other calls (>= sla_workspace_bytes); the
+ * sparse branch itself reads K and V as they are and keeps nothing there. */
 int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
                    const int32_t* row_ptr, const int32_t* col_idx, void* O_s,
                    void* ws, size_t ws_bytes, void* stream);
