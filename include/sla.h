@@ -189,7 +189,6 @@ int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const v
 int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
                   void* ws, size_t ws_bytes, void* stream);
 
-/* Static text for a status code. */
 /* ---- 8-bit sparse branch (SLA2 write-up §三: the sparse branch holds Q, K,
  * the attention probabilities P and V as 8-bit integers, scaled into the
  * 8-bit range and scaled back).  The granularity and rounding, which that
@@ -298,6 +297,7 @@ int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const vo
 int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* Static text for a status code. */
 const char* sla_status_string(int status);
 
 #ifdef __cplusplus
