@@ -18,7 +18,7 @@
 //   pool      one workgroup per (b, h, block) of Q and of K   - HBM bound
 //   router    W_q W_k^T, then the pooled Q rows times it           (optional;
 //             (q W_q).(k W_k) taken as (q W_q W_k^T).k)
-//   score     per (b, h) 64x64-tiled float64 MFMA product q_hat k_bar^T / sqrt(d)
+//   score     per (b, h) 32x32-tiled float64 MFMA product q_hat k_bar^T / sqrt(d)
 //             (q_hat = q_bar, or q_bar W_q W_k^T with the router)
 //   select    one wavefront per mask row: softmax, radix descent to the Top-k
 //             and Top-p cut points, n = max(k, kp), bitmask of the kept blocks
