@@ -112,6 +112,48 @@ def test_mask_720p():
     print(f"  sparsity {1 - rp[-1] / float(wl.B * wl.H * wl.Nq * wl.Nk):.4f}, excused {excused}")
 
 
+TIES = [
+    # name, dtype, N, d, bq, bk, k_frac, p (N a multiple of bk: every key block full)
+    ("fp32-ties-Nk16", "fp32", 1024, 64, 64, 64, 0.1, 0.5),
+    ("bf16-ties-Nk512", "bf16", 32768, 128, 128, 64, 0.03, 0.5),
+    ("bf16-ties-Nk512-p0.2", "bf16", 32768, 128, 128, 64, 0.03, 0.2),
+]
+
+
+@pytest.mark.parametrize("case", TIES, ids=[c[0] for c in TIES])
+def test_mask_exact_ties(case):
+    """Exactly tied pooled keys, decided by the lower block index on both sides,
+    so the CSR must equal the oracle's with nothing excused.  Head 0 has Q = 0:
+    every logit is 0 and P = 1/Nk exactly (Nk a power of two, so every partial
+    sum is exact), so every row keeps blocks 0 .. max(ceil(k_frac Nk),
+    ceil(p Nk)) - 1 (256 blocks at Nk = 512 and p = 0.5, past the
+    one-at-a-time selection).  Head 1 repeats key blocks 0..3 over the row
+    (four groups of equal P, the cut inside the top group); head 2 is the
+    random control."""
+    name, dtype, N, d, bq, bk, k_frac, p = case
+    print(f"[mask] {name}", flush=True)
+    x = _small_inputs(dtype, N, d, bq, bk, k_frac, p, False)
+    B, H = x.Q.shape[:2]
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    assert N == Nk * bk and Nk % 4 == 0
+    x.Q[:, 0] = 0
+    kb = x.K[:, 1].reshape(B, Nk, bk, d)
+    x.K[:, 1] = kb[:, :4].repeat(1, Nk // 4, 1, 1).reshape(B, N, d)
+    q, k = U.dev(x.Q, x.K)
+    rp, ci = S.sla_mask(q, k, bq, bk, k_frac, p)
+    torch.cuda.synchronize()
+    rp_g, ci_g = U.csr(rp, ci)
+    rp_o, ci_o, _ = U.oracle_mask_per_head(x, k_frac, p, keep_info=False)
+    U.check_csr_structure(rp_g, ci_g, B * H * Nq, Nk)
+    n0 = max(int(np.ceil(k_frac * Nk)), int(np.ceil(p * Nk - 1e-9)))
+    for b in range(B):
+        for i in range(Nq):
+            r = (b * H + 0) * Nq + i
+            assert np.array_equal(ci_g[rp_g[r]:rp_g[r + 1]], np.arange(n0)), f"head 0 row {r}"
+    assert np.array_equal(rp_g, rp_o), "row counts differ from the oracle"
+    assert np.array_equal(ci_g, ci_o), "column indices differ from the oracle"
+
+
 def test_mask_deterministic():
     wl = gen.WORKLOADS["video480p-sla2-N32760"]
     x = gen.make(wl, heads=2)
