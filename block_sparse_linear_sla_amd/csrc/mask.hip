@@ -20,8 +20,9 @@
 //             (q W_q).(k W_k) taken as (q W_q W_k^T).k)
 //   score     per (b, h) 32x32-tiled float64 MFMA product q_hat k_bar^T / sqrt(d)
 //             (q_hat = q_bar, or q_bar W_q W_k^T with the router)
-//   select    one wavefront per mask row: softmax, radix descent to the Top-k
-//             and Top-p cut points, n = max(k, kp), bitmask of the kept blocks
+//   select    one wavefront per mask row: softmax, the kept prefix taken in
+//             order while it is short (else a radix descent to the Top-k and
+//             Top-p cut points), n = max(k, kp), bitmask of the kept blocks
 //   scan      one workgroup: exclusive scan of the per-row counts -> row_ptr
 //   emit      one wavefront per row: bitmask -> ascending col_idx
 #include <cfloat>
@@ -259,9 +260,10 @@ __device__ __forceinline__ int wave_min_int(int v) {
 // The order is P descending with ties to the lower block index; Top-k keeps
 // the first k, Top-p the first kp where kp is the smallest count whose
 // cumulative mass reaches p, the union keeps the first max(k, kp) [SA2 §一].
-// Both cut points are found without sorting, by an 8-pass radix descent over
-// the key bytes with per-wavefront LDS histograms: by count for Top-k, by mass
-// for Top-p.  Mass is accumulated in 2^-62 fixed point, so the sums are exact
+// While the kept prefix is short (at most 64 blocks) it is taken one key at a
+// time from per-lane sorted lists; otherwise both cut points are found
+// without sorting, by an 8-pass radix descent over the key bytes with
+// per-wavefront LDS histograms: by count for Top-k, by mass for Top-p.  Mass is accumulated in 2^-62 fixed point, so the sums are exact
 // and independent of the order the lanes add them in (the result is
 // bit-for-bit repeatable); it differs from a sequential float64 cumulative
 // sum by at most Nk * 2^-62.  Equal keys at the cut are taken in ascending
@@ -427,6 +429,111 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(b[0], b[1]);
 }
 
+// Wavefront sums and maxima of 64-bit values through the same DPP butterflies
+// (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror) and the
+// 16- and 32-lane permlane swaps: every step combines a lane's value with its
+// partner's, and the partner combines the same two numbers, so all 64 lanes
+// end with bit-identical results (callers branch on them) at a few cycles per
+// step.
+__device__ __forceinline__ double f64_of(uint32_t lo, uint32_t hi) {
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ unsigned long long u64_of(uint32_t lo, uint32_t hi) {
+  return ((unsigned long long)hi << 32) | lo;
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long u) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return u64_of(lo, hi);
+}
+// Op(a, b) over the wavefront for a commutative Op on 64-bit patterns.
+template <class Op>
+__device__ __forceinline__ unsigned long long wave_fold_u64(unsigned long long u, Op op) {
+  u = op(u, dpp_u64<0xB1>(u));
+  u = op(u, dpp_u64<0x4E>(u));
+  u = op(u, dpp_u64<0x141>(u));
+  u = op(u, dpp_u64<0x140>(u));
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    u = op(u64_of(a[0], b[0]), u64_of(a[1], b[1]));
+  }
+  {
+    const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
+    u = op(u64_of(a[0], b[0]), u64_of(a[1], b[1]));
+  }
+  return u;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  return __longlong_as_double((long long)wave_fold_u64(
+      (unsigned long long)__double_as_longlong(v), [](unsigned long long a, unsigned long long b) {
+        return (unsigned long long)__double_as_longlong(__longlong_as_double((long long)a) +
+                                                       __longlong_as_double((long long)b));
+      }));
+}
+__device__ __forceinline__ double wave_max_f64(double v) {
+  return __longlong_as_double((long long)wave_fold_u64(
+      (unsigned long long)__double_as_longlong(v), [](unsigned long long a, unsigned long long b) {
+        return (unsigned long long)__double_as_longlong(
+            fmax(__longlong_as_double((long long)a), __longlong_as_double((long long)b)));
+      }));
+}
+// exact (the callers' totals stay below 2^64)
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+  return wave_fold_u64(v, [](unsigned long long a, unsigned long long b) { return a + b; });
+}
+
+// This lane's E values in descending order: Batcher's odd-even merge network
+// over the next power of two, with the comparators that reach past E left out
+// (those would meet padding below every value, which stays in place).
+template <int E>
+__device__ __forceinline__ void sort_desc(unsigned long long (&m)[E]) {
+  constexpr int P2 = E <= 1 ? 1 : E <= 2 ? 2 : E <= 4 ? 4 : E <= 8 ? 8 : E <= 16 ? 16 : 32;
+#pragma unroll
+  for (int p = 1; p < P2; p <<= 1)
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1)
+#pragma unroll
+      for (int j = k % p; j + k < P2; j += 2 * k)
+#pragma unroll
+        for (int i = 0; i < k; ++i) {
+          const int a = i + j, b = i + j + k;
+          if (b < E && b < P2 && a / (2 * p) == b / (2 * p)) {
+            const unsigned long long x = m[a], y = m[b];
+            const bool s = y > x;
+            m[a] = s ? y : x;
+            m[b] = s ? x : y;
+          }
+        }
+}
+
+// Mask bits of one row: every valid block when all, else those whose key is
+// above the cut key, and of the blocks whose key equals it the first
+// ties_needed in block order (ranked with ballots).
+template <int E>
+__device__ __forceinline__ void emit_row_bits(const unsigned long long (&key)[E], unsigned long long valid_bits,
+                                              bool all, int nsel, unsigned long long ckey, int ties_needed,
+                                              int lane, uint32_t* __restrict__ brow, int W) {
+  int ties_before = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const bool valid = (valid_bits >> e) & 1ull;
+    const bool gt = valid && nsel > 0 && key[e] > ckey;
+    const bool eq = valid && nsel > 0 && key[e] == ckey;
+    const unsigned long long eqm = __ballot(eq);
+    const int rank = ties_before + __popcll(eqm & ((1ull << lane) - 1ull));
+    const bool sel = all ? valid : (gt || (eq && rank < ties_needed));
+    ties_before += __popcll(eqm);
+    const unsigned long long sm = __ballot(sel);
+    if (lane == 0) {
+      if (2 * e < W) brow[2 * e] = (uint32_t)(sm & 0xffffffffull);
+      if (2 * e + 1 < W) brow[2 * e + 1] = (uint32_t)(sm >> 32);
+    }
+  }
+}
+
 template <int E>
 __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ S, long long R, int Nk,
                                                      int k, double p, int* __restrict__ counts,
@@ -440,6 +547,9 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   unsigned long long* hmass = hmass_all[wv];
   const double* srow = S + (size_t)row * Nk;
 
+  // Straight-line per-element work (every lane loads, exponentiates and
+  // divides all E of its elements; padding becomes exp(-inf) = 0), so the E
+  // independent chains overlap.
   double sv[E];
   unsigned long long valid_bits = 0;
   double mx = -INFINITY;
@@ -447,119 +557,85 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   for (int e = 0; e < E; ++e) {
     const int j = lane + 64 * e;
     const bool ok = j < Nk;
-    sv[e] = ok ? srow[j] : -INFINITY;
+    const double s = srow[ok ? j : 0];
+    sv[e] = ok ? s : -INFINITY;
     valid_bits |= (ok ? 1ull : 0ull) << e;
     mx = fmax(mx, sv[e]);
   }
-  mx = wave_max(mx);
+  mx = wave_max_f64(mx);
   double z = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    sv[e] = ((valid_bits >> e) & 1ull) ? exp(sv[e] - mx) : 0.0;
+    sv[e] = exp(sv[e] - mx);
     z += sv[e];
   }
-  z = wave_sum(z);
-  unsigned long long key[E];
+  z = wave_sum_f64(z);
+  unsigned long long key[E];  // padding: +0.0, key 0
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    key[e] = ((valid_bits >> e) & 1ull) ? (unsigned long long)__double_as_longlong(sv[e] / z) : 0ull;
+  for (int e = 0; e < E; ++e) key[e] = (unsigned long long)__double_as_longlong(sv[e] / z);
 
   const int kk = min(k, Nk);
   const unsigned long long target = p > 0.0 ? (unsigned long long)ceil(p * kMassScale) : 0ull;
   unsigned long long tot = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e)
-    if ((valid_bits >> e) & 1ull) tot += mass_of(key[e]);
-  tot = __shfl(wave_incl_scan(tot, lane), 63);
+  for (int e = 0; e < E; ++e) tot += mass_of(key[e]);  // mass_of(0) = 0
+  tot = wave_sum_u64(tot);
   const bool p_never = p > 0.0 && tot < target;  // p is never reached: every block
+  uint32_t* brow = bits + (size_t)row * W;
 
-  // Fast path: take the blocks one at a time in the selection order (largest
-  // P first, ties to the lower block index) until both the count reaches k
-  // and the mass reaches p; the taken prefix is then exactly the first
-  // max(k, kp).  Used while that prefix is short and a row has at most 1024
-  // blocks (E <= 16, for registers); the rest take the radix descent below.
+  // Fast path: take the keys one at a time in descending order until both
+  // the count reaches k and the mass reaches p; the taken prefix is then
+  // exactly the first max(k, kp) in the selection order.  Each lane sorts its
+  // own keys once, so a step compares the 64 list heads only.  Equal keys are
+  // interchangeable while counting: the step records the last key taken and
+  // how many of the taken keys equal it, and the blocks kept among equal keys
+  // are then chosen in block order.  Used while that prefix is short and a
+  // row has at most 1024 blocks (E <= 16, for registers); the rest take the
+  // radix descent below.
   constexpr int kFastMax = 64;
   if (E <= 16 && !p_never && kk < Nk) {
-    // key + 1 of the untaken blocks as high / low words, 0 for none (the P
-    // bit patterns are below 2^62); a taken block's words become 0
-    uint32_t kh[E], kl[E];
+    unsigned long long m[E];  // key + 1, 0 for padding and for keys taken
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const unsigned long long m = ((valid_bits >> e) & 1ull) ? key[e] + 1ull : 0ull;
-      kh[e] = (uint32_t)(m >> 32);
-      kl[e] = (uint32_t)m;
-    }
-    unsigned long long taken = 0ull;
-    unsigned long long mass = 0;  // wave-uniform
-    int n = 0;
+    for (int e = 0; e < E; ++e) m[e] = ((valid_bits >> e) & 1ull) ? key[e] + 1ull : 0ull;
+    sort_desc<E>(m);
+    unsigned long long mass = 0, last = 0;  // wave-uniform
+    int n = 0, run = 0;
     bool done = true;
     while (n < kk || (p > 0.0 && mass < target)) {
       if (n == kFastMax) {
         done = false;
         break;
       }
-      // the largest high word, then the blocks that hold it
-      uint32_t h = kh[0];
-#pragma unroll
-      for (int e = 1; e < E; ++e) h = max(h, kh[e]);
+      // the largest high word among the heads, then (when several heads
+      // share it) the largest low word among those
+      const uint32_t h = (uint32_t)(m[0] >> 32), l = (uint32_t)m[0];
       const uint32_t th = wave_max_u32(h);
-      unsigned hit = 0u;
-#pragma unroll
-      for (int e = 0; e < E; ++e) hit |= (kh[e] == th ? 1u : 0u) << e;
+      unsigned long long el = __ballot(h == th);
       uint32_t tl;
-      const unsigned long long hl = __ballot(hit != 0u);
-      if (__ballot(__popc(hit) > 1) != 0ull || __popcll(hl) > 1) {
-        // several blocks share it: the largest low word among them
-        uint32_t l = 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) l = ((hit >> e) & 1u) ? max(l, kl[e]) : l;
-        tl = wave_max_u32(l);
-        unsigned h2 = 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) h2 |= (((hit >> e) & 1u) && kl[e] == tl ? 1u : 0u) << e;
-        hit = h2;
+      if (__popcll(el) > 1) {
+        tl = wave_max_u32(h == th ? l : 0u);
+        el = __ballot(h == th && l == tl);
       } else {
-        // a single block: its low word, read from its lane
-        uint32_t l = 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) l = ((hit >> e) & 1u) ? kl[e] : l;
-        tl = (uint32_t)__builtin_amdgcn_readlane((int)l, __ffsll((long long)hl) - 1);
+        tl = (uint32_t)__builtin_amdgcn_readlane((int)l, __ffsll((long long)el) - 1);
       }
-      // the first block of this lane holding the maximum (the lower index on
-      // equal keys), the lowest such lane in the wavefront
-      const int ef = __ffs(hit) - 1;
-      const unsigned long long tm = __ballot(hit != 0u);
-      int owner = __ffsll((long long)tm) - 1;
-      if (__popcll(tm) > 1) {
-        const int jmin = wave_min_int(hit != 0u ? lane + 64 * ef : 0x7fffffff);
-        owner = jmin & 63;
-      }
-      if (lane == owner) {
-        taken |= 1ull << ef;
+      if (lane == __ffsll((long long)el) - 1) {  // one holder of the maximum gives it up
 #pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (e == ef) {
-            kh[e] = 0u;
-            kl[e] = 0u;
-          }
+        for (int e = 0; e + 1 < E; ++e) m[e] = m[e + 1];
+        m[E - 1] = 0ull;
       }
       const unsigned long long top = (((unsigned long long)th << 32) | tl) - 1ull;
+      run = (n > 0 && top == last) ? run + 1 : 1;
+      last = top;
       mass += mass_of(top);
       ++n;
     }
     if (done) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const unsigned long long sm = __ballot((taken >> e) & 1ull);
-        if (lane == 0) {
-          if (2 * e < W) bits[(size_t)row * W + 2 * e] = (uint32_t)(sm & 0xffffffffull);
-          if (2 * e + 1 < W) bits[(size_t)row * W + 2 * e + 1] = (uint32_t)(sm >> 32);
-        }
-      }
+      emit_row_bits<E>(key, valid_bits, n >= Nk, n, last, run, lane, brow, W);
       if (lane == 0) counts[row] = n;
       return;
     }
   }
+
 
   unsigned long long kkey = 0, kw = 0, pkey = 0, pw = 0;
   unsigned kabove = 0, ktie = 0, pabove = 0, ptie = 0;
@@ -583,24 +659,7 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
   const unsigned long long ckey = (nsel == kk) ? kkey : pkey;
   const int ties_needed = nsel - (int)((nsel == kk) ? kabove : pabove);
 
-  // kept: every valid block when all, else key > cut, or key == cut and among
-  // the first ties_needed such blocks in block order
-  int ties_before = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const bool valid = (valid_bits >> e) & 1ull;
-    const bool gt = valid && nsel > 0 && key[e] > ckey;
-    const bool eq = valid && nsel > 0 && key[e] == ckey;
-    const unsigned long long eqm = __ballot(eq);
-    const int rank = ties_before + __popcll(eqm & ((1ull << lane) - 1ull));
-    const bool sel = all ? valid : (gt || (eq && rank < ties_needed));
-    ties_before += __popcll(eqm);
-    const unsigned long long sm = __ballot(sel);
-    if (lane == 0) {
-      if (2 * e < W) bits[(size_t)row * W + 2 * e] = (uint32_t)(sm & 0xffffffffull);
-      if (2 * e + 1 < W) bits[(size_t)row * W + 2 * e + 1] = (uint32_t)(sm >> 32);
-    }
-  }
+  emit_row_bits<E>(key, valid_bits, all, nsel, ckey, ties_needed, lane, brow, W);
   if (lane == 0) counts[row] = nsel;
 }
 
@@ -615,11 +674,9 @@ __global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ 
 // exponential) to a starting point; plain float64 Newton steps from there
 // converge quadratically (the safeguarded float64 iteration takes over if
 // they do not settle), and the weights are written as float32.
-// Wavefront sums through DPP butterflies (quad_perm [1,0,3,2] and [2,3,0,1],
-// row_half_mirror, row_mirror) and the 16- and 32-lane permlane swaps, as in
-// wave_max_u64: every step adds a lane's value to its partner's, and the
-// partner adds the same two numbers, so all 64 lanes end with bit-identical
-// sums (the iteration below branches on them) at a few cycles per step.
+// Float32 wavefront sums through the butterflies of wave_fold_u64 (bit-identical
+// in every lane: the iteration below branches on them); float64 sums use
+// wave_sum_f64.
 template <int CTRL>
 __device__ __forceinline__ float add_f32_dpp(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
@@ -633,35 +690,6 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-template <int CTRL>
-__device__ __forceinline__ double add_f64_dpp(double v) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
-  return v + __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-__device__ __forceinline__ double f64_of(uint32_t lo, uint32_t hi) {
-  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
-}
-__device__ __forceinline__ double wave_sum_f64(double v) {
-  v = add_f64_dpp<0xB1>(v);
-  v = add_f64_dpp<0x4E>(v);
-  v = add_f64_dpp<0x141>(v);
-  v = add_f64_dpp<0x140>(v);
-  {
-    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)u, (uint32_t)u, false, false);
-    const auto b = __builtin_amdgcn_permlane16_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
-    v = f64_of(a[0], b[0]) + f64_of(a[1], b[1]);
-  }
-  {
-    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
-    const auto a = __builtin_amdgcn_permlane32_swap((uint32_t)u, (uint32_t)u, false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)(u >> 32), (uint32_t)(u >> 32), false, false);
-    v = f64_of(a[0], b[0]) + f64_of(a[1], b[1]);
-  }
-  return v;
 }
 
 __device__ __forceinline__ double sigmoid_f64(double x) {
