@@ -241,17 +241,6 @@ __device__ __forceinline__ double wave_max(double v) {
   for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
   return v;
 }
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ int wave_min_int(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
-}
-
 // ---------------------------------------------------------------- selection
 // One wavefront per mask row (four rows per workgroup, no barriers).  Lane l
 // holds the row's blocks j = l + 64 e, e < E.  P_j = exp(S_j - max) / sum in
@@ -376,44 +365,10 @@ __device__ void radix_cut(const unsigned long long (&key)[E], unsigned long long
   cut_key = prefix;
 }
 
-// Largest 64-bit value over the wavefront, in every lane: quad exchanges and
+// Largest 32-bit value over the wavefront, in every lane: quad exchanges and
 // row mirrors (DPP), then the 16- and 32-lane swaps.  Each step takes the
-// larger of the own value and the partner's, so every lane ends with the
-// same maximum.
-__device__ __forceinline__ void max_u64_step(uint32_t& lo, uint32_t& hi, uint32_t plo, uint32_t phi) {
-  const bool gt = phi > hi || (phi == hi && plo > lo);
-  lo = gt ? plo : lo;
-  hi = gt ? phi : hi;
-}
-template <int CTRL>
-__device__ __forceinline__ void max_u64_dpp(uint32_t& lo, uint32_t& hi) {
-  const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, CTRL, 0xF, 0xF, false);
-  const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, CTRL, 0xF, 0xF, false);
-  max_u64_step(lo, hi, plo, phi);
-}
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  max_u64_dpp<0xB1>(lo, hi);   // quad_perm [1, 0, 3, 2]
-  max_u64_dpp<0x4E>(lo, hi);   // quad_perm [2, 3, 0, 1]
-  max_u64_dpp<0x141>(lo, hi);  // row_half_mirror: the other quad of each 8
-  max_u64_dpp<0x140>(lo, hi);  // row_mirror: the other 8 of each 16
-  {
-    const auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    max_u64_step(lo, hi, a[0], b[0]);  // one of the two outputs is the own value,
-    max_u64_step(lo, hi, a[1], b[1]);  // the other the neighbouring row's
-  }
-  {
-    const auto a = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-    const auto b = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-    max_u64_step(lo, hi, a[0], b[0]);
-    max_u64_step(lo, hi, a[1], b[1]);
-  }
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-// Largest 32-bit value over the wavefront, in every lane (same exchange
-// pattern as wave_max_u64; each DPP step folds into one v_max_u32).
+// larger of the own value and the partner's, so every lane ends with the same
+// maximum (each DPP step folds into one v_max_u32).
 template <int CTRL>
 __device__ __forceinline__ uint32_t max_u32_dpp(uint32_t v) {
   return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
