@@ -232,12 +232,12 @@ def main():
     }
 
     if not args.no_dense:
-        S.sla_dense_fwd(q, k, v, wl.bq, wl.bk, out=out, ws=ws)
+        S.sla_dense_fwd(q, k, v, wl.bq, wl.bk, out=out)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.dense_steps):
-            S.sla_dense_fwd(q, k, v, wl.bq, wl.bk, out=out, ws=ws)
+            S.sla_dense_fwd(q, k, v, wl.bq, wl.bk, out=out)
         e1.record()
         torch.cuda.synchronize()
         t_dense = e0.elapsed_time(e1) / args.dense_steps
@@ -247,12 +247,12 @@ def main():
 
     # the sparse branch alone (sla_sparse_fwd) on this step's mask, for the
     # executed-block rate of the attention kernel
-    S.sla_sparse_fwd(q, k, v, wl.bq, wl.bk, rp, ci, out=out, ws=ws)
+    S.sla_sparse_fwd(q, k, v, wl.bq, wl.bk, rp, ci, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        S.sla_sparse_fwd(q, k, v, wl.bq, wl.bk, rp, ci, out=out, ws=ws)
+        S.sla_sparse_fwd(q, k, v, wl.bq, wl.bk, rp, ci, out=out)
     e1.record()
     torch.cuda.synchronize()
     t_sp = e0.elapsed_time(e1) / args.steps

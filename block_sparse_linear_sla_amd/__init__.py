@@ -71,13 +71,13 @@ def lib() -> ctypes.CDLL:
         L.sla_mask.argtypes = [P, S, vp, vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.c_size_t, vp]
         L.sla_mask_prepared.argtypes = [P, S, vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_size_t, vp]
         L.sla_soft_topk.argtypes = [P, S, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_sparse_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.sla_linear_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_attn_fwd.argtypes = [P, S, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp,
                                    ctypes.c_size_t, vp]
         L.sla_kv_prepare.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_fused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
-        L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp]
         L.sla_i8_layout_of.argtypes = [P, ctypes.POINTER(I8Layout)]
         L.sla_quantize_i8.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_sparse_fwd_i8.argtypes = [P, vp, ctypes.c_size_t, vp, vp, vp, vp]
@@ -214,14 +214,12 @@ def sla_soft_topk(q, k, bq: int, bk: int, k_frac: float, T: float, wq=None, wk=N
     return m
 
 
-def sla_sparse_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None, ws=None):
+def sla_sparse_fwd(q, k, v, bq: int, bk: int, row_ptr, col_idx, out=None):
     _need(q, k, v, like=q)
     prob = problem(q, bq, bk)
     o = out if out is not None else torch.empty_like(q)
-    w = ws if ws is not None else workspace(prob, None, q.device)
     _check("sla_sparse_fwd", lib().sla_sparse_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v),
-                                                  _ptr(row_ptr), _ptr(col_idx), _ptr(o), _ptr(w),
-                                                  w.numel(), _stream()))
+                                                  _ptr(row_ptr), _ptr(col_idx), _ptr(o), _stream()))
     return o
 
 
@@ -277,13 +275,12 @@ def sla_fused_fwd(q, k, v, alpha, bq: int, bk: int, row_ptr, col_idx, ws: torch.
     return o
 
 
-def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None, ws=None):
+def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None):
     _need(q, k, v, like=q)
     prob = problem(q, bq, bk)
     o = out if out is not None else torch.empty_like(q)
-    w = ws if ws is not None else workspace(prob, None, q.device)
     _check("sla_dense_fwd", lib().sla_dense_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                                _ptr(w), w.numel(), _stream()))
+                                                _stream()))
     return o
 
 

@@ -98,8 +98,10 @@ hipError_t run_attn(const Shape& s, Mode m, const void* Q, const void* K, const 
                     const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
                     const WsLayout& L, void* O, hipStream_t st) {
   if (s.dtype == SLA_BF16) return sla::launch_attn_bf16(s, m, Q, K, V, rp, ci, alpha, ws, L, O, st);
+  // the linear totals are read only by the modes with a linear branch
+  const bool lin = m == sla::MODE_FUSED || m == sla::MODE_LINEAR;
   return sla::launch_attn_f32(s, m, Q, K, V, rp, ci, alpha,
-                              reinterpret_cast<const float*>(ws + L.htot), O, st);
+                              lin ? reinterpret_cast<const float*>(ws + L.htot) : nullptr, O, st);
 }
 
 }  // namespace
@@ -171,18 +173,14 @@ int sla_soft_topk(const sla_problem* prob, const sla_select* sel, float T, const
 }
 
 int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
-                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* ws,
-                   size_t ws_bytes, void* stream) {
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream) {
   Shape s;
   int rc = check_problem(prob, &s);
   if (rc != SLA_OK) return rc;
   if (!Q || !K || !V || !row_ptr || !col_idx || !O_s) return SLA_ERR_INVALID_ARG;
-  const WsLayout L = sla::ws_layout(s, false);
-  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  if (run_prep(s, false, K, V, nullptr, w, L, st) != hipSuccess) return SLA_ERR_HIP;
-  return hip_status(run_attn(s, sla::MODE_SPARSE, Q, K, V, row_ptr, col_idx, nullptr, w, L, O_s, st));
+  // the softmax kernels read K and V as they are: no workspace region is used
+  return hip_status(run_attn(s, sla::MODE_SPARSE, Q, K, V, row_ptr, col_idx, nullptr, nullptr, WsLayout{}, O_s,
+                             static_cast<hipStream_t>(stream)));
 }
 
 int sla_linear_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
@@ -251,17 +249,13 @@ int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const v
 }
 
 int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
-                  void* ws, size_t ws_bytes, void* stream) {
+                  void* stream) {
   Shape s;
   int rc = check_problem(prob, &s);
   if (rc != SLA_OK) return rc;
   if (!Q || !K || !V || !O) return SLA_ERR_INVALID_ARG;
-  const WsLayout L = sla::ws_layout(s, false);
-  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* w = static_cast<char*>(ws);
-  if (run_prep(s, false, K, V, nullptr, w, L, st) != hipSuccess) return SLA_ERR_HIP;
-  return hip_status(run_attn(s, sla::MODE_DENSE, Q, K, V, nullptr, nullptr, nullptr, w, L, O, st));
+  return hip_status(run_attn(s, sla::MODE_DENSE, Q, K, V, nullptr, nullptr, nullptr, nullptr, WsLayout{}, O,
+                             static_cast<hipStream_t>(stream)));
 }
 
 int sla_i8_layout_of(const sla_problem* prob, sla_i8_layout* layout) {

@@ -124,11 +124,9 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
 /* Sparse branch alone (SLA2 write-up §一): O_s[t] = softmax over the keys of the
  * blocks listed in row (b, h, t / bq) of the mask, of q_t . k / sqrt(d), times V.
  * Rows with no selected block are written as 0.  Output O_s [B, H, N, d].
- * Takes the workspace like the other calls (>= sla_workspace_bytes); the
- * sparse branch itself reads K and V as they are and keeps nothing there. */
+ * Needs no workspace: K and V are read as they are. */
 int sla_sparse_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V,
-                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s,
-                   void* ws, size_t ws_bytes, void* stream);
+                   const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
 
 /* Linear branch alone (SLA2 write-up §一): O_l[t] = sum_u (phi(q_t).phi(k_u)) v_u /
  * sum_u phi(q_t).phi(k_u) over the keys u of the blocks NOT listed in the row;
@@ -184,10 +182,14 @@ int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const v
                   const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
                   const void* ws, size_t ws_bytes, void* stream);
 
-/* Dense softmax(Q K^T / sqrt(d)) V over every key, the comparator the sparse
- * path is measured against.  Output O [B, H, N, d].  Needs the workspace. */
+/* Dense attention softmax(Q K^T / sqrt(d)) V over every key: the textbook
+ * formula that the explainer page "清华SpargeAttention2技术解析：如何让AI视频
+ * 生成提速16倍" prints in its section 3 (implementation principle) as the
+ * conventional computation the sparse path replaces; here it is the
+ * comparator the sparse path is measured against.  Output O [B, H, N, d] in
+ * the problem dtype (bq, bk only set the tiling).  Needs no workspace. */
 int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
-                  void* ws, size_t ws_bytes, void* stream);
+                  void* stream);
 
 /* ---- 8-bit sparse branch (SLA2 write-up §三: the sparse branch holds Q, K,
  * the attention probabilities P and V as 8-bit integers, scaled into the

@@ -60,11 +60,11 @@ def test_bad_problem(kw, code):
     st = None
     assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, 1 << 30, None,
                       FAKE, 1 << 40, st) == code
-    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, st) == code
+    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, st) == code
     assert L.sla_linear_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, st) == code
     assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                           1 << 30, FAKE, 1 << 40, st) == code
-    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, st) == code
+    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, st) == code
     assert L.sla_kv_prepare(ctypes.byref(p), FAKE, FAKE, None, FAKE, 1 << 40, st) == code
     assert L.sla_fused_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                            st) == code
@@ -105,11 +105,12 @@ def test_null_tensors():
     sel = S.Select(0.1, 0.6, None, None)
     assert L.sla_mask(ctypes.byref(p), ctypes.byref(sel), None, FAKE, FAKE, FAKE, 1 << 30, None, FAKE,
                       1 << 40, None) == INVALID
-    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
+    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == INVALID
+    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == INVALID
     assert L.sla_linear_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == INVALID
     assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
                           1 << 30, FAKE, 1 << 40, None) == INVALID    # alpha
-    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == INVALID
+    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, None) == INVALID
     assert L.sla_kv_prepare(ctypes.byref(p), None, FAKE, None, FAKE, 1 << 40, None) == INVALID
     assert L.sla_fused_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                            None) == INVALID   # alpha
@@ -133,8 +134,6 @@ def test_capacity_and_workspace_checks():
     assert L.sla_attn_fwd(ctypes.byref(p), ctypes.byref(sel), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                           cap - 1, FAKE, need, None) == CAPACITY
     assert L.sla_kv_prepare(ctypes.byref(p), FAKE, FAKE, None, FAKE, 16, None) == WORKSPACE
-    assert L.sla_sparse_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == WORKSPACE
-    assert L.sla_dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, 16, None) == WORKSPACE
     assert L.sla_fused_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16,
                            None) == WORKSPACE
 
