@@ -36,6 +36,39 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+def rule_stats(S, q, k, wl, wq, wk, k_frac: float, p: float, samples):
+    """One selection rule (k_frac, p) on one head set: the library's mask and
+    the quantities of the study.  q, k [1, H, N, d] on the GPU; samples: the
+    (head, query block) pairs of the token-level mass.  Returns (row_ptr,
+    col_idx, stats) with stats = kept (fraction of blocks selected),
+    pooled_mass (mean over rows of the selected blocks' pooled
+    probabilities) and token_mass (mean over the sampled blocks' queries of
+    the exact softmax mass on the selected keys)."""
+    import torch
+    H, N, d = q.shape[1], q.shape[2], q.shape[3]
+    R = H * wl.Nq
+    rp, ci, logits = S.sla_mask(q, k, wl.bq, wl.bk, k_frac, p, wq, wk, return_logits=True)
+    torch.cuda.synchronize()
+    rp_h, ci_h = rp.cpu().long(), ci.cpu().long()
+    P = torch.softmax(logits.reshape(R, wl.Nk), dim=-1).cpu()
+    pooled = 0.0
+    for r in range(R):
+        pooled += P[r, ci_h[rp_h[r]:rp_h[r + 1]]].sum().item()
+    token = 0.0
+    for (h, i) in samples:
+        r = h * wl.Nq + i
+        sel = ci_h[rp_h[r]:rp_h[r + 1]]
+        keep = torch.zeros(N, dtype=torch.bool, device=q.device)
+        for j in sel.tolist():
+            keep[j * wl.bk:min((j + 1) * wl.bk, N)] = True
+        qi = q[0, h, i * wl.bq:min((i + 1) * wl.bq, N)].float()
+        a = torch.softmax(qi @ k[0, h].float().T / d ** 0.5, dim=-1)
+        token += a[:, keep].sum(dim=-1).mean().item()
+    stats = {"kept": int(rp_h[-1]) / (R * wl.Nk), "pooled_mass": pooled / R,
+             "token_mass": token / max(len(samples), 1)}
+    return rp, ci, stats
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--heads", type=int, default=16, help="heads of the first batch entry to generate")
@@ -58,37 +91,18 @@ def main():
         x = gen.make(wl, heads=args.heads)
         q, k, v = (t.to(dev).contiguous() for t in (x.Q, x.K, x.V))
         wq, wk = x.Wq.to(dev), x.Wk.to(dev)
-        H, N, d = q.shape[1], q.shape[2], q.shape[3]
-        R = H * wl.Nq
-        # sampled query blocks (head, block) for the token-level mass
+        H = q.shape[1]
         od = S.sla_dense_fwd(q, k, v, wl.bq, wl.bk)
         od_l1 = od.float().abs().sum().item()
         samp = [(h, int(i)) for h in range(H) for i in torch.randperm(wl.Nq, generator=gsel)[:args.samples]]
         for p in (0.3, 0.6, 0.9):
             res = {"tau": tau, "p": p, "k_frac": wl.k_frac}
             for rule, kf, pp in (("topk", wl.k_frac, 0.0), ("topp", 0.0, p), ("union", wl.k_frac, p)):
-                rp, ci, logits = S.sla_mask(q, k, wl.bq, wl.bk, kf, pp, wq, wk, return_logits=True)
-                torch.cuda.synchronize()
-                rp_h, ci_h = rp.cpu().long(), ci.cpu().long()
-                P = torch.softmax(logits.reshape(R, wl.Nk), dim=-1).cpu()
-                pooled = 0.0
-                for r in range(R):
-                    pooled += P[r, ci_h[rp_h[r]:rp_h[r + 1]]].sum().item()
-                token = 0.0
-                for (h, i) in samp:
-                    r = h * wl.Nq + i
-                    sel = ci_h[rp_h[r]:rp_h[r + 1]]
-                    keep = torch.zeros(N, dtype=torch.bool, device=dev)
-                    for j in sel.tolist():
-                        keep[j * wl.bk:min((j + 1) * wl.bk, N)] = True
-                    qi = q[0, h, i * wl.bq:min((i + 1) * wl.bq, N)].float()
-                    a = torch.softmax(qi @ k[0, h].float().T / d ** 0.5, dim=-1)
-                    token += a[:, keep].sum(dim=-1).mean().item()
+                rp, ci, st = rule_stats(S, q, k, wl, wq, wk, kf, pp, samp)
                 os_ = S.sla_sparse_fwd(q, k, v, wl.bq, wl.bk, rp, ci)
                 res[f"{rule}_rel_l1"] = (os_.float() - od.float()).abs().sum().item() / od_l1
-                res[f"{rule}_kept"] = int(rp_h[-1]) / (R * wl.Nk)
-                res[f"{rule}_pooled_mass"] = pooled / R
-                res[f"{rule}_token_mass"] = token / len(samp)
+                for key, val in st.items():
+                    res[f"{rule}_{key}"] = val
             rows.append(res)
             print(json.dumps(res), flush=True)
     print("\n| tau | p | Top-k: kept / pooled / token mass / rel-L1 | Top-p: kept / pooled / token mass "

@@ -5,7 +5,20 @@ from __future__ import annotations
 import numpy as np
 import torch
 
+import gen
 from oracle import sla_oracle as O
+
+_ROUTER_X = {}
+
+
+def router_inputs(tau):
+    """Inputs of the routed 480p workload at query temperature tau, generated
+    once and kept (one temperature at a time: the sweeps run tau-major, so
+    host memory holds one set)."""
+    if tau not in _ROUTER_X:
+        _ROUTER_X.clear()
+        _ROUTER_X[tau] = gen.make(gen.WORKLOADS["video480p-router-N32760"].with_(tau=tau))
+    return _ROUTER_X[tau]
 
 
 def has_gpu() -> bool:
@@ -107,6 +120,41 @@ def compare_rows(got: dict, ref: dict):
     g = np.concatenate([got[k].ravel() for k in sorted(ref)])
     r = np.concatenate([ref[k].ravel() for k in sorted(ref)])
     return errors(g, r)
+
+
+def xcd_ranges(R, nx=8):
+    """The contiguous mask-row range [start, end) each of the nx XCDs walks
+    under the attention kernels' workgroup-to-row mapping: the first R % nx
+    ranges hold R // nx + 1 rows, the others R // nx."""
+    q, r = divmod(R, nx)
+    out, start = [], 0
+    for x in range(nx):
+        n = q + 1 if x < r else q
+        out.append((start, start + n))
+        start += n
+    return out
+
+
+def pick_rows(rp, B, H, Nq, n=32, seed=0, heads=4):
+    """At least n mask rows (b, h, i) chosen to expose indexing mistakes:
+    the longest and the shortest row (most / fewest listed blocks), the
+    partial last query block of the first, the last and `heads` random
+    heads, the first and the last row of every XCD's range, then random
+    rows up to n."""
+    rng = np.random.default_rng(seed)
+    counts = np.diff(np.asarray(rp, dtype=np.int64))
+    R = B * H * Nq
+    assert len(counts) == R
+    rs = {int(np.argmax(counts)), int(np.argmin(counts)),
+          int(len(counts) - 1 - np.argmax(counts[::-1])), int(len(counts) - 1 - np.argmin(counts[::-1]))}
+    hs = {0, B * H - 1} | {int(v) for v in rng.integers(0, B * H, size=heads)}
+    rs |= {bh * Nq + Nq - 1 for bh in hs}
+    for a, e in xcd_ranges(R):
+        if e > a:
+            rs |= {a, e - 1}
+    while len(rs) < n:
+        rs.add(int(rng.integers(R)))
+    return sorted((r // (H * Nq), (r // Nq) % H, r % Nq) for r in rs)
 
 
 def sample_rows(B, H, Nq, n, seed=0):

@@ -1,6 +1,8 @@
 """GPU parity of the attention entry points against the oracle, with the GPU's
 own mask fed to the oracle.  Bars: fp32 max-abs <= 1e-5; bf16 max-abs <= 2e-2
 and relative L1 (sum |O - O_ref| / sum |O_ref|) <= 5e-3."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -30,7 +32,9 @@ def _adhoc(dtype, N, d, bq, bk, k_frac, p, seed=11, B=2, H=3, alpha=None):
 
 
 def _run_all(x, rows=None):
-    """Mask + every entry point; returns GPU outputs and the oracle's on `rows`."""
+    """Mask + every entry point; returns GPU outputs and the oracle's on
+    `rows` (a list of (b, h, i), a function of the GPU's row_ptr returning
+    one, or None for every row)."""
     wl = x.wl
     q, k, v, a = U.dev(x.Q, x.K, x.V, x.alpha)
     wq, wk = U.dev(x.Wq, x.Wk)
@@ -41,6 +45,8 @@ def _run_all(x, rows=None):
     rp_g, ci_g = U.csr(rp, ci)
     B, H, N, d = x.Q.shape
     Nq = O.n_blocks(N, wl.bq)
+    if callable(rows):
+        rows = rows(rp_g)
     rows = rows or [(b, h, i) for b in range(B) for h in range(H) for i in range(Nq)]
     ref_s = O.sparse_branch(x.Q, x.K, x.V, wl.bq, wl.bk, rp_g, ci_g, rows)
     ref_l = O.linear_branch(x.Q, x.K, x.V, wl.bq, wl.bk, rp_g, ci_g, rows)
@@ -115,12 +121,17 @@ def test_full_mask_is_dense_attention(dtype):
         _bar(dtype, m, r, f"full/{name}")
 
 
-def _full_size(name, n_rows, **over):
+def _full_size(name, n_rows=32, x=None, **over):
+    """Full-size parity on at least n_rows row blocks chosen from the GPU's
+    mask (longest and shortest rows, partial last blocks, the ends of every
+    XCD's row range, random rows); O, O_s and O_l each to the bf16 bar."""
     wl = gen.WORKLOADS[name].with_(**over) if over else gen.WORKLOADS[name]
     print(f"[attn] {wl.name} {over}", flush=True)
-    x = gen.make(wl)
-    rows = U.sample_rows(wl.B, wl.H, wl.Nq, n_rows, seed=1)
-    got, ref, _ = _run_all(x, rows)
+    x = gen.make(wl) if x is None else x
+    pick = lambda rp: U.pick_rows(rp, wl.B, wl.H, wl.Nq, n=n_rows, seed=1)
+    got, ref, (rp, ci) = _run_all(x, pick)
+    counts = np.diff(rp)
+    print(f"  rows {len(ref['o'])}, listed blocks per row {counts.min()}..{counts.max()}")
     for key in ("o", "s", "l"):
         if key == "l" and float(x.alpha.min()) == 1.0:
             continue
@@ -130,20 +141,25 @@ def _full_size(name, n_rows, **over):
 
 
 def test_480p_sparse_only():
-    _full_size("video480p-sparse-N32760", 8)
+    _full_size("video480p-sparse-N32760")
 
 
 def test_480p_sla2():
-    _full_size("video480p-sla2-N32760", 8)
+    _full_size("video480p-sla2-N32760")
 
 
 def test_720p_sla2():
-    _full_size("video720p-sla2-N75600", 6)
+    _full_size("video720p-sla2-N75600")
 
 
-@pytest.mark.parametrize("tau,p", [(0.25, 0.9), (4.0, 0.3)])
+SWEEP = [(t, p) for t in gen.ROUTER_TAUS for p in gen.ROUTER_PS]
+
+
+@pytest.mark.parametrize("tau,p", SWEEP, ids=[f"tau{t}-p{p}" for t, p in SWEEP])
 def test_480p_router(tau, p):
-    _full_size("video480p-router-N32760", 6, tau=tau, p=p)
+    x = U.router_inputs(tau)
+    x = dataclasses.replace(x, wl=x.wl.with_(p=p))
+    _full_size("video480p-router-N32760", x=x, tau=tau, p=p)
 
 
 def test_dense_480p_sampled():

@@ -95,13 +95,20 @@ def test_mask_480p(name):
     print(f"  sparsity {sparsity:.4f}, differing rows {rows}, excused blocks {excused}")
 
 
-@pytest.mark.parametrize("tau,p", [(0.25, 0.9), (1.0, 0.6), (4.0, 0.3)])
+SWEEP = [(t, p) for t in gen.ROUTER_TAUS for p in gen.ROUTER_PS]
+
+
+@pytest.mark.parametrize("tau,p", SWEEP, ids=[f"tau{t}-p{p}" for t, p in SWEEP])
 def test_mask_router_sweep(tau, p):
-    wl = gen.WORKLOADS["video480p-router-N32760"].with_(tau=tau, p=p)
+    """Every point of the distribution sweep: flat pooled maps (tau = 0.25,
+    where Top-p keeps up to about half of the blocks) to peaked ones (tau = 4)."""
+    x = U.router_inputs(tau)
+    wl = x.wl.with_(p=p)
     print(f"[mask] router tau={tau} p={p}", flush=True)
-    x = gen.make(wl)
     rp, ci, excused, rows = run_and_check(x, wl.k_frac, p)
-    print(f"  sparsity {1 - rp[-1] / float(wl.B * wl.H * wl.Nq * wl.Nk):.4f}, excused {excused}")
+    counts = np.diff(rp)
+    print(f"  sparsity {1 - rp[-1] / float(wl.B * wl.H * wl.Nq * wl.Nk):.4f}, blocks per row "
+          f"{counts.min()}..{counts.max()}, excused {excused}")
 
 
 def test_mask_720p():
