@@ -3,8 +3,43 @@
 // device memory to the host or allocates.
 #include <math.h>
 
+#include <mutex>
+
 #include "sla.h"
 #include "sla_internal.h"
+
+namespace {
+
+// Scratch of sla_mask_noalloc: one copy per GPU, resident from the load of
+// the library's code object on that GPU until the process ends.  In host code
+// the name is only a handle for hipGetSymbolAddress; the device address of
+// each GPU's copy is looked up once per device and kept below.
+__device__ __align__(256) char scratch[SLA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device, with the device current).
+hipError_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+}  // namespace
 
 
 namespace sla {
@@ -37,6 +72,28 @@ WsLayout ws_layout(const Shape& s, bool router) {
   L.hpart = take(BH * L.nchunk * per * sizeof(float));
   const bool bf = s.dtype == SLA_BF16;
   L.pk = bf ? take(BH * (size_t)s.Nk * s.bk * s.d * 2) : 0;
+  L.qbar = take(BH * s.Nq * s.d * sizeof(double));
+  L.kbar = take(BH * s.Nk * s.d * sizeof(double));
+  L.qhat = router ? take(BH * s.Nq * s.d * sizeof(double)) : 0;
+  L.wqk = router ? take((size_t)s.d * s.d * sizeof(double)) : 0;
+  L.S = take(BH * s.Nq * s.Nk * sizeof(double));
+  L.counts = take((size_t)s.R() * sizeof(int32_t));
+  L.bits = take((size_t)s.R() * s.words() * sizeof(uint32_t));
+  L.total = off;
+  return L;
+}
+
+// The mask's regions alone (pooled means, router products, logits, counts,
+// bitmasks), packed from offset 0: the scratch of the allocation-free mask.
+WsLayout mask_layout(const Shape& s, bool router) {
+  WsLayout L{};
+  const size_t BH = (size_t)s.B * s.H;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
   L.qbar = take(BH * s.Nq * s.d * sizeof(double));
   L.kbar = take(BH * s.Nk * s.d * sizeof(double));
   L.qhat = router ? take(BH * s.Nq * s.d * sizeof(double)) : 0;
@@ -136,6 +193,36 @@ int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, cons
   return hip_status(sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx,
                                      block_logits, static_cast<char*>(ws), L,
                                      static_cast<hipStream_t>(stream)));
+}
+
+size_t sla_mask_noalloc_bytes(const sla_problem* prob, const sla_select* sel) {
+  Shape s;
+  if (check_problem(prob, &s) != SLA_OK) return 0;
+  const bool router = sel != nullptr && sel->Wq != nullptr;
+  return sla::mask_layout(s, router).total;
+}
+
+int sla_mask_noalloc(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+                     int32_t* row_ptr, int32_t* col_idx, int64_t capacity, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  int k;
+  if ((rc = check_select(sel, &k, s)) != SLA_OK) return rc;
+  if (Q == nullptr || K == nullptr || row_ptr == nullptr || col_idx == nullptr) return SLA_ERR_INVALID_ARG;
+  if (capacity < (int64_t)s.B * s.H * s.Nq * s.Nk) return SLA_ERR_CAPACITY;
+  const WsLayout L = sla::mask_layout(s, sel->Wq != nullptr);
+  if (L.total > (size_t)SLA_NOALLOC_SCRATCH_BYTES) return SLA_ERR_TOO_LARGE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (st != nullptr) {
+    int cur = -1, sdev = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(st, &sdev) != hipSuccess) return SLA_ERR_HIP;
+    if (sdev != cur) return SLA_ERR_INVALID_ARG;
+  }
+  void* ptr = nullptr;
+  if (scratch_of_current_device(&ptr) != hipSuccess) return SLA_ERR_HIP;
+  return hip_status(sla::launch_mask(s, k, (double)sel->p, sel->Wq, sel->Wk, Q, K, row_ptr, col_idx, nullptr,
+                                     static_cast<char*>(ptr), L, st));
 }
 
 int sla_mask_prepared(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
@@ -370,6 +457,7 @@ const char* sla_status_string(int status) {
     case SLA_ERR_WORKSPACE: return "workspace missing or too small";
     case SLA_ERR_CAPACITY: return "col_idx capacity below B*H*Nq*Nk";
     case SLA_ERR_HIP: return "HIP launch failure";
+    case SLA_ERR_TOO_LARGE: return "problem exceeds the static scratch of the allocation-free mask";
     default: return "unknown status";
   }
 }

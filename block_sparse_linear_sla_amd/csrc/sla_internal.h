@@ -35,6 +35,8 @@ struct WsLayout {
 };
 
 WsLayout ws_layout(const Shape& s, bool router);
+// the mask's regions only (qbar, kbar, qhat, wqk, S, counts, bits), from offset 0
+WsLayout mask_layout(const Shape& s, bool router);
 
 // Byte offsets of the 8-bit sparse branch buffer (all 256-byte aligned).
 struct I8Layout {

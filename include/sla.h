@@ -61,7 +61,8 @@ enum sla_status {
   SLA_ERR_UNSUPPORTED = -2, /* d, bq, bk, dtype or size outside the supported set */
   SLA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than sla_workspace_bytes */
   SLA_ERR_CAPACITY = -4,    /* col_idx capacity below B*H*Nq*Nk */
-  SLA_ERR_HIP = -5          /* a kernel launch failed */
+  SLA_ERR_HIP = -5,         /* a kernel launch failed */
+  SLA_ERR_TOO_LARGE = -6    /* problem exceeds the static scratch of sla_mask_noalloc */
 };
 
 /* Problem shape.  dtype is an sla_dtype value. */
@@ -120,6 +121,27 @@ int sla_soft_topk(const sla_problem* prob, const sla_select* sel, float T, const
 int sla_mask(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
              int32_t* row_ptr, int32_t* col_idx, int64_t capacity, double* block_logits,
              void* ws, size_t ws_bytes, void* stream);
+
+/* sla_mask without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, result and errors as sla_mask (no
+ * block_logits).  Its scratch is a file-scope device array of
+ * SLA_NOALLOC_SCRATCH_BYTES (64 MiB) that every GPU the library runs on holds
+ * from the library's load until the process ends; the call allocates and
+ * frees nothing.  Problems whose mask scratch (the pooled means, the pooled
+ * logits, the per-row counts and bitmasks; sla_mask_noalloc_bytes) exceeds
+ * it return SLA_ERR_TOO_LARGE before anything is launched - the 480p
+ * workloads without the router need about 22 MB.  The array of the CURRENT
+ * device is used: a non-NULL stream must belong to it (else
+ * SLA_ERR_INVALID_ARG).  All calls on one GPU share its array, so calls that
+ * overlap in time on one GPU (different streams, or host threads) race and
+ * must be serialised by the caller; calls on one stream are ordered and safe.
+ * Every word the kernels read from the array is written earlier in the same
+ * call, so nothing depends on what a previous call left there. */
+#define SLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+size_t sla_mask_noalloc_bytes(const sla_problem* prob, const sla_select* sel);
+int sla_mask_noalloc(const sla_problem* prob, const sla_select* sel, const void* Q, const void* K,
+                     int32_t* row_ptr, int32_t* col_idx, int64_t capacity, void* stream);
 
 /* Sparse branch alone (SLA2 write-up §一): O_s[t] = softmax over the keys of the
  * blocks listed in row (b, h, t / bq) of the mask, of q_t . k / sqrt(d), times V.

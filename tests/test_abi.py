@@ -34,7 +34,7 @@ def test_exports_match_header():
 
 def test_status_strings():
     L = S.lib()
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         assert len(L.sla_status_string(code)) > 0
 
 
