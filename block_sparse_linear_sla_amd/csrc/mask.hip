@@ -14,17 +14,17 @@
 // by a few float64 ulps, far inside any cut-off tolerance a float32 pipeline
 // could meet (float32 logits of magnitude ~100 carry ~1e-5 absolute error).
 //
-// Pipeline (six launches, no host synchronisation):
+// Pipeline (four launches, six with the router; no host synchronisation):
 //   pool      one workgroup per (b, h, block) of Q and of K   - HBM bound
 //   router    W_q W_k^T, then the pooled Q rows times it           (optional;
 //             (q W_q).(k W_k) taken as (q W_q W_k^T).k)
 //   score     per (b, h) 32x32-tiled float64 MFMA product q_hat k_bar^T / sqrt(d)
 //             (q_hat = q_bar, or q_bar W_q W_k^T with the router)
-//   select    one wavefront per mask row: softmax, the kept prefix taken in
-//             order while it is short (else a radix descent to the Top-k and
-//             Top-p cut points), n = max(k, kp), bitmask of the kept blocks
-//   scan      one workgroup: exclusive scan of the per-row counts -> row_ptr
-//   emit      one wavefront per row: bitmask -> ascending col_idx
+//   select    one wavefront per mask row: softmax, the Top-k and Top-p cut
+//             points by bisection over the order-preserving keys,
+//             n = max(k, kp), bitmask of the kept blocks
+//   scan+emit one thread per row, 256 rows per workgroup: the counts of all
+//             earlier rows summed, row_ptr, bitmask -> ascending col_idx
 #include <cfloat>
 
 #include "sla_internal.h"
@@ -243,145 +243,31 @@ __device__ __forceinline__ double wave_max(double v) {
 }
 // ---------------------------------------------------------------- selection
 // One wavefront per mask row (four rows per workgroup, no barriers).  Lane l
-// holds the row's blocks j = l + 64 e, e < E.  P_j = exp(S_j - max) / sum in
-// float64; its bit pattern is an order-preserving 64-bit key (P >= 0).
+// holds the row's blocks j = l + 64 e, e < E.  The order is taken on the
+// float64 logits S (P = exp(S - max) / sum is non-decreasing in S; equal
+// logits are ties), with an order-preserving 64-bit key per logit.
 //
 // The order is P descending with ties to the lower block index; Top-k keeps
 // the first k, Top-p the first kp where kp is the smallest count whose
 // cumulative mass reaches p, the union keeps the first max(k, kp) [SA2 §一].
-// While the kept prefix is short (at most 64 blocks) it is taken one key at a
-// time from per-lane sorted lists; otherwise both cut points are found
-// without sorting, by an 8-pass radix descent over the key bytes with
-// per-wavefront LDS histograms: by count for Top-k, by mass for Top-p.  Mass is accumulated in 2^-62 fixed point, so the sums are exact
-// and independent of the order the lanes add them in (the result is
-// bit-for-bit repeatable); it differs from a sequential float64 cumulative
-// sum by at most Nk * 2^-62.  Equal keys at the cut are taken in ascending
-// block order, ranked with ballots.
+// Both cut points are found without sorting, by bisection on the logit
+// value: the Top-k cut is the largest t with count(S >= t) >= k, the Top-p
+// cut the largest t with mass(S >= t) >= p.  A count is a sum of ballot
+// popcounts (scalar), a mass a wavefront sum; each step halves the interval,
+// which stops once a single element is left in it.  When the first k blocks
+// already hold mass p, the union is the Top-k set and the Top-p cut is not
+// searched (nor, when a float32 estimate settles that, the float64
+// probabilities formed).  Mass is accumulated in 2^-62 fixed
+// point, so the sums are exact and independent of the order the lanes add
+// them in (the result is bit-for-bit repeatable); it differs from a
+// sequential float64 cumulative sum by at most Nk * 2^-62.  Equal keys at
+// the cut are taken in ascending block order, ranked with ballots.
 
 constexpr double kMassScale = 4611686018427387904.0;  // 2^62
 
 __device__ __forceinline__ unsigned long long mass_of(unsigned long long key) {
   const double pr = __longlong_as_double((long long)key);
   return (unsigned long long)(pr * kMassScale + 0.5);
-}
-
-template <typename T>
-__device__ __forceinline__ T wave_incl_scan(T v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T u = __shfl_up(v, o);
-    if (lane >= o) v += u;
-  }
-  return v;
-}
-
-// Radix descent for the element at which the running total of `weight` over
-// the descending key order first reaches `target` (which the caller guarantees
-// the total reaches).  Returns its key, the count and total weight of the
-// valid elements with a strictly larger key, and the number of elements with
-// exactly that key.  BYMASS: weight = fixed-point mass, else weight = 1.
-template <int E, bool BYMASS>
-__device__ void radix_cut(const unsigned long long (&key)[E], unsigned long long valid_bits,
-                          unsigned long long target, unsigned* hcnt, unsigned long long* hmass,
-                          int lane, unsigned long long& cut_key, unsigned& above_cnt,
-                          unsigned long long& above_w, unsigned& tie_cnt) {
-  unsigned long long prefix = 0;
-  above_cnt = 0;
-  above_w = 0;
-  tie_cnt = 0;
-#pragma unroll 1
-  for (int pass = 0; pass < 8; ++pass) {
-    const int shift = 56 - 8 * pass;
-    for (int b = lane; b < 256; b += 64) {
-      hcnt[b] = 0u;
-      if (BYMASS) hmass[b] = 0ull;
-    }
-    // LDS operations of one wavefront are performed in issue order, so the
-    // clears above land before these atomics and the reads below.
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const bool in = ((valid_bits >> e) & 1ull) && (pass == 0 || (key[e] >> (shift + 8)) == prefix);
-      if (in) {
-        const int bin = (int)((key[e] >> shift) & 255ull);
-        atomicAdd(&hcnt[bin], 1u);
-        if (BYMASS) atomicAdd(&hmass[bin], mass_of(key[e]));
-      }
-    }
-    // lane l owns bins 255-4l-i (i = 0..3): lane 0 holds the largest keys
-    unsigned c[4];
-    unsigned long long wgt[4];
-    unsigned long long wl = 0, cl = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int bin = 255 - 4 * lane - i;
-      c[i] = hcnt[bin];
-      wgt[i] = BYMASS ? hmass[bin] : (unsigned long long)c[i];
-      wl += wgt[i];
-      cl += c[i];
-    }
-    const unsigned long long w_incl = wave_incl_scan(wl, lane), w_excl = w_incl - wl;
-    const unsigned long long c_incl = wave_incl_scan(cl, lane), c_excl = c_incl - cl;
-    // the single lane whose bins hold the crossing
-    const bool here = above_w + w_excl < target && above_w + w_incl >= target;
-    const int src = __ffsll((long long)__ballot(here)) - 1;
-    // within it, the first bin (largest keys first) where the total reaches target
-    int pick = 3;
-    unsigned long long wb = above_w + w_excl;
-    unsigned cb = (unsigned)c_excl;
-    bool found = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (found) continue;
-      if (wb + wgt[i] >= target) {
-        pick = i;
-        found = true;
-      } else {
-        wb += wgt[i];
-        cb += c[i];
-      }
-    }
-    unsigned tc = c[0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) tc = (i == pick) ? c[i] : tc;
-    prefix = (prefix << 8) | (unsigned long long)__shfl(255 - 4 * lane - pick, src);
-    above_w = __shfl(wb, src);
-    above_cnt += __shfl(cb, src);
-    tie_cnt = __shfl(tc, src);
-    if (tie_cnt == 1u && pass < 7) {
-      // a single element left under this prefix: it is the cut; fetch its key
-      unsigned long long mine = 0;
-      bool has = false;
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool m = ((valid_bits >> e) & 1ull) && (key[e] >> shift) == prefix;
-        mine = m ? key[e] : mine;
-        has = has || m;
-      }
-      const int owner = __ffsll((long long)__ballot(has)) - 1;
-      cut_key = __shfl(mine, owner);
-      return;
-    }
-  }
-  cut_key = prefix;
-}
-
-// Largest 32-bit value over the wavefront, in every lane: quad exchanges and
-// row mirrors (DPP), then the 16- and 32-lane swaps.  Each step takes the
-// larger of the own value and the partner's, so every lane ends with the same
-// maximum (each DPP step folds into one v_max_u32).
-template <int CTRL>
-__device__ __forceinline__ uint32_t max_u32_dpp(uint32_t v) {
-  return max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max_u32_dpp<0xB1>(v);
-  v = max_u32_dpp<0x4E>(v);
-  v = max_u32_dpp<0x141>(v);
-  v = max_u32_dpp<0x140>(v);
-  const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  v = max(a[0], a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return max(b[0], b[1]);
 }
 
 // Wavefront sums and maxima of 64-bit values through the same DPP butterflies
@@ -440,30 +326,6 @@ __device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v)
   return wave_fold_u64(v, [](unsigned long long a, unsigned long long b) { return a + b; });
 }
 
-// This lane's E values in descending order: Batcher's odd-even merge network
-// over the next power of two, with the comparators that reach past E left out
-// (those would meet padding below every value, which stays in place).
-template <int E>
-__device__ __forceinline__ void sort_desc(unsigned long long (&m)[E]) {
-  constexpr int P2 = E <= 1 ? 1 : E <= 2 ? 2 : E <= 4 ? 4 : E <= 8 ? 8 : E <= 16 ? 16 : 32;
-#pragma unroll
-  for (int p = 1; p < P2; p <<= 1)
-#pragma unroll
-    for (int k = p; k >= 1; k >>= 1)
-#pragma unroll
-      for (int j = k % p; j + k < P2; j += 2 * k)
-#pragma unroll
-        for (int i = 0; i < k; ++i) {
-          const int a = i + j, b = i + j + k;
-          if (b < E && b < P2 && a / (2 * p) == b / (2 * p)) {
-            const unsigned long long x = m[a], y = m[b];
-            const bool s = y > x;
-            m[a] = s ? y : x;
-            m[b] = s ? x : y;
-          }
-        }
-}
-
 // Mask bits of one row: every valid block when all, else those whose key is
 // above the cut key, and of the blocks whose key equals it the first
 // ties_needed in block order (ranked with ballots).
@@ -489,146 +351,6 @@ __device__ __forceinline__ void emit_row_bits(const unsigned long long (&key)[E]
   }
 }
 
-template <int E>
-__global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ S, long long R, int Nk,
-                                                     int k, double p, int* __restrict__ counts,
-                                                     uint32_t* __restrict__ bits, int W) {
-  __shared__ unsigned hcnt_all[4][256];
-  __shared__ unsigned long long hmass_all[4][256];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const long long row = (long long)blockIdx.x * 4 + wv;
-  if (row >= R) return;  // whole wavefront; the kernel has no barrier
-  unsigned* hcnt = hcnt_all[wv];
-  unsigned long long* hmass = hmass_all[wv];
-  const double* srow = S + (size_t)row * Nk;
-
-  // Straight-line per-element work (every lane loads, exponentiates and
-  // divides all E of its elements; padding becomes exp(-inf) = 0), so the E
-  // independent chains overlap.
-  double sv[E];
-  unsigned long long valid_bits = 0;
-  double mx = -INFINITY;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int j = lane + 64 * e;
-    const bool ok = j < Nk;
-    const double s = srow[ok ? j : 0];
-    sv[e] = ok ? s : -INFINITY;
-    valid_bits |= (ok ? 1ull : 0ull) << e;
-    mx = fmax(mx, sv[e]);
-  }
-  mx = wave_max_f64(mx);
-  double z = 0.0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    sv[e] = exp(sv[e] - mx);
-    z += sv[e];
-  }
-  z = wave_sum_f64(z);
-  unsigned long long key[E];  // padding: +0.0, key 0
-#pragma unroll
-  for (int e = 0; e < E; ++e) key[e] = (unsigned long long)__double_as_longlong(sv[e] / z);
-
-  const int kk = min(k, Nk);
-  const unsigned long long target = p > 0.0 ? (unsigned long long)ceil(p * kMassScale) : 0ull;
-  unsigned long long tot = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) tot += mass_of(key[e]);  // mass_of(0) = 0
-  tot = wave_sum_u64(tot);
-  const bool p_never = p > 0.0 && tot < target;  // p is never reached: every block
-  uint32_t* brow = bits + (size_t)row * W;
-
-  // Fast path: take the keys one at a time in descending order until both
-  // the count reaches k and the mass reaches p; the taken prefix is then
-  // exactly the first max(k, kp) in the selection order.  Each lane sorts its
-  // own keys once, so a step compares the 64 list heads only.  Equal keys are
-  // interchangeable while counting: the step records the last key taken and
-  // how many of the taken keys equal it, and the blocks kept among equal keys
-  // are then chosen in block order.  Used while that prefix is short and a
-  // row has at most 1024 blocks (E <= 16, for registers); the rest take the
-  // radix descent below.
-  constexpr int kFastMax = 64;
-  if (E <= 16 && !p_never && kk < Nk) {
-    unsigned long long m[E];  // key + 1, 0 for padding and for keys taken
-#pragma unroll
-    for (int e = 0; e < E; ++e) m[e] = ((valid_bits >> e) & 1ull) ? key[e] + 1ull : 0ull;
-    sort_desc<E>(m);
-    unsigned long long mass = 0, last = 0;  // wave-uniform
-    int n = 0, run = 0;
-    bool done = true;
-    while (n < kk || (p > 0.0 && mass < target)) {
-      if (n == kFastMax) {
-        done = false;
-        break;
-      }
-      // the largest high word among the heads, then (when several heads
-      // share it) the largest low word among those
-      const uint32_t h = (uint32_t)(m[0] >> 32), l = (uint32_t)m[0];
-      const uint32_t th = wave_max_u32(h);
-      unsigned long long el = __ballot(h == th);
-      uint32_t tl;
-      if (__popcll(el) > 1) {
-        tl = wave_max_u32(h == th ? l : 0u);
-        el = __ballot(h == th && l == tl);
-      } else {
-        tl = (uint32_t)__builtin_amdgcn_readlane((int)l, __ffsll((long long)el) - 1);
-      }
-      if (lane == __ffsll((long long)el) - 1) {  // one holder of the maximum gives it up
-#pragma unroll
-        for (int e = 0; e + 1 < E; ++e) m[e] = m[e + 1];
-        m[E - 1] = 0ull;
-      }
-      const unsigned long long top = (((unsigned long long)th << 32) | tl) - 1ull;
-      run = (n > 0 && top == last) ? run + 1 : 1;
-      last = top;
-      mass += mass_of(top);
-      ++n;
-    }
-    if (done) {
-      emit_row_bits<E>(key, valid_bits, n >= Nk, n, last, run, lane, brow, W);
-      if (lane == 0) counts[row] = n;
-      return;
-    }
-  }
-
-
-  unsigned long long kkey = 0, kw = 0, pkey = 0, pw = 0;
-  unsigned kabove = 0, ktie = 0, pabove = 0, ptie = 0;
-  // Top-k cut (the kk-th element in the order)
-  if (kk > 0 && kk < Nk)
-    radix_cut<E, false>(key, valid_bits, (unsigned long long)kk, hcnt, hmass, lane, kkey, kabove, kw, ktie);
-  // Top-p cut (the element whose cumulative mass first reaches p)
-  int kp = 0;
-  if (p > 0.0) {
-    if (p_never) {
-      kp = Nk;  // p is never reached: every block
-    } else {
-      radix_cut<E, true>(key, valid_bits, target, hcnt, hmass, lane, pkey, pabove, pw, ptie);
-      const unsigned long long f = mass_of(pkey);  // > 0: this element makes the total reach p
-      const unsigned long long nt = (target - pw + f - 1) / f;
-      kp = (int)pabove + (int)min(nt, (unsigned long long)ptie);
-    }
-  }
-  const int nsel = max(kk, kp);
-  const bool all = nsel >= Nk;
-  const unsigned long long ckey = (nsel == kk) ? kkey : pkey;
-  const int ties_needed = nsel - (int)((nsel == kk) ? kabove : pabove);
-
-  emit_row_bits<E>(key, valid_bits, all, nsel, ckey, ties_needed, lane, brow, W);
-  if (lane == 0) counts[row] = nsel;
-}
-
-// ---------------------------------------------------------------- SoftTop-k
-// One wavefront per mask row: M_j = sigmoid((S_j - tau) / T) with tau such
-// that the weights of the row sum to k [SLA2 write-up §四: a sigmoid with a
-// temperature replaces the hard Top-k in the router's first training stage].
-// tau by a safeguarded Newton iteration on f(tau) = sum_j sigmoid((S_j -
-// tau)/T) - k, decreasing in tau with f'(tau) = -sum_j M_j (1 - M_j) / T,
-// inside a bisection bracket that starts where every weight is ~1 (f > 0)
-// and ~0 (f < 0).  The iteration first runs in float32 (hardware
-// exponential) to a starting point; plain float64 Newton steps from there
-// converge quadratically (the safeguarded float64 iteration takes over if
-// they do not settle), and the weights are written as float32.
 // Float32 wavefront sums through the butterflies of wave_fold_u64 (bit-identical
 // in every lane: the iteration below branches on them); float64 sums use
 // wave_sum_f64.
@@ -647,6 +369,229 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Number of valid keys >= t (wave-uniform: popcounts of ballots).
+template <int E>
+__device__ __forceinline__ int count_ge(const unsigned long long (&key)[E], unsigned long long valid_bits,
+                                        unsigned long long t) {
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) c += __popcll(__ballot(((valid_bits >> e) & 1ull) && key[e] >= t));
+  return c;
+}
+
+// Fixed-point mass of the keys >= t (wave-uniform; padding has mass 0).
+template <int E>
+__device__ __forceinline__ unsigned long long mass_ge(const unsigned long long (&key)[E],
+                                                      const unsigned long long (&mass)[E], unsigned long long t) {
+  unsigned long long m = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) m += key[e] >= t ? mass[e] : 0ull;
+  return wave_sum_u64(m);
+}
+
+// Number of valid logits >= t (wave-uniform); padding holds -inf.
+template <int E>
+__device__ __forceinline__ int count_s_ge(const double (&sv)[E], double t) {
+  int c = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) c += __popcll(__ballot(sv[e] >= t));
+  return c;
+}
+
+// Fixed-point mass of the blocks whose logit is >= t (wave-uniform).
+template <int E>
+__device__ __forceinline__ unsigned long long mass_s_ge(const double (&sv)[E], const unsigned long long (&mass)[E],
+                                                        double t) {
+  unsigned long long m = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) m += sv[e] >= t ? mass[e] : 0ull;
+  return wave_sum_u64(m);
+}
+
+// Smallest valid key >= t (wave-uniform; the caller knows one exists).
+template <int E>
+__device__ __forceinline__ unsigned long long min_key_ge(const unsigned long long (&key)[E],
+                                                         unsigned long long valid_bits, unsigned long long t) {
+  unsigned long long m = ~0ull;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (((valid_bits >> e) & 1ull) && key[e] >= t && key[e] < m) m = key[e];
+  return wave_fold_u64(m, [](unsigned long long a, unsigned long long b) { return a < b ? a : b; });
+}
+
+// Order-preserving 64-bit key of a logit (larger logit, larger key).
+__device__ __forceinline__ unsigned long long skey(double x) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(x);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+__device__ __forceinline__ double skey_value(unsigned long long k) {
+  return __longlong_as_double((long long)((k >> 63) ? (k & 0x7fffffffffffffffull) : ~k));
+}
+
+// The selection of one mask row by one wavefront: srow points at the row's
+// Nk logits (global memory or LDS); writes the row's W bitmask words and
+// its count.
+template <int E>
+__device__ __forceinline__ void select_row(const double* srow, int Nk, int k, double p, int lane,
+                                           uint32_t* __restrict__ brow, int W, int* __restrict__ count) {
+  double sl[E];  // logits (padding -inf)
+  unsigned long long key[E];
+  unsigned long long valid_bits = 0;
+  double mx = -INFINITY, mn = INFINITY;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane + 64 * e;
+    const bool ok = j < Nk;
+    const double s = srow[ok ? j : 0];
+    sl[e] = ok ? s : -INFINITY;
+    key[e] = ok ? skey(s) : 0ull;
+    valid_bits |= (ok ? 1ull : 0ull) << e;
+    mx = fmax(mx, sl[e]);
+    mn = ok ? fmin(mn, s) : mn;
+  }
+  mx = wave_max_f64(mx);
+  mn = -wave_max_f64(-mn);
+  const double above_max = mx + (fabs(mx) + 1.0);  // a finite logit above every block's
+
+  // Bisection on the logit value keeps [lo, hi) around a cut (F(lo) meets
+  // the condition, F(hi) does not) until one element is left in it, or until
+  // the interval cannot shrink (equal logits); returns the key of the
+  // smallest logit >= lo, the element at the cut.
+  auto search = [&](auto meets, double lo, double hi, int clo, int chi) __attribute__((always_inline)) {
+    while (clo - chi > 1) {
+      const double mid = 0.5 * (lo + hi);
+      if (!(mid > lo && mid < hi)) break;
+      const int c = count_s_ge<E>(sl, mid);
+      if (meets(mid, c)) {
+        lo = mid;
+        clo = c;
+      } else {
+        hi = mid;
+        chi = c;
+      }
+    }
+    return min_key_ge<E>(key, valid_bits, skey(lo));
+  };
+
+  // Top-k cut: the kk-th key in the order, and how many valid keys are above it
+  const int kk = min(k, Nk);
+  unsigned long long kkey = 0;
+  int kabove = 0;
+  if (kk > 0 && kk < Nk) {
+    kkey = search([&](double, int c) { return c >= kk; }, mn, above_max, Nk, 0);  // count(S >= mn) = Nk
+    kabove = count_ge<E>(key, valid_bits, kkey + 1);
+  }
+
+  // Top-p: needed only when the first kk blocks do not already hold mass p.
+  // A float32 estimate of their share of the softmax decides that when it is
+  // clear of p by a margin (1e-4 relative, against an estimate error below
+  // 1e-5); otherwise, and whenever Top-p runs, the masses are float64.
+  int kp = 0;
+  unsigned long long pkey = 0;
+  int pabove = 0;
+  if (p > 0.0 && kk < Nk) {
+    bool decided = false, k_enough = false;
+    if (kk > 0) {
+      const double tie_s = skey_value(kkey);
+      float zf = 0.f, mf = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float ef = __builtin_amdgcn_exp2f((float)(sl[e] - mx) * 1.44269504f);  // padding: exp2(-inf) = 0
+        zf += ef;
+        mf += key[e] > kkey ? ef : 0.f;
+      }
+      zf = wave_sum_f32(zf);
+      mf = wave_sum_f32(mf) + (float)(kk - kabove) * __builtin_amdgcn_exp2f((float)(tie_s - mx) * 1.44269504f);
+      const double share = (double)mf / (double)zf;
+      if (share >= p * (1.0 + 1e-4)) decided = k_enough = true;
+      else if (share <= p * (1.0 - 1e-4)) decided = true;
+    }
+    if (!k_enough) {
+      // float64 P = exp(S - max) / sum and its mass in 2^-62 fixed point
+      double z = 0.0, ev[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        ev[e] = exp(sl[e] - mx);
+        z += ev[e];
+      }
+      z = wave_sum_f64(z);
+      unsigned long long mass[E];
+      unsigned long long tot = 0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        mass[e] = mass_of((unsigned long long)__double_as_longlong(ev[e] / z));
+        tot += mass[e];
+      }
+      tot = wave_sum_u64(tot);
+      const unsigned long long target = (unsigned long long)ceil(p * kMassScale);
+      if (tot < target) {
+        kp = Nk;  // p is never reached: every block
+      } else {
+        if (!decided) {
+          const unsigned long long above_k = mass_ge<E>(key, mass, kkey + 1);
+          unsigned long long tie_m = 0;  // mass of one block at the Top-k cut
+#pragma unroll
+          for (int e = 0; e < E; ++e) tie_m = (((valid_bits >> e) & 1ull) && key[e] == kkey) ? mass[e] : tie_m;
+          tie_m = wave_fold_u64(tie_m, [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
+          k_enough = kk > 0 && above_k + (unsigned long long)(kk - kabove) * tie_m >= target;
+        }
+        if (!k_enough) {
+          // the largest logit t with mass(S >= t) >= target; the mass of the
+          // blocks above the Top-k cut (or above the maximum) falls short
+          double hi = above_max;
+          int chi = 0;
+          if (kk > 0 && kabove > 0) {
+            double sk = INFINITY;  // smallest logit above the cut: S >= it exactly for those blocks
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if (((valid_bits >> e) & 1ull) && key[e] > kkey && sl[e] < sk) sk = sl[e];
+            hi = -wave_max_f64(-sk);
+            chi = kabove;
+          }
+          pkey = search([&](double t, int) { return mass_s_ge<E>(sl, mass, t) >= target; }, mn, hi, Nk, chi);
+          pabove = count_ge<E>(key, valid_bits, pkey + 1);
+          const int ptie = count_ge<E>(key, valid_bits, pkey) - pabove;
+          const unsigned long long pw = mass_ge<E>(key, mass, pkey + 1);
+          unsigned long long f = 0;  // mass of one block at the cut (> 0: it makes the total reach p)
+#pragma unroll
+          for (int e = 0; e < E; ++e) f = (((valid_bits >> e) & 1ull) && key[e] == pkey) ? mass[e] : f;
+          f = wave_fold_u64(f, [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
+          const unsigned long long nt = (target - pw + f - 1) / f;
+          kp = pabove + (int)min(nt, (unsigned long long)ptie);
+        }
+      }
+    }
+  }
+  const int nsel = max(kk, kp);
+  const bool all = nsel >= Nk;
+  const unsigned long long ckey = (nsel == kk) ? kkey : pkey;
+  const int ties_needed = nsel - ((nsel == kk) ? kabove : pabove);
+
+  emit_row_bits<E>(key, valid_bits, all, nsel, ckey, ties_needed, lane, brow, W);
+  if (lane == 0) *count = nsel;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void select_kernel(const double* __restrict__ S, long long R, int Nk,
+                                                     int k, double p, int* __restrict__ counts,
+                                                     uint32_t* __restrict__ bits, int W) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + wv;
+  if (row >= R) return;  // whole wavefront; the kernel has no barrier
+  select_row<E>(S + (size_t)row * Nk, Nk, k, p, lane, bits + (size_t)row * W, W, counts + row);
+}
+
+// ---------------------------------------------------------------- SoftTop-k
+// One wavefront per mask row: M_j = sigmoid((S_j - tau) / T) with tau such
+// that the weights of the row sum to k [SLA2 write-up §四: a sigmoid with a
+// temperature replaces the hard Top-k in the router's first training stage].
+// tau by a safeguarded Newton iteration on f(tau) = sum_j sigmoid((S_j -
+// tau)/T) - k, decreasing in tau with f'(tau) = -sum_j M_j (1 - M_j) / T,
+// inside a bisection bracket that starts where every weight is ~1 (f > 0)
+// and ~0 (f < 0).  The iteration first runs in float32 (hardware
+// exponential) to a starting point; plain float64 Newton steps from there
+// converge quadratically (the safeguarded float64 iteration takes over if
+// they do not settle), and the weights are written as float32.
 __device__ __forceinline__ double sigmoid_f64(double x) {
   const double e = exp(-fabs(x));
   return x >= 0.0 ? 1.0 / (1.0 + e) : e / (1.0 + e);
@@ -773,91 +718,74 @@ __global__ __launch_bounds__(256) void soft_topk_kernel(const double* __restrict
   }
 }
 
-// Exclusive scan of counts[R] into row_ptr[R + 1] with one workgroup of 1024
-// threads, 4096 counts per pass: each thread loads 4 consecutive counts, the
-// thread totals are scanned within each wavefront (shuffles) and across the 16
-// wavefronts (LDS), and a running carry joins the passes.
-__global__ __launch_bounds__(1024) void scan_kernel(const int* __restrict__ counts, long long R,
-                                                    int* __restrict__ row_ptr) {
-  __shared__ int wtot[16];
-  __shared__ int ttot;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int carry = 0;  // sum of the counts of the earlier passes (the same in every thread)
-  for (long long t0 = 0; t0 < R; t0 += 4096) {
-    const long long i0 = t0 + 4 * (long long)tid;
-    int v[4];
-    if (i0 + 3 < R) {
-      const int4 q = *reinterpret_cast<const int4*>(counts + i0);
-      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    } else {
+// CSR from the per-row counts and bitmasks, in one launch.  Workgroup g
+// (256 threads) owns rows [256 g, 256 g + 256), one thread per row: the
+// counts of every earlier row are summed by the whole workgroup (int4 loads,
+// wavefront reductions, the four wavefronts in a fixed order), its own 256
+// counts scanned (wavefront scans, then the wavefront totals), the rows'
+// row_ptr entries written (the last row's thread also row_ptr[R]), and each
+// thread turns its row's bitmask words into ascending block indices.
+constexpr int kEmitRows = kThreads;
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = i0 + e < R ? counts[i0 + e] : 0;
-    }
-    const int tsum = v[0] + v[1] + v[2] + v[3];
-    int incl = tsum;  // inclusive scan of the thread totals within the wavefront
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int up = __shfl_up(incl, off);
-      if (lane >= off) incl += up;
-    }
-    if (lane == 63) wtot[wv] = incl;
-    __syncthreads();
-    int before = 0;  // totals of the earlier wavefronts of this pass
-    for (int u = 0; u < wv; ++u) before += wtot[u];
-    if (tid == 1023) ttot = before + incl;
-    int run = carry + before + incl - tsum;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i0 + e < R) row_ptr[i0 + e] = run;
-      run += v[e];
-    }
-    __syncthreads();  // ttot written; wtot free for the next pass
-    carry += ttot;
-    __syncthreads();  // every thread has read ttot
-  }
-  if (tid == 0) row_ptr[R] = carry;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
-// One wavefront per row: bitmask words -> ascending block indices.
-__global__ __launch_bounds__(kThreads) void emit_kernel(const uint32_t* __restrict__ bits,
-                                                        const int* __restrict__ row_ptr,
-                                                        int* __restrict__ col_idx, long long R, int W) {
-  const long long row = (long long)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (row >= R) return;
-  const int lane = threadIdx.x & 63;
-  const int WPL = (W + 63) / 64;  // words per lane (<= 2 for Nk <= 4096)
-  uint32_t w[2] = {0u, 0u};
-  int cnt = 0;
-  for (int u = 0; u < WPL; ++u) {
-    const int wi = lane * WPL + u;
-    w[u] = (wi < W) ? bits[(size_t)row * W + wi] : 0u;
-    cnt += __popc(w[u]);
+__global__ __launch_bounds__(kThreads) void scan_emit_kernel(const int* __restrict__ counts,
+                                                             const uint32_t* __restrict__ bits,
+                                                             int* __restrict__ row_ptr, int* __restrict__ col_idx,
+                                                             long long R, int W) {
+  __shared__ int wsum[kThreads / 64];
+  __shared__ int wtot[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const long long r0 = (long long)blockIdx.x * kEmitRows;
+  const long long row = r0 + tid;
+  const int c = row < R ? counts[row] : 0;
+  // counts of rows [0, r0) (r0 a multiple of 4)
+  int acc = 0;
+  for (long long i = 4 * (long long)tid; i < r0; i += 4 * kThreads) {
+    const int4 q = *reinterpret_cast<const int4*>(counts + i);
+    acc += (q.x + q.y) + (q.z + q.w);
   }
-  int incl = cnt;
+  acc = wave_sum_i32(acc);
+  int incl = c;  // inclusive scan of this wavefront's counts
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
+    const int u = __shfl_up(incl, o);
+    if (lane >= o) incl += u;
   }
-  int pos = row_ptr[row] + incl - cnt;
-  for (int u = 0; u < WPL; ++u) {
-    uint32_t x = w[u];
-    const int base = (lane * WPL + u) * 32;
-    while (x) {
-      const int bpos = __ffs(x) - 1;
-      col_idx[pos++] = base + bpos;
-      x &= x - 1u;
+  if (lane == 0) wsum[wv] = acc;
+  if (lane == 63) wtot[wv] = incl;
+  __syncthreads();
+  int start = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+  for (int u = 0; u < wv; ++u) start += wtot[u];
+  start += incl - c;
+  if (row < R) {
+    row_ptr[row] = start;
+    if (row == R - 1) row_ptr[R] = start + c;
+    const uint32_t* brow = bits + (size_t)row * W;
+    int pos = start;
+    // eight words loaded together, then expanded (the loads do not wait for
+    // one another behind the stores)
+    for (int w0 = 0; w0 < W; w0 += 8) {
+      uint32_t x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = w0 + u < W ? brow[w0 + u] : 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        while (x[u]) {
+          col_idx[pos++] = 32 * (w0 + u) + (__ffs(x[u]) - 1);
+          x[u] &= x[u] - 1u;
+        }
+      }
     }
   }
 }
 
-template <int E>
-hipError_t launch_select(const double* S, long long R, int Nk, int k, double p, int* counts,
-                         uint32_t* bits, int W, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<E>), dim3((unsigned)((R + 3) / 4)), dim3(kThreads), 0, st, S, R, Nk,
-                     k, p, counts, bits, W);
-  return hipGetLastError();
-}
+
+
 
 }  // namespace
 
@@ -965,26 +893,18 @@ hipError_t launch_mask(const Shape& s, int k, double p, const float* Wq, const f
       E = c;
       break;
     }
+  const dim3 gsel((unsigned)((R + 3) / 4));
+#define SLA_SELECT(EE) \
+  case EE: hipLaunchKernelGGL((select_kernel<EE>), gsel, dim3(kThreads), 0, st, S, R, s.Nk, k, p, counts, bits, W); break
   switch (E) {
-    case 1: e = launch_select<1>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 2: e = launch_select<2>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 4: e = launch_select<4>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 8: e = launch_select<8>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 12: e = launch_select<12>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 16: e = launch_select<16>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 20: e = launch_select<20>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 24: e = launch_select<24>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 32: e = launch_select<32>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 40: e = launch_select<40>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    case 48: e = launch_select<48>(S, R, s.Nk, k, p, counts, bits, W, st); break;
-    default: e = launch_select<64>(S, R, s.Nk, k, p, counts, bits, W, st); break;
+    SLA_SELECT(1); SLA_SELECT(2); SLA_SELECT(4); SLA_SELECT(8); SLA_SELECT(12); SLA_SELECT(16);
+    SLA_SELECT(20); SLA_SELECT(24); SLA_SELECT(32); SLA_SELECT(40); SLA_SELECT(48);
+    default: hipLaunchKernelGGL((select_kernel<64>), gsel, dim3(kThreads), 0, st, S, R, s.Nk, k, p, counts, bits, W);
   }
-  if (e != hipSuccess) return e;
-
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, counts, R, row_ptr);
+#undef SLA_SELECT
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(emit_kernel, dim3((unsigned)((R + 3) / 4)), dim3(kThreads), 0, st, bits,
-                     row_ptr, col_idx, R, W);
+  hipLaunchKernelGGL(scan_emit_kernel, dim3((unsigned)((R + kEmitRows - 1) / kEmitRows)), dim3(kThreads), 0, st,
+                     counts, bits, row_ptr, col_idx, R, W);
   return hipGetLastError();
 }
 

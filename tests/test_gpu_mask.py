@@ -25,8 +25,8 @@ SMALL = [
     ("bf16-topk-only", "bf16", 1500, 128, 128, 64, 0.25, 0.0, False),
     ("bf16-full", "bf16", 700, 128, 128, 64, 1.0, 0.5, False),
     ("bf16-p1", "bf16", 1500, 128, 128, 64, 0.0, 1.0, False),
-    # more than 64 kept blocks per row: the one-at-a-time selection hands over
-    # to the radix descent
+    # a long kept prefix (about 77 of 128 blocks per row): both cuts deep in
+    # the row
     ("bf16-long-prefix", "bf16", 8192, 128, 128, 64, 0.6, 0.5, False),
     # Top-p decides the count (k = 1)
     ("bf16-p-dominant", "bf16", 3000, 128, 128, 64, 0.02, 0.95, False),
@@ -133,8 +133,9 @@ def test_mask_exact_ties(case):
     so the CSR must equal the oracle's with nothing excused.  Head 0 has Q = 0:
     every logit is 0 and P = 1/Nk exactly (Nk a power of two, so every partial
     sum is exact), so every row keeps blocks 0 .. max(ceil(k_frac Nk),
-    ceil(p Nk)) - 1 (256 blocks at Nk = 512 and p = 0.5, past the
-    one-at-a-time selection).  Head 1 repeats key blocks 0..3 over the row
+    ceil(p Nk)) - 1 (256 blocks at Nk = 512 and p = 0.5: the Top-p cut
+    falls inside one tie of all Nk blocks, which no bisection on the logit
+    can split).  Head 1 repeats key blocks 0..3 over the row
     (four groups of equal P, the cut inside the top group); head 2 is the
     random control."""
     name, dtype, N, d, bq, bk, k_frac, p = case
