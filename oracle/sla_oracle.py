@@ -524,6 +524,134 @@ def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, wi
     return (out, sums) if with_sums else out
 
 
+# ----------------------------------- 8-bit floating-point sparse branch
+# A second reading of [SLA2 §三]'s 8-bit sparse branch: the 8-bit values are
+# floating-point numbers in the E4M3 format of the OCP 8-bit floating-point
+# specification (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
+# infinities, largest finite value 448, subnormals m * 2^-9 at exponent field
+# 0), and a row's keys are taken in ONE pass:
+# * codes: Q per query block, K per key block, V per channel over the whole
+#   sequence of a head: code = E4M3(fl32(x * fl32(448 / amax))), scale =
+#   fl32(amax / 448), E4M3() rounding to the nearest value, ties to the even
+#   mantissa (zero codes and scale when amax is 0);
+# * scores S = (q8 . k8) * c with c = fl32(fl32(sq * sk) * fl32(1 / sqrt(d))),
+#   the dot product taken exactly (float64 holds every partial sum);
+# * the row's selected keys in 64-key units, in the mask's order; m = the
+#   largest S seen so far, the current unit's included; the unit's P codes are
+#   E4M3(256 exp(S - m)), at most 256; whenever m rises, what the earlier units
+#   accumulated is multiplied by exp(m_old - m_new);
+# * O = sv * (sum_u w_u sum_j code_j v8_j) / (sum_u w_u sum_j code_j), w_u =
+#   exp(m_u - m_last); a row with no selected block gives 0.
+_E4M3_MAX = 448.0
+_F8_UNIT = 64      # keys per unit of the single pass
+_F8_PSCALE = 256.0  # P codes are 256 exp(S - m)
+
+
+def e4m3(x) -> np.ndarray:
+    """x (float64) rounded to the nearest E4M3 value, ties to the even
+    mantissa.  |x| must not exceed 449 (the callers' values stay at or below
+    448 up to float32 rounding); results above 448 become 448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    assert np.all(a <= 449.0), "value outside the E4M3 range"
+    _, e = np.frexp(a)                       # a = f 2^e, f in [0.5, 1): binade 2^(e-1)
+    e = np.maximum(e - 1, -6)                # exponent of the binade, subnormals at -6
+    step = np.ldexp(1.0, (e - 3).astype(np.int64))  # spacing of 3 mantissa bits there
+    r = np.rint(a / step) * step             # a / step is exact; rint: half to even
+    return np.copysign(np.minimum(r, _E4M3_MAX), x)
+
+
+def e4m3_decode(bits) -> np.ndarray:
+    """Values of E4M3 bit patterns (uint8); the two NaN patterns give NaN."""
+    b = np.asarray(bits, dtype=np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    E, M = (b >> 3) & 0xF, b & 0x7
+    mag = np.where(E == 0, M * 2.0 ** -9, (1.0 + M / 8.0) * np.exp2(E - 7.0))
+    mag = np.where((E == 0xF) & (M == 0x7), np.nan, mag)
+    return sign * mag
+
+
+def _f8_codes(x32: np.ndarray, amax: np.float32) -> Tuple[np.ndarray, np.float32]:
+    amax = _F32(amax)
+    if amax == 0:
+        return np.zeros(x32.shape), _F32(0.0)
+    r = _F32(_F32(_E4M3_MAX) / amax)
+    return e4m3((x32 * r).astype(np.float32).astype(np.float64)), _F32(amax / _F32(_E4M3_MAX))
+
+
+def quantize_fp8(Q, K, V, bq: int, bk: int) -> Dict:
+    """E4M3 codes (as float64 values) and float32 scales of the 8-bit
+    floating-point sparse branch: Q per query block, K per key block (scales
+    [B, H, ceil(N / b)]), V per channel (scales [B, H, d])."""
+    out = {}
+    for name, X, b in (("q", Q, bq), ("k", K, bk)):
+        X = _as_f32_exact(X)
+        B, H, N, d = X.shape
+        nb = n_blocks(N, b)
+        codes, scales = np.zeros((B, H, N, d)), np.zeros((B, H, nb), dtype=np.float32)
+        for bb in range(B):
+            for h in range(H):
+                for i in range(nb):
+                    s, e = block_range(i, b, N)
+                    blk = X[bb, h, s:e]
+                    codes[bb, h, s:e], scales[bb, h, i] = _f8_codes(blk, np.abs(blk).max())
+        out[name + "8"], out["s" + name] = codes, scales
+    Vf = _as_f32_exact(V)
+    B, H, N, d = Vf.shape
+    codes, scales = np.zeros((B, H, N, d)), np.zeros((B, H, d), dtype=np.float32)
+    for bb in range(B):
+        for h in range(H):
+            for c in range(d):
+                col = Vf[bb, h, :, c]
+                codes[bb, h, :, c], scales[bb, h, c] = _f8_codes(col, np.abs(col).max())
+    out["v8"], out["sv"] = codes, scales
+    return out
+
+
+def sparse_branch_fp8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, with_sums: bool = False):
+    """The single-pass 8-bit floating-point sparse branch on quantize_fp8's
+    codes (see the section comment).  Returns {(b, h, i): [rows_in_block, d]}
+    and with with_sums also {(b, h, i): (L, m)}: per query the weighted sum of
+    P codes relative to the final maximum and that maximum."""
+    q8, k8, v8 = qz["q8"], qz["k8"], qz["v8"]
+    sq, sk, sv = qz["sq"], qz["sk"], qz["sv"]
+    B, H, N, d = q8.shape
+    Nq = n_blocks(N, bq)
+    lam = _F32(1.0 / math.sqrt(d))
+    out, sums = {}, {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = [int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]]]
+        s, e = block_range(i, bq, N)
+        n = e - s
+        if not sel:
+            out[(b, h, i)] = np.zeros((n, d))
+            sums[(b, h, i)] = (np.zeros(n), np.full(n, -np.inf))
+            continue
+        # the row's keys block by block, each block cut into 64-key units
+        units = []
+        for j in sel:
+            ks, ke = block_range(j, bk, N)
+            c = np.float64(_F32(_F32(sq[b, h, i] * sk[b, h, j]) * lam))
+            for u0 in range(ks, ke, _F8_UNIT):
+                units.append((np.arange(u0, min(u0 + _F8_UNIT, ke)), c))
+        num, L = np.zeros((n, d)), np.zeros(n)
+        m = np.full(n, -np.inf)
+        for keys, c in units:
+            Sx = (q8[b, h, s:e] @ k8[b, h, keys].T) * c          # [n, keys]
+            mu = np.maximum(m, Sx.max(axis=1))
+            w = np.where(np.isfinite(m), np.exp(m - mu), 0.0)    # rescale of earlier units
+            num *= w[:, None]
+            L *= w
+            m = mu
+            p8 = e4m3(_F8_PSCALE * np.exp(Sx - m[:, None]))
+            num += p8 @ v8[b, h, keys]
+            L += p8.sum(axis=1)
+        out[(b, h, i)] = sv[b, h].astype(np.float64)[None, :] * num / L[:, None]
+        sums[(b, h, i)] = (L, m)
+    return (out, sums) if with_sums else out
+
+
 # -------------------------------------------------------- sparse backward
 # The gradient of the sparse branch with the mask held fixed (the block
 # selection is a discrete choice; the pages train through it with the
