@@ -534,17 +534,21 @@ def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, wi
 #   sequence of a head: code = E4M3(fl32(x * fl32(448 / amax))), scale =
 #   fl32(amax / 448), E4M3() rounding to the nearest value, ties to the even
 #   mantissa (zero codes and scale when amax is 0);
-# * scores S = (q8 . k8) * c with c = fl32(fl32(sq * sk) * fl32(1 / sqrt(d))),
-#   the dot product taken exactly (float64 holds every partial sum);
+# * raw scores R = fl32(q8 . k8) (the dot product exact, one rounding), c =
+#   fl32(fl32(sq * sk) * fl32(1 / sqrt(d))) per key block, S = R c;
 # * the row's selected keys in 64-key units, in the mask's order; m = the
-#   largest S seen so far, the current unit's included; the unit's P codes are
-#   E4M3(256 exp(S - m)), at most 256; whenever m rises, what the earlier units
-#   accumulated is multiplied by exp(m_old - m_new);
+#   largest fl32(max_unit(R) c) so far, the current unit's included; the
+#   unit's P codes are E4M3(256 exp(S - m)) (at most 256); whenever m rises,
+#   what the earlier units accumulated is multiplied by exp(m_old - m_new);
 # * O = sv * (sum_u w_u sum_j code_j v8_j) / (sum_u w_u sum_j code_j), w_u =
 #   exp(m_u - m_last); a row with no selected block gives 0.
+# A P code is a quantised value decided by floating point, so it is decided in
+# the precision the kernel computes it in (as for the integer branch's codes):
+# 256 exp(S - m) is taken as fl32(2^t), t = fl32(R a - b), a = fl32(c log2 e),
+# b = fl32(fl32(m log2 e) - 8) (f8_p_codes); tests pin that against the exact
+# value.
 _E4M3_MAX = 448.0
 _F8_UNIT = 64      # keys per unit of the single pass
-_F8_PSCALE = 256.0  # P codes are 256 exp(S - m)
 
 
 def e4m3(x) -> np.ndarray:
@@ -608,11 +612,22 @@ def quantize_fp8(Q, K, V, bq: int, bk: int) -> Dict:
     return out
 
 
+def f8_p_codes(R: np.ndarray, a, b) -> np.ndarray:
+    """E4M3 P codes of float32 raw scores R with a = fl32(c log2 e) and
+    b = fl32(fl32(m log2 e) - 8) (broadcast against R): E4M3(fl32(2^t)),
+    t = fl32(R a - b) with the product and difference exact in float64 before
+    the one rounding, 2^t taken in float64 and rounded to float32."""
+    t = (R.astype(np.float64) * np.asarray(a, np.float64) - np.asarray(b, np.float64)).astype(np.float32)
+    p = np.exp2(t.astype(np.float64)).astype(np.float32)
+    return e4m3(p.astype(np.float64))
+
+
 def sparse_branch_fp8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, with_sums: bool = False):
     """The single-pass 8-bit floating-point sparse branch on quantize_fp8's
     codes (see the section comment).  Returns {(b, h, i): [rows_in_block, d]}
-    and with with_sums also {(b, h, i): (L, m)}: per query the weighted sum of
-    P codes relative to the final maximum and that maximum."""
+    and with with_sums also {(b, h, i): (L, m, A)}: per query the weighted sum
+    of P codes relative to the final maximum, that maximum (float32), and per
+    output the same weighted mean of |v| (the scale of the float32 sums)."""
     q8, k8, v8 = qz["q8"], qz["k8"], qz["v8"]
     sq, sk, sv = qz["sq"], qz["sk"], qz["sv"]
     B, H, N, d = q8.shape
@@ -626,29 +641,34 @@ def sparse_branch_fp8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, w
         n = e - s
         if not sel:
             out[(b, h, i)] = np.zeros((n, d))
-            sums[(b, h, i)] = (np.zeros(n), np.full(n, -np.inf))
+            sums[(b, h, i)] = (np.zeros(n), np.full(n, -np.inf, dtype=np.float32), np.zeros((n, d)))
             continue
         # the row's keys block by block, each block cut into 64-key units
         units = []
         for j in sel:
             ks, ke = block_range(j, bk, N)
-            c = np.float64(_F32(_F32(sq[b, h, i] * sk[b, h, j]) * lam))
+            c = _F32(_F32(sq[b, h, i] * sk[b, h, j]) * lam)
             for u0 in range(ks, ke, _F8_UNIT):
                 units.append((np.arange(u0, min(u0 + _F8_UNIT, ke)), c))
-        num, L = np.zeros((n, d)), np.zeros(n)
-        m = np.full(n, -np.inf)
+        num, anum, L = np.zeros((n, d)), np.zeros((n, d)), np.zeros(n)
+        m = np.full(n, -np.inf, dtype=np.float32)
         for keys, c in units:
-            Sx = (q8[b, h, s:e] @ k8[b, h, keys].T) * c          # [n, keys]
-            mu = np.maximum(m, Sx.max(axis=1))
-            w = np.where(np.isfinite(m), np.exp(m - mu), 0.0)    # rescale of earlier units
+            R = (q8[b, h, s:e] @ k8[b, h, keys].T).astype(np.float32)     # [n, keys]
+            mu = np.maximum(m, (R.max(axis=1) * c).astype(np.float32))
+            w = np.where(np.isfinite(m), np.exp(m.astype(np.float64) - mu.astype(np.float64)), 0.0)
             num *= w[:, None]
+            anum *= w[:, None]
             L *= w
             m = mu
-            p8 = e4m3(_F8_PSCALE * np.exp(Sx - m[:, None]))
+            a = _F32(c * _LOG2E_F32)
+            bb = ((m * _LOG2E_F32).astype(np.float32) - _F32(8.0)).astype(np.float32)
+            p8 = f8_p_codes(R, a, bb[:, None])
             num += p8 @ v8[b, h, keys]
+            anum += p8 @ np.abs(v8[b, h, keys])
             L += p8.sum(axis=1)
-        out[(b, h, i)] = sv[b, h].astype(np.float64)[None, :] * num / L[:, None]
-        sums[(b, h, i)] = (L, m)
+        svd = sv[b, h].astype(np.float64)[None, :]
+        out[(b, h, i)] = svd * num / L[:, None]
+        sums[(b, h, i)] = (L, m, svd * anum / L[:, None])
     return (out, sums) if with_sums else out
 
 

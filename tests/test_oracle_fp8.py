@@ -105,7 +105,7 @@ def test_equal_scores_give_the_plain_mean():
     out, sums = O.sparse_branch_fp8(qz, 128, 64, rp, ci, with_sums=True)
     want = qz["sv"][0, 0].astype(np.float64) * qz["v8"][0, 0].mean(axis=0)
     np.testing.assert_allclose(out[(0, 0, 0)], np.broadcast_to(want, (128, 32)), rtol=1e-14, atol=0)
-    L, m = sums[(0, 0, 0)]
+    L, m, _ = sums[(0, 0, 0)]
     assert np.all(L == 256.0 * 256) and np.all(m == 0.0)
 
 
@@ -156,14 +156,14 @@ def test_close_to_exact_attention_with_a_rising_maximum(rising):
     rises = 0
     for (b, h, i) in rows:
         exact, Sx = _exact_on_dequantised(qz, b, h, i, bq, bk, range(Nk))
-        L, m = sums[(b, h, i)]
+        L, m, _ = sums[(b, h, i)]
         vmax = np.abs(qz["v8"][b, h] * qz["sv"][b, h].astype(np.float64)[None, :]).max(axis=0)
         n = Sx.shape[1]
         bound = vmax[None, :] * 2 * (2.0 ** -4 + 2.0 ** -10 * n / L[:, None]) * (1 + 1e-9)
         err = np.abs(out[(b, h, i)] - exact)
         assert np.all(err <= bound), (h, i, float((err / bound).max()))
         worst = max(worst, float((err / bound).max()))
-        assert np.all(np.isfinite(m)) and np.allclose(m, Sx.max(axis=1), rtol=1e-6, atol=1e-9)
+        assert np.all(np.isfinite(m)) and np.allclose(m, Sx.max(axis=1), rtol=1e-5, atol=1e-6)
         unit_max = Sx.reshape(Sx.shape[0], Nk, bk).max(axis=2)
         rises += int((np.diff(np.maximum.accumulate(unit_max, axis=1), axis=1) > 1.0).sum())
     if rising:
@@ -173,8 +173,9 @@ def test_close_to_exact_attention_with_a_rising_maximum(rising):
 
 def test_first_unit_holding_the_maximum_needs_no_rescale():
     """When the first unit of every row already holds the row maximum, no
-    rescale happens and the result is the sum over all keys of codes taken
-    against the global maximum (computed here in one product)."""
+    rescale happens and the result is the sum over all keys of the codes
+    taken against that maximum (f8_p_codes over the whole row in one
+    product), exactly."""
     rng = np.random.default_rng(4)
     B, H, N, d, bq, bk = 1, 1, 256, 32, 64, 64
     u = np.full(d, 3.0 / math.sqrt(d))                   # every query leans along u
@@ -186,16 +187,82 @@ def test_first_unit_holding_the_maximum_needs_no_rescale():
     rp, ci = _csr_all(B, H, N // bq, N // bk)
     out, sums = O.sparse_branch_fp8(qz, bq, bk, rp, ci, with_sums=True)
     lam = np.float32(1.0 / math.sqrt(d))
+    l2e = np.float32(math.log2(math.e))
     for i in range(N // bq):
         s, e = O.block_range(i, bq, N)
-        c = np.concatenate([np.full(bk, np.float64(np.float32(np.float32(qz["sq"][0, 0, i] * qz["sk"][0, 0, j]) * lam)))
-                            for j in range(N // bk)])
-        Sx = (qz["q8"][0, 0, s:e] @ qz["k8"][0, 0].T) * c[None, :]
-        assert np.all(Sx[:, :bk].max(axis=1) >= Sx.max(axis=1))
-        p8 = O.e4m3(256.0 * np.exp(Sx - Sx.max(axis=1, keepdims=True)))
+        c = [np.float32(np.float32(qz["sq"][0, 0, i] * qz["sk"][0, 0, j]) * lam) for j in range(N // bk)]
+        R = (qz["q8"][0, 0, s:e] @ qz["k8"][0, 0].T).astype(np.float32)
+        Sb = [(R[:, j * bk:(j + 1) * bk].max(axis=1) * c[j]).astype(np.float32) for j in range(N // bk)]
+        assert np.all(Sb[0] >= np.max(Sb, axis=0))
+        m = Sb[0]
+        b = ((m * l2e).astype(np.float32) - np.float32(8)).astype(np.float32)
+        a = np.concatenate([np.full(bk, np.float32(cj * l2e), np.float32) for cj in c])
+        p8 = O.f8_p_codes(R, a[None, :], b[:, None])
         want = qz["sv"][0, 0].astype(np.float64)[None, :] * (p8 @ qz["v8"][0, 0]) / p8.sum(axis=1)[:, None]
         np.testing.assert_allclose(out[(0, 0, i)], want, rtol=1e-12, atol=1e-15)
         np.testing.assert_allclose(sums[(0, 0, i)][0], p8.sum(axis=1), rtol=1e-13)
+
+
+_U = 2.0 ** -24  # float32 unit roundoff
+
+
+def _midpoint_distance(x):
+    """Distance of x >= 0 to the nearest midpoint between E4M3 neighbours."""
+    _, e = np.frexp(x)
+    step = np.ldexp(1.0, (np.maximum(e - 1, -6) - 3).astype(np.int64))
+    return np.abs(x - (np.floor(x / step) + 0.5) * step), step
+
+
+def test_float32_codes_match_the_definition_on_the_480p_sample():
+    """On the 480p SLA2 workload (two heads, the oracle's own mask), every P
+    code f8_p_codes forms for 16 sampled row blocks equals E4M3(256 exp(S -
+    m)) evaluated in float64 (S = R c exactly, m the same running maximum),
+    except where that value lies within the float32 error bound of an E4M3
+    midpoint; those few differ by one E4M3 step.  Bound on the relative error
+    of the float32 value: each rounding adds at most u |value| (u = 2^-24) to
+    t in log2 units: R (u log2(e) |S|), a and fl32(log2 e) (2 u log2(e) |S|),
+    fl32(m log2 e) (2 u log2(e) |m|), b (u |b|), t (u |t|); then 2^E - 1 <=
+    E ln 2 (1 + E), plus u for rounding 2^t; doubled for slack."""
+    import gen
+    wl = gen.WORKLOADS["video480p-sla2-N32760"]
+    x = gen.make(wl, heads=2)
+    rp, ci, _ = O.mask(x.Q, x.K, wl.bq, wl.bk, wl.k_frac, wl.p, keep_info=False)
+    qz = O.quantize_fp8(x.Q, x.K, x.V, wl.bq, wl.bk)
+    lam = np.float32(1.0 / math.sqrt(wl.d))
+    l2e = np.float32(math.log2(math.e))
+    L2 = math.log2(math.e)
+    rng = np.random.default_rng(0)
+    rows = [(h, int(i)) for h in range(2) for i in rng.choice(wl.Nq, 8, replace=False)]
+    rows[-1] = (1, wl.Nq - 1)
+    total = excused = 0
+    for h, i in rows:
+        r = h * wl.Nq + i
+        s, e = O.block_range(i, wl.bq, wl.N)
+        m = np.full(e - s, -np.inf, dtype=np.float32)
+        for j in ci[rp[r]:rp[r + 1]]:
+            ks, ke = O.block_range(int(j), wl.bk, wl.N)   # bk = 64: one unit per block
+            c = np.float32(np.float32(qz["sq"][0, h, i] * qz["sk"][0, h, j]) * lam)
+            Rx = qz["q8"][0, h, s:e] @ qz["k8"][0, h, ks:ke].T          # exact
+            R = Rx.astype(np.float32)
+            m = np.maximum(m, (R.max(axis=1) * c).astype(np.float32))
+            b = ((m * l2e).astype(np.float32) - np.float32(8)).astype(np.float32)
+            got = O.f8_p_codes(R, np.float32(c * l2e), b[:, None])
+            S = Rx * np.float64(c)
+            xv = 256.0 * np.exp(S - m.astype(np.float64)[:, None])
+            want = O.e4m3(xv)
+            t = np.log2(np.maximum(xv, 1e-300))
+            E = _U * (3 * L2 * np.abs(S) + 2 * L2 * np.abs(m.astype(np.float64))[:, None]
+                      + np.abs(b.astype(np.float64))[:, None] + np.abs(t))
+            bound = 2.0 * xv * (E * math.log(2.0) * (1 + E) + _U)
+            dist, step = _midpoint_distance(xv)
+            diff = got != want
+            assert np.all(dist[diff] <= bound[diff]), (h, i)
+            assert np.all(np.abs(got - want) <= step * (1 + 1e-12) + 1e-300)
+            total += got.size
+            excused += int(diff.sum())
+    assert total > 100000
+    print(f"codes {total}, differing from the float64 value {excused}")
+    assert excused <= 1e-3 * total, (excused, total)
 
 
 def test_empty_row_and_partial_units():
