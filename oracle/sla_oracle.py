@@ -524,27 +524,31 @@ def sparse_branch_i8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, wi
     return (out, sums) if with_sums else out
 
 
-# ----------------------------------- 8-bit floating-point sparse branch
-# A second reading of [SLA2 §三]'s 8-bit sparse branch: the 8-bit values are
-# floating-point numbers in the E4M3 format of the OCP 8-bit floating-point
-# specification (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, no
-# infinities, largest finite value 448, subnormals m * 2^-9 at exponent field
-# 0), and a row's keys are taken in ONE pass:
-# * codes: Q per query block, K per key block, V per channel over the whole
-#   sequence of a head: code = E4M3(fl32(x * fl32(448 / amax))), scale =
-#   fl32(amax / 448), E4M3() rounding to the nearest value, ties to the even
-#   mantissa (zero codes and scale when amax is 0);
-# * raw scores R = fl32(q8 . k8) (the dot product exact, one rounding), c =
-#   fl32(fl32(sq * sk) * fl32(1 / sqrt(d))) per key block, S = R c;
+# ------------------------- single-pass 8-bit sparse branch (E4M3 P and V)
+# A second reading of [SLA2 §三]'s 8-bit sparse branch, taken in ONE pass over
+# a row's keys: the scores come from the 8-bit integer codes of Q and K as in
+# the two-pass branch above, while P and V are 8-bit floating-point numbers in
+# the E4M3 format of the OCP 8-bit floating-point specification (1 sign bit, 4
+# exponent bits with bias 7, 3 mantissa bits, no infinities, largest finite
+# value 448, subnormals m * 2^-9 at exponent field 0).  A floating-point P has
+# the headroom an online softmax needs (codes up to 256 with room to 448), so
+# the row maximum need not be known before the first code is formed.
+# * codes: Q per query block and K per key block as quantize_i8 (integers in
+#   [-127, 127]); V per channel over the whole sequence of a head: code =
+#   E4M3(fl32(x * fl32(448 / amax))), scale = fl32(amax / 448), E4M3()
+#   rounding to the nearest value, ties to the even mantissa (zero codes and
+#   scale when amax is 0);
+# * scores I = q8 . k8 (exact integers), S = fl32(I c) with c = fl32(fl32(sq *
+#   sk) * fl32(1 / sqrt(d))), as in the two-pass branch;
 # * the row's selected keys in 64-key units, in the mask's order; m = the
-#   largest fl32(max_unit(R) c) so far, the current unit's included; the
-#   unit's P codes are E4M3(256 exp(S - m)) (at most 256); whenever m rises,
-#   what the earlier units accumulated is multiplied by exp(m_old - m_new);
+#   largest S so far, the current unit's included; the unit's P codes are
+#   E4M3(256 exp(S - m)) (at most 256); whenever m rises, what the earlier
+#   units accumulated is multiplied by exp(m_old - m_new);
 # * O = sv * (sum_u w_u sum_j code_j v8_j) / (sum_u w_u sum_j code_j), w_u =
 #   exp(m_u - m_last); a row with no selected block gives 0.
 # A P code is a quantised value decided by floating point, so it is decided in
-# the precision the kernel computes it in (as for the integer branch's codes):
-# 256 exp(S - m) is taken as fl32(2^t), t = fl32(R a - b), a = fl32(c log2 e),
+# the precision the kernel computes it in (as the integer branch's codes are):
+# 256 exp(S - m) is taken as fl32(2^t), t = fl32(I a - b), a = fl32(c log2 e),
 # b = fl32(fl32(m log2 e) - 8) (f8_p_codes); tests pin that against the exact
 # value.
 _E4M3_MAX = 448.0
@@ -583,23 +587,10 @@ def _f8_codes(x32: np.ndarray, amax: np.float32) -> Tuple[np.ndarray, np.float32
     return e4m3((x32 * r).astype(np.float32).astype(np.float64)), _F32(amax / _F32(_E4M3_MAX))
 
 
-def quantize_fp8(Q, K, V, bq: int, bk: int) -> Dict:
-    """E4M3 codes (as float64 values) and float32 scales of the 8-bit
-    floating-point sparse branch: Q per query block, K per key block (scales
-    [B, H, ceil(N / b)]), V per channel (scales [B, H, d])."""
-    out = {}
-    for name, X, b in (("q", Q, bq), ("k", K, bk)):
-        X = _as_f32_exact(X)
-        B, H, N, d = X.shape
-        nb = n_blocks(N, b)
-        codes, scales = np.zeros((B, H, N, d)), np.zeros((B, H, nb), dtype=np.float32)
-        for bb in range(B):
-            for h in range(H):
-                for i in range(nb):
-                    s, e = block_range(i, b, N)
-                    blk = X[bb, h, s:e]
-                    codes[bb, h, s:e], scales[bb, h, i] = _f8_codes(blk, np.abs(blk).max())
-        out[name + "8"], out["s" + name] = codes, scales
+def quantize_e4m3_channels(V) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-channel E4M3 codes (as float64 values) of V [B, H, N, d]: one scale
+    per (b, h, d index) over all N rows.  Returns (codes [B, H, N, d], scales
+    float32 [B, H, d])."""
     Vf = _as_f32_exact(V)
     B, H, N, d = Vf.shape
     codes, scales = np.zeros((B, H, N, d)), np.zeros((B, H, d), dtype=np.float32)
@@ -608,12 +599,21 @@ def quantize_fp8(Q, K, V, bq: int, bk: int) -> Dict:
             for c in range(d):
                 col = Vf[bb, h, :, c]
                 codes[bb, h, :, c], scales[bb, h, c] = _f8_codes(col, np.abs(col).max())
-    out["v8"], out["sv"] = codes, scales
-    return out
+    return codes, scales
+
+
+def quantize_i8f8(Q, K, V, bq: int, bk: int) -> Dict:
+    """The single-pass branch's 8-bit inputs: Q per query block and K per key
+    block as integers (quantize_blocks), V per channel as E4M3 values."""
+    q8, sq = quantize_blocks(Q, bq)
+    k8, sk = quantize_blocks(K, bk)
+    v8, sv = quantize_e4m3_channels(V)
+    return {"q8": q8, "sq": sq, "k8": k8, "sk": sk, "v8": v8, "sv": sv}
 
 
 def f8_p_codes(R: np.ndarray, a, b) -> np.ndarray:
-    """E4M3 P codes of float32 raw scores R with a = fl32(c log2 e) and
+    """E4M3 P codes of raw scores R (float32 values: here the exact integer
+    scores I, which float32 holds) with a = fl32(c log2 e) and
     b = fl32(fl32(m log2 e) - 8) (broadcast against R): E4M3(fl32(2^t)),
     t = fl32(R a - b) with the product and difference exact in float64 before
     the one rounding, 2^t taken in float64 and rounded to float32."""
@@ -622,14 +622,14 @@ def f8_p_codes(R: np.ndarray, a, b) -> np.ndarray:
     return e4m3(p.astype(np.float64))
 
 
-def sparse_branch_fp8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, with_sums: bool = False):
-    """The single-pass 8-bit floating-point sparse branch on quantize_fp8's
-    codes (see the section comment).  Returns {(b, h, i): [rows_in_block, d]}
-    and with with_sums also {(b, h, i): (L, m, A)}: per query the weighted sum
-    of P codes relative to the final maximum, that maximum (float32), and per
-    output the same weighted mean of |v| (the scale of the float32 sums)."""
-    q8, k8, v8 = qz["q8"], qz["k8"], qz["v8"]
-    sq, sk, sv = qz["sq"], qz["sk"], qz["sv"]
+def sparse_branch_i8f8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, with_sums: bool = False):
+    """The single-pass 8-bit sparse branch on quantize_i8f8's codes (see the
+    section comment).  Returns {(b, h, i): [rows_in_block, d]} and with
+    with_sums also {(b, h, i): (L, m, A)}: per query the weighted sum of P codes
+    relative to the final maximum, that maximum (float32), and per output the
+    same weighted mean of |v| (the scale of the float32 sums)."""
+    q8, k8 = qz["q8"].astype(np.int64), qz["k8"].astype(np.int64)
+    v8, sq, sk, sv = qz["v8"], qz["sq"], qz["sk"], qz["sv"]
     B, H, N, d = q8.shape
     Nq = n_blocks(N, bq)
     lam = _F32(1.0 / math.sqrt(d))
@@ -653,8 +653,9 @@ def sparse_branch_fp8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, w
         num, anum, L = np.zeros((n, d)), np.zeros((n, d)), np.zeros(n)
         m = np.full(n, -np.inf, dtype=np.float32)
         for keys, c in units:
-            R = (q8[b, h, s:e] @ k8[b, h, keys].T).astype(np.float32)     # [n, keys]
-            mu = np.maximum(m, (R.max(axis=1) * c).astype(np.float32))
+            I = q8[b, h, s:e] @ k8[b, h, keys].T                      # exact integers
+            S = (I.astype(np.float32) * c).astype(np.float32)
+            mu = np.maximum(m, S.max(axis=1))
             w = np.where(np.isfinite(m), np.exp(m.astype(np.float64) - mu.astype(np.float64)), 0.0)
             num *= w[:, None]
             anum *= w[:, None]
@@ -662,7 +663,7 @@ def sparse_branch_fp8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, w
             m = mu
             a = _F32(c * _LOG2E_F32)
             bb = ((m * _LOG2E_F32).astype(np.float32) - _F32(8.0)).astype(np.float32)
-            p8 = f8_p_codes(R, a, bb[:, None])
+            p8 = f8_p_codes(I.astype(np.float32), a, bb[:, None])
             num += p8 @ v8[b, h, keys]
             anum += p8 @ np.abs(v8[b, h, keys])
             L += p8.sum(axis=1)

@@ -1,7 +1,7 @@
-"""Pins of the oracle's single-pass 8-bit floating-point sparse branch (SLA2
-write-up §三: Q, K, the attention probabilities and V held in 8 bits, scaled
-into the 8-bit range and scaled back; here as E4M3 floating-point values of
-the OCP 8-bit floating-point specification).
+"""Pins of the oracle's single-pass 8-bit sparse branch (SLA2 write-up §三: Q,
+K, the attention probabilities and V held in 8 bits, scaled into the 8-bit
+range and scaled back; here Q and K as integers, P and V as E4M3
+floating-point values of the OCP 8-bit floating-point specification).
 
 Pinned by the format's definition (every bit pattern decoded from sign,
 biased exponent and mantissa, checked against hand values; the rounding
@@ -63,26 +63,29 @@ def test_rounding_matches_brute_force_nearest():
     assert np.array_equal(r, nearest)
 
 
-def test_quantiser_bound_and_granularity():
+def test_channel_quantiser_bound_and_granularity():
     rng = np.random.default_rng(1)
     X = rng.normal(size=(1, 2, 150, 16)).astype(np.float32)
-    X[0, 1, 64:128] *= 50.0
-    qz = O.quantize_fp8(X, X, X, 64, 64)
-    assert qz["sq"].shape == (1, 2, 3) and qz["sv"].shape == (1, 2, 16)
+    X[0, 1, :, 3] *= 50.0
+    codes, sv = O.quantize_e4m3_channels(X)
+    assert sv.shape == (1, 2, 16)
     for h in range(2):
-        for i in range(3):
-            s, e = O.block_range(i, 64, 150)
-            blk = X[0, h, s:e].astype(np.float64)
-            sc = float(qz["sq"][0, h, i])
-            assert qz["sq"][0, h, i] == np.float32(np.abs(X[0, h, s:e]).max()) / np.float32(448)
-            codes = qz["q8"][0, h, s:e]
-            assert np.abs(codes).max() == 448.0
+        for c in range(16):
+            col = X[0, h, :, c].astype(np.float64)
+            assert sv[0, h, c] == np.float32(np.abs(X[0, h, :, c]).max()) / np.float32(448)
+            cc = codes[0, h, :, c]
+            assert np.abs(cc).max() == 448.0
+            assert np.array_equal(O.e4m3(cc), cc)         # every code is an E4M3 value
             # 3 mantissa bits: relative error <= 2^-4 for normals, 2^-10 absolute below
-            err = np.abs(codes * sc - blk)
-            assert np.all(err <= (2.0 ** -4 * np.abs(blk) + 2.0 ** -10 * sc) * (1 + 1e-6))
+            err = np.abs(cc * float(sv[0, h, c]) - col)
+            assert np.all(err <= (2.0 ** -4 * np.abs(col) + 2.0 ** -10 * float(sv[0, h, c])) * (1 + 1e-6))
     zero = np.zeros((1, 1, 64, 8), np.float32)
-    qz0 = O.quantize_fp8(zero, zero, zero, 64, 64)
-    assert not qz0["q8"].any() and not qz0["sq"].any() and not qz0["sv"].any()
+    z, zs = O.quantize_e4m3_channels(zero)
+    assert not z.any() and not zs.any()
+    qz = O.quantize_i8f8(X, X, X, 64, 64)
+    ref, refs = O.quantize_blocks(X, 64)
+    assert np.array_equal(qz["q8"], ref) and np.array_equal(qz["sq"], refs)
+    assert np.array_equal(qz["v8"], codes) and np.array_equal(qz["sv"], sv)
 
 
 def _csr_all(B, H, Nq, Nk, order=None):
@@ -100,9 +103,9 @@ def test_equal_scores_give_the_plain_mean():
     V = rng.normal(size=(1, 1, 256, 32)).astype(np.float32)
     Q2 = np.zeros((1, 1, 256, 32), np.float32)
     Q2[:, :, :128] = Q
-    qz = O.quantize_fp8(Q2, K, V, 128, 64)
+    qz = O.quantize_i8f8(Q2, K, V, 128, 64)
     rp, ci = _csr_all(1, 1, 2, 4)
-    out, sums = O.sparse_branch_fp8(qz, 128, 64, rp, ci, with_sums=True)
+    out, sums = O.sparse_branch_i8f8(qz, 128, 64, rp, ci, with_sums=True)
     want = qz["sv"][0, 0].astype(np.float64) * qz["v8"][0, 0].mean(axis=0)
     np.testing.assert_allclose(out[(0, 0, 0)], np.broadcast_to(want, (128, 32)), rtol=1e-14, atol=0)
     L, m, _ = sums[(0, 0, 0)]
@@ -114,12 +117,12 @@ def _exact_on_dequantised(qz, b, h, i, bq, bk, sel):
     the selected blocks (no 8-bit P)."""
     N, d = qz["q8"].shape[2:]
     s, e = O.block_range(i, bq, N)
-    q = qz["q8"][b, h, s:e] * float(qz["sq"][b, h, i])
+    q = qz["q8"][b, h, s:e].astype(np.float64) * float(qz["sq"][b, h, i])
     keys, ks = [], []
     for j in sel:
         a, z = O.block_range(j, bk, N)
         keys.append(np.arange(a, z))
-        ks.append(qz["k8"][b, h, a:z] * float(qz["sk"][b, h, j]))
+        ks.append(qz["k8"][b, h, a:z].astype(np.float64) * float(qz["sk"][b, h, j]))
     keys = np.concatenate(keys)
     k = np.concatenate(ks)
     v = qz["v8"][b, h, keys] * qz["sv"][b, h].astype(np.float64)[None, :]
@@ -147,11 +150,11 @@ def test_close_to_exact_attention_with_a_rising_maximum(rising):
         qdir = Q.mean(axis=2, keepdims=True)
         for j in range(N // bk):
             K[:, :, j * bk:(j + 1) * bk] += (0.6 * j) * qdir / np.linalg.norm(qdir) * math.sqrt(d)
-    qz = O.quantize_fp8(Q, K, V, bq, bk)
+    qz = O.quantize_i8f8(Q, K, V, bq, bk)
     Nq, Nk = N // bq, N // bk
     rp, ci = _csr_all(B, H, Nq, Nk)
     rows = [(0, h, i) for h in range(H) for i in range(Nq)]
-    out, sums = O.sparse_branch_fp8(qz, bq, bk, rp, ci, rows=rows, with_sums=True)
+    out, sums = O.sparse_branch_i8f8(qz, bq, bk, rp, ci, rows=rows, with_sums=True)
     worst = 0.0
     rises = 0
     for (b, h, i) in rows:
@@ -183,16 +186,17 @@ def test_first_unit_holding_the_maximum_needs_no_rescale():
     K = (0.3 * rng.normal(size=(B, H, N, d))).astype(np.float32)
     K[:, :, :bk] += (2.0 * u).astype(np.float32)          # so block 0 scores highest for every query
     V = rng.normal(size=(B, H, N, d)).astype(np.float32)
-    qz = O.quantize_fp8(Q, K, V, bq, bk)
+    qz = O.quantize_i8f8(Q, K, V, bq, bk)
     rp, ci = _csr_all(B, H, N // bq, N // bk)
-    out, sums = O.sparse_branch_fp8(qz, bq, bk, rp, ci, with_sums=True)
+    out, sums = O.sparse_branch_i8f8(qz, bq, bk, rp, ci, with_sums=True)
     lam = np.float32(1.0 / math.sqrt(d))
     l2e = np.float32(math.log2(math.e))
     for i in range(N // bq):
         s, e = O.block_range(i, bq, N)
         c = [np.float32(np.float32(qz["sq"][0, 0, i] * qz["sk"][0, 0, j]) * lam) for j in range(N // bk)]
-        R = (qz["q8"][0, 0, s:e] @ qz["k8"][0, 0].T).astype(np.float32)
-        Sb = [(R[:, j * bk:(j + 1) * bk].max(axis=1) * c[j]).astype(np.float32) for j in range(N // bk)]
+        I = qz["q8"][0, 0, s:e].astype(np.int64) @ qz["k8"][0, 0].astype(np.int64).T
+        R = I.astype(np.float32)
+        Sb = [(R[:, j * bk:(j + 1) * bk] * c[j]).astype(np.float32).max(axis=1) for j in range(N // bk)]
         assert np.all(Sb[0] >= np.max(Sb, axis=0))
         m = Sb[0]
         b = ((m * l2e).astype(np.float32) - np.float32(8)).astype(np.float32)
@@ -216,18 +220,19 @@ def _midpoint_distance(x):
 def test_float32_codes_match_the_definition_on_the_480p_sample():
     """On the 480p SLA2 workload (two heads, the oracle's own mask), every P
     code f8_p_codes forms for 16 sampled row blocks equals E4M3(256 exp(S -
-    m)) evaluated in float64 (S = R c exactly, m the same running maximum),
+    m)) evaluated in float64 (S = fl32(I c), m the same running maximum),
     except where that value lies within the float32 error bound of an E4M3
     midpoint; those few differ by one E4M3 step.  Bound on the relative error
     of the float32 value: each rounding adds at most u |value| (u = 2^-24) to
-    t in log2 units: R (u log2(e) |S|), a and fl32(log2 e) (2 u log2(e) |S|),
-    fl32(m log2 e) (2 u log2(e) |m|), b (u |b|), t (u |t|); then 2^E - 1 <=
-    E ln 2 (1 + E), plus u for rounding 2^t; doubled for slack."""
+    t in log2 units: a and fl32(log2 e) (2 u log2(e) |I c|), fl32(m log2 e)
+    (2 u log2(e) |m|), b (u |b|), t (u |t|); then 2^E - 1 <= E ln 2 (1 + E),
+    plus u for rounding 2^t; doubled for slack."""
     import gen
     wl = gen.WORKLOADS["video480p-sla2-N32760"]
     x = gen.make(wl, heads=2)
     rp, ci, _ = O.mask(x.Q, x.K, wl.bq, wl.bk, wl.k_frac, wl.p, keep_info=False)
-    qz = O.quantize_fp8(x.Q, x.K, x.V, wl.bq, wl.bk)
+    qz = O.quantize_i8f8(x.Q, x.K, x.V, wl.bq, wl.bk)
+    q8, k8 = qz["q8"].astype(np.int64), qz["k8"].astype(np.int64)
     lam = np.float32(1.0 / math.sqrt(wl.d))
     l2e = np.float32(math.log2(math.e))
     L2 = math.log2(math.e)
@@ -242,16 +247,17 @@ def test_float32_codes_match_the_definition_on_the_480p_sample():
         for j in ci[rp[r]:rp[r + 1]]:
             ks, ke = O.block_range(int(j), wl.bk, wl.N)   # bk = 64: one unit per block
             c = np.float32(np.float32(qz["sq"][0, h, i] * qz["sk"][0, h, j]) * lam)
-            Rx = qz["q8"][0, h, s:e] @ qz["k8"][0, h, ks:ke].T          # exact
-            R = Rx.astype(np.float32)
-            m = np.maximum(m, (R.max(axis=1) * c).astype(np.float32))
+            I = q8[0, h, s:e] @ k8[0, h, ks:ke].T
+            S = (I.astype(np.float32) * c).astype(np.float32)
+            m = np.maximum(m, S.max(axis=1))
             b = ((m * l2e).astype(np.float32) - np.float32(8)).astype(np.float32)
-            got = O.f8_p_codes(R, np.float32(c * l2e), b[:, None])
-            S = Rx * np.float64(c)
-            xv = 256.0 * np.exp(S - m.astype(np.float64)[:, None])
+            got = O.f8_p_codes(I.astype(np.float32), np.float32(c * l2e), b[:, None])
+            xv = 256.0 * np.exp(S.astype(np.float64) - m.astype(np.float64)[:, None])
             want = O.e4m3(xv)
             t = np.log2(np.maximum(xv, 1e-300))
-            E = _U * (3 * L2 * np.abs(S) + 2 * L2 * np.abs(m.astype(np.float64))[:, None]
+            Ic = np.abs(I * np.float64(c))
+            E = _U * (2 * L2 * Ic + L2 * np.abs(S.astype(np.float64))
+                      + 2 * L2 * np.abs(m.astype(np.float64))[:, None]
                       + np.abs(b.astype(np.float64))[:, None] + np.abs(t))
             bound = 2.0 * xv * (E * math.log(2.0) * (1 + E) + _U)
             dist, step = _midpoint_distance(xv)
@@ -269,11 +275,11 @@ def test_empty_row_and_partial_units():
     rng = np.random.default_rng(5)
     B, H, N, d, bq, bk = 1, 1, 200, 32, 64, 128   # bk = 128: two units per block; last block 72 keys
     Q, K, V = (rng.normal(size=(B, H, N, d)).astype(np.float32) for _ in range(3))
-    qz = O.quantize_fp8(Q, K, V, bq, bk)
+    qz = O.quantize_i8f8(Q, K, V, bq, bk)
     Nq = O.n_blocks(N, bq)
     rp = np.array([0, 0, 1, 3, 4], np.int64)          # row 0 empty
     ci = np.array([1, 0, 1, 0], np.int64)
-    out = O.sparse_branch_fp8(qz, bq, bk, rp, ci)
+    out = O.sparse_branch_i8f8(qz, bq, bk, rp, ci)
     assert not out[(0, 0, 0)].any()
     for i, sel in ((1, [1]), (2, [0, 1]), (3, [0])):
         exact, Sx = _exact_on_dequantised(qz, 0, 0, i, bq, bk, sel)
