@@ -412,6 +412,28 @@ def main():
                      "frac": i8_ops / (t_i8 * 1e-3) / 1e12 / PEAK_I8_TOPS,
                      "kernel": f"attn_i8_kernel<d={wl.d},bq={wl.bq},bk={wl.bk}>",
                      "vs_bf16_sparse": t_sp / t_i8, "with_quantize_vs_bf16_sparse": t_sp / (t_q + t_i8)}
+        # the single-pass 8-bit branch (int8 scores, E4M3 P and V) on the
+        # same mask: half its matrix work is int8, half E4M3, both priced at
+        # the 5 POP/s (int8) = 5 PFLOP/s (fp8) dense peak
+        qb2 = S.sla_quantize_i8f8(q, k, v, wl.bq, wl.bk)
+        S.sla_sparse_fwd_i8f8(qb2, q, wl.bq, wl.bk, rp, ci, out=out)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(args.steps):
+            S.sla_quantize_i8f8(q, k, v, wl.bq, wl.bk, out=qb2)
+        e[1].record()
+        for _ in range(args.steps):
+            S.sla_sparse_fwd_i8f8(qb2, q, wl.bq, wl.bk, rp, ci, out=out)
+        e[2].record()
+        torch.cuda.synchronize()
+        t_q2 = e[0].elapsed_time(e[1]) / args.steps
+        t_f8 = e[1].elapsed_time(e[2]) / args.steps
+        res["i8f8"] = {"quantize_ms": t_q2, "sparse_fwd_i8f8_ms": t_f8,
+                       "achieved": i8_ops / (t_f8 * 1e-3) / 1e12, "peak": PEAK_I8_TOPS, "unit": "TOP/s",
+                       "frac": i8_ops / (t_f8 * 1e-3) / 1e12 / PEAK_I8_TOPS,
+                       "kernel": f"attn_i8f8_kernel<d={wl.d},bq={wl.bq},bk={wl.bk}>",
+                       "vs_bf16_sparse": t_sp / t_f8, "with_quantize_vs_bf16_sparse": t_sp / (t_q2 + t_f8)}
 
     # the sparse branch's backward (mask fixed) on this step's mask: the mask
     # transpose, the dQ pass and the dK/dV pass.  Algorithmic work: the five

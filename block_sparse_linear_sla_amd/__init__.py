@@ -29,6 +29,7 @@ EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_mask_pre
            "sla_sparse_fwd",
            "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
            "sla_dense_fwd", "sla_i8_layout_of", "sla_quantize_i8", "sla_sparse_fwd_i8",
+           "sla_quantize_i8f8", "sla_sparse_fwd_i8f8",
            "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_linear_bwd", "sla_attn_bwd", "sla_alpha_grad",
            "sla_status_string")
 
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.sla_i8_layout_of.argtypes = [P, ctypes.POINTER(I8Layout)]
         L.sla_quantize_i8.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_sparse_fwd_i8.argtypes = [P, vp, ctypes.c_size_t, vp, vp, vp, vp]
+        L.sla_quantize_i8f8.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_sparse_fwd_i8f8.argtypes = [P, vp, ctypes.c_size_t, vp, vp, vp, vp]
         L.sla_bwd_workspace_bytes.argtypes = [P]
         L.sla_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.sla_sparse_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -97,7 +100,8 @@ def lib() -> ctypes.CDLL:
         L.sla_status_string.restype = ctypes.c_char_p
         for fn in ("sla_mask", "sla_mask_prepared", "sla_mask_noalloc", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
                    "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd", "sla_i8_layout_of",
-                   "sla_quantize_i8", "sla_sparse_fwd_i8", "sla_sparse_bwd", "sla_linear_bwd",
+                   "sla_quantize_i8", "sla_sparse_fwd_i8", "sla_quantize_i8f8", "sla_sparse_fwd_i8f8",
+                   "sla_sparse_bwd", "sla_linear_bwd",
                    "sla_attn_bwd", "sla_alpha_grad"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
@@ -338,6 +342,30 @@ def sla_sparse_fwd_i8(qbuf: torch.Tensor, like: torch.Tensor, bq: int, bk: int, 
     o = out if out is not None else torch.empty_like(like)
     _check("sla_sparse_fwd_i8", lib().sla_sparse_fwd_i8(ctypes.byref(prob), _ptr(qbuf), qbuf.numel(),
                                                         _ptr(row_ptr), _ptr(col_idx), _ptr(o), _stream()))
+    return o
+
+
+def sla_quantize_i8f8(q, k, v, bq: int, bk: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """int8 Q, K and E4M3 V codes and their scales in one uint8 buffer (the
+    layout of sla_i8_layout_of; i8_views splits it, vt8 as E4M3 bytes)."""
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    n = sla_i8_layout_of(prob).total
+    buf = out if out is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
+    _check("sla_quantize_i8f8", lib().sla_quantize_i8f8(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(buf),
+                                                      buf.numel(), _stream()))
+    return buf
+
+
+def sla_sparse_fwd_i8f8(qbuf: torch.Tensor, like: torch.Tensor, bq: int, bk: int, row_ptr, col_idx,
+                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The single-pass 8-bit sparse branch (int8 scores, E4M3 P and V) over
+    the codes in qbuf; `like` gives the shape, dtype and device of Q (its data
+    is not read)."""
+    prob = problem(like, bq, bk)
+    o = out if out is not None else torch.empty_like(like)
+    _check("sla_sparse_fwd_i8f8", lib().sla_sparse_fwd_i8f8(ctypes.byref(prob), _ptr(qbuf), qbuf.numel(),
+                                                          _ptr(row_ptr), _ptr(col_idx), _ptr(o), _stream()))
     return o
 
 

@@ -52,6 +52,8 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -95,6 +97,30 @@ __device__ __forceinline__ uint32_t code8(float x, float r) {
   const float c = fminf(fmaxf(rintf(x * r), -127.f), 127.f);
   return (uint32_t)(int)c & 0xffu;
 }
+
+// Code formats: symmetric int8 in [-127, 127], or E4M3 (the OCP 8-bit
+// floating-point format, largest finite value 448).
+enum Fmt : int { FMT_I8 = 0, FMT_F8 = 1 };
+template <int F>
+struct CodeFmt;
+template <>
+struct CodeFmt<FMT_I8> {
+  static constexpr float RANGE = 127.f;
+  // four codes of x * r, byte e = value e
+  __device__ static uint32_t pack4(float x0, float x1, float x2, float x3, float r) {
+    return code8(x0, r) | (code8(x1, r) << 8) | (code8(x2, r) << 16) | (code8(x3, r) << 24);
+  }
+};
+template <>
+struct CodeFmt<FMT_F8> {
+  static constexpr float RANGE = 448.f;
+  // the products x * r are rounded to E4M3 by the conversion instruction
+  // (nearest, ties to even); |x * r| <= 448 up to one float32 rounding
+  __device__ static uint32_t pack4(float x0, float x1, float x2, float x3, float r) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 * r, x1 * r, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2 * r, x3 * r, lo, true);
+  }
+};
 
 __device__ __forceinline__ float block_max(float v, float* red) {
 #pragma unroll
@@ -154,10 +180,11 @@ __device__ __forceinline__ i32x16 mfma8(const i32x4& a, const i32x4& b, const i3
 // ---------------------------------------------------------------- quantisers
 // Codes of one block of BR rows of X [BH][N][D] (rows past N read as zero),
 // written to codes [BH][Nb * BR][D]; its scale to scales [BH][Nb].
-template <int ES, int D, int BR>
+template <int ES, int D, int BR, int F>
 __global__ __launch_bounds__(256) void quant_block_kernel(const char* __restrict__ X, int N, int Nb,
                                                           int8_t* __restrict__ codes,
                                                           float* __restrict__ scales) {
+  using CF = CodeFmt<F>;
   using C = Chunk<ES>;
   constexpr int CH = C::N, CPR = D / CH, NC = BR * CPR / 256;
   static_assert(NC * 256 == BR * CPR, "chunks per thread");
@@ -178,7 +205,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const char* __restrict
     for (int e = 0; e < CH; ++e) amax = fmaxf(amax, fabsf(x[k][e]));
   }
   amax = block_max(amax, red);
-  const float r = amax > 0.f ? __fdiv_rn(127.f, amax) : 0.f;
+  const float r = amax > 0.f ? __fdiv_rn(CF::RANGE, amax) : 0.f;
   int8_t* cb = codes + ((size_t)bh * Nb + blk) * BR * D;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
@@ -186,13 +213,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(const char* __restrict
     uint32_t wv[CH / 4];
 #pragma unroll
     for (int j = 0; j < CH / 4; ++j)
-      wv[j] = code8(x[k][4 * j], r) | (code8(x[k][4 * j + 1], r) << 8) | (code8(x[k][4 * j + 2], r) << 16) |
-              (code8(x[k][4 * j + 3], r) << 24);
+      wv[j] = CF::pack4(x[k][4 * j], x[k][4 * j + 1], x[k][4 * j + 2], x[k][4 * j + 3], r);
     int8_t* dst = cb + (size_t)rr * D + cc * CH;
     if (CH == 8) *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0], wv[CH / 4 - 1]);
     else *reinterpret_cast<uint32_t*>(dst) = wv[0];
   }
-  if (threadIdx.x == 0) scales[bh * Nb + blk] = __fdiv_rn(amax, 127.f);
+  if (threadIdx.x == 0) scales[bh * Nb + blk] = __fdiv_rn(amax, CF::RANGE);
 }
 
 // Per-channel absolute maxima of rows [chunk * QROWS, +QROWS) of V.
@@ -227,25 +253,31 @@ __global__ __launch_bounds__(256) void vamax_kernel(const char* __restrict__ V, 
   }
 }
 
-// sv = amax / 127 and rv = 127 / amax (0 when amax is 0) per channel.
+// sv = amax / R and rv = R / amax (0 when amax is 0) per channel, R the
+// format's range (127 or 448).
+template <int F>
 __global__ __launch_bounds__(128) void vscale_kernel(const float* __restrict__ vpart, int nchunk, int D,
                                                      float* __restrict__ sv, float* __restrict__ rv) {
+  constexpr float R = CodeFmt<F>::RANGE;
   const long long bh = blockIdx.x;
   const int c = threadIdx.x;
   if (c >= D) return;
   float a = 0.f;
   for (int k = 0; k < nchunk; ++k) a = fmaxf(a, vpart[((size_t)bh * nchunk + k) * D + c]);
-  sv[bh * D + c] = __fdiv_rn(a, 127.f);
-  rv[bh * D + c] = a > 0.f ? __fdiv_rn(127.f, a) : 0.f;
+  sv[bh * D + c] = __fdiv_rn(a, R);
+  rv[bh * D + c] = a > 0.f ? __fdiv_rn(R, a) : 0.f;
 }
 
 // Codes of one 64-key tile of V, written transposed: vt8 [BH][ntile][D][64],
 // key k of the tile at byte 32 (k / 32) + 16 ((k / 4) % 2) + 4 ((k % 32) / 8)
-// + k % 4 of its channel row (keys past N are zero).
-template <int ES, int D>
+// + k % 4 of its channel row for int8 (the order of a 32-key P operand), at
+// byte 32 ((k / 4) % 2) + 16 (k / 32) + 4 ((k % 32) / 8) + k % 4 for E4M3 (the
+// order of a 64-key P operand); keys past N are zero.
+template <int ES, int D, int F>
 __global__ __launch_bounds__(256) void quant_v_kernel(const char* __restrict__ V, int N, int ntile,
                                                       const float* __restrict__ rv,
                                                       int8_t* __restrict__ vt8) {
+  using CF = CodeFmt<F>;
   using C = Chunk<ES>;
   constexpr int CH = C::N, CPR = D / CH;
   constexpr int RS = 17;  // LDS row stride in words (64 bytes + 4 of padding against bank conflicts)
@@ -265,13 +297,12 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const char* __restrict__ V
       C::unpack(v, x[j]);
     }
     const int k = 4 * kq;
-    const int word = 8 * (k >> 5) + 4 * ((k >> 2) & 1) + ((k & 31) >> 3);
+    const int word = F == FMT_I8 ? 8 * (k >> 5) + 4 * ((k >> 2) & 1) + ((k & 31) >> 3)
+                                 : 8 * ((k >> 2) & 1) + 4 * (k >> 5) + ((k & 31) >> 3);
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       const int c = cc * CH + e;
-      const float r = rvh[c];
-      T[c * RS + word] = code8(x[0][e], r) | (code8(x[1][e], r) << 8) | (code8(x[2][e], r) << 16) |
-                         (code8(x[3][e], r) << 24);
+      T[c * RS + word] = CF::pack4(x[0][e], x[1][e], x[2][e], x[3][e], rvh[c]);
     }
   }
   __syncthreads();
@@ -543,8 +574,207 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_i8_kernel(
     }
 }
 
+// ------------------------------------- single pass: int8 scores, E4M3 P V
+// v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 operands and unit scales
+// (E8M0 127 = 2^0): lane l supplies 32 bytes of operand row / column l%32
+// from half l/32 of the k range; A and B take the same k order, whatever it
+// is, so the operands below are built to agree with each other and not with
+// any particular order.  Accumulator element i of lane l is row 8(i/4) +
+// 4(l/32) + i%4, column l%32 (as every 32 x 32 float32 MFMA).  The products
+// are exact; their sum is not always rounded once (measured: within 2^-12 of
+// the sum of |products| for operands of wide exponent range).
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 cat8(const uint4& x, const uint4& y) {
+  return i32x8{(int)x.x, (int)x.y, (int)x.z, (int)x.w, (int)y.x, (int)y.y, (int)y.z, (int)y.w};
+}
+
+// One workgroup of BQ/32 wavefronts per mask row, ONE pass over the row's
+// 64-key units (K and V^T tiles of unit u+2 loaded while unit u is computed,
+// three LDS stages as in attn_i8_kernel):
+//   S^T = K Q^T         int8 codes, exact int32 (score_tile); lane (query
+//                       l%32, half h) holds keys 32 t + 8 a + 4 h + b of the
+//                       unit (tile t, element 4 a + b)
+//   m  = running maximum of S = fl32(I c) over the units so far (lanes l,
+//        l^32 agree); when it rises, O and l are multiplied by
+//        exp(m_old - m_new)
+//   P codes = E4M3(exp2(fma(I, a, -nb))), a = fl32(c log2 e), nb =
+//        fl32(m log2 e) - 8: 256 exp(S - m), keys past N give 0
+//   O^T += V^T P^T      E4M3, 64 keys per MFMA; byte j of a lane's P operand
+//                       is tile j/16, element j%16, and the V^T tile row
+//                       holds key 32 t + 8 a + 4 h + b at byte 32 h + 16 t +
+//                       4 a + b
+//   l  += ones P^T      (one MFMA: every row of the result is the code sum)
+//   O = sv O / l at the end.
+template <int D, int BQ, int SUB, int OES>
+__global__ __launch_bounds__(BQ / 32 * 64, 2) void attn_i8f8_kernel(
+    const int8_t* __restrict__ q8, const int8_t* __restrict__ k8, const int8_t* __restrict__ vt8,
+    const float* __restrict__ sq, const float* __restrict__ sk, const float* __restrict__ sv,
+    const int* __restrict__ row_ptr, const int* __restrict__ col_idx, char* __restrict__ O, int N, int Nq,
+    int Nk, float lam, float l2e) {
+  using TT = I8Tiles<D>;
+  constexpr int NW = BQ / 32;
+  constexpr int STAGE = TT::KT + TT::VT;
+  __shared__ __attribute__((aligned(16))) char st0[STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[STAGE];
+  __shared__ __attribute__((aligned(16))) char st2[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const long long row = xcd_row(blockIdx.x, (long long)gridDim.x);
+  const long long bh = row / Nq;
+  const int qi = (int)(row % Nq);
+  const int base = row_ptr[row];
+  const int nunits = (row_ptr[row + 1] - base) * SUB;
+  const int Npad = Nk * SUB * 64;
+  const int q = qi * BQ + 32 * w + l32;  // query rows are padded to Nq * BQ
+
+  i32x4 qf[D / 32];
+  const int8_t* qrow = q8 + ((size_t)bh * Nq * BQ + q) * D;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) qf[kk] = *reinterpret_cast<const i32x4*>(qrow + 32 * kk + 16 * hi);
+  int koff[D / 32], voff[2];
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) koff[kk] = l32 * D + 16 * ((2 * kk + hi) ^ TT::swk(l32));
+  // V^T operand (A of O^T): channel row l32 of a 32-row tile, bytes 32 hi ..
+  // 32 hi + 31 of its 64-byte row (swizzled 16-byte chunks)
+#pragma unroll
+  for (int c = 0; c < 2; ++c) voff[c] = l32 * 64 + 16 * ((2 * hi + c) ^ TT::swv(l32));
+  const i32x8 ones = i32x8{0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                           0x38383838, 0x38383838, 0x38383838, 0x38383838};  // E4M3 1.0
+
+  f32x16 acc[D / 32], lacc = f32x16{};
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+  if (nunits > 0) {
+    const float sqv = sq[bh * Nq + qi];
+    const float* skh = sk + bh * Nk;
+    const auto rk = buf_rsrc(k8 + (size_t)bh * Npad * D, (uint32_t)Npad * D);
+    const auto rv = buf_rsrc(vt8 + (size_t)bh * Npad * D, (uint32_t)Npad * D);
+    using LP = I8Load<D, NW>;
+    constexpr int PF = D == 128 ? 2 : 1;
+    float m = -INFINITY, nb = 0.f;
+    auto blk_of = [&](int u) { return col_idx[base + u / SUB]; };
+    auto key0_of = [&](int u, int blk) { return (blk * SUB + u % SUB) * 64; };
+    auto issue = [&](int u, char* dst) __attribute__((always_inline)) {
+      const LP lp(w, opaque(lane));
+      const int k0 = key0_of(u, blk_of(u));
+      lp.load_k(rk, k0, dst);
+      lp.load_v(rv, k0, dst + TT::KT);
+    };
+    auto unit = [&](const char* cur, int u) __attribute__((always_inline)) {
+      const int blk = blk_of(u);
+      const int lim = min(64, N - key0_of(u, blk));  // keys of the unit below N (<= 0: none)
+      if (lim <= 0) return;
+      const float cu = (sqv * skh[blk]) * lam;       // fl32(fl32(sq sk) / sqrt(d))
+      const float au = cu * l2e;
+      i32x16 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) sc[t] = score_tile<D, PF>(cur + t * 32 * D, qf, koff);
+      // A unit that runs past N (only the last unit of a sequence, lim < 64):
+      // keys at offset >= lim do not exist; they are left out of the maximum
+      // and their code bytes are cleared after the conversion
+      const int limh = lim - 4 * hi;  // element i of tile t is key 32 t + 8 (i/4) + 4 hi + i%4
+      int im = INT_MIN;
+      if (lim < 64) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) im = max(im, 32 * t + 8 * (i >> 2) + (i & 3) < limh ? sc[t][i] : INT_MIN);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) im = max(im, max(sc[0][i], sc[1][i]));
+      }
+      im = max(im, __shfl_xor(im, 32));  // lanes l, l^32 hold the two key halves of one query
+      const float mxs = (float)im * cu;  // the unit's largest S = fl32(I c) (c >= 0)
+      if (__ballot(mxs > m)) {
+        const float m_new = fmaxf(m, mxs);
+        const float corr = __builtin_amdgcn_exp2f((m - m_new) * l2e);  // 0 on the first unit
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= corr;
+        lacc *= corr;
+        m = m_new;
+        nb = (m * l2e) - 8.f;
+      }
+      // P codes: byte j of the operand = tile j/16, element j%16
+      i32x8 pc;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[t][4 * e], au, -nb));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[t][4 * e + 1], au, -nb));
+          const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[t][4 * e + 2], au, -nb));
+          const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)sc[t][4 * e + 3], au, -nb));
+          const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          pc[4 * t + e] = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, lo, true);
+        }
+      if (lim < 64) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int nv = min(4, max(0, limh - (32 * t + 8 * e)));  // valid keys of this word
+            pc[4 * t + e] &= nv == 4 ? -1 : (int)((1u << (8 * nv)) - 1u);
+          }
+      }
+      const char* Vs = cur + TT::KT;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        acc[dt] = mfma_f8(cat8(rd16(Vs + dt * 32 * 64 + voff[0]), rd16(Vs + dt * 32 * 64 + voff[1])), pc, acc[dt]);
+      lacc = mfma_f8(ones, pc, lacc);
+    };
+    auto step = [&](int u, const char* cur, char* ahead) __attribute__((always_inline)) {
+      if (u + 1 < nunits) wait_vm<2 * LP::NK>();  // unit u landed; unit u+1 may be in flight
+      else wait_vm<0>();
+      __syncthreads();  // every wavefront's loads of unit u landed; unit u-1 consumed
+      if (u + 2 < nunits) issue(u + 2, ahead);
+      unit(cur, u);
+    };
+    issue(0, st0);
+    if (nunits > 1) issue(1, st1);
+    int u = 0;
+    for (; u + 3 <= nunits; u += 3) {
+      step(u, st0, st2);
+      step(u + 1, st1, st0);
+      step(u + 2, st2, st1);
+    }
+    if (u < nunits) step(u, st0, st2);
+    if (u + 1 < nunits) step(u + 1, st1, st0);
+  }
+
+  const float L = lacc[0];
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (q >= N) return;
+  const float* svh = sv + bh * D;
+  char* orow = O + ((size_t)bh * N + q) * D * OES;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int c0 = 32 * dt + 8 * a + 4 * hi;
+      const float4 s4 = *reinterpret_cast<const float4*>(svh + c0);
+      const float sc4[4] = {s4.x, s4.y, s4.z, s4.w};
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[j] = (acc[dt][4 * a + j] * sc4[j]) * inv;
+      if (OES == 4) {
+        *reinterpret_cast<float4*>(orow + c0 * 4) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        const f32x2 lo = {o[0], o[1]}, hi2 = {o[2], o[3]};
+        *reinterpret_cast<uint2*>(orow + c0 * 2) =
+            make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, bf16x2)),
+                       __builtin_bit_cast(uint32_t, __builtin_convertvector(hi2, bf16x2)));
+      }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
-template <int ES, int D>
+// Q and K codes in format FQK, V codes in format FV.
+template <int ES, int D, int FQK, int FV>
 hipError_t quant_dispatch(const Shape& s, const void* Q, const void* K, const void* V, char* qb,
                           const I8Layout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H;
@@ -556,26 +786,26 @@ hipError_t quant_dispatch(const Shape& s, const void* Q, const void* K, const vo
   float* sq = reinterpret_cast<float*>(qb + L.sq);
   float* sk = reinterpret_cast<float*>(qb + L.sk);
   if (s.bq == 128)
-    hipLaunchKernelGGL((quant_block_kernel<ES, D, 128>), dim3((unsigned)(BH * s.Nq)), dim3(256), 0, st, q, s.N,
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 128, FQK>), dim3((unsigned)(BH * s.Nq)), dim3(256), 0, st, q, s.N,
                        s.Nq, q8, sq);
   else
-    hipLaunchKernelGGL((quant_block_kernel<ES, D, 64>), dim3((unsigned)(BH * s.Nq)), dim3(256), 0, st, q, s.N,
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 64, FQK>), dim3((unsigned)(BH * s.Nq)), dim3(256), 0, st, q, s.N,
                        s.Nq, q8, sq);
   // K: one scale per key block of bk rows
   if (s.bk == 128)
-    hipLaunchKernelGGL((quant_block_kernel<ES, D, 128>), dim3((unsigned)(BH * s.Nk)), dim3(256), 0, st, k, s.N,
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 128, FQK>), dim3((unsigned)(BH * s.Nk)), dim3(256), 0, st, k, s.N,
                        s.Nk, k8, sk);
   else
-    hipLaunchKernelGGL((quant_block_kernel<ES, D, 64>), dim3((unsigned)(BH * s.Nk)), dim3(256), 0, st, k, s.N,
+    hipLaunchKernelGGL((quant_block_kernel<ES, D, 64, FQK>), dim3((unsigned)(BH * s.Nk)), dim3(256), 0, st, k, s.N,
                        s.Nk, k8, sk);
   float* vpart = reinterpret_cast<float*>(qb + L.vpart);
   float* sv = reinterpret_cast<float*>(qb + L.sv);
   float* rv = reinterpret_cast<float*>(qb + L.rv);
   hipLaunchKernelGGL((vamax_kernel<ES, D>), dim3((unsigned)L.vchunks, (unsigned)BH), dim3(256), 0, st, v, s.N,
                      L.vchunks, vpart);
-  hipLaunchKernelGGL(vscale_kernel, dim3((unsigned)BH), dim3(128), 0, st, vpart, L.vchunks, D, sv, rv);
+  hipLaunchKernelGGL((vscale_kernel<FV>), dim3((unsigned)BH), dim3(128), 0, st, vpart, L.vchunks, D, sv, rv);
   const int ntile = s.Nk * s.bk / 64;
-  hipLaunchKernelGGL((quant_v_kernel<ES, D>), dim3((unsigned)ntile, (unsigned)BH), dim3(256), 0, st, v, s.N,
+  hipLaunchKernelGGL((quant_v_kernel<ES, D, FV>), dim3((unsigned)ntile, (unsigned)BH), dim3(256), 0, st, v, s.N,
                      ntile, rv, reinterpret_cast<int8_t*>(qb + L.vt8));
   return hipGetLastError();
 }
@@ -600,6 +830,28 @@ hipError_t attn_i8_dispatch(const Shape& s, const char* qb, const I8Layout& L, c
   else
     hipLaunchKernelGGL((attn_i8_kernel<D, BQ, SUB, 4>), grid, block, 0, st, q8, k8, vt8, sq, sk, sv, rp, ci, o,
                        s.N, s.Nq, s.Nk, lam, l2e, l2_127);
+  return hipGetLastError();
+}
+
+template <int D, int BQ, int SUB>
+hipError_t attn_i8f8_dispatch(const Shape& s, const char* qb, const I8Layout& L, const int32_t* rp,
+                            const int32_t* ci, void* O, hipStream_t st) {
+  const float lam = (float)(1.0 / sqrt((double)D));
+  const float l2e = (float)log2(M_E);
+  const int8_t* q8 = reinterpret_cast<const int8_t*>(qb + L.q8);
+  const int8_t* k8 = reinterpret_cast<const int8_t*>(qb + L.k8);
+  const int8_t* vt8 = reinterpret_cast<const int8_t*>(qb + L.vt8);
+  const float* sq = reinterpret_cast<const float*>(qb + L.sq);
+  const float* sk = reinterpret_cast<const float*>(qb + L.sk);
+  const float* sv = reinterpret_cast<const float*>(qb + L.sv);
+  const dim3 grid((unsigned)s.R()), block(BQ / 32 * 64);
+  char* o = static_cast<char*>(O);
+  if (s.dtype == SLA_BF16)
+    hipLaunchKernelGGL((attn_i8f8_kernel<D, BQ, SUB, 2>), grid, block, 0, st, q8, k8, vt8, sq, sk, sv, rp, ci, o,
+                       s.N, s.Nq, s.Nk, lam, l2e);
+  else
+    hipLaunchKernelGGL((attn_i8f8_kernel<D, BQ, SUB, 4>), grid, block, 0, st, q8, k8, vt8, sq, sk, sv, rp, ci, o,
+                       s.N, s.Nq, s.Nk, lam, l2e);
   return hipGetLastError();
 }
 
@@ -628,12 +880,27 @@ I8Layout i8_layout(const Shape& s) {
   return L;
 }
 
+template <int FQK, int FV>
+hipError_t quant_fmt(const Shape& s, const void* Q, const void* K, const void* V, char* qbuf, const I8Layout& L,
+                     hipStream_t st) {
+  const bool bf = s.dtype == SLA_BF16;
+  if (s.d == 128)
+    return bf ? quant_dispatch<2, 128, FQK, FV>(s, Q, K, V, qbuf, L, st)
+              : quant_dispatch<4, 128, FQK, FV>(s, Q, K, V, qbuf, L, st);
+  if (s.d == 64)
+    return bf ? quant_dispatch<2, 64, FQK, FV>(s, Q, K, V, qbuf, L, st)
+              : quant_dispatch<4, 64, FQK, FV>(s, Q, K, V, qbuf, L, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_quant_i8(const Shape& s, const void* Q, const void* K, const void* V, char* qbuf,
                            const I8Layout& L, hipStream_t st) {
-  const bool bf = s.dtype == SLA_BF16;
-  if (s.d == 128) return bf ? quant_dispatch<2, 128>(s, Q, K, V, qbuf, L, st) : quant_dispatch<4, 128>(s, Q, K, V, qbuf, L, st);
-  if (s.d == 64) return bf ? quant_dispatch<2, 64>(s, Q, K, V, qbuf, L, st) : quant_dispatch<4, 64>(s, Q, K, V, qbuf, L, st);
-  return hipErrorInvalidValue;
+  return quant_fmt<FMT_I8, FMT_I8>(s, Q, K, V, qbuf, L, st);
+}
+
+hipError_t launch_quant_i8f8(const Shape& s, const void* Q, const void* K, const void* V, char* qbuf,
+                             const I8Layout& L, hipStream_t st) {
+  return quant_fmt<FMT_I8, FMT_F8>(s, Q, K, V, qbuf, L, st);
 }
 
 hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* rp,
@@ -649,6 +916,22 @@ hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, c
   SLA_I8(64, 64, 64)
   SLA_I8(64, 64, 128)
 #undef SLA_I8
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_i8f8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* rp,
+                          const int32_t* ci, void* O, hipStream_t st) {
+#define SLA_F8(DD, QQ, KK) \
+  if (s.d == DD && s.bq == QQ && s.bk == KK) return attn_i8f8_dispatch<DD, QQ, KK / 64>(s, qbuf, L, rp, ci, O, st);
+  SLA_F8(128, 128, 64)
+  SLA_F8(128, 128, 128)
+  SLA_F8(128, 64, 64)
+  SLA_F8(128, 64, 128)
+  SLA_F8(64, 128, 64)
+  SLA_F8(64, 128, 128)
+  SLA_F8(64, 64, 64)
+  SLA_F8(64, 64, 128)
+#undef SLA_F8
   return hipErrorInvalidValue;
 }
 

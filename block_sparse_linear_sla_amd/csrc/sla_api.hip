@@ -384,6 +384,32 @@ int sla_sparse_fwd_i8(const sla_problem* prob, const void* qbuf, size_t qbuf_byt
                                         static_cast<hipStream_t>(stream)));
 }
 
+int sla_quantize_i8f8(const sla_problem* prob, const void* Q, const void* K, const void* V, void* qbuf,
+                     size_t qbuf_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.N > 131072) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V) return SLA_ERR_INVALID_ARG;
+  const sla::I8Layout L = sla::i8_layout(s);
+  if (qbuf == nullptr || qbuf_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_quant_i8f8(s, Q, K, V, static_cast<char*>(qbuf), L,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int sla_sparse_fwd_i8f8(const sla_problem* prob, const void* qbuf, size_t qbuf_bytes, const int32_t* row_ptr,
+                       const int32_t* col_idx, void* O_s, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.N > 131072) return SLA_ERR_UNSUPPORTED;
+  if (!row_ptr || !col_idx || !O_s) return SLA_ERR_INVALID_ARG;
+  const sla::I8Layout L = sla::i8_layout(s);
+  if (qbuf == nullptr || qbuf_bytes < L.total) return SLA_ERR_WORKSPACE;
+  return hip_status(sla::launch_attn_i8f8(s, static_cast<const char*>(qbuf), L, row_ptr, col_idx, O_s,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 size_t sla_bwd_workspace_bytes(const sla_problem* prob) {
   Shape s;
   if (check_problem(prob, &s) != SLA_OK) return 0;

@@ -120,6 +120,13 @@ hipError_t launch_quant_i8(const Shape& s, const void* Q, const void* K, const v
                            const I8Layout& L, hipStream_t st);
 hipError_t launch_attn_i8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* row_ptr,
                           const int32_t* col_idx, void* O, hipStream_t st);
+// attn_i8.hip as well: int8 Q, K and E4M3 V codes (same buffer layout, V^T
+// tiles in the key order of a 64-key P operand) and the single-pass sparse
+// branch over them (int8 scores, E4M3 P V).
+hipError_t launch_quant_i8f8(const Shape& s, const void* Q, const void* K, const void* V, char* qbuf,
+                             const I8Layout& L, hipStream_t st);
+hipError_t launch_attn_i8f8(const Shape& s, const char* qbuf, const I8Layout& L, const int32_t* row_ptr,
+                            const int32_t* col_idx, void* O, hipStream_t st);
 
 // attn_bwd.hip: gradient of the sparse branch (bf16) with the mask fixed.
 // alpha (device [H], nullable): the outputs are scaled by alpha_h, the

@@ -257,6 +257,37 @@ int sla_quantize_i8(const sla_problem* prob, const void* Q, const void* K, const
 int sla_sparse_fwd_i8(const sla_problem* prob, const void* qbuf, size_t qbuf_bytes,
                       const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
 
+/* ---- The 8-bit sparse branch in one pass (SLA2 write-up §三): Q and K as the
+ * integer codes above, P and V as 8-bit floating-point values in the E4M3
+ * format of the OCP 8-bit floating-point specification (4 exponent bits with
+ * bias 7, 3 mantissa bits, largest finite value 448), whose headroom lets the
+ * row maximum rise while the row is being summed.  Where that section is
+ * silent:
+ *   - q8, k8, sq, sk exactly as sla_quantize_i8 makes them; V per channel:
+ *     code = E4M3(fl32(x * fl32(448 / amax))) (nearest, ties to even), scale
+ *     sv = fl32(amax / 448);
+ *   - I = q8 . k8 exact, S = fl32(I * c), c = fl32(fl32(sq * sk) * fl32(1 /
+ *     sqrt(d)));
+ *   - the row's keys in 64-key units in CSR order; m = the largest S so far,
+ *     the current unit's included; P codes = E4M3(256 exp(S - m)), taken as
+ *     E4M3(exp2(fma(I, fl32(c log2 e), -(fl32(m log2 e) - 8)))) in float32;
+ *     when m rises, the sums of the earlier units are multiplied by
+ *     exp(m_old - m_new);
+ *   - O_s = sv * (sum code v8) / (sum code), the sums on the E4M3 matrix
+ *     instruction in float32; 0 for an empty row.
+ * The buffer has the layout of sla_i8_layout_of (q8, k8, sq, sk as above; vt8
+ * E4M3 bytes, sv the E4M3 scales, rv 448 / amax), except that in vt8 key k of
+ * a 64-key tile sits at byte 32((k/4)%2) + 16(k/32) + 4((k%32)/8) + k%4 of its
+ * channel row.  Supported as the int8 calls.
+ *
+ * sla_quantize_i8f8: the codes and scales of Q, K, V into qbuf.
+ * sla_sparse_fwd_i8f8: the single-pass sparse branch on them over the CSR
+ * mask; writes O_s [B, H, N, d] in the problem dtype. */
+int sla_quantize_i8f8(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                      void* qbuf, size_t qbuf_bytes, void* stream);
+int sla_sparse_fwd_i8f8(const sla_problem* prob, const void* qbuf, size_t qbuf_bytes,
+                        const int32_t* row_ptr, const int32_t* col_idx, void* O_s, void* stream);
+
 /* ---- Backward of the sparse branch, mask fixed (SLA2 write-up §一 for the
  * branch, §四 for training the attention end to end with the selection fixed
  * per step).  For L = sum(O_s * dO_s), with P the softmax over each row's

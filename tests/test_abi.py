@@ -187,27 +187,31 @@ def test_i8_layout_and_limits():
     assert L.sla_i8_layout_of(ctypes.byref(p), None) == INVALID
     big = prob(N=131073, H=1, d=64, bk=128)
     assert L.sla_i8_layout_of(ctypes.byref(big), ctypes.byref(lay)) == UNSUPPORTED
-    assert L.sla_quantize_i8(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
-    assert L.sla_sparse_fwd_i8(ctypes.byref(big), FAKE, 1 << 40, FAKE, FAKE, FAKE, None) == UNSUPPORTED
-    bad = prob(d=96)
-    assert L.sla_quantize_i8(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+    for fmt in ("i8", "i8f8"):
+        quant, fwd = getattr(L, "sla_quantize_" + fmt), getattr(L, "sla_sparse_fwd_" + fmt)
+        assert quant(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+        assert fwd(ctypes.byref(big), FAKE, 1 << 40, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+        bad = prob(d=96)
+        assert quant(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
 
 
-def test_i8_null_and_buffer_checks():
+@pytest.mark.parametrize("fmt", ["i8", "i8f8"])
+def test_8bit_null_and_buffer_checks(fmt):
     L = S.lib()
+    quant, fwd = getattr(L, "sla_quantize_" + fmt), getattr(L, "sla_sparse_fwd_" + fmt)
     p = prob(dtype=S.SLA_BF16)
     lay = S.I8Layout()
     assert L.sla_i8_layout_of(ctypes.byref(p), ctypes.byref(lay)) == 0
     n = lay.total
     for args in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
-        assert L.sla_quantize_i8(ctypes.byref(p), *args, FAKE, n, None) == INVALID
-    assert L.sla_quantize_i8(ctypes.byref(p), FAKE, FAKE, FAKE, None, n, None) == WORKSPACE
-    assert L.sla_quantize_i8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, n - 1, None) == WORKSPACE
+        assert quant(ctypes.byref(p), *args, FAKE, n, None) == INVALID
+    assert quant(ctypes.byref(p), FAKE, FAKE, FAKE, None, n, None) == WORKSPACE
+    assert quant(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, n - 1, None) == WORKSPACE
     for args in ((None, FAKE, FAKE), (FAKE, None, FAKE), (FAKE, FAKE, None)):
-        assert L.sla_sparse_fwd_i8(ctypes.byref(p), FAKE, n, *args, None) == INVALID
-    assert L.sla_sparse_fwd_i8(ctypes.byref(p), None, n, FAKE, FAKE, FAKE, None) == WORKSPACE
-    assert L.sla_sparse_fwd_i8(ctypes.byref(p), FAKE, n - 1, FAKE, FAKE, FAKE, None) == WORKSPACE
-    assert L.sla_sparse_fwd_i8(None, FAKE, n, FAKE, FAKE, FAKE, None) == INVALID
+        assert fwd(ctypes.byref(p), FAKE, n, *args, None) == INVALID
+    assert fwd(ctypes.byref(p), None, n, FAKE, FAKE, FAKE, None) == WORKSPACE
+    assert fwd(ctypes.byref(p), FAKE, n - 1, FAKE, FAKE, FAKE, None) == WORKSPACE
+    assert fwd(None, FAKE, n, FAKE, FAKE, FAKE, None) == INVALID
 
 
 def test_bwd_checks():

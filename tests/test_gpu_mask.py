@@ -188,7 +188,9 @@ def test_mask_prepared_matches_mask(case):
     sla_mask_prepared then pools only the rest.  The CSR must be sla_mask's,
     entry for entry (the key-block means are float64 sums of bf16 values,
     exact in any order), and sla_attn_fwd, which runs the stages in that
-    order, must give the output of the three separate calls."""
+    order, must give the output of the three separate calls; so must sla_mask
+    (own workspace, on a second stream of the caller's) beside sla_kv_prepare,
+    then sla_fused_fwd."""
     name, dtype, N, d, bq, bk, router, alpha = case
     print(f"[mask-prepared] {name}", flush=True)
     wl = gen.Workload("adhoc", B=2, H=3, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.6,
@@ -211,3 +213,56 @@ def test_mask_prepared_matches_mask(case):
     torch.cuda.synchronize()
     assert torch.equal(rp0, rp2) and torch.equal(ci0[:n], ci2[:n])
     assert torch.equal(o1, o3)
+    # the overlapped schedule spelled out with torch streams
+    ws_m = S.workspace(prob, sel, q.device)
+    rp4, ci4 = torch.full_like(rp1, -1), torch.full_like(ci1, -1)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    fork = torch.cuda.Event()
+    fork.record(main)
+    side.wait_event(fork)
+    with torch.cuda.stream(side):
+        S.sla_mask(q, k, bq, bk, wl.k_frac, wl.p, wq, wk, ws=ws_m, row_ptr=rp4, col_idx=ci4)
+        join = torch.cuda.Event()
+        join.record(side)
+    ws2 = S.workspace(prob, sel, q.device)
+    S.sla_kv_prepare(k, v, bq, bk, ws2, a)
+    main.wait_event(join)
+    o4 = S.sla_fused_fwd(q, k, v, a, bq, bk, rp4, ci4, ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(rp0, rp4) and torch.equal(ci0[:n], ci4[:n])
+    assert torch.equal(o1, o4)
+
+
+def test_forward_calls_in_a_row_on_a_caller_stream():
+    """Back-to-back sla_attn_fwd calls on a (non-default) stream of the
+    caller's, on two inputs in turn with the same workspace and outputs, each
+    give their own result: nothing of one call's work overlaps the next's."""
+    wl = gen.Workload("adhoc", B=1, H=4, grid=(1, 1, 8192), d=128, bq=128, bk=64, k_frac=0.05, p=0.7,
+                      dtype="bf16", alpha_range=(0.5, 0.9), seed=23)
+    print("[attn-fwd] calls in a row on a caller stream", flush=True)
+    xs = [gen.make(wl), gen.make(wl.with_(seed=24))]
+    ins = [U.dev(x.Q, x.K, x.V, x.alpha) for x in xs]
+    ref = []
+    for q, k, v, a in ins:
+        o, rp, ci = S.sla_attn_fwd(q, k, v, a, wl.bq, wl.bk, wl.k_frac, wl.p)
+        torch.cuda.synchronize()
+        ref.append((o.clone(), rp.clone()))
+    assert not torch.equal(ref[0][0], ref[1][0])
+    q0 = ins[0][0]
+    prob, sel = S.problem(q0, wl.bq, wl.bk), S.select(wl.k_frac, wl.p)
+    ws = S.workspace(prob, sel, q0.device)
+    rp = torch.empty_like(ref[0][1])
+    ci = torch.empty(S.sla_mask_capacity(prob), dtype=torch.int32, device=q0.device)
+    out = torch.empty_like(q0)
+    st = torch.cuda.Stream()
+    got = []
+    with torch.cuda.stream(st):
+        for i in range(6):
+            q, k, v, a = ins[i % 2]
+            S.sla_attn_fwd(q, k, v, a, wl.bq, wl.bk, wl.k_frac, wl.p, out=out, ws=ws, row_ptr=rp, col_idx=ci)
+            got.append((out.clone(), rp.clone()))
+    st.synchronize()
+    for i, (o, r) in enumerate(got):
+        assert torch.equal(r, ref[i % 2][1]), f"call {i}: row_ptr"
+        assert torch.equal(o, ref[i % 2][0]), f"call {i}: output"
