@@ -85,22 +85,25 @@ struct PhiPlan {
     const int i = lane & 15, g2 = (lane >> 4) & 1, hi = lane >> 5;
     tro = (4 * hi + (i >> 2)) * 64 + 2 * (16 * g2 + 4 * (i & 3));
   }
-  __device__ __forceinline__ bf16x8 read(const char* reg, int m, int pl) const {
-    const char* b = reg + m * 4096 + pl * 1024 + tro;
+  // key plane pl of row tile m from the region half that holds it
+  __device__ __forceinline__ bf16x8 read(const char* half, int m, int pl) const {
+    const char* b = half + m * 2048 + (pl & 1) * 1024 + tro;
     return cat_tr(b, b + 512);
   }
 };
 // Half HF (key planes 2 HF, 2 HF + 1) of a wavefront's phi(K) region for the
-// unit starting at key key0: MTN x 2 loads.
+// unit starting at key key0: MTN x 2 loads.  The two halves live in distinct
+// LDS arrays, so the compiler can tell a load into one half from the reads
+// of the other (it would otherwise wait for every load in flight).
 template <int MTN, int HF>
 __device__ __forceinline__ void load_phi(__amdgpu_buffer_rsrc_t r, int mt0, int Npad, int key0, int lane,
-                                         char* reg) {
+                                         char* half) {
 #pragma unroll
   for (int m = 0; m < MTN; ++m) {
     const uint32_t soff = (uint32_t)((mt0 + m) * Npad + key0) * 64u;
 #pragma unroll
     for (int j = 2 * HF; j < 2 * HF + 2; ++j)
-      b2lds16(r, (uint32_t)(16 * lane + 1024 * j), soff, reg + m * 4096 + 1024 * j);
+      b2lds16(r, (uint32_t)(16 * lane + 1024 * j), soff, half + m * 2048 + 1024 * (j & 1));
   }
 }
 
@@ -209,7 +212,8 @@ __device__ __forceinline__ void softmax_half(f32x16& sc, bf16x8 (&bp)[2], f32x16
 //   DO_G: G += phi(K)^T V for the wavefront's G tiles (the V^T fragments of
 //         P V as the B operand) and, for the wavefront that keeps them, the
 //         column sums g of its phi(K) row tiles.  The phi(K)^T fragments of
-//         these planes come from the wavefront's private region, one plane
+//         these planes come from Ph, the half of the wavefront's private
+//         region that holds them (PL0, PL1 within one half), one plane
 //         ahead: ready() runs before the first read (it waits for the
 //         region's load), refill() after the last (it hands that part of the
 //         region to the next unit's load).
@@ -219,6 +223,7 @@ __device__ __forceinline__ void pv_g(const char* Vc, const char* Ph, const PhiPl
                                      f32x16 (&acc_g)[GSplit<D, NW>::TPW], float (&gs)[GSplit<D, NW>::MTN],
                                      const ReadPlan<D>& rp, int w, Ready&& ready, Refill&& refill) {
   using GS = GSplit<D, NW>;
+  static_assert(!DO_G || (PL0 % 2 == 0 && PL1 == PL0 + 2), "planes of one region half");
   const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
   bf16x8 vf[D / 32], pf[GS::MTN];
 #pragma unroll
@@ -472,14 +477,15 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
   using GS = GSplit<D, NW>;
   constexpr bool LIN = AS::LIN;
   constexpr int STAGE = 2 * T::KT_BYTES;
-  constexpr int PHB = LIN ? NW * GS::MTN * 4096 : 16;  // private phi(K) regions
-  static_assert(2 * (2 * STAGE + PHB) <= LDS_BYTES, "two workgroups per compute unit");
-  static_assert(!LIN || (D * D * 2 <= STAGE && D * 4 <= PHB), "epilogue areas");
+  constexpr int PHH = LIN ? NW * GS::MTN * 2048 : 16;  // halves of the private phi(K) regions
+  static_assert(2 * (2 * STAGE + 2 * PHH) <= LDS_BYTES, "two workgroups per compute unit");
+  static_assert(!LIN || (D * D * 2 <= STAGE && D * 4 <= PHH), "epilogue areas");
   // Two distinct LDS arrays: the compiler can then tell the loads into one
   // stage from the operand reads of the other.
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
-  __shared__ __attribute__((aligned(16))) char phr[PHB];
+  __shared__ __attribute__((aligned(16))) char phr0[PHH];
+  __shared__ __attribute__((aligned(16))) char phr1[PHH];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -524,7 +530,8 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
   for (int m = 0; m < GS::MTN; ++m) gs[m] = 0.f;
   Softmax sm;
   const float thr8 = 8.f / scale_log2;
-  char* myphi = phr + (LIN ? w * GS::MTN * 4096 : 0);
+  char* myphi0 = phr0 + (LIN ? w * GS::MTN * 2048 : 0);  // key planes 0, 1 of the wavefront's region
+  char* myphi1 = phr1 + (LIN ? w * GS::MTN * 2048 : 0);  // key planes 2, 3
   const auto rk = buf_rsrc(Kb, (uint32_t)((size_t)N * D * 2));
   const auto rv = buf_rsrc(Vb, (uint32_t)((size_t)N * D * 2));
   const auto rph = buf_rsrc(LIN ? pk_g + (size_t)bh * Npad * D : pk_g, (uint32_t)((size_t)Npad * D * 2));
@@ -565,19 +572,19 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
     };
     auto step = [&](int b, char* cur, char* nxt) __attribute__((always_inline)) {
       const int knext = key0(b + 1);
-      wait_kv();        // this wavefront's K | V loads of unit b have landed
-      __syncthreads();  // ... and every wavefront's; unit b-1 consumed
+      wait_kv();      // this wavefront's K | V loads of unit b have landed
+      lds_barrier();  // ... and every wavefront's; unit b-1 consumed; phi(K) loads stay in flight
       issue(knext, nxt);
       const int lim = min(KU, N - kcur);
       const int ln = G_ ? opaque(lane) : lane;
       const PhiPlan pp(ln);
       auto refill0 = [&]() __attribute__((always_inline)) {
         wait_lds();  // planes 0, 1 of the region are in registers
-        load_phi<GS::MTN, 0>(rph, mt0, Npad, knext, ln, myphi);
+        load_phi<GS::MTN, 0>(rph, mt0, Npad, knext, ln, myphi0);
       };
       auto refill1 = [&]() __attribute__((always_inline)) {
         wait_lds();  // planes 2, 3 as well
-        load_phi<GS::MTN, 1>(rph, mt0, Npad, knext, ln, myphi);
+        load_phi<GS::MTN, 1>(rph, mt0, Npad, knext, ln, myphi1);
       };
       const char* Vc = cur + T::KT_BYTES;
       if (S_ && G_) {
@@ -586,28 +593,28 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
         f32x16 s0 = score_half<D, 0, 4>(cur, qf, rdp);
         bf16x8 bp0[2];
         softmax_half<D, 0>(s0, bp0, acc_o, sm, hi, lim, scale_log2, thr8);
-        pv_g<D, NW, true, true, 0, 2>(Vc, myphi, pp, bp0, acc_o, acc_g, gs, rdp, w, wait_phi, refill0);
+        pv_g<D, NW, true, true, 0, 2>(Vc, myphi0, pp, bp0, acc_o, acc_g, gs, rdp, w, wait_phi, refill0);
         f32x16 s1 = score_half<D, 1, 4>(cur, qf, rdp);
         bf16x8 bp1[2];
         softmax_half<D, 1>(s1, bp1, acc_o, sm, hi, lim, scale_log2, thr8);
-        pv_g<D, NW, true, true, 2, 4>(Vc, myphi, pp, bp1, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
+        pv_g<D, NW, true, true, 2, 4>(Vc, myphi1, pp, bp1, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
       } else if (S_) {
         f32x16 sc[2];
         score_unit<D, 4>(cur, qf, rdp, sc);
         bf16x8 bp[4];
         softmax_p<D>(sc, bp, acc_o, sm, hi, lim, scale_log2, thr8);
-        pv_g<D, NW, true, false, 0, 4>(Vc, myphi, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
+        pv_g<D, NW, true, false, 0, 4>(Vc, myphi0, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
       } else if (G_) {
         bf16x8 bp[2];
-        pv_g<D, NW, false, true, 0, 2>(Vc, myphi, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill0);
-        pv_g<D, NW, false, true, 2, 4>(Vc, myphi, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
+        pv_g<D, NW, false, true, 0, 2>(Vc, myphi0, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill0);
+        pv_g<D, NW, false, true, 2, 4>(Vc, myphi1, pp, bp, acc_o, acc_g, gs, rdp, w, wait_phi, refill1);
       }
       kcur = knext;
     };
     issue(kcur, st0);
     if (G_) {
-      load_phi<GS::MTN, 0>(rph, mt0, Npad, kcur, lane, myphi);
-      load_phi<GS::MTN, 1>(rph, mt0, Npad, kcur, lane, myphi);
+      load_phi<GS::MTN, 0>(rph, mt0, Npad, kcur, lane, myphi0);
+      load_phi<GS::MTN, 1>(rph, mt0, Npad, kcur, lane, myphi1);
     }
     int b = 0;
     for (; b + 2 <= nunits; b += 2) {
@@ -637,7 +644,7 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
   uint4 qh[LIN ? NTQ : 1], ql[LIN ? NTQ : 1];
   char* HuHi = st0;
   char* HuLo = st1;
-  float* zu = reinterpret_cast<float*>(phr);
+  float* zu = reinterpret_cast<float*>(phr0);
   if (LIN) {
     const float* Hh = htot + (size_t)bh * (D * D + D);
     // this wavefront's tiles of H (fragment order, as G is held), loaded

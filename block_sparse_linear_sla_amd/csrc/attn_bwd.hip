@@ -19,7 +19,10 @@
 //       then for each key block the query blocks that list it, in ascending
 //       order (one thread per key block and 64-row chunk reads its bit of
 //       each row; column totals are scanned, and a chunk's rows go after
-//       those of the column's earlier chunks: deterministic, no atomics);
+//       those of the column's earlier chunks: deterministic, no atomics).
+//       The scan also orders the column kernels' units by their column's
+//       total, largest first: a key block listed by many query blocks is
+//       the longest workgroup, and started late it would finish alone;
 //   bwd_dq_kernel    one workgroup per mask row (BQ/32 wavefronts, 32
 //       queries each, queries on the lane axis as in the forward).  Pass A
 //       walks the row's 64-key units with S^T = K Q^T and dP^T = V dO^T for
@@ -36,7 +39,10 @@
 //       P and dS in registers, swaps those operands with the wavefront that
 //       shares its keys (through LDS), then accumulates dV^T += dO^T P and
 //       dK^T += Q^T dS over all of the unit's queries with Q and dO read
-//       transposed.
+//       transposed (the reads a few products ahead of their MFMAs).  The
+//       per-query log-sum-exp and D come one value per lane with the unit's
+//       tiles and reach the accumulator elements by row broadcasts, and the
+//       operand swap's barrier leaves the next unit's loads in flight.
 #include "sla.h"
 #include "sla_internal.h"
 #include "bf16_tiles.h"
@@ -84,11 +90,20 @@ __global__ __launch_bounds__(256) void csc_count_kernel(const uint32_t* __restri
 // col_ptr = exclusive prefix sum of the column totals (each the sum of the
 // column's nch cell counts; n columns, one workgroup): 1024 consecutive
 // columns per pass, a shuffle scan within each wavefront, then one across the
-// 16 wavefronts, plus the carry of the earlier passes
+// 16 wavefronts, plus the carry of the earlier passes.
+// Then the launch order of the column kernels' units (sub 64-key units per
+// column): by the column's total in OB classes of rows, largest first, so
+// the longest workgroups start first and the short ones fill in behind them
+// (a column listed by many query blocks would otherwise often start late
+// and finish alone).  Within a class the order is whatever the LDS atomics
+// give: it decides only which workgroup runs which unit, not any result.
+constexpr int OB = 64;
 __global__ __launch_bounds__(1024) void csc_scan_kernel(const int* __restrict__ counts, long long n, int nch,
-                                                        int* __restrict__ col_ptr) {
+                                                        int Nq, int sub, int* __restrict__ col_ptr,
+                                                        int* __restrict__ order) {
   __shared__ int wsum[16];
   __shared__ int carry;
+  __shared__ int cls[OB];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   if (t == 0) carry = 0;
   __syncthreads();
@@ -114,6 +129,27 @@ __global__ __launch_bounds__(1024) void csc_scan_kernel(const int* __restrict__ 
     __syncthreads();
   }
   if (t == 0) col_ptr[n] = carry;
+  if (t < OB) cls[t] = 0;
+  __syncthreads();  // col_ptr complete and visible to the workgroup
+  auto class_of = [&](long long c) { return (OB - 1) - (int)((long long)(col_ptr[c + 1] - col_ptr[c]) * OB / (Nq + 1)); };
+  for (long long c = t; c < n; c += 1024) atomicAdd(&cls[class_of(c)], sub);
+  __syncthreads();
+  if (t < 64) {  // exclusive scan of the OB class sizes (one wavefront)
+    const int v = t < OB ? cls[t] : 0;
+    int incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off);
+      if (t >= off) incl += y;
+    }
+    if (t < OB) cls[t] = incl - v;
+  }
+  __syncthreads();
+  const long long units = n * sub;
+  for (long long u = t; u < units; u += 1024) {
+    const int pos = atomicAdd(&cls[class_of(u / sub)], 1);
+    if (pos < units) order[pos] = (int)u;
+  }
 }
 
 // row_idx[...] = the rows of cell (c, k) that list j, ascending, starting
@@ -303,7 +339,7 @@ template <int D, int BQ, int SUB>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const int* __restrict__ col_ptr, const int* __restrict__ row_idx,
-    const float* __restrict__ lse2, const float* __restrict__ ddv, uint16_t* __restrict__ dK,
+    const int* __restrict__ order, const float* __restrict__ lse2, const float* __restrict__ ddv, uint16_t* __restrict__ dK,
     uint16_t* __restrict__ dV, const float* __restrict__ alpha, int H, int N, int Nq, int Nk, float scale_log2,
     float inv_sqrt_d) {
   using T = Tiles<D>;
@@ -325,7 +361,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
   const int kh = w & 1, dh = w >> 1;
   const int partner = w ^ 2;
   const ReadPlan<D> rdp(lane);
-  const long long unit = xcd_row(blockIdx.x, (long long)gridDim.x);  // (bh, key block, 64-key part)
+  // (bh, key block, 64-key part), most-listed key blocks first
+  const long long unit = order[blockIdx.x];
+  if (unit < 0 || unit >= (long long)gridDim.x) return;
   const long long bh = unit / ((long long)Nk * SUB);
   const int ku = (int)(unit % ((long long)Nk * SUB));
   const int j = ku / SUB;
@@ -358,35 +396,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
     // S and dP of this wavefront's 32 queries (half QH of the unit) x its 32
     // keys (element i: query 32 QH + 8 (i/4) + 4 hi + i%4, key = this
     // lane's); P and dS packed as the B operands of query planes 2 QH, 2 QH + 1
-    auto score = [&](const char* cur, size_t r0, bf16x8 (&bp)[2], bf16x8 (&bs)[2], auto qh_tag)
+    auto score = [&](const char* cur, float Lc, float Dc, bf16x8 (&bp)[2], bf16x8 (&bs)[2], auto qh_tag)
         __attribute__((always_inline)) {
       constexpr int QH = decltype(qh_tag)::value;
       const f32x16 s = score_half<D, QH, 4>(cur, kf, rdp);
       const f32x16 dp = score_half<D, QH, 4>(cur + T::KT_BYTES, vf, rdp);
       float pv[16], ds[16];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const size_t ro = r0 + 32 * QH + 8 * a + 4 * hi;
-        const float4 L4 = *reinterpret_cast<const float4*>(lse2 + ro);
-        const float4 D4 = *reinterpret_cast<const float4*>(ddv + ro);
-        const float Lq[4] = {L4.x, L4.y, L4.z, L4.w}, Dq[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int i = 4 * a + c;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -Lq[c]));
-          pv[i] = p;
-          ds[i] = p * (dp[i] - Dq[c]);
-        }
-      }
+      static_for<16>([&](auto it) __attribute__((always_inline)) {
+        constexpr int i = decltype(it)::value;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -row_bcast<i>(Lc)));
+        pv[i] = p;
+        ds[i] = p * (dp[i] - row_bcast<i>(Dc));
+      });
       pack_planes(pv, bp);
       pack_planes(ds, bs);
     };
+    // the unit's per-query terms (log2-sum-exp and D), one value per lane
+    // (term_query) of this wavefront's 32 queries, loaded with the unit's
+    // tiles so that the only wait for them is the one for the tiles
+    const int tq = 32 * dh + term_query(lane);
+    auto terms_at = [&](int x) { return ((size_t)(bh * Nq + qrow_of(x))) * BQ + (x % QU) * KU + tq; };
+    float Ln = lse2[terms_at(0)], Dn = ddv[terms_at(0)];
     auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
-      const int qb = qrow_of(x);
-      const size_t r0 = ((size_t)(bh * Nq + qb)) * BQ + (x % QU) * KU;  // per-query terms of the unit
       wait_vm<0>();
       __syncthreads();  // the unit's tiles landed; the previous unit's exchange consumed
-      if (x + 1 < nunits) issue(x + 1, nxt);
+      const float Lc = Ln, Dc = Dn;
+      if (x + 1 < nunits) {
+        const size_t tn = terms_at(x + 1);
+        Ln = lse2[tn];
+        Dn = ddv[tn];
+        issue(x + 1, nxt);
+      }
       // all operand indices below are compile-time (a runtime index would put
       // the operand array in scratch memory)
       auto body = [&](auto qh_tag) __attribute__((always_inline)) {
@@ -394,7 +434,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         constexpr int OWN = 2 * QH, OTH = 2 - OWN;
         bf16x8 op[2][4];  // [P, dS][query plane 0..3]
         bf16x8 bp[2], bs[2];
-        score(cur, r0, bp, bs, qh_tag);
+        score(cur, Lc, Dc, bp, bs, qh_tag);
         op[0][OWN] = bp[0];
         op[0][OWN + 1] = bp[1];
         op[1][OWN] = bs[0];
@@ -404,7 +444,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
         for (int o = 0; o < 2; ++o)
 #pragma unroll
           for (int pl = 0; pl < 2; ++pl) xch[w][2 * o + pl][lane] = __builtin_bit_cast(uint4, op[o][OWN + pl]);
-        __syncthreads();
+        lds_barrier();  // the next unit's tiles stay in flight
 #pragma unroll
         for (int o = 0; o < 2; ++o)
 #pragma unroll
@@ -412,13 +452,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(
             op[o][OTH + pl] = __builtin_bit_cast(bf16x8, xch[partner][2 * o + pl][lane]);
         // dV^T += dO^T P and dK^T += Q^T dS over the unit's four query
         // planes, d rows of this wavefront's half
-#pragma unroll
-        for (int pl = 0; pl < 4; ++pl)
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) {
-            adv[t] = mfma(rdp.vt(cur + T::KT_BYTES, NDT * QH + t, pl), op[0][pl], adv[t]);
-            adk[t] = mfma(rdp.vt(cur, NDT * QH + t, pl), op[1][pl], adk[t]);
-          }
+        col_products<D, NDT, QH, OWN, BWD_PF, 4>(cur + T::KT_BYTES, cur, rdp, op, adv, adk);
       };
       if (dh == 0) body(IntTag<0>{});
       else body(IntTag<1>{});
@@ -498,6 +532,7 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   const float isd = 1.f / sqrtf((float)D);
   const int* col_ptr = reinterpret_cast<const int*>(ws + L.col_ptr);
   const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
+  const int* order = reinterpret_cast<const int*>(ws + L.order);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* ddv = reinterpret_cast<float*>(ws + L.dd);
   if (csc) {
@@ -511,7 +546,7 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, q, k, v,
                      g, rp, ci, static_cast<uint16_t*>(dQ), lse2, ddv, alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, q, k, v,
-                     g, col_ptr, row_idx, lse2, ddv, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
+                     g, col_ptr, row_idx, order, lse2, ddv, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
                      alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd);
   return hipGetLastError();
 }
@@ -532,7 +567,9 @@ hipError_t launch_csc(const Shape& s, const int32_t* rp, const int32_t* ci, char
   hipLaunchKernelGGL(csc_bits_kernel, dim3((unsigned)((s.R() + 255) / 256)), dim3(256), 0, st, rp, ci, s.R(), words,
                      bits);
   hipLaunchKernelGGL(csc_count_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts);
-  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, nch, col_ptr);
+  int* order = reinterpret_cast<int*>(ws + L.order);
+  hipLaunchKernelGGL(csc_scan_kernel, dim3(1), dim3(1024), 0, st, counts, BH * s.Nk, nch, s.Nq, s.bk / KU, col_ptr,
+                     order);
   hipLaunchKernelGGL(csc_fill_kernel, dim3(gcell), dim3(256), 0, st, bits, s.Nq, s.Nk, words, nch, BH, counts,
                      col_ptr, row_idx);
   return hipGetLastError();
@@ -552,6 +589,7 @@ BwdLayout bwd_layout(const Shape& s) {
   L.counts = take(ncell * sizeof(int));
   L.col_ptr = take((BH * s.Nk + 1) * sizeof(int));
   L.row_idx = take(BH * (size_t)s.Nq * s.Nk * sizeof(int));
+  L.order = take(BH * s.Nk * (size_t)(s.bk / 64) * sizeof(int));
   L.lse2 = take((size_t)s.R() * s.bq * sizeof(float));
   L.dd = take((size_t)s.R() * s.bq * sizeof(float));
   L.achunks = (int)(((long long)s.N * s.d + ACH - 1) / ACH);

@@ -410,7 +410,8 @@ template <int D, int BQ, int SUB>
 __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ F, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Kraw, const int* __restrict__ col_ptr,
-    const int* __restrict__ row_idx, const float* __restrict__ invden, const float* __restrict__ dtq,
+    const int* __restrict__ row_idx, const int* __restrict__ order, const float* __restrict__ invden,
+    const float* __restrict__ dtq,
     const uint4* __restrict__ fragMT, const uint4* __restrict__ fragM, const float* __restrict__ tot_m,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int add, const float* __restrict__ alpha, int H, int N,
     int Nq, int Nk) {
@@ -429,7 +430,9 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
   const int kh = w & 1, dh = w >> 1;
   const int partner = w ^ 2;
   const ReadPlan<D> rdp(lane);
-  const long long unit = xcd_row(blockIdx.x, (long long)gridDim.x);
+  // (bh, key block, 64-key part), most-listed key blocks first
+  const long long unit = order[blockIdx.x];
+  if (unit < 0 || unit >= (long long)gridDim.x) return;
   const long long bh = unit / ((long long)Nk * SUB);
   const int ku = (int)(unit % ((long long)Nk * SUB));
   const int j = ku / SUB;
@@ -458,12 +461,22 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
       lp.load(ra, q0, sb);
       lp.load(rg, q0, sb + T::KT_BYTES);
     };
+    // the unit's per-query terms (1 / den and D~), one value per lane
+    // (term_query) of this wavefront's 32 queries, loaded with the unit's
+    // tiles so that the only wait for them is the one for the tiles
+    const int tq = 32 * dh + term_query(lane);
+    auto terms_at = [&](int x) { return ((size_t)(bh * Nq + qrow_of(x))) * BQ + (x % QU) * KU + tq; };
+    float In = invden[terms_at(0)], Dn = dtq[terms_at(0)];
     auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
-      const int qb = qrow_of(x);
-      const size_t r0 = ((size_t)(bh * Nq + qb)) * BQ + (x % QU) * KU;
       wait_vm<0>();
       __syncthreads();
-      if (x + 1 < nunits) issue(x + 1, nxt);
+      const float Ic = In, Dc = Dn;
+      if (x + 1 < nunits) {
+        const size_t tn = terms_at(x + 1);
+        In = invden[tn];
+        Dn = dtq[tn];
+        issue(x + 1, nxt);
+      }
       auto body = [&](auto qh_tag) __attribute__((always_inline)) {
         constexpr int QH = decltype(qh_tag)::value;
         constexpr int OWN = 2 * QH, OTH = 2 - OWN;
@@ -472,19 +485,12 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
         const f32x16 s = score_half<D, QH, 4>(cur, ff, rdp);
         const f32x16 dp = score_half<D, QH, 4>(cur + T::KT_BYTES, vf, rdp);
         float pv[16], ds[16];
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const size_t ro = r0 + 32 * QH + 8 * a + 4 * hi;
-          const float4 I4 = *reinterpret_cast<const float4*>(invden + ro);
-          const float4 D4 = *reinterpret_cast<const float4*>(dtq + ro);
-          const float Iq[4] = {I4.x, I4.y, I4.z, I4.w}, Dq[4] = {D4.x, D4.y, D4.z, D4.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int i = 4 * a + c;
-            pv[i] = s[i] * Iq[c];
-            ds[i] = (dp[i] - Dq[c]) * Iq[c];
-          }
-        }
+        static_for<16>([&](auto it) __attribute__((always_inline)) {
+          constexpr int i = decltype(it)::value;
+          const float iq = row_bcast<i>(Ic);
+          pv[i] = s[i] * iq;
+          ds[i] = (dp[i] - row_bcast<i>(Dc)) * iq;
+        });
         bf16x8 op[2][4];
         bf16x8 bp[2], bs[2];
         pack_planes(pv, bp);
@@ -497,19 +503,14 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
         for (int o = 0; o < 2; ++o)
 #pragma unroll
           for (int pl = 0; pl < 2; ++pl) xch[w][2 * o + pl][lane] = __builtin_bit_cast(uint4, op[o][OWN + pl]);
-        __syncthreads();
+        lds_barrier();  // the next unit's tiles stay in flight
 #pragma unroll
         for (int o = 0; o < 2; ++o)
 #pragma unroll
           for (int pl = 0; pl < 2; ++pl)
             op[o][OTH + pl] = __builtin_bit_cast(bf16x8, xch[partner][2 * o + pl][lane]);
-#pragma unroll
-        for (int pl = 0; pl < 4; ++pl)
-#pragma unroll
-          for (int t = 0; t < NDT; ++t) {
-            adv[t] = mfma(rdp.vt(cur + T::KT_BYTES, NDT * QH + t, pl), op[0][pl], adv[t]);
-            adk[t] = mfma(rdp.vt(cur, NDT * QH + t, pl), op[1][pl], adk[t]);
-          }
+        // dV^T += h^T P~ and dphi^T += phi(Q)^T dw, d rows of this wavefront's half
+        col_products<D, NDT, QH, OWN, BWD_PF, 4>(cur + T::KT_BYTES, cur, rdp, op, adv, adk);
       };
       if (dh == 0) body(IntTag<0>{});
       else body(IntTag<1>{});
@@ -609,8 +610,9 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   // keys: dk, dv
   const int* col_ptr = reinterpret_cast<const int*>(ws + L.col_ptr);
   const int* row_idx = reinterpret_cast<const int*>(ws + L.row_idx);
+  const int* order = reinterpret_cast<const int*>(ws + L.order);
   hipLaunchKernelGGL((lin_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, A, F, V, G,
-                     K, col_ptr, row_idx, invden, dtq, frag0, frag1, tot_m, static_cast<uint16_t*>(dK),
+                     K, col_ptr, row_idx, order, invden, dtq, frag0, frag1, tot_m, static_cast<uint16_t*>(dK),
                      static_cast<uint16_t*>(dV), add ? 1 : 0, alpha, s.H, s.N, s.Nq, s.Nk);
   return hipGetLastError();
 }

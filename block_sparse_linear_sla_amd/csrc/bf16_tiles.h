@@ -7,6 +7,8 @@
 // lane l is row 8*(i/4) + 4*(l/32) + i%4, column l%32.
 #pragma once
 
+#include <utility>
+
 #include "sla_internal.h"
 
 namespace sla {
@@ -23,6 +25,32 @@ template <int I>
 struct IntTag {
   static constexpr int value = I;
 };
+
+// f(IntTag<0>{}), ..., f(IntTag<N - 1>{}) in order (compile-time indices)
+template <class F, int... I>
+__device__ __forceinline__ void for_each_tag(F&& f, std::integer_sequence<int, I...>) {
+  (f(IntTag<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  for_each_tag(f, std::make_integer_sequence<int, N>{});
+}
+
+// Lane N of v's 16-lane row, in every lane of that row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  static_assert(N >= 0 && N < 16, "row lane");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + N, 0xf, 0xf,
+                                                               false));
+}
+
+// Per-query values of a 32-query accumulator tile, one value per lane: the
+// lane that holds query term_query(l) of the tile.  Accumulator element i of
+// lane l belongs to query 8 (i/4) + 4 (l/32) + i%4, and lanes 16 r .. 16 r + 15
+// share l/32, so element i takes lane i of its row (row_bcast<i>).
+__device__ __forceinline__ int term_query(int lane) {
+  return 8 * ((lane & 15) >> 2) + (lane & 3) + 4 * (lane >> 5);
+}
 
 __device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -160,6 +188,15 @@ __device__ __forceinline__ void wait_vm() {
 // s_waitcnt lgkmcnt(0) only: every LDS read of this wavefront has returned.
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
 
+// Workgroup barrier that orders LDS accesses only: each wavefront's LDS
+// reads and writes have completed when it arrives (lgkmcnt 0), while its
+// vector-memory loads in flight - direct loads of a later unit's tiles into
+// another LDS buffer - stay in flight.  (__syncthreads, and a workgroup fence
+// even when limited to LDS, also waits for those loads, since they write
+// LDS.)  The memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Buffer resource over [base, base + bytes) for raw (unstructured) buffer
 // loads; reads past the end return zeros.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
@@ -265,6 +302,52 @@ __device__ __forceinline__ f32x16 score_half(const char* Ks, const bf16x8 (&qf)[
   }
   __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
   return s;
+}
+
+#ifndef SLA_BWD_PF
+#define SLA_BWD_PF 4
+#endif
+constexpr int BWD_PF = SLA_BWD_PF;  // transposed reads in flight ahead of the column products
+
+// Column-side products of a 64-query unit for one wavefront: acc0[t] +=
+// T0^T op[0][pl] and acc1[t] += T1^T op[1][pl] over the four query planes pl,
+// with T0, T1 row-major 64-row tiles (dO and Q, or h and phi(Q)) read
+// transposed at d tile NDT DT + t.  Planes OWN, OWN + 1 come first (their
+// operands are this wavefront's own), then the other two (from another
+// wavefront through LDS).  Each transposed read is issued PF products ahead
+// of its MFMA, so LDS latency stays behind the matrix ops already issued.
+// XR: LDS reads just before (the other wavefront's operands), which the
+// scheduling groups below have to count.
+template <int D, int NDT, int DT, int OWN, int PF, int XR>
+__device__ __forceinline__ void col_products(const char* T0, const char* T1, const ReadPlan<D>& rp,
+                                             const bf16x8 (&op)[2][4], f32x16 (&acc0)[NDT],
+                                             f32x16 (&acc1)[NDT]) {
+  constexpr int NI = 4 * NDT * 2;  // products
+  static_assert(PF >= 1 && PF < NI, "prefetch depth");
+  auto plane = [](int i) { const int j = i / (2 * NDT); return j < 2 ? OWN + j : (OWN + j) & 3; };
+  auto rd = [&](auto it) __attribute__((always_inline)) {
+    constexpr int i = decltype(it)::value;
+    constexpr int pl = plane(i), t = (i / 2) % NDT;
+    return rp.vt(i % 2 == 0 ? T0 : T1, NDT * DT + t, pl);
+  };
+  bf16x8 fr[PF];
+  static_for<PF>([&](auto it) __attribute__((always_inline)) { fr[decltype(it)::value] = rd(it); });
+  static_for<NI>([&](auto it) __attribute__((always_inline)) {
+    constexpr int i = decltype(it)::value;
+    constexpr int pl = plane(i), t = (i / 2) % NDT;
+    const bf16x8 a = fr[i % PF];
+    if constexpr (i + PF < NI) fr[i % PF] = rd(IntTag<i + PF>{});
+    if constexpr (i % 2 == 0) acc0[t] = mfma(a, op[0][pl], acc0[t]);
+    else acc1[t] = mfma(a, op[1][pl], acc1[t]);
+  });
+  // keep that order (two transposed reads per operand)
+  __builtin_amdgcn_sched_group_barrier(0x100, XR + 2 * PF, 0);
+#pragma unroll
+  for (int i = 0; i + PF < NI; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
 }
 
 // Q fragments of 32 query rows (B operand of S^T = K Q^T), zero past N.

@@ -60,6 +60,7 @@ struct BwdLayout {
   size_t counts;   // int32 [B*H*Nk*ceil(Nq/64)]: rows listing each key block, per 64-row chunk
   size_t col_ptr;  // int32 [B*H*Nk + 1]: the mask's transpose (CSC)
   size_t row_idx;  // int32 [B*H*Nq*Nk]: query block indices, ascending per column
+  size_t order;    // int32 [B*H*Nk*(bk/64)]: the column kernels' 64-key units, most-listed key blocks first
   size_t lse2;     // float [R*bq]: log2-sum-exp of the scaled scores per query (+inf past N)
   size_t dd;       // float [R*bq]: D = dO . O per query (0 past N)
   size_t apart;    // double [B*H][achunks]: partial sums of the alpha gradient

@@ -300,7 +300,9 @@ int sla_sparse_fwd_i8f8(const sla_problem* prob, const void* qbuf, size_t qbuf_b
  * dV [B, H, N, d] bf16
  * (every element written; rows of keys no row lists get 0).  Needs a
  * workspace of sla_bwd_workspace_bytes (the mask's transpose, per-query
- * terms).  Deterministic: no atomics. */
+ * terms, the column kernels' launch order).  Deterministic: every sum runs
+ * in a fixed order (integer atomics in LDS pick which workgroup runs which
+ * key block first, which no result depends on). */
 size_t sla_bwd_workspace_bytes(const sla_problem* prob);
 int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_s, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK,
                    void* dV, void* ws, size_t ws_bytes, void* stream);
@@ -322,7 +324,7 @@ int sla_sparse_bwd(const sla_problem* prob, const void* Q, const void* K, const 
  * bf16, every element written; with accumulate != 0 the results are added to
  * what the buffers hold (for example the sparse branch's gradient) and
  * rounded to bf16 once more.  Needs the sla_bwd_workspace_bytes workspace
- * (its contents on entry are ignored).  Deterministic: no atomics. */
+ * (its contents on entry are ignored).  Deterministic, as sla_sparse_bwd. */
 int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO_l,
                    const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
                    int accumulate, void* ws, size_t ws_bytes, void* stream);
@@ -339,7 +341,7 @@ int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const 
  * bf16, every element written (the sparse part rounded to bf16, the linear
  * part added and rounded again).  Needs the sla_bwd_workspace_bytes
  * workspace.  The gradient with respect to alpha is sla_alpha_grad's.
- * Deterministic: no atomics. */
+ * Deterministic, as sla_sparse_bwd. */
 int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
                  const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
                  void* ws, size_t ws_bytes, void* stream);
