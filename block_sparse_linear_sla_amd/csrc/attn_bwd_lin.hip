@@ -51,18 +51,19 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&x)[8]) {
   for (int e = 0; e < 8; ++e) x[e] = bf2f(elem(v, e));
 }
 
-// 4 consecutive bf16 at p: write (or add to what is there) the 4 values
-__device__ __forceinline__ void put4(uint16_t* p, const float (&v)[4], bool add) {
-  float o[4] = {v[0], v[1], v[2], v[3]};
-  if (add) {
-    const uint2 old = *reinterpret_cast<const uint2*>(p);
-    o[0] += bf2f(old.x & 0xffffu);
-    o[1] += bf2f(old.x >> 16);
-    o[2] += bf2f(old.y & 0xffffu);
-    o[3] += bf2f(old.y >> 16);
-  }
-  *reinterpret_cast<uint2*>(p) = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
+// v += the 4 bf16 values packed in old
+__device__ __forceinline__ void add4(const uint2& old, float (&v)[4]) {
+  v[0] += bf2f(old.x & 0xffffu);
+  v[1] += bf2f(old.x >> 16);
+  v[2] += bf2f(old.y & 0xffffu);
+  v[3] += bf2f(old.y >> 16);
 }
+
+// the 4 values as 4 consecutive bf16 at p
+__device__ __forceinline__ void store4(uint16_t* p, const float (&v)[4]) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]));
+}
+
 
 // ------------------------------------------------------------------ phi rows
 __global__ __launch_bounds__(256) void lin_phi_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -272,19 +273,44 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   // acc^T starts as U^T = (H h)^T for this wavefront's queries (H as hi + lo
   // fragments; element i of tile dt: d = 32 dt + 8 (i/4) + 4 hi + i%4) and
   // ends as U - sum_sel (h . v - D~) phi(k)
+  // The fragments (a contiguous per-head block, fragment f at 1024 f) come
+  // into the stages once per workgroup by direct loads, a share per
+  // wavefront, and every wavefront reads all of them there, each PF MFMAs
+  // ahead.
   f32x16 acc[NDT];
   {
-    const uint4* fh = fragH + (size_t)bh * (2 * NDT * NKK * 64) + lane;
+    constexpr int NF = 2 * NDT * NKK, FPS = STAGE / 1024, PF = 4;
+    static_assert(NF <= 2 * FPS && NF % NW == 0, "the fragments fit the stages");
+    auto frag_at = [&](int f) -> const char* { return f < FPS ? st0 + 1024 * f : st1 + 1024 * (f - FPS); };
+    const auto r = buf_rsrc(fragH + (size_t)bh * NF * 64, (uint32_t)(NF * 1024));
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      acc[dt] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int f = 2 * (dt * NKK + kk) * 64;
-        acc[dt] = mfma(as_bf16x8(fh[f]), hf[kk], acc[dt]);
-        acc[dt] = mfma(as_bf16x8(fh[f + 64]), hf[kk], acc[dt]);
-      }
+    for (int i = 0; i < NF / NW; ++i) {
+      const int f = (NF / NW) * w + i;
+      b2lds16(r, (uint32_t)(16 * lane + 1024 * f), 0u, (char*)frag_at(f));
     }
+    wait_vm<0>();
+    __syncthreads();
+    uint4 fr[PF];
+    static_for<PF>([&](auto it) __attribute__((always_inline)) {
+      fr[decltype(it)::value] = rd16(frag_at(decltype(it)::value) + 16 * lane);
+    });
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x16{};
+    // fragment i: tile i / (2 NKK), k-step (i / 2) % NKK, hi then lo
+    static_for<NF>([&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      const uint4 a = fr[i % PF];
+      if constexpr (i + PF < NF) fr[i % PF] = rd16(frag_at(i + PF) + 16 * lane);
+      acc[i / (2 * NKK)] = mfma(as_bf16x8(a), hf[(i / 2) % NKK], acc[i / (2 * NKK)]);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i + PF < NF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+    __syncthreads();  // every wavefront has read the fragments; the stages are free
   }
   float sw = 0.f, swh = 0.f;  // this lane's sums of w and w (h . v) over its listed keys
   float inv = 0.f, dtv = 0.f;  // 1 / den and D~ (0 for a row without a linear branch)
@@ -390,19 +416,30 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   const float os = alpha != nullptr ? 1.f - alpha[bh % H] : 1.f;
   const float sinv = os * inv;
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int dt = 0; dt < NDT; ++dt) {
+    // the tile's loads together, so their latencies overlap
+    float4 z4[4];
+    uint2 q2[4], old[4];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       const int d0 = 32 * dt + 8 * a + 4 * hi;
-      const float4 z4 = *reinterpret_cast<const float4*>(z + d0);
-      const uint2 q2 = *reinterpret_cast<const uint2*>(Qraw + qrow + d0);
-      const float zz[4] = {z4.x, z4.y, z4.z, z4.w};
-      const float qq[4] = {bf2f(q2.x & 0xffffu), bf2f(q2.x >> 16), bf2f(q2.y & 0xffffu), bf2f(q2.y >> 16)};
+      z4[a] = *reinterpret_cast<const float4*>(z + d0);
+      q2[a] = *reinterpret_cast<const uint2*>(Qraw + qrow + d0);
+      if (add) old[a] = *reinterpret_cast<const uint2*>(dQ + qrow + d0);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * dt + 8 * a + 4 * hi;
+      const float zz[4] = {z4[a].x, z4[a].y, z4[a].z, z4[a].w};
+      const float qq[4] = {bf2f(q2[a].x & 0xffffu), bf2f(q2[a].x >> 16), bf2f(q2[a].y & 0xffffu),
+                           bf2f(q2[a].y >> 16)};
       float o[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[c] = dphi(qq[c]) * ((acc[dt][4 * a + c] - dtv * zz[c]) * sinv);
-      put4(dQ + qrow + d0, o, add != 0);
+      if (add) add4(old[a], o);
+      store4(dQ + qrow + d0, o);
     }
+  }
 }
 
 // ------------------------------------------------------------------ dk, dv
@@ -527,40 +564,101 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
   // dv = M^T phi(k) - acc_v and dphi = M v - m - acc_k, the products with M
   // on the matrix cores (M^T and M as hi + lo fragments, phi(k) and v from
   // this lane's key fragments); dk = phi'(k) o dphi.  Element i of tile t:
-  // d = 32 (NDT dh + t) + 8 (i/4) + 4 hi + i%4
+  // d = 32 (NDT dh + t) + 8 (i/4) + 4 hi + i%4.  Each fragment set (a
+  // contiguous per-head block, fragment f at 1024 f) comes into the free
+  // stages once per workgroup by direct loads, a quarter per wavefront, and
+  // is read from there by the two wavefronts that use each fragment.
   constexpr int NKK = D / 16;
-  const size_t fb = (size_t)bh * (2 * (D / 32) * NKK * 64) + lane;
+  constexpr int NF = 2 * (D / 32) * NKK;  // fragments per set
+  constexpr int FPS = STAGE / 1024;       // fragments per stage array
+  static_assert(NF <= 2 * FPS && NF % 4 == 0, "a fragment set fits the stages");
   const float* mv = tot_m + (size_t)bh * ((size_t)D * D + D) + (size_t)D * D;
   const size_t krow = ((size_t)bh * N + (kv ? key : 0)) * D;
   const float os = alpha != nullptr ? 1.f - alpha[bh % H] : 1.f;
+  auto frag_at = [&](int f) -> const char* { return (f < FPS ? st0 + 1024 * f : st1 + 1024 * (f - FPS)) + 16 * lane; };
+  auto stage_set = [&](const uint4* set) __attribute__((always_inline)) {
+    const auto r = buf_rsrc(set + (size_t)bh * NF * 64, (uint32_t)(NF * 1024));
+#pragma unroll
+    for (int i = 0; i < NF / 4; ++i) {
+      const int f = (NF / 4) * w + i;
+      b2lds16(r, (uint32_t)(16 * lane + 1024 * f), 0u, (char*)frag_at(f) - 16 * lane);
+    }
+  };
+  // y[t] = sum over k-steps of (hi + lo fragment of tile NDT dh + t) x x[kk],
+  // each fragment read PF products ahead of its MFMA
+  auto products = [&](const bf16x8 (&x)[NKK], f32x16 (&y)[NDT]) __attribute__((always_inline)) {
+    constexpr int NI = NDT * 2 * NKK, PF = 4;
+    const int f0 = 2 * NDT * dh * NKK;  // first fragment of this wavefront's tiles
+    uint4 fr[PF];
+    static_for<PF>([&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;
+      fr[i] = rd16(frag_at(f0 + i));
+    });
+#pragma unroll
+    for (int t = 0; t < NDT; ++t) y[t] = f32x16{};
+    static_for<NI>([&](auto it) __attribute__((always_inline)) {
+      constexpr int i = decltype(it)::value;  // fragment f0 + i: tile i / (2 NKK), k-step (i / 2) % NKK
+      const uint4 a = fr[i % PF];
+      if constexpr (i + PF < NI) fr[i % PF] = rd16(frag_at(f0 + i + PF));
+      y[i / (2 * NKK)] = mfma(as_bf16x8(a), x[(i / 2) % NKK], y[i / (2 * NKK)]);
+    });
+    __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+    for (int i = 0; i + PF < NI; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+  };
+  // the tile's elementwise terms: m, the raw k and, when adding, what dV and dK hold
+  float4 m4[NDT][4];
+  uint2 k2[NDT][4], pv2[NDT][4], pk2[NDT][4];
+  auto load_terms = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int d0 = 32 * (NDT * dh + t) + 8 * a + 4 * hi;
+      m4[t][a] = *reinterpret_cast<const float4*>(mv + d0);
+      k2[t][a] = *reinterpret_cast<const uint2*>(Kraw + krow + d0);
+      if (add) {
+        pv2[t][a] = *reinterpret_cast<const uint2*>(dV + krow + d0);
+        pk2[t][a] = *reinterpret_cast<const uint2*>(dK + krow + d0);
+      }
+    }
+  };
+  f32x16 yv[NDT], yk[NDT];
+  __syncthreads();  // every wavefront is done with the stages
+  stage_set(fragMT);
+  wait_vm<0>();
+  __syncthreads();
+  products(ff, yv);
+  __syncthreads();  // M^T read by every wavefront
+  load_terms(0);
+  stage_set(fragM);
+  wait_vm<0>();
+  __syncthreads();
+  products(vf, yk);
 #pragma unroll
   for (int t = 0; t < NDT; ++t) {
-    const int dt = NDT * dh + t;
-    f32x16 yv = f32x16{}, yk = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const size_t f = fb + (size_t)(2 * (dt * NKK + kk)) * 64;
-      yv = mfma(as_bf16x8(fragMT[f]), ff[kk], yv);
-      yv = mfma(as_bf16x8(fragMT[f + 64]), ff[kk], yv);
-      yk = mfma(as_bf16x8(fragM[f]), vf[kk], yk);
-      yk = mfma(as_bf16x8(fragM[f + 64]), vf[kk], yk);
-    }
+    if (t + 1 < NDT) load_terms(t + 1);
     if (!kv) continue;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      const int d0 = 32 * dt + 8 * a + 4 * hi;
-      const float4 m4 = *reinterpret_cast<const float4*>(mv + d0);
-      const uint2 k2 = *reinterpret_cast<const uint2*>(Kraw + krow + d0);
-      const float MM[4] = {m4.x, m4.y, m4.z, m4.w};
-      const float kk4[4] = {bf2f(k2.x & 0xffffu), bf2f(k2.x >> 16), bf2f(k2.y & 0xffffu), bf2f(k2.y >> 16)};
+      const int d0 = 32 * (NDT * dh + t) + 8 * a + 4 * hi;
+      const float MM[4] = {m4[t][a].x, m4[t][a].y, m4[t][a].z, m4[t][a].w};
+      const float kk4[4] = {bf2f(k2[t][a].x & 0xffffu), bf2f(k2[t][a].x >> 16), bf2f(k2[t][a].y & 0xffffu),
+                            bf2f(k2[t][a].y >> 16)};
       float ov[4], ok[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        ov[c] = os * (yv[4 * a + c] - adv[t][4 * a + c]);
-        ok[c] = os * dphi(kk4[c]) * (yk[4 * a + c] - MM[c] - adk[t][4 * a + c]);
+        ov[c] = os * (yv[t][4 * a + c] - adv[t][4 * a + c]);
+        ok[c] = os * dphi(kk4[c]) * (yk[t][4 * a + c] - MM[c] - adk[t][4 * a + c]);
       }
-      put4(dV + krow + d0, ov, add != 0);
-      put4(dK + krow + d0, ok, add != 0);
+      if (add) {
+        add4(pv2[t][a], ov);
+        add4(pk2[t][a], ok);
+      }
+      store4(dV + krow + d0, ov);
+      store4(dK + krow + d0, ok);
     }
   }
 }
