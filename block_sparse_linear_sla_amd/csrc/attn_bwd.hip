@@ -233,8 +233,6 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
   float dd = 0.f;  // D of this query (after pass A)
 
   f32x16 acc[D / 32];
-#pragma unroll
-  for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
   float lse2 = INFINITY;  // log2-sum-exp of the scaled scores; +inf: no key (P = 0)
   if (nunits > 0) {
     const auto rk = buf_rsrc(K + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
@@ -243,86 +241,110 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
       const int u = x % nunits;  // pass A units, then pass B units
       return (col_idx[base + u / SUB] * SUB + u % SUB) * KU;
     };
-    const int nsteps = 2 * nunits;
-    // pass A: running max (raw scores), sum of exp2 and sum of exp2 * dP
-    float m = -INFINITY, l = 0.f, dn = 0.f;
     auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
       const LP lp(w, opaque(lane));
       const int k0 = key0(x);
       lp.load(rk, k0, sb);
       lp.load(rv, k0, sb + T::KT_BYTES);
     };
-    auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+    // S (keys past N at -inf) and dP of key half KT of the unit at kcur
+    auto scores = [&](const char* cur, int kcur, auto kt_tag, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+      constexpr int KT = decltype(kt_tag)::value;
+      const int limh = min(KU, N - kcur) - 32 * KT - 4 * hi;  // element i: key 32 KT + 8 (i/4) + 4 hi + i%4
+      s = score_half<D, KT, 2>(cur, qf, rdp);
+      if (limh < 32 - 4 * hi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (8 * (i >> 2) + (i & 3) >= limh) s[i] = -INFINITY;
+      }
+      dp = score_half<D, KT, 2>(cur + T::KT_BYTES, df, rdp);
+    };
+    // pass A: running max (raw scores), sum of exp2 and sum of exp2 * dP
+    float m = -INFINITY, l = 0.f, dn = 0.f;
+    auto stepA = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
       const int kcur = key0(x);
       wait_vm<0>();
       __syncthreads();
-      if (x + 1 < nsteps) issue(x + 1, nxt);
-      const int lim = min(KU, N - kcur);
+      issue(x + 1, nxt);  // after the last unit: pass B's first
+      static_for<2>([&](auto kt) __attribute__((always_inline)) {
+        f32x16 s, dp;
+        scores(cur, kcur, kt, s, dp);
+        float mx = s[0];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int limh = lim - 32 * kt - 4 * hi;  // element i: key 32 kt + 8 (i/4) + 4 hi + i%4
-        f32x16 s = kt == 0 ? score_half<D, 0, 2>(cur, qf, rdp) : score_half<D, 1, 2>(cur, qf, rdp);
-        if (lim < KU) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) >= limh) s[i] = -INFINITY;
-        }
-        const f32x16 dp = kt == 0 ? score_half<D, 0, 2>(cur + T::KT_BYTES, df, rdp)
-                                  : score_half<D, 1, 2>(cur + T::KT_BYTES, df, rdp);
-        if (x < nunits) {
-          // pass A: online max, sum and P-weighted sum of dP (this lane's keys)
-          float mx = s[0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-          const float mn = fmaxf(m, mx);
-          if (mn != -INFINITY) {
-            float sl = 0.f, sd = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float e = __builtin_amdgcn_exp2f((s[i] - mn) * scale_log2);
-              sl += e;
-              sd = fmaf(e, dp[i], sd);
-            }
-            const float c = __builtin_amdgcn_exp2f((m - mn) * scale_log2);
-            l = l * c + sl;
-            dn = dn * c + sd;
-            m = mn;
-          }
-        } else {
-          if (x == nunits && kt == 0) {
-            // the query's log2-sum-exp and D over both key halves (lanes l, l^32)
-            const float M = pair_max(m);
-            const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - M) * scale_log2);
-            const float L = l * c + __shfl_xor(l * c, 32);
-            const float Dn = dn * c + __shfl_xor(dn * c, 32);
-            lse2 = M * scale_log2 + __log2f(L);
-            dd = Dn / L;
-          }
-          float ds[16];
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+        const float mn = fmaxf(m, mx);
+        if (mn != -INFINITY) {
+          float sl = 0.f, sd = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lse2));
-            ds[i] = p * (dp[i] - dd);
+            const float e = __builtin_amdgcn_exp2f((s[i] - mn) * scale_log2);
+            sl += e;
+            sd = fmaf(e, dp[i], sd);
           }
-          bf16x8 bp[2];
-          pack_planes(ds, bp);
-          // dQ^T += K^T dS^T over this half's two key planes
-#pragma unroll
-          for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(rdp.vt(cur, dt, 2 * kt + pl), bp[pl], acc[dt]);
+          const float c = __builtin_amdgcn_exp2f((m - mn) * scale_log2);
+          l = l * c + sl;
+          dn = dn * c + sd;
+          m = mn;
         }
         // one 32-key half at a time: keeps the two halves' scores from being live together
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     };
+    // pass B: dS in registers, dQ^T += K^T dS^T with K read transposed
+    auto stepB = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
+      const int kcur = key0(x);
+      wait_vm<0>();
+      __syncthreads();
+      if (x + 1 < nunits) issue(x + 1, nxt);
+      static_for<2>([&](auto kt) __attribute__((always_inline)) {
+        f32x16 s, dp;
+        scores(cur, kcur, kt, s, dp);
+        float ds[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -lse2));
+          ds[i] = p * (dp[i] - dd);
+        }
+        bf16x8 bp[2];
+        pack_planes(ds, bp);
+        row_products<D, decltype(kt)::value, BWD_PF>(cur, rdp, bp, acc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    // two loops, so that pass A holds no dQ accumulators; the unit after
+    // pass A's last (pass B's first) sits in stage nunits % 2
     issue(0, st0);
     int x = 0;
-    for (; x + 2 <= nsteps; x += 2) {
-      step(x, st0, st1);
-      step(x + 1, st1, st0);
+    for (; x + 2 <= nunits; x += 2) {
+      stepA(x, st0, st1);
+      stepA(x + 1, st1, st0);
     }
-    wait_vm<0>();  // nsteps is even
+    if (x < nunits) stepA(x, st0, st1);
+    {
+      // the query's log2-sum-exp and D over both key halves (lanes l, l^32)
+      const float M = pair_max(m);
+      const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - M) * scale_log2);
+      const float L = l * c + __shfl_xor(l * c, 32);
+      const float Dn = dn * c + __shfl_xor(dn * c, 32);
+      lse2 = M * scale_log2 + __log2f(L);
+      dd = Dn / L;
+    }
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
+    auto passB = [&](char* b0, char* b1) __attribute__((always_inline)) {
+      int y = 0;
+      for (; y + 2 <= nunits; y += 2) {
+        stepB(y, b0, b1);
+        stepB(y + 1, b1, b0);
+      }
+      if (y < nunits) stepB(y, b0, b1);
+    };
+    if (nunits % 2 == 0) passB(st0, st1);
+    else passB(st1, st0);
+    wait_vm<0>();
+  } else {
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) acc[t] = f32x16{};
   }
   const size_t qrow = (size_t)bh * N + min(q, N - 1);
   const float os = alpha != nullptr ? alpha[bh % H] : 1.f;  // the branch's weight in the mixed output

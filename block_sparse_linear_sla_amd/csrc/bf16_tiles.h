@@ -350,6 +350,37 @@ __device__ __forceinline__ void col_products(const char* T0, const char* T1, con
   __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
 }
 
+// Row-side products of one 32-key half KT of a unit: acc[dt] += T^T b[pl]
+// over the half's two key planes 2 KT + pl, T a row-major 64-row tile read
+// transposed at d tile dt; each transposed read issued PF products ahead
+// of its MFMA.
+template <int D, int KT, int PF>
+__device__ __forceinline__ void row_products(const char* Ts, const ReadPlan<D>& rp, const bf16x8 (&b)[2],
+                                             f32x16 (&acc)[D / 32]) {
+  constexpr int NI = 2 * (D / 32);   // products: plane-major
+  constexpr int P = PF < NI ? PF : NI - 1;  // reads in flight
+  static_assert(P >= 1, "prefetch depth");
+  auto rd = [&](auto it) __attribute__((always_inline)) {
+    constexpr int i = decltype(it)::value;
+    return rp.vt(Ts, i % (D / 32), 2 * KT + i / (D / 32));
+  };
+  bf16x8 fr[P];
+  static_for<P>([&](auto it) __attribute__((always_inline)) { fr[decltype(it)::value] = rd(it); });
+  static_for<NI>([&](auto it) __attribute__((always_inline)) {
+    constexpr int i = decltype(it)::value;
+    const bf16x8 a = fr[i % P];
+    if constexpr (i + P < NI) fr[i % P] = rd(IntTag<i + P>{});
+    acc[i % (D / 32)] = mfma(a, b[i / (D / 32)], acc[i % (D / 32)]);
+  });
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * P, 0);
+#pragma unroll
+  for (int i = 0; i + P < NI; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, P, 0);
+}
+
 // Q fragments of 32 query rows (B operand of S^T = K Q^T), zero past N.
 template <int D>
 __device__ __forceinline__ void load_q(const uint16_t* Q, long long bh, int q, int N, int hi,
