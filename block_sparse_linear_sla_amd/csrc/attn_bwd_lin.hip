@@ -362,13 +362,12 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
       wait_vm<0>();
       __syncthreads();
       if (x + 1 < nunits) issue(x + 1, nxt);
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const f32x16 dp = kt == 0 ? score_half<D, 0, 2>(cur + T::KT_BYTES, hf, rdp)
-                                  : score_half<D, 1, 2>(cur + T::KT_BYTES, hf, rdp);
+      static_for<2>([&](auto kt_tag) __attribute__((always_inline)) {
+        constexpr int KT = decltype(kt_tag)::value;
+        const f32x16 dp = score_half<D, KT, 2>(cur + T::KT_BYTES, hf, rdp);
         if (PASS == 0) {
           // pass A: w and w (h . v) summed over this lane's keys
-          const f32x16 s = kt == 0 ? score_half<D, 0, 2>(cur, af, rdp) : score_half<D, 1, 2>(cur, af, rdp);
+          const f32x16 s = score_half<D, KT, 2>(cur, af, rdp);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             sw += s[i];
@@ -381,13 +380,10 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
           for (int i = 0; i < 16; ++i) c[i] = dtv - dp[i];
           bf16x8 bp[2];
           pack_planes(c, bp);
-#pragma unroll
-          for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-            for (int dt = 0; dt < D / 32; ++dt) acc[dt] = mfma(rdp.vt(cur, dt, 2 * kt + pl), bp[pl], acc[dt]);
+          row_products<D, KT, BWD_PF>(cur, rdp, bp, acc);
         }
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     };
     auto run = [&](auto pass) __attribute__((always_inline)) {
       issue(0, st0);
