@@ -84,6 +84,35 @@ def test_sparse_bwd_small(case):
     assert not dk[0, :, 2 * bk:3 * bk].any() and not dv[0, :, 2 * bk:3 * bk].any()
 
 
+def _skewed_csr(rng, BH, Nq, Nk):
+    """Columns listed with very different frequencies, so that the column
+    kernels' launch order (most-listed key blocks first) spans its classes:
+    block 0 and the last (ragged) block by every row, block 1 by every second
+    row, block 3 by no row, the rest at random by about 10% of the rows."""
+    rp, ci = [0], []
+    for r in range(BH * Nq):
+        sel = set(np.flatnonzero(rng.random(Nk) < 0.1).tolist()) | {0, Nk - 1}
+        if r % 2 == 0:
+            sel.add(1)
+        sel.discard(3)
+        ci.extend(sorted(sel))
+        rp.append(len(ci))
+    return np.array(rp, dtype=np.int64), np.array(ci, dtype=np.int64)
+
+
+@pytest.mark.parametrize("bk", [64, 128])
+def test_sparse_bwd_skewed_columns(bk):
+    N, d, bq = 4000, 128, 128
+    print(f"[bwd] skewed columns bk={bk}", flush=True)
+    wl = gen.Workload("adhoc", B=1, H=2, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+                      dtype="bf16", router=False, seed=31)
+    x = gen.make(wl)
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp, ci = _skewed_csr(np.random.default_rng(13), 2, Nq, Nk)
+    dq, dk, dv = _run(x, bq, bk, rp, ci, seed=9)
+    assert not dk[0, :, 3 * bk:4 * bk].any() and not dv[0, :, 3 * bk:4 * bk].any()
+
+
 def test_sparse_bwd_480p_two_heads():
     """The 480p SLA2 workload at full length (N = 32760) on two heads with the
     library's own mask."""

@@ -25,7 +25,7 @@ import block_sparse_linear_sla_amd as S
 import gen
 from oracle import sla_oracle as O
 from tests import _util as U
-from tests.test_gpu_bwd import _compare, _random_csr
+from tests.test_gpu_bwd import _compare, _random_csr, _skewed_csr
 
 pytestmark = pytest.mark.gpu
 
@@ -70,6 +70,26 @@ def test_linear_bwd_small(case):
     # the fully listed row block has no linear branch: its dQ rows are 0
     s0 = (Nq - 1) * bq
     assert not dq[0, 1, s0:].any()
+
+
+@pytest.mark.parametrize("bk", [64, 128])
+def test_linear_bwd_skewed_columns(bk):
+    """Key blocks listed by every row, by half of them, by about 10% and by
+    none (the column kernel's launch order across its classes)."""
+    N, d, bq = 4000, 128, 128
+    print(f"[lin-bwd] skewed columns bk={bk}", flush=True)
+    wl = gen.Workload("adhoc", B=1, H=2, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+                      dtype="bf16", router=False, seed=37)
+    x = gen.make(wl)
+    Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
+    rp, ci = _skewed_csr(np.random.default_rng(14), 2, Nq, Nk)
+    q, k, v, dO, rpt, cit = _inputs(x, rp, ci, seed=10)
+    dq, dk, dv = S.sla_linear_bwd(q, k, v, dO.cuda(), bq, bk, rpt, cit)
+    torch.cuda.synchronize()
+    ref = O.linear_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
+    _compare(dq, ref["dQ"], "dQ")
+    _compare(dk, ref["dK"], "dK")
+    _compare(dv, ref["dV"], "dV")
 
 
 def test_linear_bwd_accumulates_onto_sparse():
