@@ -102,7 +102,10 @@ __global__ __launch_bounds__(256, 2) void lin_outer_kernel(const uint16_t* __res
   using T = Tiles<D>;
   using LP = LoadPlan<D, 4>;
   constexpr int NT = D / 32, TPW = NT * NT / 4;
-  constexpr int STAGE = 2 * T::KT_BYTES;
+  // X and Y tiles of a 64-row unit, then (M pass) the unit's 64 values of
+  // 1/den and of D~, loaded with the tiles so that no load of a later unit
+  // is waited for in the middle of a step
+  constexpr int STAGE = 2 * T::KT_BYTES + 2 * 64 * 4;
   __shared__ __attribute__((aligned(16))) char st0[STAGE];
   __shared__ __attribute__((aligned(16))) char st1[STAGE];
   const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5;
@@ -121,10 +124,16 @@ __global__ __launch_bounds__(256, 2) void lin_outer_kernel(const uint16_t* __res
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = f32x16{};
   float sp = 0.f;
+  const auto ri = buf_rsrc(inv + (inv != nullptr ? (size_t)bh * QP : 0), (uint32_t)(QP * 4));
+  const auto re = buf_rsrc(dtq + (dtq != nullptr ? (size_t)bh * QP : 0), (uint32_t)(QP * 4));
   auto issue = [&](int x, char* sb) __attribute__((always_inline)) {
     const LP lp(w, opaque(lane));
     lp.load(rx, r0 + x * KU, sb);
     lp.load(ry, r0 + x * KU, sb + T::KT_BYTES);
+    if (inv != nullptr && w == 0) {
+      b2lds4(ri, 4u * (uint32_t)lane, 4u * (uint32_t)(r0 + x * KU), sb + 2 * T::KT_BYTES);
+      b2lds4(re, 4u * (uint32_t)lane, 4u * (uint32_t)(r0 + x * KU), sb + 2 * T::KT_BYTES + 256);
+    }
   };
   auto step = [&](int x, char* cur, char* nxt) __attribute__((always_inline)) {
     wait_vm<0>();
@@ -139,11 +148,11 @@ __global__ __launch_bounds__(256, 2) void lin_outer_kernel(const uint16_t* __res
       const uint4 av = __builtin_bit_cast(uint4, rdp.vt(cur, at, pl));
       float xs[8];
       if (inv != nullptr) {
-        const size_t tq = (size_t)bh * QP + t0 + 16 * pl + 4 * hi;
-        const float4 i0 = *reinterpret_cast<const float4*>(inv + tq);
-        const float4 i1 = *reinterpret_cast<const float4*>(inv + tq + 8);
-        const float4 e0 = *reinterpret_cast<const float4*>(dtq + tq);
-        const float4 e1 = *reinterpret_cast<const float4*>(dtq + tq + 8);
+        const float* iu = reinterpret_cast<const float*>(cur + 2 * T::KT_BYTES) + 16 * pl + 4 * hi;
+        const float4 i0 = *reinterpret_cast<const float4*>(iu);
+        const float4 i1 = *reinterpret_cast<const float4*>(iu + 8);
+        const float4 e0 = *reinterpret_cast<const float4*>(iu + 64);
+        const float4 e1 = *reinterpret_cast<const float4*>(iu + 72);
         const float iv[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
         const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll

@@ -210,6 +210,12 @@ __device__ __forceinline__ void b2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, (int)soff, 0, 0);
 }
 
+// Direct buffer load of 4 bytes per lane into LDS: lane l writes
+// lds_wave_base + 4 l.
+__device__ __forceinline__ void b2lds4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, (int)voff, (int)soff, 0, 0);
+}
+
 // Direct loads of one unit's K or V tile into LDS, split over NWL wavefronts.
 // Load slot u of a tile fills the 1 KB at tile + 1024 u (8 rows of 128 bytes,
 // in the swizzled layout above): lane l brings the 16-byte chunk that belongs
