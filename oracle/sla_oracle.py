@@ -680,33 +680,34 @@ def sparse_branch_i8f8(qz: Dict, bq: int, bk: int, row_ptr, col_idx, rows=None, 
 # the derivative of the forward definition above, taken by torch's autograd
 # in float64 on the CPU, one row block at a time; pinned by central finite
 # differences and by the full-mask case (dense attention's gradient).
-def sparse_branch_backward(Q, K, V, bq: int, bk: int, row_ptr, col_idx, dO) -> Dict[str, np.ndarray]:
+def sparse_branch_backward(Q, K, V, bq: int, bk: int, row_ptr, col_idx, dO, rows=None) -> Dict[str, np.ndarray]:
     """dQ, dK, dV of L = sum(O_s * dO), O_s the sparse branch of
-    sparse_branch() (rows with no selected block contribute nothing)."""
+    sparse_branch() (rows with no selected block contribute nothing), one row
+    block at a time.  With `rows` (a list of (b, h, i)) only those row blocks
+    are differentiated: their dQ rows are exact, dK and dV hold only their
+    share."""
     import torch
     Qt, Kt, Vt = (torch.tensor(as_f64(x)) for x in (Q, K, V))
     G = torch.tensor(as_f64(dO))
     B, H, N, d = Qt.shape
     Nq = n_blocks(N, bq)
     dQ, dK, dV = torch.zeros_like(Qt), torch.zeros_like(Kt), torch.zeros_like(Vt)
-    for b in range(B):
-        for h in range(H):
-            for i in range(Nq):
-                r = (b * H + h) * Nq + i
-                sel = col_idx[row_ptr[r]:row_ptr[r + 1]]
-                if len(sel) == 0:
-                    continue
-                keys = torch.tensor(_keys_of(sel, bk, N))
-                s, e = block_range(i, bq, N)
-                q = Qt[b, h, s:e].clone().requires_grad_(True)
-                k = Kt[b, h, keys].clone().requires_grad_(True)
-                v = Vt[b, h, keys].clone().requires_grad_(True)
-                P = torch.softmax(q @ k.T / math.sqrt(d), dim=-1)
-                o = P @ v
-                (o * G[b, h, s:e]).sum().backward()
-                dQ[b, h, s:e] += q.grad
-                dK[b, h, keys] += k.grad
-                dV[b, h, keys] += v.grad
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = col_idx[row_ptr[r]:row_ptr[r + 1]]
+        if len(sel) == 0:
+            continue
+        keys = torch.tensor(_keys_of(sel, bk, N))
+        s, e = block_range(i, bq, N)
+        q = Qt[b, h, s:e].clone().requires_grad_(True)
+        k = Kt[b, h, keys].clone().requires_grad_(True)
+        v = Vt[b, h, keys].clone().requires_grad_(True)
+        P = torch.softmax(q @ k.T / math.sqrt(d), dim=-1)
+        o = P @ v
+        (o * G[b, h, s:e]).sum().backward()
+        dQ[b, h, s:e] += q.grad
+        dK[b, h, keys] += k.grad
+        dV[b, h, keys] += v.grad
     return {"dQ": dQ.numpy(), "dK": dK.numpy(), "dV": dV.numpy()}
 
 

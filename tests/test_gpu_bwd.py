@@ -125,6 +125,44 @@ def test_sparse_bwd_480p_two_heads():
     _run(x, wl.bq, wl.bk, rp, ci, seed=5)
 
 
+def test_sparse_bwd_720p_one_head():
+    """The 720p SLA2 workload at full length (N = 75600, 591 x 1182 blocks) on
+    one head with the library's mask.  The oracle differentiates sampled row
+    blocks (the longest and shortest rows, the middle one and the ragged last
+    one: their dQ rows are exact); every key is checked by two identities
+    that hold at any size: sum_u dV_u = sum_t dO_t over the rows with a
+    listed block (P's rows sum to 1), and sum_u dK_u = 0 (each row's dS sums
+    to 0, sum_u P_tu (dP_tu - D_t) = D_t - D_t)."""
+    wl = gen.WORKLOADS["video720p-sla2-N75600"]
+    print(f"[bwd] {wl.name}, 1 head", flush=True)
+    x = gen.make(wl, heads=1)
+    q, k, v = U.dev(x.Q, x.K, x.V)
+    rp_t, ci_t = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    rp, ci = U.csr(rp_t, ci_t)
+    dO = torch.from_numpy(np.random.default_rng(15).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
+    dq, dk, dv = S.sla_sparse_bwd(q, k, v, dO.cuda(), wl.bq, wl.bk, rp_t, ci_t)
+    torch.cuda.synchronize()
+    N = x.Q.shape[2]
+    counts = np.diff(rp)
+    Nq = len(counts)
+    rows = sorted({(0, 0, int(np.argmax(counts))), (0, 0, int(np.argmin(counts))), (0, 0, 137),
+                   (0, 0, Nq // 2), (0, 0, Nq - 1)})
+    print(f"  blocks per row {counts.min()}..{counts.max()}, sampled rows {[r[2] for r in rows]}")
+    ref = O.sparse_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
+    for (b, h, i) in rows:
+        s, e = O.block_range(i, wl.bq, N)
+        _compare(dq[b, h, s:e], ref["dQ"][b, h, s:e], f"dQ rows of block {i}")
+    G = O.as_f64(dO)[0, 0]
+    dkd, dvd = dk[0, 0].cpu().double().numpy(), dv[0, 0].cpu().double().numpy()
+    has = np.repeat(counts > 0, wl.bq)[:N]
+    err = np.abs(dvd.sum(0) - G[has].sum(0)).max() / np.abs(G[has]).sum(0).max()
+    print(f"  sum dV vs sum dO: {err:.3g} of sum|dO|")
+    assert err <= 1e-2
+    rel = (np.abs(dkd.sum(0)) / np.maximum(np.abs(dkd).sum(0), 1e-30)).max()
+    print(f"  sum dK: {rel:.3g} of sum|dK| (worst column)")
+    assert rel <= 1e-2
+
+
 def test_alpha_grad():
     print("[bwd] alpha gradient", flush=True)
     rng = np.random.default_rng(9)

@@ -141,6 +141,15 @@ def test_linear_bwd_480p_two_heads():
     for (b, h, i) in rows:
         s, e = i * wl.bq, min(N, (i + 1) * wl.bq)
         _compare(dq[b, h, s:e], ref["dQ"][b, h, s:e], f"dQ rows of block {i}, head {h}")
+    _linear_identities(x, wl, rp, dO, dq, dk, dv)
+
+
+def _linear_identities(x, wl, rp, dO, dq, dk, dv):
+    """Every key and query of every head: dV sums to dO_l over the rows with a
+    linear branch, sum_u phi(k_u) . dphi(k_u) = 0 per head and phi(q_t) .
+    dphi(q_t) = 0 per query."""
+    B, H, N, d = x.Q.shape
+    Nq = O.n_blocks(N, wl.bq)
     Qd, Kd = O.as_f64(x.Q), O.as_f64(x.K)
     G = O.as_f64(dO)
     dqd, dkd, dvd = (t.cpu().double().numpy() for t in (dq, dk, dv))
@@ -169,6 +178,32 @@ def test_linear_bwd_480p_two_heads():
         relq = np.abs(tq.sum(1)) / np.maximum(np.abs(tq).sum(1), 1e-30)
         print(f"  head {h}: per-query phi(q) . dphi(q): max {relq.max():.3g}, mean {relq.mean():.3g}")
         assert relq.mean() <= 2e-2
+
+
+def test_linear_bwd_720p_one_head():
+    """The 720p SLA2 workload at full length (N = 75600, 591 x 1182 blocks) on
+    one head with the library's mask: sampled row blocks (the longest and
+    shortest rows, the middle and the ragged last) against the oracle, the
+    identities for every key and query."""
+    wl = gen.WORKLOADS["video720p-sla2-N75600"]
+    print(f"[lin-bwd] {wl.name}, 1 head", flush=True)
+    x = gen.make(wl, heads=1)
+    q, k, v = U.dev(x.Q, x.K, x.V)
+    rp_t, ci_t = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    rp, ci = U.csr(rp_t, ci_t)
+    dO = torch.from_numpy(np.random.default_rng(16).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
+    dq, dk, dv = S.sla_linear_bwd(q, k, v, dO.cuda(), wl.bq, wl.bk, rp_t, ci_t)
+    torch.cuda.synchronize()
+    N = x.Q.shape[2]
+    counts = np.diff(rp)
+    Nq = len(counts)
+    rows = sorted({(0, 0, int(np.argmax(counts))), (0, 0, int(np.argmin(counts))), (0, 0, 137),
+                   (0, 0, Nq // 2), (0, 0, Nq - 1)})
+    ref = O.linear_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
+    for (b, h, i) in rows:
+        s, e = O.block_range(i, wl.bq, N)
+        _compare(dq[b, h, s:e], ref["dQ"][b, h, s:e], f"dQ rows of block {i}")
+    _linear_identities(x, wl, rp, dO, dq, dk, dv)
 
 
 @pytest.mark.parametrize("N,d,bq,bk", [(1000, 128, 128, 64), (777, 64, 64, 128)])
