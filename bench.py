@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the 8-bit, backward and SoftTop-k legs")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the leg that replays the step as captured HIP graphs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
     return ap.parse_args()
@@ -275,6 +277,32 @@ def main():
     ms_step, (st_sum, st_maskp, st_fused, ev_step) = timed_steps(step, args.steps, nset)
     ms_warm, (w_sum, w_maskp, w_fused, w_ev) = timed_steps(step, args.steps, 1)
 
+    # the same step captured once per input set as a HIP graph and replayed
+    # in the same rotation: what a caller that replays graphs sees (the
+    # library only launches kernels, so a step captures whole)
+    graph = None
+    if not args.no_graph:
+        try:
+            graphs = []
+            for si in range(nset):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(si)
+                graphs.append(g)
+            for i in range(10):
+                graphs[i % nset].replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for i in range(args.steps):
+                graphs[i % nset].replay()
+            e1.record()
+            torch.cuda.synchronize()
+            graph = {"ms_per_step": e0.elapsed_time(e1) / args.steps, "steps": args.steps, "input_sets": nset}
+            del graphs
+        except RuntimeError as err:  # reported, never fatal: the eager figures stand on their own
+            graph = {"error": str(err)[:200]}
+
     # the standalone mask call (pools Q and K itself), for the mask's HBM
     # roofline: rotating over the input sets (cold) and on one set (warm)
     rp_m, ci_m = torch.empty_like(rp), torch.empty_like(ci)
@@ -347,6 +375,7 @@ def main():
                  "stage_ms": {"kv_prepare": w_sum, "mask_prepared": w_maskp, "fused": w_fused,
                               "events_step": w_ev}},
         "settle": {"ms": settle_ms, "steps": n_settle},
+        "graph": graph,
         "sparsity": 1.0 - nnz / float(wl.B * wl.H * wl.Nq * wl.Nk), "nnz": nnz,
         "executed_TFLOPS_fused": tf(fused_flops, st_fused),
     }
