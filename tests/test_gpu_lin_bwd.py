@@ -256,7 +256,7 @@ def test_attn_bwd_480p_two_heads():
     counts = np.diff(rp)
     assert counts.min() > 0 and counts.max() < Nk  # both branches on every row
     rows = [(0, 0, 3), (0, 1, Nq - 1)]
-    rs = O.sparse_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO)
+    rs = O.sparse_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
     rl = O.linear_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
     a = alpha.double().numpy()
     for (b, h, i) in rows:

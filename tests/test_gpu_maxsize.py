@@ -4,7 +4,9 @@ layout, with an exact and a ragged last block, on a peaked map (Top-k
 decides, short rows) and a flat one (Top-p keeps a large part of each row).
 The mask is compared with the oracle's as in the other mask tests; the fused
 forward on sampled row blocks (the longest and shortest rows, the last one)
-with the bf16 bar."""
+with the bf16 bar; and the mixed backward there (dQ of sampled row blocks
+against the oracle, dV summed over the keys against dO summed over the
+queries)."""
 import numpy as np
 import pytest
 import torch
@@ -13,6 +15,7 @@ import block_sparse_linear_sla_amd as S
 import gen
 from oracle import sla_oracle as O
 from tests import _util as U
+from tests.test_gpu_bwd import _compare
 
 pytestmark = pytest.mark.gpu
 
@@ -75,3 +78,30 @@ def test_fused_forward_at_the_longest_rows():
     m, rel = U.compare_rows(U.rows_of(o, rows, wl.bq), ref)
     print(f"  o: max-abs {m:.3g} rel {rel:.3g}")
     assert m <= 2e-2 and rel <= 5e-3
+
+
+def test_mixed_backward_at_the_longest_rows():
+    name, N, tau, k_frac, p = CASES[2]
+    print(f"[maxsize] sla_attn_bwd {name}: N {N}", flush=True)
+    x = _inputs(N, tau, k_frac, p)
+    wl = x.wl
+    q, k, v, a = U.dev(x.Q, x.K, x.V, x.alpha)
+    rp_t, ci_t = S.sla_mask(q, k, wl.bq, wl.bk, k_frac, p)
+    rp, ci = U.csr(rp_t, ci_t)
+    counts = np.diff(rp)
+    assert counts.min() > 0 and counts.max() < NK_MAX  # both branches on every row
+    dO = torch.from_numpy(np.random.default_rng(17).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
+    dq, dk, dv = S.sla_attn_bwd(q, k, v, dO.cuda(), a, wl.bq, wl.bk, rp_t, ci_t)
+    torch.cuda.synchronize()
+    Nq = len(counts)
+    rows = sorted({(0, 0, int(np.argmax(counts))), (0, 0, int(np.argmin(counts))), (0, 0, Nq - 1)})
+    rs = O.sparse_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
+    rl = O.linear_branch_backward(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, dO, rows=rows)
+    for (b, h, i) in rows:
+        s, e = O.block_range(i, wl.bq, N)
+        ref = 0.7 * rs["dQ"][b, h, s:e] + 0.3 * rl["dQ"][b, h, s:e]
+        _compare(dq[b, h, s:e], ref, f"dQ rows of block {i}")
+    G = O.as_f64(dO)[0, 0]
+    err = np.abs(dv[0, 0].cpu().double().numpy().sum(0) - G.sum(0)).max() / np.abs(G).sum(0).max()
+    print(f"  sum dV vs sum dO: {err:.3g} of sum|dO|")
+    assert err <= 1e-2
