@@ -328,6 +328,48 @@ def linear_branch(Q, K, V, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dic
     return out
 
 
+def sparse_branch_lse(Q, K, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+    """Natural log of each query's sparse-branch softmax normaliser,
+        lse(t) = log sum_u exp(q_t . k_u / sqrt(d))
+    over the keys u of its block's selected key blocks [SLA2 §一; DEF]: the
+    value a backward pass needs to recover the branch's probabilities,
+    exp(q_t . k_u / sqrt(d) - lse(t)).  -inf (the log of an empty sum) when
+    no block is selected.  Returns {(b, h, i): [rows_in_block]}."""
+    Q, K = as_f64(Q), as_f64(K)
+    B, H, N, d = Q.shape
+    Nq = n_blocks(N, bq)
+    out = {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        s, e = block_range(i, bq, N)
+        keys = _keys_of(col_idx[row_ptr[r]:row_ptr[r + 1]], bk, N)
+        if len(keys) == 0:
+            out[(b, h, i)] = np.full(e - s, -np.inf)
+            continue
+        Sx = Q[b, h, s:e] @ K[b, h, keys].T / math.sqrt(d)
+        m = Sx.max(axis=1)
+        out[(b, h, i)] = m + np.log(np.exp(Sx - m[:, None]).sum(axis=1))
+    return out
+
+
+def linear_branch_den(Q, K, bq: int, bk: int, row_ptr, col_idx, rows=None) -> Dict:
+    """Each query's linear-branch normaliser,
+        den(t) = sum_u phi(q_t) . phi(k_u)
+    over the keys u of the key blocks its block did not select [SLA2 §一;
+    FM]; 0 when every block is selected.  Returns {(b, h, i): [rows_in_block]}."""
+    Q, K = as_f64(Q), as_f64(K)
+    B, H, N, d = Q.shape
+    Nq, Nk = n_blocks(N, bq), n_blocks(N, bk)
+    out = {}
+    for (b, h, i) in _rows(B, H, Nq, rows):
+        r = (b * H + h) * Nq + i
+        sel = set(int(j) for j in col_idx[row_ptr[r]:row_ptr[r + 1]])
+        s, e = block_range(i, bq, N)
+        keys = _keys_of([j for j in range(Nk) if j not in sel], bk, N)
+        out[(b, h, i)] = phi(Q[b, h, s:e]) @ phi(K[b, h, keys]).sum(axis=0) if len(keys) else np.zeros(e - s)
+    return out
+
+
 def combine(Os: np.ndarray, Ol: np.ndarray, alpha_h: float) -> np.ndarray:
     """O = alpha * O_sparse + (1 - alpha) * O_linear [SLA2 §二: the final
     result is the ratio times the sparse result plus one minus the ratio times

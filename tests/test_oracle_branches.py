@@ -149,6 +149,66 @@ def test_branches_brute_force_token_loops():
             assert abs(Ol[0, 0, t, c] - ref) < 1e-12
 
 
+def test_normalisers_brute_force_token_loops():
+    """The sparse branch's log-normaliser and the linear branch's
+    denominator against pure-Python per-token sums (math.exp, math.log) on a
+    tiny case with a ragged last block, an empty row and a full row."""
+    B, H, N, d, bq, bk = 1, 1, 45, 4, 16, 8
+    q, k, _ = _qkv(B, H, N, d, seed=9)
+    Nk = O.n_blocks(N, bk)
+    # row 0 lists nothing, row 1 every block, row 2 (ragged) blocks 1, 4, 5
+    rp = np.array([0, 0, Nk, Nk + 3])
+    ci = np.array(list(range(Nk)) + [1, 4, 5])
+    lse = O.sparse_branch_lse(q, k, bq, bk, rp, ci)
+    den = O.linear_branch_den(q, k, bq, bk, rp, ci)
+    Q, K = q[0, 0].tolist(), k[0, 0].tolist()
+
+    def ph(x):
+        return x + 1.0 if x > 0 else math.exp(x)
+
+    for t in range(N):
+        i = t // bq
+        sel = set(int(j) for j in ci[rp[i]:rp[i + 1]])
+        keys_s = [u for u in range(N) if (u // bk) in sel]
+        keys_l = [u for u in range(N) if (u // bk) not in sel]
+        got_l, got_d = lse[(0, 0, i)][t - i * bq], den[(0, 0, i)][t - i * bq]
+        if keys_s:
+            ref = math.log(sum(math.exp(sum(Q[t][a] * K[u][a] for a in range(d)) / math.sqrt(d)) for u in keys_s))
+            assert abs(got_l - ref) < 1e-12
+        else:
+            assert got_l == -math.inf
+        ref = sum(sum(ph(Q[t][a]) * ph(K[u][a]) for a in range(d)) for u in keys_l)
+        assert abs(got_d - ref) <= 1e-12 * max(1.0, ref)
+
+
+def test_normalisers_recover_the_branches():
+    """exp(score - lse) are the sparse branch's weights and phi(q).phi(k) /
+    den the linear branch's: both sum to one over their keys and reproduce
+    the branch outputs on the 480p workload's first query blocks."""
+    wl = gen.WORKLOADS["video480p-sla2-N32760"]
+    x = gen.make(wl, heads=1, N=2000)
+    rp, ci, _ = O.mask(x.Q, x.K, wl.bq, wl.bk, 0.1, 0.6)
+    rows = [(0, 0, 0), (0, 0, 7), (0, 0, O.n_blocks(2000, wl.bq) - 1)]
+    lse = O.sparse_branch_lse(x.Q, x.K, wl.bq, wl.bk, rp, ci, rows)
+    den = O.linear_branch_den(x.Q, x.K, wl.bq, wl.bk, rp, ci, rows)
+    os_ = O.sparse_branch(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, rows)
+    ol = O.linear_branch(x.Q, x.K, x.V, wl.bq, wl.bk, rp, ci, rows)
+    Qd, Kd, Vd = O.as_f64(x.Q)[0, 0], O.as_f64(x.K)[0, 0], O.as_f64(x.V)[0, 0]
+    N, d = Qd.shape
+    Nk = O.n_blocks(N, wl.bk)
+    for (b, h, i) in rows:
+        s, e = O.block_range(i, wl.bq, N)
+        sel = [int(j) for j in ci[rp[i]:rp[i + 1]]]
+        ks = np.concatenate([np.arange(*O.block_range(j, wl.bk, N)) for j in sel])
+        kl = np.concatenate([np.arange(*O.block_range(j, wl.bk, N)) for j in range(Nk) if j not in sel])
+        P = np.exp(Qd[s:e] @ Kd[ks].T / math.sqrt(d) - lse[(b, h, i)][:, None])
+        assert np.allclose(P.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        assert np.allclose(P @ Vd[ks], os_[(b, h, i)], rtol=0, atol=1e-12)
+        W = O.phi(Qd[s:e]) @ O.phi(Kd[kl]).T / den[(b, h, i)][:, None]
+        assert np.allclose(W.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+        assert np.allclose(W @ Vd[kl], ol[(b, h, i)], rtol=0, atol=1e-12)
+
+
 def test_combine_endpoints_and_linearity():
     B, H, N, d, bq, bk = 1, 3, 300, 16, 64, 64
     q, k, v = _qkv(B, H, N, d, seed=21)
