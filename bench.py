@@ -509,6 +509,25 @@ def main():
                       # transpose built once): the training backward
                       "attn_bwd_ms": e[3].elapsed_time(e[4]) / args.steps,
                       "linear_kernels": "csc_* + lin_phi + lin_outer x2 + lin_split x3 + lin_dq + lin_dkdv"}
+        # the training pair: the fused forward that also keeps each query's
+        # normalisers and the two branch outputs, and the mixed backward that
+        # reads them instead of recomputing them (the row kernels skip their
+        # first pass)
+        _, sv = S.sla_fused_fwd_save(q, k, v, alpha, wl.bq, wl.bk, rp, ci, ws, out=out)
+        da = torch.empty(wl.H, dtype=torch.float32, device=dev)
+        S.sla_attn_bwd_saved(q, k, v, dO, alpha, wl.bq, wl.bk, rp, ci, sv, ws=bws, out=grads, dalpha=da)
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        for _ in range(args.steps):
+            S.sla_fused_fwd_save(q, k, v, alpha, wl.bq, wl.bk, rp, ci, ws, out=out, saved=sv)
+        e[1].record()
+        for _ in range(args.steps):
+            S.sla_attn_bwd_saved(q, k, v, dO, alpha, wl.bq, wl.bk, rp, ci, sv, ws=bws, out=grads, dalpha=da)
+        e[2].record()
+        torch.cuda.synchronize()
+        res["bwd"]["fused_fwd_save_ms"] = e[0].elapsed_time(e[1]) / args.steps
+        res["bwd"]["attn_bwd_saved_ms"] = e[1].elapsed_time(e[2]) / args.steps
 
     # SoftTop-k weights of every mask row (pool + logits + threshold solve),
     # the router-training form of the selection, at temperature 0.5

@@ -27,10 +27,12 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTS = ("sla_workspace_bytes", "sla_mask_capacity", "sla_mask", "sla_mask_prepared", "sla_soft_topk",
            "sla_mask_noalloc_bytes", "sla_mask_noalloc",
            "sla_sparse_fwd",
-           "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd",
+           "sla_linear_fwd", "sla_attn_fwd", "sla_kv_prepare", "sla_fused_fwd", "sla_saved_terms_count",
+           "sla_fused_fwd_save",
            "sla_dense_fwd", "sla_i8_layout_of", "sla_quantize_i8", "sla_sparse_fwd_i8",
            "sla_quantize_i8f8", "sla_sparse_fwd_i8f8",
-           "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_linear_bwd", "sla_attn_bwd", "sla_alpha_grad",
+           "sla_bwd_workspace_bytes", "sla_sparse_bwd", "sla_linear_bwd", "sla_attn_bwd", "sla_attn_bwd_saved",
+           "sla_alpha_grad",
            "sla_status_string")
 
 
@@ -83,6 +85,9 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_size_t, vp]
         L.sla_kv_prepare.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_fused_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_saved_terms_count.argtypes = [P]
+        L.sla_saved_terms_count.restype = ctypes.c_int64
+        L.sla_fused_fwd_save.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp, vp]
         L.sla_dense_fwd.argtypes = [P, vp, vp, vp, vp, vp]
         L.sla_i8_layout_of.argtypes = [P, ctypes.POINTER(I8Layout)]
         L.sla_quantize_i8.argtypes = [P, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -95,14 +100,16 @@ def lib() -> ctypes.CDLL:
         L.sla_linear_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
                                      vp]
         L.sla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_attn_bwd_saved.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                         ctypes.c_size_t, vp]
         L.sla_alpha_grad.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_status_string.argtypes = [ctypes.c_int]
         L.sla_status_string.restype = ctypes.c_char_p
         for fn in ("sla_mask", "sla_mask_prepared", "sla_mask_noalloc", "sla_soft_topk", "sla_sparse_fwd", "sla_linear_fwd", "sla_attn_fwd",
-                   "sla_kv_prepare", "sla_fused_fwd", "sla_dense_fwd", "sla_i8_layout_of",
+                   "sla_kv_prepare", "sla_fused_fwd", "sla_fused_fwd_save", "sla_dense_fwd", "sla_i8_layout_of",
                    "sla_quantize_i8", "sla_sparse_fwd_i8", "sla_quantize_i8f8", "sla_sparse_fwd_i8f8",
                    "sla_sparse_bwd", "sla_linear_bwd",
-                   "sla_attn_bwd", "sla_alpha_grad"):
+                   "sla_attn_bwd", "sla_attn_bwd_saved", "sla_alpha_grad"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -306,6 +313,31 @@ def sla_fused_fwd(q, k, v, alpha, bq: int, bk: int, row_ptr, col_idx, ws: torch.
     return o
 
 
+def sla_saved_terms_count(prob: Problem) -> int:
+    return int(lib().sla_saved_terms_count(ctypes.byref(prob)))
+
+
+def sla_fused_fwd_save(q, k, v, alpha, bq: int, bk: int, row_ptr, col_idx, ws: torch.Tensor, out=None,
+                       saved=None):
+    """sla_fused_fwd that also keeps, for the backward of a training step,
+    each query's normalisers and the two branch outputs (float32).  Returns
+    (O, saved) with saved = dict(lse2, invden, o_s, o_l)."""
+    _need(q, k, v, like=q)
+    prob = problem(q, bq, bk)
+    o = out if out is not None else torch.empty_like(q)
+    if saved is None:
+        n = sla_saved_terms_count(prob)
+        saved = dict(lse2=torch.empty(max(n, 1), dtype=torch.float32, device=q.device),
+                     invden=torch.empty(max(n, 1), dtype=torch.float32, device=q.device),
+                     o_s=torch.empty(q.shape, dtype=torch.float32, device=q.device),
+                     o_l=torch.empty(q.shape, dtype=torch.float32, device=q.device))
+    _check("sla_fused_fwd_save", lib().sla_fused_fwd_save(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(row_ptr), _ptr(col_idx), _ptr(o),
+        _ptr(ws), ws.numel(), _ptr(saved["lse2"]), _ptr(saved["invden"]), _ptr(saved["o_s"]),
+        _ptr(saved["o_l"]), _stream()))
+    return o, saved
+
+
 def sla_dense_fwd(q, k, v, bq: int = 128, bk: int = 64, out=None):
     _need(q, k, v, like=q)
     prob = problem(q, bq, bk)
@@ -446,6 +478,28 @@ def sla_attn_bwd(q, k, v, do, alpha, bq: int, bk: int, row_ptr, col_idx, ws=None
                                               _ptr(alpha.contiguous()), _ptr(row_ptr), _ptr(col_idx), _ptr(dq),
                                               _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream()))
     return dq, dk, dv
+
+
+def sla_attn_bwd_saved(q, k, v, do, alpha, bq: int, bk: int, row_ptr, col_idx, saved, ws=None, out=None,
+                       dalpha=None):
+    """sla_attn_bwd reading the terms sla_fused_fwd_save kept (saved: its
+    dict) instead of recomputing them: returns (dQ, dK, dV, dalpha) with
+    dalpha the alpha gradient (float32 [H])."""
+    _need(q, k, v, do, like=q)
+    for t in (saved["o_s"], saved["o_l"]):
+        if t.dtype != torch.float32 or t.shape != q.shape or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("the saved branch outputs must be contiguous float32 CUDA tensors shaped like Q")
+    if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != q.shape[1]:
+        raise ValueError("alpha must be a float32 CUDA tensor of H values")
+    prob = problem(q, bq, bk)
+    dq, dk, dv = out if out is not None else (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    da = dalpha if dalpha is not None else torch.empty(q.shape[1], dtype=torch.float32, device=q.device)
+    w = ws if ws is not None else bwd_workspace(prob, q.device)
+    _check("sla_attn_bwd_saved", lib().sla_attn_bwd_saved(
+        ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(alpha.contiguous()), _ptr(row_ptr),
+        _ptr(col_idx), _ptr(saved["lse2"]), _ptr(saved["invden"]), _ptr(saved["o_s"]), _ptr(saved["o_l"]),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(w), w.numel(), _stream()))
+    return dq, dk, dv, da
 
 
 def sla_alpha_grad(do, o_s, o_l, bq: int = 128, bk: int = 64, ws=None) -> torch.Tensor:

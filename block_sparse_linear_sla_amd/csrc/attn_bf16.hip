@@ -464,12 +464,13 @@ struct AttnShape {
   static constexpr int NQW = BQ / 32;                                  // query wavefronts
   static constexpr int NWT = (LIN && D == 128 && NQW < 4) ? 4 : NQW;   // all wavefronts
 };
-template <int D, int BQ, int SUB, int MODE>
+template <int D, int BQ, int SUB, int MODE, bool SAVE = false>
 __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ pk_g, const int* __restrict__ row_ptr, const int* __restrict__ col_idx,
     const float* __restrict__ alpha, const float* __restrict__ htot, uint16_t* __restrict__ O, int H, int N,
-    int Nq, int Nk, float scale_log2) {
+    int Nq, int Nk, float scale_log2, FwdSaved sv) {
+  static_assert(!SAVE || MODE == MODE_FUSED, "the saved terms come from the fused mode");
   using T = Tiles<D>;
   using AS = AttnShape<D, BQ, MODE>;
   constexpr int NQW = AS::NQW, NW = AS::NWT;
@@ -510,7 +511,10 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
     ws_ = 0.f;
     wl_ = 1.f;
   }
-  const bool do_s = ws_ != 0.f;
+  // the saving variant computes the sparse branch of every head (its output
+  // is kept even where alpha is 0); the linear branch needs the totals,
+  // which the preparation pass skips for heads whose alpha is exactly 1
+  const bool do_s = SAVE || ws_ != 0.f;
   const bool lin = LIN && (wl_ != 0.f) && (nsel < Nk);
   const int nunits = (do_s || lin) ? nsel * SUB : 0;
   const int Npad = Nk * SUB * KU;
@@ -640,6 +644,7 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
   const float inv_l = lt > 0.f ? 1.f / lt : 0.f;
   const float ws_l = ws_ * inv_l;
   float wl_den = 0.f;
+  float inv_den = 0.f;  // 1 / den with a linear branch (kept by SAVE)
   constexpr int NTQ = D / 16;  // k-steps of phi(Q)
   uint4 qh[LIN ? NTQ : 1], ql[LIN ? NTQ : 1];
   char* HuHi = st0;
@@ -731,9 +736,18 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
       }
       const float den = dpart + __shfl_xor(dpart, 32);
       wl_den = wl_ / den;
+      if (SAVE && den > 0.f) inv_den = 1.f / den;
     }
   }
   if (!qw) return;
+  if (SAVE && hi == 0) {
+    // per-query terms for the backward: log2 of the sparse branch's
+    // normaliser, sum_u exp2(s_u c), as m c + log2 l (the sum of the rounded
+    // P relative to the running maximum); 1 / den of the linear branch
+    const size_t t = (size_t)row * BQ + 32 * w + l32;
+    sv.lse2[t] = (q < N && lt > 0.f) ? fmaf(sm.m, scale_log2, __log2f(lt)) : INFINITY;
+    sv.invden[t] = q < N ? inv_den : 0.f;
+  }
   const int lb = lane_base(lane);
   const size_t orow = ((size_t)bh * N + min(q, N - 1)) * D;
   // O = ws_l O_s + wl_den num, num^T = H_u^T phi(Q)^T (the D/32 output tiles
@@ -755,29 +769,49 @@ __global__ __launch_bounds__((AttnShape<D, BQ, MODE>::NWT * 64), 2) void attn_ke
         acc_n[mt] = mfma(as_bf16x8(al), as_bf16x8(qh[t]), acc_n[mt]);
       }
   }
+  // dst = fs O_s~ + fl num, O_s~ the unnormalised sparse accumulator
+  auto put = [&](uint16_t* dst, float fs, float fl) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) {
+    for (int mt = 0; mt < D / 32; ++mt) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint2 pv[2];
+      for (int j = 0; j < 2; ++j) {
+        uint2 pv[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int i4 = 2 * j + c;
-        float o[4];
+        for (int c = 0; c < 2; ++c) {
+          const int i4 = 2 * j + c;
+          float o[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          o[r] = ws_l * acc_o[mt][4 * i4 + r];
-          if (LIN) o[r] = fmaf(wl_den, acc_n[LIN ? mt : 0][4 * i4 + r], o[r]);
+          for (int r = 0; r < 4; ++r) {
+            o[r] = fs * acc_o[mt][4 * i4 + r];
+            if (LIN) o[r] = fmaf(fl, acc_n[LIN ? mt : 0][4 * i4 + r], o[r]);
+          }
+          pv[c] = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
         }
-        pv[c] = make_uint2(pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3]));
+        // lane hi = 0 keeps chunk i4 = 2j (needs the partner's pv[0]); hi = 1 keeps 2j + 1 (needs pv[1])
+        const uint2 send = hi ? pv[0] : pv[1];
+        const uint2 recv = make_uint2(__shfl_xor(send.x, 32), __shfl_xor(send.y, 32));
+        const uint4 outv = hi ? make_uint4(recv.x, recv.y, pv[1].x, pv[1].y)
+                              : make_uint4(pv[0].x, pv[0].y, recv.x, recv.y);
+        if (q < N) *reinterpret_cast<uint4*>(dst + orow + 32 * mt + 16 * j + 8 * hi) = outv;
       }
-      // lane hi = 0 keeps chunk i4 = 2j (needs the partner's pv[0]); hi = 1 keeps 2j + 1 (needs pv[1])
-      const uint2 send = hi ? pv[0] : pv[1];
-      const uint2 recv = make_uint2(__shfl_xor(send.x, 32), __shfl_xor(send.y, 32));
-      const uint4 outv = hi ? make_uint4(recv.x, recv.y, pv[1].x, pv[1].y)
-                            : make_uint4(pv[0].x, pv[0].y, recv.x, recv.y);
-      if (q < N) *reinterpret_cast<uint4*>(O + orow + 32 * mt + 16 * j + 8 * hi) = outv;
     }
+  };
+  put(O, ws_l, wl_den);
+  if (SAVE && q < N) {
+    // the branch outputs in float32: lane (query, hi) holds d = 32 mt + 8 i4
+    // + 4 hi + r of tile mt, four runs of four consecutive d
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const size_t o = orow + 32 * mt + 8 * i4 + 4 * hi;
+        const f32x16& a = acc_o[mt];
+        *reinterpret_cast<float4*>(sv.os + o) =
+            make_float4(inv_l * a[4 * i4], inv_l * a[4 * i4 + 1], inv_l * a[4 * i4 + 2], inv_l * a[4 * i4 + 3]);
+        const f32x16& n = acc_n[LIN ? mt : 0];
+        *reinterpret_cast<float4*>(sv.ol + o) = make_float4(inv_den * n[4 * i4], inv_den * n[4 * i4 + 1],
+                                                            inv_den * n[4 * i4 + 2], inv_den * n[4 * i4 + 3]);
+      }
   }
 }
 
@@ -827,7 +861,7 @@ hipError_t prep_dispatch(const Shape& s, const void* K, const void* V, const flo
 template <int D, int BQ, int SUB>
 hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
                          const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
-                         const WsLayout& L, void* O, hipStream_t st) {
+                         const WsLayout& L, void* O, hipStream_t st, const FwdSaved* saved) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const uint16_t* q = static_cast<const uint16_t*>(Q);
   const uint16_t* k = static_cast<const uint16_t*>(K);
@@ -838,7 +872,14 @@ hipError_t attn_dispatch(const Shape& s, Mode mode, const void* Q, const void* K
   const dim3 grid((unsigned)s.R());
 #define SLA_LAUNCH(M)                                                                                     \
   hipLaunchKernelGGL((attn_kernel<D, BQ, SUB, M>), grid, dim3(AttnShape<D, BQ, M>::NWT * 64), 0, st, q, k, v, \
-                     pk, rp, ci, alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2)
+                     pk, rp, ci, alpha, ht, o, s.H, s.N, s.Nq, s.Nk, sl2, FwdSaved{})
+  if (saved != nullptr) {
+    if (mode != MODE_FUSED) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_kernel<D, BQ, SUB, MODE_FUSED, true>), grid,
+                       dim3(AttnShape<D, BQ, MODE_FUSED>::NWT * 64), 0, st, q, k, v, pk, rp, ci, alpha, ht, o, s.H,
+                       s.N, s.Nq, s.Nk, sl2, *saved);
+    return hipGetLastError();
+  }
   switch (mode) {
     case MODE_SPARSE: SLA_LAUNCH(MODE_SPARSE); break;
     case MODE_DENSE: SLA_LAUNCH(MODE_DENSE); break;
@@ -863,10 +904,10 @@ hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void*
 
 hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
                             const int32_t* rp, const int32_t* ci, const float* alpha, const char* ws,
-                            const WsLayout& L, void* O, hipStream_t st) {
+                            const WsLayout& L, void* O, hipStream_t st, const FwdSaved* saved) {
 #define SLA_ATTN(DD, QQ, KK)                                                  \
   if (s.d == DD && s.bq == QQ && s.bk == KK)                                  \
-    return attn_dispatch<DD, QQ, KK / 64>(s, mode, Q, K, V, rp, ci, alpha, ws, L, O, st);
+    return attn_dispatch<DD, QQ, KK / 64>(s, mode, Q, K, V, rp, ci, alpha, ws, L, O, st, saved);
   SLA_ATTN(128, 128, 64)
   SLA_ATTN(128, 128, 128)
   SLA_ATTN(128, 64, 64)

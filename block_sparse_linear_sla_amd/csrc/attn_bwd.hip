@@ -207,7 +207,7 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ dO, const int* __restrict__ row_ptr,
     const int* __restrict__ col_idx, uint16_t* __restrict__ dQ, float* __restrict__ lse2_out,
     float* __restrict__ dd_out, const float* __restrict__ alpha, int H, int N, int Nq, int Nk, float scale_log2,
-    float inv_sqrt_d) {
+    float inv_sqrt_d, const float* __restrict__ lse2_in, const float* __restrict__ os_in) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
   using LP = LoadPlan<D, NW>;
@@ -234,6 +234,26 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
 
   f32x16 acc[D / 32];
   float lse2 = INFINITY;  // log2-sum-exp of the scaled scores; +inf: no key (P = 0)
+  // with the forward's terms: lse2 as it kept it and D = dO . O_s (this
+  // lane's half of d, then the pair sum); pass A is skipped
+  const bool saved = lse2_in != nullptr;
+  if (saved) {
+    float part = 0.f;
+    if (qv) {
+      const float* orow = os_in + ((size_t)bh * N + q) * D;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const uint4 a = __builtin_bit_cast(uint4, df[t]);
+        const float4 o0 = *reinterpret_cast<const float4*>(orow + 16 * t + 8 * hi);
+        const float4 o1 = *reinterpret_cast<const float4*>(orow + 16 * t + 8 * hi + 4);
+        const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(bf2f(elem(a, e)), o[e], part);
+      }
+    }
+    dd = part + __shfl_xor(part, 32);
+    lse2 = qv ? lse2_in[(size_t)row * BQ + 32 * w + (lane & 31)] : INFINITY;
+  }
   if (nunits > 0) {
     const auto rk = buf_rsrc(K + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
     const auto rv = buf_rsrc(V + (size_t)bh * N * D, (uint32_t)((size_t)N * D * 2));
@@ -314,13 +334,13 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
     // two loops, so that pass A holds no dQ accumulators; the unit after
     // pass A's last (pass B's first) sits in stage nunits % 2
     issue(0, st0);
-    int x = 0;
-    for (; x + 2 <= nunits; x += 2) {
-      stepA(x, st0, st1);
-      stepA(x + 1, st1, st0);
-    }
-    if (x < nunits) stepA(x, st0, st1);
-    {
+    if (!saved) {
+      int x = 0;
+      for (; x + 2 <= nunits; x += 2) {
+        stepA(x, st0, st1);
+        stepA(x + 1, st1, st0);
+      }
+      if (x < nunits) stepA(x, st0, st1);
       // the query's log2-sum-exp and D over both key halves (lanes l, l^32)
       const float M = pair_max(m);
       const float c = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m - M) * scale_log2);
@@ -339,7 +359,9 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void bwd_dq_kernel(
       }
       if (y < nunits) stepB(y, b0, b1);
     };
-    if (nunits % 2 == 0) passB(st0, st1);
+    // pass B's first unit sits in stage nunits % 2 after pass A, in stage 0
+    // without it
+    if (saved || nunits % 2 == 0) passB(st0, st1);
     else passB(st1, st0);
     wait_vm<0>();
   } else {
@@ -548,7 +570,7 @@ __global__ __launch_bounds__(64) void alpha_sum_kernel(const double* __restrict_
 template <int D, int BQ, int SUB>
 hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void* V, const void* dO, const int32_t* rp,
                         const int32_t* ci, void* dQ, void* dK, void* dV, const float* alpha, bool csc, char* ws,
-                        const BwdLayout& L, hipStream_t st) {
+                        const BwdLayout& L, hipStream_t st, const BwdSaved* saved) {
   const long long BH = (long long)s.B * s.H;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const float isd = 1.f / sqrtf((float)D);
@@ -566,7 +588,8 @@ hipError_t bwd_dispatch(const Shape& s, const void* Q, const void* K, const void
   const uint16_t* v = static_cast<const uint16_t*>(V);
   const uint16_t* g = static_cast<const uint16_t*>(dO);
   hipLaunchKernelGGL((bwd_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, q, k, v,
-                     g, rp, ci, static_cast<uint16_t*>(dQ), lse2, ddv, alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd);
+                     g, rp, ci, static_cast<uint16_t*>(dQ), lse2, ddv, alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd,
+                     saved ? saved->lse2 : nullptr, saved ? saved->os : nullptr);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, BQ, SUB>), dim3((unsigned)(BH * s.Nk * SUB)), dim3(256), 0, st, q, k, v,
                      g, col_ptr, row_idx, order, lse2, ddv, static_cast<uint16_t*>(dK), static_cast<uint16_t*>(dV),
                      alpha, s.H, s.N, s.Nq, s.Nk, sl2, isd);
@@ -632,6 +655,47 @@ BwdLayout bwd_layout(const Shape& s) {
   return L;
 }
 
+// alpha_part_kernel for bf16 dO and float32 O_s, O_l: four elements per
+// thread and step
+__global__ __launch_bounds__(256) void alpha_part_saved_kernel(const uint16_t* __restrict__ dO,
+                                                               const float* __restrict__ Os,
+                                                               const float* __restrict__ Ol, long long per, int nch,
+                                                               double* __restrict__ part) {
+  __shared__ double red[256];
+  const long long bh = blockIdx.y;
+  const long long a = (long long)blockIdx.x * ACH, b = min(per, a + ACH);
+  double acc = 0.0;
+  for (long long e = a + (long long)threadIdx.x * 4; e < b; e += 256 * 4) {
+    const size_t o = (size_t)(bh * per + e);
+    const uint2 g2 = *reinterpret_cast<const uint2*>(dO + o);
+    const float4 x = *reinterpret_cast<const float4*>(Os + o);
+    const float4 y = *reinterpret_cast<const float4*>(Ol + o);
+    const float g[4] = {bf2f(g2.x & 0xffffu), bf2f(g2.x >> 16), bf2f(g2.y & 0xffffu), bf2f(g2.y >> 16)};
+    acc += (double)g[0] * ((double)x.x - (double)y.x);
+    acc += (double)g[1] * ((double)x.y - (double)y.y);
+    acc += (double)g[2] * ((double)x.z - (double)y.z);
+    acc += (double)g[3] * ((double)x.w - (double)y.w);
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[bh * nch + blockIdx.x] = red[0];
+}
+
+hipError_t launch_alpha_grad_saved(const Shape& s, const void* dO, const float* Os, const float* Ol, float* dalpha,
+                                   char* ws, const BwdLayout& L, hipStream_t st) {
+  const long long BH = (long long)s.B * s.H, per = (long long)s.N * s.d;
+  double* part = reinterpret_cast<double*>(ws + L.apart);
+  hipLaunchKernelGGL(alpha_part_saved_kernel, dim3((unsigned)L.achunks, (unsigned)BH), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(dO), Os, Ol, per, L.achunks, part);
+  hipLaunchKernelGGL(alpha_sum_kernel, dim3((unsigned)((s.H + 63) / 64)), dim3(64), 0, st, part, s.B, s.H,
+                     L.achunks, dalpha);
+  return hipGetLastError();
+}
+
 hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
                              char* ws, const BwdLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H, per = (long long)s.N * s.d;
@@ -651,10 +715,10 @@ hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, con
 
 hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                              const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, const float* alpha,
-                             bool csc, char* ws, const BwdLayout& L, hipStream_t st) {
+                             bool csc, char* ws, const BwdLayout& L, hipStream_t st, const BwdSaved* saved) {
 #define SLA_BWD(DD, QQ, KK) \
   if (s.d == DD && s.bq == QQ && s.bk == KK) \
-    return bwd_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, alpha, csc, ws, L, st);
+    return bwd_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, alpha, csc, ws, L, st, saved);
   SLA_BWD(128, 128, 64)
   SLA_BWD(128, 128, 128)
   SLA_BWD(128, 64, 64)

@@ -253,7 +253,8 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
     const uint16_t* __restrict__ G, const uint16_t* __restrict__ Qraw, const int* __restrict__ row_ptr,
     const int* __restrict__ col_idx, const uint4* __restrict__ fragH, const float* __restrict__ tot_h,
     float* __restrict__ invden_out, float* __restrict__ dt_out, uint16_t* __restrict__ dQ, int add,
-    const float* __restrict__ alpha, int H, int N, int Nq, int Nk) {
+    const float* __restrict__ alpha, int H, int N, int Nq, int Nk, const float* __restrict__ invden_in,
+    const float* __restrict__ ol_in) {
   using T = Tiles<D>;
   constexpr int NW = BQ / 32;
   using LP = LoadPlan<D, NW>;
@@ -328,7 +329,29 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
   // phi(q) . z and phi(q) . (H h) over this lane's d of the accumulator
   // tiles; the two halves (lanes l, l^32) are added in settle
   float p1 = 0.f, p2 = 0.f;
-  if (qv) {
+  // with the forward's terms: 1 / den as it kept it (0 where the row has no
+  // linear branch) and D~ = h . O_l (this lane's half of d, then the pair
+  // sum); pass A is skipped
+  const bool saved = invden_in != nullptr;
+  if (saved) {
+    float part = 0.f;
+    if (qv) {
+      const float* orow = ol_in + ((size_t)bh * N + q) * D;
+#pragma unroll
+      for (int t = 0; t < NKK; ++t) {
+        const uint4 a = __builtin_bit_cast(uint4, hf[t]);
+        const float4 o0 = *reinterpret_cast<const float4*>(orow + 16 * t + 8 * hi);
+        const float4 o1 = *reinterpret_cast<const float4*>(orow + 16 * t + 8 * hi + 4);
+        const float o[8] = {o0.x, o0.y, o0.z, o0.w, o1.x, o1.y, o1.z, o1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = fmaf(bf2f(elem(a, e)), o[e], part);
+      }
+    }
+    const float X = part + __shfl_xor(part, 32);
+    inv = qv ? invden_in[qidx] : 0.f;
+    dtv = inv != 0.f ? X : 0.f;
+  }
+  if (qv && !saved) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -405,10 +428,12 @@ __global__ __launch_bounds__(BQ / 32 * 64, 2) void lin_dq_kernel(
       wait_vm<0>();
       __syncthreads();  // every wavefront is done with both stages
     };
-    run(IntTag<0>{});
-    settle();
+    if (!saved) {
+      run(IntTag<0>{});
+      settle();
+    }
     run(IntTag<1>{});
-  } else {
+  } else if (!saved) {
     settle();
   }
   if (hi == 0) {
@@ -671,7 +696,8 @@ __global__ __launch_bounds__(256, 2) void lin_dkdv_kernel(
 template <int D, int BQ, int SUB>
 hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const void* Vv, const void* dOv,
                         const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool add,
-                        const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st) {
+                        const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st,
+                        const BwdSaved* saved) {
   const long long BH = (long long)s.B * s.H;
   const long long QP = (long long)s.Nq * s.bq;  // per-query arrays: [bh * QP + t]
   const uint16_t* Q = static_cast<const uint16_t*>(Qv);
@@ -702,7 +728,7 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
   // rows: den, D~ and dq
   hipLaunchKernelGGL((lin_dq_kernel<D, BQ, SUB>), dim3((unsigned)s.R()), dim3(BQ / 32 * 64), 0, st, A, F, V, G, Q,
                      rp, ci, frag0, tot_h, invden, dtq, static_cast<uint16_t*>(dQ), add ? 1 : 0, alpha, s.H, s.N,
-                     s.Nq, s.Nk);
+                     s.Nq, s.Nk, saved ? saved->invden : nullptr, saved ? saved->ol : nullptr);
   // M = sum (phi(q) / den) h^T, m = sum (D~ / den) phi(q)
   hipLaunchKernelGGL((lin_outer_kernel<D>), dim3((unsigned)L.lchunks, (unsigned)BH), dim3(256), 0, st, Q, G, invden,
                      dtq, s.N, QP, L.lchunks, part);
@@ -724,10 +750,12 @@ hipError_t lin_dispatch(const Shape& s, const void* Qv, const void* Kv, const vo
 
 hipError_t launch_linear_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                              const int32_t* rp, const int32_t* ci, void* dQ, void* dK, void* dV, bool accumulate,
-                             const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st) {
+                             const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st,
+                             const BwdSaved* saved) {
 #define SLA_LBWD(DD, QQ, KK) \
   if (s.d == DD && s.bq == QQ && s.bk == KK) \
-    return lin_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, accumulate, alpha, csc, ws, L, st);
+    return lin_dispatch<DD, QQ, KK / 64>(s, Q, K, V, dO, rp, ci, dQ, dK, dV, accumulate, alpha, csc, ws, L, st, \
+                                         saved);
   SLA_LBWD(128, 128, 64)
   SLA_LBWD(128, 128, 128)
   SLA_LBWD(128, 64, 64)

@@ -335,6 +335,30 @@ int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const v
                              static_cast<const char*>(ws), L, O, static_cast<hipStream_t>(stream)));
 }
 
+int64_t sla_saved_terms_count(const sla_problem* prob) {
+  Shape s;
+  if (check_problem(prob, &s) != SLA_OK) return -1;
+  return s.R() * s.bq;
+}
+
+int sla_fused_fwd_save(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                       const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                       const void* ws, size_t ws_bytes, float* lse2, float* invden, float* O_s, float* O_l,
+                       void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !alpha || !row_ptr || !col_idx || !O || !lse2 || !invden || !O_s || !O_l)
+    return SLA_ERR_INVALID_ARG;
+  const WsLayout L = sla::ws_layout(s, false);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  const sla::FwdSaved sv{lse2, invden, O_s, O_l};
+  return hip_status(sla::launch_attn_bf16(s, sla::MODE_FUSED, Q, K, V, row_ptr, col_idx, alpha,
+                                          static_cast<const char*>(ws), L, O, static_cast<hipStream_t>(stream),
+                                          &sv));
+}
+
 int sla_dense_fwd(const sla_problem* prob, const void* Q, const void* K, const void* V, void* O,
                   void* stream) {
   Shape s;
@@ -461,6 +485,32 @@ int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const vo
     return SLA_ERR_HIP;
   return hip_status(sla::launch_linear_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, true, alpha, false, w, L,
                                            st));
+}
+
+int sla_attn_bwd_saved(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
+                       const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, const float* lse2,
+                       const float* invden, const float* O_s, const float* O_l, void* dQ, void* dK, void* dV,
+                       float* dalpha, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_problem(prob, &s);
+  if (rc != SLA_OK) return rc;
+  if (s.dtype != SLA_BF16) return SLA_ERR_UNSUPPORTED;
+  if (!Q || !K || !V || !dO || !alpha || !row_ptr || !col_idx || !lse2 || !invden || !O_s || !O_l || !dQ || !dK ||
+      !dV)
+    return SLA_ERR_INVALID_ARG;
+  const sla::BwdLayout L = sla::bwd_layout(s);
+  if (ws == nullptr || ws_bytes < L.total) return SLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(ws);
+  const sla::BwdSaved sv{lse2, invden, O_s, O_l};
+  if (sla::launch_sparse_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, alpha, true, w, L, st, &sv) !=
+      hipSuccess)
+    return SLA_ERR_HIP;
+  if (sla::launch_linear_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, true, alpha, false, w, L, st, &sv) !=
+      hipSuccess)
+    return SLA_ERR_HIP;
+  if (dalpha == nullptr) return SLA_OK;
+  return hip_status(sla::launch_alpha_grad_saved(s, dO, O_s, O_l, dalpha, w, L, st));
 }
 
 int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,

@@ -86,6 +86,23 @@ enum Mode : int {
   MODE_DENSE = 3,   // O = softmax attention over every key block
 };
 
+// What the fused forward keeps for the backward of a training step (device
+// pointers, all set; see sla_fused_fwd_save).  Per-query arrays are indexed
+// by mask row and position in the query block: row * bq + t.
+struct FwdSaved {
+  float* lse2;     // float [R*bq]: log2-sum-exp of the scaled sparse-branch scores (+inf: no listed key, or past N)
+  float* invden;   // float [R*bq]: 1 / the linear-branch denominator (0: no linear branch, or past N)
+  float* os;       // float [B,H,N,d]: the sparse branch's output O_s
+  float* ol;       // float [B,H,N,d]: the linear branch's output O_l
+};
+// The same, read by the backward.
+struct BwdSaved {
+  const float* lse2;
+  const float* invden;
+  const float* os;
+  const float* ol;
+};
+
 // mask.hip: pooling, optional router, pooled logits, selection, CSR.
 // kdone (device [H], nullable): the pooled K of every head whose value there
 // is not exactly 1 is already in the workspace (written by the preparation
@@ -109,9 +126,12 @@ hipError_t launch_soft_topk(const Shape& s, int k, double T, const float* Wq, co
 hipError_t launch_prep_bf16(const Shape& s, bool lin, const void* K, const void* V, const float* alpha,
                             bool kmeans,
                             char* ws, const WsLayout& L, hipStream_t st);
+// saved (nullable, MODE_FUSED only): also write the per-query terms and the
+// branch outputs the backward of a training step reads.
 hipError_t launch_attn_bf16(const Shape& s, Mode mode, const void* Q, const void* K, const void* V,
                             const int32_t* row_ptr, const int32_t* col_idx, const float* alpha,
-                            const char* ws, const WsLayout& L, void* O, hipStream_t st);
+                            const char* ws, const WsLayout& L, void* O, hipStream_t st,
+                            const FwdSaved* saved = nullptr);
 hipError_t launch_summary_reduce(const float* hpart, const float* alpha, int H, long long BH,
                                  int nchunk, int per, float* htot, hipStream_t st);
 
@@ -133,21 +153,29 @@ hipError_t launch_attn_i8f8(const Shape& s, const char* qbuf, const I8Layout& L,
 // alpha (device [H], nullable): the outputs are scaled by alpha_h, the
 // branch's weight in the mixed output; csc: build the mask's transpose into
 // ws first (else it is already there, from a call on the same mask).
+// saved (nullable): the forward's lse2 and O_s, so the row kernel skips the
+// pass that recomputes them (D = dO . O_s per query).
 hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                              const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
-                             const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st);
+                             const float* alpha, bool csc, char* ws, const BwdLayout& L, hipStream_t st,
+                             const BwdSaved* saved = nullptr);
 hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
                              char* ws, const BwdLayout& L, hipStream_t st);
+// the same with float32 O_s, O_l (bf16 dO), as the fused forward keeps them
+hipError_t launch_alpha_grad_saved(const Shape& s, const void* dO, const float* Os, const float* Ol, float* dalpha,
+                                   char* ws, const BwdLayout& L, hipStream_t st);
 // the mask's transpose (CSC) into the backward workspace
 hipError_t launch_csc(const Shape& s, const int32_t* row_ptr, const int32_t* col_idx, char* ws, const BwdLayout& L,
                       hipStream_t st);
 // attn_bwd_lin.hip: gradient of the linear branch (bf16) with the mask fixed;
 // accumulate: add to dQ, dK, dV instead of writing them; alpha (nullable):
 // the outputs are scaled by 1 - alpha_h; csc as for the sparse branch.
+// saved (nullable): the forward's invden and O_l, so the row kernel skips
+// the pass that recomputes them (D~ = dO . O_l per query).
 hipError_t launch_linear_bwd(const Shape& s, const void* Q, const void* K, const void* V, const void* dO,
                              const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
                              bool accumulate, const float* alpha, bool csc, char* ws, const BwdLayout& L,
-                             hipStream_t st);
+                             hipStream_t st, const BwdSaved* saved = nullptr);
 
 // attn_f32.hip: linear totals and attention for float32 inputs.
 hipError_t launch_summary_f32(const Shape& s, const void* K, const void* V, const float* alpha,

@@ -204,6 +204,37 @@ int sla_fused_fwd(const sla_problem* prob, const void* Q, const void* K, const v
                   const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
                   const void* ws, size_t ws_bytes, void* stream);
 
+/* sla_fused_fwd for a training step: the same output O (bit for bit), and
+ * also what the backward of the step reads back from the forward instead of
+ * recomputing it (sla_attn_bwd_saved), all written by the same launch:
+ *   lse2    float32 [sla_saved_terms_count] (DEVICE): for query t of mask row
+ *           r = (b, h, i) at lse2[r * bq + t - i * bq], log2 of the sparse
+ *           branch's softmax normaliser, sum over its listed keys u of
+ *           exp2(c q.k_u), c = log2(e) / sqrt(d) (SLA2 write-up §一 with the
+ *           textbook softmax); +inf where the row lists no block and past N;
+ *   invden  float32, same layout: 1 / sum over the unlisted keys of
+ *           phi(q).phi(k_u), the linear branch's denominator (SLA2 write-up
+ *           §一); 0 where the row has no linear branch (every block listed)
+ *           and past N;
+ *   O_s, O_l  float32 [B, H, N, d]: the two branches' outputs (0 for a
+ *           branch a row does not have).  float32, not bf16: the backward
+ *           forms each query's D = dO . O_s from them, and the sparse
+ *           branch's dQ carries D's error times the listed keys' common
+ *           component (a bf16 O_s puts dQ about 1.5% off on the tests'
+ *           inputs, float32 below 0.3%).
+ * The sparse branch is computed for every head, also where alpha_h is 0; the
+ * linear branch reads the totals of sla_kv_prepare, which skips heads whose
+ * alpha is exactly 1: there O_l and invden hold 0 (the branch has no weight
+ * in O, nor in the gradients of Q, K, V; the alpha gradient of such a head
+ * would need O_l from sla_linear_fwd).
+ * bf16 only (SLA_ERR_UNSUPPORTED otherwise); every pointer required.  The
+ * extra writes cost about 2 * B*H*N*d*4 bytes of HBM traffic. */
+int64_t sla_saved_terms_count(const sla_problem* prob);
+int sla_fused_fwd_save(const sla_problem* prob, const void* Q, const void* K, const void* V,
+                       const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* O,
+                       const void* ws, size_t ws_bytes, float* lse2, float* invden, float* O_s, float* O_l,
+                       void* stream);
+
 /* Dense attention softmax(Q K^T / sqrt(d)) V over every key: the textbook
  * formula that the explainer page "清华SpargeAttention2技术解析：如何让AI视频
  * 生成提速16倍" prints in its section 3 (implementation principle) as the
@@ -345,6 +376,21 @@ int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const 
 int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
                  const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
                  void* ws, size_t ws_bytes, void* stream);
+
+/* sla_attn_bwd with the terms sla_fused_fwd_save kept for the same Q, K, V,
+ * alpha and mask: the branches' row kernels take each query's normalisers
+ * from lse2 and invden and its D = dO . O_s (sparse) and dO . O_l (linear)
+ * from one dot product, instead of a first pass over the row's keys that
+ * recomputes the scores.  Same outputs and rounding as sla_attn_bwd up to
+ * those terms (the forward's normaliser sums its bf16-rounded
+ * probabilities), so within the same tolerance of the exact gradient, not
+ * bit for bit.  dalpha (DEVICE float32 [H], nullable): also the alpha
+ * gradient, as sla_alpha_grad forms it, from the float32 O_s and O_l.
+ * Terms from another forward are undefined. */
+int sla_attn_bwd_saved(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
+                       const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, const float* lse2,
+                       const float* invden, const float* O_s, const float* O_l, void* dQ, void* dK, void* dV,
+                       float* dalpha, void* ws, size_t ws_bytes, void* stream);
 
 /* Gradient of sum(O * dO) with respect to alpha for O = alpha_h O_s +
  * (1 - alpha_h) O_l (SLA2 write-up §二): dalpha[h] = sum over the head's

@@ -259,6 +259,37 @@ def test_linear_and_mixed_bwd_checks():
     assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, FAKE, n - 1, None) == WORKSPACE
 
 
+def test_saved_pair_checks():
+    """sla_fused_fwd_save and sla_attn_bwd_saved: bf16 only, every pointer
+    required, the workspaces checked; the saved-terms count is B*H*Nq*bq."""
+    L = S.lib()
+    p32 = prob()
+    p16 = prob(dtype=S.SLA_BF16, N=1000, bq=128)
+    assert L.sla_saved_terms_count(ctypes.byref(p16)) == 2 * 8 * 128
+    assert L.sla_saved_terms_count(ctypes.byref(prob(B=0))) == -1
+    sel = S.select(0.1, 0.5)
+    nf = L.sla_workspace_bytes(ctypes.byref(p16), ctypes.byref(sel))
+    fwd = [FAKE] * 7  # Q, K, V, alpha, row_ptr, col_idx, O
+    sv = [FAKE] * 4   # lse2, invden, O_s, O_l
+    assert L.sla_fused_fwd_save(ctypes.byref(p32), *fwd, FAKE, nf, *sv, None) == UNSUPPORTED
+    for i in range(11):
+        a = fwd + sv
+        a[i] = None
+        assert L.sla_fused_fwd_save(ctypes.byref(p16), *a[:7], FAKE, nf, *a[7:], None) == INVALID, i
+    assert L.sla_fused_fwd_save(ctypes.byref(p16), *fwd, None, nf, *sv, None) == WORKSPACE
+    assert L.sla_fused_fwd_save(ctypes.byref(p16), *fwd, FAKE, nf - 1, *sv, None) == WORKSPACE
+    nb = L.sla_bwd_workspace_bytes(ctypes.byref(p16))
+    bwd = [FAKE] * 14  # Q, K, V, dO, alpha, row_ptr, col_idx, lse2, invden, O_s, O_l, dQ, dK, dV
+    assert L.sla_attn_bwd_saved(ctypes.byref(p32), *bwd, None, FAKE, nb, None) == UNSUPPORTED
+    for i in range(14):
+        a = list(bwd)
+        a[i] = None
+        assert L.sla_attn_bwd_saved(ctypes.byref(p16), *a, FAKE, FAKE, nb, None) == INVALID, i
+    assert L.sla_attn_bwd_saved(ctypes.byref(p16), *bwd, FAKE, None, nb, None) == WORKSPACE
+    assert L.sla_attn_bwd_saved(ctypes.byref(p16), *bwd, None, FAKE, nb - 1, None) == WORKSPACE
+    assert L.sla_attn_bwd_saved(None, *bwd, None, FAKE, nb, None) == INVALID
+
+
 def test_mask_prepared_checks():
     L = S.lib()
     p = prob(dtype=S.SLA_BF16)
