@@ -655,27 +655,17 @@ BwdLayout bwd_layout(const Shape& s) {
   return L;
 }
 
-// alpha_part_kernel for bf16 dO and float32 O_s, O_l: four elements per
-// thread and step
-__global__ __launch_bounds__(256) void alpha_part_saved_kernel(const uint16_t* __restrict__ dO,
-                                                               const float* __restrict__ Os,
-                                                               const float* __restrict__ Ol, long long per, int nch,
+// The alpha gradient from the row kernels' per-query terms: dO . (O_s - O_l)
+// = D - D~ for every query, so each head's sum is a float64 sum of those
+// differences (chunks of ACH queries in a fixed order, then alpha_sum_kernel).
+__global__ __launch_bounds__(256) void alpha_terms_part_kernel(const float* __restrict__ dd,
+                                                               const float* __restrict__ dt, long long per, int nch,
                                                                double* __restrict__ part) {
   __shared__ double red[256];
   const long long bh = blockIdx.y;
   const long long a = (long long)blockIdx.x * ACH, b = min(per, a + ACH);
   double acc = 0.0;
-  for (long long e = a + (long long)threadIdx.x * 4; e < b; e += 256 * 4) {
-    const size_t o = (size_t)(bh * per + e);
-    const uint2 g2 = *reinterpret_cast<const uint2*>(dO + o);
-    const float4 x = *reinterpret_cast<const float4*>(Os + o);
-    const float4 y = *reinterpret_cast<const float4*>(Ol + o);
-    const float g[4] = {bf2f(g2.x & 0xffffu), bf2f(g2.x >> 16), bf2f(g2.y & 0xffffu), bf2f(g2.y >> 16)};
-    acc += (double)g[0] * ((double)x.x - (double)y.x);
-    acc += (double)g[1] * ((double)x.y - (double)y.y);
-    acc += (double)g[2] * ((double)x.z - (double)y.z);
-    acc += (double)g[3] * ((double)x.w - (double)y.w);
-  }
+  for (long long e = a + threadIdx.x; e < b; e += 256) acc += (double)dd[bh * per + e] - (double)dt[bh * per + e];
   red[threadIdx.x] = acc;
   __syncthreads();
   for (int off = 128; off > 0; off >>= 1) {
@@ -685,14 +675,15 @@ __global__ __launch_bounds__(256) void alpha_part_saved_kernel(const uint16_t* _
   if (threadIdx.x == 0) part[bh * nch + blockIdx.x] = red[0];
 }
 
-hipError_t launch_alpha_grad_saved(const Shape& s, const void* dO, const float* Os, const float* Ol, float* dalpha,
-                                   char* ws, const BwdLayout& L, hipStream_t st) {
-  const long long BH = (long long)s.B * s.H, per = (long long)s.N * s.d;
+hipError_t launch_alpha_grad_terms(const Shape& s, float* dalpha, char* ws, const BwdLayout& L, hipStream_t st) {
+  const long long BH = (long long)s.B * s.H, per = (long long)s.Nq * s.bq;
+  const int nch = (int)((per + ACH - 1) / ACH);  // <= L.achunks: per < N d
   double* part = reinterpret_cast<double*>(ws + L.apart);
-  hipLaunchKernelGGL(alpha_part_saved_kernel, dim3((unsigned)L.achunks, (unsigned)BH), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(dO), Os, Ol, per, L.achunks, part);
-  hipLaunchKernelGGL(alpha_sum_kernel, dim3((unsigned)((s.H + 63) / 64)), dim3(64), 0, st, part, s.B, s.H,
-                     L.achunks, dalpha);
+  hipLaunchKernelGGL(alpha_terms_part_kernel, dim3((unsigned)nch, (unsigned)BH), dim3(256), 0, st,
+                     reinterpret_cast<const float*>(ws + L.dd), reinterpret_cast<const float*>(ws + L.dt), per, nch,
+                     part);
+  hipLaunchKernelGGL(alpha_sum_kernel, dim3((unsigned)((s.H + 63) / 64)), dim3(64), 0, st, part, s.B, s.H, nch,
+                     dalpha);
   return hipGetLastError();
 }
 

@@ -510,7 +510,7 @@ int sla_attn_bwd_saved(const sla_problem* prob, const void* Q, const void* K, co
       hipSuccess)
     return SLA_ERR_HIP;
   if (dalpha == nullptr) return SLA_OK;
-  return hip_status(sla::launch_alpha_grad_saved(s, dO, O_s, O_l, dalpha, w, L, st));
+  return hip_status(sla::launch_alpha_grad_terms(s, dalpha, w, L, st));
 }
 
 int sla_alpha_grad(const sla_problem* prob, const void* dO, const void* O_s, const void* O_l, float* dalpha,

@@ -161,9 +161,9 @@ hipError_t launch_sparse_bwd(const Shape& s, const void* Q, const void* K, const
                              const BwdSaved* saved = nullptr);
 hipError_t launch_alpha_grad(const Shape& s, const void* dO, const void* Os, const void* Ol, float* dalpha,
                              char* ws, const BwdLayout& L, hipStream_t st);
-// the same with float32 O_s, O_l (bf16 dO), as the fused forward keeps them
-hipError_t launch_alpha_grad_saved(const Shape& s, const void* dO, const float* Os, const float* Ol, float* dalpha,
-                                   char* ws, const BwdLayout& L, hipStream_t st);
+// the same from the per-query terms D = dO . O_s and D~ = dO . O_l that the
+// row kernels of a backward call with the forward's terms left in ws
+hipError_t launch_alpha_grad_terms(const Shape& s, float* dalpha, char* ws, const BwdLayout& L, hipStream_t st);
 // the mask's transpose (CSC) into the backward workspace
 hipError_t launch_csc(const Shape& s, const int32_t* row_ptr, const int32_t* col_idx, char* ws, const BwdLayout& L,
                       hipStream_t st);

@@ -385,7 +385,9 @@ int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const vo
  * those terms (the forward's normaliser sums its bf16-rounded
  * probabilities), so within the same tolerance of the exact gradient, not
  * bit for bit.  dalpha (DEVICE float32 [H], nullable): also the alpha
- * gradient, as sla_alpha_grad forms it, from the float32 O_s and O_l.
+ * gradient, sum over the head's queries of dO . (O_s - O_l), formed as the
+ * float64 sum of the per-query D - D~ the row kernels computed from the
+ * float32 O_s and O_l (no further pass over dO).
  * Terms from another forward are undefined. */
 int sla_attn_bwd_saved(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
                        const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, const float* lse2,
