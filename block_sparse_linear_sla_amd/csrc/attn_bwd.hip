@@ -44,6 +44,8 @@
 //       tiles and reach the accumulator elements by row broadcasts, and the
 //       operand swap's barrier leaves the next unit's loads in flight.
 #include "sla.h"
+#include <algorithm>
+
 #include "sla_internal.h"
 #include "bf16_tiles.h"
 
@@ -657,13 +659,14 @@ BwdLayout bwd_layout(const Shape& s) {
 
 // The alpha gradient from the row kernels' per-query terms: dO . (O_s - O_l)
 // = D - D~ for every query, so each head's sum is a float64 sum of those
-// differences (chunks of ACH queries in a fixed order, then alpha_sum_kernel).
+// differences (chunks of `chunk` queries in a fixed order, then
+// alpha_sum_kernel).
 __global__ __launch_bounds__(256) void alpha_terms_part_kernel(const float* __restrict__ dd,
-                                                               const float* __restrict__ dt, long long per, int nch,
-                                                               double* __restrict__ part) {
+                                                               const float* __restrict__ dt, long long per,
+                                                               long long chunk, int nch, double* __restrict__ part) {
   __shared__ double red[256];
   const long long bh = blockIdx.y;
-  const long long a = (long long)blockIdx.x * ACH, b = min(per, a + ACH);
+  const long long a = (long long)blockIdx.x * chunk, b = min(per, a + chunk);
   double acc = 0.0;
   for (long long e = a + threadIdx.x; e < b; e += 256) acc += (double)dd[bh * per + e] - (double)dt[bh * per + e];
   red[threadIdx.x] = acc;
@@ -677,11 +680,14 @@ __global__ __launch_bounds__(256) void alpha_terms_part_kernel(const float* __re
 
 hipError_t launch_alpha_grad_terms(const Shape& s, float* dalpha, char* ws, const BwdLayout& L, hipStream_t st) {
   const long long BH = (long long)s.B * s.H, per = (long long)s.Nq * s.bq;
-  const int nch = (int)((per + ACH - 1) / ACH);  // <= L.achunks: per < N d
+  // chunks of 2048 queries (eight per thread) where the partials fit the
+  // region sized for L.achunks per head, longer ones otherwise
+  const long long chunk = std::max<long long>(2048, (per + L.achunks - 1) / L.achunks);
+  const int nch = (int)((per + chunk - 1) / chunk);
   double* part = reinterpret_cast<double*>(ws + L.apart);
   hipLaunchKernelGGL(alpha_terms_part_kernel, dim3((unsigned)nch, (unsigned)BH), dim3(256), 0, st,
-                     reinterpret_cast<const float*>(ws + L.dd), reinterpret_cast<const float*>(ws + L.dt), per, nch,
-                     part);
+                     reinterpret_cast<const float*>(ws + L.dd), reinterpret_cast<const float*>(ws + L.dt), per, chunk,
+                     nch, part);
   hipLaunchKernelGGL(alpha_sum_kernel, dim3((unsigned)((s.H + 63) / 64)), dim3(64), 0, st, part, s.B, s.H, nch,
                      dalpha);
   return hipGetLastError();
