@@ -489,8 +489,9 @@ def main():
         for _ in range(args.steps):
             S.sla_linear_bwd(q, k, v, dO, wl.bq, wl.bk, rp, ci, ws=bws, out=grads, accumulate=True)
         e[3].record()
+        da0 = torch.empty(wl.H, dtype=torch.float32, device=dev)
         for _ in range(args.steps):
-            S.sla_attn_bwd(q, k, v, dO, alpha, wl.bq, wl.bk, rp, ci, ws=bws, out=grads)
+            S.sla_attn_bwd(q, k, v, dO, alpha, wl.bq, wl.bk, rp, ci, ws=bws, out=grads, dalpha=da0)
         e[4].record()
         torch.cuda.synchronize()
         t_b = e[0].elapsed_time(e[1]) / args.steps
@@ -506,7 +507,8 @@ def main():
                       # float32 products and the listed-pair row and column walks
                       "linear_bwd_ms": t_lb,
                       # the mixed output's gradient (both branches, mask
-                      # transpose built once): the training backward
+                      # transpose built once, and the alpha gradient): the
+                      # training backward
                       "attn_bwd_ms": e[3].elapsed_time(e[4]) / args.steps,
                       "linear_kernels": "csc_* + lin_phi + lin_outer x2 + lin_split x3 + lin_dq + lin_dkdv"}
         # the training pair: the fused forward that also keeps each query's

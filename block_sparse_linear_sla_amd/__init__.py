@@ -99,7 +99,7 @@ def lib() -> ctypes.CDLL:
         L.sla_sparse_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_linear_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
                                      vp]
-        L.sla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.sla_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.sla_attn_bwd_saved.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                          ctypes.c_size_t, vp]
         L.sla_alpha_grad.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -465,9 +465,10 @@ def sla_linear_bwd(q, k, v, do_l, bq: int, bk: int, row_ptr, col_idx, ws=None, o
     return dq, dk, dv
 
 
-def sla_attn_bwd(q, k, v, do, alpha, bq: int, bk: int, row_ptr, col_idx, ws=None, out=None):
+def sla_attn_bwd(q, k, v, do, alpha, bq: int, bk: int, row_ptr, col_idx, ws=None, out=None, dalpha=None):
     """Gradient of sum(O * dO) for O = alpha_h O_s + (1 - alpha_h) O_l with
-    the mask fixed: returns (dQ, dK, dV)."""
+    the mask fixed: returns (dQ, dK, dV); with dalpha (float32 [H] CUDA
+    tensor) the alpha gradient is written there as well."""
     _need(q, k, v, do, like=q)
     if alpha.dtype != torch.float32 or not alpha.is_cuda or alpha.numel() != q.shape[1]:
         raise ValueError("alpha must be a float32 CUDA tensor of H values")
@@ -476,7 +477,7 @@ def sla_attn_bwd(q, k, v, do, alpha, bq: int, bk: int, row_ptr, col_idx, ws=None
     w = ws if ws is not None else bwd_workspace(prob, q.device)
     _check("sla_attn_bwd", lib().sla_attn_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
                                               _ptr(alpha.contiguous()), _ptr(row_ptr), _ptr(col_idx), _ptr(dq),
-                                              _ptr(dk), _ptr(dv), _ptr(w), w.numel(), _stream()))
+                                              _ptr(dk), _ptr(dv), _ptr(dalpha), _ptr(w), w.numel(), _stream()))
     return dq, dk, dv
 
 

@@ -471,7 +471,7 @@ int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const 
 
 int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
                  const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
-                 void* ws, size_t ws_bytes, void* stream) {
+                 float* dalpha, void* ws, size_t ws_bytes, void* stream) {
   Shape s;
   int rc = check_problem(prob, &s);
   if (rc != SLA_OK) return rc;
@@ -483,8 +483,11 @@ int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const vo
   char* w = static_cast<char*>(ws);
   if (sla::launch_sparse_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, alpha, true, w, L, st) != hipSuccess)
     return SLA_ERR_HIP;
-  return hip_status(sla::launch_linear_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, true, alpha, false, w, L,
-                                           st));
+  if (sla::launch_linear_bwd(s, Q, K, V, dO, row_ptr, col_idx, dQ, dK, dV, true, alpha, false, w, L, st) !=
+      hipSuccess)
+    return SLA_ERR_HIP;
+  if (dalpha == nullptr) return SLA_OK;
+  return hip_status(sla::launch_alpha_grad_terms(s, dalpha, w, L, st));
 }
 
 int sla_attn_bwd_saved(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,

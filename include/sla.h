@@ -371,11 +371,15 @@ int sla_linear_bwd(const sla_problem* prob, const void* Q, const void* K, const 
  * the forward's mixing ratios.  bf16 only.  Outputs dQ, dK, dV [B, H, N, d]
  * bf16, every element written (the sparse part rounded to bf16, the linear
  * part added and rounded again).  Needs the sla_bwd_workspace_bytes
- * workspace.  The gradient with respect to alpha is sla_alpha_grad's.
+ * workspace.  dalpha (DEVICE float32 [H], nullable): also the gradient with
+ * respect to alpha, sum over the head's queries of dO . (O_s - O_l), formed
+ * as the float64 sum of the per-query D = dO . O_s and D~ = dO . O_l that the
+ * branches' row kernels compute anyway (float32, from the exact branch
+ * outputs; sla_alpha_grad does the same from O_s and O_l given).
  * Deterministic, as sla_sparse_bwd. */
 int sla_attn_bwd(const sla_problem* prob, const void* Q, const void* K, const void* V, const void* dO,
                  const float* alpha, const int32_t* row_ptr, const int32_t* col_idx, void* dQ, void* dK, void* dV,
-                 void* ws, size_t ws_bytes, void* stream);
+                 float* dalpha, void* ws, size_t ws_bytes, void* stream);
 
 /* sla_attn_bwd with the terms sla_fused_fwd_save kept for the same Q, K, V,
  * alpha and mask: the branches' row kernels take each query's normalisers

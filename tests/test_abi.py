@@ -250,13 +250,13 @@ def test_linear_and_mixed_bwd_checks():
     assert L.sla_linear_bwd(ctypes.byref(p16), *lin, 0, FAKE, n - 1, None) == WORKSPACE
     assert L.sla_linear_bwd(None, *lin, 0, FAKE, n, None) == INVALID
     mixed = [FAKE] * 10  # Q, K, V, dO, alpha, row_ptr, col_idx, dQ, dK, dV
-    assert L.sla_attn_bwd(ctypes.byref(p32), *mixed, FAKE, n, None) == UNSUPPORTED
+    assert L.sla_attn_bwd(ctypes.byref(p32), *mixed, None, FAKE, n, None) == UNSUPPORTED
     for i in range(10):
         a = list(mixed)
         a[i] = None
-        assert L.sla_attn_bwd(ctypes.byref(p16), *a, FAKE, n, None) == INVALID, i
-    assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, None, n, None) == WORKSPACE
-    assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, FAKE, n - 1, None) == WORKSPACE
+        assert L.sla_attn_bwd(ctypes.byref(p16), *a, FAKE, FAKE, n, None) == INVALID, i
+    assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, FAKE, None, n, None) == WORKSPACE
+    assert L.sla_attn_bwd(ctypes.byref(p16), *mixed, None, FAKE, n - 1, None) == WORKSPACE
 
 
 def test_saved_pair_checks():

@@ -221,7 +221,8 @@ def test_attn_bwd_mixed(N, d, bq, bk):
                          full_rows={H * Nq - 1})
     q, k, v, dO, rpt, cit = _inputs(x, rp, ci, seed=9)
     alpha = torch.tensor([0.7, 1.0, 0.0, 0.35], dtype=torch.float32)
-    dq, dk, dv = S.sla_attn_bwd(q, k, v, dO.cuda(), alpha.cuda(), bq, bk, rpt, cit)
+    da = torch.full((H,), float("nan"), dtype=torch.float32, device="cuda")
+    dq, dk, dv = S.sla_attn_bwd(q, k, v, dO.cuda(), alpha.cuda(), bq, bk, rpt, cit, dalpha=da)
     torch.cuda.synchronize()
     rs = O.sparse_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
     rl = O.linear_branch_backward(x.Q, x.K, x.V, bq, bk, rp, ci, dO)
@@ -232,6 +233,15 @@ def test_attn_bwd_mixed(N, d, bq, bk):
         # alpha = 0 head the linear branch's alone
         _compare(t[:, 1:2], rs[n][:, 1:2], n + " (alpha 1)")
         _compare(t[:, 2:3], rl[n][:, 2:3], n + " (alpha 0)")
+    # the alpha gradient from the row kernels' per-query terms, every head
+    # (the ends included: both branches' terms are formed whatever alpha is)
+    Os = O.assemble(O.sparse_branch(x.Q, x.K, x.V, bq, bk, rp, ci), 1, H, N, d, bq)
+    Ol = O.assemble(O.linear_branch(x.Q, x.K, x.V, bq, bk, rp, ci), 1, H, N, d, bq)
+    exact = O.alpha_grad(dO, Os, Ol)
+    scale = (np.abs(O.as_f64(dO)) * (np.abs(Os) + np.abs(Ol))).sum(axis=(0, 2, 3))
+    got = da.cpu().double().numpy()
+    print(f"  dalpha {got}, exact {exact}")
+    assert np.all(np.abs(got - exact) <= 1e-4 * scale), (got, exact)
 
 
 def test_attn_bwd_480p_two_heads():
