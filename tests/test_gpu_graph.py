@@ -101,3 +101,55 @@ def test_backward_graph_replays():
         print(f"  replay {n}", flush=True)
         for name, t, e in zip(("dQ", "dK", "dV"), grads, egrads):
             assert torch.equal(t.view(torch.int16), e.view(torch.int16)), f"replay {n}: {name} differs"
+
+
+def test_training_pair_graph_replays():
+    """sla_fused_fwd_save followed by sla_attn_bwd_saved (with the alpha
+    gradient) captured as one graph on a ragged shape with the library's
+    mask, replayed on three input sets; every output of every replay equals
+    the eager calls' bit for bit."""
+    wl = gen.Workload("adhoc", B=1, H=3, grid=(1, 1, 5001), d=128, bq=128, bk=64, k_frac=0.1, p=0.7,
+                      dtype="bf16", router=False, seed=29)
+    sets = []
+    for s in (5, 6, 7):
+        x = gen.make(wl, seed=s)
+        g = torch.Generator().manual_seed(s)
+        sets.append(U.dev(x.Q, x.K, x.V, x.alpha) + (torch.randn(tuple(x.Q.shape), generator=g).to(torch.bfloat16).cuda(),))
+    q, k, v, a, do = (t.clone() for t in sets[0])
+    rp, ci = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    prob, sel = S.problem(q, wl.bq, wl.bk), S.select(wl.k_frac, wl.p)
+
+    def buffers():
+        ws = S.workspace(prob, sel, q.device)
+        _, sv = S.sla_fused_fwd_save(q, k, v, a, wl.bq, wl.bk, rp, ci, ws)  # allocates the saved terms
+        return dict(ws=ws, bws=S.bwd_workspace(prob, q.device), o=torch.empty_like(q), sv=sv,
+                    grads=tuple(torch.empty_like(q) for _ in range(3)),
+                    da=torch.empty(q.shape[1], dtype=torch.float32, device=q.device))
+
+    def run(b):
+        S.sla_kv_prepare(k, v, wl.bq, wl.bk, b["ws"], a)
+        S.sla_fused_fwd_save(q, k, v, a, wl.bq, wl.bk, rp, ci, b["ws"], out=b["o"], saved=b["sv"])
+        S.sla_attn_bwd_saved(q, k, v, do, a, wl.bq, wl.bk, rp, ci, b["sv"], ws=b["bws"], out=b["grads"],
+                             dalpha=b["da"])
+
+    st, eg = buffers(), buffers()
+    run(st)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    print("[graph] capturing the training pair", flush=True)
+    with torch.cuda.graph(g):
+        run(st)
+    torch.cuda.synchronize()
+    for n, src in enumerate(sets):
+        for dst, t in zip((q, k, v, a, do), src):
+            dst.copy_(t)
+        g.replay()
+        torch.cuda.synchronize()
+        run(eg)
+        torch.cuda.synchronize()
+        print(f"  replay {n}", flush=True)
+        pairs = [("O", st["o"], eg["o"]), ("dalpha", st["da"], eg["da"])]
+        pairs += [(key, st["sv"][key], eg["sv"][key]) for key in ("lse2", "invden", "o_s", "o_l")]
+        pairs += [(name, t, e) for name, t, e in zip(("dQ", "dK", "dV"), st["grads"], eg["grads"])]
+        for name, t, e in pairs:
+            assert torch.equal(t, e), f"replay {n}: {name} differs"
