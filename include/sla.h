@@ -21,7 +21,8 @@
  *      head (SLA2 write-up §二);
  *   4. with the mask held fixed, the gradients of both branches, of the mix
  *      and of alpha (SLA2 write-up §四: training with the selection fixed
- *      per step), bf16.
+ *      per step), bf16; optionally from per-query terms the forward kept
+ *      (sla_fused_fwd_save, sla_attn_bwd_saved).
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller.  Q, K, V and
@@ -38,8 +39,9 @@
  *   - Every function returns a status: SLA_OK (0) or a negative code.
  *     Argument errors are detected on the host before anything is launched
  *     and nothing is then written.  SLA_ERR_HIP reports a launch failure.
- *   - No global state: calls on different streams may run concurrently as
- *     long as their workspaces and outputs do not overlap.
+ *   - No global state, except the static scratch of sla_mask_noalloc (see
+ *     there): other calls on different streams may run concurrently as long
+ *     as their workspaces and outputs do not overlap.
  *   - Supported: dtype fp32 or bf16; d in {64, 128}; bq, bk in {64, 128};
  *     Nk <= 4096; B * H * N * d < 2^31.
  */
