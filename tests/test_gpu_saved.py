@@ -87,29 +87,31 @@ def _check_saved(x, rp, ci, alpha, sv, rows):
 
 
 SMALL = [
-    # N, d, bq, bk
-    (1000, 128, 128, 64),
-    (777, 64, 64, 128),
+    # N, d, bq, bk, B
+    (1000, 128, 128, 64, 1),
+    (777, 64, 64, 128, 1),
+    (1500, 128, 64, 64, 1),
+    (900, 64, 128, 128, 2),
 ]
 
 
-@pytest.mark.parametrize("N,d,bq,bk", SMALL)
-def test_saved_forward_and_backward_small(N, d, bq, bk):
+@pytest.mark.parametrize("N,d,bq,bk,B", SMALL)
+def test_saved_forward_and_backward_small(N, d, bq, bk, B):
     """Four heads with alpha 0.7, 1, 0, 0.35 (both ends), an empty row and a
     fully listed row: every row of the forward's terms and the backward's
     every element against the oracle."""
-    print(f"[saved] N={N} d={d} bq={bq} bk={bk}", flush=True)
+    print(f"[saved] N={N} d={d} bq={bq} bk={bk} B={B}", flush=True)
     H = 4
-    wl = gen.Workload("adhoc", B=1, H=H, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
+    wl = gen.Workload("adhoc", B=B, H=H, grid=(1, 1, N), d=d, bq=bq, bk=bk, k_frac=0.1, p=0.0,
                       dtype="bf16", router=False, seed=31)
     x = gen.make(wl)
     Nq, Nk = O.n_blocks(N, bq), O.n_blocks(N, bk)
-    rp, ci = _random_csr(np.random.default_rng(13), H, Nq, Nk, 0.3, empty_rows={2, 5},
-                         full_rows={H * Nq - 1})
+    rp, ci = _random_csr(np.random.default_rng(13), B * H, Nq, Nk, 0.3, empty_rows={2, 5},
+                         full_rows={B * H * Nq - 1})
     alpha = torch.tensor([0.7, 1.0, 0.0, 0.35], dtype=torch.float32)
     (q, k, v, a, rpt, cit), o_plain, o, sv = _forward(x, rp, ci, alpha)
     assert torch.equal(o.view(torch.int16), o_plain.view(torch.int16)), "O differs from sla_fused_fwd's"
-    rows = [(0, h, i) for h in range(H) for i in range(Nq)]
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(Nq)]
     _check_saved(x, rp, ci, alpha.numpy(), sv, rows)
     dO = torch.from_numpy(np.random.default_rng(9).normal(size=tuple(x.Q.shape))).to(torch.bfloat16)
     dq, dk, dv, da = S.sla_attn_bwd_saved(q, k, v, dO.cuda(), a, bq, bk, rpt, cit, sv)
@@ -128,8 +130,8 @@ def test_saved_forward_and_backward_small(N, d, bq, bk):
     got = da.cpu().double().numpy()
     want = (G * (os_ - ol_)).sum(axis=(0, 2, 3))
     assert np.abs(got - want).max() <= 1e-5 * np.abs(want).max(), (got, want)
-    Os_ref = O.assemble(O.sparse_branch(x.Q, x.K, x.V, bq, bk, rp, ci), 1, H, N, d, bq)
-    Ol_ref = O.assemble(O.linear_branch(x.Q, x.K, x.V, bq, bk, rp, ci), 1, H, N, d, bq)
+    Os_ref = O.assemble(O.sparse_branch(x.Q, x.K, x.V, bq, bk, rp, ci), B, H, N, d, bq)
+    Ol_ref = O.assemble(O.linear_branch(x.Q, x.K, x.V, bq, bk, rp, ci), B, H, N, d, bq)
     exact = (G * (Os_ref - Ol_ref)).sum(axis=(0, 2, 3))
     scale = (np.abs(G) * (np.abs(Os_ref) + np.abs(Ol_ref))).sum(axis=(0, 2, 3))
     print(f"  dalpha {got}, exact {exact}")
