@@ -306,3 +306,15 @@ def test_mask_prepared_checks():
     assert L.sla_mask_prepared(ctypes.byref(p), ctypes.byref(sel), *args, cap, FAKE, n - 1, None) == WORKSPACE
     assert L.sla_mask_prepared(None, ctypes.byref(sel), *args, cap, FAKE, n, None) == INVALID
     assert L.sla_mask_prepared(ctypes.byref(p), None, *args, cap, FAKE, n, None) == INVALID
+
+
+def test_binding_refuses_host_tensors_and_wrong_saved_dtypes():
+    """The Python binding checks its tensors before any call reaches the
+    library: host tensors, and saved branch outputs that are not float32."""
+    import torch
+    q = torch.zeros(1, 2, 256, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        S.sla_sparse_fwd(q, q, q, 64, 64, None, None)
+    saved = dict(lse2=torch.zeros(8), invden=torch.zeros(8), o_s=q, o_l=q)
+    with pytest.raises(ValueError):
+        S.sla_attn_bwd_saved(q, q, q, q, torch.zeros(2), 64, 64, None, None, saved)
