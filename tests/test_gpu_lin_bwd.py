@@ -303,3 +303,35 @@ def test_attn_bwd_two_batches():
     for t, n in zip((dq, dk, dv), ("dQ", "dK", "dV")):
         _compare(t, a * rs[n] + (1 - a) * rl[n], n)
         _compare(t[1:], (a * rs[n] + (1 - a) * rl[n])[1:], n + " (second batch)")
+
+
+def test_attn_bwd_bitwise_deterministic():
+    """The mixed backward at the 480p length (two heads, the library's mask):
+    two calls, the second on a workspace filled with 0xff bytes first, give
+    the same dQ, dK, dV and alpha gradient bit for bit (the column kernels'
+    launch order comes from LDS atomics and may differ between runs; every
+    sum still runs in a fixed order).  The same for the saved-terms call."""
+    wl = gen.WORKLOADS["video480p-sla2-N32760"]
+    print(f"[lin-bwd] determinism {wl.name}, 2 heads", flush=True)
+    x = gen.make(wl, heads=2)
+    q, k, v, a = U.dev(x.Q, x.K, x.V, x.alpha)
+    rp, ci = S.sla_mask(q, k, wl.bq, wl.bk, wl.k_frac, wl.p)
+    g = torch.from_numpy(np.random.default_rng(21).normal(size=tuple(x.Q.shape))).to(torch.bfloat16).cuda()
+    prob = S.problem(q, wl.bq, wl.bk)
+    ws = S.workspace(prob, S.select(wl.k_frac, wl.p), q.device)
+    S.sla_kv_prepare(k, v, wl.bq, wl.bk, ws, a)
+    _, sv = S.sla_fused_fwd_save(q, k, v, a, wl.bq, wl.bk, rp, ci, ws)
+    outs = []
+    for fill in (None, 0xFF):
+        bws = S.bwd_workspace(prob, q.device)
+        if fill is not None:
+            bws.fill_(fill)
+        da = torch.empty(2, dtype=torch.float32, device="cuda")
+        r = S.sla_attn_bwd(q, k, v, g, a, wl.bq, wl.bk, rp, ci, ws=bws, dalpha=da) + (da,)
+        bws.fill_(0xFF)
+        r2 = S.sla_attn_bwd_saved(q, k, v, g, a, wl.bq, wl.bk, rp, ci, sv, ws=bws)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in r + r2])
+    names = ("dQ", "dK", "dV", "dalpha", "saved dQ", "saved dK", "saved dV", "saved dalpha")
+    for n, t0, t1 in zip(names, outs[0], outs[1]):
+        assert torch.equal(t0, t1), f"{n} differs between runs"
